@@ -1,0 +1,219 @@
+"""CPU tests that pin the oracle (oracle/recurrence.c and oracle/chunked.py)
+to what the pages and the mathematics fix.  No GPU involved."""
+from __future__ import annotations
+
+import os
+import re
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import chunked
+from tests import pins
+from tests.pins import rel, rand_case
+
+
+@pytest.mark.parametrize("pin", pins.ALL_RECURRENCE_PINS, ids=lambda p: p.__name__)
+def test_recurrence_pin(pin):
+    pin(oracle.recurrence)
+
+
+def test_chunk_form_equals_recurrence():
+    pins.pin_chunk_form_equals_recurrence(oracle.recurrence, chunked)
+
+
+def test_printed_decay_tables():
+    """[SD] section 2.2: alpha=0.5, C=4 gives gamma = (0.5, 0.25, 0.125,
+    0.0625) and Gamma(4,1) = 0.125; the alpha=0.9 D and Gamma matrices.
+    Checked through the chunked oracle's step a1 (log2 cumsum) and step a2
+    (with one key channel and k = 1, K+ K-^T is exactly the ratio matrix)."""
+    gold = pins.read_golden("sd_decay_tables.txt")
+    C = 4
+    for alpha, key in ((0.5, None), (0.9, "Gamma_alpha0.9")):
+        g = np.full((1, C, 1), np.log(alpha))
+        gam = chunked.chunk_log2_cumsum(g, C)[0, :, 0]
+        if alpha == 0.5:
+            np.testing.assert_allclose(np.exp2(gam), gold["gamma_alpha0.5"][0], rtol=1e-14)
+        one = np.ones((1, C, 1, 1))
+        prep = chunked.separable_prep(one, one, gam[None, :, None], C)
+        full = prep["Kp"][0, :, 0] @ prep["Km"][0, :, 0].T        # D_ij = gamma_i / gamma_j
+        Gam = np.tril(full)
+        if alpha == 0.5:
+            assert abs(Gam[3, 0] - gold["gamma41_alpha0.5"][0, 0]) < 1e-14
+        else:
+            np.testing.assert_allclose(full, gold["D_alpha0.9"], atol=6e-4)
+            np.testing.assert_allclose(Gam, gold[key], atol=6e-4)
+            assert np.all(np.triu(Gam, 1) == 0)
+
+
+def test_separable_identity():
+    """[KDA] 1.2: StrictLower(K+ K-^T)_ci = sum_d k_c[d] e^(gamma_c[d]-gamma_i[d]) k_i[d]
+    for i < c (the page reports 1.94e-16 between the two); also
+    tril(Q~ K-^T) = the same weighted inner product with q on the left."""
+    r = np.random.default_rng(5)
+    C, Dk = 16, 8
+    k = r.standard_normal((1, C, 1, Dk))
+    q = r.standard_normal((1, C, 1, Dk))
+    g = np.log(r.uniform(0.9, 0.999, (1, C, 1, Dk)))
+    gam = chunked.chunk_log2_cumsum(g, C)
+    prep = chunked.separable_prep(q, k, gam, C)
+    M = np.tril(prep["Kp"][0, :, 0] @ prep["Km"][0, :, 0].T, -1)
+    Aqk = np.tril(prep["Qp"][0, :, 0] @ prep["Km"][0, :, 0].T)
+    G = np.cumsum(g[0, :, 0], axis=0)          # natural-log units
+    naive = np.zeros((C, C))
+    naive_qk = np.zeros((C, C))
+    for c in range(C):
+        for i in range(c + 1):
+            w = np.exp(G[c] - G[i])
+            naive_qk[c, i] = np.sum(q[0, c, 0] * w * k[0, i, 0])
+            if i < c:
+                naive[c, i] = np.sum(k[0, c, 0] * w * k[0, i, 0])
+    assert rel(M, naive) < 1e-14
+    assert rel(Aqk, naive_qk) < 1e-14
+    # chunk-end quantities: phi = e^(gamma_C), Kbar = k e^(gamma_C - gamma)
+    assert rel(prep["phi"][0, 0, 0], np.exp(G[-1])) < 1e-14
+    assert rel(prep["Kbar"][0, :, 0], k[0, :, 0] * np.exp(G[-1] - G)) < 1e-14
+
+
+def test_local_cumsum_resets_per_chunk():
+    """[EVO] 3.5 / [SD] section 0: the cumulative sum restarts in every chunk
+    (including a ragged last chunk)."""
+    r = np.random.default_rng(6)
+    g = -r.uniform(0, 1, (2, 37, 3))
+    gam = chunked.chunk_log2_cumsum(g, 8)
+    for s in range(0, 37, 8):
+        e = min(s + 8, 37)
+        np.testing.assert_allclose(gam[:, s:e], np.cumsum(g[:, s:e], 1) / np.log(2), rtol=1e-14)
+        np.testing.assert_allclose(gam[:, s], g[:, s] / np.log(2), rtol=1e-14)
+
+
+def test_triangular_inverse_pins():
+    """T = (I + A)^-1 for strictly lower A: equals the finite Neumann series
+    sum_{n<C} (-A)^n ([DPLR] 4.1, the path-sum view of the inverse) and a
+    textbook forward substitution (scipy solve_triangular)."""
+    from scipy.linalg import solve_triangular
+
+    r = np.random.default_rng(7)
+    C = 64
+    A = np.tril(r.standard_normal((C, C)) * 0.05, -1)
+    T = np.linalg.inv(np.eye(C) + A)
+    neu = np.zeros((C, C))
+    P = np.eye(C)
+    for _ in range(C):
+        neu += P
+        P = P @ (-A)
+    assert np.max(np.abs(P)) == 0.0 or np.max(np.abs(P)) < 1e-300  # nilpotent: (-A)^C = 0
+    assert rel(T, neu) < 1e-13
+    assert rel(T, solve_triangular(np.eye(C) + A, np.eye(C), lower=True, unit_diagonal=True)) < 1e-13
+    # the inverse the chunked oracle produces for a real chunk, same checks
+    q, k, v, g, bt, _ = rand_case("kda", B=1, T=C, H=1, Dk=16, Dv=8, seed=8)
+    res = chunked.chunk_forward("kda", q, k, v, g, bt, None, C)
+    A2, T2 = res.A[0, :, 0], res.Tinv[0, :, 0]
+    assert np.all(np.triu(A2) == 0)
+    assert rel(T2, solve_triangular(np.eye(C) + A2, np.eye(C), lower=True, unit_diagonal=True)) < 1e-12
+
+
+def test_beta_pairings():
+    """[KDA] 3.2-3.3: A = diag(beta) M with W = T diag(beta) K+ (row beta) and
+    A = M diag(beta) with W = diag(beta) T K+ (column beta) are both right;
+    mixing them is wrong and, with random beta, shows up at the 1e-1 level
+    (the page measured rel-L2 1.3e-1).  The mixed pairing is planted in the
+    oracle's step a3 and must be caught by the comparison with the
+    recurrence."""
+    def col_beta(Kp, Km, V, beta):
+        n = Kp.shape[0]
+        A = np.tril(Kp @ Km.T, -1) * beta[None, :]
+        T = np.linalg.inv(np.eye(n) + A)
+        return A, T, beta[:, None] * (T @ Kp), beta[:, None] * (T @ V)
+
+    def mixed(Kp, Km, V, beta):   # column-beta A with the row-beta application
+        n = Kp.shape[0]
+        A = np.tril(Kp @ Km.T, -1) * beta[None, :]
+        T = np.linalg.inv(np.eye(n) + A)
+        return A, T, T @ (beta[:, None] * Kp), T @ (beta[:, None] * V)
+
+    q, k, v, g, bt, _ = rand_case("kda", B=2, T=12, H=2, Dk=4, Dv=4, seed=9)
+    o, _ = oracle.recurrence("kda", q, k, v, g, bt)
+    good = chunked.chunk_forward("kda", q, k, v, g, bt, None, 4).o
+    good2 = chunked.chunk_forward("kda", q, k, v, g, bt, None, 4, ut=col_beta).o
+    bad = chunked.chunk_forward("kda", q, k, v, g, bt, None, 4, ut=mixed).o
+    l2 = lambda a, b: np.linalg.norm(a - b) / np.linalg.norm(b)
+    assert l2(good, o) < 1e-13 and l2(good2, o) < 1e-13
+    assert l2(bad, o) > 1e-2
+    # invisible when beta is constant (the page's warning)
+    btc = np.full_like(bt, 0.5)
+    o_c, _ = oracle.recurrence("kda", q, k, v, g, btc)
+    bad_c = chunked.chunk_forward("kda", q, k, v, g, btc, None, 4, ut=mixed).o
+    assert l2(bad_c, o_c) < 1e-13
+
+
+def test_value_slices_independent():
+    """[KDA] 3.4: splitting d_v into blocks changes nothing (each value column
+    of the state evolves on its own) -- the GPU path relies on this."""
+    q, k, v, g, bt, h0 = rand_case("kda", B=1, T=20, H=2, Dk=4, Dv=8, seed=12, h0_std=0.5)
+    o, s = oracle.recurrence("kda", q, k, v, g, bt, h0)
+    for blk in (1, 2, 4):
+        for j in range(0, 8, blk):
+            oj, sj = oracle.recurrence("kda", q, k, v[..., j:j + blk], g, bt, h0[:, :, j:j + blk])
+            assert rel(oj, o[..., j:j + blk]) < 1e-13 and rel(sj, s[:, :, j:j + blk]) < 1e-13
+
+
+def test_empty_and_threads():
+    q, k, v, g, bt, h0 = rand_case("gdn", B=2, T=0, H=2, Dk=4, Dv=3, seed=13, h0_std=1.0)
+    o, s = oracle.recurrence("gdn", q, k, v, g, bt, h0)
+    assert o.shape == (2, 0, 2, 3) and rel(s, h0) == 0.0
+    q, k, v, g, bt, h0 = rand_case("gdn", B=3, T=9, H=3, Dk=4, Dv=3, seed=14)
+    o1, s1 = oracle.recurrence("gdn", q, k, v, g, bt, nthreads=1)
+    o4, s4 = oracle.recurrence("gdn", q, k, v, g, bt, nthreads=4)
+    assert np.array_equal(o1, o4) and np.array_equal(s1, s4)
+
+
+# --------------------------------------------------------------------------
+# Planted mistakes: each is a plausible slip in the C oracle (dropped term,
+# wrong sign, wrong index, transposed operand, gate on the wrong side).  A
+# mutated copy is compiled into a temporary directory and the pins above must
+# reject every one of them.
+# --------------------------------------------------------------------------
+MUTATIONS = {
+    "beta_dropped_in_erase": ("S[(size_t)i * Dk + j] -= bt * Sk[i] * kt[j];",
+                              "S[(size_t)i * Dk + j] -= Sk[i] * kt[j];"),
+    "beta_dropped_in_write": ("S[(size_t)i * Dk + j] += bt * vt[i] * kt[j];",
+                              "S[(size_t)i * Dk + j] += vt[i] * kt[j];"),
+    "erase_sign": ("S[(size_t)i * Dk + j] -= bt * Sk[i] * kt[j];",
+                   "S[(size_t)i * Dk + j] += bt * Sk[i] * kt[j];"),
+    "gate_channel_reversed": ("a[j] = exp(J->g[row * Dk + j]);",
+                              "a[j] = exp(J->g[row * Dk + (Dk - 1 - j)]);"),
+    "readout_with_k": ("for (int j = 0; j < Dk; ++j) acc += S[(size_t)i * Dk + j] * qt[j];",
+                       "for (int j = 0; j < Dk; ++j) acc += S[(size_t)i * Dk + j] * kt[j];"),
+    "la_decay_after_write": ("S[(size_t)i * Dk + j] = a[j] * S[(size_t)i * Dk + j] + vt[i] * kt[j];",
+                             "S[(size_t)i * Dk + j] = a[j] * (S[(size_t)i * Dk + j] + vt[i] * kt[j]);"),
+    "gate_not_exponentiated": ("const double s = exp(J->g[row]);", "const double s = 1.0 + J->g[row];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "recurrence.c")).read()
+    old, new = MUTATIONS[name]
+    assert src.count(old) == 1, f"mutation anchor not found: {name}"
+    mut = src.replace(old, new)
+    cpath = tmp_path / "mut.c"
+    cpath.write_text(mut)
+    so = str(tmp_path / "libmut.so")
+    oracle.build(str(cpath), so)
+
+    def rec(*a, **kw):
+        return oracle.recurrence(*a, lib_path=so, **kw)
+
+    caught = []
+    for pin in pins.ALL_RECURRENCE_PINS:
+        try:
+            pin(rec)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the planted mistake {name}"
