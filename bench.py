@@ -1,0 +1,170 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunkwise gated-delta-rule forward on one MI355X.
+
+One step = one full forward pass (every step of the hot path: log2 cumsum,
+separable prep and UT transform in the chunk-parallel kernel, then the
+sequential state pass fused with the chunk output) over the KDA bf16
+long-context workload (B=1, H=32, T=32768, dk=dv=128, C=64), inputs resident
+in HBM.  Prints one JSON line.
+
+Per-kernel durations come from HIP events recorded on the launch stream
+between the two kernel launches of every timed step.  The CPU baseline is
+the fp64 oracle (test infrastructure) timed on a bounded sample of the same
+workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+METRIC = "fwd tokens/sec (1 GPU) for KDA/GDN chunked, bf16, T=32k; % MFMA peak"
+
+
+def algorithmic(kind: str, w, io_bytes: int):
+    """Bytes each kernel must move per token-head (its own inputs and
+    outputs) and the method's MFMA flops per token-head (fixed formula)."""
+    dk, dv, C = w.Dk, w.Dv, w.C
+    gate = 4 * dk if kind == "kda" else 4
+    beta = 4 if kind != "decay_la" else 0
+    # K1 reads q, k, v, g, beta; writes the chunk record (W, Q~, Kbar^T,
+    # Aqk, U^T per row of the chunk, phi per chunk)
+    rec_row = io_bytes * (3 * dk + C + dv) + 4 * dk / C
+    k1 = io_bytes * (2 * dk + dv) + gate + beta + rec_row
+    # K2 reads the record, writes o; h0/hT once per chain (negligible)
+    k2 = rec_row + io_bytes * dv
+    delta = kind != "decay_la"
+    # per token-head MFMA flops of the method: KK^T, QK^T, W/U, A*Vnew, W*S,
+    # Kbar^T*Vnew, Q*S and the inverse (full-tile count, fixed formula)
+    if delta:
+        flops = 2 * dk * C + 2 * dk * C + 2 * C * (dk + dv) + 2 * C * dv + 3 * 2 * dk * dv + 2 * C * C / 3
+    else:
+        flops = 2 * dk * C + 2 * C * dv + 2 * 2 * dk * dv
+    return k1, k2, flops
+
+
+def cpu_baseline(w, x, max_tokens: int, threads: int):
+    import oracle
+    import torch
+    Ts = min(w.T, max_tokens)
+    sl = lambda t: None if t is None else t[:, :Ts].contiguous()
+    h0 = None if x["h0"] is None else x["h0"].transpose(-1, -2).contiguous()
+    args = [sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"])]
+    t0 = time.perf_counter()
+    oracle.recurrence(w.kind, *args, h0, nthreads=threads)
+    dt = time.perf_counter() - t0
+    del torch
+    tokens = w.B * Ts
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{w.kind} B={w.B} H={w.H} first {Ts} of {w.T} tokens, fp64 token recurrence, "
+                      f"{threads} threads, {dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="kda_bf16_long")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=16384,
+                    help="tokens of the workload the CPU oracle is timed on")
+    ap.add_argument("--cpu-threads", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only (the forward is a per-(batch, head) "
+              "chain; multi-GPU sharding is a design note, not built). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import delta_rule_rnn_amd as dra
+    from delta_rule_rnn_amd import ops
+    from delta_rule_rnn_amd.inputs import WORKLOADS, generate
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = generate(w)
+    d = {n: (t.to(dev) if t is not None else None) for n, t in x.items()}
+    B, T, H, Dk, Dv = w.B, w.T, w.H, w.Dk, w.Dv
+    io = d["q"].dtype
+    ws = ops.alloc_workspace(w.kind, d["q"], d["v"], w.C)
+    o = torch.empty(B, T, H, Dv, dtype=io, device=dev)
+    hT = torch.empty(B, H, Dk, Dv, dtype=torch.float32, device=dev)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        dra.intra(w.kind, d["q"], d["k"], d["v"], d["g"], d["beta"], w.C, workspace=ws, flags=flags)
+        if ev is not None:
+            ev[1].record(stream)
+        dra.inter(w.kind, ws, B, T, H, Dk, Dv, io, h0=d["h0"], out=o, hT=hT, chunk_size=w.C)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k1 = [e[0].elapsed_time(e[1]) for e in evs]
+    k2 = [e[1].elapsed_time(e[2]) for e in evs]
+    ms = wall * 1000.0 / args.steps
+    tokens = B * T
+    value = tokens / (ms / 1000.0)
+
+    io_b = 2 if io == torch.bfloat16 else 4
+    b1, b2, flops = algorithmic(w.kind, w, io_b)
+    th = B * T * H
+    k1_ms, k2_ms = sum(k1) / len(k1), sum(k2) / len(k2)
+    kern = {
+        "intra": {"avg_ms": k1_ms, "bytes": b1 * th, "gbs": b1 * th / (k1_ms * 1e-3) / 1e9},
+        "inter": {"avg_ms": k2_ms, "bytes": b2 * th, "gbs": b2 * th / (k2_ms * 1e-3) / 1e9},
+    }
+    dom = max(kern, key=lambda n: kern[n]["avg_ms"])
+    roof = {"bound": "hbm", "kernel": dom, "achieved": round(kern[dom]["gbs"], 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(kern[dom]["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+            "per_kernel": {n: {"avg_ms": round(v["avg_ms"], 4), "alg_bytes": int(v["bytes"]),
+                               "achieved_GBs": round(v["gbs"], 1)} for n, v in kern.items()}}
+    mfma_frac = flops * th / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = args.cpu_threads or min(16, len(os.sched_getaffinity(0)))
+        cpu = cpu_baseline(w, x, args.cpu_tokens, threads)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if io == torch.bfloat16 else "f32", "data": "synthetic",
+        "config": {"workload": f"{w.kind}_fwd B={B} H={H} T={T} dk={Dk} dv={Dv} C={w.C}",
+                   "global_batch": B, "seq_len": T, "heads": H, "parallelism": "single GPU",
+                   "gate": f"a ~ U[{w.gate_lo}, {w.gate_hi}]"},
+        "mfma_frac_bf16": round(mfma_frac, 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "gate_flags": int(flags.item()),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,13 @@
+"""Chunkwise gated-delta-rule forward (KDA / Gated DeltaNet / scalar-decay
+linear attention) for AMD Instinct MI355X (gfx950).
+
+The computation lives in libdeltarule.so (HIP kernels behind the C ABI of
+include/deltarule.h); this package only marshals torch tensors into it.
+Importing the package does not load the library; the first op call does, and
+raises if the library has not been built.
+"""
+from .ops import (DeltaRuleError, chunk_cumsum, decay_la_fwd, forward, gdn_fwd, inter, intra,
+                  kda_fwd, kda_prep, unpack_records, workspace_bytes)
+
+__all__ = ["kda_fwd", "gdn_fwd", "decay_la_fwd", "forward", "chunk_cumsum", "kda_prep", "intra",
+           "inter", "unpack_records", "workspace_bytes", "DeltaRuleError"]

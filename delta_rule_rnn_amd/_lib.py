@@ -1,0 +1,52 @@
+"""ctypes loader of libdeltarule.so (the C ABI of include/deltarule.h).
+
+The library is never built on import: build it with ``__graft_entry__.build()``
+(or ``python -m delta_rule_rnn_amd.build``).  A missing library raises."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdeltarule.so")
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+
+# name -> (restype, argtypes); mirrors include/deltarule.h
+SIGNATURES = {
+    "dr_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "dr_record_bytes": (_sz, [_i, _i, _i, _i]),
+    "kda_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp, _vp]),
+    "gdn_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp, _vp]),
+    "decay_la_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "dr_chunk_cumsum": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp]),
+    "dr_kda_prep": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp]),
+    "dr_intra": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp, _vp]),
+    "dr_inter": (_i, [_i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "dr_status_string": (ctypes.c_char_p, [_i]),
+    "dr_abi_version": (_i, []),
+}
+
+_LIB = None
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise LibraryMissing(
+            f"{path} is not built; run __graft_entry__.build() (hipcc, gfx950) first")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _LIB = lib
+    return lib

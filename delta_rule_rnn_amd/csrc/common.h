@@ -1,0 +1,126 @@
+// common.h -- shared device helpers for the gfx950 kernels: element types,
+// MFMA operand fragments, and the chunk-record layout.
+//
+// MFMA operand fragments.  All matrix products use 16x16 output tiles and a
+// reduction block of 32.  For one tile, lane l (0..63) owns row/column
+// (l % 16) and the 8 reduction slots (l / 16, j), j = 0..7.  A fragment holds
+// those 8 operand values; which reduction index a slot stands for is chosen
+// by whoever fills the fragment, the same way for both operands (a dot
+// product does not depend on the order of its terms).  "Natural" fragments
+// use index 8*(l/16) + j.
+//
+//   bf16: one v_mfma_f32_16x16x32_bf16 per fragment pair.
+//   fp32: eight v_mfma_f32_16x16x4_f32; instruction j consumes slot j of
+//         every lane, so the reduction runs over the same 32 indices.
+//
+// Accumulator layout (both instruction shapes): lane l holds the four rows
+// 4*(l/16) + i, i = 0..3, of column l % 16.  Two accumulator tiles whose rows
+// are assigned with prow() form a natural B fragment over their 32 rows,
+// which lets a product's result feed the next product without leaving
+// registers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dr {
+
+typedef __bf16 bf16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kChunk = 64;     // C
+constexpr int kThreads = 256;  // 4 waves per workgroup
+constexpr float kLog2e = 1.4426950408889634f;
+
+enum Kind { KIND_KDA = 0, KIND_GDN = 1, KIND_LA = 2 };
+
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { float v[8]; };
+
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f(float x) { return x; }
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+
+__device__ __forceinline__ void mma(f32x4& c, const Frag<bf16>& a, const Frag<bf16>& b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& c, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], c, 0, 0, 0);
+}
+
+// 8 contiguous elements (16-byte aligned for bf16, 32-byte for fp32).
+__device__ __forceinline__ Frag<bf16> ld_frag(const bf16* p) {
+    Frag<bf16> f;
+    f.v = *reinterpret_cast<const bf16x8*>(p);
+    return f;
+}
+__device__ __forceinline__ Frag<float> ld_frag(const float* p) {
+    Frag<float> f;
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+    return f;
+}
+__device__ __forceinline__ void st_frag(bf16* p, const Frag<bf16>& f) {
+    *reinterpret_cast<bf16x8*>(p) = f.v;
+}
+__device__ __forceinline__ void st_frag(float* p, const Frag<float>& f) {
+    reinterpret_cast<float4*>(p)[0] = make_float4(f.v[0], f.v[1], f.v[2], f.v[3]);
+    reinterpret_cast<float4*>(p)[1] = make_float4(f.v[4], f.v[5], f.v[6], f.v[7]);
+}
+// fragment slot access
+__device__ __forceinline__ float frag_get(const Frag<bf16>& f, int j) { return (float)f.v[j]; }
+__device__ __forceinline__ float frag_get(const Frag<float>& f, int j) { return f.v[j]; }
+__device__ __forceinline__ void frag_set(Frag<bf16>& f, int j, float x) { f.v[j] = (bf16)x; }
+__device__ __forceinline__ void frag_set(Frag<float>& f, int j, float x) { f.v[j] = x; }
+
+// Four contiguous elements (8-byte aligned for bf16).
+__device__ __forceinline__ void ld4(const bf16* p, float* out) {
+    const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
+    out[0] = (float)x[0]; out[1] = (float)x[1]; out[2] = (float)x[2]; out[3] = (float)x[3];
+}
+__device__ __forceinline__ void ld4(const float* p, float* out) {
+    const float4 x = *reinterpret_cast<const float4*>(p);
+    out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
+}
+__device__ __forceinline__ void st4(bf16* p, const float* in) {
+    bf16x4 x;
+    x[0] = (bf16)in[0]; x[1] = (bf16)in[1]; x[2] = (bf16)in[2]; x[3] = (bf16)in[3];
+    *reinterpret_cast<bf16x4*>(p) = x;
+}
+__device__ __forceinline__ void st4(float* p, const float* in) {
+    *reinterpret_cast<float4*>(p) = make_float4(in[0], in[1], in[2], in[3]);
+}
+
+// Row of a 32-row block held by row r (0..15) of its first (half = 0) or
+// second (half = 1) 16-row tile, chosen so that the pair's accumulators form a
+// natural B fragment: lane group q holds rows 8q..8q+3 (half 0) and
+// 8q+4..8q+7 (half 1).
+__device__ __forceinline__ int prow(int half, int r) { return 8 * (r >> 2) + 4 * half + (r & 3); }
+
+// ---------------------------------------------------------------------------
+// Chunk record: the operands the sequential pass streams, one record per
+// (b, h, chunk).  Offsets in elements of the I/O type T except phi (float).
+// ---------------------------------------------------------------------------
+template <typename T, int DK, int DV>
+struct Rec {
+    static constexpr int C = kChunk;
+    static constexpr size_t W = 0;                   // [C][DK]
+    static constexpr size_t QT = W + (size_t)C * DK; // [C][DK]
+    static constexpr size_t KBT = QT + (size_t)C * DK; // [DK][C]
+    static constexpr size_t AQK = KBT + (size_t)DK * C; // [C][C]
+    static constexpr size_t UT = AQK + (size_t)C * C;  // [DV][C]
+    static constexpr size_t END = UT + (size_t)DV * C;
+    static constexpr size_t PHI_BYTE = END * sizeof(T);      // [DK] float
+    static constexpr size_t BYTES = ((PHI_BYTE + DK * sizeof(float)) + 255) / 256 * 256;
+};
+
+}  // namespace dr

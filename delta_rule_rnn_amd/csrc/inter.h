@@ -1,0 +1,234 @@
+// inter.h -- K2: the sequential inter-chunk state pass (step a4) fused with
+// the chunk output (step a5).
+//
+// Page keys: [KDA] "TileLang 实战：KDA 从零到一–Kimi Delta Attention";
+// [SD] "TileLang 实战：KDA 从零到一--标量衰减"; [DPLR] "RNN的复兴04:线性注意力
+// 并行计算DPLR".
+//
+// For each (batch, head), chunks in order, with S the [Dk, Dv] state
+// (transpose of the pages' S) kept in fp32 MFMA accumulators:
+//   Vnew = U - W S               (decay_la: Vnew = V)
+//   O    = Q~ S + Aqk Vnew       (entry state read + intra-chunk term)
+//   S   <- Diag(phi) S + Kbar^T Vnew
+// ([DPLR] 5.3.5 standard KDA/GDN form; [KDA] 3.2 reference B; the state is
+// updated only after the output used the entry state and the decay is
+// applied before the accumulation, [SD] 5.2 ordering rules 1 and 2).
+//
+// Work split.  A workgroup owns one (b, h) chain and DVS = 16*NTN value
+// columns (value columns evolve independently, [KDA] 3.4).  Its 4 waves split
+// the rows: wave w produces 16 positions of Vnew and O (rows 32*(w/2) +
+// prow(w%2, r)) and 32 key rows of S (rows 32w..32w+31).  Two LDS exchanges
+// per chunk hand Vnew and S to every wave as natural B fragments.  All
+// operands of the next chunk are prefetched into registers while the current
+// chunk computes.
+//
+// Block mapping: the NV = Dv/DVS workgroups of a chain read the same W, Q~,
+// Kbar, Aqk; consecutive logical ids are placed on the same XCD (hardware
+// dispatches workgroup i to XCD i % 8) so they share that XCD's L2.
+#pragma once
+
+#include "common.h"
+
+namespace dr {
+
+template <typename T, int DK, int NTN>
+struct InterOps {
+    static constexpr int NKB = DK / 32;
+    Frag<T> w[NKB];        // W rows of this wave's positions
+    Frag<T> qt[NKB];       // Q~ rows of this wave's positions
+    Frag<T> aqk[2];        // Aqk rows, key blocks 0..1
+    Frag<T> kb[2][2];      // Kbar^T rows (half, key block) of this wave's S rows
+    float u[NTN][4];       // U (or V) at this lane's 4 positions, per n-tile
+    float phi[2][4];       // phi at this lane's S rows (half, i)
+};
+
+template <int KIND, typename T, int DK, int DV, int NTN>
+__device__ __forceinline__ void inter_load(InterOps<T, DK, NTN>& op, const uint8_t* recb, int wave,
+                                           int lane, int dv0)
+{
+    using R = Rec<T, DK, DV>;
+    constexpr int C = kChunk;
+    constexpr int NKB = DK / 32;
+    constexpr bool DELTA = KIND != KIND_LA;
+    const T* base = reinterpret_cast<const T*>(recb);
+    const int r16 = lane & 15, grp = lane >> 4;
+    const int kbP = wave >> 1, halfP = wave & 1;
+    const int p = 32 * kbP + prow(halfP, r16);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+        if constexpr (DELTA) op.w[kb] = ld_frag(base + R::W + p * DK + 32 * kb + 8 * grp);
+        op.qt[kb] = ld_frag(base + R::QT + p * DK + 32 * kb + 8 * grp);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+        if (kb <= kbP) op.aqk[kb] = ld_frag(base + R::AQK + p * C + 32 * kb + 8 * grp);
+    if (wave < NKB) {
+        const float* phi = reinterpret_cast<const float*>(recb + R::PHI_BYTE);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int dk = 32 * wave + prow(half, r16);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) op.kb[half][kb] = ld_frag(base + R::KBT + dk * C + 32 * kb + 8 * grp);
+            ld4(phi + 32 * wave + 8 * grp + 4 * half, op.phi[half]);
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < NTN; ++n)
+        ld4(base + R::UT + (size_t)(dv0 + 16 * n + r16) * C + 32 * kbP + 8 * grp + 4 * halfP, op.u[n]);
+}
+
+template <int KIND, typename T, int DK, int DV, int NTN>
+__global__ __launch_bounds__(kThreads) void inter_kernel(const uint8_t* __restrict__ ws,
+                                                         const float* __restrict__ h0,
+                                                         T* __restrict__ o, float* __restrict__ hT,
+                                                         int Tlen, int H, int NT)
+{
+    using R = Rec<T, DK, DV>;
+    constexpr int C = kChunk;
+    constexpr int DVS = 16 * NTN;
+    constexpr int NV = DV / DVS;
+    constexpr int NKB = DK / 32;
+    constexpr bool DELTA = KIND != KIND_LA;
+    static_assert(DV % DVS == 0, "value split");
+
+    // B-fragment exchange buffers: [block][n-tile][lane][8 slots]
+    __shared__ __attribute__((aligned(16))) T sS[NKB][NTN][64][8];
+    __shared__ __attribute__((aligned(16))) T sV[2][NTN][64][8];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, grp = lane >> 4;
+    const int kbP = wave >> 1, halfP = wave & 1;
+    const bool ownS = wave < NKB;
+
+    const int G = gridDim.x, bid = blockIdx.x;
+    const int logical = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+    const int chain = logical / NV, slice = logical % NV;
+    const int b = chain / H, h = chain % H;
+    const int dv0 = slice * DVS;
+
+    // ---- initial state --------------------------------------------------
+    f32x4 S[2][NTN];
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int n = 0; n < NTN; ++n) {
+            f32x4 s = {0.f, 0.f, 0.f, 0.f};
+            if (ownS && h0 != nullptr) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int dk = 32 * wave + 8 * grp + 4 * half + i;
+                    s[i] = h0[(((size_t)b * H + h) * DK + dk) * DV + dv0 + 16 * n + r16];
+                }
+            }
+            S[half][n] = s;
+        }
+    auto publish_state = [&]() {
+        if (ownS) {
+#pragma unroll
+            for (int n = 0; n < NTN; ++n)
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    float tmp[4] = {S[half][n][0], S[half][n][1], S[half][n][2], S[half][n][3]};
+                    st4(&sS[wave][n][lane][4 * half], tmp);
+                }
+        }
+    };
+    publish_state();
+    __syncthreads();
+
+    const uint8_t* chain_rec = ws + ((size_t)b * H + h) * (size_t)NT * R::BYTES;
+    InterOps<T, DK, NTN> cur, nxt;
+    if (NT > 0) inter_load<KIND, T, DK, DV, NTN>(cur, chain_rec, wave, lane, dv0);
+
+    for (int c = 0; c < NT; ++c) {
+        if (c + 1 < NT)
+            inter_load<KIND, T, DK, DV, NTN>(nxt, chain_rec + (size_t)(c + 1) * R::BYTES, wave, lane, dv0);
+
+        // entry-state fragments
+        Frag<T> fS[NKB][NTN];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int n = 0; n < NTN; ++n) fS[kb][n] = ld_frag(&sS[kb][n][lane][0]);
+
+        f32x4 P[NTN], O[NTN];
+#pragma unroll
+        for (int n = 0; n < NTN; ++n) {
+            P[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+            O[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int n = 0; n < NTN; ++n) {
+                if constexpr (DELTA) mma(P[n], cur.w[kb], fS[kb][n]);
+                mma(O[n], cur.qt[kb], fS[kb][n]);
+            }
+        // Vnew at this lane's 4 positions
+#pragma unroll
+        for (int n = 0; n < NTN; ++n) {
+            float vn[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vn[i] = DELTA ? cur.u[n][i] - P[n][i] : cur.u[n][i];
+            st4(&sV[kbP][n][lane][4 * halfP], vn);
+        }
+        __syncthreads();
+
+        Frag<T> fV[2][NTN];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int n = 0; n < NTN; ++n) fV[kb][n] = ld_frag(&sV[kb][n][lane][0]);
+
+        // intra-chunk term (causal: key blocks up to this wave's block)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            if (kb > kbP) break;
+#pragma unroll
+            for (int n = 0; n < NTN; ++n) mma(O[n], cur.aqk[kb], fV[kb][n]);
+        }
+        // store O
+        {
+            const int pbase = c * C + 32 * kbP + 8 * grp + 4 * halfP;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = pbase + i;
+                if (t < Tlen) {
+                    T* dst = o + (((size_t)b * Tlen + t) * H + h) * DV + dv0 + r16;
+#pragma unroll
+                    for (int n = 0; n < NTN; ++n) dst[16 * n] = from_f<T>(O[n][i]);
+                }
+            }
+        }
+        // state update: decay first, then accumulate
+        if (ownS) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+#pragma unroll
+                for (int n = 0; n < NTN; ++n) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) S[half][n][i] *= cur.phi[half][i];
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) mma(S[half][n], cur.kb[half][kb], fV[kb][n]);
+                }
+        }
+        publish_state();
+        __syncthreads();
+        if (c + 1 < NT) cur = nxt;
+    }
+
+    // ---- final state -----------------------------------------------------
+    if (ownS && hT != nullptr) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int n = 0; n < NTN; ++n)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int dk = 32 * wave + 8 * grp + 4 * half + i;
+                    hT[(((size_t)b * H + h) * DK + dk) * DV + dv0 + 16 * n + r16] = S[half][n][i];
+                }
+    }
+}
+
+}  // namespace dr

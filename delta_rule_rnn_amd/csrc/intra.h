@@ -1,0 +1,440 @@
+// intra.h -- K1: chunk-parallel steps a1 (log2 cumsum), a2 (separable
+// exponent prep) and a3 (UT transform), fused.  One 256-thread workgroup per
+// (chunk, head, batch); everything stays in LDS until the chunk record is
+// written.
+//
+// Page keys: [KDA] "TileLang 实战：KDA 从零到一–Kimi Delta Attention";
+// [SD] "TileLang 实战：KDA 从零到一--标量衰减"; [GDN] "Gated DeltaNet";
+// [DPLR] "RNN的复兴04:线性注意力并行计算DPLR".
+//
+// Per chunk (r, i = positions, d = key channel, gamma in log2 units):
+//   a1  gamma_r = log2(e) * sum_{s<=r} g_s                 [KDA] section 0
+//   a2  K+ = k 2^gamma, K- = k 2^-gamma, Q~ = q 2^gamma,
+//       Kbar = k 2^(gamma_last - gamma), phi = 2^gamma_last  [KDA] 1.2, [DPLR] 5.3.4
+//       (scalar gates keep raw k, q and apply the ratio 2^(gamma_r - gamma_i)
+//        only where i <= r, [SD] 2.2)
+//   a3  A = diag(beta) StrictLower(K+ K-^T) (bf16 MFMA, fp32 accumulate),
+//       Aqk = Tril_incl(Q~ K-^T),
+//       T = (I + A)^-1: the four 16x16 diagonal blocks by forward
+//       substitution (one lane per column), the off-diagonal blocks by
+//       T_ij = -T_ii sum_{j<=m<i} A_im T_mj on fp32 MFMA,
+//       W = T diag(beta) K+, U = T diag(beta) V                [KDA] 3.2-3.3
+#pragma once
+
+#include "common.h"
+
+namespace dr {
+
+template <int KIND, typename T, int DK, int DV>
+struct IntraCfg {
+    static constexpr int C = kChunk;
+    static constexpr int LDK = DK + 8;   // padded row (elements) of [C][DK] tiles
+    static constexpr int LDF = C + 4;    // padded row (floats) of [C][C] fp32 tiles
+    static constexpr int LDV = C + 8;    // padded row (elements) of [DV][C] tiles
+    static constexpr size_t R_KP = 0;
+    static constexpr size_t SZ_KP = (size_t)C * LDK * sizeof(T);
+    static constexpr size_t SZ_VT = (size_t)DV * LDV * sizeof(T);
+    static constexpr size_t SZ_F = (size_t)C * LDF * sizeof(float);
+    static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
+    static constexpr size_t R_KM = R_KP + SZ_KP;                 // K-  | later beta*V^T
+    static constexpr size_t R_QP = R_KM + mx(SZ_KP, SZ_VT);      // Q~  | later T (fp32)
+    static constexpr size_t R_A = R_QP + mx(SZ_KP, SZ_F);        // A   | later W staging
+    static constexpr size_t R_SMALL = R_A + mx(SZ_F, SZ_KP);
+    static constexpr int NCP = DK / 2;          // channel pairs
+    static constexpr int NQ = kThreads / NCP;   // position groups
+    static constexpr int PL = C / NQ;           // positions per group
+    static constexpr size_t R_BETA = R_SMALL;                        // [C] float
+    static constexpr size_t R_GAM = R_BETA + C * sizeof(float);      // [C] float (scalar gates)
+    static constexpr size_t R_TOT = R_GAM + C * sizeof(float);       // [NQ][DK] float
+    static constexpr size_t BYTES = R_TOT + (size_t)NQ * DK * sizeof(float);
+    static_assert(DK == 64 || DK == 128, "DK");
+    static_assert(DV == DK, "DV == DK");
+    static_assert(NQ * PL == C, "thread layout");
+};
+
+// Lower-triangular 16x16 tiles (ti >= tj) of a 64x64 matrix, in a fixed order.
+__device__ __forceinline__ void lower_tile(int idx, int& ti, int& tj) {
+    // 0:(0,0) 1:(1,0) 2:(1,1) 3:(2,0) 4:(2,1) 5:(2,2) 6:(3,0) 7:(3,1) 8:(3,2) 9:(3,3)
+    ti = idx >= 6 ? 3 : idx >= 3 ? 2 : idx >= 1 ? 1 : 0;
+    tj = idx - (ti * (ti + 1)) / 2;
+}
+
+// 16x16x16 fp32 product of two LDS blocks: Y = X[16x16] * Z[16x16]
+// (natural reduction index 4*(lane/16) + s for step s).
+__device__ __forceinline__ f32x4 mm16_lds(const float* X, int ldx, const float* Z, int ldz, int lane,
+                                         f32x4 acc) {
+    const int r = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[r * ldx + 4 * q + s], Z[(4 * q + s) * ldz + r], acc,
+                                                   0, 0, 0);
+    return acc;
+}
+// Y = X[16x16] (LDS) * Z where Z is a 16x16 accumulator tile in registers:
+// step i uses accumulator element i, i.e. reduction index 4*(lane/16) + i.
+__device__ __forceinline__ f32x4 mm16_acc(const float* X, int ldx, f32x4 Z, int lane) {
+    const int r = lane & 15, q = lane >> 4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[r * ldx + 4 * q + i], Z[i], acc, 0, 0, 0);
+    return acc;
+}
+
+template <int KIND, typename T, int DK, int DV>
+__global__ __launch_bounds__(kThreads) void intra_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, uint8_t* __restrict__ ws,
+    unsigned* __restrict__ flags, int Tlen, int H, int NT)
+{
+    using Cfg = IntraCfg<KIND, T, DK, DV>;
+    using R = Rec<T, DK, DV>;
+    constexpr int C = kChunk;
+    constexpr bool DELTA = KIND != KIND_LA;
+    constexpr bool PERCH = KIND == KIND_KDA;
+    constexpr int LDK = Cfg::LDK, LDF = Cfg::LDF, LDV = Cfg::LDV;
+    constexpr int NCP = Cfg::NCP, PL = Cfg::PL, NQ = Cfg::NQ;
+
+    __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::BYTES];
+    T* sKp = reinterpret_cast<T*>(smem + Cfg::R_KP);
+    T* sKm = reinterpret_cast<T*>(smem + Cfg::R_KM);
+    T* sVt = reinterpret_cast<T*>(smem + Cfg::R_KM);
+    T* sQp = reinterpret_cast<T*>(smem + Cfg::R_QP);
+    float* sT = reinterpret_cast<float*>(smem + Cfg::R_QP);
+    float* sA = reinterpret_cast<float*>(smem + Cfg::R_A);
+    T* sW = reinterpret_cast<T*>(smem + Cfg::R_A);
+    float* sBeta = reinterpret_cast<float*>(smem + Cfg::R_BETA);
+    float* sGam = reinterpret_cast<float*>(smem + Cfg::R_GAM);
+    float* sTot = reinterpret_cast<float*>(smem + Cfg::R_TOT);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, grp = lane >> 4;
+    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int t0 = c * C;
+    const int nvalid = min(C, Tlen - t0);
+    const size_t row0 = ((size_t)b * Tlen + t0) * H + h;   // token-head index of position 0
+    auto trow = [&](int p) { return row0 + (size_t)p * H; };
+
+    uint8_t* recb = ws + (((size_t)b * H + h) * NT + c) * R::BYTES;
+    T* rW = reinterpret_cast<T*>(recb) + R::W;
+    T* rQ = reinterpret_cast<T*>(recb) + R::QT;
+    T* rKb = reinterpret_cast<T*>(recb) + R::KBT;
+    T* rAqk = reinterpret_cast<T*>(recb) + R::AQK;
+    T* rU = reinterpret_cast<T*>(recb) + R::UT;
+    float* rPhi = reinterpret_cast<float*>(recb + R::PHI_BYTE);
+
+    // ---- P0: beta -------------------------------------------------------
+    if (tid < C) sBeta[tid] = (DELTA && tid < nvalid) ? beta[trow(tid)] : 0.f;
+
+    // ---- P1: a1 (gamma) + a2 (prep) -------------------------------------
+    const int cp = tid % NCP, qg = tid / NCP, ch0 = 2 * cp, p0 = qg * PL;
+    float gam[PL][2];
+    float glast[2];
+    if constexpr (PERCH) {
+        // per-channel inclusive scan: each thread owns 2 channels x PL positions
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < PL; ++i) {
+            const int p = p0 + i;
+            float2 gv = make_float2(0.f, 0.f);
+            if (p < nvalid) gv = *reinterpret_cast<const float2*>(g + trow(p) * DK + ch0);
+            s0 += gv.x; s1 += gv.y;
+            gam[i][0] = s0; gam[i][1] = s1;
+        }
+        sTot[qg * DK + ch0] = s0;
+        sTot[qg * DK + ch0 + 1] = s1;
+        __syncthreads();
+        float pre0 = 0.f, pre1 = 0.f, all0 = 0.f, all1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            const float a0 = sTot[j * DK + ch0], a1 = sTot[j * DK + ch0 + 1];
+            if (j < qg) { pre0 += a0; pre1 += a1; }
+            if (j < NQ - 1) { all0 += a0; all1 += a1; }
+        }
+        // last position of the chunk: (sum of the first NQ-1 group totals) + last total,
+        // added in the same order as the last group's own prefix + running sum
+        all0 += sTot[(NQ - 1) * DK + ch0];
+        all1 += sTot[(NQ - 1) * DK + ch0 + 1];
+        glast[0] = all0 * kLog2e; glast[1] = all1 * kLog2e;
+#pragma unroll
+        for (int i = 0; i < PL; ++i) {
+            gam[i][0] = (pre0 + gam[i][0]) * kLog2e;
+            gam[i][1] = (pre1 + gam[i][1]) * kLog2e;
+        }
+    } else {
+        // scalar gate: wave 0 scans the 64 positions
+        if (wave == 0) {
+            float x = (lane < nvalid) ? g[trow(lane)] : 0.f;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(x, off, 64);
+                if (lane >= off) x += y;
+            }
+            sGam[lane] = x * kLog2e;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < PL; ++i) gam[i][0] = gam[i][1] = sGam[p0 + i];
+        glast[0] = glast[1] = sGam[C - 1];
+    }
+
+    {
+        float kb[2][PL];
+        float mxneg = 0.f;
+#pragma unroll
+        for (int i = 0; i < PL; ++i) {
+            const int p = p0 + i;
+            float k0 = 0.f, k1 = 0.f, q0 = 0.f, q1 = 0.f;
+            if (p < nvalid) {
+                const size_t off = trow(p) * DK + ch0;
+                k0 = to_f(k[off]); k1 = to_f(k[off + 1]);
+                q0 = to_f(q[off]); q1 = to_f(q[off + 1]);
+            }
+            const float e0 = __builtin_amdgcn_exp2f(gam[i][0]);
+            const float e1 = __builtin_amdgcn_exp2f(gam[i][1]);
+            if constexpr (PERCH) {
+                const float ei0 = __builtin_amdgcn_exp2f(-gam[i][0]);
+                const float ei1 = __builtin_amdgcn_exp2f(-gam[i][1]);
+                mxneg = fmaxf(mxneg, fmaxf(-gam[i][0], -gam[i][1]));
+                sKp[p * LDK + ch0] = from_f<T>(k0 * e0);
+                sKp[p * LDK + ch0 + 1] = from_f<T>(k1 * e1);
+                sKm[p * LDK + ch0] = from_f<T>(k0 * ei0);
+                sKm[p * LDK + ch0 + 1] = from_f<T>(k1 * ei1);
+                sQp[p * LDK + ch0] = from_f<T>(q0 * e0);
+                sQp[p * LDK + ch0 + 1] = from_f<T>(q1 * e1);
+            } else {
+                sKp[p * LDK + ch0] = from_f<T>(k0);
+                sKp[p * LDK + ch0 + 1] = from_f<T>(k1);
+                sQp[p * LDK + ch0] = from_f<T>(q0);
+                sQp[p * LDK + ch0 + 1] = from_f<T>(q1);
+            }
+            rQ[p * DK + ch0] = from_f<T>(q0 * e0);
+            rQ[p * DK + ch0 + 1] = from_f<T>(q1 * e1);
+            kb[0][i] = k0 * __builtin_amdgcn_exp2f(glast[0] - gam[i][0]);
+            kb[1][i] = k1 * __builtin_amdgcn_exp2f(glast[1] - gam[i][1]);
+        }
+        // Kbar^T: PL consecutive positions per channel
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            T* dst = rKb + (size_t)(ch0 + cc) * C + p0;
+#pragma unroll
+            for (int i = 0; i < PL; i += 4) st4(dst + i, &kb[cc][i]);
+        }
+        if (qg == 0) {
+            rPhi[ch0] = __builtin_amdgcn_exp2f(glast[0]);
+            rPhi[ch0 + 1] = __builtin_amdgcn_exp2f(glast[1]);
+        }
+        if constexpr (PERCH) {
+            if (flags) {
+                const unsigned long long b16 = __ballot(mxneg >= 16.f);
+                const unsigned long long b126 = __ballot(mxneg >= 126.f);
+                if (lane == 0 && (b16 | b126))
+                    atomicOr(flags, (b16 ? 1u : 0u) | (b126 ? 2u : 0u));
+            }
+        }
+        if constexpr (!DELTA) {
+            // decay_la: the state pass reads V^T from the U^T slot
+            float vv[2][PL];
+#pragma unroll
+            for (int i = 0; i < PL; ++i) {
+                const int p = p0 + i;
+                float v0 = 0.f, v1 = 0.f;
+                if (p < nvalid) {
+                    const size_t off = trow(p) * DV + ch0;
+                    v0 = to_f(v[off]); v1 = to_f(v[off + 1]);
+                }
+                vv[0][i] = v0; vv[1][i] = v1;
+            }
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                T* dst = rU + (size_t)(ch0 + cc) * C + p0;
+#pragma unroll
+                for (int i = 0; i < PL; i += 4) st4(dst + i, &vv[cc][i]);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- P2: A and Aqk on MFMA ---------------------------------------------
+    {
+        constexpr int NKB = DK / 32;
+        constexpr int NTL = DELTA ? 20 : 10;
+        const T* kminus = PERCH ? sKm : sKp;
+        for (int idx = wave; idx < NTL; idx += 4) {
+            const bool isA = DELTA && idx < 10;
+            int ti, tj;
+            lower_tile(isA ? idx : idx - (DELTA ? 10 : 0), ti, tj);
+            const T* lhs = isA ? sKp : sQp;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const Frag<T> fa = ld_frag(lhs + (16 * ti + r16) * LDK + 32 * kb + 8 * grp);
+                const Frag<T> fb = ld_frag(kminus + (16 * tj + r16) * LDK + 32 * kb + 8 * grp);
+                mma(acc, fa, fb);
+            }
+            const int col = 16 * tj + r16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * ti + 4 * grp + i;
+                float ratio = 1.f;
+                if constexpr (!PERCH) ratio = (col <= row) ? __builtin_amdgcn_exp2f(sGam[row] - sGam[col]) : 0.f;
+                if (isA) {
+                    sA[row * LDF + col] = (col < row) ? sBeta[row] * ratio * acc[i] : 0.f;
+                } else {
+                    rAqk[row * C + col] = from_f<T>((col <= row) ? ratio * acc[i] : 0.f);
+                }
+            }
+        }
+        // zero the six upper 16x16 tiles of Aqk
+        for (int e = tid; e < 6 * 256; e += kThreads) {
+            const int u = e >> 8, x = e & 255;
+            const int ti = u < 3 ? 0 : u < 5 ? 1 : 2;
+            const int tj = u < 3 ? 1 + u : u < 5 ? u - 1 : 3;
+            rAqk[(16 * ti + (x >> 4)) * C + 16 * tj + (x & 15)] = from_f<T>(0.f);
+        }
+    }
+    if constexpr (!DELTA) return;
+    __syncthreads();
+
+    // ---- P3: T = (I + A)^-1 -----------------------------------------------
+    if (wave == 0) {
+        // diagonal blocks by forward substitution: lane = (block, column)
+        const int blk = lane >> 4, col = lane & 15;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float* arow = sA + (16 * blk + r) * LDF + 16 * blk;
+            float acc = (r == col) ? 1.f : 0.f;
+#pragma unroll
+            for (int j = 0; j < r; ++j) acc -= arow[j] * x[j];
+            x[r] = acc;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sT[(16 * blk + r) * LDF + 16 * blk + col] = x[r];
+        if ((blk & 1) == 0) {   // T01 and T23 are read by the 32-wide product below
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sT[(16 * blk + r) * LDF + 16 * (blk + 1) + col] = 0.f;
+        }
+    } else {
+        // beta * V, transposed: sVt[e][p] = beta_p v[p][e]
+        for (int e = tid - 64; e < C * (DV / 8); e += kThreads - 64) {
+            const int p = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
+            float vv[8];
+            if (p < nvalid) {
+                const T* src = v + trow(p) * DV + c8;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) vv[j] = to_f(src[j]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) vv[j] = 0.f;
+            }
+            const float bp = sBeta[p];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sVt[(c8 + j) * LDV + p] = from_f<T>(bp * vv[j]);
+        }
+    }
+    __syncthreads();
+    // off-diagonal blocks, by distance from the diagonal
+#pragma unroll
+    for (int dist = 1; dist <= 3; ++dist) {
+        if (wave < 4 - dist) {
+            const int i = wave + dist, j = wave;
+            f32x4 y = {0.f, 0.f, 0.f, 0.f};
+            for (int m = j; m < i; ++m)
+                y = mm16_lds(sA + 16 * i * LDF + 16 * m, LDF, sT + 16 * m * LDF + 16 * j, LDF, lane, y);
+            const f32x4 z = mm16_acc(sT + 16 * i * LDF + 16 * i, LDF, y, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sT[(16 * i + 4 * grp + e) * LDF + 16 * j + r16] = -z[e];
+        }
+        __syncthreads();
+    }
+
+    // ---- P4: [W | U] = T diag(beta) [K+ | V] --------------------------------
+    {
+        constexpr int NTW = DK / 16, NTN = (DK + DV) / 16, PER = NTN / 4;
+        static_assert(NTN % 4 == 0 && (NTW % PER) == 0, "n-tile split");
+        const int nt0 = wave * PER;
+        const bool isW = nt0 < NTW;
+        Frag<T> fb[PER][2];
+#pragma unroll
+        for (int n = 0; n < PER; ++n) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                if (isW) {
+                    const int col = 16 * (nt0 + n) + r16;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int p = 32 * kb + 8 * grp + j;
+                        float s = sBeta[p];
+                        if constexpr (!PERCH) s *= __builtin_amdgcn_exp2f(sGam[p]);
+                        frag_set(fb[n][kb], j, s * to_f(sKp[p * LDK + col]));
+                    }
+                } else {
+                    const int e = 16 * (nt0 + n - NTW) + r16;
+                    fb[n][kb] = ld_frag(sVt + e * LDV + 32 * kb + 8 * grp);
+                }
+            }
+        }
+        f32x4 acc[4][PER];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int n = 0; n < PER; ++n) acc[mt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                if (kb == 1 && mt < 2) continue;   // T is lower triangular
+                Frag<T> fa;
+                const float* src = sT + (16 * mt + r16) * LDF + 32 * kb + 8 * grp;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) frag_set(fa, j, src[j]);
+#pragma unroll
+                for (int n = 0; n < PER; ++n) mma(acc[mt][n], fa, fb[n][kb]);
+            }
+        }
+        if (isW) {
+            if constexpr (sizeof(T) == 2) {
+                // bf16: stage W in LDS (the A region is free now) so the global
+                // stores below are 16-byte row segments
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int n = 0; n < PER; ++n)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            sW[(16 * mt + 4 * grp + i) * LDK + 16 * (nt0 + n) + r16] = from_f<T>(acc[mt][n][i]);
+            } else {
+                // fp32: 4-byte elements, stored straight from the accumulators.
+                // (Staging these through LDS hit a miscompile in this toolchain:
+                // two of the four row stores were merged into one ds_write2_b32
+                // whose first offset was encoded wrong at Dk = 128.)
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int n = 0; n < PER; ++n)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            rW[(16 * mt + 4 * grp + i) * DK + 16 * (nt0 + n) + r16] = from_f<T>(acc[mt][n][i]);
+            }
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int n = 0; n < PER; ++n) {
+                    const int e = 16 * (nt0 + n - NTW) + r16;
+                    float vals[4] = {acc[mt][n][0], acc[mt][n][1], acc[mt][n][2], acc[mt][n][3]};
+                    st4(rU + (size_t)e * C + 16 * mt + 4 * grp, vals);
+                }
+        }
+    }
+    if constexpr (sizeof(T) == 2) {
+        __syncthreads();
+        for (int e = tid; e < C * (DK / 8); e += kThreads) {
+            const int p = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
+            st_frag(rW + p * DK + c8, ld_frag(sW + p * LDK + c8));
+        }
+    }
+}
+
+}  // namespace dr

@@ -1,0 +1,110 @@
+// steps.h -- the first two steps as stand-alone kernels.  Both are
+// bandwidth-bound elementwise/scan passes.
+//
+// Step a1, chunk-local log2 cumsum ("TileLang 实战：KDA 从零到一–Kimi Delta
+// Attention" section 0; "07 · linear 路线（二）：衰减机制的演进" section 3.5):
+//   gamma[cC + r] = log2(e) * sum_{s <= r} g[cC + s], restarting each chunk.
+// Step a2, separable-exponent prep (same KDA page, section 1.2; "RNN的复兴04"
+// section 5.3.4 for phi and Kbar):
+//   kp = k 2^gamma, km = k 2^-gamma, qp = q 2^gamma,
+//   kbar = k 2^(gamma_last - gamma), phi = 2^gamma_last.
+#pragma once
+
+#include "common.h"
+
+namespace dr {
+
+// One workgroup per (chunk, b*H + h).  D >= 2: thread d walks the chunk's
+// positions for channel d (loads of consecutive channels are contiguous).
+// D == 1: wave 0 scans the 64 positions with lane shuffles.
+__global__ __launch_bounds__(kThreads) void cumsum_kernel(const float* __restrict__ g,
+                                                          float* __restrict__ gamma, int Tlen, int H,
+                                                          int D)
+{
+    constexpr int C = kChunk;
+    const int c = blockIdx.x, bh = blockIdx.y;
+    const int b = bh / H, h = bh % H;
+    const int t0 = c * C;
+    const int nvalid = min(C, Tlen - t0);
+    const size_t row0 = ((size_t)b * Tlen + t0) * H + h;
+    if (D == 1) {
+        if (threadIdx.x < 64) {
+            const int lane = threadIdx.x;
+            float x = (lane < nvalid) ? g[row0 + (size_t)lane * H] : 0.f;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(x, off, 64);
+                if (lane >= off) x += y;
+            }
+            if (lane < nvalid) gamma[row0 + (size_t)lane * H] = x * kLog2e;
+        }
+        return;
+    }
+    for (int d = threadIdx.x; d < D; d += blockDim.x) {
+        float s = 0.f;
+        for (int p = 0; p < nvalid; ++p) {
+            const size_t off = (row0 + (size_t)p * H) * D + d;
+            s += g[off];
+            gamma[off] = s * kLog2e;
+        }
+    }
+}
+
+// One thread per (token-head row, 8 channels).
+template <typename T, int DK>
+__global__ __launch_bounds__(kThreads) void prep_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ gamma,
+    T* __restrict__ qp, T* __restrict__ kp, T* __restrict__ km, T* __restrict__ kbar,
+    float* __restrict__ phi, unsigned* __restrict__ flags, int B, int Tlen, int H, int NT)
+{
+    constexpr int C = kChunk;
+    constexpr int G8 = DK / 8;
+    const size_t nitems = (size_t)B * Tlen * H * G8;
+    const size_t it = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    bool f16 = false, f126 = false;
+    if (it < nitems) {
+        const int cg = (int)(it % G8);
+        const size_t row = it / G8;                 // ((b*T + t)*H + h)
+        const int h = (int)(row % H);
+        const size_t bt = row / H;
+        const int t = (int)(bt % Tlen);
+        const int b = (int)(bt / Tlen);
+        const int c = t / C;
+        const int tl = min(Tlen, (c + 1) * C) - 1;  // last valid row of this chunk
+        const size_t lrow = ((size_t)b * Tlen + tl) * H + h;
+        const size_t off = row * DK + 8 * cg;
+        const Frag<float> gm = ld_frag(gamma + off);
+        const Frag<float> gl = ld_frag(gamma + lrow * DK + 8 * cg);
+        Frag<T> fk = ld_frag(k + off), fq = ld_frag(q + off);
+        Frag<T> okp, okm, oqp, okb;
+        float mx = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float x = gm.v[j];
+            const float e = __builtin_amdgcn_exp2f(x), ei = __builtin_amdgcn_exp2f(-x);
+            const float kk = frag_get(fk, j), qq = frag_get(fq, j);
+            mx = fmaxf(mx, -x);
+            frag_set(okp, j, kk * e);
+            frag_set(okm, j, kk * ei);
+            frag_set(oqp, j, qq * e);
+            frag_set(okb, j, kk * __builtin_amdgcn_exp2f(gl.v[j] - x));
+        }
+        if (kp) st_frag(kp + off, okp);
+        if (km) st_frag(km + off, okm);
+        if (qp) st_frag(qp + off, oqp);
+        if (kbar) st_frag(kbar + off, okb);
+        if (phi && t == c * C) {
+            float* dst = phi + (((size_t)b * NT + c) * H + h) * DK + 8 * cg;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dst[j] = __builtin_amdgcn_exp2f(gl.v[j]);
+        }
+        f16 = mx >= 16.f;
+        f126 = mx >= 126.f;
+    }
+    if (flags) {
+        const unsigned long long b16 = __ballot(f16), b126 = __ballot(f126);
+        if ((threadIdx.x & 63) == 0 && (b16 | b126)) atomicOr(flags, (b16 ? 1u : 0u) | (b126 ? 2u : 0u));
+    }
+}
+
+}  // namespace dr

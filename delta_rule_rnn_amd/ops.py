@@ -1,0 +1,215 @@
+"""Thin torch-facing binding over the C ABI (argument marshalling only: every
+step of the computation runs in the library's HIP kernels).
+
+Tensors must live on the GPU, be contiguous and use the documented dtypes;
+outputs and the workspace are allocated here with torch and handed to the
+library as raw pointers, together with torch's current HIP stream.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+DR_F32, DR_BF16 = 0, 1
+KINDS = {"kda": 0, "gdn": 1, "decay_la": 2}
+CHUNK = 64
+
+
+class DeltaRuleError(RuntimeError):
+    pass
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        msg = _lib.load().dr_status_string(status).decode()
+        raise DeltaRuleError(f"{what} failed: {msg} (status {status})")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DR_BF16
+    if t.dtype == torch.float32:
+        return DR_F32
+    raise DeltaRuleError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _need(t: Optional[torch.Tensor], name: str, dtype=None, shape=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise DeltaRuleError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise DeltaRuleError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise DeltaRuleError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise DeltaRuleError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def workspace_bytes(kind: str, B: int, T: int, H: int, Dk: int, Dv: int, dtype: torch.dtype,
+                    chunk_size: int = CHUNK) -> int:
+    code = DR_BF16 if dtype == torch.bfloat16 else DR_F32
+    return int(_lib.load().dr_workspace_bytes(KINDS[kind], B, T, H, Dk, Dv, chunk_size, code))
+
+
+def record_bytes(Dk: int, Dv: int, dtype: torch.dtype, chunk_size: int = CHUNK) -> int:
+    code = DR_BF16 if dtype == torch.bfloat16 else DR_F32
+    return int(_lib.load().dr_record_bytes(Dk, Dv, chunk_size, code))
+
+
+def alloc_workspace(kind, q: torch.Tensor, v: torch.Tensor, chunk_size: int = CHUNK) -> torch.Tensor:
+    B, T, H, Dk = q.shape
+    n = workspace_bytes(kind, B, T, H, Dk, v.shape[-1], q.dtype, chunk_size)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+
+
+def _forward(kind: str, q, k, v, g, beta, h0, output_final_state, chunk_size, workspace, flags,
+             stream) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    lib = _lib.load()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    _need(q, "q"); _need(k, "k", dt, q.shape); _need(v, "v", dt, (B, T, H, Dv))
+    gshape = (B, T, H, Dk) if kind == "kda" else (B, T, H)
+    _need(g, "g", torch.float32, gshape)
+    if kind != "decay_la":
+        if beta is None:
+            raise DeltaRuleError("beta is required")
+        _need(beta, "beta", torch.float32, (B, T, H))
+    _need(h0, "h0", torch.float32, (B, H, Dk, Dv))
+    o = torch.empty(B, T, H, Dv, dtype=dt, device=q.device)
+    hT = torch.empty(B, H, Dk, Dv, dtype=torch.float32, device=q.device) if output_final_state else None
+    if workspace is None:
+        workspace = alloc_workspace(kind, q, v, chunk_size)
+    _need(workspace, "workspace", torch.uint8)
+    if flags is not None:
+        _need(flags, "flags", torch.int32, (1,))
+    code = _dtype_code(q)
+    common = (B, T, H, Dk, Dv, chunk_size, code, _ptr(workspace), workspace.numel())
+    s = _stream(stream)
+    if kind == "kda":
+        st = lib.kda_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT),
+                         *common, _ptr(flags), s)
+    elif kind == "gdn":
+        st = lib.gdn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT),
+                         *common, _ptr(flags), s)
+    else:
+        st = lib.decay_la_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h0), _ptr(o), _ptr(hT), *common, s)
+    _check(st, f"{kind}_fwd")
+    return o, hT
+
+
+def kda_fwd(q, k, v, g, beta, h0=None, output_final_state=True, chunk_size=CHUNK, workspace=None,
+            flags=None, stream=None):
+    """KDA forward.  q, k [B,T,H,Dk], v [B,T,H,Dv] (bf16 or fp32); g [B,T,H,Dk]
+    fp32 (ln a); beta [B,T,H] fp32; h0 [B,H,Dk,Dv] fp32 or None.
+    Returns (o [B,T,H,Dv], hT [B,H,Dk,Dv] fp32 or None)."""
+    return _forward("kda", q, k, v, g, beta, h0, output_final_state, chunk_size, workspace, flags, stream)
+
+
+def gdn_fwd(q, k, v, g, beta, h0=None, output_final_state=True, chunk_size=CHUNK, workspace=None,
+            flags=None, stream=None):
+    """Gated DeltaNet forward: as kda_fwd with g [B,T,H]."""
+    return _forward("gdn", q, k, v, g, beta, h0, output_final_state, chunk_size, workspace, flags, stream)
+
+
+def decay_la_fwd(q, k, v, g, h0=None, output_final_state=True, chunk_size=CHUNK, workspace=None,
+                 stream=None):
+    """Scalar-decay linear attention (no delta term): g [B,T,H], no beta."""
+    return _forward("decay_la", q, k, v, g, None, h0, output_final_state, chunk_size, workspace, None,
+                    stream)
+
+
+FORWARDS = {"kda": kda_fwd, "gdn": gdn_fwd, "decay_la": decay_la_fwd}
+
+
+def forward(kind: str, q, k, v, g, beta=None, h0=None, **kw):
+    if kind == "decay_la":
+        return decay_la_fwd(q, k, v, g, h0, **kw)
+    return FORWARDS[kind](q, k, v, g, beta, h0, **kw)
+
+
+# ---- individual steps ------------------------------------------------------
+
+def chunk_cumsum(g: torch.Tensor, chunk_size: int = CHUNK, stream=None) -> torch.Tensor:
+    """Step a1: chunk-local inclusive cumsum of g along T, in log2 units.
+    g: [B,T,H,D] or [B,T,H] fp32."""
+    _need(g, "g", torch.float32)
+    B, T, H = g.shape[:3]
+    D = g.shape[3] if g.dim() == 4 else 1
+    out = torch.empty_like(g)
+    _check(_lib.load().dr_chunk_cumsum(_ptr(g), _ptr(out), B, T, H, D, chunk_size, _stream(stream)),
+           "dr_chunk_cumsum")
+    return out
+
+
+def kda_prep(q, k, gamma, chunk_size: int = CHUNK, flags=None, stream=None):
+    """Step a2: (qp, kp, km, kbar, phi) from q, k and gamma (step a1 output)."""
+    _need(q, "q"); _need(k, "k", q.dtype, q.shape); _need(gamma, "gamma", torch.float32, q.shape)
+    B, T, H, Dk = q.shape
+    NT = (T + chunk_size - 1) // chunk_size
+    qp, kp, km, kbar = (torch.empty_like(q) for _ in range(4))
+    phi = torch.empty(B, NT, H, Dk, dtype=torch.float32, device=q.device)
+    _check(_lib.load().dr_kda_prep(_ptr(q), _ptr(k), _ptr(gamma), _ptr(qp), _ptr(kp), _ptr(km), _ptr(kbar),
+                                   _ptr(phi), B, T, H, Dk, chunk_size, _dtype_code(q), _ptr(flags),
+                                   _stream(stream)), "dr_kda_prep")
+    return qp, kp, km, kbar, phi
+
+
+def intra(kind: str, q, k, v, g, beta=None, chunk_size: int = CHUNK, workspace=None, flags=None,
+          stream=None) -> torch.Tensor:
+    """K1 (steps a1-a3 fused): fills and returns the chunk-record workspace."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if workspace is None:
+        workspace = alloc_workspace(kind, q, v, chunk_size)
+    _check(_lib.load().dr_intra(KINDS[kind], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), B, T, H, Dk,
+                                Dv, chunk_size, _dtype_code(q), _ptr(workspace), workspace.numel(),
+                                _ptr(flags), _stream(stream)), "dr_intra")
+    return workspace
+
+
+def inter(kind: str, workspace, B, T, H, Dk, Dv, dtype, h0=None, out=None, hT=None,
+          chunk_size: int = CHUNK, stream=None):
+    """K2 (steps a4-a5 fused): state pass + output from a filled workspace."""
+    dev = workspace.device
+    if out is None:
+        out = torch.empty(B, T, H, Dv, dtype=dtype, device=dev)
+    code = DR_BF16 if dtype == torch.bfloat16 else DR_F32
+    _check(_lib.load().dr_inter(KINDS[kind], _ptr(h0), _ptr(out), _ptr(hT), B, T, H, Dk, Dv, chunk_size,
+                                code, _ptr(workspace), workspace.numel(), _stream(stream)), "dr_inter")
+    return out, hT
+
+
+def unpack_records(workspace: torch.Tensor, B: int, T: int, H: int, Dk: int, Dv: int,
+                   dtype: torch.dtype, chunk_size: int = CHUNK) -> dict:
+    """View the K1 records as named tensors (layout of include/deltarule.h,
+    dr_intra): W [B,H,NT,C,Dk], Qt [..,C,Dk], KbT [..,Dk,C], Aqk [..,C,C],
+    UT [..,Dv,C], phi [..,Dk] (fp32)."""
+    C = chunk_size
+    NT = (T + C - 1) // C
+    rb = record_bytes(Dk, Dv, dtype, C)
+    esz = torch.tensor([], dtype=dtype).element_size()
+    recs = workspace[: B * H * NT * rb].view(B, H, NT, rb)
+    sizes = [("W", C * Dk, (C, Dk)), ("Qt", C * Dk, (C, Dk)), ("KbT", Dk * C, (Dk, C)),
+             ("Aqk", C * C, (C, C)), ("UT", Dv * C, (Dv, C))]
+    out, off = {}, 0
+    for name, n, shp in sizes:
+        out[name] = recs[..., off * esz:(off + n) * esz].contiguous().view(dtype).view(B, H, NT, *shp)
+        off += n
+    pb = off * esz
+    out["phi"] = recs[..., pb:pb + Dk * 4].contiguous().view(torch.float32).view(B, H, NT, Dk)
+    return out

@@ -1,0 +1,194 @@
+/*
+ * deltarule.h -- C ABI of the chunkwise gated-delta-rule forward for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation (paper orientation, S in R^{dv x dk}):
+ *     S_t = S_{t-1} Diag(a_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = S_t q_t,                      a_t = exp(g_t)
+ * as defined by the page "TileLang 实战：KDA 从零到一–Kimi Delta Attention"
+ * (opening equation and section 3.1).  Its special cases:
+ *   - gdn_fwd: one scalar gate per token and head (Gated DeltaNet; page
+ *     "Gated DeltaNet", section "DeltaNet 与 Gated Delta Rule");
+ *   - decay_la_fwd: no delta term, S_t = a_t S_{t-1} + v_t k_t^T (page
+ *     "TileLang 实战：KDA 从零到一--标量衰减", section 1.1; RetNet /
+ *     Lightning-style decay on the page "07 · linear 路线（二）：衰减机制的演进",
+ *     sections 1-2).
+ * There is no output scale: callers pre-scale q if they want one.
+ *
+ * Conventions shared by every entry point
+ *   Pointers: all tensor pointers are DEVICE pointers owned by the caller.
+ *     The library allocates nothing and keeps no pointer after returning.
+ *   Layout: dense, row-major, time-major [B, T, H, D] for q, k, v, o and the
+ *     per-channel gate; [B, T, H] for scalar gates and beta.  The recurrent
+ *     state h0 / hT is fp32 [B, H, Dk, Dv], i.e. the TRANSPOSE of the pages'
+ *     S (key index first), as the pages' own kernels store it ("TileLang
+ *     实战：KDA 从零到一--标量衰减", section 4.0).
+ *   Alignment: every device pointer must be 16-byte aligned.
+ *   Dtypes: q, k, v, o are DR_F32 (float) or DR_BF16 (bfloat16 bit pattern,
+ *     uint16 storage); g, beta, h0, hT are always float.
+ *   Gates: g = ln a, natural log, expected <= 0 (a in (0, 1]).  The library
+ *     does not clamp.  Per-channel gates should be lower-bounded (the KDA
+ *     page, section 2: a >= 0.9 keeps 2^(-gamma) small); the range is
+ *     reported through `flags`, see DR_FLAG_*.
+ *   Shapes: B, H >= 1, T >= 0 (T = 0 copies h0 to hT, or zeros it),
+ *     Dk == Dv in {64, 128}, C == 64.  T need not be a multiple of C: the
+ *     last chunk is masked.
+ *   Streams: `stream` is a hipStream_t (0 = the null stream).  All work is
+ *     enqueued on it; nothing synchronises with the host.
+ *   Errors: argument problems are detected on the host and return a negative
+ *     status with nothing enqueued.  A failed launch returns DR_ERR_HIP.
+ *     No exception crosses the ABI.  All entry points are reentrant; calls
+ *     that share a workspace must not overlap.
+ */
+#ifndef DELTARULE_H
+#define DELTARULE_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DR_OK = 0,
+    DR_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, bad size or dtype   */
+    DR_ERR_UNSUPPORTED = -2,   /* valid but not built: Dk/Dv/C combination     */
+    DR_ERR_HIP = -3,           /* a HIP launch failed                          */
+    DR_ERR_WORKSPACE = -4      /* workspace pointer null or too small          */
+} dr_status;
+
+typedef enum { DR_F32 = 0, DR_BF16 = 1 } dr_dtype;
+typedef enum { DR_KIND_KDA = 0, DR_KIND_GDN = 1, DR_KIND_DECAY_LA = 2 } dr_kind;
+
+/* Gate-range flags, OR-ed into *flags (a device uint32) when flags != NULL.
+ * The caller clears the word before the call and reads it after syncing.
+ * Only the per-channel (KDA) path materialises 2^(-gamma):
+ *   DR_FLAG_KM_FP16_RANGE: some chunk has -gamma_log2 >= 16 somewhere, so
+ *     |k| * 2^(-gamma) could exceed the fp16 maximum 65504 (values are kept in
+ *     bf16/fp32 here, so results stay valid);
+ *   DR_FLAG_KM_OVERFLOW:   some chunk has -gamma_log2 >= 126: 2^(-gamma) is
+ *     near the fp32/bf16 limit and results are not trustworthy. */
+#define DR_FLAG_KM_FP16_RANGE 0x1u
+#define DR_FLAG_KM_OVERFLOW   0x2u
+
+/* Bytes of device workspace kda_fwd / gdn_fwd / decay_la_fwd need for these
+ * sizes (0 for invalid sizes).  The workspace holds one record per chunk and
+ * head (the operands the sequential state pass streams). */
+size_t dr_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, int C, int dtype);
+
+/*
+ * Full forward, KDA (per-channel gate).
+ *   q, k:  [B,T,H,Dk] (dtype);  v: [B,T,H,Dv] (dtype)
+ *   g:     [B,T,H,Dk] float, ln a
+ *   beta:  [B,T,H] float
+ *   h0:    [B,H,Dk,Dv] float, or NULL for a zero initial state
+ *   o:     [B,T,H,Dv] (dtype), written
+ *   hT:    [B,H,Dk,Dv] float, written, or NULL
+ *   workspace: device buffer of at least dr_workspace_bytes(DR_KIND_KDA, ...)
+ *   flags: device uint32 or NULL (see DR_FLAG_*)
+ * Steps (all on `stream`): chunk-local log2 cumsum of g, the separable
+ * exponent prep, the UT transform (K1, chunk-parallel), then the sequential
+ * state pass fused with the chunk output (K2).  Page sections: "TileLang
+ * 实战：KDA 从零到一–Kimi Delta Attention" sections 1.2, 3.2, 3.3; "RNN的复兴04"
+ * (DPLR) section 5.3.5.
+ */
+dr_status kda_fwd(const void* q, const void* k, const void* v, const float* g,
+                  const float* beta, const float* h0, void* o, float* hT,
+                  int B, int T, int H, int Dk, int Dv, int C, int dtype,
+                  void* workspace, size_t workspace_bytes, unsigned* flags,
+                  void* stream);
+
+/* Full forward, Gated DeltaNet: as kda_fwd but g is [B,T,H] (one scalar gate
+ * per token and head).  The decay inside a chunk uses the ratio form
+ * 2^(gamma_i - gamma_j), evaluated only where j <= i ("TileLang 实战：KDA
+ * 从零到一--标量衰减" section 2.2), so no flag is ever raised. */
+dr_status gdn_fwd(const void* q, const void* k, const void* v, const float* g,
+                  const float* beta, const float* h0, void* o, float* hT,
+                  int B, int T, int H, int Dk, int Dv, int C, int dtype,
+                  void* workspace, size_t workspace_bytes, unsigned* flags,
+                  void* stream);
+
+/* Full forward, scalar-decay linear attention without the delta term:
+ * S_t = a_t S_{t-1} + v_t k_t^T, o_t = S_t q_t; g is [B,T,H]; no beta. */
+dr_status decay_la_fwd(const void* q, const void* k, const void* v, const float* g,
+                       const float* h0, void* o, float* hT,
+                       int B, int T, int H, int Dk, int Dv, int C, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- the individual steps ---------------------------------------------- */
+
+/*
+ * Step a1: chunk-local inclusive cumsum of log gates, converted to log2 units:
+ *   gamma[b, cC + r, h, d] = log2(e) * sum_{s <= r} g[b, cC + s, h, d]
+ * restarting in every chunk of C tokens ("TileLang 实战：KDA 从零到一–Kimi Delta
+ * Attention" section 0; "07 · linear 路线（二）" section 3.5: the cumsum is local).
+ *   g, gamma: [B,T,H,D] float (D = Dk for per-channel gates, D = 1 for scalar
+ *   gates).  D in [1, 256].  gamma may not alias g.
+ */
+dr_status dr_chunk_cumsum(const float* g, float* gamma, int B, int T, int H, int D, int C,
+                          void* stream);
+
+/*
+ * Step a2: separable-exponent prep for per-channel gates ("TileLang 实战：KDA
+ * 从零到一–Kimi Delta Attention" section 1.2; "RNN的复兴04" section 5.3.4):
+ *   kp   = k * 2^gamma,        km = k * 2^(-gamma),     qp = q * 2^gamma,
+ *   kbar = k * 2^(gamma_last - gamma)  (gamma_last: last valid row of the chunk),
+ *   phi[b, c, h, d] = 2^(gamma_last)
+ *   q, k, kp, km, qp, kbar: [B,T,H,Dk] (dtype); gamma: [B,T,H,Dk] float (from
+ *   step a1); phi: [B,ceil(T/C),H,Dk] float.  Any output pointer may be NULL
+ *   to skip it.  flags: as for kda_fwd.
+ */
+dr_status dr_kda_prep(const void* q, const void* k, const float* gamma,
+                      void* qp, void* kp, void* km, void* kbar, float* phi,
+                      int B, int T, int H, int Dk, int C, int dtype, unsigned* flags,
+                      void* stream);
+
+/*
+ * K1 alone: steps a1 + a2 + a3 fused, chunk-parallel.  Fills `workspace`
+ * with one record per (b, h, chunk), record index (b*H + h)*NT + c,
+ * NT = ceil(T/C).  Record layout (elements of the I/O dtype unless noted,
+ * each block dense row-major, r/i = position in the chunk, d = key channel,
+ * e = value channel):
+ *   W    [C][Dk]   W = T diag(beta) K+   (delta kinds; unused for decay_la)
+ *   Qt   [C][Dk]   q * 2^gamma
+ *   KbT  [Dk][C]   (k * 2^(gamma_last - gamma))^T
+ *   Aqk  [C][C]    Tril_incl(Q~ K-^T)  (zero above the diagonal)
+ *   UT   [Dv][C]   U^T, U = T diag(beta) V  (decay_la: V^T)
+ *   phi  [Dk]      float, 2^(gamma_last)
+ * with T = (I + A)^-1, A = diag(beta) StrictLower(K+ K-^T) ("TileLang 实战：
+ * KDA 从零到一–Kimi Delta Attention" sections 3.2-3.3, row-beta pairing).
+ * Rows of a ragged last chunk beyond T are zero.  Record size:
+ * dr_record_bytes().  For GDN / decay_la, g is [B,T,H] and beta may be NULL
+ * for decay_la.
+ */
+dr_status dr_intra(int kind, const void* q, const void* k, const void* v, const float* g,
+                   const float* beta, int B, int T, int H, int Dk, int Dv, int C, int dtype,
+                   void* workspace, size_t workspace_bytes, unsigned* flags, void* stream);
+
+/*
+ * K2 alone: steps a4 + a5 fused.  For each (b, h), in chunk order:
+ *   Vnew = U - W S  (decay_la: Vnew = V),
+ *   O    = Qt S + Aqk Vnew,
+ *   S   <- Diag(phi) S + KbT Vnew
+ * starting from S = h0 (or 0) and writing o and hT ("RNN的复兴04" section
+ * 5.3.5; "TileLang 实战：KDA 从零到一–Kimi Delta Attention" section 3.2).
+ * Reads the records written by dr_intra with the same arguments.
+ */
+dr_status dr_inter(int kind, const float* h0, void* o, float* hT,
+                   int B, int T, int H, int Dk, int Dv, int C, int dtype,
+                   const void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of one workspace record (0 for unsupported sizes). */
+size_t dr_record_bytes(int Dk, int Dv, int C, int dtype);
+
+/* Human-readable text for a status code (static storage). */
+const char* dr_status_string(int status);
+
+/* ABI version of this library: 1. */
+int dr_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DELTARULE_H */

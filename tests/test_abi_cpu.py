@@ -1,0 +1,103 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol,
+sizes its workspace as documented and rejects bad arguments on the host
+before any GPU call (no compute call is made here)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "deltarule.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from delta_rule_rnn_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from delta_rule_rnn_amd.build import build_library
+        build_library()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+def test_header_and_binding_agree():
+    from delta_rule_rnn_amd import _lib
+    decl = declared_functions()
+    assert decl == sorted(_lib.SIGNATURES), (decl, sorted(_lib.SIGNATURES))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.dr_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for s in (0, -1, -2, -3, -4):
+        assert lib.dr_status_string(s)
+    assert lib.dr_status_string(7) == b"unknown status"
+
+
+def test_workspace_sizes(lib):
+    # one record per (b, h, chunk); bf16 D=128 record: (3*64*128 + 64*64 + 128*64)*2 + 128*4
+    rec = lib.dr_record_bytes(128, 128, 64, 1)
+    assert rec == ((3 * 64 * 128 + 64 * 64 + 128 * 64) * 2 + 128 * 4 + 255) // 256 * 256
+    assert lib.dr_workspace_bytes(0, 2, 130, 3, 128, 128, 64, 1) == 2 * 3 * 3 * rec
+    assert lib.dr_workspace_bytes(1, 1, 0, 1, 64, 64, 64, 0) == 0
+    assert lib.dr_record_bytes(96, 96, 64, 1) == 0
+    assert lib.dr_record_bytes(128, 64, 64, 1) == 0
+    assert lib.dr_record_bytes(128, 128, 32, 1) == 0
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(B=0), -1), (dict(H=0), -1), (dict(T=-1), -1), (dict(dtype=5), -1),
+    (dict(Dk=96, Dv=96), -2), (dict(Dk=128, Dv=64), -2), (dict(C=32), -2),
+    (dict(q=None), -1), (dict(beta=None), -1), (dict(q=FAKE + 4), -1), (dict(o=FAKE + 8), -1),
+    (dict(ws=None), -4), (dict(ws_bytes=100), -4),
+])
+def test_kda_fwd_rejects(lib, case, expect):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=None, o=FAKE, hT=None, B=1, T=64, H=1,
+             Dk=64, Dv=64, C=64, dtype=1, ws=FAKE, ws_bytes=1 << 30, flags=None, stream=None)
+    a.update(case)
+    st = lib.kda_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["o"], a["hT"], a["B"],
+                     a["T"], a["H"], a["Dk"], a["Dv"], a["C"], a["dtype"], a["ws"], a["ws_bytes"],
+                     a["flags"], a["stream"])
+    assert st == expect
+
+
+def test_other_entry_points_reject(lib):
+    assert lib.decay_la_fwd(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 1, 64, 1, 64, 64, 64, 1, None, 0,
+                            None) == -4
+    assert lib.gdn_fwd(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None, 1, 64, 1, 64, 64, 64, 1, FAKE,
+                       1 << 30, None, None) == -1
+    assert lib.dr_chunk_cumsum(FAKE, FAKE, 1, 64, 1, 0, 64, None) == -1
+    assert lib.dr_chunk_cumsum(FAKE, FAKE, 1, 64, 1, 4, 32, None) == -2
+    assert lib.dr_chunk_cumsum(FAKE, FAKE, 1, 64, 1, 4, 64, None) == -1   # aliasing
+    assert lib.dr_kda_prep(FAKE, FAKE, FAKE, None, None, None, None, None, 1, 64, 1, 96, 64, 1, None,
+                           None) == -2
+    assert lib.dr_intra(3, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 1, 64, 64, 64, 1, FAKE, 1 << 30, None,
+                        None) == -1
+    assert lib.dr_inter(0, None, FAKE, None, 1, 64, 1, 64, 64, 64, 1, FAKE, 10, None) == -4
+    # nothing to do: T = 0 and no final state requested
+    assert lib.kda_fwd(None, None, None, None, None, None, None, None, 1, 0, 1, 64, 64, 64, 1, None, 0,
+                       None, None) == 0
+
+
+def test_python_binding_requires_library(tmp_path, monkeypatch):
+    """The product path fails loudly (no CPU fallback) when the library is missing."""
+    from delta_rule_rnn_amd import _lib
+    monkeypatch.setattr(_lib, "_LIB", None)
+    with pytest.raises(_lib.LibraryMissing):
+        _lib.load(str(tmp_path / "nope.so"))
