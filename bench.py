@@ -74,10 +74,24 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="kda_bf16_long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=16384,
+    ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens of the workload the CPU oracle is timed on")
     ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes (3 times): the "
+                         "reference for scaling the HBM byte counters of a profile")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only (the forward is a per-(batch, head) "

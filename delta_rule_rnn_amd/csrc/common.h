@@ -82,6 +82,23 @@ __device__ __forceinline__ float frag_get(const Frag<float>& f, int j) { return 
 __device__ __forceinline__ void frag_set(Frag<bf16>& f, int j, float x) { f.v[j] = (bf16)x; }
 __device__ __forceinline__ void frag_set(Frag<float>& f, int j, float x) { f.v[j] = x; }
 
+// Two adjacent elements as one 4-byte (bf16) or 8-byte (fp32) access.
+template <typename T> struct Pair;
+template <> struct Pair<bf16> {
+    typedef bf16x2 type;
+    __device__ static type zero() { type z; z[0] = (bf16)0.f; z[1] = (bf16)0.f; return z; }
+    __device__ static type make(float a, float b) { type z; z[0] = (bf16)a; z[1] = (bf16)b; return z; }
+    __device__ static float lo(type x) { return (float)x[0]; }
+    __device__ static float hi(type x) { return (float)x[1]; }
+};
+template <> struct Pair<float> {
+    typedef float2 type;
+    __device__ static type zero() { return make_float2(0.f, 0.f); }
+    __device__ static type make(float a, float b) { return make_float2(a, b); }
+    __device__ static float lo(type x) { return x.x; }
+    __device__ static float hi(type x) { return x.y; }
+};
+
 // Four contiguous elements (8-byte aligned for bf16).
 __device__ __forceinline__ void ld4(const bf16* p, float* out) {
     const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
@@ -98,6 +115,15 @@ __device__ __forceinline__ void st4(bf16* p, const float* in) {
 }
 __device__ __forceinline__ void st4(float* p, const float* in) {
     *reinterpret_cast<float4*>(p) = make_float4(in[0], in[1], in[2], in[3]);
+}
+
+// Workgroup barrier that orders LDS traffic only: waits for this wave's LDS
+// operations, then meets the other waves.  Unlike __syncthreads() it does not
+// wait for outstanding global loads and stores, so prefetches and record
+// stores stay in flight across it.  Every barrier in these kernels exchanges
+// LDS data only; global results are consumed by later kernels.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Row of a 32-row block held by row r (0..15) of its first (half = 0) or

@@ -2,6 +2,7 @@
 // argument validation, workspace sizing and kernel dispatch for gfx950.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "../../include/deltarule.h"
 #include "common.h"
@@ -12,8 +13,6 @@
 namespace {
 
 using dr::bf16;
-
-constexpr int kNTN = 2;   // value columns per state-pass workgroup = 16 * kNTN
 
 bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -56,15 +55,57 @@ dr_status launch_intra(const void* q, const void* k, const void* v, const float*
     return check_launch();
 }
 
+// Value columns per state-pass workgroup (16 * ntn).  Fewer columns per
+// workgroup means more workgroups: with few (b, h) chains the narrow split
+// fills the 256 CUs; with many chains wider slices cut the repeated reads of
+// the shared W / Q~ / Kbar / Aqk operands.  DR_INTER_NTN (1, 2 or 4)
+// overrides the choice for tuning.
+int pick_ntn(int chains, int D) {
+    if (const char* e = getenv("DR_INTER_NTN")) {
+        const int v = atoi(e);
+        if ((v == 1 || v == 2 || v == 4) && 16 * v <= D) return v;
+    }
+    const int cols = D / 16;                         // 16-column slices per chain
+    if (chains * cols <= 512) return 1;              // <= 512 workgroups: narrowest
+    if (chains * cols / 2 <= 512 || D == 64) return 2;
+    return 4;
+}
+
+int pick_nbuf() {
+    if (const char* e = getenv("DR_INTER_NBUF")) {
+        const int v = atoi(e);
+        if (v == 2 || v == 3) return v;
+    }
+    return 2;
+}
+
+template <int KIND, typename E, int D, int NTN, int NBUF>
+dr_status launch_inter_n(const float* h0, void* o, float* hT, int B, int T, int H, const void* ws,
+                         hipStream_t st) {
+    const int NT = ceil_div(T, dr::kChunk);
+    constexpr int NV = D / (16 * NTN);
+    dim3 grid(B * H * NV);
+    hipLaunchKernelGGL((dr::inter_kernel<KIND, E, D, D, NTN, NBUF>), grid, dim3(dr::kThreads), 0, st,
+                       static_cast<const uint8_t*>(ws), h0, static_cast<E*>(o), hT, T, H, NT);
+    return check_launch();
+}
+
 template <int KIND, typename E, int D>
 dr_status launch_inter(const float* h0, void* o, float* hT, int B, int T, int H, const void* ws,
                        hipStream_t st) {
-    const int NT = ceil_div(T, dr::kChunk);
-    constexpr int NV = D / (16 * kNTN);
-    dim3 grid(B * H * NV);
-    hipLaunchKernelGGL((dr::inter_kernel<KIND, E, D, D, kNTN>), grid, dim3(dr::kThreads), 0, st,
-                       static_cast<const uint8_t*>(ws), h0, static_cast<E*>(o), hT, T, H, NT);
-    return check_launch();
+    const int ntn = pick_ntn(B * H, D);
+    // fp32 operands are twice as large: one chunk of prefetch only
+    const int nbuf = sizeof(E) == 4 ? 2 : pick_nbuf();
+    if constexpr (sizeof(E) == 2) {
+        if (nbuf == 3) {
+            if (ntn == 1) return launch_inter_n<KIND, E, D, 1, 3>(h0, o, hT, B, T, H, ws, st);
+            if (ntn == 2) return launch_inter_n<KIND, E, D, 2, 3>(h0, o, hT, B, T, H, ws, st);
+            // 64 columns with three buffers does not fit in registers: two buffers
+        }
+    }
+    if (ntn == 1) return launch_inter_n<KIND, E, D, 1, 2>(h0, o, hT, B, T, H, ws, st);
+    if (ntn == 2) return launch_inter_n<KIND, E, D, 2, 2>(h0, o, hT, B, T, H, ws, st);
+    return launch_inter_n<KIND, E, D, 4, 2>(h0, o, hT, B, T, H, ws, st);
 }
 
 template <int KIND>

@@ -18,14 +18,16 @@
 // columns (value columns evolve independently, [KDA] 3.4).  Its 4 waves split
 // the rows: wave w produces 16 positions of Vnew and O (rows 32*(w/2) +
 // prow(w%2, r)) and 32 key rows of S (rows 32w..32w+31).  Two LDS exchanges
-// per chunk hand Vnew and S to every wave as natural B fragments.  All
-// operands of the next chunk are prefetched into registers while the current
-// chunk computes.
+// per chunk hand Vnew and S to every wave as natural B fragments.  The
+// operands of the next NBUF-1 chunks are prefetched into registers while the
+// current chunk computes.
 //
 // Block mapping: the NV = Dv/DVS workgroups of a chain read the same W, Q~,
 // Kbar, Aqk; consecutive logical ids are placed on the same XCD (hardware
 // dispatches workgroup i to XCD i % 8) so they share that XCD's L2.
 #pragma once
+
+#include <type_traits>
 
 #include "common.h"
 
@@ -59,10 +61,11 @@ __device__ __forceinline__ void inter_load(InterOps<T, DK, NTN>& op, const uint8
         if constexpr (DELTA) op.w[kb] = ld_frag(base + R::W + p * DK + 32 * kb + 8 * grp);
         op.qt[kb] = ld_frag(base + R::QT + p * DK + 32 * kb + 8 * grp);
     }
+    // both key blocks: the record holds zeros above the diagonal, so the
+    // block past this wave's positions contributes nothing
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-        if (kb <= kbP) op.aqk[kb] = ld_frag(base + R::AQK + p * C + 32 * kb + 8 * grp);
-    if (wave < NKB) {
+    for (int kb = 0; kb < 2; ++kb) op.aqk[kb] = ld_frag(base + R::AQK + p * C + 32 * kb + 8 * grp);
+    if (NKB >= 4 || wave < NKB) {
         const float* phi = reinterpret_cast<const float*>(recb + R::PHI_BYTE);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -77,7 +80,7 @@ __device__ __forceinline__ void inter_load(InterOps<T, DK, NTN>& op, const uint8
         ld4(base + R::UT + (size_t)(dv0 + 16 * n + r16) * C + 32 * kbP + 8 * grp + 4 * halfP, op.u[n]);
 }
 
-template <int KIND, typename T, int DK, int DV, int NTN>
+template <int KIND, typename T, int DK, int DV, int NTN, int NBUF>
 __global__ __launch_bounds__(kThreads) void inter_kernel(const uint8_t* __restrict__ ws,
                                                          const float* __restrict__ h0,
                                                          T* __restrict__ o, float* __restrict__ hT,
@@ -94,11 +97,15 @@ __global__ __launch_bounds__(kThreads) void inter_kernel(const uint8_t* __restri
     // B-fragment exchange buffers: [block][n-tile][lane][8 slots]
     __shared__ __attribute__((aligned(16))) T sS[NKB][NTN][64][8];
     __shared__ __attribute__((aligned(16))) T sV[2][NTN][64][8];
+    // per-wave output staging: 16 positions x 16*NTN columns, one row per
+    // position, so the tile leaves as 16-byte row segments
+    constexpr int LDO = 16 * NTN + 8;
+    __shared__ __attribute__((aligned(16))) T sO[4][16][LDO];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, grp = lane >> 4;
     const int kbP = wave >> 1, halfP = wave & 1;
-    const bool ownS = wave < NKB;
+    const bool ownS = NKB >= 4 || wave < NKB;   // Dk = 128: every wave owns 32 state rows
 
     const int G = gridDim.x, bid = blockIdx.x;
     const int logical = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
@@ -134,16 +141,19 @@ __global__ __launch_bounds__(kThreads) void inter_kernel(const uint8_t* __restri
         }
     };
     publish_state();
-    __syncthreads();
+    lds_barrier();
 
     const uint8_t* chain_rec = ws + ((size_t)b * H + h) * (size_t)NT * R::BYTES;
-    InterOps<T, DK, NTN> cur, nxt;
-    if (NT > 0) inter_load<KIND, T, DK, DV, NTN>(cur, chain_rec, wave, lane, dv0);
+    // output rows are H*DV elements apart; orow0 = column dv0 of token 0
+    const size_t ostride = (size_t)H * DV;
+    T* const orow0 = o + ((size_t)b * Tlen * H + h) * DV + dv0;
+    auto load = [&](InterOps<T, DK, NTN>& op, int c) {
+        inter_load<KIND, T, DK, DV, NTN>(op, chain_rec + (size_t)c * R::BYTES, wave, lane, dv0);
+    };
 
-    for (int c = 0; c < NT; ++c) {
-        if (c + 1 < NT)
-            inter_load<KIND, T, DK, DV, NTN>(nxt, chain_rec + (size_t)(c + 1) * R::BYTES, wave, lane, dv0);
-
+    // One chunk step with the operands in `cur` (loaded earlier).
+    auto step = [&](int c, const InterOps<T, DK, NTN>& cur, auto guard_tag) {
+        constexpr bool GUARD = decltype(guard_tag)::value;
         // entry-state fragments
         Frag<T> fS[NKB][NTN];
 #pragma unroll
@@ -172,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void inter_kernel(const uint8_t* __restri
             for (int i = 0; i < 4; ++i) vn[i] = DELTA ? cur.u[n][i] - P[n][i] : cur.u[n][i];
             st4(&sV[kbP][n][lane][4 * halfP], vn);
         }
-        __syncthreads();
+        lds_barrier();
 
         Frag<T> fV[2][NTN];
 #pragma unroll
@@ -180,24 +190,28 @@ __global__ __launch_bounds__(kThreads) void inter_kernel(const uint8_t* __restri
 #pragma unroll
             for (int n = 0; n < NTN; ++n) fV[kb][n] = ld_frag(&sV[kb][n][lane][0]);
 
-        // intra-chunk term (causal: key blocks up to this wave's block)
+        // intra-chunk term (Aqk is zero past the diagonal)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            if (kb > kbP) break;
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int n = 0; n < NTN; ++n) mma(O[n], cur.aqk[kb], fV[kb][n]);
-        }
-        // store O
+        // store O.  The accumulator gives this lane 4 rows of one column; the
+        // tile goes through this wave's own LDS staging area (no other wave
+        // touches it, so no barrier) and leaves as 16-byte row segments.
         {
-            const int pbase = c * C + 32 * kbP + 8 * grp + 4 * halfP;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = pbase + i;
-                if (t < Tlen) {
-                    T* dst = o + (((size_t)b * Tlen + t) * H + h) * DV + dv0 + r16;
+            for (int n = 0; n < NTN; ++n)
 #pragma unroll
-                    for (int n = 0; n < NTN; ++n) dst[16 * n] = from_f<T>(O[n][i]);
-                }
+                for (int i = 0; i < 4; ++i) sO[wave][4 * grp + i][16 * n + r16] = from_f<T>(O[n][i]);
+            constexpr int SEGS = 16 * NTN / 8;          // 8-element segments per row
+#pragma unroll
+            for (int it = lane; it < 16 * SEGS; it += 64) {
+                const int rr = it / SEGS, sg = it % SEGS;
+                // staging row rr holds position 32*kbP + prow(halfP, rr)
+                const int pos = 32 * kbP + prow(halfP, rr);
+                const Frag<T> f = ld_frag(&sO[wave][rr][8 * sg]);
+                if (!GUARD || c * C + pos < Tlen)
+                    st_frag(orow0 + ((size_t)c * C + pos) * ostride + 8 * sg, f);
             }
         }
         // state update: decay first, then accumulate
@@ -213,8 +227,59 @@ __global__ __launch_bounds__(kThreads) void inter_kernel(const uint8_t* __restri
                 }
         }
         publish_state();
-        __syncthreads();
-        if (c + 1 < NT) cur = nxt;
+        lds_barrier();
+    };
+
+    // Operands are loaded NBUF-1 chunks ahead into a ring of register buffers.  Every load and
+    // store inside the steady-state loop is unconditional (prefetch indices are
+    // clamped to the last chunk, only the last chunk guards its output rows),
+    // so the compiler can keep the prefetches in flight across steps instead of
+    // draining the memory counter at control-flow joins.
+    using Full = std::integral_constant<bool, false>;
+    using Tail = std::integral_constant<bool, true>;
+    const int last = NT - 1;
+    auto cl = [&](int c) { return c < last ? c : last; };
+    static_assert(NBUF == 2 || NBUF == 3, "prefetch depth");
+    if constexpr (NBUF == 3) {
+        InterOps<T, DK, NTN> b0, b1, b2;
+        int c = 0;
+        if (NT > 0) {
+            load(b0, 0);
+            load(b1, cl(1));
+            for (; c + 3 <= last; c += 3) {
+                load(b2, cl(c + 2)); step(c, b0, Full{});
+                load(b0, cl(c + 3)); step(c + 1, b1, Full{});
+                load(b1, cl(c + 4)); step(c + 2, b2, Full{});
+            }
+            if (c == last) {
+                step(c, b0, Tail{});
+            } else if (c + 1 == last) {
+                step(c, b0, Full{});
+                step(c + 1, b1, Tail{});
+            } else {
+                load(b2, c + 2);
+                step(c, b0, Full{});
+                step(c + 1, b1, Full{});
+                step(c + 2, b2, Tail{});
+            }
+        }
+    } else {
+        InterOps<T, DK, NTN> b0, b1;
+        int c = 0;
+        if (NT > 0) {
+            load(b0, 0);
+            for (; c + 2 <= last; c += 2) {
+                load(b1, cl(c + 1)); step(c, b0, Full{});
+                load(b0, cl(c + 2)); step(c + 1, b1, Full{});
+            }
+            if (c == last) {
+                step(c, b0, Tail{});
+            } else {
+                load(b1, c + 1);
+                step(c, b0, Full{});
+                step(c + 1, b1, Tail{});
+            }
+        }
     }
 
     // ---- final state -----------------------------------------------------

@@ -123,11 +123,29 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(
     T* rU = reinterpret_cast<T*>(recb) + R::UT;
     float* rPhi = reinterpret_cast<float*>(recb + R::PHI_BYTE);
 
-    // ---- P0: beta -------------------------------------------------------
+    // ---- P0: every global load of the chunk is issued up front ------------
+    // thread layout: channel pair cp (2 key/value channels), position group qg
+    const int cp = tid % NCP, qg = tid / NCP, ch0 = 2 * cp, p0 = qg * PL;
+    using T2 = typename Pair<T>::type;
+    T2 kv[PL], qv[PL], vv[PL];
+    float2 gv[PERCH ? PL : 1];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+        const int p = p0 + i;
+        if (p < nvalid) {
+            const size_t off = trow(p) * DK + ch0;
+            kv[i] = *reinterpret_cast<const T2*>(k + off);
+            qv[i] = *reinterpret_cast<const T2*>(q + off);
+            vv[i] = *reinterpret_cast<const T2*>(v + trow(p) * DV + ch0);
+            if constexpr (PERCH) gv[i] = *reinterpret_cast<const float2*>(g + off);
+        } else {
+            kv[i] = Pair<T>::zero(); qv[i] = Pair<T>::zero(); vv[i] = Pair<T>::zero();
+            if constexpr (PERCH) gv[i] = make_float2(0.f, 0.f);
+        }
+    }
     if (tid < C) sBeta[tid] = (DELTA && tid < nvalid) ? beta[trow(tid)] : 0.f;
 
     // ---- P1: a1 (gamma) + a2 (prep) -------------------------------------
-    const int cp = tid % NCP, qg = tid / NCP, ch0 = 2 * cp, p0 = qg * PL;
     float gam[PL][2];
     float glast[2];
     if constexpr (PERCH) {
@@ -135,15 +153,12 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(
         float s0 = 0.f, s1 = 0.f;
 #pragma unroll
         for (int i = 0; i < PL; ++i) {
-            const int p = p0 + i;
-            float2 gv = make_float2(0.f, 0.f);
-            if (p < nvalid) gv = *reinterpret_cast<const float2*>(g + trow(p) * DK + ch0);
-            s0 += gv.x; s1 += gv.y;
+            s0 += gv[i].x; s1 += gv[i].y;
             gam[i][0] = s0; gam[i][1] = s1;
         }
         sTot[qg * DK + ch0] = s0;
         sTot[qg * DK + ch0 + 1] = s1;
-        __syncthreads();
+        lds_barrier();
         float pre0 = 0.f, pre1 = 0.f, all0 = 0.f, all1 = 0.f;
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
@@ -172,46 +187,42 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(
             }
             sGam[lane] = x * kLog2e;
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int i = 0; i < PL; ++i) gam[i][0] = gam[i][1] = sGam[p0 + i];
         glast[0] = glast[1] = sGam[C - 1];
     }
 
     {
+        const float phi0 = __builtin_amdgcn_exp2f(glast[0]);
+        const float phi1 = __builtin_amdgcn_exp2f(glast[1]);
         float kb[2][PL];
         float mxneg = 0.f;
 #pragma unroll
         for (int i = 0; i < PL; ++i) {
             const int p = p0 + i;
-            float k0 = 0.f, k1 = 0.f, q0 = 0.f, q1 = 0.f;
-            if (p < nvalid) {
-                const size_t off = trow(p) * DK + ch0;
-                k0 = to_f(k[off]); k1 = to_f(k[off + 1]);
-                q0 = to_f(q[off]); q1 = to_f(q[off + 1]);
-            }
+            const float k0 = Pair<T>::lo(kv[i]), k1 = Pair<T>::hi(kv[i]);
+            const float q0 = Pair<T>::lo(qv[i]), q1 = Pair<T>::hi(qv[i]);
             const float e0 = __builtin_amdgcn_exp2f(gam[i][0]);
             const float e1 = __builtin_amdgcn_exp2f(gam[i][1]);
             if constexpr (PERCH) {
                 const float ei0 = __builtin_amdgcn_exp2f(-gam[i][0]);
                 const float ei1 = __builtin_amdgcn_exp2f(-gam[i][1]);
                 mxneg = fmaxf(mxneg, fmaxf(-gam[i][0], -gam[i][1]));
-                sKp[p * LDK + ch0] = from_f<T>(k0 * e0);
-                sKp[p * LDK + ch0 + 1] = from_f<T>(k1 * e1);
-                sKm[p * LDK + ch0] = from_f<T>(k0 * ei0);
-                sKm[p * LDK + ch0 + 1] = from_f<T>(k1 * ei1);
-                sQp[p * LDK + ch0] = from_f<T>(q0 * e0);
-                sQp[p * LDK + ch0 + 1] = from_f<T>(q1 * e1);
+                *reinterpret_cast<T2*>(sKp + p * LDK + ch0) = Pair<T>::make(k0 * e0, k1 * e1);
+                *reinterpret_cast<T2*>(sKm + p * LDK + ch0) = Pair<T>::make(k0 * ei0, k1 * ei1);
+                *reinterpret_cast<T2*>(sQp + p * LDK + ch0) = Pair<T>::make(q0 * e0, q1 * e1);
+                // Kbar = k 2^(gamma_last - gamma) = (k 2^-gamma) 2^gamma_last
+                kb[0][i] = k0 * (ei0 * phi0);
+                kb[1][i] = k1 * (ei1 * phi1);
             } else {
-                sKp[p * LDK + ch0] = from_f<T>(k0);
-                sKp[p * LDK + ch0 + 1] = from_f<T>(k1);
-                sQp[p * LDK + ch0] = from_f<T>(q0);
-                sQp[p * LDK + ch0 + 1] = from_f<T>(q1);
+                *reinterpret_cast<T2*>(sKp + p * LDK + ch0) = kv[i];
+                *reinterpret_cast<T2*>(sQp + p * LDK + ch0) = qv[i];
+                const float r = __builtin_amdgcn_exp2f(glast[0] - gam[i][0]);   // <= 1
+                kb[0][i] = k0 * r;
+                kb[1][i] = k1 * r;
             }
-            rQ[p * DK + ch0] = from_f<T>(q0 * e0);
-            rQ[p * DK + ch0 + 1] = from_f<T>(q1 * e1);
-            kb[0][i] = k0 * __builtin_amdgcn_exp2f(glast[0] - gam[i][0]);
-            kb[1][i] = k1 * __builtin_amdgcn_exp2f(glast[1] - gam[i][1]);
+            *reinterpret_cast<T2*>(rQ + p * DK + ch0) = Pair<T>::make(q0 * e0, q1 * e1);
         }
         // Kbar^T: PL consecutive positions per channel
 #pragma unroll
@@ -221,8 +232,8 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(
             for (int i = 0; i < PL; i += 4) st4(dst + i, &kb[cc][i]);
         }
         if (qg == 0) {
-            rPhi[ch0] = __builtin_amdgcn_exp2f(glast[0]);
-            rPhi[ch0 + 1] = __builtin_amdgcn_exp2f(glast[1]);
+            rPhi[ch0] = phi0;
+            rPhi[ch0 + 1] = phi1;
         }
         if constexpr (PERCH) {
             if (flags) {
@@ -234,26 +245,18 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(
         }
         if constexpr (!DELTA) {
             // decay_la: the state pass reads V^T from the U^T slot
-            float vv[2][PL];
-#pragma unroll
-            for (int i = 0; i < PL; ++i) {
-                const int p = p0 + i;
-                float v0 = 0.f, v1 = 0.f;
-                if (p < nvalid) {
-                    const size_t off = trow(p) * DV + ch0;
-                    v0 = to_f(v[off]); v1 = to_f(v[off + 1]);
-                }
-                vv[0][i] = v0; vv[1][i] = v1;
-            }
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
+                float vt[PL];
+#pragma unroll
+                for (int i = 0; i < PL; ++i) vt[i] = cc ? Pair<T>::hi(vv[i]) : Pair<T>::lo(vv[i]);
                 T* dst = rU + (size_t)(ch0 + cc) * C + p0;
 #pragma unroll
-                for (int i = 0; i < PL; i += 4) st4(dst + i, &vv[cc][i]);
+                for (int i = 0; i < PL; i += 4) st4(dst + i, &vt[i]);
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- P2: A and Aqk on MFMA ---------------------------------------------
     {
@@ -294,7 +297,7 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(
         }
     }
     if constexpr (!DELTA) return;
-    __syncthreads();
+    lds_barrier();
 
     // ---- P3: T = (I + A)^-1 -----------------------------------------------
     if (wave == 0) {
@@ -315,25 +318,22 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) sT[(16 * blk + r) * LDF + 16 * (blk + 1) + col] = 0.f;
         }
-    } else {
-        // beta * V, transposed: sVt[e][p] = beta_p v[p][e]
-        for (int e = tid - 64; e < C * (DV / 8); e += kThreads - 64) {
-            const int p = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
-            float vv[8];
-            if (p < nvalid) {
-                const T* src = v + trow(p) * DV + c8;
+    }
+    {
+        // beta * V, transposed into sVt[e][p] (the K- region is free now):
+        // each thread writes its PL consecutive positions of 2 value channels
 #pragma unroll
-                for (int j = 0; j < 8; ++j) vv[j] = to_f(src[j]);
-            } else {
+        for (int cc = 0; cc < 2; ++cc) {
+            float vt[PL];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) vv[j] = 0.f;
-            }
-            const float bp = sBeta[p];
+            for (int i = 0; i < PL; ++i)
+                vt[i] = sBeta[p0 + i] * (cc ? Pair<T>::hi(vv[i]) : Pair<T>::lo(vv[i]));
+            T* dst = sVt + (ch0 + cc) * LDV + p0;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) sVt[(c8 + j) * LDV + p] = from_f<T>(bp * vv[j]);
+            for (int i = 0; i < PL; i += 4) st4(dst + i, &vt[i]);
         }
     }
-    __syncthreads();
+    lds_barrier();
     // off-diagonal blocks, by distance from the diagonal
 #pragma unroll
     for (int dist = 1; dist <= 3; ++dist) {
@@ -346,7 +346,7 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) sT[(16 * i + 4 * grp + e) * LDF + 16 * j + r16] = -z[e];
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     // ---- P4: [W | U] = T diag(beta) [K+ | V] --------------------------------
@@ -429,7 +429,7 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(
         }
     }
     if constexpr (sizeof(T) == 2) {
-        __syncthreads();
+        lds_barrier();
         for (int e = tid; e < C * (DK / 8); e += kThreads) {
             const int p = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
             st_frag(rW + p * DK + c8, ld_frag(sW + p * LDK + c8));
