@@ -132,18 +132,31 @@ __device__ __forceinline__ void lds_barrier() {
 // 8q+4..8q+7 (half 1).
 __device__ __forceinline__ int prow(int half, int r) { return 8 * (r >> 2) + 4 * half + (r & 3); }
 
+// Chunk position held by row r of the state pass's wave w (w = 0..3): wave w
+// owns the 16 positions of 32-block w/2 selected by prow(w%2, .).
+__device__ __forceinline__ int pw(int w, int r) { return 32 * (w >> 1) + prow(w & 1, r); }
+
 // ---------------------------------------------------------------------------
 // Chunk record: the operands the sequential pass streams, one record per
 // (b, h, chunk).  Offsets in elements of the I/O type T except phi (float).
+//
+// Every block is stored in MFMA fragment order for the state pass, so one
+// wave-wide load of 8 elements per lane reads a contiguous 64*8-element run
+// (lane l, element j; NKB = DK/32; pw() and prow() above):
+//   W, QT  [w 4][kb NKB][l 64][j 8]    = X[pw(w, l%16)][32kb + 8(l/16) + j]
+//   KBT    [w NKB][h 2][kb 2][l][j 8]  = Kbar[32kb + 8(l/16) + j][32w + prow(h, l%16)]
+//   AQK    [w 4][kb 2][l][j 8]         = Aqk[pw(w, l%16)][32kb + 8(l/16) + j]
+//   UT     [t DV/16][w 4][l][i 4]      = U[32(w/2) + 8(l/16) + 4(w%2) + i][16t + l%16]
+//   PHI    [DK] float
 // ---------------------------------------------------------------------------
 template <typename T, int DK, int DV>
 struct Rec {
     static constexpr int C = kChunk;
-    static constexpr size_t W = 0;                   // [C][DK]
-    static constexpr size_t QT = W + (size_t)C * DK; // [C][DK]
-    static constexpr size_t KBT = QT + (size_t)C * DK; // [DK][C]
-    static constexpr size_t AQK = KBT + (size_t)DK * C; // [C][C]
-    static constexpr size_t UT = AQK + (size_t)C * C;  // [DV][C]
+    static constexpr size_t W = 0;                       // C*DK
+    static constexpr size_t QT = W + (size_t)C * DK;     // C*DK
+    static constexpr size_t KBT = QT + (size_t)C * DK;   // DK*C
+    static constexpr size_t AQK = KBT + (size_t)DK * C;  // C*C
+    static constexpr size_t UT = AQK + (size_t)C * C;    // DV*C
     static constexpr size_t END = UT + (size_t)DV * C;
     static constexpr size_t PHI_BYTE = END * sizeof(T);      // [DK] float
     static constexpr size_t BYTES = ((PHI_BYTE + DK * sizeof(float)) + 255) / 256 * 256;

@@ -53,31 +53,32 @@ __device__ __forceinline__ void inter_load(InterOps<T, DK, NTN>& op, const uint8
     constexpr int NKB = DK / 32;
     constexpr bool DELTA = KIND != KIND_LA;
     const T* base = reinterpret_cast<const T*>(recb);
-    const int r16 = lane & 15, grp = lane >> 4;
-    const int kbP = wave >> 1, halfP = wave & 1;
-    const int p = 32 * kbP + prow(halfP, r16);
+    // all blocks are in fragment order: lane l's 8 (or 4) elements are
+    // contiguous and a wave-wide load is one contiguous run
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-        if constexpr (DELTA) op.w[kb] = ld_frag(base + R::W + p * DK + 32 * kb + 8 * grp);
-        op.qt[kb] = ld_frag(base + R::QT + p * DK + 32 * kb + 8 * grp);
+        const size_t f = ((size_t)(wave * NKB + kb) * 64 + lane) * 8;
+        if constexpr (DELTA) op.w[kb] = ld_frag(base + R::W + f);
+        op.qt[kb] = ld_frag(base + R::QT + f);
     }
     // both key blocks: the record holds zeros above the diagonal, so the
     // block past this wave's positions contributes nothing
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) op.aqk[kb] = ld_frag(base + R::AQK + p * C + 32 * kb + 8 * grp);
+    for (int kb = 0; kb < 2; ++kb) op.aqk[kb] = ld_frag(base + R::AQK + ((size_t)(wave * 2 + kb) * 64 + lane) * 8);
     if (NKB >= 4 || wave < NKB) {
         const float* phi = reinterpret_cast<const float*>(recb + R::PHI_BYTE);
+        const int grp = lane >> 4;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-            const int dk = 32 * wave + prow(half, r16);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) op.kb[half][kb] = ld_frag(base + R::KBT + dk * C + 32 * kb + 8 * grp);
+            for (int kb = 0; kb < 2; ++kb)
+                op.kb[half][kb] = ld_frag(base + R::KBT + ((size_t)((wave * 2 + half) * 2 + kb) * 64 + lane) * 8);
             ld4(phi + 32 * wave + 8 * grp + 4 * half, op.phi[half]);
         }
     }
 #pragma unroll
     for (int n = 0; n < NTN; ++n)
-        ld4(base + R::UT + (size_t)(dv0 + 16 * n + r16) * C + 32 * kbP + 8 * grp + 4 * halfP, op.u[n]);
+        ld4(base + R::UT + ((size_t)((dv0 / 16 + n) * 4 + wave) * 64 + lane) * 4, op.u[n]);
 }
 
 template <int KIND, typename T, int DK, int DV, int NTN, int NBUF>

@@ -222,14 +222,21 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(
                 kb[0][i] = k0 * r;
                 kb[1][i] = k1 * r;
             }
-            *reinterpret_cast<T2*>(rQ + p * DK + ch0) = Pair<T>::make(q0 * e0, q1 * e1);
         }
-        // Kbar^T: PL consecutive positions per channel
+        // Kbar in fragment order: channel ch is row prow(h, r) of key block
+        // ch/32; each run of 8 positions is one 16-byte store
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
-            T* dst = rKb + (size_t)(ch0 + cc) * C + p0;
+            const int ch = ch0 + cc, qq = ch & 31;
+            const int wk = ch >> 5, hh = (qq >> 2) & 1, rr = 4 * (qq >> 3) + (qq & 3);
 #pragma unroll
-            for (int i = 0; i < PL; i += 4) st4(dst + i, &kb[cc][i]);
+            for (int i0 = 0; i0 < PL; i0 += 8) {
+                const int p = p0 + i0;
+                Frag<T> f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) frag_set(f, j, kb[cc][i0 + j]);
+                st_frag(rKb + ((size_t)(((wk * 2 + hh) * 2 + (p >> 5)) * 64) + rr + 16 * ((p & 31) >> 3)) * 8, f);
+            }
         }
         if (qg == 0) {
             rPhi[ch0] = phi0;
@@ -244,56 +251,100 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(
             }
         }
         if constexpr (!DELTA) {
-            // decay_la: the state pass reads V^T from the U^T slot
+            // decay_la: the state pass reads V from the U slot (fragment order)
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
+                const int ch = ch0 + cc;
                 float vt[PL];
 #pragma unroll
                 for (int i = 0; i < PL; ++i) vt[i] = cc ? Pair<T>::hi(vv[i]) : Pair<T>::lo(vv[i]);
-                T* dst = rU + (size_t)(ch0 + cc) * C + p0;
 #pragma unroll
-                for (int i = 0; i < PL; i += 4) st4(dst + i, &vt[i]);
+                for (int i = 0; i < PL; i += 4) {
+                    const int p = p0 + i;
+                    const int wv = 2 * (p >> 5) + ((p >> 2) & 1);
+                    st4(rU + ((size_t)(((ch >> 4) * 4 + wv) * 64) + (ch & 15) + 16 * ((p & 31) >> 3)) * 4, &vt[i]);
+                }
             }
         }
     }
     lds_barrier();
 
-    // ---- P2: A and Aqk on MFMA ---------------------------------------------
+    // ---- P2: A (natural layout, LDS) and Aqk (fragment order, record) ------
     {
         constexpr int NKB = DK / 32;
-        constexpr int NTL = DELTA ? 20 : 10;
+        constexpr int NA = DELTA ? 10 : 0;      // lower 16x16 tiles of A
         const T* kminus = PERCH ? sKm : sKp;
-        for (int idx = wave; idx < NTL; idx += 4) {
-            const bool isA = DELTA && idx < 10;
-            int ti, tj;
-            lower_tile(isA ? idx : idx - (DELTA ? 10 : 0), ti, tj);
-            const T* lhs = isA ? sKp : sQp;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        // items: NA tiles of A, then the 6 nonzero 32x32 blocks (w, kb) of Aqk,
+        // kb <= w/2, each computed transposed (keys x queries) with rows and
+        // columns permuted so that the accumulators are fragment-ordered
+        for (int idx = wave; idx < NA + 6; idx += 4) {
+            if (idx < NA) {
+                int ti, tj;
+                lower_tile(idx, ti, tj);
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                const Frag<T> fa = ld_frag(lhs + (16 * ti + r16) * LDK + 32 * kb + 8 * grp);
-                const Frag<T> fb = ld_frag(kminus + (16 * tj + r16) * LDK + 32 * kb + 8 * grp);
-                mma(acc, fa, fb);
-            }
-            const int col = 16 * tj + r16;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * ti + 4 * grp + i;
-                float ratio = 1.f;
-                if constexpr (!PERCH) ratio = (col <= row) ? __builtin_amdgcn_exp2f(sGam[row] - sGam[col]) : 0.f;
-                if (isA) {
-                    sA[row * LDF + col] = (col < row) ? sBeta[row] * ratio * acc[i] : 0.f;
-                } else {
-                    rAqk[row * C + col] = from_f<T>((col <= row) ? ratio * acc[i] : 0.f);
+                for (int kb = 0; kb < NKB; ++kb) {
+                    const Frag<T> fa = ld_frag(sKp + (16 * ti + r16) * LDK + 32 * kb + 8 * grp);
+                    const Frag<T> fb = ld_frag(kminus + (16 * tj + r16) * LDK + 32 * kb + 8 * grp);
+                    mma(acc, fa, fb);
                 }
+                const int col = 16 * tj + r16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * ti + 4 * grp + i;
+                    float ratio = 1.f;
+                    if constexpr (!PERCH) ratio = (col < row) ? __builtin_amdgcn_exp2f(sGam[row] - sGam[col]) : 0.f;
+                    sA[row * LDF + col] = (col < row) ? sBeta[row] * ratio * acc[i] : 0.f;
+                }
+            } else {
+                const int bI = idx - NA;   // (w, kb): (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+                const int w = bI < 2 ? bI : 2 + ((bI - 2) >> 1);
+                const int kbk = bI < 2 ? 0 : ((bI - 2) & 1);
+                const int query = pw(w, r16);
+                f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+                for (int kd = 0; kd < NKB; ++kd) {
+                    const Frag<T> fq = ld_frag(sQp + query * LDK + 32 * kd + 8 * grp);
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const Frag<T> fk = ld_frag(kminus + (32 * kbk + prow(hh, r16)) * LDK + 32 * kd + 8 * grp);
+                        mma(acc[hh], fk, fq);   // [key][query]
+                    }
+                }
+                Frag<T> out;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int key = 32 * kbk + 8 * grp + 4 * hh + i;
+                        float val = 0.f;
+                        if (key <= query) {
+                            val = acc[hh][i];
+                            if constexpr (!PERCH) val *= __builtin_amdgcn_exp2f(sGam[query] - sGam[key]);
+                        }
+                        frag_set(out, 4 * hh + i, val);
+                    }
+                st_frag(rAqk + ((size_t)(w * 2 + kbk) * 64 + lane) * 8, out);
             }
         }
-        // zero the six upper 16x16 tiles of Aqk
-        for (int e = tid; e < 6 * 256; e += kThreads) {
-            const int u = e >> 8, x = e & 255;
-            const int ti = u < 3 ? 0 : u < 5 ? 1 : 2;
-            const int tj = u < 3 ? 1 + u : u < 5 ? u - 1 : 3;
-            rAqk[(16 * ti + (x >> 4)) * C + 16 * tj + (x & 15)] = from_f<T>(0.f);
+        // the two blocks above the diagonal (w = 0, 1; kb = 1) are zero
+        if (tid < 128) {
+            Frag<T> z;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) frag_set(z, j, 0.f);
+            st_frag(rAqk + ((size_t)((tid >> 6) * 2 + 1) * 64 + (tid & 63)) * 8, z);
+        }
+        // Q~ in fragment order, from the LDS copy (scalar gates scale it here)
+        for (int e = tid; e < 4 * NKB * 64; e += kThreads) {
+            const int l = e & 63, kq = (e >> 6) % NKB, w = (e >> 6) / NKB;
+            const int row = pw(w, l & 15);
+            Frag<T> f = ld_frag(sQp + row * LDK + 32 * kq + 8 * (l >> 4));
+            if constexpr (!PERCH) {
+                const float sc = __builtin_amdgcn_exp2f(sGam[row]);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) frag_set(f, j, frag_get(f, j) * sc);
+            }
+            st_frag(rQ + (size_t)e * 8, f);
         }
     }
     if constexpr (!DELTA) return;
@@ -382,11 +433,13 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(
             for (int n = 0; n < PER; ++n) acc[mt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
+            // U rows are taken in the state pass's order (pw), W rows naturally
+            const int arow = isW ? 16 * mt + r16 : pw(mt, r16);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 if (kb == 1 && mt < 2) continue;   // T is lower triangular
                 Frag<T> fa;
-                const float* src = sT + (16 * mt + r16) * LDF + 32 * kb + 8 * grp;
+                const float* src = sT + arow * LDF + 32 * kb + 8 * grp;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) frag_set(fa, j, src[j]);
 #pragma unroll
@@ -405,34 +458,44 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(
                         for (int i = 0; i < 4; ++i)
                             sW[(16 * mt + 4 * grp + i) * LDK + 16 * (nt0 + n) + r16] = from_f<T>(acc[mt][n][i]);
             } else {
-                // fp32: 4-byte elements, stored straight from the accumulators.
-                // (Staging these through LDS hit a miscompile in this toolchain:
-                // two of the four row stores were merged into one ds_write2_b32
-                // whose first offset was encoded wrong at Dk = 128.)
+                // fp32: 4-byte elements, stored straight from the accumulators
+                // into their fragment-order slots.  (Staging these through LDS
+                // hit a miscompile in this toolchain: two of the four row stores
+                // were merged into one ds_write2_b32 whose first offset was
+                // encoded wrong at Dk = 128.)
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                     for (int n = 0; n < PER; ++n)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            rW[(16 * mt + 4 * grp + i) * DK + 16 * (nt0 + n) + r16] = from_f<T>(acc[mt][n][i]);
+                        for (int i = 0; i < 4; ++i) {
+                            const int row = 16 * mt + 4 * grp + i, col = 16 * (nt0 + n) + r16;
+                            const int qq = row & 31;
+                            const int wr = 2 * (row >> 5) + ((qq >> 2) & 1), rr = 4 * (qq >> 3) + (qq & 3);
+                            const size_t e = ((size_t)(wr * (DK / 32) + (col >> 5)) * 64 + rr + 16 * ((col & 31) >> 3)) * 8 + (col & 7);
+                            rW[e] = from_f<T>(acc[mt][n][i]);
+                        }
             }
         } else {
+            // U: m-tile mt holds the rows of state-pass wave mt, so each lane's 4
+            // values are one fragment-order slot group
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int n = 0; n < PER; ++n) {
-                    const int e = 16 * (nt0 + n - NTW) + r16;
+                    const int t = nt0 + n - NTW;
                     float vals[4] = {acc[mt][n][0], acc[mt][n][1], acc[mt][n][2], acc[mt][n][3]};
-                    st4(rU + (size_t)e * C + 16 * mt + 4 * grp, vals);
+                    st4(rU + ((size_t)(t * 4 + mt) * 64 + lane) * 4, vals);
                 }
         }
     }
     if constexpr (sizeof(T) == 2) {
         lds_barrier();
-        for (int e = tid; e < C * (DK / 8); e += kThreads) {
-            const int p = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
-            st_frag(rW + p * DK + c8, ld_frag(sW + p * LDK + c8));
+        // W in fragment order from the staged natural tile
+        constexpr int NKB = DK / 32;
+        for (int e = tid; e < 4 * NKB * 64; e += kThreads) {
+            const int l = e & 63, kq = (e >> 6) % NKB, w = (e >> 6) / NKB;
+            st_frag(rW + (size_t)e * 8, ld_frag(sW + pw(w, l & 15) * LDK + 32 * kq + 8 * (l >> 4)));
         }
     }
 }

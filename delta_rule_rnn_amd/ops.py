@@ -194,21 +194,55 @@ def inter(kind: str, workspace, B, T, H, Dk, Dv, dtype, h0=None, out=None, hT=No
     return out, hT
 
 
+def _prow(half, r):
+    return 8 * (r >> 2) + 4 * half + (r & 3)
+
+
+def _pw(w, r):
+    return 32 * (w >> 1) + _prow(w & 1, r)
+
+
+def _frag_maps(C: int, Dk: int, Dv: int):
+    """For each record block, the natural (row, col) of every stored element,
+    in storage order (the fragment order of include/deltarule.h, dr_intra)."""
+    import numpy as np
+    nkb = Dk // 32
+    w, kb, l, j = np.meshgrid(np.arange(4), np.arange(nkb), np.arange(64), np.arange(8), indexing="ij")
+    wq = (_pw(w, l % 16), 32 * kb + 8 * (l // 16) + j)                      # W, Qt: [pos][dk]
+    w2, h, kb2, l2, j2 = np.meshgrid(np.arange(nkb), np.arange(2), np.arange(2), np.arange(64),
+                                     np.arange(8), indexing="ij")
+    kbt = (32 * w2 + _prow(h, l2 % 16), 32 * kb2 + 8 * (l2 // 16) + j2)     # KbT: [dk][pos]
+    w3, kb3, l3, j3 = np.meshgrid(np.arange(4), np.arange(2), np.arange(64), np.arange(8), indexing="ij")
+    aqk = (_pw(w3, l3 % 16), 32 * kb3 + 8 * (l3 // 16) + j3)                # Aqk: [pos][pos]
+    t4, w4, l4, i4 = np.meshgrid(np.arange(Dv // 16), np.arange(4), np.arange(64), np.arange(4),
+                                 indexing="ij")
+    ut = (16 * t4 + l4 % 16, 32 * (w4 >> 1) + 8 * (l4 // 16) + 4 * (w4 & 1) + i4)  # UT: [dv][pos]
+    return {"W": wq, "Qt": wq, "KbT": kbt, "Aqk": aqk, "UT": ut}
+
+
 def unpack_records(workspace: torch.Tensor, B: int, T: int, H: int, Dk: int, Dv: int,
                    dtype: torch.dtype, chunk_size: int = CHUNK) -> dict:
-    """View the K1 records as named tensors (layout of include/deltarule.h,
-    dr_intra): W [B,H,NT,C,Dk], Qt [..,C,Dk], KbT [..,Dk,C], Aqk [..,C,C],
-    UT [..,Dv,C], phi [..,Dk] (fp32)."""
+    """View the K1 records as natural named tensors: W [B,H,NT,C,Dk],
+    Qt [..,C,Dk], KbT [..,Dk,C], Aqk [..,C,C], UT [..,Dv,C], phi [..,Dk]
+    (fp32).  The records store each block in the state pass's fragment order
+    (include/deltarule.h, dr_intra); this undoes that permutation."""
+    import numpy as np
     C = chunk_size
     NT = (T + C - 1) // C
     rb = record_bytes(Dk, Dv, dtype, C)
     esz = torch.tensor([], dtype=dtype).element_size()
     recs = workspace[: B * H * NT * rb].view(B, H, NT, rb)
+    maps = _frag_maps(C, Dk, Dv)
     sizes = [("W", C * Dk, (C, Dk)), ("Qt", C * Dk, (C, Dk)), ("KbT", Dk * C, (Dk, C)),
              ("Aqk", C * C, (C, C)), ("UT", Dv * C, (Dv, C))]
     out, off = {}, 0
     for name, n, shp in sizes:
-        out[name] = recs[..., off * esz:(off + n) * esz].contiguous().view(dtype).view(B, H, NT, *shp)
+        flat = recs[..., off * esz:(off + n) * esz].contiguous().view(dtype).view(B, H, NT, n)
+        rows, cols = (np.asarray(a).reshape(-1) for a in maps[name])
+        lin = torch.as_tensor(rows * shp[1] + cols, device=flat.device)
+        nat = torch.empty(B, H, NT, n, dtype=dtype, device=flat.device)
+        nat[..., lin] = flat
+        out[name] = nat.view(B, H, NT, *shp)
         off += n
     pb = off * esz
     out["phi"] = recs[..., pb:pb + Dk * 4].contiguous().view(torch.float32).view(B, H, NT, Dk)

@@ -146,17 +146,23 @@ dr_status dr_kda_prep(const void* q, const void* k, const float* gamma,
 /*
  * K1 alone: steps a1 + a2 + a3 fused, chunk-parallel.  Fills `workspace`
  * with one record per (b, h, chunk), record index (b*H + h)*NT + c,
- * NT = ceil(T/C).  Record layout (elements of the I/O dtype unless noted,
- * each block dense row-major, r/i = position in the chunk, d = key channel,
- * e = value channel):
- *   W    [C][Dk]   W = T diag(beta) K+   (delta kinds; unused for decay_la)
- *   Qt   [C][Dk]   q * 2^gamma
- *   KbT  [Dk][C]   (k * 2^(gamma_last - gamma))^T
- *   Aqk  [C][C]    Tril_incl(Q~ K-^T)  (zero above the diagonal)
- *   UT   [Dv][C]   U^T, U = T diag(beta) V  (decay_la: V^T)
- *   phi  [Dk]      float, 2^(gamma_last)
+ * NT = ceil(T/C).  A record holds, in elements of the I/O dtype (r, i =
+ * positions in the chunk, d = key channel, e = value channel):
+ *   W    C*Dk     W = T diag(beta) K+   (delta kinds; unused for decay_la)
+ *   Qt   C*Dk     q * 2^gamma
+ *   KbT  Dk*C     k * 2^(gamma_last - gamma), key-major
+ *   Aqk  C*C      Tril_incl(Q~ K-^T)  (zero above the diagonal)
+ *   UT   Dv*C     U = T diag(beta) V  (decay_la: V)
+ *   phi  Dk float 2^(gamma_last)
  * with T = (I + A)^-1, A = diag(beta) StrictLower(K+ K-^T) ("TileLang 实战：
  * KDA 从零到一–Kimi Delta Attention" sections 3.2-3.3, row-beta pairing).
+ * Each block is stored in the MFMA fragment order the state pass reads
+ * (lane l, element j, 32-row blocks split by prow(h, r) = 8(r/4) + 4h + r%4,
+ * pw(w, r) = 32(w/2) + prow(w%2, r)):
+ *   W, Qt [w<4][kb<Dk/32][l<64][j<8] = X[pw(w, l%16)][32kb + 8(l/16) + j]
+ *   KbT   [w<Dk/32][h<2][kb<2][l][j<8] = Kbar[32kb + 8(l/16) + j][32w + prow(h, l%16)]
+ *   Aqk   [w<4][kb<2][l][j<8] = Aqk[pw(w, l%16)][32kb + 8(l/16) + j]
+ *   UT    [t<Dv/16][w<4][l][i<4] = U[32(w/2) + 8(l/16) + 4(w%2) + i][16t + l%16]
  * Rows of a ragged last chunk beyond T are zero.  Record size:
  * dr_record_bytes().  For GDN / decay_la, g is [B,T,H] and beta may be NULL
  * for decay_la.
