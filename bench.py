@@ -8,15 +8,23 @@ long-context workload (B=1, H=32, T=32768, dk=dv=128, C=64), inputs resident
 in HBM.  Prints one JSON line.
 
 Per-kernel durations come from HIP events recorded on the launch stream
-between the two kernel launches of every timed step.  The CPU baseline is
-the fp64 oracle (test infrastructure) timed on a bounded sample of the same
-workload on the host cores.
+between the two kernel launches of every timed step.  The step makes the same
+two launches, on the same stream, as the kda_fwd entry point.  The HBM
+traffic of each kernel comes from the committed counter summary under
+profiles/ (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by a copy-kernel
+calibration); it is reported only while the kernel sources still hash to the
+value recorded there.  The CPU baseline is the fp64 oracle (test
+infrastructure) timed on a bounded sample of the same workload on the host
+cores.
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -48,6 +56,34 @@ def algorithmic(kind: str, w, io_bytes: int):
     else:
         flops = 2 * dk * C + 2 * C * dv + 2 * 2 * dk * dv
     return k1, k2, flops
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the kernel sources and the build script, in name order."""
+    pkg = os.path.join(ROOT, "delta_rule_rnn_amd")
+    files = sorted(glob.glob(os.path.join(pkg, "csrc", "*"))) + [os.path.join(pkg, "build.py")]
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of each kernel from profiles/<workload>_traffic.txt,
+    or {} when absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return {}
+    text = open(path).read()
+    m = re.search(r"^source_sha256:\s*([0-9a-f]{64})", text, re.M)
+    if not m or m.group(1) != kernel_source_hash():
+        return {}
+    out = {}
+    for name, b in re.findall(r"^traffic\s+(\w+):.*\bbytes=(\d+)", text, re.M):
+        out[name] = int(b)
+    return out
 
 
 def cpu_baseline(w, x, max_tokens: int, threads: int):
@@ -140,6 +176,7 @@ def main():
     wall = time.perf_counter() - t0
     k1 = [e[0].elapsed_time(e[1]) for e in evs]
     k2 = [e[1].elapsed_time(e[2]) for e in evs]
+    per_step = sorted(e[0].elapsed_time(e[2]) for e in evs)
     ms = wall * 1000.0 / args.steps
     tokens = B * T
     value = tokens / (ms / 1000.0)
@@ -153,10 +190,13 @@ def main():
         "inter": {"avg_ms": k2_ms, "bytes": b2 * th, "gbs": b2 * th / (k2_ms * 1e-3) / 1e9},
     }
     dom = max(kern, key=lambda n: kern[n]["avg_ms"])
+    traffic = measured_traffic(args.workload)
     roof = {"bound": "hbm", "kernel": dom, "achieved": round(kern[dom]["gbs"], 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(kern[dom]["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+            "unit": "GB/s", "frac": round(kern[dom]["gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": traffic.get(dom),
             "per_kernel": {n: {"avg_ms": round(v["avg_ms"], 4), "alg_bytes": int(v["bytes"]),
-                               "achieved_GBs": round(v["gbs"], 1)} for n, v in kern.items()}}
+                               "achieved_GBs": round(v["gbs"], 1), "traffic": traffic.get(n)}
+                           for n, v in kern.items()}}
     mfma_frac = flops * th / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)
 
     cpu = None
@@ -172,6 +212,7 @@ def main():
         "config": {"workload": f"{w.kind}_fwd B={B} H={H} T={T} dk={Dk} dv={Dv} C={w.C}",
                    "global_batch": B, "seq_len": T, "heads": H, "parallelism": "single GPU",
                    "gate": f"a ~ U[{w.gate_lo}, {w.gate_hi}]"},
+        "median_ms_per_step_events": round(per_step[len(per_step) // 2], 4),
         "mfma_frac_bf16": round(mfma_frac, 4),
         "roofline": roof,
         "cpu_baseline": cpu,

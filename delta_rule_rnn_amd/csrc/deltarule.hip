@@ -43,32 +43,41 @@ dr_status validate(int kind, const void* q, const void* k, const void* v, const 
     return DR_OK;
 }
 
-template <int KIND, typename E, int D>
-dr_status launch_intra(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                       int B, int T, int H, void* ws, unsigned* flags, hipStream_t st) {
-    const int NT = ceil_div(T, dr::kChunk);
-    if (NT == 0) return DR_OK;
-    dim3 grid(NT, H, B);
-    hipLaunchKernelGGL((dr::intra_kernel<KIND, E, D, D>), grid, dim3(dr::kThreads), 0, st,
-                       static_cast<const E*>(q), static_cast<const E*>(k), static_cast<const E*>(v), g,
-                       beta, static_cast<uint8_t*>(ws), flags, T, H, NT);
-    return check_launch();
+// One forward problem: the arguments every launch needs.
+struct Problem {
+    int kind, dtype, D, B, T, H, NT;
+    const void *q, *k, *v;
+    const float *g, *beta;
+    void* o;
+    uint8_t* ws;
+    unsigned* flags;
+};
+
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
 }
 
-// Value columns per state-pass workgroup (16 * ntn).  Fewer columns per
-// workgroup means more workgroups: with few (b, h) chains the narrow split
-// fills the 256 CUs; with many chains wider slices cut the repeated reads of
-// the shared W / Q~ / Kbar / Aqk operands.  DR_INTER_NTN (1, 2 or 4)
-// overrides the choice for tuning.
+// Value columns per state-pass workgroup (16 * ntn): the widest slice that
+// still gives every CU a workgroup.  Narrow slices multiply the reads of the
+// operands all slices of a chain share (W, Q~, Kbar, Aqk); too few workgroups
+// leave CUs idle.  DR_INTER_NTN (1, 2 or 4) overrides the choice for tuning.
 int pick_ntn(int chains, int D) {
     if (const char* e = getenv("DR_INTER_NTN")) {
         const int v = atoi(e);
         if ((v == 1 || v == 2 || v == 4) && 16 * v <= D) return v;
     }
-    const int cols = D / 16;                         // 16-column slices per chain
-    if (chains * cols <= 512) return 1;              // <= 512 workgroups: narrowest
-    if (chains * cols / 2 <= 512 || D == 64) return 2;
-    return 4;
+    const int cols = D / 16, cus = device_cus();
+    int ntn = 4;
+    while (ntn > 1 && (ntn > cols || (long long)chains * (cols / ntn) < cus)) ntn /= 2;
+    return ntn;
 }
 
 int pick_nbuf() {
@@ -79,75 +88,89 @@ int pick_nbuf() {
     return 2;
 }
 
+// ---- chunk-parallel kernel over chunks [c0, c0 + n) -----------------------
+template <int KIND, typename E, int D>
+dr_status launch_intra_t(const Problem& p, int c0, int n, hipStream_t st) {
+    dim3 grid(n, p.H, p.B);
+    hipLaunchKernelGGL((dr::intra_kernel<KIND, E, D, D>), grid, dim3(dr::kThreads), 0, st,
+                       static_cast<const E*>(p.q), static_cast<const E*>(p.k), static_cast<const E*>(p.v),
+                       p.g, p.beta, p.ws, p.flags, p.T, p.H, p.NT, c0);
+    return check_launch();
+}
+
+template <int KIND>
+dr_status launch_intra_k(const Problem& p, int c0, int n, hipStream_t st) {
+    if (p.dtype == DR_BF16) {
+        if (p.D == 64) return launch_intra_t<KIND, bf16, 64>(p, c0, n, st);
+        return launch_intra_t<KIND, bf16, 128>(p, c0, n, st);
+    }
+    if (p.D == 64) return launch_intra_t<KIND, float, 64>(p, c0, n, st);
+    return launch_intra_t<KIND, float, 128>(p, c0, n, st);
+}
+
+dr_status launch_intra(const Problem& p, int c0, int n, hipStream_t st) {
+    if (n <= 0) return DR_OK;
+    switch (p.kind) {
+        case DR_KIND_KDA: return launch_intra_k<dr::KIND_KDA>(p, c0, n, st);
+        case DR_KIND_GDN: return launch_intra_k<dr::KIND_GDN>(p, c0, n, st);
+        default: return launch_intra_k<dr::KIND_LA>(p, c0, n, st);
+    }
+}
+
+// ---- state pass + output over chunks [c0, c0 + n) ------------------------
 template <int KIND, typename E, int D, int NTN, int NBUF>
-dr_status launch_inter_n(const float* h0, void* o, float* hT, int B, int T, int H, const void* ws,
-                         hipStream_t st) {
-    const int NT = ceil_div(T, dr::kChunk);
+dr_status launch_inter_n(const Problem& p, const float* h0, float* hT, int c0, int n, hipStream_t st) {
     constexpr int NV = D / (16 * NTN);
-    dim3 grid(B * H * NV);
+    dim3 grid(p.B * p.H * NV);
     hipLaunchKernelGGL((dr::inter_kernel<KIND, E, D, D, NTN, NBUF>), grid, dim3(dr::kThreads), 0, st,
-                       static_cast<const uint8_t*>(ws), h0, static_cast<E*>(o), hT, T, H, NT);
+                       p.ws, h0, static_cast<E*>(p.o), hT, p.T, p.H, p.NT, c0, n);
     return check_launch();
 }
 
 template <int KIND, typename E, int D>
-dr_status launch_inter(const float* h0, void* o, float* hT, int B, int T, int H, const void* ws,
-                       hipStream_t st) {
-    const int ntn = pick_ntn(B * H, D);
+dr_status launch_inter_t(const Problem& p, const float* h0, float* hT, int c0, int n, hipStream_t st) {
+    const int ntn = pick_ntn(p.B * p.H, D);
     // fp32 operands are twice as large: one chunk of prefetch only
     const int nbuf = sizeof(E) == 4 ? 2 : pick_nbuf();
     if constexpr (sizeof(E) == 2) {
         if (nbuf == 3) {
-            if (ntn == 1) return launch_inter_n<KIND, E, D, 1, 3>(h0, o, hT, B, T, H, ws, st);
-            if (ntn == 2) return launch_inter_n<KIND, E, D, 2, 3>(h0, o, hT, B, T, H, ws, st);
+            if (ntn == 1) return launch_inter_n<KIND, E, D, 1, 3>(p, h0, hT, c0, n, st);
+            if (ntn == 2) return launch_inter_n<KIND, E, D, 2, 3>(p, h0, hT, c0, n, st);
             // 64 columns with three buffers does not fit in registers: two buffers
         }
     }
-    if (ntn == 1) return launch_inter_n<KIND, E, D, 1, 2>(h0, o, hT, B, T, H, ws, st);
-    if (ntn == 2) return launch_inter_n<KIND, E, D, 2, 2>(h0, o, hT, B, T, H, ws, st);
-    return launch_inter_n<KIND, E, D, 4, 2>(h0, o, hT, B, T, H, ws, st);
+    if (ntn == 1) return launch_inter_n<KIND, E, D, 1, 2>(p, h0, hT, c0, n, st);
+    if (ntn == 2) return launch_inter_n<KIND, E, D, 2, 2>(p, h0, hT, c0, n, st);
+    return launch_inter_n<KIND, E, D, 4, 2>(p, h0, hT, c0, n, st);
 }
 
 template <int KIND>
-dr_status dispatch_intra(int dtype, int D, const void* q, const void* k, const void* v, const float* g,
-                         const float* beta, int B, int T, int H, void* ws, unsigned* flags,
-                         hipStream_t st) {
-    if (dtype == DR_BF16) {
-        if (D == 64) return launch_intra<KIND, bf16, 64>(q, k, v, g, beta, B, T, H, ws, flags, st);
-        return launch_intra<KIND, bf16, 128>(q, k, v, g, beta, B, T, H, ws, flags, st);
+dr_status launch_inter_k(const Problem& p, const float* h0, float* hT, int c0, int n, hipStream_t st) {
+    if (p.dtype == DR_BF16) {
+        if (p.D == 64) return launch_inter_t<KIND, bf16, 64>(p, h0, hT, c0, n, st);
+        return launch_inter_t<KIND, bf16, 128>(p, h0, hT, c0, n, st);
     }
-    if (D == 64) return launch_intra<KIND, float, 64>(q, k, v, g, beta, B, T, H, ws, flags, st);
-    return launch_intra<KIND, float, 128>(q, k, v, g, beta, B, T, H, ws, flags, st);
+    if (p.D == 64) return launch_inter_t<KIND, float, 64>(p, h0, hT, c0, n, st);
+    return launch_inter_t<KIND, float, 128>(p, h0, hT, c0, n, st);
 }
 
-template <int KIND>
-dr_status dispatch_inter(int dtype, int D, const float* h0, void* o, float* hT, int B, int T, int H,
-                         const void* ws, hipStream_t st) {
-    if (dtype == DR_BF16) {
-        if (D == 64) return launch_inter<KIND, bf16, 64>(h0, o, hT, B, T, H, ws, st);
-        return launch_inter<KIND, bf16, 128>(h0, o, hT, B, T, H, ws, st);
-    }
-    if (D == 64) return launch_inter<KIND, float, 64>(h0, o, hT, B, T, H, ws, st);
-    return launch_inter<KIND, float, 128>(h0, o, hT, B, T, H, ws, st);
-}
-
-dr_status run_intra(int kind, const void* q, const void* k, const void* v, const float* g,
-                    const float* beta, int B, int T, int H, int D, int dtype, void* ws, unsigned* flags,
-                    hipStream_t st) {
-    switch (kind) {
-        case DR_KIND_KDA: return dispatch_intra<dr::KIND_KDA>(dtype, D, q, k, v, g, beta, B, T, H, ws, flags, st);
-        case DR_KIND_GDN: return dispatch_intra<dr::KIND_GDN>(dtype, D, q, k, v, g, beta, B, T, H, ws, flags, st);
-        default: return dispatch_intra<dr::KIND_LA>(dtype, D, q, k, v, g, nullptr, B, T, H, ws, flags, st);
+dr_status launch_inter(const Problem& p, const float* h0, float* hT, int c0, int n, hipStream_t st) {
+    switch (p.kind) {
+        case DR_KIND_KDA: return launch_inter_k<dr::KIND_KDA>(p, h0, hT, c0, n, st);
+        case DR_KIND_GDN: return launch_inter_k<dr::KIND_GDN>(p, h0, hT, c0, n, st);
+        default: return launch_inter_k<dr::KIND_LA>(p, h0, hT, c0, n, st);
     }
 }
 
-dr_status run_inter(int kind, const float* h0, void* o, float* hT, int B, int T, int H, int D, int dtype,
-                    const void* ws, hipStream_t st) {
-    switch (kind) {
-        case DR_KIND_KDA: return dispatch_inter<dr::KIND_KDA>(dtype, D, h0, o, hT, B, T, H, ws, st);
-        case DR_KIND_GDN: return dispatch_inter<dr::KIND_GDN>(dtype, D, h0, o, hT, B, T, H, ws, st);
-        default: return dispatch_inter<dr::KIND_LA>(dtype, D, h0, o, hT, B, T, H, ws, st);
-    }
+Problem make_problem(int kind, const void* q, const void* k, const void* v, const float* g,
+                     const float* beta, void* o, int B, int T, int H, int D, int dtype, void* ws,
+                     unsigned* flags) {
+    Problem p;
+    p.kind = kind; p.dtype = dtype; p.D = D; p.B = B; p.T = T; p.H = H;
+    p.NT = ceil_div(T, dr::kChunk);
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = kind == DR_KIND_DECAY_LA ? nullptr : beta;
+    p.o = o; p.ws = static_cast<uint8_t*>(ws); p.flags = flags;
+    return p;
 }
 
 dr_status forward(int kind, const void* q, const void* k, const void* v, const float* g,
@@ -160,12 +183,12 @@ dr_status forward(int kind, const void* q, const void* k, const void* v, const f
     const size_t need = dr_workspace_bytes(kind, B, T, H, Dk, Dv, C, dtype);
     if (T > 0 && (ws == nullptr || ws_bytes < need)) return DR_ERR_WORKSPACE;
     if (T == 0 && hT == nullptr) return DR_OK;
+    const Problem p = make_problem(kind, q, k, v, g, beta, o, B, T, H, Dk, dtype, ws, flags);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (T > 0) {
-        s = run_intra(kind, q, k, v, g, beta, B, T, H, Dk, dtype, ws, flags, st);
-        if (s != DR_OK) return s;
-    }
-    return run_inter(kind, h0, o, hT, B, T, H, Dk, dtype, ws, st);
+    if (T == 0) return launch_inter(p, h0, hT, 0, 0, st);
+    s = launch_intra(p, 0, p.NT, st);
+    if (s != DR_OK) return s;
+    return launch_inter(p, h0, hT, 0, p.NT, st);
 }
 
 }  // namespace
@@ -214,8 +237,8 @@ dr_status dr_intra(int kind, const void* q, const void* k, const void* v, const 
     if (!aligned16(workspace)) return DR_ERR_INVALID_ARG;
     if (T > 0 && (!workspace || workspace_bytes < dr_workspace_bytes(kind, B, T, H, Dk, Dv, C, dtype)))
         return DR_ERR_WORKSPACE;
-    return run_intra(kind, q, k, v, g, beta, B, T, H, Dk, dtype, workspace, flags,
-                     static_cast<hipStream_t>(stream));
+    const Problem p = make_problem(kind, q, k, v, g, beta, nullptr, B, T, H, Dk, dtype, workspace, flags);
+    return launch_intra(p, 0, p.NT, static_cast<hipStream_t>(stream));
 }
 
 dr_status dr_inter(int kind, const float* h0, void* o, float* hT, int B, int T, int H, int Dk, int Dv,
@@ -228,7 +251,9 @@ dr_status dr_inter(int kind, const float* h0, void* o, float* hT, int B, int T, 
     if (T > 0 && (!workspace || workspace_bytes < dr_workspace_bytes(kind, B, T, H, Dk, Dv, C, dtype)))
         return DR_ERR_WORKSPACE;
     if (T == 0 && hT == nullptr) return DR_OK;
-    return run_inter(kind, h0, o, hT, B, T, H, Dk, dtype, workspace, static_cast<hipStream_t>(stream));
+    const Problem p = make_problem(kind, nullptr, nullptr, nullptr, nullptr, nullptr, o, B, T, H, Dk, dtype,
+                                   const_cast<void*>(workspace), nullptr);
+    return launch_inter(p, h0, hT, 0, p.NT, static_cast<hipStream_t>(stream));
 }
 
 dr_status dr_chunk_cumsum(const float* g, float* gamma, int B, int T, int H, int D, int C, void* stream) {

@@ -85,7 +85,8 @@ template <int KIND, typename T, int DK, int DV, int NTN, int NBUF>
 __global__ __launch_bounds__(kThreads) void inter_kernel(const uint8_t* __restrict__ ws,
                                                          const float* __restrict__ h0,
                                                          T* __restrict__ o, float* __restrict__ hT,
-                                                         int Tlen, int H, int NT)
+                                                         int Tlen, int H, int NT, int c0,
+                                                         int nseg)
 {
     using R = Rec<T, DK, DV>;
     constexpr int C = kChunk;
@@ -144,10 +145,13 @@ __global__ __launch_bounds__(kThreads) void inter_kernel(const uint8_t* __restri
     publish_state();
     lds_barrier();
 
-    const uint8_t* chain_rec = ws + ((size_t)b * H + h) * (size_t)NT * R::BYTES;
+    // this launch runs chunks c0 .. c0+nseg-1 of the chain (a segment; the
+    // state enters through h0 and leaves through hT)
+    const uint8_t* chain_rec = ws + (((size_t)b * H + h) * (size_t)NT + c0) * R::BYTES;
     // output rows are H*DV elements apart; orow0 = column dv0 of token 0
     const size_t ostride = (size_t)H * DV;
-    T* const orow0 = o + ((size_t)b * Tlen * H + h) * DV + dv0;
+    T* const orow0 = o + (((size_t)b * Tlen + (size_t)c0 * C) * H + h) * DV + dv0;
+    const int tlim = Tlen - c0 * C;   // valid positions from the segment start
     auto load = [&](InterOps<T, DK, NTN>& op, int c) {
         inter_load<KIND, T, DK, DV, NTN>(op, chain_rec + (size_t)c * R::BYTES, wave, lane, dv0);
     };
@@ -211,7 +215,7 @@ __global__ __launch_bounds__(kThreads) void inter_kernel(const uint8_t* __restri
                 // staging row rr holds position 32*kbP + prow(halfP, rr)
                 const int pos = 32 * kbP + prow(halfP, rr);
                 const Frag<T> f = ld_frag(&sO[wave][rr][8 * sg]);
-                if (!GUARD || c * C + pos < Tlen)
+                if (!GUARD || c * C + pos < tlim)
                     st_frag(orow0 + ((size_t)c * C + pos) * ostride + 8 * sg, f);
             }
         }
@@ -238,13 +242,13 @@ __global__ __launch_bounds__(kThreads) void inter_kernel(const uint8_t* __restri
     // draining the memory counter at control-flow joins.
     using Full = std::integral_constant<bool, false>;
     using Tail = std::integral_constant<bool, true>;
-    const int last = NT - 1;
+    const int last = nseg - 1;
     auto cl = [&](int c) { return c < last ? c : last; };
     static_assert(NBUF == 2 || NBUF == 3, "prefetch depth");
     if constexpr (NBUF == 3) {
         InterOps<T, DK, NTN> b0, b1, b2;
         int c = 0;
-        if (NT > 0) {
+        if (nseg > 0) {
             load(b0, 0);
             load(b1, cl(1));
             for (; c + 3 <= last; c += 3) {
@@ -267,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void inter_kernel(const uint8_t* __restri
     } else {
         InterOps<T, DK, NTN> b0, b1;
         int c = 0;
-        if (NT > 0) {
+        if (nseg > 0) {
             load(b0, 0);
             for (; c + 2 <= last; c += 2) {
                 load(b1, cl(c + 1)); step(c, b0, Full{});

@@ -85,7 +85,7 @@ template <int KIND, typename T, int DK, int DV>
 __global__ __launch_bounds__(kThreads) void intra_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, uint8_t* __restrict__ ws,
-    unsigned* __restrict__ flags, int Tlen, int H, int NT)
+    unsigned* __restrict__ flags, int Tlen, int H, int NT, int c0)
 {
     using Cfg = IntraCfg<KIND, T, DK, DV>;
     using R = Rec<T, DK, DV>;
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, grp = lane >> 4;
-    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int c = c0 + blockIdx.x, h = blockIdx.y, b = blockIdx.z;   // chunks c0.. of a segment
     const int t0 = c * C;
     const int nvalid = min(C, Tlen - t0);
     const size_t row0 = ((size_t)b * Tlen + t0) * H + h;   // token-head index of position 0
