@@ -117,6 +117,30 @@ __device__ __forceinline__ void st4(float* p, const float* in) {
     *reinterpret_cast<float4*>(p) = make_float4(in[0], in[1], in[2], in[3]);
 }
 
+// Four contiguous elements kept in their storage type, so that a prefetch
+// does not force an early wait for the load (the conversion to float happens
+// at the use).
+template <typename T> struct Raw4;
+template <> struct Raw4<bf16> {
+    bf16x4 v;
+    __device__ void load(const bf16* p) { v = *reinterpret_cast<const bf16x4*>(p); }
+    __device__ float operator[](int i) const { return (float)v[i]; }
+};
+template <> struct Raw4<float> {
+    float4 v;
+    __device__ void load(const float* p) { v = *reinterpret_cast<const float4*>(p); }
+    __device__ float operator[](int i) const { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
+};
+
+// Copy of four contiguous elements as one access (8 bytes for bf16, 16 for
+// fp32; both addresses aligned to that size).
+__device__ __forceinline__ void cp4(bf16* dst, const bf16* src) {
+    *reinterpret_cast<bf16x4*>(dst) = *reinterpret_cast<const bf16x4*>(src);
+}
+__device__ __forceinline__ void cp4(float* dst, const float* src) {
+    *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(src);
+}
+
 // Workgroup barrier that orders LDS traffic only: waits for this wave's LDS
 // operations, then meets the other waves.  Unlike __syncthreads() it does not
 // wait for outstanding global loads and stores, so prefetches and record

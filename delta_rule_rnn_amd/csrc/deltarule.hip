@@ -80,10 +80,10 @@ int pick_ntn(int chains, int D) {
     return ntn;
 }
 
-int pick_nbuf() {
-    if (const char* e = getenv("DR_INTER_NBUF")) {
+int pick_pfd() {
+    if (const char* e = getenv("DR_INTER_PFD")) {
         const int v = atoi(e);
-        if (v == 2 || v == 3) return v;
+        if (v == 0 || v == 2) return v;
     }
     return 2;
 }
@@ -118,30 +118,34 @@ dr_status launch_intra(const Problem& p, int c0, int n, hipStream_t st) {
 }
 
 // ---- state pass + output over chunks [c0, c0 + n) ------------------------
-template <int KIND, typename E, int D, int NTN, int NBUF>
-dr_status launch_inter_n(const Problem& p, const float* h0, float* hT, int c0, int n, hipStream_t st) {
+// L2 prefetch distance of the state pass in chunks (0 = no prefetch wave);
+// DR_INTER_PFD=0 switches it off for comparison.
+template <int KIND, typename E, int D, int NTN, int PFD>
+dr_status launch_inter_p(const Problem& p, const float* h0, float* hT, int c0, int n, hipStream_t st) {
     constexpr int NV = D / (16 * NTN);
     dim3 grid(p.B * p.H * NV);
-    hipLaunchKernelGGL((dr::inter_kernel<KIND, E, D, D, NTN, NBUF>), grid, dim3(dr::kThreads), 0, st,
-                       p.ws, h0, static_cast<E*>(p.o), hT, p.T, p.H, p.NT, c0, n);
+    hipLaunchKernelGGL((dr::inter_kernel<KIND, E, D, D, NTN, PFD>), grid, dim3(dr::inter_threads<PFD>()), 0,
+                       st, p.ws, h0, static_cast<E*>(p.o), hT, p.T, p.H, p.NT, c0, n);
     return check_launch();
+}
+
+// The ninth (prefetch) wave lowers the register budget of every wave to 168;
+// the fp32 and 64-column variants need more, so they run without it.
+template <int KIND, typename E, int D, int NTN>
+dr_status launch_inter_n(const Problem& p, const float* h0, float* hT, int c0, int n, hipStream_t st) {
+    if constexpr (sizeof(E) == 2 && NTN <= 2)
+        if (pick_pfd() != 0) return launch_inter_p<KIND, E, D, NTN, 2>(p, h0, hT, c0, n, st);
+    return launch_inter_p<KIND, E, D, NTN, 0>(p, h0, hT, c0, n, st);
 }
 
 template <int KIND, typename E, int D>
 dr_status launch_inter_t(const Problem& p, const float* h0, float* hT, int c0, int n, hipStream_t st) {
     const int ntn = pick_ntn(p.B * p.H, D);
-    // fp32 operands are twice as large: one chunk of prefetch only
-    const int nbuf = sizeof(E) == 4 ? 2 : pick_nbuf();
-    if constexpr (sizeof(E) == 2) {
-        if (nbuf == 3) {
-            if (ntn == 1) return launch_inter_n<KIND, E, D, 1, 3>(p, h0, hT, c0, n, st);
-            if (ntn == 2) return launch_inter_n<KIND, E, D, 2, 3>(p, h0, hT, c0, n, st);
-            // 64 columns with three buffers does not fit in registers: two buffers
-        }
-    }
-    if (ntn == 1) return launch_inter_n<KIND, E, D, 1, 2>(p, h0, hT, c0, n, st);
-    if (ntn == 2) return launch_inter_n<KIND, E, D, 2, 2>(p, h0, hT, c0, n, st);
-    return launch_inter_n<KIND, E, D, 4, 2>(p, h0, hT, c0, n, st);
+    if (ntn == 1) return launch_inter_n<KIND, E, D, 1>(p, h0, hT, c0, n, st);
+    // fp32 operands at 64 columns do not fit in registers: at most 32 columns
+    if (ntn == 2 || sizeof(E) == 4) return launch_inter_n<KIND, E, D, 2>(p, h0, hT, c0, n, st);
+    if constexpr (sizeof(E) == 2) return launch_inter_n<KIND, E, D, 4>(p, h0, hT, c0, n, st);
+    return DR_ERR_UNSUPPORTED;
 }
 
 template <int KIND>

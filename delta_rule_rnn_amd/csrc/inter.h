@@ -15,12 +15,26 @@
 // applied before the accumulation, [SD] 5.2 ordering rules 1 and 2).
 //
 // Work split.  A workgroup owns one (b, h) chain and DVS = 16*NTN value
-// columns (value columns evolve independently, [KDA] 3.4).  Its 4 waves split
-// the rows: wave w produces 16 positions of Vnew and O (rows 32*(w/2) +
-// prow(w%2, r)) and 32 key rows of S (rows 32w..32w+31).  Two LDS exchanges
-// per chunk hand Vnew and S to every wave as natural B fragments.  The
-// operands of the next NBUF-1 chunks are prefetched into registers while the
-// current chunk computes.
+// columns (value columns evolve independently, [KDA] 3.4).  It has 8 waves:
+//   recurrence waves 0..3 compute Vnew for 16 positions each (rows
+//     32*(w/2) + prow(w%2, r)) and own 32 key rows of S (rows 32w..32w+31);
+//   output waves 4..7 compute O for the same 16 positions of wave w-4.
+// The output is off the recurrence's critical path: it only reads the state
+// and Vnew that the recurrence waves publish in LDS.  Per chunk there are two
+// barriers:
+//   phase A (after the previous chunk's second barrier): sS holds the entry
+//     state; recurrence waves form Vnew into sV, output waves form Q~ S;
+//   barrier 1;
+//   phase B: recurrence waves update S and publish it to sS (the output
+//     waves finished reading sS before barrier 1); output waves add Aqk Vnew
+//     (sV) and store O;
+//   barrier 2.
+// Each wave prefetches its own operands one chunk ahead into registers, and a
+// ninth wave pulls the record lines of later chunks into L2 (PFD below).
+//
+// The output waves compute O^T = S^T Q~^T + Vnew^T Aqk^T (operands swapped):
+// the accumulator then gives each lane 4 consecutive value columns of one
+// position, which leave as one 8-byte (bf16) or 16-byte (fp32) store.
 //
 // Block mapping: the NV = Dv/DVS workgroups of a chain read the same W, Q~,
 // Kbar, Aqk; consecutive logical ids are placed on the same XCD (hardware
@@ -33,38 +47,40 @@
 
 namespace dr {
 
+constexpr int kInterThreads = 512;   // 4 recurrence + 4 output waves
+
+// Operands of one chunk for a recurrence wave.
 template <typename T, int DK, int NTN>
-struct InterOps {
+struct RecurOps {
     static constexpr int NKB = DK / 32;
     Frag<T> w[NKB];        // W rows of this wave's positions
-    Frag<T> qt[NKB];       // Q~ rows of this wave's positions
-    Frag<T> aqk[2];        // Aqk rows, key blocks 0..1
     Frag<T> kb[2][2];      // Kbar^T rows (half, key block) of this wave's S rows
-    float u[NTN][4];       // U (or V) at this lane's 4 positions, per n-tile
+    Raw4<T> u[NTN];        // U (or V) at this lane's 4 positions, per n-tile
     float phi[2][4];       // phi at this lane's S rows (half, i)
 };
 
+// Operands of one chunk for an output wave.
+template <typename T, int DK>
+struct OutOps {
+    static constexpr int NKB = DK / 32;
+    Frag<T> qt[NKB];       // Q~ rows of this wave's positions
+    Frag<T> aqk[2];        // Aqk rows, key blocks 0..1
+};
+
+// All record blocks are in fragment order: lane l's 8 (or 4) elements are
+// contiguous and a wave-wide load is one contiguous run.
 template <int KIND, typename T, int DK, int DV, int NTN>
-__device__ __forceinline__ void inter_load(InterOps<T, DK, NTN>& op, const uint8_t* recb, int wave,
+__device__ __forceinline__ void load_recur(RecurOps<T, DK, NTN>& op, const uint8_t* recb, int wave,
                                            int lane, int dv0)
 {
     using R = Rec<T, DK, DV>;
-    constexpr int C = kChunk;
     constexpr int NKB = DK / 32;
-    constexpr bool DELTA = KIND != KIND_LA;
     const T* base = reinterpret_cast<const T*>(recb);
-    // all blocks are in fragment order: lane l's 8 (or 4) elements are
-    // contiguous and a wave-wide load is one contiguous run
+    if constexpr (KIND != KIND_LA) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-        const size_t f = ((size_t)(wave * NKB + kb) * 64 + lane) * 8;
-        if constexpr (DELTA) op.w[kb] = ld_frag(base + R::W + f);
-        op.qt[kb] = ld_frag(base + R::QT + f);
+        for (int kb = 0; kb < NKB; ++kb)
+            op.w[kb] = ld_frag(base + R::W + ((size_t)(wave * NKB + kb) * 64 + lane) * 8);
     }
-    // both key blocks: the record holds zeros above the diagonal, so the
-    // block past this wave's positions contributes nothing
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) op.aqk[kb] = ld_frag(base + R::AQK + ((size_t)(wave * 2 + kb) * 64 + lane) * 8);
     if (NKB >= 4 || wave < NKB) {
         const float* phi = reinterpret_cast<const float*>(recb + R::PHI_BYTE);
         const int grp = lane >> 4;
@@ -78,15 +94,117 @@ __device__ __forceinline__ void inter_load(InterOps<T, DK, NTN>& op, const uint8
     }
 #pragma unroll
     for (int n = 0; n < NTN; ++n)
-        ld4(base + R::UT + ((size_t)((dv0 / 16 + n) * 4 + wave) * 64 + lane) * 4, op.u[n]);
+        op.u[n].load(base + R::UT + ((size_t)((dv0 / 16 + n) * 4 + wave) * 64 + lane) * 4);
 }
 
-template <int KIND, typename T, int DK, int DV, int NTN, int NBUF>
-__global__ __launch_bounds__(kThreads) void inter_kernel(const uint8_t* __restrict__ ws,
-                                                         const float* __restrict__ h0,
-                                                         T* __restrict__ o, float* __restrict__ hT,
-                                                         int Tlen, int H, int NT, int c0,
-                                                         int nseg)
+template <typename T, int DK, int DV>
+__device__ __forceinline__ void load_out(OutOps<T, DK>& op, const uint8_t* recb, int wave, int lane)
+{
+    using R = Rec<T, DK, DV>;
+    constexpr int NKB = DK / 32;
+    const T* base = reinterpret_cast<const T*>(recb);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+        op.qt[kb] = ld_frag(base + R::QT + ((size_t)(wave * NKB + kb) * 64 + lane) * 8);
+    // both key blocks: the record holds zeros above the diagonal, so the
+    // block past this wave's positions contributes nothing
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) op.aqk[kb] = ld_frag(base + R::AQK + ((size_t)(wave * 2 + kb) * 64 + lane) * 8);
+}
+
+// Asynchronous copy global -> LDS of BYTES bytes per lane from the lane's own
+// address; lane l's bytes land at lds + l*BYTES (lds is the same for every
+// lane).
+template <int BYTES>
+__device__ __forceinline__ void copy_to_lds_lane(const uint8_t* gsrc_lane, uint8_t* lds) {
+    static_assert(BYTES == 4 || BYTES == 16, "copy width");
+    const auto src = (const __attribute__((address_space(1))) void*)gsrc_lane;
+    const auto dst = (__attribute__((address_space(3))) void*)lds;
+    if constexpr (BYTES == 16) __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+    else __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+}
+
+// Wait until this wave has no outstanding vector memory operation (the
+// copies above count there until their data is in LDS).
+__device__ __forceinline__ void wait_vm_all() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Body of the L2 prefetch wave: for every chunk step c of the workgroup
+// (two barriers each, after the one that publishes the initial state), touch
+// this workgroup's share of the record lines of chunk c+PFD: one 4-byte copy
+// per 128-byte line into a scratch LDS word.  Lines are split between the NV
+// workgroups of a chain, which share one XCD's L2.  The wave never reads the
+// copies; it drains them before it ends.
+template <typename T, int DK, int DV, int NV, int PFD>
+__device__ __forceinline__ void l2_prefetch_wave(const uint8_t* chain_rec, int nseg, int slice, int lane,
+                                                 uint8_t* sink)
+{
+    using R = Rec<T, DK, DV>;
+    constexpr int LINES = (int)(R::BYTES / 128);
+    constexpr int PER = (LINES + NV - 1) / NV;          // lines of this workgroup
+    lds_barrier();   // initial state published
+    for (int c = 0; c < nseg; ++c) {
+        const int cp = c + PFD;
+        if (cp < nseg) {
+            const uint8_t* rec = chain_rec + (size_t)cp * R::BYTES;
+#pragma unroll
+            for (int i = 0; i < (PER + 63) / 64; ++i) {
+                const int line = (i * 64 + lane) * NV + slice;
+                if (i * 64 + lane < PER && line < LINES) copy_to_lds_lane<4>(rec + (size_t)line * 128, sink);
+            }
+        }
+        lds_barrier();
+        lds_barrier();
+    }
+    wait_vm_all();
+}
+
+// Runs step(c, ops, guard) for c = 0..n-1 with the operands of chunk c loaded
+// one chunk ahead into a pair of register buffers.  Every load inside the
+// steady-state loop is unconditional (the prefetch index is clamped to the
+// last chunk) and only the last step gets the Tail guard tag, so the compiler
+// can keep prefetches in flight across steps instead of draining the memory
+// counter at control-flow joins.  (A third buffer was measured slower: the
+// L2 prefetch wave covers the latency that deeper register prefetch would.)
+template <typename Ops, typename Load, typename Step>
+__device__ __forceinline__ void prefetch_pair(int n, Load&& load, Step&& step)
+{
+    using Full = std::integral_constant<bool, false>;
+    using Tail = std::integral_constant<bool, true>;
+    if (n <= 0) return;
+    const int last = n - 1;
+    auto cl = [&](int c) { return c < last ? c : last; };
+    int c = 0;
+    Ops b0, b1;
+    load(b0, 0);
+    for (; c + 2 <= last; c += 2) {
+        load(b1, cl(c + 1)); step(c, b0, Full{});
+        load(b0, cl(c + 2)); step(c + 1, b1, Full{});
+    }
+    if (c == last) {
+        step(c, b0, Tail{});
+    } else {
+        load(b1, c + 1);
+        step(c, b0, Full{});
+        step(c + 1, b1, Tail{});
+    }
+}
+
+// With PFD > 0 a ninth wave touches this workgroup's share of the record
+// lines of chunk c+PFD while the others work on chunk c: one 4-byte copy per
+// 128-byte line into a scratch LDS word, so the lines are in L2 by the time
+// the compute waves load them.  The NV workgroups of a chain share the
+// chain's L2 (same XCD) and split the lines between them.
+template <int PFD>
+constexpr int inter_threads() { return PFD > 0 ? kInterThreads + 64 : kInterThreads; }
+
+template <int KIND, typename T, int DK, int DV, int NTN, int PFD>
+__global__ __launch_bounds__(inter_threads<PFD>()) void inter_kernel(const uint8_t* __restrict__ ws,
+                                                              const float* __restrict__ h0,
+                                                              T* __restrict__ o, float* __restrict__ hT,
+                                                              int Tlen, int H, int NT, int c0,
+                                                              int nseg)
 {
     using R = Rec<T, DK, DV>;
     constexpr int C = kChunk;
@@ -99,15 +217,14 @@ __global__ __launch_bounds__(kThreads) void inter_kernel(const uint8_t* __restri
     // B-fragment exchange buffers: [block][n-tile][lane][8 slots]
     __shared__ __attribute__((aligned(16))) T sS[NKB][NTN][64][8];
     __shared__ __attribute__((aligned(16))) T sV[2][NTN][64][8];
-    // per-wave output staging: 16 positions x 16*NTN columns, one row per
-    // position, so the tile leaves as 16-byte row segments
-    constexpr int LDO = 16 * NTN + 8;
-    __shared__ __attribute__((aligned(16))) T sO[4][16][LDO];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const bool recur = tid < 256;               // waves 0..3
+    const int wave = (tid >> 6) & 3;            // position group of either role
+    __shared__ __attribute__((aligned(16))) uint8_t sink[PFD > 0 ? 256 : 16];
     const int r16 = lane & 15, grp = lane >> 4;
     const int kbP = wave >> 1, halfP = wave & 1;
-    const bool ownS = NKB >= 4 || wave < NKB;   // Dk = 128: every wave owns 32 state rows
+    const bool ownS = recur && (NKB >= 4 || wave < NKB);   // Dk = 128: every recurrence wave
 
     const int G = gridDim.x, bid = blockIdx.x;
     const int logical = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
@@ -115,189 +232,161 @@ __global__ __launch_bounds__(kThreads) void inter_kernel(const uint8_t* __restri
     const int b = chain / H, h = chain % H;
     const int dv0 = slice * DVS;
 
-    // ---- initial state --------------------------------------------------
-    f32x4 S[2][NTN];
-#pragma unroll
-    for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int n = 0; n < NTN; ++n) {
-            f32x4 s = {0.f, 0.f, 0.f, 0.f};
-            if (ownS && h0 != nullptr) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int dk = 32 * wave + 8 * grp + 4 * half + i;
-                    s[i] = h0[(((size_t)b * H + h) * DK + dk) * DV + dv0 + 16 * n + r16];
-                }
-            }
-            S[half][n] = s;
-        }
-    auto publish_state = [&]() {
-        if (ownS) {
-#pragma unroll
-            for (int n = 0; n < NTN; ++n)
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    float tmp[4] = {S[half][n][0], S[half][n][1], S[half][n][2], S[half][n][3]};
-                    st4(&sS[wave][n][lane][4 * half], tmp);
-                }
-        }
-    };
-    publish_state();
-    lds_barrier();
-
-    // this launch runs chunks c0 .. c0+nseg-1 of the chain (a segment; the
-    // state enters through h0 and leaves through hT)
+    // this launch runs chunks c0 .. c0+nseg-1 of the chain; the state enters
+    // through h0 and leaves through hT
     const uint8_t* chain_rec = ws + (((size_t)b * H + h) * (size_t)NT + c0) * R::BYTES;
-    // output rows are H*DV elements apart; orow0 = column dv0 of token 0
-    const size_t ostride = (size_t)H * DV;
-    T* const orow0 = o + (((size_t)b * Tlen + (size_t)c0 * C) * H + h) * DV + dv0;
-    const int tlim = Tlen - c0 * C;   // valid positions from the segment start
-    auto load = [&](InterOps<T, DK, NTN>& op, int c) {
-        inter_load<KIND, T, DK, DV, NTN>(op, chain_rec + (size_t)c * R::BYTES, wave, lane, dv0);
-    };
 
-    // One chunk step with the operands in `cur` (loaded earlier).
-    auto step = [&](int c, const InterOps<T, DK, NTN>& cur, auto guard_tag) {
-        constexpr bool GUARD = decltype(guard_tag)::value;
-        // entry-state fragments
-        Frag<T> fS[NKB][NTN];
+    auto fS_read = [&](Frag<T> (&fS)[NKB][NTN]) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int n = 0; n < NTN; ++n) fS[kb][n] = ld_frag(&sS[kb][n][lane][0]);
-
-        f32x4 P[NTN], O[NTN];
-#pragma unroll
-        for (int n = 0; n < NTN; ++n) {
-            P[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-            O[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int n = 0; n < NTN; ++n) {
-                if constexpr (DELTA) mma(P[n], cur.w[kb], fS[kb][n]);
-                mma(O[n], cur.qt[kb], fS[kb][n]);
-            }
-        // Vnew at this lane's 4 positions
-#pragma unroll
-        for (int n = 0; n < NTN; ++n) {
-            float vn[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) vn[i] = DELTA ? cur.u[n][i] - P[n][i] : cur.u[n][i];
-            st4(&sV[kbP][n][lane][4 * halfP], vn);
-        }
-        lds_barrier();
-
-        Frag<T> fV[2][NTN];
+    };
+    auto fV_read = [&](Frag<T> (&fV)[2][NTN]) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int n = 0; n < NTN; ++n) fV[kb][n] = ld_frag(&sV[kb][n][lane][0]);
-
-        // intra-chunk term (Aqk is zero past the diagonal)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int n = 0; n < NTN; ++n) mma(O[n], cur.aqk[kb], fV[kb][n]);
-        // store O.  The accumulator gives this lane 4 rows of one column; the
-        // tile goes through this wave's own LDS staging area (no other wave
-        // touches it, so no barrier) and leaves as 16-byte row segments.
-        {
-#pragma unroll
-            for (int n = 0; n < NTN; ++n)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sO[wave][4 * grp + i][16 * n + r16] = from_f<T>(O[n][i]);
-            constexpr int SEGS = 16 * NTN / 8;          // 8-element segments per row
-#pragma unroll
-            for (int it = lane; it < 16 * SEGS; it += 64) {
-                const int rr = it / SEGS, sg = it % SEGS;
-                // staging row rr holds position 32*kbP + prow(halfP, rr)
-                const int pos = 32 * kbP + prow(halfP, rr);
-                const Frag<T> f = ld_frag(&sO[wave][rr][8 * sg]);
-                if (!GUARD || c * C + pos < tlim)
-                    st_frag(orow0 + ((size_t)c * C + pos) * ostride + 8 * sg, f);
-            }
-        }
-        // state update: decay first, then accumulate
-        if (ownS) {
-#pragma unroll
-            for (int half = 0; half < 2; ++half)
-#pragma unroll
-                for (int n = 0; n < NTN; ++n) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) S[half][n][i] *= cur.phi[half][i];
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb) mma(S[half][n], cur.kb[half][kb], fV[kb][n]);
-                }
-        }
-        publish_state();
-        lds_barrier();
     };
 
-    // Operands are loaded NBUF-1 chunks ahead into a ring of register buffers.  Every load and
-    // store inside the steady-state loop is unconditional (prefetch indices are
-    // clamped to the last chunk, only the last chunk guards its output rows),
-    // so the compiler can keep the prefetches in flight across steps instead of
-    // draining the memory counter at control-flow joins.
-    using Full = std::integral_constant<bool, false>;
-    using Tail = std::integral_constant<bool, true>;
-    const int last = nseg - 1;
-    auto cl = [&](int c) { return c < last ? c : last; };
-    static_assert(NBUF == 2 || NBUF == 3, "prefetch depth");
-    if constexpr (NBUF == 3) {
-        InterOps<T, DK, NTN> b0, b1, b2;
-        int c = 0;
-        if (nseg > 0) {
-            load(b0, 0);
-            load(b1, cl(1));
-            for (; c + 3 <= last; c += 3) {
-                load(b2, cl(c + 2)); step(c, b0, Full{});
-                load(b0, cl(c + 3)); step(c + 1, b1, Full{});
-                load(b1, cl(c + 4)); step(c + 2, b2, Full{});
-            }
-            if (c == last) {
-                step(c, b0, Tail{});
-            } else if (c + 1 == last) {
-                step(c, b0, Full{});
-                step(c + 1, b1, Tail{});
-            } else {
-                load(b2, c + 2);
-                step(c, b0, Full{});
-                step(c + 1, b1, Full{});
-                step(c + 2, b2, Tail{});
-            }
-        }
-    } else {
-        InterOps<T, DK, NTN> b0, b1;
-        int c = 0;
-        if (nseg > 0) {
-            load(b0, 0);
-            for (; c + 2 <= last; c += 2) {
-                load(b1, cl(c + 1)); step(c, b0, Full{});
-                load(b0, cl(c + 2)); step(c + 1, b1, Full{});
-            }
-            if (c == last) {
-                step(c, b0, Tail{});
-            } else {
-                load(b1, c + 1);
-                step(c, b0, Full{});
-                step(c + 1, b1, Tail{});
-            }
+    if constexpr (PFD > 0) {
+        if (tid >= kInterThreads) {
+            l2_prefetch_wave<T, DK, DV, NV, PFD>(chain_rec, nseg, slice, lane, sink);
+            return;
         }
     }
-
-    // ---- final state -----------------------------------------------------
-    if (ownS && hT != nullptr) {
+    if (recur) {
+        // ---- recurrence waves ---------------------------------------------
+        f32x4 S[2][NTN];
 #pragma unroll
         for (int half = 0; half < 2; ++half)
 #pragma unroll
-            for (int n = 0; n < NTN; ++n)
+            for (int n = 0; n < NTN; ++n) {
+                f32x4 s = {0.f, 0.f, 0.f, 0.f};
+                if (ownS && h0 != nullptr) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int dk = 32 * wave + 8 * grp + 4 * half + i;
-                    hT[(((size_t)b * H + h) * DK + dk) * DV + dv0 + 16 * n + r16] = S[half][n][i];
+                    for (int i = 0; i < 4; ++i) {
+                        const int dk = 32 * wave + 8 * grp + 4 * half + i;
+                        s[i] = h0[(((size_t)b * H + h) * DK + dk) * DV + dv0 + 16 * n + r16];
+                    }
                 }
+                S[half][n] = s;
+            }
+        auto publish_state = [&]() {
+            if (ownS) {
+#pragma unroll
+                for (int n = 0; n < NTN; ++n)
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        float tmp[4] = {S[half][n][0], S[half][n][1], S[half][n][2], S[half][n][3]};
+                        st4(&sS[wave][n][lane][4 * half], tmp);
+                    }
+            }
+        };
+        publish_state();
+        lds_barrier();
+
+        using Ops = RecurOps<T, DK, NTN>;
+        auto load = [&](Ops& op, int c) {
+            load_recur<KIND, T, DK, DV, NTN>(op, chain_rec + (size_t)c * R::BYTES, wave, lane, dv0);
+        };
+        auto step = [&](int, const Ops& cur, auto) {
+            // phase A: Vnew at this lane's 4 positions
+            f32x4 P[NTN];
+#pragma unroll
+            for (int n = 0; n < NTN; ++n) P[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (DELTA) {
+                Frag<T> fS[NKB][NTN];
+                fS_read(fS);
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int n = 0; n < NTN; ++n) mma(P[n], cur.w[kb], fS[kb][n]);
+            }
+#pragma unroll
+            for (int n = 0; n < NTN; ++n) {
+                float vn[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) vn[i] = cur.u[n][i] - P[n][i];
+                st4(&sV[kbP][n][lane][4 * halfP], vn);
+            }
+            lds_barrier();
+            // phase B: state update, decay first, then accumulate
+            Frag<T> fV[2][NTN];
+            fV_read(fV);
+            if (ownS) {
+#pragma unroll
+                for (int half = 0; half < 2; ++half)
+#pragma unroll
+                    for (int n = 0; n < NTN; ++n) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) S[half][n][i] *= cur.phi[half][i];
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb) mma(S[half][n], cur.kb[half][kb], fV[kb][n]);
+                    }
+            }
+            publish_state();
+            lds_barrier();
+        };
+        prefetch_pair<Ops>(nseg, load, step);
+
+        // ---- final state ---------------------------------------------------
+        if (ownS && hT != nullptr) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+#pragma unroll
+                for (int n = 0; n < NTN; ++n)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int dk = 32 * wave + 8 * grp + 4 * half + i;
+                        hT[(((size_t)b * H + h) * DK + dk) * DV + dv0 + 16 * n + r16] = S[half][n][i];
+                    }
+        }
+    } else {
+        // ---- output waves ---------------------------------------------------
+        lds_barrier();   // initial state published
+        // this lane's output row: position pw(wave, r16), columns 4*grp.. of each n-tile
+        const int pos = 32 * kbP + prow(halfP, r16);
+        const size_t ostride = (size_t)H * DV;
+        T* const orow = o + (((size_t)b * Tlen + (size_t)c0 * C + pos) * H + h) * DV + dv0 + 4 * grp;
+        const int tlim = Tlen - c0 * C;   // valid positions from the segment start
+
+        using Ops = OutOps<T, DK>;
+        auto load = [&](Ops& op, int c) {
+            load_out<T, DK, DV>(op, chain_rec + (size_t)c * R::BYTES, wave, lane);
+        };
+        auto step = [&](int c, const Ops& cur, auto guard_tag) {
+            constexpr bool GUARD = decltype(guard_tag)::value;
+            // phase A: O^T = S^T Q~^T with the entry state
+            f32x4 Ot[NTN];
+#pragma unroll
+            for (int n = 0; n < NTN; ++n) Ot[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+            {
+                Frag<T> fS[NKB][NTN];
+                fS_read(fS);
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int n = 0; n < NTN; ++n) mma(Ot[n], fS[kb][n], cur.qt[kb]);
+            }
+            lds_barrier();
+            // phase B: intra-chunk term (Aqk is zero past the diagonal), store
+            Frag<T> fV[2][NTN];
+            fV_read(fV);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int n = 0; n < NTN; ++n) mma(Ot[n], fV[kb][n], cur.aqk[kb]);
+            if (!GUARD || c * C + pos < tlim) {
+#pragma unroll
+                for (int n = 0; n < NTN; ++n) {
+                    const float v4[4] = {Ot[n][0], Ot[n][1], Ot[n][2], Ot[n][3]};
+                    st4(orow + (size_t)c * C * ostride + 16 * n, v4);
+                }
+            }
+            lds_barrier();
+        };
+        prefetch_pair<Ops>(nseg, load, step);
     }
 }
 

@@ -150,6 +150,29 @@ def test_resume_is_exact():
     assert torch.equal(h2, hT)
 
 
+
+@pytest.mark.parametrize("kind", ["kda", "gdn", "decay_la"])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_state_pass_layouts_agree(kind, dt, monkeypatch):
+    """The state pass may give each workgroup 16, 32 or 64 value columns and
+    may run an L2 prefetch wave; the arithmetic of every column is the same
+    in all of them, so results are bit-identical (small problems pick 16
+    columns on their own, so the others are forced here)."""
+    dra = _ops()
+    w = Workload(f"{kind}_layouts", kind, dt, B=2, H=3, T=64 * 5 + 9, Dk=128, Dv=128, h0_std=0.1, seed=9)
+    x = to_dev(generate(w))
+    monkeypatch.setenv("DR_INTER_NTN", "1")
+    monkeypatch.setenv("DR_INTER_PFD", "0")
+    o1, h1 = dra.forward(kind, x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"])
+    torch.cuda.synchronize()
+    for ntn in ("1", "2", "4"):
+        for pfd in ("0", "2"):
+            monkeypatch.setenv("DR_INTER_NTN", ntn)
+            monkeypatch.setenv("DR_INTER_PFD", pfd)
+            o2, h2 = dra.forward(kind, x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"])
+            torch.cuda.synchronize()
+            assert torch.equal(o2, o1) and torch.equal(h2, h1), f"columns {16 * int(ntn)}, prefetch {pfd}"
+
 def test_deterministic():
     w = Workload("gdn_det", "gdn", "bf16", B=2, H=4, T=500, Dk=128, Dv=128, h0_std=0.1, seed=6)
     x = generate(w)
