@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace dr {
 
 typedef __bf16 bf16;
@@ -36,6 +38,12 @@ constexpr int kThreads = 256;  // 4 waves per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 
 enum Kind { KIND_KDA = 0, KIND_GDN = 1, KIND_LA = 2 };
+
+// N contiguous elements as one vector value (ext_vector_type: element
+// access with [], one load or store).
+template <typename T, int N> struct VecOf;
+template <int N> struct VecOf<bf16, N> { typedef __bf16 type __attribute__((ext_vector_type(N))); };
+template <int N> struct VecOf<float, N> { typedef float type __attribute__((ext_vector_type(N))); };
 
 template <typename T> struct Frag;
 template <> struct Frag<bf16> { bf16x8 v; };
@@ -185,5 +193,35 @@ struct Rec {
     static constexpr size_t PHI_BYTE = END * sizeof(T);      // [DK] float
     static constexpr size_t BYTES = ((PHI_BYTE + DK * sizeof(float)) + 255) / 256 * 256;
 };
+
+// Runs step(i, ops, guard) for i = 0..n-1 with the operands of step i loaded
+// one step ahead into a pair of register buffers.  Every load inside the
+// steady-state loop is unconditional (the prefetch index is clamped to the
+// last chunk) and only the last step gets the Tail guard tag, so the compiler
+// can keep prefetches in flight across steps instead of draining the memory
+// counter at control-flow joins.
+template <typename Ops, typename Load, typename Step>
+__device__ __forceinline__ void prefetch_pair(int n, Load&& load, Step&& step)
+{
+    using Full = std::integral_constant<bool, false>;
+    using Tail = std::integral_constant<bool, true>;
+    if (n <= 0) return;
+    const int last = n - 1;
+    auto cl = [&](int c) { return c < last ? c : last; };
+    int c = 0;
+    Ops b0, b1;
+    load(b0, 0);
+    for (; c + 2 <= last; c += 2) {
+        load(b1, cl(c + 1)); step(c, b0, Full{});
+        load(b0, cl(c + 2)); step(c + 1, b1, Full{});
+    }
+    if (c == last) {
+        step(c, b0, Tail{});
+    } else {
+        load(b1, c + 1);
+        step(c, b0, Full{});
+        step(c + 1, b1, Tail{});
+    }
+}
 
 }  // namespace dr

@@ -91,10 +91,11 @@ int pick_pfd() {
 // ---- chunk-parallel kernel over chunks [c0, c0 + n) -----------------------
 template <int KIND, typename E, int D>
 dr_status launch_intra_t(const Problem& p, int c0, int n, hipStream_t st) {
-    dim3 grid(n, p.H, p.B);
-    hipLaunchKernelGGL((dr::intra_kernel<KIND, E, D, D>), grid, dim3(dr::kThreads), 0, st,
+    const long long items = (long long)p.B * n * p.H;
+    if (items > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL((dr::intra_kernel<KIND, E, D, D>), dim3((unsigned)items), dim3(dr::kThreads), 0, st,
                        static_cast<const E*>(p.q), static_cast<const E*>(p.k), static_cast<const E*>(p.v),
-                       p.g, p.beta, p.ws, p.flags, p.T, p.H, p.NT, c0);
+                       p.g, p.beta, p.ws, p.flags, p.T, p.H, p.NT, c0, n, p.B);
     return check_launch();
 }
 

@@ -41,8 +41,6 @@
 // dispatches workgroup i to XCD i % 8) so they share that XCD's L2.
 #pragma once
 
-#include <type_traits>
-
 #include "common.h"
 
 namespace dr {
@@ -158,37 +156,6 @@ __device__ __forceinline__ void l2_prefetch_wave(const uint8_t* chain_rec, int n
         lds_barrier();
     }
     wait_vm_all();
-}
-
-// Runs step(c, ops, guard) for c = 0..n-1 with the operands of chunk c loaded
-// one chunk ahead into a pair of register buffers.  Every load inside the
-// steady-state loop is unconditional (the prefetch index is clamped to the
-// last chunk) and only the last step gets the Tail guard tag, so the compiler
-// can keep prefetches in flight across steps instead of draining the memory
-// counter at control-flow joins.  (A third buffer was measured slower: the
-// L2 prefetch wave covers the latency that deeper register prefetch would.)
-template <typename Ops, typename Load, typename Step>
-__device__ __forceinline__ void prefetch_pair(int n, Load&& load, Step&& step)
-{
-    using Full = std::integral_constant<bool, false>;
-    using Tail = std::integral_constant<bool, true>;
-    if (n <= 0) return;
-    const int last = n - 1;
-    auto cl = [&](int c) { return c < last ? c : last; };
-    int c = 0;
-    Ops b0, b1;
-    load(b0, 0);
-    for (; c + 2 <= last; c += 2) {
-        load(b1, cl(c + 1)); step(c, b0, Full{});
-        load(b0, cl(c + 2)); step(c + 1, b1, Full{});
-    }
-    if (c == last) {
-        step(c, b0, Tail{});
-    } else {
-        load(b1, c + 1);
-        step(c, b0, Full{});
-        step(c + 1, b1, Tail{});
-    }
 }
 
 // With PFD > 0 a ninth wave touches this workgroup's share of the record

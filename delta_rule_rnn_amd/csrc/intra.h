@@ -40,16 +40,19 @@ struct IntraCfg {
     static constexpr size_t R_QP = R_KM + mx(SZ_KP, SZ_VT);      // Q~  | later T (fp32)
     static constexpr size_t R_A = R_QP + mx(SZ_KP, SZ_F);        // A   | later W staging
     static constexpr size_t R_SMALL = R_A + mx(SZ_F, SZ_KP);
-    static constexpr int NCP = DK / 2;          // channel pairs
-    static constexpr int NQ = kThreads / NCP;   // position groups
-    static constexpr int PL = C / NQ;           // positions per group
+    // thread layout of the elementwise steps: CPT adjacent channels (one
+    // 8-byte bf16 / 16-byte fp32 load) at PL consecutive positions
+    static constexpr int CPT = DK / 32;         // channels per thread
+    static constexpr int NCG = DK / CPT;        // channel groups (32)
+    static constexpr int NQ = kThreads / NCG;   // position groups (8)
+    static constexpr int PL = C / NQ;           // positions per group (8)
     static constexpr size_t R_BETA = R_SMALL;                        // [C] float
     static constexpr size_t R_GAM = R_BETA + C * sizeof(float);      // [C] float (scalar gates)
     static constexpr size_t R_TOT = R_GAM + C * sizeof(float);       // [NQ][DK] float
     static constexpr size_t BYTES = R_TOT + (size_t)NQ * DK * sizeof(float);
     static_assert(DK == 64 || DK == 128, "DK");
     static_assert(DV == DK, "DV == DK");
-    static_assert(NQ * PL == C, "thread layout");
+    static_assert(NQ * PL == C && PL == 8, "thread layout");
 };
 
 // Lower-triangular 16x16 tiles (ti >= tj) of a 64x64 matrix, in a fixed order.
@@ -81,11 +84,63 @@ __device__ __forceinline__ f32x4 mm16_acc(const float* X, int ldx, f32x4 Z, int 
     return acc;
 }
 
+// Inputs of one chunk as this thread holds them: channels CPT*cg .. +CPT-1
+// (cg = tid % NCG) at positions qg*PL .. qg*PL+PL-1 (qg = tid / NCG), plus
+// beta at position tid
+// and, for scalar gates, the gate at position lane of wave 0.  Rows past the
+// end of a ragged last chunk are loaded from the last valid row (so every load
+// is unconditional) and replaced by zeros where they are used.
 template <int KIND, typename T, int DK, int DV>
-__global__ __launch_bounds__(kThreads) void intra_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, uint8_t* __restrict__ ws,
-    unsigned* __restrict__ flags, int Tlen, int H, int NT, int c0)
+struct IntraIn {
+    using Cfg = IntraCfg<KIND, T, DK, DV>;
+    using VT = typename VecOf<T, Cfg::CPT>::type;
+    using VG = typename VecOf<float, Cfg::CPT>::type;
+    VT kv[Cfg::PL], qv[Cfg::PL], vv[Cfg::PL];
+    VG gv[KIND == KIND_KDA ? Cfg::PL : 1];
+    float bt, gs;
+};
+
+template <int KIND, typename T, int DK, int DV>
+__device__ __forceinline__ void intra_load(IntraIn<KIND, T, DK, DV>& in, const T* __restrict__ q,
+                                           const T* __restrict__ k, const T* __restrict__ v,
+                                           const float* __restrict__ g, const float* __restrict__ beta,
+                                           int b, int c, int h, int Tlen, int H)
+{
+    using In = IntraIn<KIND, T, DK, DV>;
+    using VT = typename In::VT;
+    using VG = typename In::VG;
+    constexpr int C = kChunk;
+    constexpr int NCG = In::Cfg::NCG, PL = In::Cfg::PL, CPT = In::Cfg::CPT;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int t0 = c * C;
+    const int last = min(C, Tlen - t0) - 1;
+    const size_t row0 = ((size_t)b * Tlen + t0) * H + h;
+    const int ch0 = CPT * (tid % NCG), p0 = (tid / NCG) * PL;
+    // gates first, then k and q (step a1 needs them first), v last
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+        const size_t off = (row0 + (size_t)min(p0 + i, last) * H) * DK + ch0;
+        if constexpr (KIND == KIND_KDA) in.gv[i] = *reinterpret_cast<const VG*>(g + off);
+    }
+    if constexpr (KIND != KIND_KDA) in.gs = (tid < 64) ? g[row0 + (size_t)min(lane, last) * H] : 0.f;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+        const size_t off = (row0 + (size_t)min(p0 + i, last) * H) * DK + ch0;
+        in.kv[i] = *reinterpret_cast<const VT*>(k + off);
+        in.qv[i] = *reinterpret_cast<const VT*>(q + off);
+    }
+    if constexpr (KIND != KIND_LA) in.bt = (tid < C) ? beta[row0 + (size_t)min(tid, last) * H] : 0.f;
+#pragma unroll
+    for (int i = 0; i < PL; ++i)
+        in.vv[i] = *reinterpret_cast<const VT*>(v + (row0 + (size_t)min(p0 + i, last) * H) * DV + ch0);
+}
+
+// Steps a1-a3 (and the output operands) of chunk c of head h, batch b, from
+// inputs already in registers; writes the chunk's record.
+template <int KIND, typename T, int DK, int DV>
+__device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, uint8_t* smem,
+                                            uint8_t* __restrict__ ws, unsigned* __restrict__ flags,
+                                            int Tlen, int H, int NT, int b, int c, int h)
 {
     using Cfg = IntraCfg<KIND, T, DK, DV>;
     using R = Rec<T, DK, DV>;
@@ -93,9 +148,11 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(
     constexpr bool DELTA = KIND != KIND_LA;
     constexpr bool PERCH = KIND == KIND_KDA;
     constexpr int LDK = Cfg::LDK, LDF = Cfg::LDF, LDV = Cfg::LDV;
-    constexpr int NCP = Cfg::NCP, PL = Cfg::PL, NQ = Cfg::NQ;
+    constexpr int NCG = Cfg::NCG, PL = Cfg::PL, NQ = Cfg::NQ, CPT = Cfg::CPT;
+    using In = IntraIn<KIND, T, DK, DV>;
+    using VT = typename In::VT;
+    using VG = typename In::VG;
 
-    __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::BYTES];
     T* sKp = reinterpret_cast<T*>(smem + Cfg::R_KP);
     T* sKm = reinterpret_cast<T*>(smem + Cfg::R_KM);
     T* sVt = reinterpret_cast<T*>(smem + Cfg::R_KM);
@@ -109,7 +166,6 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, grp = lane >> 4;
-    const int c = c0 + blockIdx.x, h = blockIdx.y, b = blockIdx.z;   // chunks c0.. of a segment
     const int t0 = c * C;
     const int nvalid = min(C, Tlen - t0);
     const size_t row0 = ((size_t)b * Tlen + t0) * H + h;   // token-head index of position 0
@@ -123,63 +179,68 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(
     T* rU = reinterpret_cast<T*>(recb) + R::UT;
     float* rPhi = reinterpret_cast<float*>(recb + R::PHI_BYTE);
 
-    // ---- P0: every global load of the chunk is issued up front ------------
-    // thread layout: channel pair cp (2 key/value channels), position group qg
-    const int cp = tid % NCP, qg = tid / NCP, ch0 = 2 * cp, p0 = qg * PL;
-    using T2 = typename Pair<T>::type;
-    T2 kv[PL], qv[PL], vv[PL];
-    float2 gv[PERCH ? PL : 1];
+    // ---- P0: this chunk's inputs (loaded one step ahead), rows past the end
+    // of a ragged chunk zeroed
+    const int cg = tid % NCG, qg = tid / NCG, ch0 = CPT * cg, p0 = qg * PL;
+    VT kv[PL], qv[PL], vv[PL];
+    VG gv[PERCH ? PL : 1];
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
-        const int p = p0 + i;
-        if (p < nvalid) {
-            const size_t off = trow(p) * DK + ch0;
-            kv[i] = *reinterpret_cast<const T2*>(k + off);
-            qv[i] = *reinterpret_cast<const T2*>(q + off);
-            vv[i] = *reinterpret_cast<const T2*>(v + trow(p) * DV + ch0);
-            if constexpr (PERCH) gv[i] = *reinterpret_cast<const float2*>(g + off);
-        } else {
-            kv[i] = Pair<T>::zero(); qv[i] = Pair<T>::zero(); vv[i] = Pair<T>::zero();
-            if constexpr (PERCH) gv[i] = make_float2(0.f, 0.f);
-        }
+        const bool ok = p0 + i < nvalid;
+        kv[i] = ok ? in.kv[i] : VT{};
+        qv[i] = ok ? in.qv[i] : VT{};
+        vv[i] = ok ? in.vv[i] : VT{};
+        if constexpr (PERCH) gv[i] = ok ? in.gv[i] : VG{};
     }
-    if (tid < C) sBeta[tid] = (DELTA && tid < nvalid) ? beta[trow(tid)] : 0.f;
+    if (tid < C) sBeta[tid] = (DELTA && tid < nvalid) ? in.bt : 0.f;
 
     // ---- P1: a1 (gamma) + a2 (prep) -------------------------------------
-    float gam[PL][2];
-    float glast[2];
+    float gam[PL][CPT];
+    float glast[CPT];
     if constexpr (PERCH) {
-        // per-channel inclusive scan: each thread owns 2 channels x PL positions
-        float s0 = 0.f, s1 = 0.f;
+        // per-channel inclusive scan: each thread owns CPT channels x PL positions
+        float sc[CPT];
 #pragma unroll
-        for (int i = 0; i < PL; ++i) {
-            s0 += gv[i].x; s1 += gv[i].y;
-            gam[i][0] = s0; gam[i][1] = s1;
+        for (int j = 0; j < CPT; ++j) sc[j] = 0.f;
+#pragma unroll
+        for (int i = 0; i < PL; ++i)
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) {
+                sc[j] += gv[i][j];
+                gam[i][j] = sc[j];
+            }
+        {
+            VG tot;
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) tot[j] = sc[j];
+            *reinterpret_cast<VG*>(sTot + qg * DK + ch0) = tot;
         }
-        sTot[qg * DK + ch0] = s0;
-        sTot[qg * DK + ch0 + 1] = s1;
         lds_barrier();
-        float pre0 = 0.f, pre1 = 0.f, all0 = 0.f, all1 = 0.f;
+        float pre[CPT], all[CPT];
 #pragma unroll
-        for (int j = 0; j < NQ; ++j) {
-            const float a0 = sTot[j * DK + ch0], a1 = sTot[j * DK + ch0 + 1];
-            if (j < qg) { pre0 += a0; pre1 += a1; }
-            if (j < NQ - 1) { all0 += a0; all1 += a1; }
-        }
-        // last position of the chunk: (sum of the first NQ-1 group totals) + last total,
-        // added in the same order as the last group's own prefix + running sum
-        all0 += sTot[(NQ - 1) * DK + ch0];
-        all1 += sTot[(NQ - 1) * DK + ch0 + 1];
-        glast[0] = all0 * kLog2e; glast[1] = all1 * kLog2e;
+        for (int j = 0; j < CPT; ++j) pre[j] = all[j] = 0.f;
 #pragma unroll
-        for (int i = 0; i < PL; ++i) {
-            gam[i][0] = (pre0 + gam[i][0]) * kLog2e;
-            gam[i][1] = (pre1 + gam[i][1]) * kLog2e;
+        for (int jq = 0; jq < NQ; ++jq) {
+            const VG a = *reinterpret_cast<const VG*>(sTot + jq * DK + ch0);
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) {
+                if (jq < qg) pre[j] += a[j];
+                // last position of the chunk: (sum of the first NQ-1 group
+                // totals) + last total, added in the same order as the last
+                // group's own prefix + running sum
+                all[j] += a[j];
+            }
         }
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) glast[j] = all[j] * kLog2e;
+#pragma unroll
+        for (int i = 0; i < PL; ++i)
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) gam[i][j] = (pre[j] + gam[i][j]) * kLog2e;
     } else {
         // scalar gate: wave 0 scans the 64 positions
         if (wave == 0) {
-            float x = (lane < nvalid) ? g[trow(lane)] : 0.f;
+            float x = (lane < nvalid) ? in.gs : 0.f;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float y = __shfl_up(x, off, 64);
@@ -189,44 +250,51 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(
         }
         lds_barrier();
 #pragma unroll
-        for (int i = 0; i < PL; ++i) gam[i][0] = gam[i][1] = sGam[p0 + i];
-        glast[0] = glast[1] = sGam[C - 1];
+        for (int i = 0; i < PL; ++i)
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) gam[i][j] = sGam[p0 + i];
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) glast[j] = sGam[C - 1];
     }
 
     {
-        const float phi0 = __builtin_amdgcn_exp2f(glast[0]);
-        const float phi1 = __builtin_amdgcn_exp2f(glast[1]);
-        float kb[2][PL];
+        float phi[CPT];
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) phi[j] = __builtin_amdgcn_exp2f(glast[j]);
+        float kb[CPT][PL];
         float mxneg = 0.f;
 #pragma unroll
         for (int i = 0; i < PL; ++i) {
             const int p = p0 + i;
-            const float k0 = Pair<T>::lo(kv[i]), k1 = Pair<T>::hi(kv[i]);
-            const float q0 = Pair<T>::lo(qv[i]), q1 = Pair<T>::hi(qv[i]);
-            const float e0 = __builtin_amdgcn_exp2f(gam[i][0]);
-            const float e1 = __builtin_amdgcn_exp2f(gam[i][1]);
             if constexpr (PERCH) {
-                const float ei0 = __builtin_amdgcn_exp2f(-gam[i][0]);
-                const float ei1 = __builtin_amdgcn_exp2f(-gam[i][1]);
-                mxneg = fmaxf(mxneg, fmaxf(-gam[i][0], -gam[i][1]));
-                *reinterpret_cast<T2*>(sKp + p * LDK + ch0) = Pair<T>::make(k0 * e0, k1 * e1);
-                *reinterpret_cast<T2*>(sKm + p * LDK + ch0) = Pair<T>::make(k0 * ei0, k1 * ei1);
-                *reinterpret_cast<T2*>(sQp + p * LDK + ch0) = Pair<T>::make(q0 * e0, q1 * e1);
-                // Kbar = k 2^(gamma_last - gamma) = (k 2^-gamma) 2^gamma_last
-                kb[0][i] = k0 * (ei0 * phi0);
-                kb[1][i] = k1 * (ei1 * phi1);
+                VT kp, km, qp;
+#pragma unroll
+                for (int j = 0; j < CPT; ++j) {
+                    const float kk = (float)kv[i][j], qq = (float)qv[i][j];
+                    const float e = __builtin_amdgcn_exp2f(gam[i][j]);
+                    const float ei = __builtin_amdgcn_exp2f(-gam[i][j]);
+                    mxneg = fmaxf(mxneg, -gam[i][j]);
+                    kp[j] = from_f<T>(kk * e);
+                    km[j] = from_f<T>(kk * ei);
+                    qp[j] = from_f<T>(qq * e);
+                    // Kbar = k 2^(gamma_last - gamma) = (k 2^-gamma) 2^gamma_last
+                    kb[j][i] = kk * (ei * phi[j]);
+                }
+                *reinterpret_cast<VT*>(sKp + p * LDK + ch0) = kp;
+                *reinterpret_cast<VT*>(sKm + p * LDK + ch0) = km;
+                *reinterpret_cast<VT*>(sQp + p * LDK + ch0) = qp;
             } else {
-                *reinterpret_cast<T2*>(sKp + p * LDK + ch0) = kv[i];
-                *reinterpret_cast<T2*>(sQp + p * LDK + ch0) = qv[i];
+                *reinterpret_cast<VT*>(sKp + p * LDK + ch0) = kv[i];
+                *reinterpret_cast<VT*>(sQp + p * LDK + ch0) = qv[i];
                 const float r = __builtin_amdgcn_exp2f(glast[0] - gam[i][0]);   // <= 1
-                kb[0][i] = k0 * r;
-                kb[1][i] = k1 * r;
+#pragma unroll
+                for (int j = 0; j < CPT; ++j) kb[j][i] = (float)kv[i][j] * r;
             }
         }
         // Kbar in fragment order: channel ch is row prow(h, r) of key block
         // ch/32; each run of 8 positions is one 16-byte store
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
+        for (int cc = 0; cc < CPT; ++cc) {
             const int ch = ch0 + cc, qq = ch & 31;
             const int wk = ch >> 5, hh = (qq >> 2) & 1, rr = 4 * (qq >> 3) + (qq & 3);
 #pragma unroll
@@ -239,8 +307,10 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(
             }
         }
         if (qg == 0) {
-            rPhi[ch0] = phi0;
-            rPhi[ch0 + 1] = phi1;
+            VG ph;
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) ph[j] = phi[j];
+            *reinterpret_cast<VG*>(rPhi + ch0) = ph;
         }
         if constexpr (PERCH) {
             if (flags) {
@@ -253,11 +323,11 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(
         if constexpr (!DELTA) {
             // decay_la: the state pass reads V from the U slot (fragment order)
 #pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
+            for (int cc = 0; cc < CPT; ++cc) {
                 const int ch = ch0 + cc;
                 float vt[PL];
 #pragma unroll
-                for (int i = 0; i < PL; ++i) vt[i] = cc ? Pair<T>::hi(vv[i]) : Pair<T>::lo(vv[i]);
+                for (int i = 0; i < PL; ++i) vt[i] = (float)vv[i][cc];
 #pragma unroll
                 for (int i = 0; i < PL; i += 4) {
                     const int p = p0 + i;
@@ -372,13 +442,12 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(
     }
     {
         // beta * V, transposed into sVt[e][p] (the K- region is free now):
-        // each thread writes its PL consecutive positions of 2 value channels
+        // each thread writes its PL consecutive positions of CPT value channels
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
+        for (int cc = 0; cc < CPT; ++cc) {
             float vt[PL];
 #pragma unroll
-            for (int i = 0; i < PL; ++i)
-                vt[i] = sBeta[p0 + i] * (cc ? Pair<T>::hi(vv[i]) : Pair<T>::lo(vv[i]));
+            for (int i = 0; i < PL; ++i) vt[i] = sBeta[p0 + i] * (float)vv[i][cc];
             T* dst = sVt + (ch0 + cc) * LDV + p0;
 #pragma unroll
             for (int i = 0; i < PL; i += 4) st4(dst + i, &vt[i]);
@@ -498,6 +567,28 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(
             st_frag(rW + (size_t)e * 8, ld_frag(sW + pw(w, l & 15) * LDK + 32 * kq + 8 * (l >> 4)));
         }
     }
+}
+
+// One workgroup per item (chunk, head, batch) of chunks c0 .. c0+n-1,
+// numbered heads fastest: the workgroups in flight at any time cover few
+// chunks, so the rows of beta and of scalar gates that neighbouring heads
+// share are fetched while still cached.  (Grouping a chunk's heads on one
+// XCD, or numbering chunks fastest, measured slower.)
+template <int KIND, typename T, int DK, int DV>
+__global__ __launch_bounds__(kThreads, 2) void intra_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, uint8_t* __restrict__ ws,
+    unsigned* __restrict__ flags, int Tlen, int H, int NT, int c0, int n, int B)
+{
+    using Cfg = IntraCfg<KIND, T, DK, DV>;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::BYTES];
+    const unsigned it = blockIdx.x;
+    const int h = (int)(it % (unsigned)H);
+    const unsigned t = it / (unsigned)H;
+    const int c = c0 + (int)(t % (unsigned)n), b = (int)(t / (unsigned)n);
+    IntraIn<KIND, T, DK, DV> in;
+    intra_load<KIND, T, DK, DV>(in, q, k, v, g, beta, b, c, h, Tlen, H);
+    intra_chunk<KIND, T, DK, DV>(in, smem, ws, flags, Tlen, H, NT, b, c, h);
 }
 
 }  // namespace dr
