@@ -40,15 +40,16 @@ def algorithmic(kind: str, w, io_bytes: int):
     """Bytes each kernel must move per token-head (its own inputs and
     outputs) and the method's MFMA flops per token-head (fixed formula)."""
     dk, dv, C = w.Dk, w.Dv, w.C
+    delta = kind != "decay_la"
     gate = 4 * dk if kind == "kda" else 4
-    beta = 4 if kind != "decay_la" else 0
-    # K1 reads q, k, v, g, beta; writes the chunk record (W, Q~, Kbar^T,
-    # Aqk, U^T per row of the chunk, phi per chunk)
-    rec_row = io_bytes * (3 * dk + C + dv) + 4 * dk / C
+    beta = 4 if delta else 0
+    # K1 reads q, k, v, g, beta; writes the chunk record: per row of the
+    # chunk W (delta kinds only), Q~, Kbar^T, Aqk, U^T (V for decay_la), and
+    # phi once per chunk
+    rec_row = io_bytes * ((3 if delta else 2) * dk + C + dv) + 4 * dk / C
     k1 = io_bytes * (2 * dk + dv) + gate + beta + rec_row
     # K2 reads the record, writes o; h0/hT once per chain (negligible)
     k2 = rec_row + io_bytes * dv
-    delta = kind != "decay_la"
     # per token-head MFMA flops of the method: KK^T, QK^T, W/U, A*Vnew, W*S,
     # Kbar^T*Vnew, Q*S and the inverse (full-tile count, fixed formula)
     if delta:
