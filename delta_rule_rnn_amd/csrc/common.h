@@ -149,6 +149,41 @@ __device__ __forceinline__ void cp4(float* dst, const float* src) {
     *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(src);
 }
 
+// Streaming (non-temporal) global accesses for data touched once: the
+// chunk-parallel kernel's inputs and its record (measured a few percent
+// faster than ordinary accesses there; the state pass, whose slices share
+// the record through L2, keeps ordinary loads).  V is a 4-, 8- or 16-byte
+// type; the access goes through a same-size vector of 32-bit words.
+template <int N> struct WordsOf;
+template <> struct WordsOf<4> { typedef unsigned type; };
+template <> struct WordsOf<8> { typedef unsigned type __attribute__((ext_vector_type(2))); };
+template <> struct WordsOf<16> { typedef unsigned type __attribute__((ext_vector_type(4))); };
+template <typename V>
+__device__ __forceinline__ V ld_stream(const V* p) {
+    using U = typename WordsOf<sizeof(V)>::type;
+    return __builtin_bit_cast(V, __builtin_nontemporal_load(reinterpret_cast<const U*>(p)));
+}
+template <typename V>
+__device__ __forceinline__ void st_stream(V* p, const V& v) {
+    using U = typename WordsOf<sizeof(V)>::type;
+    __builtin_nontemporal_store(__builtin_bit_cast(U, v), reinterpret_cast<U*>(p));
+}
+__device__ __forceinline__ void st_frag_stream(bf16* p, const Frag<bf16>& f) {
+    st_stream(reinterpret_cast<bf16x8*>(p), f.v);
+}
+__device__ __forceinline__ void st_frag_stream(float* p, const Frag<float>& f) {
+    st_stream(reinterpret_cast<float4*>(p), make_float4(f.v[0], f.v[1], f.v[2], f.v[3]));
+    st_stream(reinterpret_cast<float4*>(p) + 1, make_float4(f.v[4], f.v[5], f.v[6], f.v[7]));
+}
+__device__ __forceinline__ void st4_stream(bf16* p, const float* in) {
+    bf16x4 x;
+    x[0] = (bf16)in[0]; x[1] = (bf16)in[1]; x[2] = (bf16)in[2]; x[3] = (bf16)in[3];
+    st_stream(reinterpret_cast<bf16x4*>(p), x);
+}
+__device__ __forceinline__ void st4_stream(float* p, const float* in) {
+    st_stream(reinterpret_cast<float4*>(p), make_float4(in[0], in[1], in[2], in[3]));
+}
+
 // Workgroup barrier that orders LDS traffic only: waits for this wave's LDS
 // operations, then meets the other waves.  Unlike __syncthreads() it does not
 // wait for outstanding global loads and stores, so prefetches and record

@@ -120,19 +120,19 @@ __device__ __forceinline__ void intra_load(IntraIn<KIND, T, DK, DV>& in, const T
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
         const size_t off = (row0 + (size_t)min(p0 + i, last) * H) * DK + ch0;
-        if constexpr (KIND == KIND_KDA) in.gv[i] = *reinterpret_cast<const VG*>(g + off);
+        if constexpr (KIND == KIND_KDA) in.gv[i] = ld_stream(reinterpret_cast<const VG*>(g + off));
     }
-    if constexpr (KIND != KIND_KDA) in.gs = (tid < 64) ? g[row0 + (size_t)min(lane, last) * H] : 0.f;
+    if constexpr (KIND != KIND_KDA) in.gs = (tid < 64) ? ld_stream(g + row0 + (size_t)min(lane, last) * H) : 0.f;
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
         const size_t off = (row0 + (size_t)min(p0 + i, last) * H) * DK + ch0;
-        in.kv[i] = *reinterpret_cast<const VT*>(k + off);
-        in.qv[i] = *reinterpret_cast<const VT*>(q + off);
+        in.kv[i] = ld_stream(reinterpret_cast<const VT*>(k + off));
+        in.qv[i] = ld_stream(reinterpret_cast<const VT*>(q + off));
     }
-    if constexpr (KIND != KIND_LA) in.bt = (tid < C) ? beta[row0 + (size_t)min(tid, last) * H] : 0.f;
+    if constexpr (KIND != KIND_LA) in.bt = (tid < C) ? ld_stream(beta + row0 + (size_t)min(tid, last) * H) : 0.f;
 #pragma unroll
     for (int i = 0; i < PL; ++i)
-        in.vv[i] = *reinterpret_cast<const VT*>(v + (row0 + (size_t)min(p0 + i, last) * H) * DV + ch0);
+        in.vv[i] = ld_stream(reinterpret_cast<const VT*>(v + (row0 + (size_t)min(p0 + i, last) * H) * DV + ch0));
 }
 
 // Steps a1-a3 (and the output operands) of chunk c of head h, batch b, from
@@ -303,14 +303,14 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
                 Frag<T> f;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) frag_set(f, j, kb[cc][i0 + j]);
-                st_frag(rKb + ((size_t)(((wk * 2 + hh) * 2 + (p >> 5)) * 64) + rr + 16 * ((p & 31) >> 3)) * 8, f);
+                st_frag_stream(rKb + ((size_t)(((wk * 2 + hh) * 2 + (p >> 5)) * 64) + rr + 16 * ((p & 31) >> 3)) * 8, f);
             }
         }
         if (qg == 0) {
             VG ph;
 #pragma unroll
             for (int j = 0; j < CPT; ++j) ph[j] = phi[j];
-            *reinterpret_cast<VG*>(rPhi + ch0) = ph;
+            st_stream(reinterpret_cast<VG*>(rPhi + ch0), ph);
         }
         if constexpr (PERCH) {
             if (flags) {
@@ -332,7 +332,7 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
                 for (int i = 0; i < PL; i += 4) {
                     const int p = p0 + i;
                     const int wv = 2 * (p >> 5) + ((p >> 2) & 1);
-                    st4(rU + ((size_t)(((ch >> 4) * 4 + wv) * 64) + (ch & 15) + 16 * ((p & 31) >> 3)) * 4, &vt[i]);
+                    st4_stream(rU + ((size_t)(((ch >> 4) * 4 + wv) * 64) + (ch & 15) + 16 * ((p & 31) >> 3)) * 4, &vt[i]);
                 }
             }
         }
@@ -394,7 +394,7 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
                         }
                         frag_set(out, 4 * hh + i, val);
                     }
-                st_frag(rAqk + ((size_t)(w * 2 + kbk) * 64 + lane) * 8, out);
+                st_frag_stream(rAqk + ((size_t)(w * 2 + kbk) * 64 + lane) * 8, out);
             }
         }
         // the two blocks above the diagonal (w = 0, 1; kb = 1) are zero
@@ -402,7 +402,7 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
             Frag<T> z;
 #pragma unroll
             for (int j = 0; j < 8; ++j) frag_set(z, j, 0.f);
-            st_frag(rAqk + ((size_t)((tid >> 6) * 2 + 1) * 64 + (tid & 63)) * 8, z);
+            st_frag_stream(rAqk + ((size_t)((tid >> 6) * 2 + 1) * 64 + (tid & 63)) * 8, z);
         }
         // Q~ in fragment order, from the LDS copy (scalar gates scale it here)
         for (int e = tid; e < 4 * NKB * 64; e += kThreads) {
@@ -414,7 +414,7 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
 #pragma unroll
                 for (int j = 0; j < 8; ++j) frag_set(f, j, frag_get(f, j) * sc);
             }
-            st_frag(rQ + (size_t)e * 8, f);
+            st_frag_stream(rQ + (size_t)e * 8, f);
         }
     }
     if constexpr (!DELTA) return;
@@ -554,7 +554,7 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
                 for (int n = 0; n < PER; ++n) {
                     const int t = nt0 + n - NTW;
                     float vals[4] = {acc[mt][n][0], acc[mt][n][1], acc[mt][n][2], acc[mt][n][3]};
-                    st4(rU + ((size_t)(t * 4 + mt) * 64 + lane) * 4, vals);
+                    st4_stream(rU + ((size_t)(t * 4 + mt) * 64 + lane) * 4, vals);
                 }
         }
     }
@@ -564,7 +564,7 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
         constexpr int NKB = DK / 32;
         for (int e = tid; e < 4 * NKB * 64; e += kThreads) {
             const int l = e & 63, kq = (e >> 6) % NKB, w = (e >> 6) / NKB;
-            st_frag(rW + (size_t)e * 8, ld_frag(sW + pw(w, l & 15) * LDK + 32 * kq + 8 * (l >> 4)));
+            st_frag_stream(rW + (size_t)e * 8, ld_frag(sW + pw(w, l & 15) * LDK + 32 * kq + 8 * (l >> 4)));
         }
     }
 }
