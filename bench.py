@@ -104,6 +104,58 @@ def cpu_baseline(w, x, max_tokens: int, threads: int):
                       f"{threads} threads, {dt:.2f} s wall"}
 
 
+def decode_bench(args):
+    """Recurrent decode step: --decode-batch sequences x the workload's heads
+    and head size, --decode-tokens new tokens each per call, the state
+    resident in HBM and updated in place.  One JSON line; HBM roofline of the
+    decode kernel from the state read + write and the token I/O."""
+    import torch
+    import delta_rule_rnn_amd as dra
+    from delta_rule_rnn_amd.inputs import WORKLOADS, generate
+
+    w0 = WORKLOADS[args.workload]
+    w = w0.with_(name=w0.name + "_decode", B=args.decode_batch, T=args.decode_tokens, h0_std=0.5)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = {n: (t.to(dev) if t is not None else None) for n, t in generate(w).items()}
+    state = d["h0"].clone()
+    o = torch.empty(w.B, w.T, w.H, w.Dv, dtype=d["q"].dtype, device=dev)
+    stream = torch.cuda.current_stream()
+    call = lambda: dra.decode(w.kind, d["q"], d["k"], d["v"], d["g"], d["beta"], state, out=o)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record(stream)
+        call()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1000.0 / args.steps
+    k_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    io = 2 if d["q"].dtype == torch.bfloat16 else 4
+    th = w.B * w.T * w.H
+    per_chain = 2 * w.Dk * w.Dv * 4                      # state read + write
+    per_token = io * (2 * w.Dk + 2 * w.Dv) + (4 * w.Dk if w.kind == "kda" else 4) + (4 if w.kind != "decay_la" else 0)
+    alg = w.B * w.H * per_chain + th * per_token
+    gbs = alg / (k_ms * 1e-3) / 1e9
+    line = {
+        "metric": "decode tokens/sec (1 GPU), recurrent step", "value": round(w.B * w.T / (ms / 1000.0), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if io == 2 else "f32", "data": "synthetic",
+        "config": {"workload": f"{w.kind}_decode B={w.B} H={w.H} T={w.T} dk={w.Dk} dv={w.Dv}",
+                   "global_batch": w.B, "seq_len": w.T, "heads": w.H, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "decode", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_ms": round(k_ms, 4), "alg_bytes": int(alg)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,6 +166,11 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens of the workload the CPU oracle is timed on")
     ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--mode", choices=("prefill", "decode"), default="prefill",
+                    help="prefill: the chunked forward (the benchmark line); decode: the "
+                         "recurrent step on a serving-sized batch")
+    ap.add_argument("--decode-batch", type=int, default=64, help="sequences per decode call")
+    ap.add_argument("--decode-tokens", type=int, default=1, help="new tokens per sequence per call")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (3 times): the "
                          "reference for scaling the HBM byte counters of a profile")
@@ -135,6 +192,10 @@ def main():
               "chain; multi-GPU sharding is a design note, not built). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.mode == "decode":
+        decode_bench(args)
+        return
 
     import torch
     import delta_rule_rnn_amd as dra

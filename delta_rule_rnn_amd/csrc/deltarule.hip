@@ -8,6 +8,7 @@
 #include "common.h"
 #include "inter.h"
 #include "intra.h"
+#include "decode.h"
 #include "steps.h"
 
 namespace {
@@ -196,6 +197,47 @@ dr_status forward(int kind, const void* q, const void* k, const void* v, const f
     return launch_inter(p, h0, hT, 0, p.NT, st);
 }
 
+// ---- recurrent decode step --------------------------------------------------
+template <int KIND, typename E, int D>
+dr_status launch_decode_t(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                          float* state, void* o, int B, int T, int H, hipStream_t st) {
+    dim3 grid((unsigned)((long long)B * H * (D / 64)));
+    hipLaunchKernelGGL((dr::decode_kernel<KIND, E, D, D>), grid, dim3(64), 0, st, static_cast<const E*>(q),
+                       static_cast<const E*>(k), static_cast<const E*>(v), g, beta, state, static_cast<E*>(o), T, H);
+    return check_launch();
+}
+
+template <int KIND>
+dr_status launch_decode_k(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                          float* state, void* o, int B, int T, int H, int D, int dtype, hipStream_t st) {
+    if (dtype == DR_BF16) {
+        if (D == 64) return launch_decode_t<KIND, bf16, 64>(q, k, v, g, beta, state, o, B, T, H, st);
+        return launch_decode_t<KIND, bf16, 128>(q, k, v, g, beta, state, o, B, T, H, st);
+    }
+    if (D == 64) return launch_decode_t<KIND, float, 64>(q, k, v, g, beta, state, o, B, T, H, st);
+    return launch_decode_t<KIND, float, 128>(q, k, v, g, beta, state, o, B, T, H, st);
+}
+
+dr_status decode(int kind, const void* q, const void* k, const void* v, const float* g, const float* beta,
+                 float* state, void* o, int B, int T, int H, int Dk, int Dv, int dtype, void* stream) {
+    // same argument rules as the forward, with the chunk size not involved
+    dr_status s = validate(kind, q, k, v, g, beta, B, T, H, Dk, Dv, dr::kChunk, dtype);
+    if (s != DR_OK) return s;
+    if (T > 0 && (!o || !state)) return DR_ERR_INVALID_ARG;
+    if (!aligned16(o) || !aligned16(state)) return DR_ERR_INVALID_ARG;
+    if (T == 0) return DR_OK;
+    if ((long long)B * H * (Dv / 64) > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    switch (kind) {
+        case DR_KIND_KDA:
+            return launch_decode_k<dr::KIND_KDA>(q, k, v, g, beta, state, o, B, T, H, Dk, dtype, st);
+        case DR_KIND_GDN:
+            return launch_decode_k<dr::KIND_GDN>(q, k, v, g, beta, state, o, B, T, H, Dk, dtype, st);
+        default:
+            return launch_decode_k<dr::KIND_LA>(q, k, v, g, nullptr, state, o, B, T, H, Dk, dtype, st);
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -259,6 +301,21 @@ dr_status dr_inter(int kind, const float* h0, void* o, float* hT, int B, int T, 
     const Problem p = make_problem(kind, nullptr, nullptr, nullptr, nullptr, nullptr, o, B, T, H, Dk, dtype,
                                    const_cast<void*>(workspace), nullptr);
     return launch_inter(p, h0, hT, 0, p.NT, static_cast<hipStream_t>(stream));
+}
+
+dr_status kda_decode(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                     float* state, void* o, int B, int T, int H, int Dk, int Dv, int dtype, void* stream) {
+    return decode(DR_KIND_KDA, q, k, v, g, beta, state, o, B, T, H, Dk, Dv, dtype, stream);
+}
+
+dr_status gdn_decode(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                     float* state, void* o, int B, int T, int H, int Dk, int Dv, int dtype, void* stream) {
+    return decode(DR_KIND_GDN, q, k, v, g, beta, state, o, B, T, H, Dk, Dv, dtype, stream);
+}
+
+dr_status decay_la_decode(const void* q, const void* k, const void* v, const float* g, float* state, void* o,
+                          int B, int T, int H, int Dk, int Dv, int dtype, void* stream) {
+    return decode(DR_KIND_DECAY_LA, q, k, v, g, nullptr, state, o, B, T, H, Dk, Dv, dtype, stream);
 }
 
 dr_status dr_chunk_cumsum(const float* g, float* gamma, int B, int T, int H, int D, int C, void* stream) {

@@ -142,6 +142,60 @@ def forward(kind: str, q, k, v, g, beta=None, h0=None, **kw):
     return FORWARDS[kind](q, k, v, g, beta, h0, **kw)
 
 
+# ---- recurrent decode step ---------------------------------------------------
+
+def _decode(kind: str, q, k, v, g, beta, state, out, stream) -> torch.Tensor:
+    lib = _lib.load()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    _need(q, "q"); _need(k, "k", dt, q.shape); _need(v, "v", dt, (B, T, H, Dv))
+    _need(g, "g", torch.float32, (B, T, H, Dk) if kind == "kda" else (B, T, H))
+    if kind != "decay_la":
+        if beta is None:
+            raise DeltaRuleError("beta is required")
+        _need(beta, "beta", torch.float32, (B, T, H))
+    if state is None:
+        raise DeltaRuleError("state is required (fp32 [B,H,Dk,Dv], updated in place)")
+    _need(state, "state", torch.float32, (B, H, Dk, Dv))
+    o = torch.empty(B, T, H, Dv, dtype=dt, device=q.device) if out is None else out
+    _need(o, "out", dt, (B, T, H, Dv))
+    code, s = _dtype_code(q), _stream(stream)
+    if kind == "kda":
+        st = lib.kda_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
+                            B, T, H, Dk, Dv, code, s)
+    elif kind == "gdn":
+        st = lib.gdn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
+                            B, T, H, Dk, Dv, code, s)
+    else:
+        st = lib.decay_la_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(state), _ptr(o),
+                                 B, T, H, Dk, Dv, code, s)
+    _check(st, f"{kind}_decode")
+    return o
+
+
+def kda_decode(q, k, v, g, beta, state, out=None, stream=None) -> torch.Tensor:
+    """Apply T new tokens per (b, h) to ``state`` (fp32 [B,H,Dk,Dv], updated
+    in place; the layout of a forward's hT) and return o [B,T,H,Dv]."""
+    return _decode("kda", q, k, v, g, beta, state, out, stream)
+
+
+def gdn_decode(q, k, v, g, beta, state, out=None, stream=None) -> torch.Tensor:
+    """As kda_decode with g [B,T,H]."""
+    return _decode("gdn", q, k, v, g, beta, state, out, stream)
+
+
+def decay_la_decode(q, k, v, g, state, out=None, stream=None) -> torch.Tensor:
+    """As gdn_decode without beta (no delta term)."""
+    return _decode("decay_la", q, k, v, g, None, state, out, stream)
+
+
+def decode(kind: str, q, k, v, g, beta=None, state=None, **kw) -> torch.Tensor:
+    if kind == "decay_la":
+        return decay_la_decode(q, k, v, g, state, **kw)
+    return {"kda": kda_decode, "gdn": gdn_decode}[kind](q, k, v, g, beta, state, **kw)
+
+
 # ---- individual steps ------------------------------------------------------
 
 def chunk_cumsum(g: torch.Tensor, chunk_size: int = CHUNK, stream=None) -> torch.Tensor:

@@ -115,6 +115,37 @@ dr_status decay_la_fwd(const void* q, const void* k, const void* v, const float*
                        int B, int T, int H, int Dk, int Dv, int C, int dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- recurrent decode step ----------------------------------------------- */
+
+/*
+ * Decode: apply T new tokens per (b, h), one after the other, to a state kept
+ * between calls, and return their outputs.  Same recurrence as kda_fwd, token
+ * by token ("TileLang 实战：KDA 从零到一–Kimi Delta Attention" opening equation
+ * and section 3.1; "Gated DeltaNet" section "Recurrent 算法代码解析"):
+ *   S <- Diag(a_t) S;  r = beta_t (v_t - S^T k_t);  S <- S + k_t r^T;  o_t = S^T q_t
+ * (decay_la_decode: S <- a_t S + k_t v_t^T).
+ *   q, k:  [B,T,H,Dk] (dtype);  v: [B,T,H,Dv] (dtype)
+ *   g:     [B,T,H,Dk] float for kda_decode, [B,T,H] float otherwise (ln a)
+ *   beta:  [B,T,H] float (not for decay_la_decode)
+ *   state: [B,H,Dk,Dv] float, the layout of h0/hT: read, then overwritten
+ *          with the state after the T tokens (pass a forward's hT to
+ *          continue a prefilled sequence)
+ *   o:     [B,T,H,Dv] (dtype), written
+ * Sizes as for the forward (Dk == Dv in {64, 128}); T = 0 leaves the state
+ * unchanged and launches nothing.  All arithmetic is fp32; the state is read
+ * and written once per call.  Nothing is allocated.  o may not alias the
+ * inputs or the state.
+ */
+dr_status kda_decode(const void* q, const void* k, const void* v, const float* g,
+                     const float* beta, float* state, void* o,
+                     int B, int T, int H, int Dk, int Dv, int dtype, void* stream);
+dr_status gdn_decode(const void* q, const void* k, const void* v, const float* g,
+                     const float* beta, float* state, void* o,
+                     int B, int T, int H, int Dk, int Dv, int dtype, void* stream);
+dr_status decay_la_decode(const void* q, const void* k, const void* v, const float* g,
+                          float* state, void* o,
+                          int B, int T, int H, int Dk, int Dv, int dtype, void* stream);
+
 /* ---- the individual steps ---------------------------------------------- */
 
 /*

@@ -90,6 +90,14 @@ def test_other_entry_points_reject(lib):
     assert lib.dr_intra(3, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 1, 64, 64, 64, 1, FAKE, 1 << 30, None,
                         None) == -1
     assert lib.dr_inter(0, None, FAKE, None, 1, 64, 1, 64, 64, 64, 1, FAKE, 10, None) == -4
+    # decode: state required, sizes as for the forward, aligned pointers
+    assert lib.kda_decode(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 1, 1, 128, 128, 1, None) == -1
+    assert lib.gdn_decode(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 96, 96, 1, None) == -2
+    assert lib.gdn_decode(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1, 1, 1, 64, 64, 1, None) == -1
+    assert lib.decay_la_decode(FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE, 1, 1, 1, 64, 64, 1, None) == -1
+    assert lib.decay_la_decode(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 64, 64, 2, None) == -1
+    # decode with no tokens touches nothing
+    assert lib.kda_decode(None, None, None, None, None, None, None, 1, 0, 1, 64, 64, 1, None) == 0
     # nothing to do: T = 0 and no final state requested
     assert lib.kda_fwd(None, None, None, None, None, None, None, None, 1, 0, 1, 64, 64, 64, 1, None, 0,
                        None, None) == 0
