@@ -52,6 +52,12 @@ struct Problem {
     void* o;
     uint8_t* ws;
     unsigned* flags;
+    // packed sequences only: B sequences, chunk table and descriptors in the
+    // workspace (see varlen_layout)
+    const int4* table = nullptr;
+    const int4* seqinfo = nullptr;
+    const int* total = nullptr;
+    int maxchunks = 0;
 };
 
 int device_cus() {
@@ -126,8 +132,15 @@ template <int KIND, typename E, int D, int NTN, int PFD>
 dr_status launch_inter_p(const Problem& p, const float* h0, float* hT, int c0, int n, hipStream_t st) {
     constexpr int NV = D / (16 * NTN);
     dim3 grid(p.B * p.H * NV);
-    hipLaunchKernelGGL((dr::inter_kernel<KIND, E, D, D, NTN, PFD>), grid, dim3(dr::inter_threads<PFD>()), 0,
-                       st, p.ws, h0, static_cast<E*>(p.o), hT, p.T, p.H, p.NT, c0, n);
+    if (p.seqinfo) {
+        // packed sequences: p.B is the sequence count
+        hipLaunchKernelGGL((dr::inter_kernel<KIND, E, D, D, NTN, PFD, true>), grid, dim3(dr::inter_threads<PFD>()),
+                           0, st, p.ws, h0, static_cast<E*>(p.o), hT, p.T, p.H, p.NT, 0, 0, p.seqinfo,
+                           p.maxchunks);
+    } else {
+        hipLaunchKernelGGL((dr::inter_kernel<KIND, E, D, D, NTN, PFD, false>), grid, dim3(dr::inter_threads<PFD>()),
+                           0, st, p.ws, h0, static_cast<E*>(p.o), hT, p.T, p.H, p.NT, c0, n, nullptr, 0);
+    }
     return check_launch();
 }
 
@@ -195,6 +208,83 @@ dr_status forward(int kind, const void* q, const void* k, const void* v, const f
     s = launch_intra(p, 0, p.NT, st);
     if (s != DR_OK) return s;
     return launch_inter(p, h0, hT, 0, p.NT, st);
+}
+
+// ---- packed sequences ---------------------------------------------------------
+// Workspace of the varlen forward: records [H][maxchunks], then the chunk
+// table [maxchunks] int4, the sequence descriptors [N] int4 and the slot
+// count, each block 256-byte aligned.  maxchunks = ceil(T/C) + N bounds
+// sum_i ceil(len_i / C).
+struct VarlenLayout {
+    size_t rec, table, seqinfo, total, bytes;
+    int maxchunks;
+};
+VarlenLayout varlen_layout(int N, int T, int H, int D, int dtype) {
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    VarlenLayout L;
+    L.maxchunks = ceil_div(T, dr::kChunk) + N;
+    L.rec = 0;
+    L.table = up((size_t)H * L.maxchunks * record_bytes(D, dtype));
+    L.seqinfo = L.table + up((size_t)L.maxchunks * sizeof(int4));
+    L.total = L.seqinfo + up((size_t)N * sizeof(int4));
+    L.bytes = L.total + 256;
+    return L;
+}
+
+template <int KIND, typename E, int D>
+dr_status launch_intra_varlen_t(const Problem& p, hipStream_t st) {
+    const long long items = (long long)p.maxchunks * p.H;
+    if (items > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL((dr::intra_varlen_kernel<KIND, E, D, D>), dim3((unsigned)items), dim3(dr::kThreads), 0, st,
+                       static_cast<const E*>(p.q), static_cast<const E*>(p.k), static_cast<const E*>(p.v), p.g,
+                       p.beta, p.ws, p.flags, p.table, p.total, p.H, p.maxchunks);
+    return check_launch();
+}
+template <int KIND>
+dr_status launch_intra_varlen_k(const Problem& p, hipStream_t st) {
+    if (p.dtype == DR_BF16) {
+        if (p.D == 64) return launch_intra_varlen_t<KIND, bf16, 64>(p, st);
+        return launch_intra_varlen_t<KIND, bf16, 128>(p, st);
+    }
+    if (p.D == 64) return launch_intra_varlen_t<KIND, float, 64>(p, st);
+    return launch_intra_varlen_t<KIND, float, 128>(p, st);
+}
+
+dr_status forward_varlen(int kind, const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const int* cu_seqlens, int N, const float* h0, void* o, float* hT,
+                         int T, int H, int Dk, int Dv, int C, int dtype, void* ws, size_t ws_bytes,
+                         unsigned* flags, void* stream) {
+    dr_status s = validate(kind, q, k, v, g, beta, 1, T, H, Dk, Dv, C, dtype);
+    if (s != DR_OK) return s;
+    if (N < 1 || !cu_seqlens) return DR_ERR_INVALID_ARG;
+    if ((long long)N * H * (Dv / 16) > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
+    if (T > 0 && !o) return DR_ERR_INVALID_ARG;
+    if (!aligned16(o) || !aligned16(h0) || !aligned16(hT) || !aligned16(ws)) return DR_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return DR_ERR_INVALID_ARG;
+    const VarlenLayout L = varlen_layout(N, T, H, Dk, dtype);
+    if (!ws || ws_bytes < L.bytes) return DR_ERR_WORKSPACE;
+    Problem p = make_problem(kind, q, k, v, g, beta, o, N, T, H, Dk, dtype, ws, flags);
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    p.table = reinterpret_cast<const int4*>(w + L.table);
+    p.seqinfo = reinterpret_cast<const int4*>(w + L.seqinfo);
+    p.total = reinterpret_cast<const int*>(w + L.total);
+    p.maxchunks = L.maxchunks;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(dr::varlen_table_kernel, dim3(1), dim3(1024), 0, st, cu_seqlens, N, T, L.maxchunks,
+                       reinterpret_cast<int4*>(w + L.table), reinterpret_cast<int4*>(w + L.seqinfo),
+                       reinterpret_cast<int*>(w + L.total), flags);
+    if ((s = check_launch()) != DR_OK) return s;
+    if (T > 0) {
+        switch (kind) {
+            case DR_KIND_KDA: s = launch_intra_varlen_k<dr::KIND_KDA>(p, st); break;
+            case DR_KIND_GDN: s = launch_intra_varlen_k<dr::KIND_GDN>(p, st); break;
+            default: s = launch_intra_varlen_k<dr::KIND_LA>(p, st); break;
+        }
+        if (s != DR_OK) return s;
+    }
+    if (T == 0 && hT == nullptr) return DR_OK;
+    // the state pass reads nseg, tokens and record slots from the descriptors
+    return launch_inter(p, h0, hT, 0, 0, st);
 }
 
 // ---- recurrent decode step --------------------------------------------------
@@ -301,6 +391,35 @@ dr_status dr_inter(int kind, const float* h0, void* o, float* hT, int B, int T, 
     const Problem p = make_problem(kind, nullptr, nullptr, nullptr, nullptr, nullptr, o, B, T, H, Dk, dtype,
                                    const_cast<void*>(workspace), nullptr);
     return launch_inter(p, h0, hT, 0, p.NT, static_cast<hipStream_t>(stream));
+}
+
+size_t dr_workspace_bytes_varlen(int kind, int N, int T, int H, int Dk, int Dv, int C, int dtype) {
+    if (kind < 0 || kind > 2 || N < 1 || H <= 0 || T < 0) return 0;
+    if (dr_record_bytes(Dk, Dv, C, dtype) == 0) return 0;
+    return varlen_layout(N, T, H, Dk, dtype).bytes;
+}
+
+dr_status kda_fwd_varlen(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                         const int* cu_seqlens, int N, const float* h0, void* o, float* hT, int T, int H, int Dk,
+                         int Dv, int C, int dtype, void* workspace, size_t workspace_bytes, unsigned* flags,
+                         void* stream) {
+    return forward_varlen(DR_KIND_KDA, q, k, v, g, beta, cu_seqlens, N, h0, o, hT, T, H, Dk, Dv, C, dtype,
+                          workspace, workspace_bytes, flags, stream);
+}
+
+dr_status gdn_fwd_varlen(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                         const int* cu_seqlens, int N, const float* h0, void* o, float* hT, int T, int H, int Dk,
+                         int Dv, int C, int dtype, void* workspace, size_t workspace_bytes, unsigned* flags,
+                         void* stream) {
+    return forward_varlen(DR_KIND_GDN, q, k, v, g, beta, cu_seqlens, N, h0, o, hT, T, H, Dk, Dv, C, dtype,
+                          workspace, workspace_bytes, flags, stream);
+}
+
+dr_status decay_la_fwd_varlen(const void* q, const void* k, const void* v, const float* g, const int* cu_seqlens,
+                              int N, const float* h0, void* o, float* hT, int T, int H, int Dk, int Dv, int C,
+                              int dtype, void* workspace, size_t workspace_bytes, unsigned* flags, void* stream) {
+    return forward_varlen(DR_KIND_DECAY_LA, q, k, v, g, nullptr, cu_seqlens, N, h0, o, hT, T, H, Dk, Dv, C, dtype,
+                          workspace, workspace_bytes, flags, stream);
 }
 
 dr_status kda_decode(const void* q, const void* k, const void* v, const float* g, const float* beta,

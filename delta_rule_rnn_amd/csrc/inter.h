@@ -166,12 +166,17 @@ __device__ __forceinline__ void l2_prefetch_wave(const uint8_t* chain_rec, int n
 template <int PFD>
 constexpr int inter_threads() { return PFD > 0 ? kInterThreads + 64 : kInterThreads; }
 
-template <int KIND, typename T, int DK, int DV, int NTN, int PFD>
+// VARLEN: chains are (sequence, head) of packed sequences; seqinfo[i] =
+// {first record slot, chunks, first token, tokens} of sequence i (written by
+// varlen_table_kernel) replaces the dense layout's (Tlen, NT, c0, nseg).
+template <int KIND, typename T, int DK, int DV, int NTN, int PFD, bool VARLEN>
 __global__ __launch_bounds__(inter_threads<PFD>()) void inter_kernel(const uint8_t* __restrict__ ws,
                                                               const float* __restrict__ h0,
                                                               T* __restrict__ o, float* __restrict__ hT,
                                                               int Tlen, int H, int NT, int c0,
-                                                              int nseg)
+                                                              int nseg_arg,
+                                                              const int4* __restrict__ seqinfo,
+                                                              int maxchunks)
 {
     using R = Rec<T, DK, DV>;
     constexpr int C = kChunk;
@@ -199,9 +204,24 @@ __global__ __launch_bounds__(inter_threads<PFD>()) void inter_kernel(const uint8
     const int b = chain / H, h = chain % H;
     const int dv0 = slice * DVS;
 
-    // this launch runs chunks c0 .. c0+nseg-1 of the chain; the state enters
-    // through h0 and leaves through hT
-    const uint8_t* chain_rec = ws + (((size_t)b * H + h) * (size_t)NT + c0) * R::BYTES;
+    // this launch runs nseg chunks of the chain from its record chain_rec on,
+    // covering tokens tok0 .. tok0+tlim-1; the state enters through h0 and
+    // leaves through hT
+    int nseg, tlim;
+    size_t tok0;
+    const uint8_t* chain_rec;
+    if constexpr (VARLEN) {
+        const int4 si = seqinfo[b];   // b is the sequence here
+        nseg = si.y;
+        tok0 = (size_t)si.z;
+        tlim = si.w;
+        chain_rec = ws + ((size_t)h * maxchunks + si.x) * R::BYTES;
+    } else {
+        nseg = nseg_arg;
+        tok0 = (size_t)b * Tlen + (size_t)c0 * C;
+        tlim = Tlen - c0 * C;
+        chain_rec = ws + (((size_t)b * H + h) * (size_t)NT + c0) * R::BYTES;
+    }
 
     auto fS_read = [&](Frag<T> (&fS)[NKB][NTN]) {
 #pragma unroll
@@ -315,8 +335,7 @@ __global__ __launch_bounds__(inter_threads<PFD>()) void inter_kernel(const uint8
         // this lane's output row: position pw(wave, r16), columns 4*grp.. of each n-tile
         const int pos = 32 * kbP + prow(halfP, r16);
         const size_t ostride = (size_t)H * DV;
-        T* const orow = o + (((size_t)b * Tlen + (size_t)c0 * C + pos) * H + h) * DV + dv0 + 4 * grp;
-        const int tlim = Tlen - c0 * C;   // valid positions from the segment start
+        T* const orow = o + ((tok0 + pos) * H + h) * DV + dv0 + 4 * grp;
 
         using Ops = OutOps<T, DK>;
         auto load = [&](Ops& op, int c) {

@@ -104,7 +104,7 @@ template <int KIND, typename T, int DK, int DV>
 __device__ __forceinline__ void intra_load(IntraIn<KIND, T, DK, DV>& in, const T* __restrict__ q,
                                            const T* __restrict__ k, const T* __restrict__ v,
                                            const float* __restrict__ g, const float* __restrict__ beta,
-                                           int b, int c, int h, int Tlen, int H)
+                                           size_t row0, int nvalid, int H)
 {
     using In = IntraIn<KIND, T, DK, DV>;
     using VT = typename In::VT;
@@ -112,9 +112,7 @@ __device__ __forceinline__ void intra_load(IntraIn<KIND, T, DK, DV>& in, const T
     constexpr int C = kChunk;
     constexpr int NCG = In::Cfg::NCG, PL = In::Cfg::PL, CPT = In::Cfg::CPT;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int t0 = c * C;
-    const int last = min(C, Tlen - t0) - 1;
-    const size_t row0 = ((size_t)b * Tlen + t0) * H + h;
+    const int last = nvalid - 1;
     const int ch0 = CPT * (tid % NCG), p0 = (tid / NCG) * PL;
     // gates first, then k and q (step a1 needs them first), v last
 #pragma unroll
@@ -135,12 +133,13 @@ __device__ __forceinline__ void intra_load(IntraIn<KIND, T, DK, DV>& in, const T
         in.vv[i] = ld_stream(reinterpret_cast<const VT*>(v + (row0 + (size_t)min(p0 + i, last) * H) * DV + ch0));
 }
 
-// Steps a1-a3 (and the output operands) of chunk c of head h, batch b, from
-// inputs already in registers; writes the chunk's record.
+// Steps a1-a3 (and the output operands) of one chunk from inputs already in
+// registers (nvalid of its C rows are tokens); writes the chunk's record at
+// recb.
 template <int KIND, typename T, int DK, int DV>
 __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, uint8_t* smem,
-                                            uint8_t* __restrict__ ws, unsigned* __restrict__ flags,
-                                            int Tlen, int H, int NT, int b, int c, int h)
+                                            unsigned* __restrict__ flags,
+                                            uint8_t* __restrict__ recb, int nvalid)
 {
     using Cfg = IntraCfg<KIND, T, DK, DV>;
     using R = Rec<T, DK, DV>;
@@ -166,12 +165,6 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, grp = lane >> 4;
-    const int t0 = c * C;
-    const int nvalid = min(C, Tlen - t0);
-    const size_t row0 = ((size_t)b * Tlen + t0) * H + h;   // token-head index of position 0
-    auto trow = [&](int p) { return row0 + (size_t)p * H; };
-
-    uint8_t* recb = ws + (((size_t)b * H + h) * NT + c) * R::BYTES;
     T* rW = reinterpret_cast<T*>(recb) + R::W;
     T* rQ = reinterpret_cast<T*>(recb) + R::QT;
     T* rKb = reinterpret_cast<T*>(recb) + R::KBT;
@@ -586,9 +579,35 @@ __global__ __launch_bounds__(kThreads, 2) void intra_kernel(
     const int h = (int)(it % (unsigned)H);
     const unsigned t = it / (unsigned)H;
     const int c = c0 + (int)(t % (unsigned)n), b = (int)(t / (unsigned)n);
+    const int nvalid = min(kChunk, Tlen - c * kChunk);
     IntraIn<KIND, T, DK, DV> in;
-    intra_load<KIND, T, DK, DV>(in, q, k, v, g, beta, b, c, h, Tlen, H);
-    intra_chunk<KIND, T, DK, DV>(in, smem, ws, flags, Tlen, H, NT, b, c, h);
+    intra_load<KIND, T, DK, DV>(in, q, k, v, g, beta, ((size_t)b * Tlen + (size_t)c * kChunk) * H + h, nvalid, H);
+    intra_chunk<KIND, T, DK, DV>(in, smem, flags, ws + (((size_t)b * H + h) * NT + c) * Rec<T, DK, DV>::BYTES,
+                                 nvalid);
+}
+
+// Packed sequences: one workgroup per (chunk slot, head), heads fastest.  The
+// slot table written by varlen_table_kernel gives each chunk's first token
+// and its valid rows; slots past the table's count exit at once.  Records go
+// to index h * maxchunks + slot, so each sequence's chunks are contiguous for
+// the state pass.
+template <int KIND, typename T, int DK, int DV>
+__global__ __launch_bounds__(kThreads, 2) void intra_varlen_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, uint8_t* __restrict__ ws,
+    unsigned* __restrict__ flags, const int4* __restrict__ table, const int* __restrict__ total, int H,
+    int maxchunks)
+{
+    using Cfg = IntraCfg<KIND, T, DK, DV>;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::BYTES];
+    const unsigned it = blockIdx.x;
+    const int h = (int)(it % (unsigned)H), slot = (int)(it / (unsigned)H);
+    if (slot >= *total) return;
+    const int4 e = table[slot];     // {sequence, first token, valid rows, -}
+    IntraIn<KIND, T, DK, DV> in;
+    intra_load<KIND, T, DK, DV>(in, q, k, v, g, beta, (size_t)e.y * H + h, e.z, H);
+    intra_chunk<KIND, T, DK, DV>(in, smem, flags, ws + ((size_t)h * maxchunks + slot) * Rec<T, DK, DV>::BYTES,
+                                 e.z);
 }
 
 }  // namespace dr

@@ -107,4 +107,63 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     }
 }
 
+// Packed sequences: from cu_seqlens (N+1 token offsets) build, in one
+// workgroup, the table of chunks (slot -> {sequence, first token, valid rows})
+// and per-sequence descriptors {first slot, chunks, first token, tokens}, the
+// slot count in *total.  Offsets are clamped into [0, T] and kept
+// non-decreasing, and slots beyond maxchunks are dropped, so every kernel
+// stays in bounds whatever cu_seqlens holds; malformed offsets raise
+// flag 0x4 (DR_FLAG_BAD_SEQLENS).
+__global__ __launch_bounds__(1024) void varlen_table_kernel(const int* __restrict__ cu, int N, int T,
+                                                            int maxchunks, int4* __restrict__ table,
+                                                            int4* __restrict__ seqinfo, int* __restrict__ total,
+                                                            unsigned* __restrict__ flags)
+{
+    __shared__ int wsum[16];
+    __shared__ int carry_s;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    if (tid == 0) carry_s = 0;
+    __syncthreads();
+    bool bad = false;
+    for (int base = 0; base < N; base += 1024) {
+        const int i = base + tid;
+        int s = 0, len = 0, nch = 0;
+        if (i < N) {
+            const int a = cu[i], e = cu[i + 1];
+            s = min(max(a, 0), T);
+            len = min(max(e, s), T) - s;
+            nch = (len + kChunk - 1) / kChunk;
+            bad = bad || a < 0 || e < a || e > T || (i == 0 && a != 0) || (i == N - 1 && e != T);
+        }
+        // inclusive scan of the chunk counts over the workgroup
+        int x = nch;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(x, off, 64);
+            if (lane >= off) x += y;
+        }
+        if (lane == 63) wsum[wid] = x;
+        __syncthreads();
+        int wpre = 0, btot = 0;
+        for (int w = 0; w < 16; ++w) {
+            if (w < wid) wpre += wsum[w];
+            btot += wsum[w];
+        }
+        const int carry = carry_s;
+        if (i < N) {
+            const int first = carry + wpre + x - nch;
+            const int off = min(first, maxchunks);
+            const int nc = min(first + nch, maxchunks) - off;
+            seqinfo[i] = make_int4(off, nc, s, len);
+            for (int j = 0; j < nc; ++j)
+                table[off + j] = make_int4(i, s + j * kChunk, min(kChunk, len - j * kChunk), 0);
+        }
+        __syncthreads();
+        if (tid == 0) carry_s = carry + btot;
+        __syncthreads();
+    }
+    if (tid == 0) *total = min(carry_s, maxchunks);
+    if (flags && bad) atomicOr(flags, 4u);
+}
+
 }  // namespace dr

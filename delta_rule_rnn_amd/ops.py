@@ -142,6 +142,71 @@ def forward(kind: str, q, k, v, g, beta=None, h0=None, **kw):
     return FORWARDS[kind](q, k, v, g, beta, h0, **kw)
 
 
+# ---- packed sequences -----------------------------------------------------------
+
+def workspace_bytes_varlen(kind: str, N: int, T: int, H: int, Dk: int, Dv: int, dtype: torch.dtype,
+                           chunk_size: int = CHUNK) -> int:
+    code = DR_BF16 if dtype == torch.bfloat16 else DR_F32
+    return int(_lib.load().dr_workspace_bytes_varlen(KINDS[kind], N, T, H, Dk, Dv, chunk_size, code))
+
+
+def _forward_varlen(kind, q, k, v, g, beta, cu_seqlens, h0, output_final_state, chunk_size, workspace,
+                    flags, stream):
+    lib = _lib.load()
+    squeeze = q.dim() == 4
+    if squeeze:
+        if q.shape[0] != 1:
+            raise DeltaRuleError("packed sequences take q as [T,H,D] or [1,T,H,D]")
+        q, k, v = q[0], k[0], v[0]
+        g = g[0]
+        beta = None if beta is None else beta[0]
+    T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    _need(q, "q"); _need(k, "k", dt, q.shape); _need(v, "v", dt, (T, H, Dv))
+    _need(g, "g", torch.float32, (T, H, Dk) if kind == "kda" else (T, H))
+    if kind != "decay_la":
+        if beta is None:
+            raise DeltaRuleError("beta is required")
+        _need(beta, "beta", torch.float32, (T, H))
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise DeltaRuleError("cu_seqlens must be int32 [N+1] with N >= 1")
+    N = cu_seqlens.numel() - 1
+    _need(h0, "h0", torch.float32, (N, H, Dk, Dv))
+    o = torch.empty(T, H, Dv, dtype=dt, device=q.device)
+    hT = torch.empty(N, H, Dk, Dv, dtype=torch.float32, device=q.device) if output_final_state else None
+    need = workspace_bytes_varlen(kind, N, T, H, Dk, Dv, dt, chunk_size)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8)
+    if flags is not None:
+        _need(flags, "flags", torch.int32, (1,))
+    code, s = _dtype_code(q), _stream(stream)
+    common = (N, _ptr(h0), _ptr(o), _ptr(hT), T, H, Dk, Dv, chunk_size, code, _ptr(workspace),
+              workspace.numel(), _ptr(flags), s)
+    if kind == "kda":
+        st = lib.kda_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), *common)
+    elif kind == "gdn":
+        st = lib.gdn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), *common)
+    else:
+        st = lib.decay_la_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(cu_seqlens), *common)
+    _check(st, f"{kind}_fwd_varlen")
+    return (o[None] if squeeze else o), hT
+
+
+def forward_varlen(kind: str, q, k, v, g, beta=None, cu_seqlens=None, h0=None, output_final_state=True,
+                   chunk_size=CHUNK, workspace=None, flags=None, stream=None):
+    """Forward over sequences packed along the token axis.  q, k [T,H,Dk]
+    (or [1,T,H,Dk]), v [T,H,Dv]; g [T,H,Dk] (kda) or [T,H]; beta [T,H];
+    cu_seqlens int32 [N+1] on the device; h0 [N,H,Dk,Dv] or None.
+    Returns (o like q with Dv, hT [N,H,Dk,Dv] or None)."""
+    if cu_seqlens is None:
+        raise DeltaRuleError("cu_seqlens is required")
+    return _forward_varlen(kind, q, k, v, g, beta, cu_seqlens, h0, output_final_state, chunk_size,
+                           workspace, flags, stream)
+
+
 # ---- recurrent decode step ---------------------------------------------------
 
 def _decode(kind: str, q, k, v, g, beta, state, out, stream) -> torch.Tensor:

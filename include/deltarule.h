@@ -70,6 +70,10 @@ typedef enum { DR_KIND_KDA = 0, DR_KIND_GDN = 1, DR_KIND_DECAY_LA = 2 } dr_kind;
  *     near the fp32/bf16 limit and results are not trustworthy. */
 #define DR_FLAG_KM_FP16_RANGE 0x1u
 #define DR_FLAG_KM_OVERFLOW   0x2u
+/* Packed-sequence forwards only: cu_seqlens was not 0 = cu[0] <= cu[1] <=
+ * ... <= cu[N] = T.  The kernels clamp the offsets into [0, T] (they stay in
+ * bounds) but the results are not meaningful. */
+#define DR_FLAG_BAD_SEQLENS   0x4u
 
 /* Bytes of device workspace kda_fwd / gdn_fwd / decay_la_fwd need for these
  * sizes (0 for invalid sizes).  The workspace holds one record per chunk and
@@ -114,6 +118,45 @@ dr_status decay_la_fwd(const void* q, const void* k, const void* v, const float*
                        const float* h0, void* o, float* hT,
                        int B, int T, int H, int Dk, int Dv, int C, int dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- packed sequences (varlen) ------------------------------------------- */
+
+/*
+ * Forward over N sequences packed along the token axis: token range
+ * [cu_seqlens[i], cu_seqlens[i+1]) is sequence i.  Chunks never cross a
+ * sequence boundary (each sequence is chunked from its own first token, its
+ * last chunk masked), and each sequence has its own initial and final state:
+ * the results equal N separate forwards.
+ *   q, k, o: [T,H,Dk|Dv] (dtype; a batch of one), v: [T,H,Dv]
+ *   g:       [T,H,Dk] float (kda) or [T,H] float; beta: [T,H] float
+ *   cu_seqlens: DEVICE int32 [N+1], 4-byte aligned, with 0 = cu[0] <= cu[1]
+ *            <= ... <= cu[N] = T.  Its contents are not read on the host:
+ *            violations raise DR_FLAG_BAD_SEQLENS and are clamped.
+ *   h0, hT:  [N,H,Dk,Dv] float or NULL
+ *   workspace: at least dr_workspace_bytes_varlen(...): chunk records of all
+ *            sequences plus the chunk table built on the device
+ * Other arguments, conventions and errors as for kda_fwd / gdn_fwd /
+ * decay_la_fwd.  N >= 1.
+ */
+size_t dr_workspace_bytes_varlen(int kind, int N, int T, int H, int Dk, int Dv, int C, int dtype);
+dr_status kda_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const int* cu_seqlens, int N,
+                         const float* h0, void* o, float* hT,
+                         int T, int H, int Dk, int Dv, int C, int dtype,
+                         void* workspace, size_t workspace_bytes, unsigned* flags,
+                         void* stream);
+dr_status gdn_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const int* cu_seqlens, int N,
+                         const float* h0, void* o, float* hT,
+                         int T, int H, int Dk, int Dv, int C, int dtype,
+                         void* workspace, size_t workspace_bytes, unsigned* flags,
+                         void* stream);
+dr_status decay_la_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
+                              const int* cu_seqlens, int N,
+                              const float* h0, void* o, float* hT,
+                              int T, int H, int Dk, int Dv, int C, int dtype,
+                              void* workspace, size_t workspace_bytes, unsigned* flags,
+                              void* stream);
 
 /* ---- recurrent decode step ----------------------------------------------- */
 

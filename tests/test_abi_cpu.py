@@ -96,6 +96,17 @@ def test_other_entry_points_reject(lib):
     assert lib.gdn_decode(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1, 1, 1, 64, 64, 1, None) == -1
     assert lib.decay_la_decode(FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE, 1, 1, 1, 64, 64, 1, None) == -1
     assert lib.decay_la_decode(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 64, 64, 2, None) == -1
+    # packed sequences: cu_seqlens and N >= 1 required, workspace sized by its own query
+    assert lib.kda_fwd_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, None, 2, None, FAKE, None, 128, 1, 64, 64, 64, 1,
+                              FAKE, 1 << 30, None, None) == -1
+    assert lib.gdn_fwd_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None, FAKE, None, 128, 1, 64, 64, 64, 1,
+                              FAKE, 1 << 30, None, None) == -1
+    assert lib.decay_la_fwd_varlen(FAKE, FAKE, FAKE, FAKE, FAKE + 2, 2, None, FAKE, None, 128, 1, 64, 64, 64,
+                                   1, FAKE, 1 << 30, None, None) == -1
+    need = lib.dr_workspace_bytes_varlen(0, 2, 128, 1, 64, 64, 64, 1)
+    assert need > 0 and lib.dr_workspace_bytes_varlen(0, 0, 128, 1, 64, 64, 64, 1) == 0
+    assert lib.kda_fwd_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, None, FAKE, None, 128, 1, 64, 64, 64, 1,
+                              FAKE, need - 1, None, None) == -4
     # decode with no tokens touches nothing
     assert lib.kda_decode(None, None, None, None, None, None, None, 1, 0, 1, 64, 64, 1, None) == 0
     # nothing to do: T = 0 and no final state requested
