@@ -156,6 +156,54 @@ def decode_bench(args):
     print(json.dumps(line), flush=True)
 
 
+def varlen_bench(args):
+    """Forward over packed sequences: the workload's B*T tokens cut into
+    sequences of seeded lengths uniform in [64, 4096] (the last one takes the
+    remainder); same heads, head size and distributions as the workload."""
+    import torch
+    import delta_rule_rnn_amd as dra
+    from delta_rule_rnn_amd.inputs import WORKLOADS, generate
+
+    w0 = WORKLOADS[args.workload]
+    T = w0.B * w0.T
+    w = w0.with_(name=w0.name + "_packed", B=1, T=T)
+    rng = torch.Generator().manual_seed(7)
+    lengths, left = [], T
+    while left > 0:
+        n = min(left, int(torch.randint(64, 4097, (1,), generator=rng).item()))
+        lengths.append(n)
+        left -= n
+    cu = torch.tensor([0] + list(torch.tensor(lengths).cumsum(0).tolist()), dtype=torch.int32)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = {n: (t.to(dev) if t is not None else None) for n, t in generate(w).items()}
+    sq = lambda t: None if t is None else t[0]
+    cu = cu.to(dev)
+    N = len(lengths)
+    ws = torch.empty(dra.workspace_bytes_varlen(w.kind, N, T, w.H, w.Dk, w.Dv, d["q"].dtype), dtype=torch.uint8,
+                     device=dev)
+    call = lambda: dra.forward_varlen(w.kind, sq(d["q"]), sq(d["k"]), sq(d["v"]), sq(d["g"]), sq(d["beta"]), cu,
+                                      workspace=ws)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+    line = {
+        "metric": "packed-sequence fwd tokens/sec (1 GPU)", "value": round(T / (ms / 1000.0), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if d["q"].dtype == torch.bfloat16 else "f32", "data": "synthetic",
+        "config": {"workload": f"{w.kind}_fwd_varlen N={N} T={T} H={w.H} dk={w.Dk} dv={w.Dv} C={w.C}",
+                   "sequences": N, "min_len": min(lengths), "max_len": max(lengths), "parallelism": "single GPU"},
+        "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,9 +214,10 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens of the workload the CPU oracle is timed on")
     ap.add_argument("--cpu-threads", type=int, default=0)
-    ap.add_argument("--mode", choices=("prefill", "decode"), default="prefill",
+    ap.add_argument("--mode", choices=("prefill", "decode", "varlen"), default="prefill",
                     help="prefill: the chunked forward (the benchmark line); decode: the "
-                         "recurrent step on a serving-sized batch")
+                         "recurrent step on a serving-sized batch; varlen: the forward over "
+                         "packed sequences of mixed lengths with the workload's token count")
     ap.add_argument("--decode-batch", type=int, default=64, help="sequences per decode call")
     ap.add_argument("--decode-tokens", type=int, default=1, help="new tokens per sequence per call")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -195,6 +244,9 @@ def main():
 
     if args.mode == "decode":
         decode_bench(args)
+        return
+    if args.mode == "varlen":
+        varlen_bench(args)
         return
 
     import torch
