@@ -204,6 +204,69 @@ def varlen_bench(args):
     print(json.dumps(line), flush=True)
 
 
+def prologue_bench(args):
+    """Forward with the fused input prologue on raw projections (the
+    workload's sizes; q, k unnormalised, beta logits, and for scalar gates
+    the gate input with per-head A_log, dt_bias), timed as whole calls.
+    Beside it, the same forward after an unfused pre-pass in plain torch ops
+    on the GPU (L2 norm, scale, sigmoid, gate), which the prologue replaces."""
+    import torch
+    import delta_rule_rnn_amd as dra
+    from delta_rule_rnn_amd.inputs import WORKLOADS, generate_raw
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = {n: (t.to(dev) if t is not None else None) for n, t in generate_raw(w).items()}
+    has_beta = w.kind != "decay_la"
+    scale = w.Dk ** -0.5
+    pro = dra.Prologue(qk_l2norm=True, scale=scale, beta_sigmoid=has_beta,
+                       A_log=d["A_log"], dt_bias=d["dt_bias"])
+    ws = dra.ops.alloc_workspace(w.kind, d["q"], d["v"], w.C)
+
+    def fused():
+        return dra.forward(w.kind, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], workspace=ws,
+                           prologue=pro)
+
+    def unfused():
+        qf, kf = d["q"].float(), d["k"].float()
+        q = (qf / torch.sqrt((qf * qf).sum(-1, keepdim=True) + 1e-6) * scale).to(d["q"].dtype)
+        k = (kf / torch.sqrt((kf * kf).sum(-1, keepdim=True) + 1e-6)).to(d["k"].dtype)
+        beta = torch.sigmoid(d["beta"]) if has_beta else None
+        g = d["g"]
+        if d["A_log"] is not None:
+            g = -torch.exp(d["A_log"]) * torch.nn.functional.softplus(g + d["dt_bias"])
+        return dra.forward(w.kind, q, k, d["v"], g, beta, d["h0"], workspace=ws)
+
+    def timeit(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1000.0 / args.steps
+
+    ms = timeit(fused)
+    ms_unfused = timeit(unfused)
+    tokens = w.B * w.T
+    line = {
+        "metric": "fwd tokens/sec (1 GPU) with the fused input prologue", "value": round(tokens / (ms / 1000.0), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if d["q"].dtype == torch.bfloat16 else "f32", "data": "synthetic",
+        "config": {"workload": f"{w.kind}_fwd+prologue B={w.B} H={w.H} T={w.T} dk={w.Dk} dv={w.Dv} C={w.C}",
+                   "prologue": "qk_l2norm, scale dk^-1/2" + (", beta sigmoid" if has_beta else "")
+                               + (", gate generation" if d["A_log"] is not None else ""),
+                   "parallelism": "single GPU"},
+        "unfused_prepass": {"ms_per_step": round(ms_unfused, 4),
+                            "tokens_per_s": round(tokens / (ms_unfused / 1000.0), 1)},
+        "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -214,10 +277,11 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens of the workload the CPU oracle is timed on")
     ap.add_argument("--cpu-threads", type=int, default=0)
-    ap.add_argument("--mode", choices=("prefill", "decode", "varlen"), default="prefill",
+    ap.add_argument("--mode", choices=("prefill", "decode", "varlen", "prologue"), default="prefill",
                     help="prefill: the chunked forward (the benchmark line); decode: the "
                          "recurrent step on a serving-sized batch; varlen: the forward over "
-                         "packed sequences of mixed lengths with the workload's token count")
+                         "packed sequences of mixed lengths with the workload's token count; "
+                         "prologue: the forward with the fused input prologue on raw inputs")
     ap.add_argument("--decode-batch", type=int, default=64, help="sequences per decode call")
     ap.add_argument("--decode-tokens", type=int, default=1, help="new tokens per sequence per call")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -247,6 +311,9 @@ def main():
         return
     if args.mode == "varlen":
         varlen_bench(args)
+        return
+    if args.mode == "prologue":
+        prologue_bench(args)
         return
 
     import torch

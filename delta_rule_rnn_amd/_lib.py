@@ -28,6 +28,11 @@ SIGNATURES = {
     "kda_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "gdn_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "decay_la_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
+    "dr_forward": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp,
+                        _vp]),
+    "dr_forward_varlen": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp,
+                               _vp, _sz, _vp, _vp]),
+    "dr_decode": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp]),
     "dr_chunk_cumsum": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "dr_kda_prep": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp]),
     "dr_intra": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp, _vp]),
@@ -35,6 +40,16 @@ SIGNATURES = {
     "dr_status_string": (ctypes.c_char_p, [_i]),
     "dr_abi_version": (_i, []),
 }
+
+
+
+class DrPrologue(ctypes.Structure):
+    """struct dr_prologue of include/deltarule.h."""
+    _fields_ = [("ops", ctypes.c_uint), ("scale", ctypes.c_float), ("A_log", ctypes.c_void_p),
+                ("dt_bias", ctypes.c_void_p)]
+
+
+PRO_QK_L2NORM, PRO_BETA_SIGMOID, PRO_BETA_X2, PRO_GATE = 0x1, 0x2, 0x4, 0x8
 
 _LIB = None
 

@@ -55,6 +55,50 @@ template <typename T> __device__ __forceinline__ T from_f(float x);
 template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
 template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
 
+// ---- input prologue -------------------------------------------------------
+// Optional elementwise pre-pass on the raw inputs, applied where the kernels
+// load them (page "Gated DeltaNet": the gate and write strength of the layer's
+// forward, section "门控与 Head 映射", and the token loads of the recurrent
+// kernel, "加载 Token 与写入系数"):
+//   PRO_QK_L2NORM     q, k <- x / sqrt(sum_d x_d^2 + 1e-6)   (per token, head)
+//   (always)          q <- q * scale, after the normalisation
+//   PRO_BETA_SIGMOID  beta <- 1 / (1 + exp(-beta)),  PRO_BETA_X2: doubled
+//   PRO_GATE          scalar gates: g <- -exp(A_log[h]) * softplus(g + dt_bias[h])
+enum : unsigned { PRO_QK_L2NORM = 1u, PRO_BETA_SIGMOID = 2u, PRO_BETA_X2 = 4u, PRO_GATE = 8u };
+constexpr float kNormEps = 1e-6f;
+
+struct Prologue {
+    unsigned ops;
+    float scale;
+    const float* A_log;     // [H], PRO_GATE only
+    const float* dt_bias;   // [H] or null
+};
+
+// The prologue's per-head constants: ops, query scale, exp(A_log[h]) and
+// dt_bias[h].
+struct ProHead {
+    unsigned ops;
+    float scale, gA, gdt;
+};
+__device__ __forceinline__ ProHead pro_head(const Prologue& p, int h) {
+    ProHead r{p.ops, p.scale, 1.f, 0.f};
+    if (p.ops & PRO_GATE) {
+        r.gA = expf(p.A_log[h]);
+        r.gdt = p.dt_bias ? p.dt_bias[h] : 0.f;
+    }
+    return r;
+}
+// log(1 + e^x) without overflow: max(x, 0) + log1p(e^-|x|)
+__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
+__device__ __forceinline__ float pro_gate(const ProHead& p, float a) {
+    return (p.ops & PRO_GATE) ? -p.gA * softplus_f(a + p.gdt) : a;
+}
+__device__ __forceinline__ float pro_beta(const ProHead& p, float b) {
+    if (!(p.ops & PRO_BETA_SIGMOID)) return b;
+    const float s = 1.f / (1.f + expf(-b));
+    return (p.ops & PRO_BETA_X2) ? 2.f * s : s;
+}
+
 __device__ __forceinline__ void mma(f32x4& c, const Frag<bf16>& a, const Frag<bf16>& b) {
     c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
 }

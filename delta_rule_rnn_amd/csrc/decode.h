@@ -19,7 +19,8 @@
 // dot products over the key channels need no cross-lane reduction, and the
 // state is read and written once per call with 256-byte row segments.  The
 // token's k, q and gate are staged in LDS and read as broadcasts.  All
-// arithmetic is fp32.
+// arithmetic is fp32.  With PRO, the input prologue (common.h) is applied to
+// each token's q, k, gate and beta as they are loaded.
 #pragma once
 
 #include "common.h"
@@ -28,11 +29,11 @@ namespace dr {
 
 // At least two waves per SIMD (at most 256 VGPRs): the state column takes Dk
 // registers and the compiler would otherwise also keep the staged key there.
-template <int KIND, typename T, int DK, int DV>
+template <int KIND, typename T, int DK, int DV, bool PRO>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                     const T* __restrict__ v, const float* __restrict__ g,
                                                     const float* __restrict__ beta, float* __restrict__ state,
-                                                    T* __restrict__ o, int Tlen, int H)
+                                                    T* __restrict__ o, int Tlen, int H, Prologue pro)
 {
     constexpr int NS = DV / 64;                 // workgroups per (b, h)
     constexpr bool DELTA = KIND != KIND_LA;
@@ -48,6 +49,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     const int b = chain / H, h = chain % H;
     const int col = slice * 64 + lane;
     float* st = state + (size_t)chain * DK * DV + col;
+    ProHead ph{};
+    if constexpr (PRO) ph = pro_head(pro, h);
 
     float S[DK];
 #pragma unroll
@@ -55,14 +58,47 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 
     for (int t = 0; t < Tlen; ++t) {
         const size_t row = ((size_t)b * Tlen + t) * H + h;
+        constexpr int NPL = DK / 64;     // channels per lane
+        float kl[NPL], ql[NPL];
 #pragma unroll
-        for (int d = lane; d < DK; d += 64) {
-            sk[d] = to_f(k[row * DK + d]);
-            sq[d] = to_f(q[row * DK + d]);
+        for (int j = 0; j < NPL; ++j) {
+            kl[j] = to_f(k[row * DK + lane + 64 * j]);
+            ql[j] = to_f(q[row * DK + lane + 64 * j]);
+        }
+        if constexpr (PRO) {
+            // L2 normalisation over the DK channels (a butterfly over the
+            // wave), then the query scale
+            float nk = 1.f, nq = ph.scale;
+            if (ph.ops & PRO_QK_L2NORM) {
+                float sk2 = 0.f, sq2 = 0.f;
+#pragma unroll
+                for (int j = 0; j < NPL; ++j) {
+                    sk2 += kl[j] * kl[j];
+                    sq2 += ql[j] * ql[j];
+                }
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    sk2 += __shfl_xor(sk2, off, 64);
+                    sq2 += __shfl_xor(sq2, off, 64);
+                }
+                nk = 1.f / sqrtf(sk2 + kNormEps);
+                nq *= 1.f / sqrtf(sq2 + kNormEps);
+            }
+#pragma unroll
+            for (int j = 0; j < NPL; ++j) {
+                kl[j] *= nk;
+                ql[j] *= nq;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) {
+            const int d = lane + 64 * j;
+            sk[d] = kl[j];
+            sq[d] = ql[j];
             if constexpr (PERCH) sa[d] = __builtin_amdgcn_exp2f(g[row * DK + d] * kLog2e);
         }
-        const float a = PERCH ? 1.f : __builtin_amdgcn_exp2f(g[row] * kLog2e);
-        const float bt = DELTA ? beta[row] : 0.f;
+        const float a = PERCH ? 1.f : __builtin_amdgcn_exp2f((PRO ? pro_gate(ph, g[row]) : g[row]) * kLog2e);
+        const float bt = DELTA ? (PRO ? pro_beta(ph, beta[row]) : beta[row]) : 0.f;
         const float vv = to_f(v[row * DV + col]);
         lds_barrier();
 

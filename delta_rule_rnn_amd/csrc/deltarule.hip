@@ -58,7 +58,36 @@ struct Problem {
     const int4* seqinfo = nullptr;
     const int* total = nullptr;
     int maxchunks = 0;
+    // input prologue (use_pro selects the kernels that apply it)
+    dr::Prologue pro{0u, 1.f, nullptr, nullptr};
+    bool use_pro = false;
 };
+
+// Checks a caller's prologue and converts it; *use is false when it is
+// absent or does nothing (no ops, scale 1).
+dr_status resolve_prologue(int kind, const dr_prologue* in, dr::Prologue* out, bool* use) {
+    *use = false;
+    *out = dr::Prologue{0u, 1.f, nullptr, nullptr};
+    if (in == nullptr) return DR_OK;
+    const unsigned known = DR_PRO_QK_L2NORM | DR_PRO_BETA_SIGMOID | DR_PRO_BETA_X2 | DR_PRO_GATE;
+    if (in->ops & ~known) return DR_ERR_INVALID_ARG;
+    if (!(in->scale == in->scale) || in->scale > 3.0e38f || in->scale < -3.0e38f) return DR_ERR_INVALID_ARG;
+    if ((in->ops & DR_PRO_BETA_X2) && !(in->ops & DR_PRO_BETA_SIGMOID)) return DR_ERR_INVALID_ARG;
+    if ((in->ops & (DR_PRO_BETA_SIGMOID | DR_PRO_BETA_X2)) && kind == DR_KIND_DECAY_LA) return DR_ERR_INVALID_ARG;
+    if (in->ops & DR_PRO_GATE) {
+        if (kind == DR_KIND_KDA) return DR_ERR_UNSUPPORTED;
+        if (!in->A_log) return DR_ERR_INVALID_ARG;
+        if ((reinterpret_cast<uintptr_t>(in->A_log) & 3u) || (reinterpret_cast<uintptr_t>(in->dt_bias) & 3u))
+            return DR_ERR_INVALID_ARG;
+    }
+    static_assert(DR_PRO_QK_L2NORM == dr::PRO_QK_L2NORM && DR_PRO_BETA_SIGMOID == dr::PRO_BETA_SIGMOID &&
+                      DR_PRO_BETA_X2 == dr::PRO_BETA_X2 && DR_PRO_GATE == dr::PRO_GATE,
+                  "prologue bits");
+    *out = dr::Prologue{in->ops, in->scale, (in->ops & DR_PRO_GATE) ? in->A_log : nullptr,
+                        (in->ops & DR_PRO_GATE) ? in->dt_bias : nullptr};
+    *use = in->ops != 0 || in->scale != 1.f;
+    return DR_OK;
+}
 
 int device_cus() {
     static int cached[64] = {0};
@@ -96,24 +125,29 @@ int pick_pfd() {
 }
 
 // ---- chunk-parallel kernel over chunks [c0, c0 + n) -----------------------
-template <int KIND, typename E, int D>
+template <int KIND, typename E, int D, bool PRO>
 dr_status launch_intra_t(const Problem& p, int c0, int n, hipStream_t st) {
     const long long items = (long long)p.B * n * p.H;
     if (items > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((dr::intra_kernel<KIND, E, D, D>), dim3((unsigned)items), dim3(dr::kThreads), 0, st,
+    hipLaunchKernelGGL((dr::intra_kernel<KIND, E, D, D, PRO>), dim3((unsigned)items), dim3(dr::kThreads), 0, st,
                        static_cast<const E*>(p.q), static_cast<const E*>(p.k), static_cast<const E*>(p.v),
-                       p.g, p.beta, p.ws, p.flags, p.T, p.H, p.NT, c0, n, p.B);
+                       p.g, p.beta, p.ws, p.flags, p.T, p.H, p.NT, c0, n, p.B, p.pro);
     return check_launch();
+}
+
+template <int KIND, bool PRO>
+dr_status launch_intra_p(const Problem& p, int c0, int n, hipStream_t st) {
+    if (p.dtype == DR_BF16) {
+        if (p.D == 64) return launch_intra_t<KIND, bf16, 64, PRO>(p, c0, n, st);
+        return launch_intra_t<KIND, bf16, 128, PRO>(p, c0, n, st);
+    }
+    if (p.D == 64) return launch_intra_t<KIND, float, 64, PRO>(p, c0, n, st);
+    return launch_intra_t<KIND, float, 128, PRO>(p, c0, n, st);
 }
 
 template <int KIND>
 dr_status launch_intra_k(const Problem& p, int c0, int n, hipStream_t st) {
-    if (p.dtype == DR_BF16) {
-        if (p.D == 64) return launch_intra_t<KIND, bf16, 64>(p, c0, n, st);
-        return launch_intra_t<KIND, bf16, 128>(p, c0, n, st);
-    }
-    if (p.D == 64) return launch_intra_t<KIND, float, 64>(p, c0, n, st);
-    return launch_intra_t<KIND, float, 128>(p, c0, n, st);
+    return p.use_pro ? launch_intra_p<KIND, true>(p, c0, n, st) : launch_intra_p<KIND, false>(p, c0, n, st);
 }
 
 dr_status launch_intra(const Problem& p, int c0, int n, hipStream_t st) {
@@ -194,15 +228,21 @@ Problem make_problem(int kind, const void* q, const void* k, const void* v, cons
 
 dr_status forward(int kind, const void* q, const void* k, const void* v, const float* g,
                   const float* beta, const float* h0, void* o, float* hT, int B, int T, int H, int Dk,
-                  int Dv, int C, int dtype, void* ws, size_t ws_bytes, unsigned* flags, void* stream) {
+                  int Dv, int C, int dtype, void* ws, size_t ws_bytes, unsigned* flags, void* stream,
+                  const dr_prologue* pro = nullptr) {
     dr_status s = validate(kind, q, k, v, g, beta, B, T, H, Dk, Dv, C, dtype);
     if (s != DR_OK) return s;
+    dr::Prologue pr;
+    bool use_pro;
+    if ((s = resolve_prologue(kind, pro, &pr, &use_pro)) != DR_OK) return s;
     if (T > 0 && !o) return DR_ERR_INVALID_ARG;
     if (!aligned16(o) || !aligned16(h0) || !aligned16(hT) || !aligned16(ws)) return DR_ERR_INVALID_ARG;
     const size_t need = dr_workspace_bytes(kind, B, T, H, Dk, Dv, C, dtype);
     if (T > 0 && (ws == nullptr || ws_bytes < need)) return DR_ERR_WORKSPACE;
     if (T == 0 && hT == nullptr) return DR_OK;
-    const Problem p = make_problem(kind, q, k, v, g, beta, o, B, T, H, Dk, dtype, ws, flags);
+    Problem p = make_problem(kind, q, k, v, g, beta, o, B, T, H, Dk, dtype, ws, flags);
+    p.pro = pr;
+    p.use_pro = use_pro;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (T == 0) return launch_inter(p, h0, hT, 0, 0, st);
     s = launch_intra(p, 0, p.NT, st);
@@ -231,31 +271,38 @@ VarlenLayout varlen_layout(int N, int T, int H, int D, int dtype) {
     return L;
 }
 
-template <int KIND, typename E, int D>
+template <int KIND, typename E, int D, bool PRO>
 dr_status launch_intra_varlen_t(const Problem& p, hipStream_t st) {
     const long long items = (long long)p.maxchunks * p.H;
     if (items > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((dr::intra_varlen_kernel<KIND, E, D, D>), dim3((unsigned)items), dim3(dr::kThreads), 0, st,
-                       static_cast<const E*>(p.q), static_cast<const E*>(p.k), static_cast<const E*>(p.v), p.g,
-                       p.beta, p.ws, p.flags, p.table, p.total, p.H, p.maxchunks);
+    hipLaunchKernelGGL((dr::intra_varlen_kernel<KIND, E, D, D, PRO>), dim3((unsigned)items), dim3(dr::kThreads), 0,
+                       st, static_cast<const E*>(p.q), static_cast<const E*>(p.k), static_cast<const E*>(p.v), p.g,
+                       p.beta, p.ws, p.flags, p.table, p.total, p.H, p.maxchunks, p.pro);
     return check_launch();
+}
+template <int KIND, bool PRO>
+dr_status launch_intra_varlen_p(const Problem& p, hipStream_t st) {
+    if (p.dtype == DR_BF16) {
+        if (p.D == 64) return launch_intra_varlen_t<KIND, bf16, 64, PRO>(p, st);
+        return launch_intra_varlen_t<KIND, bf16, 128, PRO>(p, st);
+    }
+    if (p.D == 64) return launch_intra_varlen_t<KIND, float, 64, PRO>(p, st);
+    return launch_intra_varlen_t<KIND, float, 128, PRO>(p, st);
 }
 template <int KIND>
 dr_status launch_intra_varlen_k(const Problem& p, hipStream_t st) {
-    if (p.dtype == DR_BF16) {
-        if (p.D == 64) return launch_intra_varlen_t<KIND, bf16, 64>(p, st);
-        return launch_intra_varlen_t<KIND, bf16, 128>(p, st);
-    }
-    if (p.D == 64) return launch_intra_varlen_t<KIND, float, 64>(p, st);
-    return launch_intra_varlen_t<KIND, float, 128>(p, st);
+    return p.use_pro ? launch_intra_varlen_p<KIND, true>(p, st) : launch_intra_varlen_p<KIND, false>(p, st);
 }
 
 dr_status forward_varlen(int kind, const void* q, const void* k, const void* v, const float* g,
                          const float* beta, const int* cu_seqlens, int N, const float* h0, void* o, float* hT,
                          int T, int H, int Dk, int Dv, int C, int dtype, void* ws, size_t ws_bytes,
-                         unsigned* flags, void* stream) {
+                         unsigned* flags, void* stream, const dr_prologue* pro = nullptr) {
     dr_status s = validate(kind, q, k, v, g, beta, 1, T, H, Dk, Dv, C, dtype);
     if (s != DR_OK) return s;
+    dr::Prologue pr;
+    bool use_pro;
+    if ((s = resolve_prologue(kind, pro, &pr, &use_pro)) != DR_OK) return s;
     if (N < 1 || !cu_seqlens) return DR_ERR_INVALID_ARG;
     if ((long long)N * H * (Dv / 16) > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
     if (T > 0 && !o) return DR_ERR_INVALID_ARG;
@@ -269,6 +316,8 @@ dr_status forward_varlen(int kind, const void* q, const void* k, const void* v, 
     p.seqinfo = reinterpret_cast<const int4*>(w + L.seqinfo);
     p.total = reinterpret_cast<const int*>(w + L.total);
     p.maxchunks = L.maxchunks;
+    p.pro = pr;
+    p.use_pro = use_pro;
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipLaunchKernelGGL(dr::varlen_table_kernel, dim3(1), dim3(1024), 0, st, cu_seqlens, N, T, L.maxchunks,
                        reinterpret_cast<int4*>(w + L.table), reinterpret_cast<int4*>(w + L.seqinfo),
@@ -288,43 +337,58 @@ dr_status forward_varlen(int kind, const void* q, const void* k, const void* v, 
 }
 
 // ---- recurrent decode step --------------------------------------------------
-template <int KIND, typename E, int D>
-dr_status launch_decode_t(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                          float* state, void* o, int B, int T, int H, hipStream_t st) {
-    dim3 grid((unsigned)((long long)B * H * (D / 64)));
-    hipLaunchKernelGGL((dr::decode_kernel<KIND, E, D, D>), grid, dim3(64), 0, st, static_cast<const E*>(q),
-                       static_cast<const E*>(k), static_cast<const E*>(v), g, beta, state, static_cast<E*>(o), T, H);
+struct DecodeArgs {
+    const void *q, *k, *v;
+    const float *g, *beta;
+    float* state;
+    void* o;
+    int B, T, H;
+    dr::Prologue pro;
+};
+
+template <int KIND, typename E, int D, bool PRO>
+dr_status launch_decode_t(const DecodeArgs& a, hipStream_t st) {
+    dim3 grid((unsigned)((long long)a.B * a.H * (D / 64)));
+    hipLaunchKernelGGL((dr::decode_kernel<KIND, E, D, D, PRO>), grid, dim3(64), 0, st, static_cast<const E*>(a.q),
+                       static_cast<const E*>(a.k), static_cast<const E*>(a.v), a.g, a.beta, a.state,
+                       static_cast<E*>(a.o), a.T, a.H, a.pro);
     return check_launch();
 }
 
-template <int KIND>
-dr_status launch_decode_k(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                          float* state, void* o, int B, int T, int H, int D, int dtype, hipStream_t st) {
+template <int KIND, bool PRO>
+dr_status launch_decode_p(const DecodeArgs& a, int D, int dtype, hipStream_t st) {
     if (dtype == DR_BF16) {
-        if (D == 64) return launch_decode_t<KIND, bf16, 64>(q, k, v, g, beta, state, o, B, T, H, st);
-        return launch_decode_t<KIND, bf16, 128>(q, k, v, g, beta, state, o, B, T, H, st);
+        if (D == 64) return launch_decode_t<KIND, bf16, 64, PRO>(a, st);
+        return launch_decode_t<KIND, bf16, 128, PRO>(a, st);
     }
-    if (D == 64) return launch_decode_t<KIND, float, 64>(q, k, v, g, beta, state, o, B, T, H, st);
-    return launch_decode_t<KIND, float, 128>(q, k, v, g, beta, state, o, B, T, H, st);
+    if (D == 64) return launch_decode_t<KIND, float, 64, PRO>(a, st);
+    return launch_decode_t<KIND, float, 128, PRO>(a, st);
+}
+
+template <int KIND>
+dr_status launch_decode_k(const DecodeArgs& a, bool use_pro, int D, int dtype, hipStream_t st) {
+    return use_pro ? launch_decode_p<KIND, true>(a, D, dtype, st) : launch_decode_p<KIND, false>(a, D, dtype, st);
 }
 
 dr_status decode(int kind, const void* q, const void* k, const void* v, const float* g, const float* beta,
-                 float* state, void* o, int B, int T, int H, int Dk, int Dv, int dtype, void* stream) {
+                 float* state, void* o, int B, int T, int H, int Dk, int Dv, int dtype, void* stream,
+                 const dr_prologue* pro = nullptr) {
     // same argument rules as the forward, with the chunk size not involved
     dr_status s = validate(kind, q, k, v, g, beta, B, T, H, Dk, Dv, dr::kChunk, dtype);
     if (s != DR_OK) return s;
+    dr::Prologue pr;
+    bool use_pro;
+    if ((s = resolve_prologue(kind, pro, &pr, &use_pro)) != DR_OK) return s;
     if (T > 0 && (!o || !state)) return DR_ERR_INVALID_ARG;
     if (!aligned16(o) || !aligned16(state)) return DR_ERR_INVALID_ARG;
     if (T == 0) return DR_OK;
     if ((long long)B * H * (Dv / 64) > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const DecodeArgs a{q, k, v, g, kind == DR_KIND_DECAY_LA ? nullptr : beta, state, o, B, T, H, pr};
     switch (kind) {
-        case DR_KIND_KDA:
-            return launch_decode_k<dr::KIND_KDA>(q, k, v, g, beta, state, o, B, T, H, Dk, dtype, st);
-        case DR_KIND_GDN:
-            return launch_decode_k<dr::KIND_GDN>(q, k, v, g, beta, state, o, B, T, H, Dk, dtype, st);
-        default:
-            return launch_decode_k<dr::KIND_LA>(q, k, v, g, nullptr, state, o, B, T, H, Dk, dtype, st);
+        case DR_KIND_KDA: return launch_decode_k<dr::KIND_KDA>(a, use_pro, Dk, dtype, st);
+        case DR_KIND_GDN: return launch_decode_k<dr::KIND_GDN>(a, use_pro, Dk, dtype, st);
+        default: return launch_decode_k<dr::KIND_LA>(a, use_pro, Dk, dtype, st);
     }
 }
 
@@ -437,6 +501,32 @@ dr_status decay_la_decode(const void* q, const void* k, const void* v, const flo
     return decode(DR_KIND_DECAY_LA, q, k, v, g, nullptr, state, o, B, T, H, Dk, Dv, dtype, stream);
 }
 
+dr_status dr_forward(int kind, const void* q, const void* k, const void* v, const float* g, const float* beta,
+                     const float* h0, void* o, float* hT, int B, int T, int H, int Dk, int Dv, int C, int dtype,
+                     const dr_prologue* prologue, void* workspace, size_t workspace_bytes, unsigned* flags,
+                     void* stream) {
+    if (kind < 0 || kind > 2) return DR_ERR_INVALID_ARG;
+    return forward(kind, q, k, v, g, kind == DR_KIND_DECAY_LA ? nullptr : beta, h0, o, hT, B, T, H, Dk, Dv, C,
+                   dtype, workspace, workspace_bytes, flags, stream, prologue);
+}
+
+dr_status dr_forward_varlen(int kind, const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, const int* cu_seqlens, int N, const float* h0, void* o, float* hT,
+                            int T, int H, int Dk, int Dv, int C, int dtype, const dr_prologue* prologue,
+                            void* workspace, size_t workspace_bytes, unsigned* flags, void* stream) {
+    if (kind < 0 || kind > 2) return DR_ERR_INVALID_ARG;
+    return forward_varlen(kind, q, k, v, g, kind == DR_KIND_DECAY_LA ? nullptr : beta, cu_seqlens, N, h0, o, hT,
+                          T, H, Dk, Dv, C, dtype, workspace, workspace_bytes, flags, stream, prologue);
+}
+
+dr_status dr_decode(int kind, const void* q, const void* k, const void* v, const float* g, const float* beta,
+                    float* state, void* o, int B, int T, int H, int Dk, int Dv, int dtype,
+                    const dr_prologue* prologue, void* stream) {
+    if (kind < 0 || kind > 2) return DR_ERR_INVALID_ARG;
+    return decode(kind, q, k, v, g, kind == DR_KIND_DECAY_LA ? nullptr : beta, state, o, B, T, H, Dk, Dv, dtype,
+                  stream, prologue);
+}
+
 dr_status dr_chunk_cumsum(const float* g, float* gamma, int B, int T, int H, int D, int C, void* stream) {
     if (B <= 0 || H <= 0 || T < 0 || D < 1 || D > 256) return DR_ERR_INVALID_ARG;
     if (C != dr::kChunk) return DR_ERR_UNSUPPORTED;
@@ -490,6 +580,6 @@ const char* dr_status_string(int status) {
     }
 }
 
-int dr_abi_version(void) { return 1; }
+int dr_abi_version(void) { return 2; }
 
 }  // extern "C"

@@ -135,11 +135,12 @@ __device__ __forceinline__ void intra_load(IntraIn<KIND, T, DK, DV>& in, const T
 
 // Steps a1-a3 (and the output operands) of one chunk from inputs already in
 // registers (nvalid of its C rows are tokens); writes the chunk's record at
-// recb.
-template <int KIND, typename T, int DK, int DV>
+// recb.  With PRO, the input prologue (common.h) is applied to the loaded
+// q, k, beta and scalar gates first.
+template <int KIND, typename T, int DK, int DV, bool PRO>
 __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, uint8_t* smem,
                                             unsigned* __restrict__ flags,
-                                            uint8_t* __restrict__ recb, int nvalid)
+                                            uint8_t* __restrict__ recb, int nvalid, const ProHead& ph)
 {
     using Cfg = IntraCfg<KIND, T, DK, DV>;
     using R = Rec<T, DK, DV>;
@@ -185,7 +186,36 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
         vv[i] = ok ? in.vv[i] : VT{};
         if constexpr (PERCH) gv[i] = ok ? in.gv[i] : VG{};
     }
-    if (tid < C) sBeta[tid] = (DELTA && tid < nvalid) ? in.bt : 0.f;
+    if (tid < C) sBeta[tid] = (DELTA && tid < nvalid) ? (PRO ? pro_beta(ph, in.bt) : in.bt) : 0.f;
+    // prologue: per-row factors of k and q (L2 normalisation, query scale).
+    // A row's DK channels sit in the NCG = 32 adjacent lanes of one half
+    // wave, so its sum of squares is a butterfly over lane offsets 1..16.
+    float nk[PL], nq[PL];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) nk[i] = nq[i] = 1.f;
+    if constexpr (PRO) {
+        if (ph.ops & PRO_QK_L2NORM) {
+#pragma unroll
+            for (int i = 0; i < PL; ++i) {
+                float sk = 0.f, sq = 0.f;
+#pragma unroll
+                for (int j = 0; j < CPT; ++j) {
+                    const float kk = (float)kv[i][j], qq = (float)qv[i][j];
+                    sk += kk * kk;
+                    sq += qq * qq;
+                }
+#pragma unroll
+                for (int off = 1; off < NCG; off <<= 1) {
+                    sk += __shfl_xor(sk, off, 64);
+                    sq += __shfl_xor(sq, off, 64);
+                }
+                nk[i] = 1.f / sqrtf(sk + kNormEps);
+                nq[i] = 1.f / sqrtf(sq + kNormEps);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < PL; ++i) nq[i] *= ph.scale;
+    }
 
     // ---- P1: a1 (gamma) + a2 (prep) -------------------------------------
     float gam[PL][CPT];
@@ -233,7 +263,7 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
     } else {
         // scalar gate: wave 0 scans the 64 positions
         if (wave == 0) {
-            float x = (lane < nvalid) ? in.gs : 0.f;
+            float x = (lane < nvalid) ? (PRO ? pro_gate(ph, in.gs) : in.gs) : 0.f;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float y = __shfl_up(x, off, 64);
@@ -263,7 +293,7 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
                 VT kp, km, qp;
 #pragma unroll
                 for (int j = 0; j < CPT; ++j) {
-                    const float kk = (float)kv[i][j], qq = (float)qv[i][j];
+                    const float kk = (float)kv[i][j] * nk[i], qq = (float)qv[i][j] * nq[i];
                     const float e = __builtin_amdgcn_exp2f(gam[i][j]);
                     const float ei = __builtin_amdgcn_exp2f(-gam[i][j]);
                     mxneg = fmaxf(mxneg, -gam[i][j]);
@@ -277,9 +307,17 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
                 *reinterpret_cast<VT*>(sKm + p * LDK + ch0) = km;
                 *reinterpret_cast<VT*>(sQp + p * LDK + ch0) = qp;
             } else {
-                *reinterpret_cast<VT*>(sKp + p * LDK + ch0) = kv[i];
-                *reinterpret_cast<VT*>(sQp + p * LDK + ch0) = qv[i];
-                const float r = __builtin_amdgcn_exp2f(glast[0] - gam[i][0]);   // <= 1
+                VT kn = kv[i], qn = qv[i];
+                if constexpr (PRO) {
+#pragma unroll
+                    for (int j = 0; j < CPT; ++j) {
+                        kn[j] = from_f<T>((float)kv[i][j] * nk[i]);
+                        qn[j] = from_f<T>((float)qv[i][j] * nq[i]);
+                    }
+                }
+                *reinterpret_cast<VT*>(sKp + p * LDK + ch0) = kn;
+                *reinterpret_cast<VT*>(sQp + p * LDK + ch0) = qn;
+                const float r = __builtin_amdgcn_exp2f(glast[0] - gam[i][0]) * nk[i];   // <= 1 (times nk)
 #pragma unroll
                 for (int j = 0; j < CPT; ++j) kb[j][i] = (float)kv[i][j] * r;
             }
@@ -567,11 +605,11 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
 // chunks, so the rows of beta and of scalar gates that neighbouring heads
 // share are fetched while still cached.  (Grouping a chunk's heads on one
 // XCD, or numbering chunks fastest, measured slower.)
-template <int KIND, typename T, int DK, int DV>
+template <int KIND, typename T, int DK, int DV, bool PRO>
 __global__ __launch_bounds__(kThreads, 2) void intra_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, uint8_t* __restrict__ ws,
-    unsigned* __restrict__ flags, int Tlen, int H, int NT, int c0, int n, int B)
+    unsigned* __restrict__ flags, int Tlen, int H, int NT, int c0, int n, int B, Prologue pro)
 {
     using Cfg = IntraCfg<KIND, T, DK, DV>;
     __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::BYTES];
@@ -582,8 +620,10 @@ __global__ __launch_bounds__(kThreads, 2) void intra_kernel(
     const int nvalid = min(kChunk, Tlen - c * kChunk);
     IntraIn<KIND, T, DK, DV> in;
     intra_load<KIND, T, DK, DV>(in, q, k, v, g, beta, ((size_t)b * Tlen + (size_t)c * kChunk) * H + h, nvalid, H);
-    intra_chunk<KIND, T, DK, DV>(in, smem, flags, ws + (((size_t)b * H + h) * NT + c) * Rec<T, DK, DV>::BYTES,
-                                 nvalid);
+    ProHead ph{};
+    if constexpr (PRO) ph = pro_head(pro, h);
+    intra_chunk<KIND, T, DK, DV, PRO>(in, smem, flags,
+                                      ws + (((size_t)b * H + h) * NT + c) * Rec<T, DK, DV>::BYTES, nvalid, ph);
 }
 
 // Packed sequences: one workgroup per (chunk slot, head), heads fastest.  The
@@ -591,12 +631,12 @@ __global__ __launch_bounds__(kThreads, 2) void intra_kernel(
 // and its valid rows; slots past the table's count exit at once.  Records go
 // to index h * maxchunks + slot, so each sequence's chunks are contiguous for
 // the state pass.
-template <int KIND, typename T, int DK, int DV>
+template <int KIND, typename T, int DK, int DV, bool PRO>
 __global__ __launch_bounds__(kThreads, 2) void intra_varlen_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, uint8_t* __restrict__ ws,
     unsigned* __restrict__ flags, const int4* __restrict__ table, const int* __restrict__ total, int H,
-    int maxchunks)
+    int maxchunks, Prologue pro)
 {
     using Cfg = IntraCfg<KIND, T, DK, DV>;
     __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::BYTES];
@@ -606,8 +646,10 @@ __global__ __launch_bounds__(kThreads, 2) void intra_varlen_kernel(
     const int4 e = table[slot];     // {sequence, first token, valid rows, -}
     IntraIn<KIND, T, DK, DV> in;
     intra_load<KIND, T, DK, DV>(in, q, k, v, g, beta, (size_t)e.y * H + h, e.z, H);
-    intra_chunk<KIND, T, DK, DV>(in, smem, flags, ws + ((size_t)h * maxchunks + slot) * Rec<T, DK, DV>::BYTES,
-                                 e.z);
+    ProHead ph{};
+    if constexpr (PRO) ph = pro_head(pro, h);
+    intra_chunk<KIND, T, DK, DV, PRO>(in, smem, flags, ws + ((size_t)h * maxchunks + slot) * Rec<T, DK, DV>::BYTES,
+                                      e.z, ph);
 }
 
 }  // namespace dr

@@ -26,6 +26,10 @@ Workloads (name: path, sizes, distributions):
                   with a zero initial state (the GDN line of the T=32k metric)
 
 h0 is returned in the library's state layout [B, H, Dk, Dv] (fp32).
+
+generate_raw() draws the raw projections the input prologue takes instead
+(unnormalised q, k; beta logits; the scalar gate's input and its per-head
+A_log, dt_bias as the Gated DeltaNet layer initialises them).
 """
 from __future__ import annotations
 
@@ -108,6 +112,44 @@ def generate(w: Workload, device: Optional[str] = None) -> Dict[str, Optional[to
     dt = io_torch_dtype(w)
     out = {"q": q.to(dt).contiguous(), "k": k.to(dt).contiguous(), "v": v.to(dt).contiguous(),
            "g": g.contiguous(), "beta": beta, "h0": h0}
+    if device is not None:
+        out = {n: (t.to(device) if t is not None else None) for n, t in out.items()}
+    return out
+
+
+def generate_raw(w: Workload, device: Optional[str] = None) -> Dict[str, Optional[torch.Tensor]]:
+    """Raw inputs for the input prologue, in the draw order q, k, row scales,
+    v, beta logits, gates, A_log, h0:
+      q, k ~ N(0,1) times a per-(b,t,h) scale U[0.25, 4] (not normalised);
+      v ~ N(0,1); beta logits ~ N(0,1) (None for decay_la);
+      kda: g = ln U[gate_lo, gate_hi] per channel (no gate generation);
+      gdn, decay_la: gate input a ~ N(0,1), A_log = ln U[0.01, 16] and
+      dt_bias = 1 per head (the layer's initialisation on the Gated DeltaNet
+      page, section "输入投影").
+    Returns the dict of generate() plus "A_log" and "dt_bias" (fp32 [H] or
+    None)."""
+    gen = torch.Generator().manual_seed(w.seed)
+    B, T, H, Dk, Dv = w.B, w.T, w.H, w.Dk, w.Dv
+    q = torch.randn(B, T, H, Dk, generator=gen)
+    k = torch.randn(B, T, H, Dk, generator=gen)
+    sc = torch.rand(2, B, T, H, 1, generator=gen) * 3.75 + 0.25
+    q, k = q * sc[0], k * sc[1]
+    v = torch.randn(B, T, H, Dv, generator=gen)
+    beta = None if w.kind == "decay_la" else torch.randn(B, T, H, generator=gen)
+    A_log = dt_bias = None
+    if w.kind == "kda":
+        a = torch.rand(B, T, H, Dk, generator=gen) * (w.gate_hi - w.gate_lo) + w.gate_lo
+        g = torch.log(a)
+    else:
+        g = torch.randn(B, T, H, generator=gen)
+        A_log = torch.log(torch.rand(H, generator=gen) * (16.0 - 0.01) + 0.01)
+        dt_bias = torch.ones(H)
+    h0 = None
+    if w.h0_std > 0:
+        h0 = torch.randn(B, H, Dk, Dv, generator=gen) * w.h0_std
+    dt = io_torch_dtype(w)
+    out = {"q": q.to(dt).contiguous(), "k": k.to(dt).contiguous(), "v": v.to(dt).contiguous(),
+           "g": g.contiguous(), "beta": beta, "h0": h0, "A_log": A_log, "dt_bias": dt_bias}
     if device is not None:
         out = {n: (t.to(device) if t is not None else None) for n, t in out.items()}
     return out

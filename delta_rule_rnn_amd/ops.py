@@ -7,6 +7,8 @@ library as raw pointers, together with torch's current HIP stream.
 """
 from __future__ import annotations
 
+import ctypes
+from dataclasses import dataclass
 from typing import Optional, Tuple
 
 import torch
@@ -59,6 +61,39 @@ def _need(t: Optional[torch.Tensor], name: str, dtype=None, shape=None):
         raise DeltaRuleError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
+@dataclass
+class Prologue:
+    """Input prologue applied inside the kernels (struct dr_prologue):
+    q, k L2-normalised per token and head (eps 1e-6) when ``qk_l2norm``, then
+    q scaled by ``scale``; beta through a sigmoid (doubled with ``beta_x2``);
+    and, when ``A_log`` is given (scalar gates only), the gate input taken as
+    the raw projection a: g = -exp(A_log[h]) * softplus(a + dt_bias[h]).
+    A_log and dt_bias are fp32 [H] tensors on the GPU."""
+    qk_l2norm: bool = False
+    scale: float = 1.0
+    beta_sigmoid: bool = False
+    beta_x2: bool = False
+    A_log: Optional[torch.Tensor] = None
+    dt_bias: Optional[torch.Tensor] = None
+
+    def to_c(self, H: int) -> _lib.DrPrologue:
+        ops = ((_lib.PRO_QK_L2NORM if self.qk_l2norm else 0) | (_lib.PRO_BETA_SIGMOID if self.beta_sigmoid else 0)
+               | (_lib.PRO_BETA_X2 if self.beta_x2 else 0) | (_lib.PRO_GATE if self.A_log is not None else 0))
+        _need(self.A_log, "A_log", torch.float32, (H,))
+        _need(self.dt_bias, "dt_bias", torch.float32, (H,))
+        if self.dt_bias is not None and self.A_log is None:
+            raise DeltaRuleError("dt_bias without A_log")
+        return _lib.DrPrologue(ops, float(self.scale), _ptr(self.A_log), _ptr(self.dt_bias))
+
+
+def _pro_arg(prologue: Optional[Prologue], H: int):
+    """(struct to keep alive, pointer argument) for a prologue or None."""
+    if prologue is None:
+        return None, None
+    c = prologue.to_c(H)
+    return c, ctypes.addressof(c)
+
+
 def workspace_bytes(kind: str, B: int, T: int, H: int, Dk: int, Dv: int, dtype: torch.dtype,
                     chunk_size: int = CHUNK) -> int:
     code = DR_BF16 if dtype == torch.bfloat16 else DR_F32
@@ -77,7 +112,7 @@ def alloc_workspace(kind, q: torch.Tensor, v: torch.Tensor, chunk_size: int = CH
 
 
 def _forward(kind: str, q, k, v, g, beta, h0, output_final_state, chunk_size, workspace, flags,
-             stream) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+             stream, prologue=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     lib = _lib.load()
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
@@ -100,6 +135,14 @@ def _forward(kind: str, q, k, v, g, beta, h0, output_final_state, chunk_size, wo
     code = _dtype_code(q)
     common = (B, T, H, Dk, Dv, chunk_size, code, _ptr(workspace), workspace.numel())
     s = _stream(stream)
+    if prologue is not None:
+        keep, pro = _pro_arg(prologue, H)
+        st = lib.dr_forward(KINDS[kind], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o),
+                            _ptr(hT), B, T, H, Dk, Dv, chunk_size, code, pro, _ptr(workspace), workspace.numel(),
+                            _ptr(flags), s)
+        del keep
+        _check(st, "dr_forward")
+        return o, hT
     if kind == "kda":
         st = lib.kda_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT),
                          *common, _ptr(flags), s)
@@ -113,24 +156,26 @@ def _forward(kind: str, q, k, v, g, beta, h0, output_final_state, chunk_size, wo
 
 
 def kda_fwd(q, k, v, g, beta, h0=None, output_final_state=True, chunk_size=CHUNK, workspace=None,
-            flags=None, stream=None):
+            flags=None, stream=None, prologue: Optional[Prologue] = None):
     """KDA forward.  q, k [B,T,H,Dk], v [B,T,H,Dv] (bf16 or fp32); g [B,T,H,Dk]
     fp32 (ln a); beta [B,T,H] fp32; h0 [B,H,Dk,Dv] fp32 or None.
     Returns (o [B,T,H,Dv], hT [B,H,Dk,Dv] fp32 or None)."""
-    return _forward("kda", q, k, v, g, beta, h0, output_final_state, chunk_size, workspace, flags, stream)
+    return _forward("kda", q, k, v, g, beta, h0, output_final_state, chunk_size, workspace, flags, stream,
+                    prologue)
 
 
 def gdn_fwd(q, k, v, g, beta, h0=None, output_final_state=True, chunk_size=CHUNK, workspace=None,
-            flags=None, stream=None):
+            flags=None, stream=None, prologue: Optional[Prologue] = None):
     """Gated DeltaNet forward: as kda_fwd with g [B,T,H]."""
-    return _forward("gdn", q, k, v, g, beta, h0, output_final_state, chunk_size, workspace, flags, stream)
+    return _forward("gdn", q, k, v, g, beta, h0, output_final_state, chunk_size, workspace, flags, stream,
+                    prologue)
 
 
 def decay_la_fwd(q, k, v, g, h0=None, output_final_state=True, chunk_size=CHUNK, workspace=None,
-                 stream=None):
+                 stream=None, prologue: Optional[Prologue] = None):
     """Scalar-decay linear attention (no delta term): g [B,T,H], no beta."""
     return _forward("decay_la", q, k, v, g, None, h0, output_final_state, chunk_size, workspace, None,
-                    stream)
+                    stream, prologue)
 
 
 FORWARDS = {"kda": kda_fwd, "gdn": gdn_fwd, "decay_la": decay_la_fwd}
@@ -151,7 +196,7 @@ def workspace_bytes_varlen(kind: str, N: int, T: int, H: int, Dk: int, Dv: int, 
 
 
 def _forward_varlen(kind, q, k, v, g, beta, cu_seqlens, h0, output_final_state, chunk_size, workspace,
-                    flags, stream):
+                    flags, stream, prologue=None):
     lib = _lib.load()
     squeeze = q.dim() == 4
     if squeeze:
@@ -183,6 +228,14 @@ def _forward_varlen(kind, q, k, v, g, beta, cu_seqlens, h0, output_final_state, 
     if flags is not None:
         _need(flags, "flags", torch.int32, (1,))
     code, s = _dtype_code(q), _stream(stream)
+    if prologue is not None:
+        keep, pro = _pro_arg(prologue, H)
+        st = lib.dr_forward_varlen(KINDS[kind], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                                   N, _ptr(h0), _ptr(o), _ptr(hT), T, H, Dk, Dv, chunk_size, code, pro,
+                                   _ptr(workspace), workspace.numel(), _ptr(flags), s)
+        del keep
+        _check(st, "dr_forward_varlen")
+        return (o[None] if squeeze else o), hT
     common = (N, _ptr(h0), _ptr(o), _ptr(hT), T, H, Dk, Dv, chunk_size, code, _ptr(workspace),
               workspace.numel(), _ptr(flags), s)
     if kind == "kda":
@@ -196,7 +249,8 @@ def _forward_varlen(kind, q, k, v, g, beta, cu_seqlens, h0, output_final_state, 
 
 
 def forward_varlen(kind: str, q, k, v, g, beta=None, cu_seqlens=None, h0=None, output_final_state=True,
-                   chunk_size=CHUNK, workspace=None, flags=None, stream=None):
+                   chunk_size=CHUNK, workspace=None, flags=None, stream=None,
+                   prologue: Optional[Prologue] = None):
     """Forward over sequences packed along the token axis.  q, k [T,H,Dk]
     (or [1,T,H,Dk]), v [T,H,Dv]; g [T,H,Dk] (kda) or [T,H]; beta [T,H];
     cu_seqlens int32 [N+1] on the device; h0 [N,H,Dk,Dv] or None.
@@ -204,12 +258,12 @@ def forward_varlen(kind: str, q, k, v, g, beta=None, cu_seqlens=None, h0=None, o
     if cu_seqlens is None:
         raise DeltaRuleError("cu_seqlens is required")
     return _forward_varlen(kind, q, k, v, g, beta, cu_seqlens, h0, output_final_state, chunk_size,
-                           workspace, flags, stream)
+                           workspace, flags, stream, prologue)
 
 
 # ---- recurrent decode step ---------------------------------------------------
 
-def _decode(kind: str, q, k, v, g, beta, state, out, stream) -> torch.Tensor:
+def _decode(kind: str, q, k, v, g, beta, state, out, stream, prologue=None) -> torch.Tensor:
     lib = _lib.load()
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
@@ -226,6 +280,13 @@ def _decode(kind: str, q, k, v, g, beta, state, out, stream) -> torch.Tensor:
     o = torch.empty(B, T, H, Dv, dtype=dt, device=q.device) if out is None else out
     _need(o, "out", dt, (B, T, H, Dv))
     code, s = _dtype_code(q), _stream(stream)
+    if prologue is not None:
+        keep, pro = _pro_arg(prologue, H)
+        st = lib.dr_decode(KINDS[kind], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
+                           B, T, H, Dk, Dv, code, pro, s)
+        del keep
+        _check(st, "dr_decode")
+        return o
     if kind == "kda":
         st = lib.kda_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
                             B, T, H, Dk, Dv, code, s)
@@ -239,20 +300,20 @@ def _decode(kind: str, q, k, v, g, beta, state, out, stream) -> torch.Tensor:
     return o
 
 
-def kda_decode(q, k, v, g, beta, state, out=None, stream=None) -> torch.Tensor:
+def kda_decode(q, k, v, g, beta, state, out=None, stream=None, prologue: Optional[Prologue] = None) -> torch.Tensor:
     """Apply T new tokens per (b, h) to ``state`` (fp32 [B,H,Dk,Dv], updated
     in place; the layout of a forward's hT) and return o [B,T,H,Dv]."""
-    return _decode("kda", q, k, v, g, beta, state, out, stream)
+    return _decode("kda", q, k, v, g, beta, state, out, stream, prologue)
 
 
-def gdn_decode(q, k, v, g, beta, state, out=None, stream=None) -> torch.Tensor:
+def gdn_decode(q, k, v, g, beta, state, out=None, stream=None, prologue: Optional[Prologue] = None) -> torch.Tensor:
     """As kda_decode with g [B,T,H]."""
-    return _decode("gdn", q, k, v, g, beta, state, out, stream)
+    return _decode("gdn", q, k, v, g, beta, state, out, stream, prologue)
 
 
-def decay_la_decode(q, k, v, g, state, out=None, stream=None) -> torch.Tensor:
+def decay_la_decode(q, k, v, g, state, out=None, stream=None, prologue: Optional[Prologue] = None) -> torch.Tensor:
     """As gdn_decode without beta (no delta term)."""
-    return _decode("decay_la", q, k, v, g, None, state, out, stream)
+    return _decode("decay_la", q, k, v, g, None, state, out, stream, prologue)
 
 
 def decode(kind: str, q, k, v, g, beta=None, state=None, **kw) -> torch.Tensor:

@@ -13,7 +13,9 @@
  *     "TileLang 实战：KDA 从零到一--标量衰减", section 1.1; RetNet /
  *     Lightning-style decay on the page "07 · linear 路线（二）：衰减机制的演进",
  *     sections 1-2).
- * There is no output scale: callers pre-scale q if they want one.
+ * The plain entry points apply no output scale and take q, k, beta and g as
+ * given; the kind-generic entry points dr_forward / dr_forward_varlen /
+ * dr_decode can apply an input prologue first (see dr_prologue).
  *
  * Conventions shared by every entry point
  *   Pointers: all tensor pointers are DEVICE pointers owned by the caller.
@@ -189,6 +191,65 @@ dr_status decay_la_decode(const void* q, const void* k, const void* v, const flo
                           float* state, void* o,
                           int B, int T, int H, int Dk, int Dv, int dtype, void* stream);
 
+/* ---- input prologue ------------------------------------------------------ */
+
+/*
+ * Optional elementwise pre-pass, fused into the kernels' input loads, that
+ * turns a layer's raw projections into the recurrence's inputs (page "Gated
+ * DeltaNet": the layer forward, section "门控与 Head 映射", and the token loads
+ * of the recurrent kernel, section "加载 Token 与写入系数").  In this order:
+ *   DR_PRO_QK_L2NORM    q <- q / sqrt(sum_d q_d^2 + 1e-6), the same for k,
+ *                       per token and head over the Dk key channels
+ *   (always)            q <- q * scale
+ *   DR_PRO_BETA_SIGMOID beta <- 1 / (1 + exp(-beta))      (not for decay_la)
+ *   DR_PRO_BETA_X2      with DR_PRO_BETA_SIGMOID: beta <- 2 / (1 + exp(-beta)),
+ *                       a write strength in (0, 2)
+ *   DR_PRO_GATE         scalar gates (gdn, decay_la) only:
+ *                       g <- -exp(A_log[h]) * log(1 + exp(g + dt_bias[h])),
+ *                       so the gate input g is the raw projection `a`
+ * The transformed values are what the forward computes with; the input
+ * tensors are not modified.  A NULL prologue, or ops = 0 with scale = 1,
+ * runs the plain path.  The struct is read on the host during the call; the
+ * A_log / dt_bias arrays are read by the kernels (device memory, 4-byte
+ * aligned).
+ * Errors: unknown bits, a non-finite scale, DR_PRO_BETA_X2 without
+ * DR_PRO_BETA_SIGMOID, beta ops for decay_la, or DR_PRO_GATE without A_log
+ * return DR_ERR_INVALID_ARG; DR_PRO_GATE for the per-channel (kda) gate
+ * returns DR_ERR_UNSUPPORTED (the pages define gate generation for the scalar
+ * gate only).
+ */
+#define DR_PRO_QK_L2NORM    0x1u
+#define DR_PRO_BETA_SIGMOID 0x2u
+#define DR_PRO_BETA_X2      0x4u
+#define DR_PRO_GATE         0x8u
+typedef struct {
+    unsigned ops;            /* OR of DR_PRO_*                                */
+    float scale;             /* query scale after normalisation (1 = none)    */
+    const float* A_log;      /* DEVICE float [H], DR_PRO_GATE                 */
+    const float* dt_bias;    /* DEVICE float [H] or NULL (no bias)            */
+} dr_prologue;
+
+/* kda_fwd / gdn_fwd / decay_la_fwd selected by `kind` (DR_KIND_*), with a
+ * prologue (may be NULL).  beta is ignored for decay_la. */
+dr_status dr_forward(int kind, const void* q, const void* k, const void* v, const float* g,
+                     const float* beta, const float* h0, void* o, float* hT,
+                     int B, int T, int H, int Dk, int Dv, int C, int dtype,
+                     const dr_prologue* prologue, void* workspace, size_t workspace_bytes,
+                     unsigned* flags, void* stream);
+/* The packed-sequence forwards selected by `kind`, with a prologue. */
+dr_status dr_forward_varlen(int kind, const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, const int* cu_seqlens, int N,
+                            const float* h0, void* o, float* hT,
+                            int T, int H, int Dk, int Dv, int C, int dtype,
+                            const dr_prologue* prologue, void* workspace, size_t workspace_bytes,
+                            unsigned* flags, void* stream);
+/* The decode steps selected by `kind`, with a prologue applied to each new
+ * token. */
+dr_status dr_decode(int kind, const void* q, const void* k, const void* v, const float* g,
+                    const float* beta, float* state, void* o,
+                    int B, int T, int H, int Dk, int Dv, int dtype,
+                    const dr_prologue* prologue, void* stream);
+
 /* ---- the individual steps ---------------------------------------------- */
 
 /*
@@ -264,7 +325,7 @@ size_t dr_record_bytes(int Dk, int Dv, int C, int dtype);
 /* Human-readable text for a status code (static storage). */
 const char* dr_status_string(int status);
 
-/* ABI version of this library: 1. */
+/* ABI version of this library: 2 (1 plus the prologue entry points). */
 int dr_abi_version(void);
 
 #ifdef __cplusplus

@@ -312,3 +312,96 @@ def read_golden(name):
     if cur is not None:
         out[cur] = np.array(rows, dtype=np.float64)
     return out
+
+
+# --------------------------------------------------------------------------
+# Input prologue ([GDN] sections "门控与 Head 映射" and "加载 Token 与写入系数").
+# Each pin takes ``pro`` -- a module with the interface of oracle.prologue --
+# so the pins can be run against broken copies of it.
+# --------------------------------------------------------------------------
+def pin_l2_normalize(pro):
+    """x / sqrt(|x|^2 + 1e-6) per token and head: closed forms and the
+    per-row invariant."""
+    # [3, 4] -> [0.6, 0.8] up to the epsilon: 25 / (25 + 1e-6) of unit norm
+    y = pro.l2_normalize(np.array([[[[3.0, 4.0]]]]))
+    assert rel(y[0, 0, 0], np.array([0.6, 0.8])) < 1e-7
+    # a row whose squares sum to exactly the epsilon: [1e-3, 0] -> [1/sqrt(2), 0]
+    y = pro.l2_normalize(np.array([[[[1e-3, 0.0]]]]))
+    assert abs(y[0, 0, 0, 0] - 2 ** -0.5) < 1e-12 and y[0, 0, 0, 1] == 0.0
+    # the zero row stays zero
+    assert np.all(pro.l2_normalize(np.zeros((1, 2, 3, 4))) == 0.0)
+    # every [b, t, h, :] row separately: |y|^2 = s / (s + eps), direction kept
+    r = np.random.default_rng(40)
+    x = r.standard_normal((2, 5, 3, 8)) * r.uniform(0.1, 10.0, (2, 5, 3, 1))
+    y = pro.l2_normalize(x)
+    s = np.sum(x * x, axis=-1)
+    assert rel(np.sum(y * y, axis=-1), s / (s + 1e-6)) < 1e-13
+    cos = np.sum(x * y, axis=-1) / np.sqrt(s * np.sum(y * y, axis=-1))
+    assert np.max(np.abs(cos - 1.0)) < 1e-13
+
+
+def pin_sigmoid_softplus(pro):
+    """sigmoid(ln 3) = 3/4, sigmoid(x) + sigmoid(-x) = 1; softplus(0) = ln 2,
+    softplus(ln(e - 1)) = 1, softplus(x) - softplus(-x) = x, no overflow."""
+    assert abs(pro.sigmoid(np.log(3.0)) - 0.75) < 1e-15
+    assert abs(pro.sigmoid(-np.log(3.0)) - 0.25) < 1e-15
+    assert pro.sigmoid(0.0) == 0.5
+    x = np.linspace(-30, 30, 121)
+    assert np.max(np.abs(pro.sigmoid(x) + pro.sigmoid(-x) - 1.0)) < 1e-15
+    assert abs(pro.softplus(0.0) - np.log(2.0)) < 1e-15
+    assert abs(pro.softplus(np.log(np.e - 1.0)) - 1.0) < 1e-15
+    assert np.max(np.abs(pro.softplus(x) - pro.softplus(-x) - x)) < 1e-12
+    assert pro.softplus(800.0) == 800.0 and 0.0 < pro.softplus(-700.0) < 1e-300
+
+
+def pin_scalar_gate(pro):
+    """g = -exp(A_log[h]) softplus(a + dt_bias[h]): a worked value per head,
+    g < 0 everywhere, and the large-input asymptote -exp(A_log)(a + dt)."""
+    A_log = np.log(np.array([2.0, 0.5, 16.0]))
+    dt = np.array([0.5, -1.0, 0.0])
+    # a chosen per head so that a + dt = ln(e - 1): softplus = 1, g = -exp(A_log)
+    a = np.broadcast_to(np.log(np.e - 1.0) - dt, (2, 4, 3)).copy()
+    g = pro.scalar_gate(a, A_log, dt)
+    assert rel(g, np.broadcast_to(-np.array([2.0, 0.5, 16.0]), (2, 4, 3))) < 1e-14
+    r = np.random.default_rng(41)
+    a = r.standard_normal((2, 6, 3)) * 4.0
+    g = pro.scalar_gate(a, A_log, dt)
+    assert np.all(g < 0.0)
+    big = pro.scalar_gate(np.full((1, 1, 3), 50.0), A_log, dt)
+    assert rel(big[0, 0], -np.array([2.0, 0.5, 16.0]) * (50.0 + dt)) < 1e-14
+    # no bias = zero bias
+    assert rel(pro.scalar_gate(a, A_log), pro.scalar_gate(a, A_log, np.zeros(3))) == 0.0
+
+
+def pin_prologue_order(pro):
+    """The scale applies after the normalisation (|q| = scale), beta_x2
+    doubles the sigmoid, and with every option off the inputs pass through."""
+    r = np.random.default_rng(42)
+    q, k = (r.standard_normal((1, 3, 2, 16)) * 5.0 for _ in range(2))
+    g, b = r.standard_normal((1, 3, 2)), r.standard_normal((1, 3, 2))
+    q2, k2, g2, b2 = pro.apply("gdn", q, k, g, b, qk_l2norm=True, scale=0.25, beta_sigmoid=True,
+                               beta_x2=True)
+    assert np.max(np.abs(np.linalg.norm(q2, axis=-1) - 0.25)) < 1e-8
+    assert np.max(np.abs(np.linalg.norm(k2, axis=-1) - 1.0)) < 1e-8
+    assert rel(b2, 2.0 / (1.0 + np.exp(-b))) < 1e-15 and np.array_equal(g2, g)
+    q3, k3, g3, b3 = pro.apply("kda", q, k, g, b)
+    assert all(np.array_equal(x, y) for x, y in ((q3, q), (k3, k), (g3, g), (b3, b)))
+
+
+def pin_prologue_householder(pro, rec):
+    """Through the recurrence: with q = k (raw, same vector), L2
+    normalisation, beta = 2 sigmoid(0) = 1 and no decay, each step is the
+    Householder write S k = v, so o_t = v_t up to the epsilon's deficit in
+    |k|^2 ([GDN] section "DeltaNet 与 Gated Delta Rule": unit keys and beta = 1
+    give a reflection that writes v at k)."""
+    r = np.random.default_rng(43)
+    B, T, H, D = 1, 10, 2, 8
+    k = r.standard_normal((B, T, H, D)) * 3.0
+    v = r.standard_normal((B, T, H, D))
+    q2, k2, g2, b2 = pro.apply("gdn", k.copy(), k, np.zeros((B, T, H)), np.zeros((B, T, H)),
+                               qk_l2norm=True, beta_sigmoid=True, beta_x2=True)
+    o, _ = rec("gdn", q2, k2, v, g2, b2)
+    assert rel(o, v) < 1e-5
+
+
+ALL_PROLOGUE_PINS = [pin_l2_normalize, pin_sigmoid_softplus, pin_scalar_gate, pin_prologue_order]

@@ -38,7 +38,7 @@ def test_header_and_binding_agree():
 def test_every_declared_symbol_is_exported(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.dr_abi_version() == 1
+    assert lib.dr_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -120,3 +120,34 @@ def test_python_binding_requires_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "_LIB", None)
     with pytest.raises(_lib.LibraryMissing):
         _lib.load(str(tmp_path / "nope.so"))
+
+
+def test_prologue_rejects(lib):
+    """Bad prologues are refused on the host, before any launch."""
+    from delta_rule_rnn_amd._lib import DrPrologue
+    base = dict(B=1, T=64, H=1, D=64)
+
+    def fwd(kind, pro):
+        return lib.dr_forward(kind, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, base["B"], base["T"],
+                              base["H"], base["D"], base["D"], 64, 1, ctypes.addressof(pro), FAKE, 1 << 30, None,
+                              None)
+
+    nan = float("nan")
+    assert fwd(1, DrPrologue(0x10, 1.0, None, None)) == -1                 # unknown bit
+    assert fwd(1, DrPrologue(0x4, 1.0, None, None)) == -1                  # x2 without sigmoid
+    assert fwd(1, DrPrologue(0x0, nan, None, None)) == -1                  # non-finite scale
+    assert fwd(1, DrPrologue(0x8, 1.0, None, None)) == -1                  # gate without A_log
+    assert fwd(1, DrPrologue(0x8, 1.0, FAKE + 2, None)) == -1              # misaligned A_log
+    assert fwd(0, DrPrologue(0x8, 1.0, FAKE, None)) == -2                  # per-channel gate: not defined
+    assert fwd(2, DrPrologue(0x2, 1.0, None, None)) == -1                  # decay_la has no beta
+    assert fwd(3, DrPrologue(0x0, 1.0, None, None)) == -1                  # bad kind
+    pro = DrPrologue(0x10, 1.0, None, None)
+    assert lib.dr_decode(0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 64, 64, 1,
+                         ctypes.addressof(pro), None) == -1
+    assert lib.dr_forward_varlen(1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None, FAKE, None, 64, 1, 64, 64, 64, 1,
+                                 ctypes.addressof(pro), FAKE, 1 << 30, None, None) == -1
+    # the binding refuses a dt_bias without A_log before calling the library
+    import torch
+    from delta_rule_rnn_amd import DeltaRuleError, Prologue
+    with pytest.raises(DeltaRuleError):
+        Prologue(dt_bias=torch.zeros(1)).to_c(1)

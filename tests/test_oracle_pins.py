@@ -217,3 +217,59 @@ def test_pins_catch_planted_mistake(name, tmp_path):
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, f"no pin caught the planted mistake {name}"
+
+
+# --------------------------------------------------------------------------
+# Input prologue (oracle/prologue.py)
+# --------------------------------------------------------------------------
+from oracle import prologue as _prologue  # noqa: E402
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PROLOGUE_PINS, ids=lambda p: p.__name__)
+def test_prologue_pin(pin):
+    pin(_prologue)
+
+
+def test_prologue_householder_through_recurrence():
+    pins.pin_prologue_householder(_prologue, oracle.recurrence)
+
+
+def test_prologue_gate_rejected_for_per_channel():
+    with pytest.raises(ValueError):
+        _prologue.apply("kda", np.ones((1, 1, 1, 4)), np.ones((1, 1, 1, 4)), np.zeros((1, 1, 1, 4)),
+                        np.zeros((1, 1, 1)), A_log=np.zeros(1))
+
+
+# Planted mistakes in the prologue: each must be caught by some prologue pin.
+PROLOGUE_MUTATIONS = {
+    "eps_outside_sqrt": ("x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)",
+                         "x / (np.sqrt(np.sum(x * x, axis=-1, keepdims=True)) + eps)"),
+    "norm_over_heads": ("np.sum(x * x, axis=-1, keepdims=True)", "np.sum(x * x, axis=-2, keepdims=True)"),
+    "sigmoid_sign": ("1.0 / (1.0 + np.exp(-x))", "1.0 / (1.0 + np.exp(x))"),
+    "softplus_as_log1p_of_x": ("np.logaddexp(0.0, _f64(x))", "np.log1p(np.abs(_f64(x)))"),
+    "gate_without_exp": ("-np.exp(A_log) * softplus(a + bias)", "-A_log * softplus(a + bias)"),
+    "gate_bias_dropped": ("softplus(a + bias)", "softplus(a)"),
+    "scale_before_norm": ("    if qk_l2norm:\n        q, k = l2_normalize(q), l2_normalize(k)\n    q = q * scale\n",
+                          "    q = q * scale\n    if qk_l2norm:\n        q, k = l2_normalize(q), l2_normalize(k)\n"),
+    "beta_x2_ignored": ("sigmoid(beta) * (2.0 if beta_x2 else 1.0)", "sigmoid(beta)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PROLOGUE_MUTATIONS))
+def test_prologue_pins_catch_planted_mistake(name, tmp_path):
+    import importlib.util
+    src = open(_prologue.__file__).read()
+    old, new = PROLOGUE_MUTATIONS[name]
+    assert src.count(old) == 1, f"mutation anchor not found: {name}"
+    path = tmp_path / "prologue_mut.py"
+    path.write_text(src.replace(old, new))
+    spec = importlib.util.spec_from_file_location("prologue_mut", str(path))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    caught = []
+    for pin in pins.ALL_PROLOGUE_PINS:
+        try:
+            pin(mod)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no prologue pin caught the planted mistake {name}"
