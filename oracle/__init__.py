@@ -8,6 +8,10 @@ Contents
   recurrence.c   the definition: a token-by-token fp64 recurrence (C, pthreads)
   chunked.py     the chunk-form algorithm in fp64 numpy, exposing every
                  intermediate (gamma, K+, K-, A, T, W, U, state per chunk)
+  prologue.py    the input prologue (q/k L2 norm, scale, beta sigmoid, scalar
+                 gate generation) in fp64 numpy
+  backward.py    the gradients of the token recurrence (its reverse sweep),
+                 fp64 numpy
 
 Page keys used in citations (title of the page, then the section):
   [SD]   "TileLang 实战：KDA 从零到一--标量衰减"

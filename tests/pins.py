@@ -405,3 +405,74 @@ def pin_prologue_householder(pro, rec):
 
 
 ALL_PROLOGUE_PINS = [pin_l2_normalize, pin_sigmoid_softplus, pin_scalar_gate, pin_prologue_order]
+
+
+# --------------------------------------------------------------------------
+# Backward pass (oracle/backward.py).  Each pin takes ``bwd`` -- a callable
+# with the signature of oracle.backward.recurrence_backward -- so that broken
+# copies can be run through them.
+# --------------------------------------------------------------------------
+def _fd_case(kind, seed):
+    r = np.random.default_rng(seed)
+    B, T, H, Dk, Dv = 1, 6, 2, 3, 4
+    q, k = r.standard_normal((B, T, H, Dk)), r.standard_normal((B, T, H, Dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = r.standard_normal((B, T, H, Dv))
+    g = np.log(r.uniform(0.5, 0.99, (B, T, H, Dk) if kind == "kda" else (B, T, H)))
+    bt = r.uniform(0.2, 0.9, (B, T, H)) if kind != "decay_la" else None
+    h0 = r.standard_normal((B, H, Dv, Dk)) * 0.5
+    do = r.standard_normal((B, T, H, Dv))
+    dhT = r.standard_normal((B, H, Dv, Dk))
+    return dict(q=q, k=k, v=v, g=g, beta=bt, h0=h0), do, dhT
+
+
+def pin_backward_finite_differences(bwd, rec):
+    """Every gradient against central differences of the loss
+    L = <do, o> + <dhT, hT> evaluated by the forward oracle, on small random
+    inputs of each kind (with an initial state and a final-state cotangent)."""
+    eps = 1e-6
+    for kind in ("kda", "gdn", "decay_la"):
+        x, do, dhT = _fd_case(kind, {"kda": 60, "gdn": 61, "decay_la": 62}[kind])
+
+        def loss(xx):
+            o, hT = rec(kind, xx["q"], xx["k"], xx["v"], xx["g"], xx["beta"], xx["h0"])
+            return float(np.sum(o * do) + np.sum(hT * dhT))
+
+        grads = bwd(kind, x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"], do, dhT)
+        for name in ("q", "k", "v", "g", "beta", "h0"):
+            if x[name] is None:
+                continue
+            gnum = np.zeros_like(x[name])
+            it = np.nditer(x[name], flags=["multi_index"])
+            for _ in it:
+                idx = it.multi_index
+                xp = {n: (None if t is None else t.copy()) for n, t in x.items()}
+                xm = {n: (None if t is None else t.copy()) for n, t in x.items()}
+                xp[name][idx] += eps
+                xm[name][idx] -= eps
+                gnum[idx] = (loss(xp) - loss(xm)) / (2 * eps)
+            got = grads["d" + name]
+            assert rel(got, gnum) < 1e-6, f"{kind} d{name}: rel err {rel(got, gnum):.2e}"
+
+
+def pin_backward_retention_closed_form(bwd):
+    """Scalar-decay linear attention with a constant per-head decay is
+    o = (Q K^T .* D) V, D_nm = gamma^(n-m) for n >= m ("07 · linear 路线（二）",
+    section 1): dv = (Q K^T .* D)^T do, dq = (do V^T .* D) K,
+    dk = (do V^T .* D)^T Q."""
+    r = np.random.default_rng(63)
+    B, T, H, D = 1, 40, 2, 5
+    q, k, v, do = (r.standard_normal((B, T, H, D)) for _ in range(4))
+    gam = np.array([0.9, 0.97])
+    g = np.broadcast_to(np.log(gam)[None, None, :], (B, T, H)).copy()
+    res = bwd("decay_la", q, k, v, g, None, None, do, None)
+    n = np.arange(T)
+    for h in range(H):
+        Dm = np.where(n[:, None] >= n[None, :], gam[h] ** np.maximum(n[:, None] - n[None, :], 0), 0.0)
+        Q, K, V, dO = q[0, :, h], k[0, :, h], v[0, :, h], do[0, :, h]
+        P = (Q @ K.T) * Dm
+        G = (dO @ V.T) * Dm
+        assert rel(res["o"][0, :, h], P @ V) < 1e-12
+        assert rel(res["dv"][0, :, h], P.T @ dO) < 1e-12
+        assert rel(res["dq"][0, :, h], G @ K) < 1e-12
+        assert rel(res["dk"][0, :, h], G.T @ Q) < 1e-12

@@ -273,3 +273,61 @@ def test_prologue_pins_catch_planted_mistake(name, tmp_path):
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, f"no prologue pin caught the planted mistake {name}"
+
+
+# --------------------------------------------------------------------------
+# Backward pass (oracle/backward.py)
+# --------------------------------------------------------------------------
+from oracle import backward as _backward  # noqa: E402
+
+
+def test_backward_finite_differences():
+    pins.pin_backward_finite_differences(_backward.recurrence_backward, oracle.recurrence)
+
+
+def test_backward_retention_closed_form():
+    pins.pin_backward_retention_closed_form(_backward.recurrence_backward)
+
+
+def test_backward_forward_matches_recurrence():
+    """The forward the backward recomputes is the C oracle's."""
+    for kind in ("kda", "gdn", "decay_la"):
+        x, do, dhT = pins._fd_case(kind, 64)
+        res = _backward.recurrence_backward(kind, x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"], do, dhT)
+        o, hT = oracle.recurrence(kind, x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"])
+        assert rel(res["o"], o) < 1e-13 and rel(res["hT"], hT) < 1e-13
+
+
+BACKWARD_MUTATIONS = {
+    "dq_from_entry_state": ('out["dq"][b, t, h] = S[t + 1].T @ dot', 'out["dq"][b, t, h] = S[t].T @ dot'),
+    "readout_adjoint_after_use": ("                dS += np.outer(dot, qt)\n", ""),
+    "dv_without_beta": ('out["dv"][b, t, h] = beta[b, t, h] * dr', 'out["dv"][b, t, h] = dr'),
+    "du_sign": ("du = -beta[b, t, h] * dr", "du = beta[b, t, h] * dr"),
+    "dbeta_uses_v_only": ('out["dbeta"][b, t, h] = dr @ (v[b, t, h] - u)', 'out["dbeta"][b, t, h] = dr @ v[b, t, h]'),
+    "dk_misses_read_term": ("dkt = dkt + Sbar.T @ du", "dkt = dkt"),
+    "dg_without_a": ('out["dg"][b, t, h] = a * da if perch else a * np.sum(da)',
+                     'out["dg"][b, t, h] = da if perch else np.sum(da)'),
+    "gate_adjoint_not_decayed": ("                dS = dS * a\n", ""),
+    "dg_from_exit_state": ("da = np.sum(dS * S[t], axis=0)", "da = np.sum(dS * S[t + 1], axis=0)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BACKWARD_MUTATIONS))
+def test_backward_pins_catch_planted_mistake(name, tmp_path):
+    import importlib.util
+    src = open(_backward.__file__).read()
+    old, new = BACKWARD_MUTATIONS[name]
+    assert src.count(old) == 1, f"mutation anchor not found: {name}"
+    path = tmp_path / "backward_mut.py"
+    path.write_text(src.replace(old, new))
+    spec = importlib.util.spec_from_file_location("backward_mut", str(path))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    caught = []
+    for pin in (lambda f: pins.pin_backward_finite_differences(f, oracle.recurrence),
+                pins.pin_backward_retention_closed_form):
+        try:
+            pin(mod.recurrence_backward)
+        except AssertionError:
+            caught.append(pin)
+    assert caught, f"no backward pin caught the planted mistake {name}"
