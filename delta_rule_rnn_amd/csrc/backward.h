@@ -1,0 +1,839 @@
+// backward.h -- gradients of the chunkwise gated delta rule: four kernels.
+//
+// Page keys: [KDA] "TileLang 实战：KDA 从零到一–Kimi Delta Attention";
+// [SD] "TileLang 实战：KDA 从零到一--标量衰减"; [GDN] "Gated DeltaNet"
+// (section "反向传播：状态伴随与三角变换梯度": the forward's operands are recomputed, the chunk entry
+// states are rebuilt by a forward pass, the state adjoint runs backwards over
+// the chunks, then the per-chunk gradients and the WY-representation backward
+// go through the triangular inverse, and the gate gradient is a reverse
+// cumulative sum inside each chunk).
+//
+// Chunk quantities (rows r, i, j = positions, d = key channel; kernel
+// orientation, state S in R^{Dk x Dv}), as in the forward:
+//   gamma = log2 cumsum of g;  e = 2^gamma;  phi = 2^gamma_last
+//   Q~ = q e,  K+ = k e,  K- = k / e,  Kbar = k phi / e
+//   L  = StrictLower(K+ K-^T)      (scalar gates: (k_i.k_j) 2^(gamma_i - gamma_j))
+//   Aqk = TrilIncl(Q~ K-^T)        (scalar gates: (q_i.k_j) 2^(gamma_i - gamma_j))
+//   T = (I + diag(beta) L)^-1,  W = T diag(beta) K+,  U = T diag(beta) V
+//   Vnew = U - W S,  O = Q~ S + Aqk Vnew,  S' = diag(phi) S + Kbar^T Vnew
+// and backwards, with dS' the adjoint of the exit state:
+//   dVnew = Aqk^T dO + Kbar dS'              (state adjoint pass)
+//   dS    = Q~^T dO + diag(phi) dS' - W^T dVnew
+//   dQ~ = dO S^T,  dAqk = dO Vnew^T,  dKbar = Vnew dS'^T,  dphi = rowsum(S .* dS')
+//   dW = -dVnew S^T,  dU = dVnew
+//   dT = dW M^T + dU N^T  (M = diag(beta) K+, N = diag(beta) V),  dM = T^T dW,
+//   dN = T^T dU,  dA = -T^T dT T^T (strictly lower),  dL = diag(beta) dA
+// then through the separable exponents to dq, dk, dv, dbeta and the log-gate
+// adjoint E; dg_s = sum_{r >= s} E_r + F with F the gamma_last terms (the
+// ln 2 of d2^x/dx and the log2(e) of gamma cancel).
+//
+// All four kernels compute in fp32 on fp32 MFMA (v_mfma_f32_16x16x4_f32) with
+// operands staged in LDS in natural row-major layout; the I/O dtype only
+// changes the loads of q, k, v, dO and the stores of dq, dk, dv.
+//   bwd_prep_kernel     chunk-parallel: writes the natural fp32 chunk arrays
+//                       (Q~, W, Kbar, U, Aqk, L, T, phi, gamma)
+//   bwd_state_fwd_kernel   per (chain, 32 value columns), chunks in order:
+//                       entry states S_c and Vnew
+//   bwd_state_rev_kernel   per (chain, 32 value columns), chunks in reverse:
+//                       exit adjoints dS'_c, dVnew, and dh0
+//   bwd_grad_kernel     chunk-parallel: dq, dk, dv, dbeta, dg
+#pragma once
+
+#include "common.h"
+
+namespace dr {
+namespace bw {
+
+constexpr int C = kChunk;
+constexpr int kVS = 32;            // value columns per state-pass workgroup / gradient slice
+constexpr int LVS = kVS + 4;       // padded row of [*, 32] fp32 tiles
+constexpr int LDC = C + 4;         // padded row of [C, C] fp32 tiles
+
+// Natural fp32 arrays of one chunk of one (b, h), written by bwd_prep_kernel.
+template <int DK>
+struct Prep {
+    static constexpr int DV = DK;
+    static constexpr size_t QT = 0;                         // [C][DK]  Q~
+    static constexpr size_t W = QT + (size_t)C * DK;        // [C][DK]  W
+    static constexpr size_t KB = W + (size_t)C * DK;        // [C][DK]  Kbar
+    static constexpr size_t U = KB + (size_t)C * DK;        // [C][DV]  U (decay_la: V)
+    static constexpr size_t AQK = U + (size_t)C * DV;       // [C][C]   Aqk
+    static constexpr size_t L = AQK + (size_t)C * C;        // [C][C]   L (strictly lower)
+    static constexpr size_t TI = L + (size_t)C * C;         // [C][C]   T = (I + diag(beta) L)^-1
+    static constexpr size_t PHI = TI + (size_t)C * C;       // [DK]     phi
+    static constexpr size_t GAM = PHI + DK;                 // [C][DK] (kda) or [C]: gamma (log2)
+    static constexpr size_t FLOATS = GAM + (size_t)C * DK;
+};
+
+// acc[16x16] += A[16 x K] * B[K x 16] on fp32 MFMA, A(r, k) = A[r*ar + k*ak],
+// B(k, c) = B[k*bk + c*bc].  At step k0 lane l supplies A(l%16, k0 + l/16)
+// and B(k0 + l/16, l%16); the result is in the accumulator layout (lane l:
+// rows 4*(l/16) + i, column l%16).  Wave-uniform control flow only.
+template <int K>
+__device__ __forceinline__ f32x4 mmk(f32x4 acc, const float* A, int ar, int ak, const float* B, int bk, int bc,
+                                     int lane) {
+    const int r = lane & 15, q = lane >> 4;
+    const float* a = A + r * ar + q * ak;
+    const float* b = B + q * bk + r * bc;
+#pragma unroll 8
+    for (int k0 = 0; k0 < K; k0 += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[k0 * ak], b[k0 * bk], acc, 0, 0, 0);
+    return acc;
+}
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ int arow(int lane, int i) { return 4 * (lane >> 4) + i; }
+
+// Cooperative copy of a [rows][cols] fp32 block (row stride gs floats) into
+// LDS (row stride ls floats); cols % 4 == 0, both strides multiples of 4.
+__device__ __forceinline__ void stage(float* dst, int ls, const float* __restrict__ src, size_t gs, int rows, int cols,
+                                      int tid, int nthr) {
+    const int per = cols / 4;
+    for (int idx = tid; idx < rows * per; idx += nthr) {
+        const int r = idx / per, c4 = (idx % per) * 4;
+        *reinterpret_cast<float4*>(dst + r * ls + c4) = *reinterpret_cast<const float4*>(src + r * gs + c4);
+    }
+}
+__device__ __forceinline__ void unstage(float* __restrict__ dst, size_t gs, const float* src, int ls, int rows,
+                                        int cols, int tid, int nthr) {
+    const int per = cols / 4;
+    for (int idx = tid; idx < rows * per; idx += nthr) {
+        const int r = idx / per, c4 = (idx % per) * 4;
+        *reinterpret_cast<float4*>(dst + r * gs + c4) = *reinterpret_cast<const float4*>(src + r * ls + c4);
+    }
+}
+
+// ===========================================================================
+// Prep: one 256-thread workgroup per (chunk, head, batch), heads fastest.
+// ===========================================================================
+template <int KIND, typename T, int DK>
+struct PrepSmem {
+    static constexpr int LDK = DK + 4;
+    static constexpr size_t MAT = (size_t)C * LDK;
+    static constexpr size_t SA = 0, SB = SA + MAT, SQ = SB + MAT, SL = SQ + MAT, ST = SL + (size_t)C * LDC;
+    static constexpr size_t SBETA = ST + (size_t)C * LDC, SGAM = SBETA + C, SPHI = SGAM + C;
+    static constexpr size_t FLOATS = SPHI + DK;
+};
+
+template <int KIND, typename T, int DK>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                       const T* __restrict__ v, const float* __restrict__ g,
+                                                       const float* __restrict__ beta, float* __restrict__ prep,
+                                                       int Tlen, int H, int NT)
+{
+    using P = Prep<DK>;
+    using SM = PrepSmem<KIND, T, DK>;
+    constexpr int DV = DK, LDK = SM::LDK;
+    constexpr bool DELTA = KIND != KIND_LA;
+    constexpr bool PERCH = KIND == KIND_KDA;
+    __shared__ __attribute__((aligned(16))) float smem[SM::FLOATS];
+    float* sA = smem + SM::SA;     // kda: K+ (then M);  scalar: k (then M)
+    float* sB = smem + SM::SB;     // kda: g, then K-
+    float* sQ = smem + SM::SQ;     // q (kda: Q~), later N = diag(beta) V
+    float* sL = smem + SM::SL;
+    float* sT = smem + SM::ST;
+    float* sBeta = smem + SM::SBETA;
+    float* sGam = smem + SM::SGAM;
+    float* sPhi = smem + SM::SPHI;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const unsigned it = blockIdx.x;
+    const int h = (int)(it % (unsigned)H);
+    const unsigned tt = it / (unsigned)H;
+    const int c = (int)(tt % (unsigned)NT), b = (int)(tt / (unsigned)NT);
+    const int nvalid = min(C, Tlen - c * C);
+    const size_t row0 = ((size_t)b * Tlen + (size_t)c * C) * H + h;   // token row of position 0
+    float* out = prep + (((size_t)b * H + h) * NT + c) * P::FLOATS;
+
+    // ---- inputs, rows past the end of a ragged chunk zero
+    for (int idx = tid; idx < C * DK; idx += 256) {
+        const int r = idx / DK, d = idx % DK;
+        const bool ok = r < nvalid;
+        const size_t off = (row0 + (size_t)r * H) * DK + d;
+        sA[r * LDK + d] = ok ? to_f(k[off]) : 0.f;
+        sQ[r * LDK + d] = ok ? to_f(q[off]) : 0.f;
+        if constexpr (PERCH) sB[r * LDK + d] = ok ? g[off] : 0.f;
+    }
+    if (tid < C) {
+        const bool ok = tid < nvalid;
+        sBeta[tid] = (DELTA && ok) ? beta[row0 + (size_t)tid * H] : 0.f;
+        if constexpr (!PERCH) sGam[tid] = ok ? g[row0 + (size_t)tid * H] : 0.f;
+    }
+    __syncthreads();
+
+    // ---- gamma and the separable operands
+    if constexpr (PERCH) {
+        if (tid < DK) {
+            const int d = tid;
+            float run = 0.f;
+            for (int r = 0; r < C; ++r) {
+                run += sB[r * LDK + d] * kLog2e;
+                const float e = __builtin_amdgcn_exp2f(run), ei = __builtin_amdgcn_exp2f(-run);
+                const float kk = sA[r * LDK + d];
+                sA[r * LDK + d] = kk * e;
+                sB[r * LDK + d] = kk * ei;
+                sQ[r * LDK + d] *= e;
+                out[P::GAM + (size_t)r * DK + d] = run;
+            }
+            const float phi = __builtin_amdgcn_exp2f(run);
+            sPhi[d] = phi;
+            out[P::PHI + d] = phi;
+            for (int r = 0; r < C; ++r) {
+                out[P::KB + (size_t)r * DK + d] = sB[r * LDK + d] * phi;
+                out[P::QT + (size_t)r * DK + d] = sQ[r * LDK + d];
+            }
+        }
+    } else {
+        if (wave == 0) {
+            float x = sGam[lane];
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(x, off, 64);
+                if (lane >= off) x += y;
+            }
+            x *= kLog2e;
+            sGam[lane] = x;
+            out[P::GAM + lane] = x;
+        }
+        __syncthreads();
+        const float gl = sGam[C - 1];
+        for (int idx = tid; idx < C * DK; idx += 256) {
+            const int r = idx / DK, d = idx % DK;
+            out[P::QT + (size_t)r * DK + d] = sQ[r * LDK + d] * __builtin_amdgcn_exp2f(sGam[r]);
+            out[P::KB + (size_t)r * DK + d] = sA[r * LDK + d] * __builtin_amdgcn_exp2f(gl - sGam[r]);
+        }
+        if (tid < DK) {
+            sPhi[tid] = __builtin_amdgcn_exp2f(gl);
+            out[P::PHI + tid] = sPhi[tid];
+        }
+    }
+    __syncthreads();
+
+    // ---- L and Aqk: 16 tiles each, 32 jobs over 4 waves
+    for (int job = wave; job < 32; job += 4) {
+        const bool isL = job < 16;
+        const int t = job & 15, ti = t >> 2, tj = t & 3;
+        f32x4 acc = zero4();
+        if (ti >= tj && (isL ? DELTA : true)) {
+            const float* Aop = isL ? sA : sQ;
+            const float* Bop = PERCH ? sB : sA;
+            acc = mmk<DK>(acc, Aop + ti * 16 * LDK, LDK, 1, Bop + tj * 16 * LDK, 1, LDK, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = ti * 16 + arow(lane, i), cc = tj * 16 + (lane & 15);
+            float x = acc[i];
+            if constexpr (!PERCH) x *= (cc <= r) ? __builtin_amdgcn_exp2f(sGam[r] - sGam[cc]) : 0.f;
+            if (isL) {
+                x = cc < r ? x : 0.f;
+                sL[r * LDC + cc] = x;
+                out[P::L + (size_t)r * C + cc] = x;
+            } else {
+                out[P::AQK + (size_t)r * C + cc] = cc <= r ? x : 0.f;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- T = (I + diag(beta) L)^-1 by forward substitution, one column per lane
+    if constexpr (DELTA) {
+        if (wave == 0) {
+            const int j = lane;
+            for (int i = 0; i < C; ++i) sT[i * LDC + j] = (i == j) ? 1.f : 0.f;
+            for (int i = j + 1; i < C; ++i) {
+                float s = 0.f;
+                for (int m = j; m < i; ++m) s += sL[i * LDC + m] * sT[m * LDC + j];
+                sT[i * LDC + j] = -sBeta[i] * s;
+            }
+        }
+        __syncthreads();
+        for (int idx = tid; idx < C * C; idx += 256) out[P::TI + idx] = sT[(idx / C) * LDC + idx % C];
+    }
+
+    // ---- M = diag(beta) K+ (in place) and N = diag(beta) V (into sQ)
+    for (int idx = tid; idx < C * DK; idx += 256) {
+        const int r = idx / DK, d = idx % DK;
+        const float vv = r < nvalid ? to_f(v[(row0 + (size_t)r * H) * DV + d]) : 0.f;
+        if constexpr (DELTA) {
+            const float rs = PERCH ? sBeta[r] : sBeta[r] * __builtin_amdgcn_exp2f(sGam[r]);
+            sA[r * LDK + d] *= rs;
+            sQ[r * LDK + d] = sBeta[r] * vv;
+        } else {
+            out[P::U + (size_t)r * DV + d] = vv;
+        }
+    }
+    if constexpr (DELTA) {
+        __syncthreads();
+        // W = T M, U = T N: (C/16) x (DK/16) tiles each
+        constexpr int NTL = 4 * (DK / 16);
+        for (int job = wave; job < 2 * NTL; job += 4) {
+            const bool isW = job < NTL;
+            const int t = isW ? job : job - NTL, ti = t / (DK / 16), tj = t % (DK / 16);
+            const float* Bop = isW ? sA : sQ;
+            f32x4 acc = mmk<C>(zero4(), sT + ti * 16 * LDC, LDC, 1, Bop + tj * 16, LDK, 1, lane);
+            float* dst = out + (isW ? P::W : P::U);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[(size_t)(ti * 16 + arow(lane, i)) * DK + tj * 16 + (lane & 15)] = acc[i];
+        }
+    }
+}
+
+// ===========================================================================
+// Forward state pass: one 256-thread workgroup per (chain, 32 value columns).
+// Writes the entry state S_c [DK][DV] and Vnew_c [C][DV] of every chunk.
+// ===========================================================================
+template <int KIND, int DK>
+struct StateSmem {
+    static constexpr int LDK = DK + 4;
+    static constexpr size_t MAT = (size_t)C * LDK;
+    static constexpr size_t S = 0, X1 = S + (size_t)DK * LVS, X2 = X1 + MAT, VN = X2 + MAT, DO = VN + (size_t)C * LVS,
+                            PHI = DO + (size_t)C * LVS, FLOATS = PHI + DK;
+};
+
+template <int KIND, int DK>
+__global__ __launch_bounds__(256) void bwd_state_fwd_kernel(const float* __restrict__ prep, const float* __restrict__ h0,
+                                                            float* __restrict__ hs, float* __restrict__ vn, int H,
+                                                            int NT)
+{
+    using P = Prep<DK>;
+    using SM = StateSmem<KIND, DK>;
+    constexpr int DV = DK, LDK = SM::LDK, NVS = DV / kVS;
+    constexpr bool DELTA = KIND != KIND_LA;
+    __shared__ __attribute__((aligned(16))) float smem[SM::FLOATS];
+    float* sS = smem + SM::S;
+    float* sW = smem + SM::X1;
+    float* sKb = smem + SM::X2;
+    float* sVn = smem + SM::VN;
+    float* sPhi = smem + SM::PHI;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int chain = blockIdx.x / NVS, dv0 = (blockIdx.x % NVS) * kVS;
+    for (int idx = tid; idx < DK * kVS; idx += 256) {
+        const int r = idx / kVS, cc = idx % kVS;
+        sS[r * LVS + cc] = h0 ? h0[((size_t)chain * DK + r) * DV + dv0 + cc] : 0.f;
+    }
+    __syncthreads();
+    for (int c = 0; c < NT; ++c) {
+        const size_t ci = (size_t)chain * NT + c;
+        const float* pc = prep + ci * P::FLOATS;
+        unstage(hs + ci * DK * DV + dv0, DV, sS, LVS, DK, kVS, tid, 256);
+        if constexpr (DELTA) stage(sW, LDK, pc + P::W, DK, C, DK, tid, 256);
+        stage(sKb, LDK, pc + P::KB, DK, C, DK, tid, 256);
+        stage(sVn, LVS, pc + P::U + dv0, DV, C, kVS, tid, 256);
+        if (tid < DK) sPhi[tid] = pc[P::PHI + tid];
+        __syncthreads();
+        // Vnew = U - W S: 4 x 2 tiles, two per wave
+        if constexpr (DELTA) {
+            for (int t = wave; t < 8; t += 4) {
+                const int ti = t >> 1, tj = t & 1;
+                const f32x4 acc = mmk<DK>(zero4(), sW + ti * 16 * LDK, LDK, 1, sS + tj * 16, LVS, 1, lane);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sVn[(ti * 16 + arow(lane, i)) * LVS + tj * 16 + (lane & 15)] -= acc[i];
+            }
+            __syncthreads();
+        }
+        unstage(vn + ci * C * DV + dv0, DV, sVn, LVS, C, kVS, tid, 256);
+        // S' = diag(phi) S + Kbar^T Vnew, in place (each element has one owner)
+        for (int t = wave; t < 2 * (DK / 16); t += 4) {
+            const int ti = t >> 1, tj = t & 1;
+            f32x4 acc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = ti * 16 + arow(lane, i);
+                acc[i] = sPhi[r] * sS[r * LVS + tj * 16 + (lane & 15)];
+            }
+            acc = mmk<C>(acc, sKb + ti * 16, 1, LDK, sVn + tj * 16, LVS, 1, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sS[(ti * 16 + arow(lane, i)) * LVS + tj * 16 + (lane & 15)] = acc[i];
+        }
+        __syncthreads();
+    }
+}
+
+// ===========================================================================
+// Reverse state pass: one 256-thread workgroup per (chain, 32 value columns),
+// chunks in reverse.  Writes dS'_c (the exit-state adjoint of chunk c) and
+// dVnew_c, and dh0.
+// ===========================================================================
+template <int KIND, typename T, int DK>
+__global__ __launch_bounds__(256) void bwd_state_rev_kernel(const float* __restrict__ prep,
+                                                            const T* __restrict__ dout,
+                                                            const float* __restrict__ dhT, float* __restrict__ dhs,
+                                                            float* __restrict__ dvn, float* __restrict__ dh0,
+                                                            int Tlen, int H, int NT)
+{
+    using P = Prep<DK>;
+    using SM = StateSmem<KIND, DK>;
+    constexpr int DV = DK, LDK = SM::LDK, NVS = DV / kVS;
+    constexpr bool DELTA = KIND != KIND_LA;
+    __shared__ __attribute__((aligned(16))) float smem[SM::FLOATS + (size_t)C * LDC];
+    float* sD = smem + SM::S;         // dS'
+    float* sX = smem + SM::X1;        // Kbar, then W
+    float* sQt = smem + SM::X2;
+    float* sDV = smem + SM::VN;       // dVnew
+    float* sDO = smem + SM::DO;
+    float* sPhi = smem + SM::PHI;
+    float* sAqk = smem + SM::FLOATS;  // [C][LDC] after the shared layout
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int chain = blockIdx.x / NVS, dv0 = (blockIdx.x % NVS) * kVS;
+    const int b = chain / H, h = chain % H;
+    for (int idx = tid; idx < DK * kVS; idx += 256) {
+        const int r = idx / kVS, cc = idx % kVS;
+        sD[r * LVS + cc] = dhT ? dhT[((size_t)chain * DK + r) * DV + dv0 + cc] : 0.f;
+    }
+    __syncthreads();
+    for (int c = NT - 1; c >= 0; --c) {
+        const size_t ci = (size_t)chain * NT + c;
+        const float* pc = prep + ci * P::FLOATS;
+        unstage(dhs + ci * DK * DV + dv0, DV, sD, LVS, DK, kVS, tid, 256);
+        stage(sAqk, LDC, pc + P::AQK, C, C, C, tid, 256);
+        stage(sX, LDK, pc + P::KB, DK, C, DK, tid, 256);
+        stage(sQt, LDK, pc + P::QT, DK, C, DK, tid, 256);
+        if (tid < DK) sPhi[tid] = pc[P::PHI + tid];
+        for (int idx = tid; idx < C * kVS; idx += 256) {
+            const int r = idx / kVS, cc = idx % kVS;
+            const int tok = c * C + r;
+            sDO[r * LVS + cc] = tok < Tlen ? to_f(dout[(((size_t)b * Tlen + tok) * H + h) * DV + dv0 + cc]) : 0.f;
+        }
+        __syncthreads();
+        // dVnew = Aqk^T dO + Kbar dS'
+        for (int t = wave; t < 8; t += 4) {
+            const int ti = t >> 1, tj = t & 1;
+            f32x4 acc = mmk<C>(zero4(), sAqk + ti * 16, 1, LDC, sDO + tj * 16, LVS, 1, lane);
+            acc = mmk<DK>(acc, sX + ti * 16 * LDK, LDK, 1, sD + tj * 16, LVS, 1, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sDV[(ti * 16 + arow(lane, i)) * LVS + tj * 16 + (lane & 15)] = acc[i];
+        }
+        __syncthreads();
+        unstage(dvn + ci * C * DV + dv0, DV, sDV, LVS, C, kVS, tid, 256);
+        if constexpr (DELTA) {
+            stage(sX, LDK, pc + P::W, DK, C, DK, tid, 256);
+            __syncthreads();
+        }
+        // dS = Q~^T dO + diag(phi) dS' - W^T dVnew, in place
+        for (int t = wave; t < 2 * (DK / 16); t += 4) {
+            const int ti = t >> 1, tj = t & 1;
+            f32x4 acc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = ti * 16 + arow(lane, i);
+                acc[i] = sPhi[r] * sD[r * LVS + tj * 16 + (lane & 15)];
+            }
+            acc = mmk<C>(acc, sQt + ti * 16, 1, LDK, sDO + tj * 16, LVS, 1, lane);
+            if constexpr (DELTA) {
+                const f32x4 wv = mmk<C>(zero4(), sX + ti * 16, 1, LDK, sDV + tj * 16, LVS, 1, lane);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] -= wv[i];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sD[(ti * 16 + arow(lane, i)) * LVS + tj * 16 + (lane & 15)] = acc[i];
+        }
+        __syncthreads();
+    }
+    if (dh0) unstage(dh0 + (size_t)chain * DK * DV + dv0, DV, sD, LVS, DK, kVS, tid, 256);
+}
+
+// ===========================================================================
+// Gradients: one 512-thread workgroup per (chunk, head, batch).
+// ===========================================================================
+template <int DK>
+struct GradSmem {
+    static constexpr int LDK = DK + 4;
+    static constexpr size_t MAT = (size_t)C * LDK, SQ = (size_t)C * LDC;
+    static constexpr size_t SL = (size_t)DK * LVS, VS = (size_t)C * LVS;
+    // phase 1
+    static constexpr size_t KP = 0;                 // K+ (kda) or k (scalar): persists
+    static constexpr size_t TI = KP + MAT;          // T
+    static constexpr size_t S1 = TI + SQ, DS1 = S1 + SL, VN1 = DS1 + SL, DVN1 = VN1 + VS, DO1 = DVN1 + VS,
+                            V1 = DO1 + VS, P1 = V1 + VS, END1 = P1 + VS;
+    // phase 2 (after phase 1): nW at TI + SQ; dT, Y at TI + SQ, TI + 2 SQ; dL, dAqk; then K- / raw q and Q~
+    static constexpr size_t NW = TI + SQ, DT = TI + SQ, Y = TI + 2 * SQ, DL = TI + 3 * SQ, DAQK = TI + 4 * SQ,
+                            KM = TI, QT = TI + 5 * SQ, END2 = QT + MAT;
+    static constexpr size_t E = TI;                  // phase 3: E over the K- slot
+    static constexpr size_t BIG = END1 > END2 ? END1 : END2;
+    static constexpr size_t DB = BIG, SE = DB + C, GAM = SE + C, PHI = GAM + C, FCOL = PHI + DK, DPHI = FCOL + DK,
+                            ROW = DPHI + DK, FLOATS = ROW + C;
+    static_assert(KM + MAT <= DL, "K- slot overlaps dL");
+    static_assert(NW + MAT <= DL, "nW slot overlaps dL");
+};
+
+template <int KIND, typename T, int DK>
+__global__ __launch_bounds__(512) void bwd_grad_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ beta,
+    const T* __restrict__ dout, const float* __restrict__ prep, const float* __restrict__ hs,
+    const float* __restrict__ dhs, const float* __restrict__ vn, const float* __restrict__ dvn,
+    T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv, float* __restrict__ dg, float* __restrict__ dbeta,
+    int Tlen, int H, int NT)
+{
+    using P = Prep<DK>;
+    using SM = GradSmem<DK>;
+    constexpr int DV = DK, LDK = SM::LDK, NCT = DK / 16, NTL = 4 * NCT, OWN = NTL / 8, NVS = DV / kVS;
+    constexpr bool DELTA = KIND != KIND_LA;
+    constexpr bool PERCH = KIND == KIND_KDA;
+    __shared__ __attribute__((aligned(16))) float smem[SM::FLOATS];
+    float* sKp = smem + SM::KP;
+    float* sT = smem + SM::TI;
+    float* sDb = smem + SM::DB;
+    float* sE = smem + SM::SE;
+    float* sGam = smem + SM::GAM;
+    float* sPhi = smem + SM::PHI;
+    float* sF = smem + SM::FCOL;
+    float* sDphi = smem + SM::DPHI;
+    float* sRow = smem + SM::ROW;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const unsigned it = blockIdx.x;
+    const int h = (int)(it % (unsigned)H);
+    const unsigned tt = it / (unsigned)H;
+    const int c = (int)(tt % (unsigned)NT), b = (int)(tt / (unsigned)NT);
+    const int nvalid = min(C, Tlen - c * C);
+    const size_t row0 = ((size_t)b * Tlen + (size_t)c * C) * H + h;
+    const size_t ci = ((size_t)b * H + h) * NT + c;
+    const float* pc = prep + ci * P::FLOATS;
+
+    // owned tiles of every [C][DK] result: t = wave + 8 m
+    auto trc = [&](int m, int& ti, int& tj) { const int t = wave + 8 * m; ti = t / NCT; tj = t % NCT; };
+    // element (r, d) of owned tile m, accumulator slot i
+    auto erow = [&](int m, int i) { int ti, tj; trc(m, ti, tj); return ti * 16 + arow(lane, i); };
+    auto ecol = [&](int m) { int ti, tj; trc(m, ti, tj); return tj * 16 + (lane & 15); };
+    // gamma (log2) and e = 2^gamma at element (r, d)
+    auto gam_at = [&](int r, int d) { return PERCH ? pc[P::GAM + (size_t)r * DK + d] : sGam[r]; };
+    auto in_at = [&](const T* __restrict__ x, int r, int d) {
+        return r < nvalid ? to_f(x[(row0 + (size_t)r * H) * DK + d]) : 0.f;
+    };
+
+    // ---- set-up: K+ (or k), T, beta, gamma, phi
+    for (int idx = tid; idx < C * DK; idx += 512) {
+        const int r = idx / DK, d = idx % DK;
+        const float kk = r < nvalid ? to_f(k[(row0 + (size_t)r * H) * DK + d]) : 0.f;
+        sKp[r * LDK + d] = PERCH ? kk * __builtin_amdgcn_exp2f(pc[P::GAM + (size_t)r * DK + d]) : kk;
+    }
+    if constexpr (DELTA) stage(sT, LDC, pc + P::TI, C, C, C, tid, 512);
+    if (tid < C) {
+        sDb[tid] = 0.f;
+        sE[tid] = 0.f;
+        sRow[tid] = 0.f;
+        if constexpr (!PERCH) sGam[tid] = pc[P::GAM + tid];
+    }
+    if (tid < DK) {
+        sPhi[tid] = pc[P::PHI + tid];
+        sF[tid] = 0.f;
+    }
+    __syncthreads();
+    auto beta_at = [&](int r) { return (DELTA && r < nvalid) ? beta[row0 + (size_t)r * H] : 0.f; };
+    // row scale of M = diag(rs) K+ (scalar gates: K+ = k 2^gamma_r)
+    auto mscale = [&](int r) { return PERCH ? beta_at(r) : beta_at(r) * __builtin_amdgcn_exp2f(sGam[r]); };
+
+    // ---- phase 1: value slices
+    f32x4 dQt[OWN], nW[OWN], dKb[OWN], dAqk[2], dT[2];
+#pragma unroll
+    for (int m = 0; m < OWN; ++m) dQt[m] = nW[m] = dKb[m] = zero4();
+    dAqk[0] = dAqk[1] = dT[0] = dT[1] = zero4();
+    float dphi = 0.f;
+    float* s1 = smem + SM::S1;
+    float* ds1 = smem + SM::DS1;
+    float* vn1 = smem + SM::VN1;
+    float* dvn1 = smem + SM::DVN1;
+    float* do1 = smem + SM::DO1;
+    float* v1 = smem + SM::V1;
+    float* p1 = smem + SM::P1;
+    for (int s = 0; s < NVS; ++s) {
+        const int dv0 = s * kVS;
+        stage(s1, LVS, hs + ci * DK * DV + dv0, DV, DK, kVS, tid, 512);
+        stage(ds1, LVS, dhs + ci * DK * DV + dv0, DV, DK, kVS, tid, 512);
+        stage(vn1, LVS, vn + ci * C * DV + dv0, DV, C, kVS, tid, 512);
+        stage(dvn1, LVS, dvn + ci * C * DV + dv0, DV, C, kVS, tid, 512);
+        for (int idx = tid; idx < C * kVS; idx += 512) {
+            const int r = idx / kVS, cc = idx % kVS;
+            const bool ok = r < nvalid;
+            const size_t off = (row0 + (size_t)r * H) * DV + dv0 + cc;
+            do1[r * LVS + cc] = ok ? to_f(dout[off]) : 0.f;
+            v1[r * LVS + cc] = ok ? to_f(v[off]) : 0.f;
+        }
+        __syncthreads();
+        {
+            const int ti = wave >> 1, tj = wave & 1;    // one [C][32] tile per wave
+            if constexpr (DELTA) {
+                // P = N - M S_s (N = diag(beta) V), and dN = T^T dVnew -> dv, dbeta
+                const f32x4 x = mmk<DK>(zero4(), sKp + ti * 16 * LDK, LDK, 1, s1 + tj * 16, LVS, 1, lane);
+                const f32x4 dn = mmk<C>(zero4(), sT + ti * 16, 1, LDC, dvn1 + tj * 16, LVS, 1, lane);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = ti * 16 + arow(lane, i), cc = tj * 16 + (lane & 15);
+                    const float bt = beta_at(r), vv = v1[r * LVS + cc];
+                    p1[r * LVS + cc] = bt * vv - mscale(r) * x[i];
+                    if (r < nvalid) dv[(row0 + (size_t)r * H) * DV + dv0 + cc] = from_f<T>(bt * dn[i]);
+                    float part = dn[i] * vv;
+#pragma unroll
+                    for (int off = 1; off < 16; off <<= 1) part += __shfl_xor(part, off, 64);
+                    if ((lane & 15) == 0) atomicAdd(&sDb[r], part);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = ti * 16 + arow(lane, i), cc = tj * 16 + (lane & 15);
+                    if (r < nvalid) dv[(row0 + (size_t)r * H) * DV + dv0 + cc] = from_f<T>(dvn1[r * LVS + cc]);
+                }
+            }
+        }
+        if (tid < DK) {
+#pragma unroll 8
+            for (int e = 0; e < kVS; ++e) dphi += s1[tid * LVS + e] * ds1[tid * LVS + e];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < OWN; ++m) {
+            int ti, tj;
+            trc(m, ti, tj);
+            dQt[m] = mmk<kVS>(dQt[m], do1 + ti * 16 * LVS, LVS, 1, s1 + tj * 16 * LVS, 1, LVS, lane);
+            nW[m] = mmk<kVS>(nW[m], dvn1 + ti * 16 * LVS, LVS, 1, s1 + tj * 16 * LVS, 1, LVS, lane);
+            dKb[m] = mmk<kVS>(dKb[m], vn1 + ti * 16 * LVS, LVS, 1, ds1 + tj * 16 * LVS, 1, LVS, lane);
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int t = wave + 8 * m, ti = t >> 2, tj = t & 3;
+            dAqk[m] = mmk<kVS>(dAqk[m], do1 + ti * 16 * LVS, LVS, 1, vn1 + tj * 16 * LVS, 1, LVS, lane);
+            if constexpr (DELTA)
+                dT[m] = mmk<kVS>(dT[m], dvn1 + ti * 16 * LVS, LVS, 1, p1 + tj * 16 * LVS, 1, LVS, lane);
+        }
+        __syncthreads();
+    }
+    if (tid < DK) sDphi[tid] = dphi;
+
+    // ---- per-element accumulators: dq, dk, E (gamma adjoint, natural units)
+    f32x4 aq[OWN], ak[OWN], aE[OWN];
+#pragma unroll
+    for (int m = 0; m < OWN; ++m) {
+        const int d = ecol(m);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = erow(m, i);
+            const float gm = gam_at(r, d), e = __builtin_amdgcn_exp2f(gm);
+            const float qq = in_at(q, r, d), kk = in_at(k, r, d);
+            // Q~ = q e;  Kbar = k 2^(gamma_last - gamma)
+            const float kbf = __builtin_amdgcn_exp2f((PERCH ? pc[P::GAM + (size_t)(C - 1) * DK + d] : sGam[C - 1]) - gm);
+            const float kbar = kk * kbf;
+            aq[m][i] = dQt[m][i] * e;
+            ak[m][i] = dKb[m][i] * kbf;
+            aE[m][i] = dQt[m][i] * qq * e - dKb[m][i] * kbar;
+            float part = dKb[m][i] * kbar;
+            if constexpr (PERCH) {
+                atomicAdd(&sF[d], part);
+            } else {
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) part += __shfl_xor(part, off, 64);
+                if ((lane & 15) == 0) atomicAdd(&sF[0], part);
+            }
+        }
+    }
+
+    if constexpr (DELTA) {
+        // ---- phase 2a: dM = T^T dW = -T^T nW
+        float* sNW = smem + SM::NW;
+#pragma unroll
+        for (int m = 0; m < OWN; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sNW[erow(m, i) * LDK + ecol(m)] = nW[m][i];
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < OWN; ++m) {
+            int ti, tj;
+            trc(m, ti, tj);
+            const f32x4 acc = mmk<C>(zero4(), sT + ti * 16, 1, LDC, sNW + tj * 16, LDK, 1, lane);
+            const int d = ecol(m);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = erow(m, i);
+                const float dm = -acc[i];
+                const float e = __builtin_amdgcn_exp2f(gam_at(r, d));
+                const float kp = PERCH ? sKp[r * LDK + d] : sKp[r * LDK + d] * e;   // K+ = k e
+                const float bt = beta_at(r);
+                // M = diag(beta) K+ with K+ = k e:  dk += beta e dM,  E += dM M,  dbeta += dM K+
+                ak[m][i] += bt * e * dm;
+                aE[m][i] += dm * bt * kp;
+                float part = dm * kp;
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) part += __shfl_xor(part, off, 64);
+                if ((lane & 15) == 0) atomicAdd(&sDb[r], part);
+            }
+        }
+        __syncthreads();
+        // ---- phase 2b: dA = -T^T dT T^T (strictly lower), dL = diag(beta) dA
+        float* sDT = smem + SM::DT;
+        float* sY = smem + SM::Y;
+        float* sDL = smem + SM::DL;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int t = wave + 8 * m, ti = t >> 2, tj = t & 3;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sDT[(ti * 16 + arow(lane, i)) * LDC + tj * 16 + (lane & 15)] = dT[m][i];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int t = wave + 8 * m, ti = t >> 2, tj = t & 3;
+            const f32x4 acc = mmk<C>(zero4(), sDT + ti * 16 * LDC, LDC, 1, sT + tj * 16 * LDC, 1, LDC, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sY[(ti * 16 + arow(lane, i)) * LDC + tj * 16 + (lane & 15)] = acc[i];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int t = wave + 8 * m, ti = t >> 2, tj = t & 3;
+            const f32x4 acc = mmk<C>(zero4(), sT + ti * 16, 1, LDC, sY + tj * 16, LDC, 1, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = ti * 16 + arow(lane, i), cc = tj * 16 + (lane & 15);
+                const float da = cc < r ? -acc[i] : 0.f;
+                const float lrc = pc[P::L + (size_t)r * C + cc];
+                sDL[r * LDC + cc] = beta_at(r) * da;
+                float part = da * lrc;
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) part += __shfl_xor(part, off, 64);
+                if ((lane & 15) == 0) atomicAdd(&sDb[r], part);
+            }
+        }
+    }
+    // ---- dAqk (lower incl.) to LDS
+    float* sDAqk = smem + SM::DAQK;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const int t = wave + 8 * m, ti = t >> 2, tj = t & 3;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = ti * 16 + arow(lane, i), cc = tj * 16 + (lane & 15);
+            sDAqk[r * LDC + cc] = cc <= r ? dAqk[m][i] : 0.f;
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 2c: the pairwise products
+    float* sKm = smem + SM::KM;     // kda: K-;  scalar: raw q
+    float* sQt = smem + SM::QT;     // kda: Q~
+    float* sDL = smem + SM::DL;
+    for (int idx = tid; idx < C * DK; idx += 512) {
+        const int r = idx / DK, d = idx % DK;
+        const float qq = in_at(q, r, d);
+        if constexpr (PERCH) {
+            const float gm = pc[P::GAM + (size_t)r * DK + d];
+            const float kk = in_at(k, r, d);
+            sKm[r * LDK + d] = kk * __builtin_amdgcn_exp2f(-gm);
+            sQt[r * LDK + d] = qq * __builtin_amdgcn_exp2f(gm);
+        } else {
+            sKm[r * LDK + d] = qq;
+        }
+    }
+    if constexpr (!PERCH) {
+        // G = dX .* Gamma in place, and the log-gate terms of the pair products:
+        // E_i += sum_j dX_ij X_ij,  E_j -= sum_i dX_ij X_ij  (X = L, Aqk)
+        for (int idx = tid; idx < C * C; idx += 512) {
+            const int r = idx / C, cc = idx % C;
+            float contrib = 0.f;
+            if (cc <= r) {
+                const float gmm = __builtin_amdgcn_exp2f(sGam[r] - sGam[cc]);
+                const float daq = sDAqk[r * LDC + cc];
+                contrib += daq * pc[P::AQK + idx];
+                sDAqk[r * LDC + cc] = daq * gmm;
+                if constexpr (DELTA) {
+                    const float dl = sDL[r * LDC + cc];
+                    contrib += dl * pc[P::L + idx];
+                    sDL[r * LDC + cc] = dl * gmm;
+                }
+            }
+            if (contrib != 0.f) {
+                atomicAdd(&sE[r], contrib);
+                atomicAdd(&sE[cc], -contrib);
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < OWN; ++m) {
+        int ti, tj;
+        trc(m, ti, tj);
+        const int d = ecol(m);
+        if constexpr (PERCH) {
+            // dK+ += dL K-;  dK- = dL^T K+ + dAqk^T Q~;  dQ~ += dAqk K-
+            const f32x4 dkp = mmk<C>(zero4(), sDL + ti * 16 * LDC, LDC, 1, sKm + tj * 16, LDK, 1, lane);
+            f32x4 dkm = mmk<C>(zero4(), sDL + ti * 16, 1, LDC, sKp + tj * 16, LDK, 1, lane);
+            dkm = mmk<C>(dkm, sDAqk + ti * 16, 1, LDC, sQt + tj * 16, LDK, 1, lane);
+            const f32x4 dqt = mmk<C>(zero4(), sDAqk + ti * 16 * LDC, LDC, 1, sKm + tj * 16, LDK, 1, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = erow(m, i);
+                const float gm = pc[P::GAM + (size_t)r * DK + d];
+                const float e = __builtin_amdgcn_exp2f(gm), ei = __builtin_amdgcn_exp2f(-gm);
+                ak[m][i] += dkp[i] * e + dkm[i] * ei;
+                aq[m][i] += dqt[i] * e;
+                aE[m][i] += dkp[i] * sKp[r * LDK + d] - dkm[i] * sKm[r * LDK + d] + dqt[i] * sQt[r * LDK + d];
+            }
+        } else {
+            // raw k (sKp), raw q (sKm): dk += G_L k + G_L^T k + G_Q^T q;  dq += G_Q k
+            f32x4 dkk = mmk<C>(zero4(), sDAqk + ti * 16, 1, LDC, sKm + tj * 16, LDK, 1, lane);
+            if constexpr (DELTA) {
+                dkk = mmk<C>(dkk, sDL + ti * 16 * LDC, LDC, 1, sKp + tj * 16, LDK, 1, lane);
+                dkk = mmk<C>(dkk, sDL + ti * 16, 1, LDC, sKp + tj * 16, LDK, 1, lane);
+            }
+            const f32x4 dqq = mmk<C>(zero4(), sDAqk + ti * 16 * LDC, LDC, 1, sKp + tj * 16, LDK, 1, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ak[m][i] += dkk[i];
+                aq[m][i] += dqq[i];
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 3: write dq, dk; E to LDS, then the reverse cumsum per column
+    float* sEm = smem + SM::E;
+#pragma unroll
+    for (int m = 0; m < OWN; ++m) {
+        const int d = ecol(m);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = erow(m, i);
+            sEm[r * LDK + d] = aE[m][i];
+            if (r < nvalid) {
+                const size_t off = (row0 + (size_t)r * H) * DK + d;
+                dq[off] = from_f<T>(aq[m][i]);
+                dk[off] = from_f<T>(ak[m][i]);
+            }
+        }
+    }
+    __syncthreads();
+    if constexpr (PERCH) {
+        if (tid < DK) {
+            const int d = tid;
+            float acc = sF[d] + sDphi[d] * sPhi[d];
+            for (int r = C - 1; r >= 0; --r) {
+                acc += sEm[r * LDK + d];
+                if (r < nvalid) dg[(row0 + (size_t)r * H) * DK + d] = acc;
+            }
+        }
+    } else {
+        if (tid < C) {
+            float s = sE[tid];
+            for (int d = 0; d < DK; ++d) s += sEm[tid * LDK + d];
+            sRow[tid] = s;
+        }
+        if (tid == C) {
+            float s = 0.f;
+            for (int d = 0; d < DK; ++d) s += sDphi[d];
+            sF[1] = s * sPhi[0];
+        }
+        __syncthreads();
+        if (tid == 0) {
+            float acc = sF[0] + sF[1];
+            for (int r = C - 1; r >= 0; --r) {
+                acc += sRow[r];
+                if (r < nvalid) dg[row0 + (size_t)r * H] = acc;
+            }
+        }
+    }
+    if constexpr (DELTA) {
+        if (tid < nvalid) dbeta[row0 + (size_t)tid * H] = sDb[tid];
+    }
+}
+
+}  // namespace bw
+}  // namespace dr

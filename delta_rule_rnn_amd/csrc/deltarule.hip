@@ -10,6 +10,7 @@
 #include "intra.h"
 #include "decode.h"
 #include "steps.h"
+#include "backward.h"
 
 namespace {
 
@@ -392,9 +393,118 @@ dr_status decode(int kind, const void* q, const void* k, const void* v, const fl
     }
 }
 
+// ---- backward ------------------------------------------------------------------
+// Workspace: the natural fp32 chunk arrays of the prep kernel, then the entry
+// states S_c [DK][DV], the exit adjoints dS'_c [DK][DV], Vnew_c and dVnew_c
+// [C][DV] of every chunk, each block 256-byte aligned.
+struct BwdLayout {
+    size_t prep, hs, dhs, vn, dvn, bytes;
+};
+BwdLayout bwd_layout(int B, int T, int H, int D) {
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t n = (size_t)B * H * (size_t)ceil_div(T, dr::kChunk);
+    const size_t pf = D == 64 ? dr::bw::Prep<64>::FLOATS : dr::bw::Prep<128>::FLOATS;
+    BwdLayout L;
+    L.prep = 0;
+    L.hs = up(n * pf * 4);
+    L.dhs = L.hs + up(n * D * D * 4);
+    L.vn = L.dhs + up(n * D * D * 4);
+    L.dvn = L.vn + up(n * dr::kChunk * D * 4);
+    L.bytes = L.dvn + up(n * dr::kChunk * D * 4);
+    return L;
+}
+
+struct BwdArgs {
+    const void *q, *k, *v, *dout;
+    const float *g, *beta, *h0, *dhT;
+    void *dq, *dk, *dv;
+    float *dg, *dbeta, *dh0;
+    int B, T, H, NT;
+    uint8_t* ws;
+    BwdLayout L;
+};
+
+template <int KIND, typename E, int D>
+dr_status launch_backward_t(const BwdArgs& a, hipStream_t st) {
+    using namespace dr::bw;
+    float* prep = reinterpret_cast<float*>(a.ws + a.L.prep);
+    float* hs = reinterpret_cast<float*>(a.ws + a.L.hs);
+    float* dhs = reinterpret_cast<float*>(a.ws + a.L.dhs);
+    float* vn = reinterpret_cast<float*>(a.ws + a.L.vn);
+    float* dvn = reinterpret_cast<float*>(a.ws + a.L.dvn);
+    const E* q = static_cast<const E*>(a.q);
+    const E* k = static_cast<const E*>(a.k);
+    const E* v = static_cast<const E*>(a.v);
+    const E* dout = static_cast<const E*>(a.dout);
+    const long long items = (long long)a.B * a.NT * a.H;
+    const long long slices = (long long)a.B * a.H * (D / kVS);
+    if (items > 0x7fffffffLL || slices > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL((bwd_prep_kernel<KIND, E, D>), dim3((unsigned)items), dim3(256), 0, st, q, k, v, a.g, a.beta,
+                       prep, a.T, a.H, a.NT);
+    dr_status s = check_launch();
+    if (s != DR_OK) return s;
+    hipLaunchKernelGGL((bwd_state_fwd_kernel<KIND, D>), dim3((unsigned)slices), dim3(256), 0, st, prep, a.h0, hs, vn,
+                       a.H, a.NT);
+    if ((s = check_launch()) != DR_OK) return s;
+    hipLaunchKernelGGL((bwd_state_rev_kernel<KIND, E, D>), dim3((unsigned)slices), dim3(256), 0, st, prep, dout, a.dhT,
+                       dhs, dvn, a.dh0, a.T, a.H, a.NT);
+    if ((s = check_launch()) != DR_OK) return s;
+    hipLaunchKernelGGL((bwd_grad_kernel<KIND, E, D>), dim3((unsigned)items), dim3(512), 0, st, q, k, v, a.beta, dout,
+                       prep, hs, dhs, vn, dvn, static_cast<E*>(a.dq), static_cast<E*>(a.dk), static_cast<E*>(a.dv),
+                       a.dg, a.dbeta, a.T, a.H, a.NT);
+    return check_launch();
+}
+
+template <int KIND>
+dr_status launch_backward_k(const BwdArgs& a, int D, int dtype, hipStream_t st) {
+    if (dtype == DR_BF16) {
+        if (D == 64) return launch_backward_t<KIND, bf16, 64>(a, st);
+        return launch_backward_t<KIND, bf16, 128>(a, st);
+    }
+    if (D == 64) return launch_backward_t<KIND, float, 64>(a, st);
+    return launch_backward_t<KIND, float, 128>(a, st);
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t dr_backward_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, int C, int dtype) {
+    if (kind < 0 || kind > 2 || B <= 0 || H <= 0 || T < 0) return 0;
+    if (dr_record_bytes(Dk, Dv, C, dtype) == 0) return 0;
+    return bwd_layout(B, T, H, Dk).bytes;
+}
+
+dr_status dr_backward(int kind, const void* q, const void* k, const void* v, const float* g, const float* beta,
+                      const float* h0, const void* dout, const float* dhT, void* dq, void* dk, void* dv, float* dg,
+                      float* dbeta, float* dh0, int B, int T, int H, int Dk, int Dv, int C, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    dr_status s = validate(kind, q, k, v, g, beta, B, T, H, Dk, Dv, C, dtype);
+    if (s != DR_OK) return s;
+    const bool delta = kind != DR_KIND_DECAY_LA;
+    if (T > 0 && (!dout || !dq || !dk || !dv || !dg || (delta && !dbeta))) return DR_ERR_INVALID_ARG;
+    const void* ptrs[] = {h0, dout, dhT, dq, dk, dv, dg, dbeta, dh0, workspace};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return DR_ERR_INVALID_ARG;
+    const BwdLayout L = bwd_layout(B, T, H, Dk);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (T == 0) {
+        // no tokens: dh0 = dhT (or zero); nothing else to write
+        if (!dh0) return DR_OK;
+        const size_t n = (size_t)B * H * Dk * Dv;
+        hipLaunchKernelGGL(dr::copy_or_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dh0, dhT, n);
+        return check_launch();
+    }
+    if (!workspace || workspace_bytes < L.bytes) return DR_ERR_WORKSPACE;
+    BwdArgs a{q, k, v, dout, g, delta ? beta : nullptr, h0, dhT, dq, dk, dv, dg, delta ? dbeta : nullptr, dh0,
+              B, T, H, ceil_div(T, dr::kChunk), static_cast<uint8_t*>(workspace), L};
+    switch (kind) {
+        case DR_KIND_KDA: return launch_backward_k<dr::KIND_KDA>(a, Dk, dtype, st);
+        case DR_KIND_GDN: return launch_backward_k<dr::KIND_GDN>(a, Dk, dtype, st);
+        default: return launch_backward_k<dr::KIND_LA>(a, Dk, dtype, st);
+    }
+}
+
 
 size_t dr_record_bytes(int Dk, int Dv, int C, int dtype) {
     if (Dk != Dv || (Dk != 64 && Dk != 128) || C != dr::kChunk) return 0;
@@ -580,6 +690,6 @@ const char* dr_status_string(int status) {
     }
 }
 
-int dr_abi_version(void) { return 2; }
+int dr_abi_version(void) { return 3; }
 
 }  // extern "C"

@@ -166,4 +166,13 @@ __global__ __launch_bounds__(1024) void varlen_table_kernel(const int* __restric
     if (flags && bad) atomicOr(flags, 4u);
 }
 
+// dst[i] = src ? src[i] : 0 for i < n (a fill that graph capture records as
+// a kernel node).
+__global__ __launch_bounds__(256) void copy_or_zero_kernel(float* __restrict__ dst, const float* __restrict__ src,
+                                                           size_t n)
+{
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) dst[i] = src ? src[i] : 0.f;
+}
+
 }  // namespace dr

@@ -322,6 +322,53 @@ def decode(kind: str, q, k, v, g, beta=None, state=None, **kw) -> torch.Tensor:
     return {"kda": kda_decode, "gdn": gdn_decode}[kind](q, k, v, g, beta, state, **kw)
 
 
+# ---- backward -------------------------------------------------------------------
+
+def backward_workspace_bytes(kind: str, B: int, T: int, H: int, Dk: int, Dv: int, dtype: torch.dtype,
+                             chunk_size: int = CHUNK) -> int:
+    code = DR_BF16 if dtype == torch.bfloat16 else DR_F32
+    return int(_lib.load().dr_backward_workspace_bytes(KINDS[kind], B, T, H, Dk, Dv, chunk_size, code))
+
+
+def backward(kind: str, q, k, v, g, beta=None, h0=None, do=None, dhT=None, chunk_size=CHUNK, workspace=None,
+             stream=None):
+    """Gradients of the forward of ``kind`` given do (the adjoint of o, like
+    o) and dhT (the adjoint of hT, fp32 [B,H,Dk,Dv] or None).  Returns
+    (dq, dk, dv, dg, dbeta, dh0): dq, dk, dv in the I/O dtype, dg like g,
+    dbeta [B,T,H] fp32 (None for decay_la), dh0 fp32 [B,H,Dk,Dv] (zeros
+    of h0's shape also when h0 is None)."""
+    lib = _lib.load()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    _need(q, "q"); _need(k, "k", dt, q.shape); _need(v, "v", dt, (B, T, H, Dv))
+    _need(g, "g", torch.float32, (B, T, H, Dk) if kind == "kda" else (B, T, H))
+    if kind != "decay_la":
+        if beta is None:
+            raise DeltaRuleError("beta is required")
+        _need(beta, "beta", torch.float32, (B, T, H))
+    else:
+        beta = None
+    if do is None:
+        raise DeltaRuleError("do (the adjoint of o) is required")
+    _need(do, "do", dt, (B, T, H, Dv))
+    _need(h0, "h0", torch.float32, (B, H, Dk, Dv))
+    _need(dhT, "dhT", torch.float32, (B, H, Dk, Dv))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg = torch.empty_like(g)
+    dbeta = torch.empty_like(beta) if beta is not None else None
+    dh0 = torch.empty(B, H, Dk, Dv, dtype=torch.float32, device=q.device)
+    need = backward_workspace_bytes(kind, B, T, H, Dk, Dv, dt, chunk_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8)
+    st = lib.dr_backward(KINDS[kind], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(do), _ptr(dhT),
+                         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0), B, T, H, Dk, Dv, chunk_size,
+                         _dtype_code(q), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "dr_backward")
+    return dq, dk, dv, dg, dbeta, dh0
+
+
 # ---- individual steps ------------------------------------------------------
 
 def chunk_cumsum(g: torch.Tensor, chunk_size: int = CHUNK, stream=None) -> torch.Tensor:

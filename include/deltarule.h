@@ -250,6 +250,37 @@ dr_status dr_decode(int kind, const void* q, const void* k, const void* v, const
                     int B, int T, int H, int Dk, int Dv, int dtype,
                     const dr_prologue* prologue, void* stream);
 
+/* ---- backward -------------------------------------------------------------- */
+
+/*
+ * Gradients of the forward selected by `kind` (the plain path: inputs as the
+ * recurrence takes them, no prologue) with respect to q, k, v, g, beta and
+ * h0, given the adjoints of o and hT (page "Gated DeltaNet", section
+ * "反向传播：状态伴随与三角变换梯度"): the chunk operands are recomputed, the
+ * chunk entry states rebuilt by a forward state pass, the state adjoint run
+ * backwards over the chunks, and the per-chunk gradients taken through the
+ * triangular inverse; the gate gradient is the reverse cumulative sum of the
+ * log-gate adjoint inside each chunk.
+ *   q, k, v, g, beta, h0: as for the forward (same sizes and layouts)
+ *   dout:  [B,T,H,Dv] (dtype), the adjoint of o
+ *   dhT:   [B,H,Dk,Dv] float, the adjoint of hT, or NULL (zero)
+ *   dq, dk: [B,T,H,Dk] (dtype); dv: [B,T,H,Dv] (dtype), written
+ *   dg:    float, shape of g, written
+ *   dbeta: [B,T,H] float, written (delta kinds; ignored for decay_la)
+ *   dh0:   [B,H,Dk,Dv] float, written, or NULL
+ *   workspace: at least dr_backward_workspace_bytes(...): the recomputed
+ *          fp32 chunk operands, the chunk entry states and exit adjoints
+ *          (fp32 [Dk,Dv] per chunk) and Vnew / dVnew per chunk
+ * All arithmetic is fp32.  Other conventions and errors as for kda_fwd.
+ * T = 0 writes dh0 = dhT (or zero) and nothing else.
+ */
+size_t dr_backward_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, int C, int dtype);
+dr_status dr_backward(int kind, const void* q, const void* k, const void* v, const float* g,
+                      const float* beta, const float* h0, const void* dout, const float* dhT,
+                      void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dh0,
+                      int B, int T, int H, int Dk, int Dv, int C, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- the individual steps ---------------------------------------------- */
 
 /*
@@ -325,7 +356,8 @@ size_t dr_record_bytes(int Dk, int Dv, int C, int dtype);
 /* Human-readable text for a status code (static storage). */
 const char* dr_status_string(int status);
 
-/* ABI version of this library: 2 (1 plus the prologue entry points). */
+/* ABI version of this library: 3 (1, plus the prologue entry points in 2, plus
+ * the backward in 3). */
 int dr_abi_version(void);
 
 #ifdef __cplusplus

@@ -1,0 +1,122 @@
+"""GPU parity of the backward (dr_backward through the C ABI) against the
+fp64 oracle's reverse sweep of the token recurrence (oracle/backward.py).
+Page: "Gated DeltaNet", section "反向传播：状态伴随与三角变换梯度".
+
+Tolerances: fp32 I/O max-rel 1e-4 for every gradient; bf16 I/O rel-L2 and
+max-rel 2e-2 (the inputs are the same bf16 values on both sides; the kernels
+compute in fp32 and round dq, dk, dv once to bf16 on the store; dg, dbeta
+and dh0 are fp32 outputs).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.backward import recurrence_backward
+from delta_rule_rnn_amd.inputs import Workload, generate
+
+from .test_gpu_parity import assert_close, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _ops():
+    import delta_rule_rnn_amd as dra
+    return dra
+
+
+def _cotangents(w, seed):
+    gen = torch.Generator().manual_seed(seed)
+    do = torch.randn(w.B, w.T, w.H, w.Dv, generator=gen)
+    dhT = torch.randn(w.B, w.H, w.Dk, w.Dv, generator=gen) * 0.1
+    return do, dhT
+
+
+def _run(kind, dt, D, B, H, T, seed, with_h0=True, with_dhT=True):
+    dra = _ops()
+    w = Workload(f"{kind}_bwd", kind, dt, B=B, H=H, T=T, Dk=D, Dv=D, h0_std=0.2 if with_h0 else 0.0, seed=seed)
+    x = generate(w)
+    do, dhT = _cotangents(w, seed + 100)
+    do = do.to(x["q"].dtype)
+    dhT = dhT if with_dhT else None
+    d = to_dev(x)
+    res = dra.backward(kind, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], do.to("cuda:0"),
+                       None if dhT is None else dhT.to("cuda:0"))
+    torch.cuda.synchronize()
+    ref = recurrence_backward(kind, x["q"], x["k"], x["v"], x["g"], x["beta"],
+                              None if x["h0"] is None else x["h0"].transpose(-1, -2), do,
+                              None if dhT is None else dhT.transpose(-1, -2))
+    return res, ref
+
+
+def _check(res, ref, kind, dt, what):
+    dq, dk, dv, dg, dbeta, dh0 = (None if t is None else t.float().cpu().numpy() for t in res)
+    assert_close(dq, ref["dq"], dt, f"{what} dq")
+    assert_close(dk, ref["dk"], dt, f"{what} dk")
+    assert_close(dv, ref["dv"], dt, f"{what} dv")
+    assert_close(dg, ref["dg"], "f32" if dt == "f32" else dt, f"{what} dg")
+    if kind != "decay_la":
+        assert_close(dbeta, ref["dbeta"], dt, f"{what} dbeta")
+    assert_close(dh0, np.swapaxes(ref["dh0"], -1, -2), dt, f"{what} dh0")
+
+
+CASES = [(kind, dt, D) for kind in ("kda", "gdn", "decay_la") for dt in ("f32", "bf16") for D in (64, 128)]
+
+
+@pytest.mark.parametrize("kind,dt,D", CASES, ids=lambda c: str(c))
+def test_backward_matches_oracle(kind, dt, D):
+    """Three chunks, the last ragged (150 = 64 + 64 + 22), two batches and
+    heads, an initial state and a final-state cotangent."""
+    res, ref = _run(kind, dt, D, B=2, H=2, T=150, seed=71)
+    _check(res, ref, kind, dt, f"{kind} {dt} D{D}")
+
+
+@pytest.mark.parametrize("kind", ["kda", "gdn", "decay_la"])
+@pytest.mark.parametrize("T", [1, 64, 65])
+def test_backward_lengths(kind, T):
+    """One token, exactly one chunk, one chunk plus one token (with an
+    initial state, so that every gradient is nonzero)."""
+    res, ref = _run(kind, "f32", 64, B=1, H=3, T=T, seed=72, with_h0=True, with_dhT=False)
+    _check(res, ref, kind, "f32", f"{kind} T={T}")
+
+
+@pytest.mark.parametrize("kind", ["kda", "gdn", "decay_la"])
+def test_backward_zero_initial_state(kind):
+    """No initial state and no final-state cotangent (h0 = dhT = NULL)."""
+    res, ref = _run(kind, "bf16", 128, B=1, H=2, T=200, seed=75, with_h0=False, with_dhT=False)
+    _check(res, ref, kind, "bf16", f"{kind} zero h0")
+
+
+def test_backward_no_tokens():
+    dra = _ops()
+    w = Workload("gdn_bwd0", "gdn", "f32", B=2, H=2, T=0, Dk=64, Dv=64, h0_std=1.0, seed=73)
+    d = to_dev(generate(w))
+    dhT = torch.randn(2, 2, 64, 64, device="cuda:0")
+    do = torch.empty(2, 0, 2, 64, device="cuda:0")
+    _, _, _, _, _, dh0 = dra.backward("gdn", d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], do, dhT)
+    _, _, _, _, _, dz = dra.backward("gdn", d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], do, None)
+    torch.cuda.synchronize()
+    assert torch.equal(dh0, dhT) and torch.count_nonzero(dz).item() == 0
+
+
+def test_backward_long_sampled():
+    """KDA bf16 d=128 over 1000 tokens (16 chunks): every gradient of two
+    sampled (b, h) chains against the oracle run on those chains."""
+    dra = _ops()
+    w = Workload("kda_bwd_long", "kda", "bf16", B=1, H=6, T=1000, Dk=128, Dv=128, h0_std=0.1, seed=74)
+    x = generate(w)
+    do, dhT = _cotangents(w, 174)
+    do = do.to(torch.bfloat16)
+    d = to_dev(x)
+    res = dra.backward("kda", d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], do.to("cuda:0"), dhT.to("cuda:0"))
+    torch.cuda.synchronize()
+    res = [t.float().cpu().numpy() for t in res]
+    for h in (1, 4):
+        sl = lambda t: t[:, :, h:h + 1].contiguous()
+        ref = recurrence_backward("kda", sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]),
+                                  x["h0"][:, h:h + 1].transpose(-1, -2), sl(do), dhT[:, h:h + 1].transpose(-1, -2))
+        names = ["dq", "dk", "dv", "dg", "dbeta"]
+        for n, r in zip(names, res[:5]):
+            assert_close(r[:, :, h:h + 1], ref[n], "bf16", f"head {h} {n}")
+        assert_close(res[5][:, h:h + 1], np.swapaxes(ref["dh0"], -1, -2), "bf16", f"head {h} dh0")
