@@ -204,6 +204,53 @@ def varlen_bench(args):
     print(json.dumps(line), flush=True)
 
 
+def backward_bench(args):
+    """Backward of the workload's forward (dq, dk, dv, dg, dbeta, dh0 from do
+    and dhT), inputs and cotangents resident in HBM, one dr_backward call per
+    step timed with HIP events on the launch stream.  The split between its
+    four kernels comes from a rocprofv3 kernel trace (profiles/)."""
+    import torch
+    import delta_rule_rnn_amd as dra
+    from delta_rule_rnn_amd.inputs import WORKLOADS, generate
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = {n: (t.to(dev) if t is not None else None) for n, t in generate(w).items()}
+    gen = torch.Generator().manual_seed(99)
+    do = torch.randn(w.B, w.T, w.H, w.Dv, generator=gen).to(d["q"].dtype).to(dev)
+    dhT = (torch.randn(w.B, w.H, w.Dk, w.Dv, generator=gen) * 0.1).to(dev)
+    ws = torch.empty(dra.backward_workspace_bytes(w.kind, w.B, w.T, w.H, w.Dk, w.Dv, d["q"].dtype),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    call = lambda: dra.backward(w.kind, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], do, dhT, workspace=ws)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record(stream)
+        call()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+    ev_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    tokens = w.B * w.T
+    line = {
+        "metric": "bwd tokens/sec (1 GPU), all gradients", "value": round(tokens / (ms / 1000.0), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 compute, " + ("bf16" if d["q"].dtype == torch.bfloat16 else "f32") + " I/O",
+        "data": "synthetic",
+        "config": {"workload": f"{w.kind}_bwd B={w.B} H={w.H} T={w.T} dk={w.Dk} dv={w.Dv} C={w.C}",
+                   "workspace_bytes": ws.numel(), "parallelism": "single GPU"},
+        "median_ms_per_call_events": round(ev_ms[len(ev_ms) // 2], 4),
+        "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def prologue_bench(args):
     """Forward with the fused input prologue on raw projections (the
     workload's sizes; q, k unnormalised, beta logits, and for scalar gates
@@ -277,11 +324,12 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens of the workload the CPU oracle is timed on")
     ap.add_argument("--cpu-threads", type=int, default=0)
-    ap.add_argument("--mode", choices=("prefill", "decode", "varlen", "prologue"), default="prefill",
+    ap.add_argument("--mode", choices=("prefill", "decode", "varlen", "prologue", "backward"), default="prefill",
                     help="prefill: the chunked forward (the benchmark line); decode: the "
                          "recurrent step on a serving-sized batch; varlen: the forward over "
                          "packed sequences of mixed lengths with the workload's token count; "
-                         "prologue: the forward with the fused input prologue on raw inputs")
+                         "prologue: the forward with the fused input prologue on raw inputs; "
+                         "backward: all gradients of the forward")
     ap.add_argument("--decode-batch", type=int, default=64, help="sequences per decode call")
     ap.add_argument("--decode-tokens", type=int, default=1, help="new tokens per sequence per call")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -314,6 +362,9 @@ def main():
         return
     if args.mode == "prologue":
         prologue_bench(args)
+        return
+    if args.mode == "backward":
+        backward_bench(args)
         return
 
     import torch

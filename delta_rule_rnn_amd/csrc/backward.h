@@ -45,6 +45,7 @@ namespace dr {
 namespace bw {
 
 constexpr int C = kChunk;
+static_assert(C * C % 512 == 0 && C * 16 % 256 == 0, "strided loops assume exact trip counts");
 constexpr int kVS = 32;            // value columns per state-pass workgroup / gradient slice
 constexpr int LVS = kVS + 4;       // padded row of [*, 32] fp32 tiles
 constexpr int LDC = C + 4;         // padded row of [C, C] fp32 tiles
@@ -83,21 +84,36 @@ __device__ __forceinline__ f32x4 mmk(f32x4 acc, const float* A, int ar, int ak, 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 __device__ __forceinline__ int arow(int lane, int i) { return 4 * (lane >> 4) + i; }
 
-// Cooperative copy of a [rows][cols] fp32 block (row stride gs floats) into
-// LDS (row stride ls floats); cols % 4 == 0, both strides multiples of 4.
-__device__ __forceinline__ void stage(float* dst, int ls, const float* __restrict__ src, size_t gs, int rows, int cols,
-                                      int tid, int nthr) {
-    const int per = cols / 4;
-    for (int idx = tid; idx < rows * per; idx += nthr) {
-        const int r = idx / per, c4 = (idx % per) * 4;
-        *reinterpret_cast<float4*>(dst + r * ls + c4) = *reinterpret_cast<const float4*>(src + r * gs + c4);
+// Cooperative copy of a [ROWS][COLS] fp32 block (row stride gs floats) into
+// LDS (row stride ls floats, a multiple of 4) by NTHR threads.  The shape is
+// known at compile time, so each thread issues up to 8 float4 loads before
+// the first store (the loads' latencies overlap instead of adding up).
+template <int ROWS, int COLS, int NTHR>
+__device__ __forceinline__ void stage(float* dst, int ls, const float* __restrict__ src, size_t gs, int tid) {
+    constexpr int PER = COLS / 4, N = ROWS * PER, IT = N / NTHR, BT = IT < 8 ? IT : 8;
+    static_assert(COLS % 4 == 0 && N % NTHR == 0 && IT % BT == 0, "staging shape");
+#pragma unroll
+    for (int i0 = 0; i0 < IT; i0 += BT) {
+        float4 buf[BT];
+#pragma unroll
+        for (int j = 0; j < BT; ++j) {
+            const int idx = tid + (i0 + j) * NTHR, r = idx / PER, c4 = (idx % PER) * 4;
+            buf[j] = *reinterpret_cast<const float4*>(src + r * gs + c4);
+        }
+#pragma unroll
+        for (int j = 0; j < BT; ++j) {
+            const int idx = tid + (i0 + j) * NTHR, r = idx / PER, c4 = (idx % PER) * 4;
+            *reinterpret_cast<float4*>(dst + r * ls + c4) = buf[j];
+        }
     }
 }
-__device__ __forceinline__ void unstage(float* __restrict__ dst, size_t gs, const float* src, int ls, int rows,
-                                        int cols, int tid, int nthr) {
-    const int per = cols / 4;
-    for (int idx = tid; idx < rows * per; idx += nthr) {
-        const int r = idx / per, c4 = (idx % per) * 4;
+template <int ROWS, int COLS, int NTHR>
+__device__ __forceinline__ void unstage(float* __restrict__ dst, size_t gs, const float* src, int ls, int tid) {
+    constexpr int PER = COLS / 4, N = ROWS * PER, IT = N / NTHR;
+    static_assert(COLS % 4 == 0 && N % NTHR == 0, "staging shape");
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+        const int idx = tid + i * NTHR, r = idx / PER, c4 = (idx % PER) * 4;
         *reinterpret_cast<float4*>(dst + r * gs + c4) = *reinterpret_cast<const float4*>(src + r * ls + c4);
     }
 }
@@ -145,18 +161,30 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
     float* out = prep + (((size_t)b * H + h) * NT + c) * P::FLOATS;
 
     // ---- inputs, rows past the end of a ragged chunk zero
-    for (int idx = tid; idx < C * DK; idx += 256) {
+    #pragma unroll 8
+    for (int it_ = 0; it_ < (C * DK) / 256; ++it_) {
+        const int idx = tid + it_ * 256;
         const int r = idx / DK, d = idx % DK;
+        // rows past the end load the last valid row (every load unconditional)
         const bool ok = r < nvalid;
-        const size_t off = (row0 + (size_t)r * H) * DK + d;
-        sA[r * LDK + d] = ok ? to_f(k[off]) : 0.f;
-        sQ[r * LDK + d] = ok ? to_f(q[off]) : 0.f;
-        if constexpr (PERCH) sB[r * LDK + d] = ok ? g[off] : 0.f;
+        const size_t off = (row0 + (size_t)min(r, nvalid - 1) * H) * DK + d;
+        const float kk = to_f(k[off]), qq = to_f(q[off]);
+        sA[r * LDK + d] = ok ? kk : 0.f;
+        sQ[r * LDK + d] = ok ? qq : 0.f;
+        if constexpr (PERCH) {
+            const float gg = g[off];
+            sB[r * LDK + d] = ok ? gg : 0.f;
+        }
     }
     if (tid < C) {
         const bool ok = tid < nvalid;
-        sBeta[tid] = (DELTA && ok) ? beta[row0 + (size_t)tid * H] : 0.f;
-        if constexpr (!PERCH) sGam[tid] = ok ? g[row0 + (size_t)tid * H] : 0.f;
+        const size_t rr = row0 + (size_t)min(tid, nvalid - 1) * H;
+        const float bb = DELTA ? beta[rr] : 0.f;
+        sBeta[tid] = ok ? bb : 0.f;
+        if constexpr (!PERCH) {
+            const float gg = g[rr];
+            sGam[tid] = ok ? gg : 0.f;
+        }
     }
     __syncthreads();
 
@@ -196,7 +224,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
         }
         __syncthreads();
         const float gl = sGam[C - 1];
-        for (int idx = tid; idx < C * DK; idx += 256) {
+        #pragma unroll 8
+        for (int it_ = 0; it_ < (C * DK) / 256; ++it_) {
+            const int idx = tid + it_ * 256;
             const int r = idx / DK, d = idx % DK;
             out[P::QT + (size_t)r * DK + d] = sQ[r * LDK + d] * __builtin_amdgcn_exp2f(sGam[r]);
             out[P::KB + (size_t)r * DK + d] = sA[r * LDK + d] * __builtin_amdgcn_exp2f(gl - sGam[r]);
@@ -234,25 +264,39 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
     }
     __syncthreads();
 
-    // ---- T = (I + diag(beta) L)^-1 by forward substitution, one column per lane
+    // ---- T = (I + diag(beta) L)^-1 by forward substitution, one column per
+    // lane held in registers (fully unrolled: the rows of L are broadcast
+    // LDS reads, no LDS round trip through T)
     if constexpr (DELTA) {
         if (wave == 0) {
             const int j = lane;
-            for (int i = 0; i < C; ++i) sT[i * LDC + j] = (i == j) ? 1.f : 0.f;
-            for (int i = j + 1; i < C; ++i) {
+            float t[C];
+#pragma unroll
+            for (int i = 0; i < C; ++i) {
                 float s = 0.f;
-                for (int m = j; m < i; ++m) s += sL[i * LDC + m] * sT[m * LDC + j];
-                sT[i * LDC + j] = -sBeta[i] * s;
+#pragma unroll
+                for (int m = 0; m < i; ++m) s += sL[i * LDC + m] * t[m];
+                // t[m] = 0 for m < j, so rows above the diagonal contribute nothing
+                t[i] = i < j ? 0.f : (i == j ? 1.f : -sBeta[i] * s);
             }
+#pragma unroll
+            for (int i = 0; i < C; ++i) sT[i * LDC + j] = t[i];
         }
         __syncthreads();
-        for (int idx = tid; idx < C * C; idx += 256) out[P::TI + idx] = sT[(idx / C) * LDC + idx % C];
+        #pragma unroll 8
+        for (int it_ = 0; it_ < (C * C) / 256; ++it_) {
+            const int idx = tid + it_ * 256;
+            out[P::TI + idx] = sT[(idx / C) * LDC + idx % C];
+        }
     }
 
     // ---- M = diag(beta) K+ (in place) and N = diag(beta) V (into sQ)
-    for (int idx = tid; idx < C * DK; idx += 256) {
+    #pragma unroll 8
+    for (int it_ = 0; it_ < (C * DK) / 256; ++it_) {
+        const int idx = tid + it_ * 256;
         const int r = idx / DK, d = idx % DK;
-        const float vv = r < nvalid ? to_f(v[(row0 + (size_t)r * H) * DV + d]) : 0.f;
+        const float vl = to_f(v[(row0 + (size_t)min(r, nvalid - 1) * H) * DV + d]);
+        const float vv = r < nvalid ? vl : 0.f;
         if constexpr (DELTA) {
             const float rs = PERCH ? sBeta[r] : sBeta[r] * __builtin_amdgcn_exp2f(sGam[r]);
             sA[r * LDK + d] *= rs;
@@ -278,25 +322,50 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
 }
 
 // ===========================================================================
-// Forward state pass: one 256-thread workgroup per (chain, 32 value columns).
-// Writes the entry state S_c [DK][DV] and Vnew_c [C][DV] of every chunk.
+// State passes: one 256-thread workgroup per (chain, SV = 16 value columns)
+// (value columns evolve independently, [KDA] section 3.4).  Consecutive
+// logical ids -- the slices of one chain -- are placed on one XCD (hardware
+// dispatches workgroup i to XCD i % 8) so they share its L2, and while a
+// chunk is computed the next chunk's operand lines are pulled into L2 (one
+// 4-byte LDS-DMA per 128-byte line into a scratch word).
 // ===========================================================================
-template <int KIND, int DK>
+constexpr int kSV = 16;              // value columns per state-pass workgroup
+constexpr int LSV = kSV + 4;
+
+template <int DK>
 struct StateSmem {
     static constexpr int LDK = DK + 4;
     static constexpr size_t MAT = (size_t)C * LDK;
-    static constexpr size_t S = 0, X1 = S + (size_t)DK * LVS, X2 = X1 + MAT, VN = X2 + MAT, DO = VN + (size_t)C * LVS,
-                            PHI = DO + (size_t)C * LVS, FLOATS = PHI + DK;
+    static constexpr size_t S = 0, X1 = S + (size_t)DK * LSV, X2 = X1 + MAT, VN = X2 + MAT, DO = VN + (size_t)C * LSV,
+                            PHI = DO + (size_t)C * LSV, SINK = PHI + DK, FLOATS = SINK + 64;
 };
 
+__device__ __forceinline__ int xcd_logical(int bid, int G) {
+    return (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+}
+
+// Pull the 128-byte lines of [rows][cols] fp32 blocks (row stride gs) into
+// L2: one 4-byte LDS-DMA per line, spread over the workgroup's threads.
+__device__ __forceinline__ void l2_touch(const float* __restrict__ src, size_t gs, int rows, int cols, int tid,
+                                         int nthr, float* sink) {
+    const int lpr = (cols * 4 + 127) / 128;    // lines per row (rows start 16-byte aligned)
+    for (int idx = tid; idx < rows * lpr; idx += nthr) {
+        const int r = idx / lpr, l = idx % lpr;
+        const auto gp = (const __attribute__((address_space(1))) void*)(src + r * gs + 32 * l);
+        __builtin_amdgcn_global_load_lds(gp, (__attribute__((address_space(3))) void*)sink, 4, 0, 0);
+    }
+}
+
+// Forward state pass: writes the entry state S_c [DK][DV] and Vnew_c [C][DV]
+// of every chunk.
 template <int KIND, int DK>
 __global__ __launch_bounds__(256) void bwd_state_fwd_kernel(const float* __restrict__ prep, const float* __restrict__ h0,
                                                             float* __restrict__ hs, float* __restrict__ vn, int H,
                                                             int NT)
 {
     using P = Prep<DK>;
-    using SM = StateSmem<KIND, DK>;
-    constexpr int DV = DK, LDK = SM::LDK, NVS = DV / kVS;
+    using SM = StateSmem<DK>;
+    constexpr int DV = DK, LDK = SM::LDK, NVS = DV / kSV;
     constexpr bool DELTA = KIND != KIND_LA;
     __shared__ __attribute__((aligned(16))) float smem[SM::FLOATS];
     float* sS = smem + SM::S;
@@ -304,56 +373,61 @@ __global__ __launch_bounds__(256) void bwd_state_fwd_kernel(const float* __restr
     float* sKb = smem + SM::X2;
     float* sVn = smem + SM::VN;
     float* sPhi = smem + SM::PHI;
+    float* sink = smem + SM::SINK;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int chain = blockIdx.x / NVS, dv0 = (blockIdx.x % NVS) * kVS;
-    for (int idx = tid; idx < DK * kVS; idx += 256) {
-        const int r = idx / kVS, cc = idx % kVS;
-        sS[r * LVS + cc] = h0 ? h0[((size_t)chain * DK + r) * DV + dv0 + cc] : 0.f;
+    const int logical = xcd_logical(blockIdx.x, gridDim.x);
+    const int chain = logical / NVS, dv0 = (logical % NVS) * kSV;
+    #pragma unroll 8
+    for (int it_ = 0; it_ < (DK * kSV) / 256; ++it_) {
+        const int idx = tid + it_ * 256;
+        const int r = idx / kSV, cc = idx % kSV;
+        sS[r * LSV + cc] = h0 ? h0[((size_t)chain * DK + r) * DV + dv0 + cc] : 0.f;
     }
     __syncthreads();
     for (int c = 0; c < NT; ++c) {
         const size_t ci = (size_t)chain * NT + c;
         const float* pc = prep + ci * P::FLOATS;
-        unstage(hs + ci * DK * DV + dv0, DV, sS, LVS, DK, kVS, tid, 256);
-        if constexpr (DELTA) stage(sW, LDK, pc + P::W, DK, C, DK, tid, 256);
-        stage(sKb, LDK, pc + P::KB, DK, C, DK, tid, 256);
-        stage(sVn, LVS, pc + P::U + dv0, DV, C, kVS, tid, 256);
+        unstage<DK, kSV, 256>(hs + ci * DK * DV + dv0, DV, sS, LSV, tid);
+        if constexpr (DELTA) stage<C, DK, 256>(sW, LDK, pc + P::W, DK, tid);
+        stage<C, DK, 256>(sKb, LDK, pc + P::KB, DK, tid);
+        stage<C, kSV, 256>(sVn, LSV, pc + P::U + dv0, DV, tid);
         if (tid < DK) sPhi[tid] = pc[P::PHI + tid];
         __syncthreads();
-        // Vnew = U - W S: 4 x 2 tiles, two per wave
+        if (c + 1 < NT) {
+            const float* pn = pc + P::FLOATS;
+            if constexpr (DELTA) l2_touch(pn + P::W, DK, C, DK, tid, 256, sink);
+            l2_touch(pn + P::KB, DK, C, DK, tid, 256, sink);
+            l2_touch(pn + P::U + dv0, DV, C, kSV, tid, 256, sink);
+        }
+        // Vnew = U - W S: 4 tiles, one per wave
         if constexpr (DELTA) {
-            for (int t = wave; t < 8; t += 4) {
-                const int ti = t >> 1, tj = t & 1;
-                const f32x4 acc = mmk<DK>(zero4(), sW + ti * 16 * LDK, LDK, 1, sS + tj * 16, LVS, 1, lane);
+            const int ti = wave;
+            const f32x4 acc = mmk<DK>(zero4(), sW + ti * 16 * LDK, LDK, 1, sS, LSV, 1, lane);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sVn[(ti * 16 + arow(lane, i)) * LVS + tj * 16 + (lane & 15)] -= acc[i];
-            }
+            for (int i = 0; i < 4; ++i) sVn[(ti * 16 + arow(lane, i)) * LSV + (lane & 15)] -= acc[i];
             __syncthreads();
         }
-        unstage(vn + ci * C * DV + dv0, DV, sVn, LVS, C, kVS, tid, 256);
+        unstage<C, kSV, 256>(vn + ci * C * DV + dv0, DV, sVn, LSV, tid);
         // S' = diag(phi) S + Kbar^T Vnew, in place (each element has one owner)
-        for (int t = wave; t < 2 * (DK / 16); t += 4) {
-            const int ti = t >> 1, tj = t & 1;
+        for (int ti = wave; ti < DK / 16; ti += 4) {
             f32x4 acc;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = ti * 16 + arow(lane, i);
-                acc[i] = sPhi[r] * sS[r * LVS + tj * 16 + (lane & 15)];
+                acc[i] = sPhi[r] * sS[r * LSV + (lane & 15)];
             }
-            acc = mmk<C>(acc, sKb + ti * 16, 1, LDK, sVn + tj * 16, LVS, 1, lane);
+            acc = mmk<C>(acc, sKb + ti * 16, 1, LDK, sVn, LSV, 1, lane);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sS[(ti * 16 + arow(lane, i)) * LVS + tj * 16 + (lane & 15)] = acc[i];
+            for (int i = 0; i < 4; ++i) sS[(ti * 16 + arow(lane, i)) * LSV + (lane & 15)] = acc[i];
         }
         __syncthreads();
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// ===========================================================================
-// Reverse state pass: one 256-thread workgroup per (chain, 32 value columns),
-// chunks in reverse.  Writes dS'_c (the exit-state adjoint of chunk c) and
-// dVnew_c, and dh0.
-// ===========================================================================
+// Reverse state pass, chunks in reverse: writes dS'_c (the exit-state adjoint
+// of chunk c) and dVnew_c, and dh0.
 template <int KIND, typename T, int DK>
 __global__ __launch_bounds__(256) void bwd_state_rev_kernel(const float* __restrict__ prep,
                                                             const T* __restrict__ dout,
@@ -362,75 +436,87 @@ __global__ __launch_bounds__(256) void bwd_state_rev_kernel(const float* __restr
                                                             int Tlen, int H, int NT)
 {
     using P = Prep<DK>;
-    using SM = StateSmem<KIND, DK>;
-    constexpr int DV = DK, LDK = SM::LDK, NVS = DV / kVS;
+    using SM = StateSmem<DK>;
+    constexpr int DV = DK, LDK = SM::LDK, NVS = DV / kSV;
     constexpr bool DELTA = KIND != KIND_LA;
-    __shared__ __attribute__((aligned(16))) float smem[SM::FLOATS + (size_t)C * LDC];
+    __shared__ __attribute__((aligned(16))) float smem[SM::FLOATS + (size_t)C * LDC + (size_t)C * LDK];
     float* sD = smem + SM::S;         // dS'
-    float* sX = smem + SM::X1;        // Kbar, then W
+    float* sKb = smem + SM::X1;
     float* sQt = smem + SM::X2;
     float* sDV = smem + SM::VN;       // dVnew
     float* sDO = smem + SM::DO;
     float* sPhi = smem + SM::PHI;
-    float* sAqk = smem + SM::FLOATS;  // [C][LDC] after the shared layout
+    float* sink = smem + SM::SINK;
+    float* sAqk = smem + SM::FLOATS;                       // [C][LDC]
+    float* sW = smem + SM::FLOATS + (size_t)C * LDC;       // [C][LDK]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int chain = blockIdx.x / NVS, dv0 = (blockIdx.x % NVS) * kVS;
+    const int logical = xcd_logical(blockIdx.x, gridDim.x);
+    const int chain = logical / NVS, dv0 = (logical % NVS) * kSV;
     const int b = chain / H, h = chain % H;
-    for (int idx = tid; idx < DK * kVS; idx += 256) {
-        const int r = idx / kVS, cc = idx % kVS;
-        sD[r * LVS + cc] = dhT ? dhT[((size_t)chain * DK + r) * DV + dv0 + cc] : 0.f;
+    #pragma unroll 8
+    for (int it_ = 0; it_ < (DK * kSV) / 256; ++it_) {
+        const int idx = tid + it_ * 256;
+        const int r = idx / kSV, cc = idx % kSV;
+        sD[r * LSV + cc] = dhT ? dhT[((size_t)chain * DK + r) * DV + dv0 + cc] : 0.f;
     }
     __syncthreads();
     for (int c = NT - 1; c >= 0; --c) {
         const size_t ci = (size_t)chain * NT + c;
         const float* pc = prep + ci * P::FLOATS;
-        unstage(dhs + ci * DK * DV + dv0, DV, sD, LVS, DK, kVS, tid, 256);
-        stage(sAqk, LDC, pc + P::AQK, C, C, C, tid, 256);
-        stage(sX, LDK, pc + P::KB, DK, C, DK, tid, 256);
-        stage(sQt, LDK, pc + P::QT, DK, C, DK, tid, 256);
+        unstage<DK, kSV, 256>(dhs + ci * DK * DV + dv0, DV, sD, LSV, tid);
+        stage<C, C, 256>(sAqk, LDC, pc + P::AQK, C, tid);
+        stage<C, DK, 256>(sKb, LDK, pc + P::KB, DK, tid);
+        stage<C, DK, 256>(sQt, LDK, pc + P::QT, DK, tid);
+        if constexpr (DELTA) stage<C, DK, 256>(sW, LDK, pc + P::W, DK, tid);
         if (tid < DK) sPhi[tid] = pc[P::PHI + tid];
-        for (int idx = tid; idx < C * kVS; idx += 256) {
-            const int r = idx / kVS, cc = idx % kVS;
+        #pragma unroll 8
+        for (int it_ = 0; it_ < (C * kSV) / 256; ++it_) {
+            const int idx = tid + it_ * 256;
+            const int r = idx / kSV, cc = idx % kSV;
             const int tok = c * C + r;
-            sDO[r * LVS + cc] = tok < Tlen ? to_f(dout[(((size_t)b * Tlen + tok) * H + h) * DV + dv0 + cc]) : 0.f;
+            const float x = to_f(dout[(((size_t)b * Tlen + min(tok, Tlen - 1)) * H + h) * DV + dv0 + cc]);
+            sDO[r * LSV + cc] = tok < Tlen ? x : 0.f;
         }
         __syncthreads();
-        // dVnew = Aqk^T dO + Kbar dS'
-        for (int t = wave; t < 8; t += 4) {
-            const int ti = t >> 1, tj = t & 1;
-            f32x4 acc = mmk<C>(zero4(), sAqk + ti * 16, 1, LDC, sDO + tj * 16, LVS, 1, lane);
-            acc = mmk<DK>(acc, sX + ti * 16 * LDK, LDK, 1, sD + tj * 16, LVS, 1, lane);
+        if (c > 0) {
+            const float* pn = pc - P::FLOATS;
+            l2_touch(pn + P::AQK, C, C, C, tid, 256, sink);
+            l2_touch(pn + P::KB, DK, C, DK, tid, 256, sink);
+            l2_touch(pn + P::QT, DK, C, DK, tid, 256, sink);
+            if constexpr (DELTA) l2_touch(pn + P::W, DK, C, DK, tid, 256, sink);
+        }
+        // dVnew = Aqk^T dO + Kbar dS': 4 tiles, one per wave
+        {
+            const int ti = wave;
+            f32x4 acc = mmk<C>(zero4(), sAqk + ti * 16, 1, LDC, sDO, LSV, 1, lane);
+            acc = mmk<DK>(acc, sKb + ti * 16 * LDK, LDK, 1, sD, LSV, 1, lane);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sDV[(ti * 16 + arow(lane, i)) * LVS + tj * 16 + (lane & 15)] = acc[i];
+            for (int i = 0; i < 4; ++i) sDV[(ti * 16 + arow(lane, i)) * LSV + (lane & 15)] = acc[i];
         }
         __syncthreads();
-        unstage(dvn + ci * C * DV + dv0, DV, sDV, LVS, C, kVS, tid, 256);
-        if constexpr (DELTA) {
-            stage(sX, LDK, pc + P::W, DK, C, DK, tid, 256);
-            __syncthreads();
-        }
+        unstage<C, kSV, 256>(dvn + ci * C * DV + dv0, DV, sDV, LSV, tid);
         // dS = Q~^T dO + diag(phi) dS' - W^T dVnew, in place
-        for (int t = wave; t < 2 * (DK / 16); t += 4) {
-            const int ti = t >> 1, tj = t & 1;
+        for (int ti = wave; ti < DK / 16; ti += 4) {
             f32x4 acc;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = ti * 16 + arow(lane, i);
-                acc[i] = sPhi[r] * sD[r * LVS + tj * 16 + (lane & 15)];
+                acc[i] = sPhi[r] * sD[r * LSV + (lane & 15)];
             }
-            acc = mmk<C>(acc, sQt + ti * 16, 1, LDK, sDO + tj * 16, LVS, 1, lane);
+            acc = mmk<C>(acc, sQt + ti * 16, 1, LDK, sDO, LSV, 1, lane);
             if constexpr (DELTA) {
-                const f32x4 wv = mmk<C>(zero4(), sX + ti * 16, 1, LDK, sDV + tj * 16, LVS, 1, lane);
+                const f32x4 wv = mmk<C>(zero4(), sW + ti * 16, 1, LDK, sDV, LSV, 1, lane);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[i] -= wv[i];
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sD[(ti * 16 + arow(lane, i)) * LVS + tj * 16 + (lane & 15)] = acc[i];
+            for (int i = 0; i < 4; ++i) sD[(ti * 16 + arow(lane, i)) * LSV + (lane & 15)] = acc[i];
         }
         __syncthreads();
     }
-    if (dh0) unstage(dh0 + (size_t)chain * DK * DV + dv0, DV, sD, LVS, DK, kVS, tid, 256);
+    if (dh0) unstage<DK, kSV, 256>(dh0 + (size_t)chain * DK * DV + dv0, DV, sD, LSV, tid);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // ===========================================================================
@@ -452,7 +538,7 @@ struct GradSmem {
     static constexpr size_t E = TI;                  // phase 3: E over the K- slot
     static constexpr size_t BIG = END1 > END2 ? END1 : END2;
     static constexpr size_t DB = BIG, SE = DB + C, GAM = SE + C, PHI = GAM + C, FCOL = PHI + DK, DPHI = FCOL + DK,
-                            ROW = DPHI + DK, FLOATS = ROW + C;
+                            ROW = DPHI + DK, BT = ROW + C, FLOATS = BT + C;
     static_assert(KM + MAT <= DL, "K- slot overlaps dL");
     static_assert(NW + MAT <= DL, "nW slot overlaps dL");
 };
@@ -480,6 +566,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     float* sF = smem + SM::FCOL;
     float* sDphi = smem + SM::DPHI;
     float* sRow = smem + SM::ROW;
+    float* sBt = smem + SM::BT;      // beta, zero past the end and for decay_la
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const unsigned it = blockIdx.x;
@@ -499,17 +586,23 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     // gamma (log2) and e = 2^gamma at element (r, d)
     auto gam_at = [&](int r, int d) { return PERCH ? pc[P::GAM + (size_t)r * DK + d] : sGam[r]; };
     auto in_at = [&](const T* __restrict__ x, int r, int d) {
-        return r < nvalid ? to_f(x[(row0 + (size_t)r * H) * DK + d]) : 0.f;
+        const float y = to_f(x[(row0 + (size_t)min(r, nvalid - 1) * H) * DK + d]);
+        return r < nvalid ? y : 0.f;
     };
 
     // ---- set-up: K+ (or k), T, beta, gamma, phi
-    for (int idx = tid; idx < C * DK; idx += 512) {
+    #pragma unroll 8
+    for (int it_ = 0; it_ < (C * DK) / 512; ++it_) {
+        const int idx = tid + it_ * 512;
         const int r = idx / DK, d = idx % DK;
-        const float kk = r < nvalid ? to_f(k[(row0 + (size_t)r * H) * DK + d]) : 0.f;
+        const float kl = to_f(k[(row0 + (size_t)min(r, nvalid - 1) * H) * DK + d]);
+        const float kk = r < nvalid ? kl : 0.f;
         sKp[r * LDK + d] = PERCH ? kk * __builtin_amdgcn_exp2f(pc[P::GAM + (size_t)r * DK + d]) : kk;
     }
-    if constexpr (DELTA) stage(sT, LDC, pc + P::TI, C, C, C, tid, 512);
+    if constexpr (DELTA) stage<C, C, 512>(sT, LDC, pc + P::TI, C, tid);
     if (tid < C) {
+        const float bb = DELTA ? beta[row0 + (size_t)min(tid, nvalid - 1) * H] : 0.f;
+        sBt[tid] = tid < nvalid ? bb : 0.f;
         sDb[tid] = 0.f;
         sE[tid] = 0.f;
         sRow[tid] = 0.f;
@@ -520,7 +613,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         sF[tid] = 0.f;
     }
     __syncthreads();
-    auto beta_at = [&](int r) { return (DELTA && r < nvalid) ? beta[row0 + (size_t)r * H] : 0.f; };
+    auto beta_at = [&](int r) { return sBt[r]; };
     // row scale of M = diag(rs) K+ (scalar gates: K+ = k 2^gamma_r)
     auto mscale = [&](int r) { return PERCH ? beta_at(r) : beta_at(r) * __builtin_amdgcn_exp2f(sGam[r]); };
 
@@ -539,16 +632,19 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     float* p1 = smem + SM::P1;
     for (int s = 0; s < NVS; ++s) {
         const int dv0 = s * kVS;
-        stage(s1, LVS, hs + ci * DK * DV + dv0, DV, DK, kVS, tid, 512);
-        stage(ds1, LVS, dhs + ci * DK * DV + dv0, DV, DK, kVS, tid, 512);
-        stage(vn1, LVS, vn + ci * C * DV + dv0, DV, C, kVS, tid, 512);
-        stage(dvn1, LVS, dvn + ci * C * DV + dv0, DV, C, kVS, tid, 512);
-        for (int idx = tid; idx < C * kVS; idx += 512) {
+        stage<DK, kVS, 512>(s1, LVS, hs + ci * DK * DV + dv0, DV, tid);
+        stage<DK, kVS, 512>(ds1, LVS, dhs + ci * DK * DV + dv0, DV, tid);
+        stage<C, kVS, 512>(vn1, LVS, vn + ci * C * DV + dv0, DV, tid);
+        stage<C, kVS, 512>(dvn1, LVS, dvn + ci * C * DV + dv0, DV, tid);
+        #pragma unroll 8
+        for (int it_ = 0; it_ < (C * kVS) / 512; ++it_) {
+            const int idx = tid + it_ * 512;
             const int r = idx / kVS, cc = idx % kVS;
             const bool ok = r < nvalid;
-            const size_t off = (row0 + (size_t)r * H) * DV + dv0 + cc;
-            do1[r * LVS + cc] = ok ? to_f(dout[off]) : 0.f;
-            v1[r * LVS + cc] = ok ? to_f(v[off]) : 0.f;
+            const size_t off = (row0 + (size_t)min(r, nvalid - 1) * H) * DV + dv0 + cc;
+            const float dd = to_f(dout[off]), vv = to_f(v[off]);
+            do1[r * LVS + cc] = ok ? dd : 0.f;
+            v1[r * LVS + cc] = ok ? vv : 0.f;
         }
         __syncthreads();
         {
@@ -581,13 +677,28 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             for (int e = 0; e < kVS; ++e) dphi += s1[tid * LVS + e] * ds1[tid * LVS + e];
         }
         __syncthreads();
+        // one product at a time (compiler barriers between them keep the
+        // LDS operand loads of different products from piling up in registers)
 #pragma unroll
         for (int m = 0; m < OWN; ++m) {
             int ti, tj;
             trc(m, ti, tj);
             dQt[m] = mmk<kVS>(dQt[m], do1 + ti * 16 * LVS, LVS, 1, s1 + tj * 16 * LVS, 1, LVS, lane);
+            asm volatile("" ::: "memory");
+        }
+#pragma unroll
+        for (int m = 0; m < OWN; ++m) {
+            int ti, tj;
+            trc(m, ti, tj);
             nW[m] = mmk<kVS>(nW[m], dvn1 + ti * 16 * LVS, LVS, 1, s1 + tj * 16 * LVS, 1, LVS, lane);
+            asm volatile("" ::: "memory");
+        }
+#pragma unroll
+        for (int m = 0; m < OWN; ++m) {
+            int ti, tj;
+            trc(m, ti, tj);
             dKb[m] = mmk<kVS>(dKb[m], vn1 + ti * 16 * LVS, LVS, 1, ds1 + tj * 16 * LVS, 1, LVS, lane);
+            asm volatile("" ::: "memory");
         }
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
@@ -625,6 +736,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
                 if ((lane & 15) == 0) atomicAdd(&sF[0], part);
             }
         }
+        asm volatile("" ::: "memory");   // one tile's global loads in flight at a time
     }
 
     if constexpr (DELTA) {
@@ -711,7 +823,9 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     float* sKm = smem + SM::KM;     // kda: K-;  scalar: raw q
     float* sQt = smem + SM::QT;     // kda: Q~
     float* sDL = smem + SM::DL;
-    for (int idx = tid; idx < C * DK; idx += 512) {
+    #pragma unroll 8
+    for (int it_ = 0; it_ < (C * DK) / 512; ++it_) {
+        const int idx = tid + it_ * 512;
         const int r = idx / DK, d = idx % DK;
         const float qq = in_at(q, r, d);
         if constexpr (PERCH) {
@@ -726,7 +840,9 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     if constexpr (!PERCH) {
         // G = dX .* Gamma in place, and the log-gate terms of the pair products:
         // E_i += sum_j dX_ij X_ij,  E_j -= sum_i dX_ij X_ij  (X = L, Aqk)
-        for (int idx = tid; idx < C * C; idx += 512) {
+        #pragma unroll 8
+        for (int it_ = 0; it_ < (C * C) / 512; ++it_) {
+            const int idx = tid + it_ * 512;
             const int r = idx / C, cc = idx % C;
             float contrib = 0.f;
             if (cc <= r) {
@@ -747,26 +863,55 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         }
     }
     __syncthreads();
+    if constexpr (PERCH) {
+        // dK+ += dL K-;  dK- = dL^T K+ + dAqk^T Q~;  dQ~ += dAqk K- (one
+        // product at a time over the owned tiles, which keeps few results live)
 #pragma unroll
-    for (int m = 0; m < OWN; ++m) {
-        int ti, tj;
-        trc(m, ti, tj);
-        const int d = ecol(m);
-        if constexpr (PERCH) {
-            // dK+ += dL K-;  dK- = dL^T K+ + dAqk^T Q~;  dQ~ += dAqk K-
+        for (int m = 0; m < OWN; ++m) {
+            int ti, tj;
+            trc(m, ti, tj);
+            const int d = ecol(m);
             const f32x4 dkp = mmk<C>(zero4(), sDL + ti * 16 * LDC, LDC, 1, sKm + tj * 16, LDK, 1, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = erow(m, i);
+                ak[m][i] += dkp[i] * __builtin_amdgcn_exp2f(pc[P::GAM + (size_t)r * DK + d]);
+                aE[m][i] += dkp[i] * sKp[r * LDK + d];
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < OWN; ++m) {
+            int ti, tj;
+            trc(m, ti, tj);
+            const int d = ecol(m);
             f32x4 dkm = mmk<C>(zero4(), sDL + ti * 16, 1, LDC, sKp + tj * 16, LDK, 1, lane);
             dkm = mmk<C>(dkm, sDAqk + ti * 16, 1, LDC, sQt + tj * 16, LDK, 1, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = erow(m, i);
+                ak[m][i] += dkm[i] * __builtin_amdgcn_exp2f(-pc[P::GAM + (size_t)r * DK + d]);
+                aE[m][i] -= dkm[i] * sKm[r * LDK + d];
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < OWN; ++m) {
+            int ti, tj;
+            trc(m, ti, tj);
+            const int d = ecol(m);
             const f32x4 dqt = mmk<C>(zero4(), sDAqk + ti * 16 * LDC, LDC, 1, sKm + tj * 16, LDK, 1, lane);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = erow(m, i);
-                const float gm = pc[P::GAM + (size_t)r * DK + d];
-                const float e = __builtin_amdgcn_exp2f(gm), ei = __builtin_amdgcn_exp2f(-gm);
-                ak[m][i] += dkp[i] * e + dkm[i] * ei;
-                aq[m][i] += dqt[i] * e;
-                aE[m][i] += dkp[i] * sKp[r * LDK + d] - dkm[i] * sKm[r * LDK + d] + dqt[i] * sQt[r * LDK + d];
+                aq[m][i] += dqt[i] * __builtin_amdgcn_exp2f(pc[P::GAM + (size_t)r * DK + d]);
+                aE[m][i] += dqt[i] * sQt[r * LDK + d];
             }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < OWN; ++m) {
+        int ti, tj;
+        trc(m, ti, tj);
+        if constexpr (PERCH) {
         } else {
             // raw k (sKp), raw q (sKm): dk += G_L k + G_L^T k + G_Q^T q;  dq += G_Q k
             f32x4 dkk = mmk<C>(zero4(), sDAqk + ti * 16, 1, LDC, sKm + tj * 16, LDK, 1, lane);

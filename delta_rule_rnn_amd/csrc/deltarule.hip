@@ -437,7 +437,7 @@ dr_status launch_backward_t(const BwdArgs& a, hipStream_t st) {
     const E* v = static_cast<const E*>(a.v);
     const E* dout = static_cast<const E*>(a.dout);
     const long long items = (long long)a.B * a.NT * a.H;
-    const long long slices = (long long)a.B * a.H * (D / kVS);
+    const long long slices = (long long)a.B * a.H * (D / kSV);
     if (items > 0x7fffffffLL || slices > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
     hipLaunchKernelGGL((bwd_prep_kernel<KIND, E, D>), dim3((unsigned)items), dim3(256), 0, st, q, k, v, a.g, a.beta,
                        prep, a.T, a.H, a.NT);
