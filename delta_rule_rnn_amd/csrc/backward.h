@@ -27,6 +27,11 @@
 // adjoint E; dg_s = sum_{r >= s} E_r + F with F the gamma_last terms (the
 // ln 2 of d2^x/dx and the log2(e) of gamma cancel).
 //
+// Barriers are LDS-only (lds_barrier: wait for this wave's LDS operations,
+// then s_barrier): threads of a workgroup exchange data through LDS only, and
+// a full __syncthreads would also wait for every outstanding global load and
+// store (prefetches and result stores included).
+//
 // All four kernels compute in fp32 on fp32 MFMA (v_mfma_f32_16x16x4_f32) with
 // operands staged in LDS in natural row-major layout; the I/O dtype only
 // changes the loads of q, k, v, dO and the stores of dq, dk, dv.
@@ -81,6 +86,33 @@ __device__ __forceinline__ f32x4 mmk(f32x4 acc, const float* A, int ar, int ak, 
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[k0 * ak], b[k0 * bk], acc, 0, 0, 0);
     return acc;
 }
+// The same product with both operands contiguous along k (A(r, k) =
+// A[r*ar + k], B(k, c) = B[c*bc + k]) on bf16 MFMA (v_mfma_f32_16x16x32_bf16):
+// lane l reads 8 consecutive fp32 values of row / column l%16 at k0 + 8*(l/16)
+// (two 16-byte LDS reads each) and rounds them to bf16; fp32 accumulation.
+// ar, bc and the pointers must keep those reads 16-byte aligned.
+template <int K>
+__device__ __forceinline__ f32x4 mmb(f32x4 acc, const float* A, int ar, const float* B, int bc, int lane) {
+    const int r = lane & 15, q = lane >> 4;
+    const float* a = A + r * ar + 8 * q;
+    const float* b = B + r * bc + 8 * q;
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 32) {
+        const float4 a0 = *reinterpret_cast<const float4*>(a + k0), a1 = *reinterpret_cast<const float4*>(a + k0 + 4);
+        const float4 b0 = *reinterpret_cast<const float4*>(b + k0), b1 = *reinterpret_cast<const float4*>(b + k0 + 4);
+        const bf16x8 fa = {(bf16)a0.x, (bf16)a0.y, (bf16)a0.z, (bf16)a0.w, (bf16)a1.x, (bf16)a1.y, (bf16)a1.z, (bf16)a1.w};
+        const bf16x8 fb = {(bf16)b0.x, (bf16)b0.y, (bf16)b0.z, (bf16)b0.w, (bf16)b1.x, (bf16)b1.y, (bf16)b1.z, (bf16)b1.w};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc, 0, 0, 0);
+    }
+    return acc;
+}
+// Product with k contiguous in both operands, on the MFMA of the I/O dtype:
+// bf16 operands for bf16 I/O (as the forward's products), fp32 otherwise.
+template <typename T, int K>
+__device__ __forceinline__ f32x4 mmc(f32x4 acc, const float* A, int ar, const float* B, int bc, int lane) {
+    if constexpr (sizeof(T) == 2) return mmb<K>(acc, A, ar, B, bc, lane);
+    else return mmk<K>(acc, A, ar, 1, B, 1, bc, lane);
+}
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 __device__ __forceinline__ int arow(int lane, int i) { return 4 * (lane >> 4) + i; }
 
@@ -107,6 +139,28 @@ __device__ __forceinline__ void stage(float* dst, int ls, const float* __restric
         }
     }
 }
+// The two halves of a staging copy, for issuing the loads of several blocks
+// before any of their LDS stores.
+template <int ROWS, int COLS, int NTHR>
+struct Staged {
+    static constexpr int PER = COLS / 4, IT = ROWS * PER / NTHR;
+    static_assert(COLS % 4 == 0 && (ROWS * PER) % NTHR == 0, "staging shape");
+    float4 v[IT];
+    __device__ __forceinline__ void load(const float* __restrict__ src, size_t gs, int tid) {
+#pragma unroll
+        for (int j = 0; j < IT; ++j) {
+            const int idx = tid + j * NTHR, r = idx / PER, c4 = (idx % PER) * 4;
+            v[j] = *reinterpret_cast<const float4*>(src + r * gs + c4);
+        }
+    }
+    __device__ __forceinline__ void store(float* dst, int ls, int tid) const {
+#pragma unroll
+        for (int j = 0; j < IT; ++j) {
+            const int idx = tid + j * NTHR, r = idx / PER, c4 = (idx % PER) * 4;
+            *reinterpret_cast<float4*>(dst + r * ls + c4) = v[j];
+        }
+    }
+};
 template <int ROWS, int COLS, int NTHR>
 __device__ __forceinline__ void unstage(float* __restrict__ dst, size_t gs, const float* src, int ls, int tid) {
     constexpr int PER = COLS / 4, N = ROWS * PER, IT = N / NTHR;
@@ -186,7 +240,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
             sGam[tid] = ok ? gg : 0.f;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- gamma and the separable operands
     if constexpr (PERCH) {
@@ -222,7 +276,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
             sGam[lane] = x;
             out[P::GAM + lane] = x;
         }
-        __syncthreads();
+        lds_barrier();
         const float gl = sGam[C - 1];
         #pragma unroll 8
         for (int it_ = 0; it_ < (C * DK) / 256; ++it_) {
@@ -236,7 +290,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
             out[P::PHI + tid] = sPhi[tid];
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- L and Aqk: 16 tiles each, 32 jobs over 4 waves
     for (int job = wave; job < 32; job += 4) {
@@ -262,7 +316,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- T = (I + diag(beta) L)^-1 by forward substitution, one column per
     // lane held in registers (fully unrolled: the rows of L are broadcast
@@ -282,7 +336,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
 #pragma unroll
             for (int i = 0; i < C; ++i) sT[i * LDC + j] = t[i];
         }
-        __syncthreads();
+        lds_barrier();
         #pragma unroll 8
         for (int it_ = 0; it_ < (C * C) / 256; ++it_) {
             const int idx = tid + it_ * 256;
@@ -306,7 +360,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
         }
     }
     if constexpr (DELTA) {
-        __syncthreads();
+        lds_barrier();
         // W = T M, U = T N: (C/16) x (DK/16) tiles each
         constexpr int NTL = 4 * (DK / 16);
         for (int job = wave; job < 2 * NTL; job += 4) {
@@ -330,14 +384,25 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
 // 4-byte LDS-DMA per 128-byte line into a scratch word).
 // ===========================================================================
 constexpr int kSV = 16;              // value columns per state-pass workgroup
-constexpr int LSV = kSV + 4;
+// LDS row strides.  The tile product reads an operand either with the lane
+// index along the row stride (A(r, k) = A[r*s + k]) or along the row (the k
+// index strided: transposed A, and B).  With 64 four-byte banks the first is
+// conflict-free for s = 4 (mod 64), the second for s = 16 (mod 64); each
+// buffer is padded for the way it is read.
+constexpr int LSV = kSV;             // [*][16] value-slice tiles, read with k strided
 
 template <int DK>
 struct StateSmem {
-    static constexpr int LDK = DK + 4;
-    static constexpr size_t MAT = (size_t)C * LDK;
-    static constexpr size_t S = 0, X1 = S + (size_t)DK * LSV, X2 = X1 + MAT, VN = X2 + MAT, DO = VN + (size_t)C * LSV,
-                            PHI = DO + (size_t)C * LSV, SINK = PHI + DK, FLOATS = SINK + 64;
+    static constexpr int LDN = DK + 4;     // [C][DK] read with the lane index along rows
+    static constexpr int LDT = DK + 16;    // [C][DK] read transposed
+    static constexpr int LCT = C + 16;     // [C][C] read transposed
+    // forward pass
+    static constexpr size_t S = 0, W = S + (size_t)DK * LSV, KBT = W + (size_t)C * LDN, VN = KBT + (size_t)C * LDT,
+                            PHI = VN + (size_t)C * LSV, SINK = PHI + DK, FWD = SINK + 64;
+    // reverse pass
+    static constexpr size_t D = 0, KBN = D + (size_t)DK * LSV, QT = KBN + (size_t)C * LDN, WT = QT + (size_t)C * LDT,
+                            AQK = WT + (size_t)C * LDT, DV = AQK + (size_t)C * LCT, DO = DV + (size_t)C * LSV,
+                            RPHI = DO + (size_t)C * LSV, RSINK = RPHI + DK, REV = RSINK + 64;
 };
 
 __device__ __forceinline__ int xcd_logical(int bid, int G) {
@@ -356,72 +421,101 @@ __device__ __forceinline__ void l2_touch(const float* __restrict__ src, size_t g
     }
 }
 
+// Both state passes run 4 compute waves and a fifth store wave.  The store
+// wave copies the tiles the compute waves publish in LDS (states, adjoints,
+// Vnew / dVnew) to HBM, so the compute waves never wait on a store (vector
+// memory counters count stores and loads in issue order).  Per chunk, three
+// barriers separate: (A) staging of the chunk's operands | the store wave
+// writing the state that enters the chunk; (B) the Vnew / dVnew products;
+// (C) the state update in place | the store wave writing Vnew / dVnew.
+constexpr int kStateThreads = 320;
+
 // Forward state pass: writes the entry state S_c [DK][DV] and Vnew_c [C][DV]
 // of every chunk.
 template <int KIND, int DK>
-__global__ __launch_bounds__(256) void bwd_state_fwd_kernel(const float* __restrict__ prep, const float* __restrict__ h0,
-                                                            float* __restrict__ hs, float* __restrict__ vn, int H,
-                                                            int NT)
+__global__ __launch_bounds__(kStateThreads) void bwd_state_fwd_kernel(const float* __restrict__ prep,
+                                                                      const float* __restrict__ h0,
+                                                                      float* __restrict__ hs, float* __restrict__ vn,
+                                                                      int H, int NT)
 {
     using P = Prep<DK>;
     using SM = StateSmem<DK>;
-    constexpr int DV = DK, LDK = SM::LDK, NVS = DV / kSV;
+    constexpr int DV = DK, LDN = SM::LDN, LDT = SM::LDT, NVS = DV / kSV;
     constexpr bool DELTA = KIND != KIND_LA;
-    __shared__ __attribute__((aligned(16))) float smem[SM::FLOATS];
+    __shared__ __attribute__((aligned(16))) float smem[SM::FWD];
     float* sS = smem + SM::S;
-    float* sW = smem + SM::X1;
-    float* sKb = smem + SM::X2;
+    float* sW = smem + SM::W;
+    float* sKb = smem + SM::KBT;
     float* sVn = smem + SM::VN;
     float* sPhi = smem + SM::PHI;
     float* sink = smem + SM::SINK;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool storer = tid >= 256;
     const int logical = xcd_logical(blockIdx.x, gridDim.x);
     const int chain = logical / NVS, dv0 = (logical % NVS) * kSV;
-    #pragma unroll 8
-    for (int it_ = 0; it_ < (DK * kSV) / 256; ++it_) {
-        const int idx = tid + it_ * 256;
-        const int r = idx / kSV, cc = idx % kSV;
-        sS[r * LSV + cc] = h0 ? h0[((size_t)chain * DK + r) * DV + dv0 + cc] : 0.f;
+    if (!storer) {
+#pragma unroll
+        for (int it_ = 0; it_ < (DK * kSV) / 256; ++it_) {
+            const int idx = tid + it_ * 256, r = idx / kSV, cc = idx % kSV;
+            sS[r * LSV + cc] = h0 ? h0[((size_t)chain * DK + r) * DV + dv0 + cc] : 0.f;
+        }
     }
-    __syncthreads();
+    lds_barrier();
     for (int c = 0; c < NT; ++c) {
         const size_t ci = (size_t)chain * NT + c;
         const float* pc = prep + ci * P::FLOATS;
-        unstage<DK, kSV, 256>(hs + ci * DK * DV + dv0, DV, sS, LSV, tid);
-        if constexpr (DELTA) stage<C, DK, 256>(sW, LDK, pc + P::W, DK, tid);
-        stage<C, DK, 256>(sKb, LDK, pc + P::KB, DK, tid);
-        stage<C, kSV, 256>(sVn, LSV, pc + P::U + dv0, DV, tid);
-        if (tid < DK) sPhi[tid] = pc[P::PHI + tid];
-        __syncthreads();
-        if (c + 1 < NT) {
-            const float* pn = pc + P::FLOATS;
-            if constexpr (DELTA) l2_touch(pn + P::W, DK, C, DK, tid, 256, sink);
-            l2_touch(pn + P::KB, DK, C, DK, tid, 256, sink);
-            l2_touch(pn + P::U + dv0, DV, C, kSV, tid, 256, sink);
+        // (A)
+        if (!storer) {
+            // every load of the chunk in flight before the first LDS store
+            Staged<C, DK, 256> gw, gk;
+            Staged<C, kSV, 256> gu;
+            if constexpr (DELTA) gw.load(pc + P::W, DK, tid);
+            gk.load(pc + P::KB, DK, tid);
+            gu.load(pc + P::U + dv0, DV, tid);
+            const float ph = tid < DK ? pc[P::PHI + tid] : 0.f;
+            if constexpr (DELTA) gw.store(sW, LDN, tid);
+            gk.store(sKb, LDT, tid);
+            gu.store(sVn, LSV, tid);
+            if (tid < DK) sPhi[tid] = ph;
+        } else {
+            unstage<DK, kSV, 64>(hs + ci * DK * DV + dv0, DV, sS, LSV, tid - 256);
         }
-        // Vnew = U - W S: 4 tiles, one per wave
-        if constexpr (DELTA) {
-            const int ti = wave;
-            const f32x4 acc = mmk<DK>(zero4(), sW + ti * 16 * LDK, LDK, 1, sS, LSV, 1, lane);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sVn[(ti * 16 + arow(lane, i)) * LSV + (lane & 15)] -= acc[i];
-            __syncthreads();
-        }
-        unstage<C, kSV, 256>(vn + ci * C * DV + dv0, DV, sVn, LSV, tid);
-        // S' = diag(phi) S + Kbar^T Vnew, in place (each element has one owner)
-        for (int ti = wave; ti < DK / 16; ti += 4) {
-            f32x4 acc;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = ti * 16 + arow(lane, i);
-                acc[i] = sPhi[r] * sS[r * LSV + (lane & 15)];
+        lds_barrier();
+        // (B) Vnew = U - W S: 4 tiles, one per compute wave
+        if (!storer) {
+            if (c + 1 < NT) {
+                const float* pn = pc + P::FLOATS;
+                if constexpr (DELTA) l2_touch(pn + P::W, DK, C, DK, tid, 256, sink);
+                l2_touch(pn + P::KB, DK, C, DK, tid, 256, sink);
+                l2_touch(pn + P::U + dv0, DV, C, kSV, tid, 256, sink);
             }
-            acc = mmk<C>(acc, sKb + ti * 16, 1, LDK, sVn, LSV, 1, lane);
+            if constexpr (DELTA) {
+                const int ti = wave;
+                const f32x4 acc = mmk<DK>(zero4(), sW + ti * 16 * LDN, LDN, 1, sS, LSV, 1, lane);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sS[(ti * 16 + arow(lane, i)) * LSV + (lane & 15)] = acc[i];
+                for (int i = 0; i < 4; ++i) sVn[(ti * 16 + arow(lane, i)) * LSV + (lane & 15)] -= acc[i];
+            }
         }
-        __syncthreads();
+        lds_barrier();
+        // (C) S' = diag(phi) S + Kbar^T Vnew, in place (each element has one
+        // owner); the store wave writes Vnew
+        if (!storer) {
+            for (int ti = wave; ti < DK / 16; ti += 4) {
+                f32x4 acc;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = ti * 16 + arow(lane, i);
+                    acc[i] = sPhi[r] * sS[r * LSV + (lane & 15)];
+                }
+                acc = mmk<C>(acc, sKb + ti * 16, 1, LDT, sVn, LSV, 1, lane);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sS[(ti * 16 + arow(lane, i)) * LSV + (lane & 15)] = acc[i];
+            }
+        } else {
+            unstage<C, kSV, 64>(vn + ci * C * DV + dv0, DV, sVn, LSV, tid - 256);
+        }
+        lds_barrier();
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -429,93 +523,118 @@ __global__ __launch_bounds__(256) void bwd_state_fwd_kernel(const float* __restr
 // Reverse state pass, chunks in reverse: writes dS'_c (the exit-state adjoint
 // of chunk c) and dVnew_c, and dh0.
 template <int KIND, typename T, int DK>
-__global__ __launch_bounds__(256) void bwd_state_rev_kernel(const float* __restrict__ prep,
-                                                            const T* __restrict__ dout,
-                                                            const float* __restrict__ dhT, float* __restrict__ dhs,
-                                                            float* __restrict__ dvn, float* __restrict__ dh0,
-                                                            int Tlen, int H, int NT)
+__global__ __launch_bounds__(kStateThreads) void bwd_state_rev_kernel(const float* __restrict__ prep,
+                                                                      const T* __restrict__ dout,
+                                                                      const float* __restrict__ dhT,
+                                                                      float* __restrict__ dhs,
+                                                                      float* __restrict__ dvn,
+                                                                      float* __restrict__ dh0, int Tlen, int H,
+                                                                      int NT)
 {
     using P = Prep<DK>;
     using SM = StateSmem<DK>;
-    constexpr int DV = DK, LDK = SM::LDK, NVS = DV / kSV;
+    constexpr int DV = DK, LDN = SM::LDN, LDT = SM::LDT, LCT = SM::LCT, NVS = DV / kSV;
     constexpr bool DELTA = KIND != KIND_LA;
-    __shared__ __attribute__((aligned(16))) float smem[SM::FLOATS + (size_t)C * LDC + (size_t)C * LDK];
-    float* sD = smem + SM::S;         // dS'
-    float* sKb = smem + SM::X1;
-    float* sQt = smem + SM::X2;
-    float* sDV = smem + SM::VN;       // dVnew
+    __shared__ __attribute__((aligned(16))) float smem[SM::REV];
+    float* sD = smem + SM::D;         // dS'
+    float* sKb = smem + SM::KBN;
+    float* sQt = smem + SM::QT;
+    float* sW = smem + SM::WT;
+    float* sAqk = smem + SM::AQK;
+    float* sDV = smem + SM::DV;       // dVnew
     float* sDO = smem + SM::DO;
-    float* sPhi = smem + SM::PHI;
-    float* sink = smem + SM::SINK;
-    float* sAqk = smem + SM::FLOATS;                       // [C][LDC]
-    float* sW = smem + SM::FLOATS + (size_t)C * LDC;       // [C][LDK]
+    float* sPhi = smem + SM::RPHI;
+    float* sink = smem + SM::RSINK;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool storer = tid >= 256;
     const int logical = xcd_logical(blockIdx.x, gridDim.x);
     const int chain = logical / NVS, dv0 = (logical % NVS) * kSV;
     const int b = chain / H, h = chain % H;
-    #pragma unroll 8
-    for (int it_ = 0; it_ < (DK * kSV) / 256; ++it_) {
-        const int idx = tid + it_ * 256;
-        const int r = idx / kSV, cc = idx % kSV;
-        sD[r * LSV + cc] = dhT ? dhT[((size_t)chain * DK + r) * DV + dv0 + cc] : 0.f;
+    if (!storer) {
+#pragma unroll
+        for (int it_ = 0; it_ < (DK * kSV) / 256; ++it_) {
+            const int idx = tid + it_ * 256, r = idx / kSV, cc = idx % kSV;
+            sD[r * LSV + cc] = dhT ? dhT[((size_t)chain * DK + r) * DV + dv0 + cc] : 0.f;
+        }
     }
-    __syncthreads();
+    lds_barrier();
     for (int c = NT - 1; c >= 0; --c) {
         const size_t ci = (size_t)chain * NT + c;
         const float* pc = prep + ci * P::FLOATS;
-        unstage<DK, kSV, 256>(dhs + ci * DK * DV + dv0, DV, sD, LSV, tid);
-        stage<C, C, 256>(sAqk, LDC, pc + P::AQK, C, tid);
-        stage<C, DK, 256>(sKb, LDK, pc + P::KB, DK, tid);
-        stage<C, DK, 256>(sQt, LDK, pc + P::QT, DK, tid);
-        if constexpr (DELTA) stage<C, DK, 256>(sW, LDK, pc + P::W, DK, tid);
-        if (tid < DK) sPhi[tid] = pc[P::PHI + tid];
-        #pragma unroll 8
-        for (int it_ = 0; it_ < (C * kSV) / 256; ++it_) {
-            const int idx = tid + it_ * 256;
-            const int r = idx / kSV, cc = idx % kSV;
-            const int tok = c * C + r;
-            const float x = to_f(dout[(((size_t)b * Tlen + min(tok, Tlen - 1)) * H + h) * DV + dv0 + cc]);
-            sDO[r * LSV + cc] = tok < Tlen ? x : 0.f;
+        // (A)
+        if (!storer) {
+            // every load of the chunk in flight before the first LDS store
+            Staged<C, C, 256> ga;
+            Staged<C, DK, 256> gk, gq, gw;
+            constexpr int NDO = (C * kSV) / 256;
+            float xo[NDO];
+            ga.load(pc + P::AQK, C, tid);
+            gk.load(pc + P::KB, DK, tid);
+            gq.load(pc + P::QT, DK, tid);
+            if constexpr (DELTA) gw.load(pc + P::W, DK, tid);
+            const float ph = tid < DK ? pc[P::PHI + tid] : 0.f;
+#pragma unroll
+            for (int it_ = 0; it_ < NDO; ++it_) {
+                const int idx = tid + it_ * 256, r = idx / kSV, cc = idx % kSV;
+                const int tok = c * C + r;
+                xo[it_] = to_f(dout[(((size_t)b * Tlen + min(tok, Tlen - 1)) * H + h) * DV + dv0 + cc]);
+            }
+            ga.store(sAqk, LCT, tid);
+            gk.store(sKb, LDN, tid);
+            gq.store(sQt, LDT, tid);
+            if constexpr (DELTA) gw.store(sW, LDT, tid);
+            if (tid < DK) sPhi[tid] = ph;
+#pragma unroll
+            for (int it_ = 0; it_ < NDO; ++it_) {
+                const int idx = tid + it_ * 256, r = idx / kSV, cc = idx % kSV;
+                sDO[r * LSV + cc] = c * C + r < Tlen ? xo[it_] : 0.f;
+            }
+        } else {
+            unstage<DK, kSV, 64>(dhs + ci * DK * DV + dv0, DV, sD, LSV, tid - 256);
         }
-        __syncthreads();
-        if (c > 0) {
-            const float* pn = pc - P::FLOATS;
-            l2_touch(pn + P::AQK, C, C, C, tid, 256, sink);
-            l2_touch(pn + P::KB, DK, C, DK, tid, 256, sink);
-            l2_touch(pn + P::QT, DK, C, DK, tid, 256, sink);
-            if constexpr (DELTA) l2_touch(pn + P::W, DK, C, DK, tid, 256, sink);
-        }
-        // dVnew = Aqk^T dO + Kbar dS': 4 tiles, one per wave
-        {
+        lds_barrier();
+        // (B) dVnew = Aqk^T dO + Kbar dS': 4 tiles, one per compute wave
+        if (!storer) {
+            if (c > 0) {
+                const float* pn = pc - P::FLOATS;
+                l2_touch(pn + P::AQK, C, C, C, tid, 256, sink);
+                l2_touch(pn + P::KB, DK, C, DK, tid, 256, sink);
+                l2_touch(pn + P::QT, DK, C, DK, tid, 256, sink);
+                if constexpr (DELTA) l2_touch(pn + P::W, DK, C, DK, tid, 256, sink);
+            }
             const int ti = wave;
-            f32x4 acc = mmk<C>(zero4(), sAqk + ti * 16, 1, LDC, sDO, LSV, 1, lane);
-            acc = mmk<DK>(acc, sKb + ti * 16 * LDK, LDK, 1, sD, LSV, 1, lane);
+            f32x4 acc = mmk<C>(zero4(), sAqk + ti * 16, 1, LCT, sDO, LSV, 1, lane);
+            acc = mmk<DK>(acc, sKb + ti * 16 * LDN, LDN, 1, sD, LSV, 1, lane);
 #pragma unroll
             for (int i = 0; i < 4; ++i) sDV[(ti * 16 + arow(lane, i)) * LSV + (lane & 15)] = acc[i];
         }
-        __syncthreads();
-        unstage<C, kSV, 256>(dvn + ci * C * DV + dv0, DV, sDV, LSV, tid);
-        // dS = Q~^T dO + diag(phi) dS' - W^T dVnew, in place
-        for (int ti = wave; ti < DK / 16; ti += 4) {
-            f32x4 acc;
+        lds_barrier();
+        // (C) dS = Q~^T dO + diag(phi) dS' - W^T dVnew, in place; the store
+        // wave writes dVnew
+        if (!storer) {
+            for (int ti = wave; ti < DK / 16; ti += 4) {
+                f32x4 acc;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = ti * 16 + arow(lane, i);
-                acc[i] = sPhi[r] * sD[r * LSV + (lane & 15)];
+                for (int i = 0; i < 4; ++i) {
+                    const int r = ti * 16 + arow(lane, i);
+                    acc[i] = sPhi[r] * sD[r * LSV + (lane & 15)];
+                }
+                acc = mmk<C>(acc, sQt + ti * 16, 1, LDT, sDO, LSV, 1, lane);
+                if constexpr (DELTA) {
+                    const f32x4 wv = mmk<C>(zero4(), sW + ti * 16, 1, LDT, sDV, LSV, 1, lane);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[i] -= wv[i];
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sD[(ti * 16 + arow(lane, i)) * LSV + (lane & 15)] = acc[i];
             }
-            acc = mmk<C>(acc, sQt + ti * 16, 1, LDK, sDO, LSV, 1, lane);
-            if constexpr (DELTA) {
-                const f32x4 wv = mmk<C>(zero4(), sW + ti * 16, 1, LDK, sDV, LSV, 1, lane);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] -= wv[i];
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sD[(ti * 16 + arow(lane, i)) * LSV + (lane & 15)] = acc[i];
+        } else {
+            unstage<C, kSV, 64>(dvn + ci * C * DV + dv0, DV, sDV, LSV, tid - 256);
         }
-        __syncthreads();
+        lds_barrier();
     }
-    if (dh0) unstage<DK, kSV, 256>(dh0 + (size_t)chain * DK * DV + dv0, DV, sD, LSV, tid);
+    if (dh0 && !storer) unstage<DK, kSV, 256>(dh0 + (size_t)chain * DK * DV + dv0, DV, sD, LSV, tid);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
@@ -612,7 +731,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         sPhi[tid] = pc[P::PHI + tid];
         sF[tid] = 0.f;
     }
-    __syncthreads();
+    lds_barrier();
     auto beta_at = [&](int r) { return sBt[r]; };
     // row scale of M = diag(rs) K+ (scalar gates: K+ = k 2^gamma_r)
     auto mscale = [&](int r) { return PERCH ? beta_at(r) : beta_at(r) * __builtin_amdgcn_exp2f(sGam[r]); };
@@ -632,21 +751,35 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     float* p1 = smem + SM::P1;
     for (int s = 0; s < NVS; ++s) {
         const int dv0 = s * kVS;
-        stage<DK, kVS, 512>(s1, LVS, hs + ci * DK * DV + dv0, DV, tid);
-        stage<DK, kVS, 512>(ds1, LVS, dhs + ci * DK * DV + dv0, DV, tid);
-        stage<C, kVS, 512>(vn1, LVS, vn + ci * C * DV + dv0, DV, tid);
-        stage<C, kVS, 512>(dvn1, LVS, dvn + ci * C * DV + dv0, DV, tid);
-        #pragma unroll 8
-        for (int it_ = 0; it_ < (C * kVS) / 512; ++it_) {
-            const int idx = tid + it_ * 512;
-            const int r = idx / kVS, cc = idx % kVS;
-            const bool ok = r < nvalid;
-            const size_t off = (row0 + (size_t)min(r, nvalid - 1) * H) * DV + dv0 + cc;
-            const float dd = to_f(dout[off]), vv = to_f(v[off]);
-            do1[r * LVS + cc] = ok ? dd : 0.f;
-            v1[r * LVS + cc] = ok ? vv : 0.f;
+        {
+            // every load of the slice in flight before the first LDS store
+            Staged<DK, kVS, 512> g1, g2;
+            Staged<C, kVS, 512> g3, g4;
+            constexpr int NE = (C * kVS) / 512;
+            float xd[NE], xv[NE];
+            g1.load(hs + ci * DK * DV + dv0, DV, tid);
+            g2.load(dhs + ci * DK * DV + dv0, DV, tid);
+            g3.load(vn + ci * C * DV + dv0, DV, tid);
+            g4.load(dvn + ci * C * DV + dv0, DV, tid);
+#pragma unroll
+            for (int it_ = 0; it_ < NE; ++it_) {
+                const int idx = tid + it_ * 512, r = idx / kVS, cc = idx % kVS;
+                const size_t off = (row0 + (size_t)min(r, nvalid - 1) * H) * DV + dv0 + cc;
+                xd[it_] = to_f(dout[off]);
+                xv[it_] = to_f(v[off]);
+            }
+            g1.store(s1, LVS, tid);
+            g2.store(ds1, LVS, tid);
+            g3.store(vn1, LVS, tid);
+            g4.store(dvn1, LVS, tid);
+#pragma unroll
+            for (int it_ = 0; it_ < NE; ++it_) {
+                const int idx = tid + it_ * 512, r = idx / kVS, cc = idx % kVS;
+                do1[r * LVS + cc] = r < nvalid ? xd[it_] : 0.f;
+                v1[r * LVS + cc] = r < nvalid ? xv[it_] : 0.f;
+            }
         }
-        __syncthreads();
+        lds_barrier();
         {
             const int ti = wave >> 1, tj = wave & 1;    // one [C][32] tile per wave
             if constexpr (DELTA) {
@@ -676,53 +809,70 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
 #pragma unroll 8
             for (int e = 0; e < kVS; ++e) dphi += s1[tid * LVS + e] * ds1[tid * LVS + e];
         }
-        __syncthreads();
+        lds_barrier();
         // one product at a time (compiler barriers between them keep the
         // LDS operand loads of different products from piling up in registers)
 #pragma unroll
         for (int m = 0; m < OWN; ++m) {
             int ti, tj;
             trc(m, ti, tj);
-            dQt[m] = mmk<kVS>(dQt[m], do1 + ti * 16 * LVS, LVS, 1, s1 + tj * 16 * LVS, 1, LVS, lane);
+            dQt[m] = mmc<T, kVS>(dQt[m], do1 + ti * 16 * LVS, LVS, s1 + tj * 16 * LVS, LVS, lane);
             asm volatile("" ::: "memory");
         }
 #pragma unroll
         for (int m = 0; m < OWN; ++m) {
             int ti, tj;
             trc(m, ti, tj);
-            nW[m] = mmk<kVS>(nW[m], dvn1 + ti * 16 * LVS, LVS, 1, s1 + tj * 16 * LVS, 1, LVS, lane);
+            nW[m] = mmc<T, kVS>(nW[m], dvn1 + ti * 16 * LVS, LVS, s1 + tj * 16 * LVS, LVS, lane);
             asm volatile("" ::: "memory");
         }
 #pragma unroll
         for (int m = 0; m < OWN; ++m) {
             int ti, tj;
             trc(m, ti, tj);
-            dKb[m] = mmk<kVS>(dKb[m], vn1 + ti * 16 * LVS, LVS, 1, ds1 + tj * 16 * LVS, 1, LVS, lane);
+            dKb[m] = mmc<T, kVS>(dKb[m], vn1 + ti * 16 * LVS, LVS, ds1 + tj * 16 * LVS, LVS, lane);
             asm volatile("" ::: "memory");
         }
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const int t = wave + 8 * m, ti = t >> 2, tj = t & 3;
-            dAqk[m] = mmk<kVS>(dAqk[m], do1 + ti * 16 * LVS, LVS, 1, vn1 + tj * 16 * LVS, 1, LVS, lane);
+            dAqk[m] = mmc<T, kVS>(dAqk[m], do1 + ti * 16 * LVS, LVS, vn1 + tj * 16 * LVS, LVS, lane);
             if constexpr (DELTA)
-                dT[m] = mmk<kVS>(dT[m], dvn1 + ti * 16 * LVS, LVS, 1, p1 + tj * 16 * LVS, 1, LVS, lane);
+                dT[m] = mmc<T, kVS>(dT[m], dvn1 + ti * 16 * LVS, LVS, p1 + tj * 16 * LVS, LVS, lane);
         }
-        __syncthreads();
+        lds_barrier();
     }
     if (tid < DK) sDphi[tid] = dphi;
 
     // ---- per-element accumulators: dq, dk, E (gamma adjoint, natural units)
     f32x4 aq[OWN], ak[OWN], aE[OWN];
+    // e = 2^gamma at every owned element, kept for the later phases; the
+    // element loads (gamma, q, k) are issued together, ahead of their use
+    f32x4 ee[OWN];
+    f32x4 lq[OWN], lk[OWN], lg[OWN];
+    float lgl[OWN];
+#pragma unroll
+    for (int m = 0; m < OWN; ++m) {
+        const int d = ecol(m);
+        lgl[m] = PERCH ? pc[P::GAM + (size_t)(C - 1) * DK + d] : sGam[C - 1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = erow(m, i);
+            lg[m][i] = gam_at(r, d);
+            lq[m][i] = in_at(q, r, d);
+            lk[m][i] = in_at(k, r, d);
+        }
+    }
 #pragma unroll
     for (int m = 0; m < OWN; ++m) {
         const int d = ecol(m);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = erow(m, i);
-            const float gm = gam_at(r, d), e = __builtin_amdgcn_exp2f(gm);
-            const float qq = in_at(q, r, d), kk = in_at(k, r, d);
+            const float gm = lg[m][i], e = __builtin_amdgcn_exp2f(gm);
+            ee[m][i] = e;
+            const float qq = lq[m][i], kk = lk[m][i];
             // Q~ = q e;  Kbar = k 2^(gamma_last - gamma)
-            const float kbf = __builtin_amdgcn_exp2f((PERCH ? pc[P::GAM + (size_t)(C - 1) * DK + d] : sGam[C - 1]) - gm);
+            const float kbf = __builtin_amdgcn_exp2f(lgl[m] - gm);
             const float kbar = kk * kbf;
             aq[m][i] = dQt[m][i] * e;
             ak[m][i] = dKb[m][i] * kbf;
@@ -736,7 +886,6 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
                 if ((lane & 15) == 0) atomicAdd(&sF[0], part);
             }
         }
-        asm volatile("" ::: "memory");   // one tile's global loads in flight at a time
     }
 
     if constexpr (DELTA) {
@@ -746,7 +895,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         for (int m = 0; m < OWN; ++m)
 #pragma unroll
             for (int i = 0; i < 4; ++i) sNW[erow(m, i) * LDK + ecol(m)] = nW[m][i];
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int m = 0; m < OWN; ++m) {
             int ti, tj;
@@ -757,7 +906,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             for (int i = 0; i < 4; ++i) {
                 const int r = erow(m, i);
                 const float dm = -acc[i];
-                const float e = __builtin_amdgcn_exp2f(gam_at(r, d));
+                const float e = ee[m][i];
                 const float kp = PERCH ? sKp[r * LDK + d] : sKp[r * LDK + d] * e;   // K+ = k e
                 const float bt = beta_at(r);
                 // M = diag(beta) K+ with K+ = k e:  dk += beta e dM,  E += dM M,  dbeta += dM K+
@@ -769,18 +918,27 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
                 if ((lane & 15) == 0) atomicAdd(&sDb[r], part);
             }
         }
-        __syncthreads();
+        lds_barrier();
         // ---- phase 2b: dA = -T^T dT T^T (strictly lower), dL = diag(beta) dA
         float* sDT = smem + SM::DT;
         float* sY = smem + SM::Y;
         float* sDL = smem + SM::DL;
+        // L at this lane's dA elements, loaded ahead of the two products
+        float lrc[2][4];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int t = wave + 8 * m, ti = t >> 2, tj = t & 3;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                lrc[m][i] = pc[P::L + (size_t)(ti * 16 + arow(lane, i)) * C + tj * 16 + (lane & 15)];
+        }
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const int t = wave + 8 * m, ti = t >> 2, tj = t & 3;
 #pragma unroll
             for (int i = 0; i < 4; ++i) sDT[(ti * 16 + arow(lane, i)) * LDC + tj * 16 + (lane & 15)] = dT[m][i];
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const int t = wave + 8 * m, ti = t >> 2, tj = t & 3;
@@ -788,7 +946,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) sY[(ti * 16 + arow(lane, i)) * LDC + tj * 16 + (lane & 15)] = acc[i];
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const int t = wave + 8 * m, ti = t >> 2, tj = t & 3;
@@ -797,9 +955,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             for (int i = 0; i < 4; ++i) {
                 const int r = ti * 16 + arow(lane, i), cc = tj * 16 + (lane & 15);
                 const float da = cc < r ? -acc[i] : 0.f;
-                const float lrc = pc[P::L + (size_t)r * C + cc];
                 sDL[r * LDC + cc] = beta_at(r) * da;
-                float part = da * lrc;
+                float part = da * lrc[m][i];
 #pragma unroll
                 for (int off = 1; off < 16; off <<= 1) part += __shfl_xor(part, off, 64);
                 if ((lane & 15) == 0) atomicAdd(&sDb[r], part);
@@ -817,7 +974,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             sDAqk[r * LDC + cc] = cc <= r ? dAqk[m][i] : 0.f;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- phase 2c: the pairwise products
     float* sKm = smem + SM::KM;     // kda: K-;  scalar: raw q
@@ -862,7 +1019,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     if constexpr (PERCH) {
         // dK+ += dL K-;  dK- = dL^T K+ + dAqk^T Q~;  dQ~ += dAqk K- (one
         // product at a time over the owned tiles, which keeps few results live)
@@ -875,7 +1032,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = erow(m, i);
-                ak[m][i] += dkp[i] * __builtin_amdgcn_exp2f(pc[P::GAM + (size_t)r * DK + d]);
+                ak[m][i] += dkp[i] * ee[m][i];
                 aE[m][i] += dkp[i] * sKp[r * LDK + d];
             }
         }
@@ -889,7 +1046,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = erow(m, i);
-                ak[m][i] += dkm[i] * __builtin_amdgcn_exp2f(-pc[P::GAM + (size_t)r * DK + d]);
+                ak[m][i] += dkm[i] / ee[m][i];
                 aE[m][i] -= dkm[i] * sKm[r * LDK + d];
             }
         }
@@ -902,7 +1059,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = erow(m, i);
-                aq[m][i] += dqt[i] * __builtin_amdgcn_exp2f(pc[P::GAM + (size_t)r * DK + d]);
+                aq[m][i] += dqt[i] * ee[m][i];
                 aE[m][i] += dqt[i] * sQt[r * LDK + d];
             }
         }
@@ -927,7 +1084,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- phase 3: write dq, dk; E to LDS, then the reverse cumsum per column
     float* sEm = smem + SM::E;
@@ -945,7 +1102,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     if constexpr (PERCH) {
         if (tid < DK) {
             const int d = tid;
@@ -966,7 +1123,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             for (int d = 0; d < DK; ++d) s += sDphi[d];
             sF[1] = s * sPhi[0];
         }
-        __syncthreads();
+        lds_barrier();
         if (tid == 0) {
             float acc = sF[0] + sF[1];
             for (int r = C - 1; r >= 0; --r) {

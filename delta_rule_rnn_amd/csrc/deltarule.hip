@@ -443,10 +443,10 @@ dr_status launch_backward_t(const BwdArgs& a, hipStream_t st) {
                        prep, a.T, a.H, a.NT);
     dr_status s = check_launch();
     if (s != DR_OK) return s;
-    hipLaunchKernelGGL((bwd_state_fwd_kernel<KIND, D>), dim3((unsigned)slices), dim3(256), 0, st, prep, a.h0, hs, vn,
+    hipLaunchKernelGGL((bwd_state_fwd_kernel<KIND, D>), dim3((unsigned)slices), dim3(kStateThreads), 0, st, prep, a.h0, hs, vn,
                        a.H, a.NT);
     if ((s = check_launch()) != DR_OK) return s;
-    hipLaunchKernelGGL((bwd_state_rev_kernel<KIND, E, D>), dim3((unsigned)slices), dim3(256), 0, st, prep, dout, a.dhT,
+    hipLaunchKernelGGL((bwd_state_rev_kernel<KIND, E, D>), dim3((unsigned)slices), dim3(kStateThreads), 0, st, prep, dout, a.dhT,
                        dhs, dvn, a.dh0, a.T, a.H, a.NT);
     if ((s = check_launch()) != DR_OK) return s;
     hipLaunchKernelGGL((bwd_grad_kernel<KIND, E, D>), dim3((unsigned)items), dim3(512), 0, st, q, k, v, a.beta, dout,
