@@ -300,7 +300,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
         if (ti >= tj && (isL ? DELTA : true)) {
             const float* Aop = isL ? sA : sQ;
             const float* Bop = PERCH ? sB : sA;
-            acc = mmk<DK>(acc, Aop + ti * 16 * LDK, LDK, 1, Bop + tj * 16 * LDK, 1, LDK, lane);
+            // both operands run along the key channels (contiguous): bf16 MFMA
+            // for bf16 I/O, as the forward's products
+            acc = mmc<T, DK>(acc, Aop + ti * 16 * LDK, LDK, Bop + tj * 16 * LDK, LDK, lane);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -318,25 +320,53 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
     }
     lds_barrier();
 
-    // ---- T = (I + diag(beta) L)^-1 by forward substitution, one column per
-    // lane held in registers (fully unrolled: the rows of L are broadcast
-    // LDS reads, no LDS round trip through T)
+    // ---- T = (I + diag(beta) L)^-1, blocked over 16 x 16 blocks:
+    //   diagonal blocks T_ii = (I + A_ii)^-1 by forward substitution (one
+    //   column per lane, in registers), then by block distance
+    //   T_ij = -T_ii sum_{j <= m < i} A_im T_mj  (A = diag(beta) L)
+    //   on fp32 MFMA, with sB (free after L and Aqk) as scratch
     if constexpr (DELTA) {
         if (wave == 0) {
-            const int j = lane;
-            float t[C];
+            const int o = (lane >> 4) * 16, j = lane & 15;
+            float t[16];
 #pragma unroll
-            for (int i = 0; i < C; ++i) {
-                float s = 0.f;
+            for (int i = 0; i < 16; ++i) {
+                float sacc = 0.f;
 #pragma unroll
-                for (int m = 0; m < i; ++m) s += sL[i * LDC + m] * t[m];
-                // t[m] = 0 for m < j, so rows above the diagonal contribute nothing
-                t[i] = i < j ? 0.f : (i == j ? 1.f : -sBeta[i] * s);
+                for (int m = 0; m < i; ++m) sacc += sL[(o + i) * LDC + o + m] * t[m];
+                t[i] = i < j ? 0.f : (i == j ? 1.f : -sBeta[o + i] * sacc);
             }
 #pragma unroll
-            for (int i = 0; i < C; ++i) sT[i * LDC + j] = t[i];
+            for (int i = 0; i < 16; ++i) sT[(o + i) * LDC + o + j] = t[i];
+        } else {
+            // zero blocks above the diagonal: 6 blocks of 256 over 192 threads
+            for (int idx = tid - 64; idx < 6 * 256; idx += 192) {
+                const int blk = idx >> 8, e = idx & 255;
+                const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+                const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+                sT[(bi * 16 + (e >> 4)) * LDC + bj * 16 + (e & 15)] = 0.f;
+            }
         }
         lds_barrier();
+        float* sX = sB;
+#pragma unroll
+        for (int dist = 1; dist < 4; ++dist) {
+            const int i = dist + wave, j = wave;      // block (i, j), one per wave
+            if (i < 4) {
+                f32x4 x = zero4();
+                for (int m = j; m < i; ++m)
+                    x = mmk<16>(x, sL + i * 16 * LDC + m * 16, LDC, 1, sT + m * 16 * LDC + j * 16, LDC, 1, lane);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) sX[wave * 256 + arow(lane, q) * 16 + (lane & 15)] = sBeta[i * 16 + arow(lane, q)] * x[q];
+            }
+            lds_barrier();
+            if (i < 4) {
+                const f32x4 y = mmk<16>(zero4(), sT + i * 16 * LDC + i * 16, LDC, 1, sX + wave * 256, 16, 1, lane);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) sT[(i * 16 + arow(lane, q)) * LDC + j * 16 + (lane & 15)] = -y[q];
+            }
+            lds_barrier();
+        }
         #pragma unroll 8
         for (int it_ = 0; it_ < (C * C) / 256; ++it_) {
             const int idx = tid + it_ * 256;
@@ -367,7 +397,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
             const bool isW = job < NTL;
             const int t = isW ? job : job - NTL, ti = t / (DK / 16), tj = t % (DK / 16);
             const float* Bop = isW ? sA : sQ;
-            f32x4 acc = mmk<C>(zero4(), sT + ti * 16 * LDC, LDC, 1, Bop + tj * 16, LDK, 1, lane);
+            // T is lower triangular: the reduction stops at block ti
+            f32x4 acc = zero4();
+            for (int kb = 0; kb <= ti; ++kb)
+                acc = mmk<16>(acc, sT + ti * 16 * LDC + kb * 16, LDC, 1, Bop + kb * 16 * LDK + tj * 16, LDK, 1, lane);
             float* dst = out + (isW ? P::W : P::U);
 #pragma unroll
             for (int i = 0; i < 4; ++i) dst[(size_t)(ti * 16 + arow(lane, i)) * DK + tj * 16 + (lane & 15)] = acc[i];
