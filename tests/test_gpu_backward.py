@@ -120,3 +120,26 @@ def test_backward_long_sampled():
         for n, r in zip(names, res[:5]):
             assert_close(r[:, :, h:h + 1], ref[n], "bf16", f"head {h} {n}")
         assert_close(res[5][:, h:h + 1], np.swapaxes(ref["dh0"], -1, -2), "bf16", f"head {h} dh0")
+
+
+def test_backward_full_size_sampled():
+    """The benchmark workload (KDA bf16, B=1, H=32, T=32768, d=128) through
+    the same call bench.py --mode backward times; every gradient of one
+    sampled head against the oracle run on that head alone."""
+    dra = _ops()
+    from delta_rule_rnn_amd.inputs import WORKLOADS
+    w = WORKLOADS["kda_bf16_long"]
+    x = generate(w)
+    gen = torch.Generator().manual_seed(99)
+    do = torch.randn(w.B, w.T, w.H, w.Dv, generator=gen).to(torch.bfloat16)
+    dhT = torch.randn(w.B, w.H, w.Dk, w.Dv, generator=gen) * 0.1
+    d = to_dev(x)
+    res = dra.backward("kda", d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], do.to("cuda:0"), dhT.to("cuda:0"))
+    torch.cuda.synchronize()
+    h = 13
+    sl = lambda t: t[:, :, h:h + 1].contiguous()
+    ref = recurrence_backward("kda", sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]), None,
+                              sl(do), dhT[:, h:h + 1].transpose(-1, -2))
+    for n, r in zip(["dq", "dk", "dv", "dg", "dbeta"], res[:5]):
+        assert_close(r[:, :, h:h + 1].float().cpu().numpy(), ref[n], "bf16", f"full size head {h} {n}")
+    assert_close(res[5][:, h:h + 1].cpu().numpy(), np.swapaxes(ref["dh0"], -1, -2), "bf16", f"full size head {h} dh0")
