@@ -153,3 +153,25 @@ def test_prefill_then_decode_with_prologue(kind):
     ro, rs = _oracle(kind, x, ok)
     assert_close(o2.float().cpu().numpy(), ro[:, T1:], "bf16", f"{kind} decode after prefill, output")
     assert_close(hT.cpu().numpy(), np.swapaxes(rs, -1, -2), "bf16", f"{kind} decode after prefill, state")
+
+
+def test_prologue_full_size_sampled():
+    """GDN at the long workload's sizes (B=1, H=32, T=32768, d=128, bf16)
+    from raw projections with the full prologue (bench.py --mode prologue):
+    two sampled heads against the oracle's prologue and recurrence."""
+    dra = _ops()
+    from delta_rule_rnn_amd.inputs import WORKLOADS
+    w = WORKLOADS["gdn_bf16_long"]
+    x = generate_raw(w)
+    d = to_dev(x)
+    gp, ok = _pro(dra, x, d, scale=w.Dk ** -0.5)
+    o, hT = dra.forward("gdn", d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], prologue=gp)
+    torch.cuda.synchronize()
+    o, hT = o.float().cpu().numpy(), hT.cpu().numpy()
+    for h in (0, 21):
+        sl = lambda t: t[:, :, h:h + 1].contiguous()
+        okh = dict(ok, A_log=ok["A_log"][h:h + 1], dt_bias=ok["dt_bias"][h:h + 1])
+        q2, k2, g2, b2 = opro.apply("gdn", sl(x["q"]), sl(x["k"]), sl(x["g"]), sl(x["beta"]), **okh)
+        ro, rs = oracle.recurrence("gdn", q2, k2, sl(x["v"]), g2, b2)
+        assert_close(o[:, :, h:h + 1], ro, "bf16", f"head {h} output")
+        assert_close(hT[:, h:h + 1], np.swapaxes(rs, -1, -2), "bf16", f"head {h} state")

@@ -95,3 +95,38 @@ def test_malformed_offsets_raise_flag():
         torch.cuda.synchronize()
         assert int(flags.item()) & 4, cu
         assert torch.isfinite(hT).all()
+
+
+def test_varlen_full_size_sampled():
+    """The packed workload bench.py --mode varlen times: the 32 768 tokens of
+    the KDA benchmark workload cut into sequences of seeded lengths in
+    [64, 4096]; three sampled sequences on two heads against the oracle run
+    on each alone."""
+    dra = _ops()
+    from delta_rule_rnn_amd.inputs import WORKLOADS
+    w0 = WORKLOADS["kda_bf16_long"]
+    T = w0.B * w0.T
+    w = w0.with_(name=w0.name + "_packed", B=1, T=T)
+    rng = torch.Generator().manual_seed(7)
+    lengths, left = [], T
+    while left > 0:
+        n = min(left, int(torch.randint(64, 4097, (1,), generator=rng).item()))
+        lengths.append(n)
+        left -= n
+    cu = [0]
+    for n in lengths:
+        cu.append(cu[-1] + n)
+    x = generate(w)
+    d = to_dev(x)
+    sq = lambda t: None if t is None else t[0]
+    cu_t = torch.tensor(cu, dtype=torch.int32, device="cuda:0")
+    o, hT = dra.forward_varlen("kda", sq(d["q"]), sq(d["k"]), sq(d["v"]), sq(d["g"]), sq(d["beta"]), cu_t)
+    torch.cuda.synchronize()
+    o, hT = o.float().cpu().numpy(), hT.cpu().numpy()
+    for i in (0, len(lengths) // 2, len(lengths) - 1):
+        a, b = cu[i], cu[i + 1]
+        for h in (3, 29):
+            sl = lambda t: t[:, a:b, h:h + 1].contiguous()
+            ro, rs = oracle.recurrence("kda", sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]))
+            assert_close(o[a:b, h:h + 1][None], ro, "bf16", f"sequence {i} head {h} output")
+            assert_close(hT[i:i + 1, h:h + 1], np.swapaxes(rs, -1, -2), "bf16", f"sequence {i} head {h} state")
