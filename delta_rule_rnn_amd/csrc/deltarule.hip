@@ -347,12 +347,22 @@ struct DecodeArgs {
     dr::Prologue pro;
 };
 
+// State sizes above half the MI355X last-level cache (256 MB) use streaming
+// state stores (see decode.h).
+constexpr size_t kDecodeStreamBytes = (size_t)128 << 20;
+
 template <int KIND, typename E, int D, bool PRO>
 dr_status launch_decode_t(const DecodeArgs& a, hipStream_t st) {
     dim3 grid((unsigned)((long long)a.B * a.H * (D / 64)));
-    hipLaunchKernelGGL((dr::decode_kernel<KIND, E, D, D, PRO>), grid, dim3(64), 0, st, static_cast<const E*>(a.q),
-                       static_cast<const E*>(a.k), static_cast<const E*>(a.v), a.g, a.beta, a.state,
-                       static_cast<E*>(a.o), a.T, a.H, a.pro);
+    const bool nts = (size_t)a.B * a.H * D * D * sizeof(float) > kDecodeStreamBytes;
+    if (nts)
+        hipLaunchKernelGGL((dr::decode_kernel<KIND, E, D, D, PRO, true>), grid, dim3(64), 0, st,
+                           static_cast<const E*>(a.q), static_cast<const E*>(a.k), static_cast<const E*>(a.v), a.g,
+                           a.beta, a.state, static_cast<E*>(a.o), a.T, a.H, a.pro);
+    else
+        hipLaunchKernelGGL((dr::decode_kernel<KIND, E, D, D, PRO, false>), grid, dim3(64), 0, st,
+                           static_cast<const E*>(a.q), static_cast<const E*>(a.k), static_cast<const E*>(a.v), a.g,
+                           a.beta, a.state, static_cast<E*>(a.o), a.T, a.H, a.pro);
     return check_launch();
 }
 
