@@ -101,3 +101,28 @@ def test_decode_large_batch_sampled():
         ro, rs = _oracle("kda", xs, x["h0"][b:b + 1, h:h + 1])
         assert_close(o[b:b + 1, :, h:h + 1], ro, "bf16", f"chain ({b},{h}) output")
         assert_close(state[b:b + 1, h:h + 1], rs, "f32", f"chain ({b},{h}) state")
+
+
+def test_decode_streaming_stores_sampled():
+    """A call whose state (160 x 32 heads x 64 KB = 335 MB) exceeds the
+    128 MB threshold above which the state is written back with streaming
+    stores; sampled chains against the oracle, two calls in a row."""
+    dra = _ops()
+    w = Workload("kda_dec_stream", "kda", "bf16", B=160, H=32, T=2, Dk=128, Dv=128, h0_std=0.5, seed=25)
+    x = generate(w)
+    d = to_dev(x)
+    state = d["h0"].clone()
+    cut = lambda t, a, b: t[:, a:b].contiguous()
+    o1 = dra.kda_decode(cut(d["q"], 0, 1), cut(d["k"], 0, 1), cut(d["v"], 0, 1), cut(d["g"], 0, 1),
+                        cut(d["beta"], 0, 1), state)
+    o2 = dra.kda_decode(cut(d["q"], 1, 2), cut(d["k"], 1, 2), cut(d["v"], 1, 2), cut(d["g"], 1, 2),
+                        cut(d["beta"], 1, 2), state)
+    torch.cuda.synchronize()
+    o = torch.cat([o1, o2], dim=1).float().cpu().numpy()
+    state = state.cpu().numpy()
+    for (b, h) in [(0, 0), (97, 13), (159, 31)]:
+        sl = lambda t: None if t is None else t[b:b + 1, :, h:h + 1].contiguous()
+        xs = {n: sl(t) for n, t in x.items() if n != "h0"}
+        ro, rs = _oracle("kda", xs, x["h0"][b:b + 1, h:h + 1])
+        assert_close(o[b:b + 1, :, h:h + 1], ro, "bf16", f"chain ({b},{h}) output")
+        assert_close(state[b:b + 1, h:h + 1], rs, "f32", f"chain ({b},{h}) state")
