@@ -151,3 +151,23 @@ def test_prologue_rejects(lib):
     from delta_rule_rnn_amd import DeltaRuleError, Prologue
     with pytest.raises(DeltaRuleError):
         Prologue(dt_bias=torch.zeros(1)).to_c(1)
+
+
+def test_backward_rejects(lib):
+    """dr_backward refuses bad arguments on the host, before any launch."""
+    need = lib.dr_backward_workspace_bytes(1, 1, 128, 2, 64, 64, 64, 1)
+    assert need > 0 and lib.dr_backward_workspace_bytes(1, 1, 128, 2, 96, 96, 64, 1) == 0
+
+    def bwd(kind=1, dout=FAKE, dq=FAKE, dbeta=FAKE, ws=FAKE, wsb=1 << 40, D=64, T=128, dg=FAKE, q=FAKE):
+        return lib.dr_backward(kind, q, FAKE, FAKE, FAKE, FAKE, None, dout, None, dq, FAKE, FAKE, dg, dbeta, None,
+                               1, T, 2, D, D, 64, 1, ws, wsb, None)
+
+    assert bwd(kind=3) == -1
+    assert bwd(dout=None) == -1
+    assert bwd(dq=None) == -1
+    assert bwd(dg=None) == -1
+    assert bwd(dbeta=None) == -1                 # gdn needs dbeta
+    assert bwd(q=FAKE + 8) == -1                 # misaligned
+    assert bwd(D=96) == -2
+    assert bwd(ws=None) == -4
+    assert bwd(wsb=need - 1) == -4
