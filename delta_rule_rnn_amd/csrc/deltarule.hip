@@ -11,6 +11,7 @@
 #include "decode.h"
 #include "steps.h"
 #include "backward.h"
+#include "prologue.h"
 
 namespace {
 
@@ -465,6 +466,58 @@ dr_status launch_backward_t(const BwdArgs& a, hipStream_t st) {
     return check_launch();
 }
 
+// Workspace of the backward through the prologue: the recurrence's inputs
+// (q^, k^ in the I/O dtype, g^ and beta^ fp32), then the backward's own.
+struct ProBwdLayout {
+    size_t qh, kh, gh, bh, core, bytes;
+};
+ProBwdLayout probwd_layout(int kind, int B, int T, int H, int D, int dtype) {
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t n = (size_t)B * T * H, esz = dtype == DR_BF16 ? 2 : 4;
+    ProBwdLayout L;
+    L.qh = 0;
+    L.kh = up(n * D * esz);
+    L.gh = L.kh + up(n * D * esz);
+    L.bh = L.gh + up(n * (kind == DR_KIND_KDA ? D : 1) * 4);
+    L.core = L.bh + up(n * 4);
+    L.bytes = L.core + bwd_layout(B, T, H, D).bytes;
+    return L;
+}
+
+template <typename E, int D, bool PERCH>
+dr_status launch_prologue_t(bool backward, const void* q, const void* k, const float* g, const float* beta, void* qh,
+                            void* kh, float* gh, float* bh, void* dq, void* dk, float* dg, float* dbeta,
+                            float* dA_log, float* ddt, int B, int T, int H, const dr::Prologue& pro, hipStream_t st) {
+    const long long rows = (long long)B * T;
+    const long long blocks = (long long)H * ((rows + dr::kProRows - 1) / dr::kProRows);
+    if (blocks > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
+    if (!backward)
+        hipLaunchKernelGGL((dr::prologue_apply_kernel<E, D, PERCH>), dim3((unsigned)blocks), dim3(256), 0, st,
+                           static_cast<const E*>(q), static_cast<const E*>(k), g, beta, static_cast<E*>(qh),
+                           static_cast<E*>(kh), gh, bh, rows, H, pro);
+    else
+        hipLaunchKernelGGL((dr::prologue_backward_kernel<E, D, PERCH>), dim3((unsigned)blocks), dim3(256), 0, st,
+                           static_cast<const E*>(q), static_cast<const E*>(k), g, beta, static_cast<E*>(dq),
+                           static_cast<E*>(dk), dg, dbeta, dA_log, ddt, rows, H, pro);
+    return check_launch();
+}
+
+dr_status launch_prologue(bool backward, int kind, int D, int dtype, const void* q, const void* k, const float* g,
+                          const float* beta, void* qh, void* kh, float* gh, float* bh, void* dq, void* dk, float* dg,
+                          float* dbeta, float* dA_log, float* ddt, int B, int T, int H, const dr::Prologue& pro,
+                          hipStream_t st) {
+#define DR_PRO(E, DD, PC) \
+    return launch_prologue_t<E, DD, PC>(backward, q, k, g, beta, qh, kh, gh, bh, dq, dk, dg, dbeta, dA_log, ddt, B, T, H, pro, st)
+    const bool perch = kind == DR_KIND_KDA;
+    if (dtype == DR_BF16) {
+        if (D == 64) { if (perch) DR_PRO(bf16, 64, true); else DR_PRO(bf16, 64, false); }
+        if (perch) DR_PRO(bf16, 128, true); else DR_PRO(bf16, 128, false);
+    }
+    if (D == 64) { if (perch) DR_PRO(float, 64, true); else DR_PRO(float, 64, false); }
+    if (perch) DR_PRO(float, 128, true); else DR_PRO(float, 128, false);
+#undef DR_PRO
+}
+
 template <int KIND>
 dr_status launch_backward_k(const BwdArgs& a, int D, int dtype, hipStream_t st) {
     if (dtype == DR_BF16) {
@@ -489,15 +542,45 @@ dr_status dr_backward(int kind, const void* q, const void* k, const void* v, con
                       const float* h0, const void* dout, const float* dhT, void* dq, void* dk, void* dv, float* dg,
                       float* dbeta, float* dh0, int B, int T, int H, int Dk, int Dv, int C, int dtype,
                       void* workspace, size_t workspace_bytes, void* stream) {
+    return dr_backward_prologue(kind, q, k, v, g, beta, h0, dout, dhT, dq, dk, dv, dg, dbeta, dh0, nullptr, nullptr,
+                                B, T, H, Dk, Dv, C, dtype, nullptr, workspace, workspace_bytes, stream);
+}
+
+size_t dr_backward_prologue_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, int C, int dtype) {
+    if (kind < 0 || kind > 2 || B <= 0 || H <= 0 || T < 0) return 0;
+    if (dr_record_bytes(Dk, Dv, C, dtype) == 0) return 0;
+    return probwd_layout(kind, B, T, H, Dk, dtype).bytes;
+}
+
+dr_status dr_backward_prologue(int kind, const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, const float* h0, const void* dout, const float* dhT, void* dq,
+                               void* dk, void* dv, float* dg, float* dbeta, float* dh0, float* dA_log,
+                               float* ddt_bias, int B, int T, int H, int Dk, int Dv, int C, int dtype,
+                               const dr_prologue* prologue, void* workspace, size_t workspace_bytes, void* stream) {
     dr_status s = validate(kind, q, k, v, g, beta, B, T, H, Dk, Dv, C, dtype);
     if (s != DR_OK) return s;
+    dr::Prologue pr;
+    bool use_pro;
+    if ((s = resolve_prologue(kind, prologue, &pr, &use_pro)) != DR_OK) return s;
     const bool delta = kind != DR_KIND_DECAY_LA;
+    const bool gate = use_pro && (pr.ops & dr::PRO_GATE);
     if (T > 0 && (!dout || !dq || !dk || !dv || !dg || (delta && !dbeta))) return DR_ERR_INVALID_ARG;
+    if (gate && (!dA_log || (pr.dt_bias && !ddt_bias))) return DR_ERR_INVALID_ARG;
     const void* ptrs[] = {h0, dout, dhT, dq, dk, dv, dg, dbeta, dh0, workspace};
     for (const void* p : ptrs)
         if (!aligned16(p)) return DR_ERR_INVALID_ARG;
-    const BwdLayout L = bwd_layout(B, T, H, Dk);
+    if ((reinterpret_cast<uintptr_t>(dA_log) & 3u) || (reinterpret_cast<uintptr_t>(ddt_bias) & 3u))
+        return DR_ERR_INVALID_ARG;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (gate) {
+        // accumulated below (or left zero without tokens)
+        hipLaunchKernelGGL(dr::copy_or_zero_kernel, dim3(((size_t)H + 255) / 256), dim3(256), 0, st, dA_log,
+                           (const float*)nullptr, (size_t)H);
+        if (ddt_bias)
+            hipLaunchKernelGGL(dr::copy_or_zero_kernel, dim3(((size_t)H + 255) / 256), dim3(256), 0, st, ddt_bias,
+                               (const float*)nullptr, (size_t)H);
+        if ((s = check_launch()) != DR_OK) return s;
+    }
     if (T == 0) {
         // no tokens: dh0 = dhT (or zero); nothing else to write
         if (!dh0) return DR_OK;
@@ -505,14 +588,36 @@ dr_status dr_backward(int kind, const void* q, const void* k, const void* v, con
         hipLaunchKernelGGL(dr::copy_or_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dh0, dhT, n);
         return check_launch();
     }
-    if (!workspace || workspace_bytes < L.bytes) return DR_ERR_WORKSPACE;
-    BwdArgs a{q, k, v, dout, g, delta ? beta : nullptr, h0, dhT, dq, dk, dv, dg, delta ? dbeta : nullptr, dh0,
-              B, T, H, ceil_div(T, dr::kChunk), static_cast<uint8_t*>(workspace), L};
-    switch (kind) {
-        case DR_KIND_KDA: return launch_backward_k<dr::KIND_KDA>(a, Dk, dtype, st);
-        case DR_KIND_GDN: return launch_backward_k<dr::KIND_GDN>(a, Dk, dtype, st);
-        default: return launch_backward_k<dr::KIND_LA>(a, Dk, dtype, st);
+    uint8_t* w = static_cast<uint8_t*>(workspace);
+    const ProBwdLayout PL = probwd_layout(kind, B, T, H, Dk, dtype);
+    const BwdLayout L = bwd_layout(B, T, H, Dk);
+    if (!workspace || workspace_bytes < (use_pro ? PL.bytes : L.bytes)) return DR_ERR_WORKSPACE;
+    // the recurrence's inputs: the caller's, or the prologue's outputs
+    const void *rq = q, *rk = k;
+    const float *rg = g, *rb = delta ? beta : nullptr;
+    uint8_t* core = w;
+    if (use_pro) {
+        void* qh = w + PL.qh;
+        void* kh = w + PL.kh;
+        float* gh = reinterpret_cast<float*>(w + PL.gh);
+        float* bh = delta ? reinterpret_cast<float*>(w + PL.bh) : nullptr;
+        s = launch_prologue(false, kind, Dk, dtype, q, k, g, rb, qh, kh, gh, bh, nullptr, nullptr, nullptr, nullptr,
+                            nullptr, nullptr, B, T, H, pr, st);
+        if (s != DR_OK) return s;
+        rq = qh; rk = kh; rg = gh; rb = bh;
+        core = w + PL.core;
     }
+    BwdArgs a{rq, rk, v, dout, rg, rb, h0, dhT, dq, dk, dv, dg, delta ? dbeta : nullptr, dh0,
+              B, T, H, ceil_div(T, dr::kChunk), core, L};
+    switch (kind) {
+        case DR_KIND_KDA: s = launch_backward_k<dr::KIND_KDA>(a, Dk, dtype, st); break;
+        case DR_KIND_GDN: s = launch_backward_k<dr::KIND_GDN>(a, Dk, dtype, st); break;
+        default: s = launch_backward_k<dr::KIND_LA>(a, Dk, dtype, st); break;
+    }
+    if (s != DR_OK || !use_pro) return s;
+    // gradients with respect to the raw inputs, in place
+    return launch_prologue(true, kind, Dk, dtype, q, k, g, delta ? beta : nullptr, nullptr, nullptr, nullptr,
+                           nullptr, dq, dk, dg, delta ? dbeta : nullptr, dA_log, ddt_bias, B, T, H, pr, st);
 }
 
 
@@ -700,6 +805,6 @@ const char* dr_status_string(int status) {
     }
 }
 
-int dr_abi_version(void) { return 3; }
+int dr_abi_version(void) { return 4; }
 
 }  // extern "C"

@@ -331,12 +331,17 @@ def backward_workspace_bytes(kind: str, B: int, T: int, H: int, Dk: int, Dv: int
 
 
 def backward(kind: str, q, k, v, g, beta=None, h0=None, do=None, dhT=None, chunk_size=CHUNK, workspace=None,
-             stream=None):
+             stream=None, prologue: Optional[Prologue] = None):
     """Gradients of the forward of ``kind`` given do (the adjoint of o, like
     o) and dhT (the adjoint of hT, fp32 [B,H,Dk,Dv] or None).  Returns
     (dq, dk, dv, dg, dbeta, dh0): dq, dk, dv in the I/O dtype, dg like g,
     dbeta [B,T,H] fp32 (None for decay_la), dh0 fp32 [B,H,Dk,Dv] (zeros
-    of h0's shape also when h0 is None)."""
+    of h0's shape also when h0 is None).
+
+    With a ``prologue`` (the one the forward took), q, k, g and beta are the
+    raw inputs, the gradients are with respect to them, and two more results
+    follow: (..., dA_log, ddt_bias), fp32 [H] each (None without gate
+    generation, ddt_bias None without dt_bias)."""
     lib = _lib.load()
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
@@ -358,15 +363,31 @@ def backward(kind: str, q, k, v, g, beta=None, h0=None, do=None, dhT=None, chunk
     dg = torch.empty_like(g)
     dbeta = torch.empty_like(beta) if beta is not None else None
     dh0 = torch.empty(B, H, Dk, Dv, dtype=torch.float32, device=q.device)
-    need = backward_workspace_bytes(kind, B, T, H, Dk, Dv, dt, chunk_size)
+    code = DR_BF16 if dt == torch.bfloat16 else DR_F32
+    if prologue is not None:
+        need = int(lib.dr_backward_prologue_workspace_bytes(KINDS[kind], B, T, H, Dk, Dv, chunk_size, code))
+    else:
+        need = backward_workspace_bytes(kind, B, T, H, Dk, Dv, dt, chunk_size)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     _need(workspace, "workspace", torch.uint8)
-    st = lib.dr_backward(KINDS[kind], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(do), _ptr(dhT),
-                         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0), B, T, H, Dk, Dv, chunk_size,
-                         _dtype_code(q), _ptr(workspace), workspace.numel(), _stream(stream))
-    _check(st, "dr_backward")
-    return dq, dk, dv, dg, dbeta, dh0
+    if prologue is None:
+        st = lib.dr_backward(KINDS[kind], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(do),
+                             _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0), B, T, H, Dk,
+                             Dv, chunk_size, code, _ptr(workspace), workspace.numel(), _stream(stream))
+        _check(st, "dr_backward")
+        return dq, dk, dv, dg, dbeta, dh0
+    gate = prologue.A_log is not None
+    dA_log = torch.empty(H, dtype=torch.float32, device=q.device) if gate else None
+    ddt = torch.empty(H, dtype=torch.float32, device=q.device) if gate and prologue.dt_bias is not None else None
+    keep, pro = _pro_arg(prologue, H)
+    st = lib.dr_backward_prologue(KINDS[kind], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(do),
+                                  _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0),
+                                  _ptr(dA_log), _ptr(ddt), B, T, H, Dk, Dv, chunk_size, code, pro, _ptr(workspace),
+                                  workspace.numel(), _stream(stream))
+    del keep
+    _check(st, "dr_backward_prologue")
+    return dq, dk, dv, dg, dbeta, dh0, dA_log, ddt
 
 
 # ---- individual steps ------------------------------------------------------

@@ -281,6 +281,40 @@ dr_status dr_backward(int kind, const void* q, const void* k, const void* v, con
                       int B, int T, int H, int Dk, int Dv, int C, int dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Backward through the input prologue: the gradients with respect to the RAW
+ * inputs a forward with the same dr_prologue took (dr_forward), i.e. the
+ * recurrence's backward followed by the chain rule through the prologue
+ * ("Gated DeltaNet", sections "门控与 Head 映射", "加载 Token 与写入系数" and
+ * "反向传播：状态伴随与三角变换梯度"):
+ *   dq = scale (dq^ - y_q (y_q . dq^)) / n_q,  dk = (dk^ - y_k (y_k . dk^)) / n_k
+ *        (y = x / n, n = sqrt(|x|^2 + 1e-6); without DR_PRO_QK_L2NORM dq =
+ *        scale dq^, dk = dk^)
+ *   dbeta (raw logits) = s sigmoid(b) (1 - sigmoid(b)) dbeta^   (DR_PRO_BETA_SIGMOID)
+ *   dg (raw gate input a) = -exp(A_log) sigmoid(a + dt_bias) dg^ (DR_PRO_GATE)
+ *   dA_log[h] = sum over tokens of g^ dg^,  ddt_bias[h] = sum of dg
+ * where ^ marks the recurrence's inputs and their gradients.  Arguments as
+ * for dr_backward plus:
+ *   dA_log:   DEVICE float [H], written (required with DR_PRO_GATE, else
+ *             ignored); ddt_bias: DEVICE float [H], written (required when
+ *             the prologue has a dt_bias, else ignored).  Both are sums of
+ *             per-workgroup partials added atomically: their summation order
+ *             is not fixed.
+ *   prologue: as for dr_forward; NULL gives dr_backward.
+ *   workspace: at least dr_backward_prologue_workspace_bytes(...): the
+ *             recurrence's inputs (q^, k^, g^, beta^) plus dr_backward's.
+ * dq, dk, dg and dbeta are first written with the recurrence's gradients and
+ * then transformed in place.
+ */
+size_t dr_backward_prologue_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, int C, int dtype);
+dr_status dr_backward_prologue(int kind, const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, const float* h0, const void* dout, const float* dhT,
+                               void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dh0,
+                               float* dA_log, float* ddt_bias,
+                               int B, int T, int H, int Dk, int Dv, int C, int dtype,
+                               const dr_prologue* prologue, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 /* ---- the individual steps ---------------------------------------------- */
 
 /*
@@ -356,8 +390,8 @@ size_t dr_record_bytes(int Dk, int Dv, int C, int dtype);
 /* Human-readable text for a status code (static storage). */
 const char* dr_status_string(int status);
 
-/* ABI version of this library: 3 (1, plus the prologue entry points in 2, plus
- * the backward in 3). */
+/* ABI version of this library: 4 (1, plus the prologue entry points in 2, the
+ * backward in 3, the backward through the prologue in 4). */
 int dr_abi_version(void);
 
 #ifdef __cplusplus

@@ -476,3 +476,53 @@ def pin_backward_retention_closed_form(bwd):
         assert rel(res["dv"][0, :, h], P.T @ dO) < 1e-12
         assert rel(res["dq"][0, :, h], G @ K) < 1e-12
         assert rel(res["dk"][0, :, h], G.T @ Q) < 1e-12
+
+
+def pin_prologue_backward_fd(pro, rec, bwd):
+    """The prologue's chain rule (pro.apply_backward on top of the core
+    backward ``bwd``) against central finite differences of
+    L = <do, o> + <dhT, hT> through the prologue followed by the recurrence,
+    with respect to every raw input and parameter."""
+    eps = 1e-6
+    r = np.random.default_rng(65)
+    B, T, H, Dk, Dv = 1, 5, 2, 3, 4
+    for kind, opts in (("gdn", dict(qk_l2norm=True, scale=0.7, beta_sigmoid=True, beta_x2=True)),
+                       ("kda", dict(qk_l2norm=True, scale=1.3, beta_sigmoid=True)),
+                       ("decay_la", dict(qk_l2norm=True, scale=0.9))):
+        x = dict(q=r.standard_normal((B, T, H, Dk)) * 2, k=r.standard_normal((B, T, H, Dk)) * 2,
+                 v=r.standard_normal((B, T, H, Dv)),
+                 g=(np.log(r.uniform(0.6, 0.99, (B, T, H, Dk))) if kind == "kda"
+                    else r.standard_normal((B, T, H))),
+                 beta=None if kind == "decay_la" else r.standard_normal((B, T, H)),
+                 A_log=None if kind == "kda" else np.log(r.uniform(0.2, 2.0, H)),
+                 dt_bias=None if kind == "kda" else r.standard_normal(H))
+        h0 = r.standard_normal((B, H, Dv, Dk)) * 0.3
+        do, dhT = r.standard_normal((B, T, H, Dv)), r.standard_normal((B, H, Dv, Dk))
+
+        def prep(xx):
+            return pro.apply(kind, xx["q"], xx["k"], xx["g"], xx["beta"], A_log=xx["A_log"], dt_bias=xx["dt_bias"],
+                             **opts)
+
+        def loss(xx):
+            q2, k2, g2, b2 = prep(xx)
+            o, hT = rec(kind, q2, k2, xx["v"], g2, b2, h0)
+            return float(np.sum(o * do) + np.sum(hT * dhT))
+
+        q2, k2, g2, b2 = prep(x)
+        core = bwd(kind, q2, k2, x["v"], g2, b2, h0, do, dhT)
+        got = pro.apply_backward(kind, x["q"], x["k"], x["g"], x["beta"], core["dq"], core["dk"], core["dg"],
+                                 core["dbeta"], A_log=x["A_log"], dt_bias=x["dt_bias"], **opts)
+        for name, key in (("q", "dq"), ("k", "dk"), ("g", "dg"), ("beta", "dbeta"), ("A_log", "dA_log"),
+                          ("dt_bias", "ddt_bias")):
+            if x[name] is None:
+                continue
+            gnum = np.zeros_like(x[name])
+            it = np.nditer(x[name], flags=["multi_index"])
+            for _ in it:
+                idx = it.multi_index
+                xp = {n: (None if t is None else t.copy()) for n, t in x.items()}
+                xm = {n: (None if t is None else t.copy()) for n, t in x.items()}
+                xp[name][idx] += eps
+                xm[name][idx] -= eps
+                gnum[idx] = (loss(xp) - loss(xm)) / (2 * eps)
+            assert rel(got[key], gnum) < 1e-6, f"{kind} {key}: rel err {rel(got[key], gnum):.2e}"

@@ -38,7 +38,7 @@ def test_header_and_binding_agree():
 def test_every_declared_symbol_is_exported(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.dr_abi_version() == 3
+    assert lib.dr_abi_version() == 4
 
 
 def test_status_strings(lib):

@@ -143,3 +143,68 @@ def test_backward_full_size_sampled():
     for n, r in zip(["dq", "dk", "dv", "dg", "dbeta"], res[:5]):
         assert_close(r[:, :, h:h + 1].float().cpu().numpy(), ref[n], "bf16", f"full size head {h} {n}")
     assert_close(res[5][:, h:h + 1].cpu().numpy(), np.swapaxes(ref["dh0"], -1, -2), "bf16", f"full size head {h} dh0")
+
+
+PRO_CASES = [("kda", "bf16", 128, dict(qk=True, sig=True, x2=False, scale=0.5)),
+             ("kda", "f32", 64, dict(qk=True, sig=True, x2=True, scale=1.2)),
+             ("gdn", "bf16", 128, dict(qk=True, sig=True, x2=False, scale=0.09)),
+             ("gdn", "f32", 64, dict(qk=True, sig=True, x2=True, scale=1.0)),
+             ("decay_la", "bf16", 64, dict(qk=True, sig=False, x2=False, scale=0.125)),
+             ("decay_la", "f32", 128, dict(qk=False, sig=False, x2=False, scale=0.7))]
+
+
+@pytest.mark.parametrize("kind,dt,D,opts", PRO_CASES, ids=lambda c: str(c))
+def test_backward_through_prologue(kind, dt, D, opts):
+    """Raw projections in (generate_raw): the backward through the prologue
+    against the oracle's prologue chain rule on top of its reverse sweep of
+    the prologue's outputs; dA_log and ddt_bias included for scalar gates."""
+    from oracle import prologue as opro
+    from delta_rule_rnn_amd.inputs import generate_raw
+    dra = _ops()
+    w = Workload(f"{kind}_bwd_pro", kind, dt, B=2, H=3, T=150, Dk=D, Dv=D, h0_std=0.2, seed=76)
+    x = generate_raw(w)
+    do, dhT = _cotangents(w, 176)
+    do = do.to(x["q"].dtype)
+    gate = x["A_log"] is not None
+    if not opts["qk"]:
+        # without the normalisation the raw keys must already be short enough
+        # for a stable recurrence
+        x = dict(x, k=(x["k"].float() * 0.02).to(x["k"].dtype))
+    d = to_dev(x)
+    pro = dra.Prologue(qk_l2norm=opts["qk"], scale=opts["scale"], beta_sigmoid=opts["sig"] and kind != "decay_la",
+                       beta_x2=opts["x2"] and kind != "decay_la",
+                       A_log=d["A_log"] if gate else None, dt_bias=d["dt_bias"] if gate else None)
+    ok = dict(qk_l2norm=pro.qk_l2norm, scale=pro.scale, beta_sigmoid=pro.beta_sigmoid, beta_x2=pro.beta_x2,
+              A_log=x["A_log"] if gate else None, dt_bias=x["dt_bias"] if gate else None)
+    res = dra.backward(kind, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], do.to("cuda:0"), dhT.to("cuda:0"),
+                       prologue=pro)
+    torch.cuda.synchronize()
+    q2, k2, g2, b2 = opro.apply(kind, x["q"], x["k"], x["g"], x["beta"], **ok)
+    core = recurrence_backward(kind, q2, k2, x["v"], g2, b2, x["h0"].transpose(-1, -2), do, dhT.transpose(-1, -2))
+    ref = opro.apply_backward(kind, x["q"], x["k"], x["g"], x["beta"], core["dq"], core["dk"], core["dg"],
+                              core["dbeta"], **ok)
+    got = [None if t is None else t.float().cpu().numpy() for t in res]
+    what = f"{kind} {dt} D{D} {opts}"
+    assert_close(got[0], ref["dq"], dt, f"{what} dq")
+    assert_close(got[1], ref["dk"], dt, f"{what} dk")
+    assert_close(got[2], core["dv"], dt, f"{what} dv")
+    assert_close(got[3], ref["dg"], dt, f"{what} dg")
+    if kind != "decay_la":
+        assert_close(got[4], ref["dbeta"], dt, f"{what} dbeta")
+    assert_close(got[5], np.swapaxes(core["dh0"], -1, -2), dt, f"{what} dh0")
+    if gate:
+        # sums over all tokens of coef_t * dg^_t, with cancellation.  The
+        # per-token dg^ is held to the dtype's tolerance relative to its
+        # largest element, so the sum is held to that tolerance times
+        # sum_t |coef_t| * max_t |dg^_t| (the same bound carried through the
+        # sum)
+        tol = 1e-4 if dt == "f32" else 2e-2
+        gh = opro.scalar_gate(x["g"], x["A_log"], x["dt_bias"])
+        coef_dt = -np.exp(opro._f64(x["A_log"])) * opro.sigmoid(opro._f64(x["g"]) + opro._f64(x["dt_bias"]))
+        dgmax = np.max(np.abs(core["dg"]), axis=(0, 1))
+        for name, val, coef in (("dA_log", got[6], gh), ("ddt_bias", got[7], coef_dt)):
+            scale = np.sum(np.abs(coef), axis=(0, 1)) * dgmax
+            err = np.abs(val - ref[name])
+            assert np.all(err <= tol * scale), f"{what} {name}: |err| {err} > {tol} * {scale}"
+    else:
+        assert got[6] is None and got[7] is None

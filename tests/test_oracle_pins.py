@@ -244,7 +244,8 @@ def test_prologue_gate_rejected_for_per_channel():
 PROLOGUE_MUTATIONS = {
     "eps_outside_sqrt": ("x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)",
                          "x / (np.sqrt(np.sum(x * x, axis=-1, keepdims=True)) + eps)"),
-    "norm_over_heads": ("np.sum(x * x, axis=-1, keepdims=True)", "np.sum(x * x, axis=-2, keepdims=True)"),
+    "norm_over_heads": ("return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)",
+                        "return x / np.sqrt(np.sum(x * x, axis=-2, keepdims=True) + eps)"),
     "sigmoid_sign": ("1.0 / (1.0 + np.exp(-x))", "1.0 / (1.0 + np.exp(x))"),
     "softplus_as_log1p_of_x": ("np.logaddexp(0.0, _f64(x))", "np.log1p(np.abs(_f64(x)))"),
     "gate_without_exp": ("-np.exp(A_log) * softplus(a + bias)", "-A_log * softplus(a + bias)"),
@@ -331,3 +332,32 @@ def test_backward_pins_catch_planted_mistake(name, tmp_path):
         except AssertionError:
             caught.append(pin)
     assert caught, f"no backward pin caught the planted mistake {name}"
+
+
+def test_prologue_backward_finite_differences():
+    pins.pin_prologue_backward_fd(_prologue, oracle.recurrence, _backward.recurrence_backward)
+
+
+PROLOGUE_BACKWARD_MUTATIONS = {
+    "scale_dropped": ("    dyq = dq * scale\n", "    dyq = dq\n"),
+    "projection_sign": ("return (dy - y * np.sum(y * dy, axis=-1, keepdims=True)) / n",
+                        "return (dy + y * np.sum(y * dy, axis=-1, keepdims=True)) / n"),
+    "sigmoid_derivative": ("(2.0 if beta_x2 else 1.0) * s * (1.0 - s) * dbeta", "(2.0 if beta_x2 else 1.0) * s * dbeta"),
+    "gate_exp_dropped": ("da = -np.exp(A_log) * sigmoid(g + bias) * dg", "da = -sigmoid(g + bias) * dg"),
+    "dA_log_without_g": ('out["dA_log"] = np.sum(gout * dg, axis=red)', 'out["dA_log"] = np.sum(dg, axis=red)'),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PROLOGUE_BACKWARD_MUTATIONS))
+def test_prologue_backward_pins_catch_planted_mistake(name, tmp_path):
+    import importlib.util
+    src = open(_prologue.__file__).read()
+    old, new = PROLOGUE_BACKWARD_MUTATIONS[name]
+    assert src.count(old) == 1, f"mutation anchor not found: {name}"
+    path = tmp_path / "prologue_bmut.py"
+    path.write_text(src.replace(old, new))
+    spec = importlib.util.spec_from_file_location("prologue_bmut", str(path))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    with pytest.raises(AssertionError):
+        pins.pin_prologue_backward_fd(mod, oracle.recurrence, _backward.recurrence_backward)
