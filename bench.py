@@ -162,17 +162,12 @@ def varlen_bench(args):
     remainder); same heads, head size and distributions as the workload."""
     import torch
     import delta_rule_rnn_amd as dra
-    from delta_rule_rnn_amd.inputs import WORKLOADS, generate
+    from delta_rule_rnn_amd.inputs import WORKLOADS, generate, packed_lengths
 
     w0 = WORKLOADS[args.workload]
     T = w0.B * w0.T
     w = w0.with_(name=w0.name + "_packed", B=1, T=T)
-    rng = torch.Generator().manual_seed(7)
-    lengths, left = [], T
-    while left > 0:
-        n = min(left, int(torch.randint(64, 4097, (1,), generator=rng).item()))
-        lengths.append(n)
-        left -= n
+    lengths = packed_lengths(T, seed=7)
     cu = torch.tensor([0] + list(torch.tensor(lengths).cumsum(0).tolist()), dtype=torch.int32)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -251,6 +246,55 @@ def backward_bench(args):
     print(json.dumps(line), flush=True)
 
 
+def backward_varlen_bench(args):
+    """Backward over the packed batch of --mode varlen (the workload's B*T
+    tokens in sequences of seeded lengths uniform in [64, 4096]), inputs,
+    per-sequence initial states and cotangents resident in HBM, one
+    dr_backward_varlen call per step."""
+    import torch
+    import delta_rule_rnn_amd as dra
+    from delta_rule_rnn_amd.inputs import WORKLOADS, generate, packed_lengths
+
+    w0 = WORKLOADS[args.workload]
+    T = w0.B * w0.T
+    w = w0.with_(name=w0.name + "_packed", B=1, T=T)
+    lengths = packed_lengths(T, seed=7)
+    N = len(lengths)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = {n: (t.to(dev) if t is not None else None) for n, t in generate(w).items()}
+    sq = lambda t: None if t is None else t[0]
+    cu = torch.tensor([0] + list(torch.tensor(lengths).cumsum(0).tolist()), dtype=torch.int32).to(dev)
+    gen = torch.Generator().manual_seed(99)
+    do = torch.randn(T, w.H, w.Dv, generator=gen).to(d["q"].dtype).to(dev)
+    dhT = (torch.randn(N, w.H, w.Dk, w.Dv, generator=gen) * 0.1).to(dev)
+    h0 = (torch.randn(N, w.H, w.Dk, w.Dv, generator=gen) * 0.1).to(dev)
+    ws = torch.empty(dra.backward_varlen_workspace_bytes(w.kind, N, T, w.H, w.Dk, w.Dv, d["q"].dtype),
+                     dtype=torch.uint8, device=dev)
+    call = lambda: dra.backward_varlen(w.kind, sq(d["q"]), sq(d["k"]), sq(d["v"]), sq(d["g"]), sq(d["beta"]), cu,
+                                       h0, do, dhT, workspace=ws)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+    line = {
+        "metric": "packed-sequence bwd tokens/sec (1 GPU), all gradients", "value": round(T / (ms / 1000.0), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 compute, " + ("bf16" if d["q"].dtype == torch.bfloat16 else "f32") + " I/O",
+        "data": "synthetic",
+        "config": {"workload": f"{w.kind}_bwd_varlen N={N} T={T} H={w.H} dk={w.Dk} dv={w.Dv} C={w.C}",
+                   "sequences": N, "min_len": min(lengths), "max_len": max(lengths),
+                   "workspace_bytes": ws.numel(), "parallelism": "single GPU"},
+        "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def prologue_bench(args):
     """Forward with the fused input prologue on raw projections (the
     workload's sizes; q, k unnormalised, beta logits, and for scalar gates
@@ -324,7 +368,7 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens of the workload the CPU oracle is timed on")
     ap.add_argument("--cpu-threads", type=int, default=0)
-    ap.add_argument("--mode", choices=("prefill", "decode", "varlen", "prologue", "backward"), default="prefill",
+    ap.add_argument("--mode", choices=("prefill", "decode", "varlen", "prologue", "backward", "backward_varlen"), default="prefill",
                     help="prefill: the chunked forward (the benchmark line); decode: the "
                          "recurrent step on a serving-sized batch; varlen: the forward over "
                          "packed sequences of mixed lengths with the workload's token count; "
@@ -365,6 +409,9 @@ def main():
         return
     if args.mode == "backward":
         backward_bench(args)
+        return
+    if args.mode == "backward_varlen":
+        backward_varlen_bench(args)
         return
 
     import torch

@@ -39,6 +39,9 @@ SIGNATURES = {
     "dr_backward_prologue_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "dr_backward_prologue": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                   _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
+    "dr_backward_varlen_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i, _i]),
+    "dr_backward_varlen": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp, _vp]),
     "dr_chunk_cumsum": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "dr_kda_prep": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp]),
     "dr_intra": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp, _vp]),

@@ -71,6 +71,80 @@ struct Prep {
     static constexpr size_t FLOATS = GAM + (size_t)C * DK;
 };
 
+// Packed sequences (table == null: the dense [B, T] layout).  The chunk table
+// and sequence descriptors are those of the packed forward
+// (varlen_table_kernel): table[slot] = {sequence, first token, valid rows, -},
+// seqinfo[n] = {first slot, chunks, first token, tokens}; per-chunk arrays
+// are indexed h * maxchunks + slot.
+struct Pack {
+    const int4* table;
+    const int4* seqinfo;
+    const int* total;
+    int maxchunks;
+};
+
+// The chunk a chunk-parallel workgroup handles: its first token row (token
+// index times H plus h), its valid rows and its per-chunk array index; false
+// for a packed slot past the table's count.
+struct ChunkLoc {
+    size_t row0, ci;
+    int nvalid;
+};
+__device__ __forceinline__ bool locate_chunk(const Pack& pk, unsigned it, int H, int Tlen, int NT, ChunkLoc& L) {
+    const int h = (int)(it % (unsigned)H);
+    const unsigned tt = it / (unsigned)H;
+    if (pk.table) {
+        const int slot = (int)tt;
+        if (slot >= *pk.total) return false;
+        const int4 e = pk.table[slot];
+        L.row0 = (size_t)e.y * H + h;
+        L.nvalid = e.z;
+        L.ci = (size_t)h * pk.maxchunks + slot;
+    } else {
+        const int c = (int)(tt % (unsigned)NT), b = (int)(tt / (unsigned)NT);
+        L.row0 = ((size_t)b * Tlen + (size_t)c * C) * H + h;
+        L.nvalid = min(C, Tlen - c * C);
+        L.ci = ((size_t)b * H + h) * NT + c;
+    }
+    return true;
+}
+
+// The (sequence or batch) * H + head index of logical chain lc out of
+// nchains.  Packed sequences take chains head-major (lc = h * N + sequence),
+// so that each XCD's contiguous range of logical ids (xcd_logical) holds
+// every sequence for a few heads and the XCDs get equal token counts
+// whatever the lengths; the dense layout keeps (b, h) order.
+__device__ __forceinline__ int chain_of(const Pack& pk, int lc, int H, int nchains) {
+    if (!pk.table) return lc;
+    const int nseq = nchains / H;
+    return (lc % nseq) * H + lc / nseq;
+}
+
+// The chain a state-pass workgroup follows: chunks ci0 + c*cstep for
+// c = 0..nseg-1, tokens tok0 .. tok0 + tlim - 1 (token index; rows are
+// token * H + h).
+struct ChainLoc {
+    size_t ci0, tok0;
+    int nseg, tlim;
+};
+__device__ __forceinline__ ChainLoc locate_chain(const Pack& pk, int chain, int H, int Tlen, int NT) {
+    const int b = chain / H, h = chain % H;
+    ChainLoc L;
+    if (pk.table) {
+        const int4 si = pk.seqinfo[b];   // b is the sequence
+        L.ci0 = (size_t)h * pk.maxchunks + si.x;
+        L.nseg = si.y;
+        L.tok0 = (size_t)si.z;
+        L.tlim = si.w;
+    } else {
+        L.ci0 = (size_t)chain * NT;
+        L.nseg = NT;
+        L.tok0 = (size_t)b * Tlen;
+        L.tlim = Tlen;
+    }
+    return L;
+}
+
 // acc[16x16] += A[16 x K] * B[K x 16] on fp32 MFMA, A(r, k) = A[r*ar + k*ak],
 // B(k, c) = B[k*bk + c*bc].  At step k0 lane l supplies A(l%16, k0 + l/16)
 // and B(k0 + l/16, l%16); the result is in the accumulator layout (lane l:
@@ -188,7 +262,7 @@ template <int KIND, typename T, int DK>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                        const T* __restrict__ v, const float* __restrict__ g,
                                                        const float* __restrict__ beta, float* __restrict__ prep,
-                                                       int Tlen, int H, int NT)
+                                                       int Tlen, int H, int NT, Pack pk)
 {
     using P = Prep<DK>;
     using SM = PrepSmem<KIND, T, DK>;
@@ -206,13 +280,11 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
     float* sPhi = smem + SM::SPHI;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const unsigned it = blockIdx.x;
-    const int h = (int)(it % (unsigned)H);
-    const unsigned tt = it / (unsigned)H;
-    const int c = (int)(tt % (unsigned)NT), b = (int)(tt / (unsigned)NT);
-    const int nvalid = min(C, Tlen - c * C);
-    const size_t row0 = ((size_t)b * Tlen + (size_t)c * C) * H + h;   // token row of position 0
-    float* out = prep + (((size_t)b * H + h) * NT + c) * P::FLOATS;
+    ChunkLoc loc;
+    if (!locate_chunk(pk, blockIdx.x, H, Tlen, NT, loc)) return;
+    const int nvalid = loc.nvalid;
+    const size_t row0 = loc.row0;   // token row of position 0
+    float* out = prep + loc.ci * P::FLOATS;
 
     // ---- inputs, rows past the end of a ragged chunk zero
     #pragma unroll 8
@@ -469,7 +541,7 @@ template <int KIND, int DK>
 __global__ __launch_bounds__(kStateThreads) void bwd_state_fwd_kernel(const float* __restrict__ prep,
                                                                       const float* __restrict__ h0,
                                                                       float* __restrict__ hs, float* __restrict__ vn,
-                                                                      int H, int NT)
+                                                                      int H, int NT, int Tlen, Pack pk)
 {
     using P = Prep<DK>;
     using SM = StateSmem<DK>;
@@ -486,7 +558,8 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_fwd_kernel(const floa
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool storer = tid >= 256;
     const int logical = xcd_logical(blockIdx.x, gridDim.x);
-    const int chain = logical / NVS, dv0 = (logical % NVS) * kSV;
+    const int chain = chain_of(pk, logical / NVS, H, (int)gridDim.x / NVS), dv0 = (logical % NVS) * kSV;
+    const ChainLoc cl = locate_chain(pk, chain, H, Tlen, NT);
     if (!storer) {
 #pragma unroll
         for (int it_ = 0; it_ < (DK * kSV) / 256; ++it_) {
@@ -495,8 +568,8 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_fwd_kernel(const floa
         }
     }
     lds_barrier();
-    for (int c = 0; c < NT; ++c) {
-        const size_t ci = (size_t)chain * NT + c;
+    for (int c = 0; c < cl.nseg; ++c) {
+        const size_t ci = cl.ci0 + c;
         const float* pc = prep + ci * P::FLOATS;
         // (A)
         if (!storer) {
@@ -517,7 +590,7 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_fwd_kernel(const floa
         lds_barrier();
         // (B) Vnew = U - W S: 4 tiles, one per compute wave
         if (!storer) {
-            if (c + 1 < NT) {
+            if (c + 1 < cl.nseg) {
                 const float* pn = pc + P::FLOATS;
                 if constexpr (DELTA) l2_touch(pn + P::W, DK, C, DK, tid, 256, sink);
                 l2_touch(pn + P::KB, DK, C, DK, tid, 256, sink);
@@ -562,7 +635,7 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_rev_kernel(const floa
                                                                       float* __restrict__ dhs,
                                                                       float* __restrict__ dvn,
                                                                       float* __restrict__ dh0, int Tlen, int H,
-                                                                      int NT)
+                                                                      int NT, Pack pk)
 {
     using P = Prep<DK>;
     using SM = StateSmem<DK>;
@@ -582,8 +655,9 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_rev_kernel(const floa
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool storer = tid >= 256;
     const int logical = xcd_logical(blockIdx.x, gridDim.x);
-    const int chain = logical / NVS, dv0 = (logical % NVS) * kSV;
-    const int b = chain / H, h = chain % H;
+    const int chain = chain_of(pk, logical / NVS, H, (int)gridDim.x / NVS), dv0 = (logical % NVS) * kSV;
+    const int h = chain % H;
+    const ChainLoc cl = locate_chain(pk, chain, H, Tlen, NT);
     if (!storer) {
 #pragma unroll
         for (int it_ = 0; it_ < (DK * kSV) / 256; ++it_) {
@@ -592,8 +666,8 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_rev_kernel(const floa
         }
     }
     lds_barrier();
-    for (int c = NT - 1; c >= 0; --c) {
-        const size_t ci = (size_t)chain * NT + c;
+    for (int c = cl.nseg - 1; c >= 0; --c) {
+        const size_t ci = cl.ci0 + c;
         const float* pc = prep + ci * P::FLOATS;
         // (A)
         if (!storer) {
@@ -611,7 +685,7 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_rev_kernel(const floa
             for (int it_ = 0; it_ < NDO; ++it_) {
                 const int idx = tid + it_ * 256, r = idx / kSV, cc = idx % kSV;
                 const int tok = c * C + r;
-                xo[it_] = to_f(dout[(((size_t)b * Tlen + min(tok, Tlen - 1)) * H + h) * DV + dv0 + cc]);
+                xo[it_] = to_f(dout[((cl.tok0 + min(tok, cl.tlim - 1)) * H + h) * DV + dv0 + cc]);
             }
             ga.store(sAqk, LCT, tid);
             gk.store(sKb, LDN, tid);
@@ -621,7 +695,7 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_rev_kernel(const floa
 #pragma unroll
             for (int it_ = 0; it_ < NDO; ++it_) {
                 const int idx = tid + it_ * 256, r = idx / kSV, cc = idx % kSV;
-                sDO[r * LSV + cc] = c * C + r < Tlen ? xo[it_] : 0.f;
+                sDO[r * LSV + cc] = c * C + r < cl.tlim ? xo[it_] : 0.f;
             }
         } else {
             unstage<DK, kSV, 64>(dhs + ci * DK * DV + dv0, DV, sD, LSV, tid - 256);
@@ -701,7 +775,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     const T* __restrict__ dout, const float* __restrict__ prep, const float* __restrict__ hs,
     const float* __restrict__ dhs, const float* __restrict__ vn, const float* __restrict__ dvn,
     T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv, float* __restrict__ dg, float* __restrict__ dbeta,
-    int Tlen, int H, int NT)
+    int Tlen, int H, int NT, Pack pk)
 {
     using P = Prep<DK>;
     using SM = GradSmem<DK>;
@@ -721,13 +795,11 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     float* sBt = smem + SM::BT;      // beta, zero past the end and for decay_la
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const unsigned it = blockIdx.x;
-    const int h = (int)(it % (unsigned)H);
-    const unsigned tt = it / (unsigned)H;
-    const int c = (int)(tt % (unsigned)NT), b = (int)(tt / (unsigned)NT);
-    const int nvalid = min(C, Tlen - c * C);
-    const size_t row0 = ((size_t)b * Tlen + (size_t)c * C) * H + h;
-    const size_t ci = ((size_t)b * H + h) * NT + c;
+    ChunkLoc loc;
+    if (!locate_chunk(pk, blockIdx.x, H, Tlen, NT, loc)) return;
+    const int nvalid = loc.nvalid;
+    const size_t row0 = loc.row0;
+    const size_t ci = loc.ci;
     const float* pc = prep + ci * P::FLOATS;
 
     // owned tiles of every [C][DK] result: t = wave + 8 m

@@ -411,9 +411,10 @@ dr_status decode(int kind, const void* q, const void* k, const void* v, const fl
 struct BwdLayout {
     size_t prep, hs, dhs, vn, dvn, bytes;
 };
-BwdLayout bwd_layout(int B, int T, int H, int D) {
+// n = number of per-chunk entries (dense: B * H * ceil(T/C); packed:
+// H * maxchunks)
+BwdLayout bwd_layout_n(size_t n, int D) {
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-    const size_t n = (size_t)B * H * (size_t)ceil_div(T, dr::kChunk);
     const size_t pf = D == 64 ? dr::bw::Prep<64>::FLOATS : dr::bw::Prep<128>::FLOATS;
     BwdLayout L;
     L.prep = 0;
@@ -424,7 +425,12 @@ BwdLayout bwd_layout(int B, int T, int H, int D) {
     L.bytes = L.dvn + up(n * dr::kChunk * D * 4);
     return L;
 }
+BwdLayout bwd_layout(int B, int T, int H, int D) {
+    return bwd_layout_n((size_t)B * H * (size_t)ceil_div(T, dr::kChunk), D);
+}
 
+// B is the sequence count for packed sequences (pk.table set; T is then the
+// packed token count and the tensors have a batch of one).
 struct BwdArgs {
     const void *q, *k, *v, *dout;
     const float *g, *beta, *h0, *dhT;
@@ -433,6 +439,7 @@ struct BwdArgs {
     int B, T, H, NT;
     uint8_t* ws;
     BwdLayout L;
+    dr::bw::Pack pk;
 };
 
 template <int KIND, typename E, int D>
@@ -447,22 +454,22 @@ dr_status launch_backward_t(const BwdArgs& a, hipStream_t st) {
     const E* k = static_cast<const E*>(a.k);
     const E* v = static_cast<const E*>(a.v);
     const E* dout = static_cast<const E*>(a.dout);
-    const long long items = (long long)a.B * a.NT * a.H;
+    const long long items = a.pk.table ? (long long)a.pk.maxchunks * a.H : (long long)a.B * a.NT * a.H;
     const long long slices = (long long)a.B * a.H * (D / kSV);
     if (items > 0x7fffffffLL || slices > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
     hipLaunchKernelGGL((bwd_prep_kernel<KIND, E, D>), dim3((unsigned)items), dim3(256), 0, st, q, k, v, a.g, a.beta,
-                       prep, a.T, a.H, a.NT);
+                       prep, a.T, a.H, a.NT, a.pk);
     dr_status s = check_launch();
     if (s != DR_OK) return s;
     hipLaunchKernelGGL((bwd_state_fwd_kernel<KIND, D>), dim3((unsigned)slices), dim3(kStateThreads), 0, st, prep, a.h0, hs, vn,
-                       a.H, a.NT);
+                       a.H, a.NT, a.T, a.pk);
     if ((s = check_launch()) != DR_OK) return s;
     hipLaunchKernelGGL((bwd_state_rev_kernel<KIND, E, D>), dim3((unsigned)slices), dim3(kStateThreads), 0, st, prep, dout, a.dhT,
-                       dhs, dvn, a.dh0, a.T, a.H, a.NT);
+                       dhs, dvn, a.dh0, a.T, a.H, a.NT, a.pk);
     if ((s = check_launch()) != DR_OK) return s;
     hipLaunchKernelGGL((bwd_grad_kernel<KIND, E, D>), dim3((unsigned)items), dim3(512), 0, st, q, k, v, a.beta, dout,
                        prep, hs, dhs, vn, dvn, static_cast<E*>(a.dq), static_cast<E*>(a.dk), static_cast<E*>(a.dv),
-                       a.dg, a.dbeta, a.T, a.H, a.NT);
+                       a.dg, a.dbeta, a.T, a.H, a.NT, a.pk);
     return check_launch();
 }
 
@@ -471,7 +478,9 @@ dr_status launch_backward_t(const BwdArgs& a, hipStream_t st) {
 struct ProBwdLayout {
     size_t qh, kh, gh, bh, core, bytes;
 };
-ProBwdLayout probwd_layout(int kind, int B, int T, int H, int D, int dtype) {
+// core: the bytes of what follows the prologue's part (the backward's own
+// workspace, with the chunk table first for packed sequences)
+ProBwdLayout probwd_layout(int kind, int B, int T, int H, int D, int dtype, size_t core) {
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     const size_t n = (size_t)B * T * H, esz = dtype == DR_BF16 ? 2 : 4;
     ProBwdLayout L;
@@ -480,7 +489,7 @@ ProBwdLayout probwd_layout(int kind, int B, int T, int H, int D, int dtype) {
     L.gh = L.kh + up(n * D * esz);
     L.bh = L.gh + up(n * (kind == DR_KIND_KDA ? D : 1) * 4);
     L.core = L.bh + up(n * 4);
-    L.bytes = L.core + bwd_layout(B, T, H, D).bytes;
+    L.bytes = L.core + core;
     return L;
 }
 
@@ -528,6 +537,102 @@ dr_status launch_backward_k(const BwdArgs& a, int D, int dtype, hipStream_t st) 
     return launch_backward_t<KIND, float, 128>(a, st);
 }
 
+// Backward for the dense layout (cu_seqlens == null, B batches) or packed
+// sequences (cu_seqlens set, N sequences, B == 1), with or without a
+// prologue.  Workspace: [prologue part][chunk table (packed)][core].
+dr_status backward_impl(int kind, const void* q, const void* k, const void* v, const float* g, const float* beta,
+                        const int* cu_seqlens, int N, const float* h0, const void* dout, const float* dhT, void* dq,
+                        void* dk, void* dv, float* dg, float* dbeta, float* dh0, float* dA_log, float* ddt_bias,
+                        int B, int T, int H, int Dk, int Dv, int C, int dtype, const dr_prologue* prologue,
+                        void* workspace, size_t workspace_bytes, unsigned* flags, void* stream) {
+    dr_status s = validate(kind, q, k, v, g, beta, B, T, H, Dk, Dv, C, dtype);
+    if (s != DR_OK) return s;
+    dr::Prologue pr;
+    bool use_pro;
+    if ((s = resolve_prologue(kind, prologue, &pr, &use_pro)) != DR_OK) return s;
+    const bool delta = kind != DR_KIND_DECAY_LA;
+    const bool packed = cu_seqlens != nullptr;
+    const int chains = packed ? N : B;
+    const bool gate = use_pro && (pr.ops & dr::PRO_GATE);
+    if (T > 0 && (!dout || !dq || !dk || !dv || !dg || (delta && !dbeta))) return DR_ERR_INVALID_ARG;
+    if (gate && (!dA_log || (pr.dt_bias && !ddt_bias))) return DR_ERR_INVALID_ARG;
+    const void* ptrs[] = {h0, dout, dhT, dq, dk, dv, dg, dbeta, dh0, workspace};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return DR_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(dA_log) & 3u) || (reinterpret_cast<uintptr_t>(ddt_bias) & 3u))
+        return DR_ERR_INVALID_ARG;
+    if ((long long)chains * H * (Dv / 16) > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
+    // workspace: [prologue part][chunk table (packed)][core]; every check
+    // before the first launch
+    VarlenLayout V{};
+    size_t table_bytes = 0;
+    BwdLayout L;
+    if (packed) {
+        V = varlen_layout(N, T, H, Dk, dtype);
+        table_bytes = V.bytes - V.table;
+        L = bwd_layout_n((size_t)H * V.maxchunks, Dk);
+    } else {
+        L = bwd_layout(B, T, H, Dk);
+    }
+    const size_t core_bytes = table_bytes + L.bytes;
+    const ProBwdLayout PL = probwd_layout(kind, B, T, H, Dk, dtype, core_bytes);
+    if (T > 0 && (!workspace || workspace_bytes < (use_pro ? PL.bytes : core_bytes))) return DR_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (gate) {
+        // accumulated below (or left zero without tokens)
+        hipLaunchKernelGGL(dr::copy_or_zero_kernel, dim3(((size_t)H + 255) / 256), dim3(256), 0, st, dA_log,
+                           (const float*)nullptr, (size_t)H);
+        if (ddt_bias)
+            hipLaunchKernelGGL(dr::copy_or_zero_kernel, dim3(((size_t)H + 255) / 256), dim3(256), 0, st, ddt_bias,
+                               (const float*)nullptr, (size_t)H);
+        if ((s = check_launch()) != DR_OK) return s;
+    }
+    if (T == 0) {
+        // no tokens: dh0 = dhT (or zero); nothing else to write
+        if (!dh0) return DR_OK;
+        const size_t n = (size_t)chains * H * Dk * Dv;
+        hipLaunchKernelGGL(dr::copy_or_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dh0, dhT, n);
+        return check_launch();
+    }
+    uint8_t* w = static_cast<uint8_t*>(workspace);
+    uint8_t* rest = use_pro ? w + PL.core : w;     // [chunk table][core]
+    dr::bw::Pack pk{nullptr, nullptr, nullptr, 0};
+    if (packed) {
+        // the chunk table of the packed forward, rebased to this workspace
+        int4* table = reinterpret_cast<int4*>(rest);
+        int4* seqinfo = reinterpret_cast<int4*>(rest + (V.seqinfo - V.table));
+        int* total = reinterpret_cast<int*>(rest + (V.total - V.table));
+        hipLaunchKernelGGL(dr::varlen_table_kernel, dim3(1), dim3(1024), 0, st, cu_seqlens, N, T, V.maxchunks, table,
+                           seqinfo, total, flags);
+        if ((s = check_launch()) != DR_OK) return s;
+        pk = dr::bw::Pack{table, seqinfo, total, V.maxchunks};
+    }
+    // the recurrence's inputs: the caller's, or the prologue's outputs
+    const void *rq = q, *rk = k;
+    const float *rg = g, *rb = delta ? beta : nullptr;
+    if (use_pro) {
+        void* qh = w + PL.qh;
+        void* kh = w + PL.kh;
+        float* gh = reinterpret_cast<float*>(w + PL.gh);
+        float* bh = delta ? reinterpret_cast<float*>(w + PL.bh) : nullptr;
+        s = launch_prologue(false, kind, Dk, dtype, q, k, g, rb, qh, kh, gh, bh, nullptr, nullptr, nullptr, nullptr,
+                            nullptr, nullptr, B, T, H, pr, st);
+        if (s != DR_OK) return s;
+        rq = qh; rk = kh; rg = gh; rb = bh;
+    }
+    BwdArgs a{rq, rk, v, dout, rg, rb, h0, dhT, dq, dk, dv, dg, delta ? dbeta : nullptr, dh0,
+              chains, T, H, ceil_div(T, dr::kChunk), rest + table_bytes, L, pk};
+    switch (kind) {
+        case DR_KIND_KDA: s = launch_backward_k<dr::KIND_KDA>(a, Dk, dtype, st); break;
+        case DR_KIND_GDN: s = launch_backward_k<dr::KIND_GDN>(a, Dk, dtype, st); break;
+        default: s = launch_backward_k<dr::KIND_LA>(a, Dk, dtype, st); break;
+    }
+    if (s != DR_OK || !use_pro) return s;
+    // gradients with respect to the raw inputs, in place
+    return launch_prologue(true, kind, Dk, dtype, q, k, g, delta ? beta : nullptr, nullptr, nullptr, nullptr,
+                           nullptr, dq, dk, dg, delta ? dbeta : nullptr, dA_log, ddt_bias, B, T, H, pr, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -549,7 +654,7 @@ dr_status dr_backward(int kind, const void* q, const void* k, const void* v, con
 size_t dr_backward_prologue_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, int C, int dtype) {
     if (kind < 0 || kind > 2 || B <= 0 || H <= 0 || T < 0) return 0;
     if (dr_record_bytes(Dk, Dv, C, dtype) == 0) return 0;
-    return probwd_layout(kind, B, T, H, Dk, dtype).bytes;
+    return probwd_layout(kind, B, T, H, Dk, dtype, bwd_layout(B, T, H, Dk).bytes).bytes;
 }
 
 dr_status dr_backward_prologue(int kind, const void* q, const void* k, const void* v, const float* g,
@@ -557,69 +662,29 @@ dr_status dr_backward_prologue(int kind, const void* q, const void* k, const voi
                                void* dk, void* dv, float* dg, float* dbeta, float* dh0, float* dA_log,
                                float* ddt_bias, int B, int T, int H, int Dk, int Dv, int C, int dtype,
                                const dr_prologue* prologue, void* workspace, size_t workspace_bytes, void* stream) {
-    dr_status s = validate(kind, q, k, v, g, beta, B, T, H, Dk, Dv, C, dtype);
-    if (s != DR_OK) return s;
-    dr::Prologue pr;
-    bool use_pro;
-    if ((s = resolve_prologue(kind, prologue, &pr, &use_pro)) != DR_OK) return s;
-    const bool delta = kind != DR_KIND_DECAY_LA;
-    const bool gate = use_pro && (pr.ops & dr::PRO_GATE);
-    if (T > 0 && (!dout || !dq || !dk || !dv || !dg || (delta && !dbeta))) return DR_ERR_INVALID_ARG;
-    if (gate && (!dA_log || (pr.dt_bias && !ddt_bias))) return DR_ERR_INVALID_ARG;
-    const void* ptrs[] = {h0, dout, dhT, dq, dk, dv, dg, dbeta, dh0, workspace};
-    for (const void* p : ptrs)
-        if (!aligned16(p)) return DR_ERR_INVALID_ARG;
-    if ((reinterpret_cast<uintptr_t>(dA_log) & 3u) || (reinterpret_cast<uintptr_t>(ddt_bias) & 3u))
-        return DR_ERR_INVALID_ARG;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if (gate) {
-        // accumulated below (or left zero without tokens)
-        hipLaunchKernelGGL(dr::copy_or_zero_kernel, dim3(((size_t)H + 255) / 256), dim3(256), 0, st, dA_log,
-                           (const float*)nullptr, (size_t)H);
-        if (ddt_bias)
-            hipLaunchKernelGGL(dr::copy_or_zero_kernel, dim3(((size_t)H + 255) / 256), dim3(256), 0, st, ddt_bias,
-                               (const float*)nullptr, (size_t)H);
-        if ((s = check_launch()) != DR_OK) return s;
-    }
-    if (T == 0) {
-        // no tokens: dh0 = dhT (or zero); nothing else to write
-        if (!dh0) return DR_OK;
-        const size_t n = (size_t)B * H * Dk * Dv;
-        hipLaunchKernelGGL(dr::copy_or_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dh0, dhT, n);
-        return check_launch();
-    }
-    uint8_t* w = static_cast<uint8_t*>(workspace);
-    const ProBwdLayout PL = probwd_layout(kind, B, T, H, Dk, dtype);
-    const BwdLayout L = bwd_layout(B, T, H, Dk);
-    if (!workspace || workspace_bytes < (use_pro ? PL.bytes : L.bytes)) return DR_ERR_WORKSPACE;
-    // the recurrence's inputs: the caller's, or the prologue's outputs
-    const void *rq = q, *rk = k;
-    const float *rg = g, *rb = delta ? beta : nullptr;
-    uint8_t* core = w;
-    if (use_pro) {
-        void* qh = w + PL.qh;
-        void* kh = w + PL.kh;
-        float* gh = reinterpret_cast<float*>(w + PL.gh);
-        float* bh = delta ? reinterpret_cast<float*>(w + PL.bh) : nullptr;
-        s = launch_prologue(false, kind, Dk, dtype, q, k, g, rb, qh, kh, gh, bh, nullptr, nullptr, nullptr, nullptr,
-                            nullptr, nullptr, B, T, H, pr, st);
-        if (s != DR_OK) return s;
-        rq = qh; rk = kh; rg = gh; rb = bh;
-        core = w + PL.core;
-    }
-    BwdArgs a{rq, rk, v, dout, rg, rb, h0, dhT, dq, dk, dv, dg, delta ? dbeta : nullptr, dh0,
-              B, T, H, ceil_div(T, dr::kChunk), core, L};
-    switch (kind) {
-        case DR_KIND_KDA: s = launch_backward_k<dr::KIND_KDA>(a, Dk, dtype, st); break;
-        case DR_KIND_GDN: s = launch_backward_k<dr::KIND_GDN>(a, Dk, dtype, st); break;
-        default: s = launch_backward_k<dr::KIND_LA>(a, Dk, dtype, st); break;
-    }
-    if (s != DR_OK || !use_pro) return s;
-    // gradients with respect to the raw inputs, in place
-    return launch_prologue(true, kind, Dk, dtype, q, k, g, delta ? beta : nullptr, nullptr, nullptr, nullptr,
-                           nullptr, dq, dk, dg, delta ? dbeta : nullptr, dA_log, ddt_bias, B, T, H, pr, st);
+    return backward_impl(kind, q, k, v, g, beta, nullptr, B, h0, dout, dhT, dq, dk, dv, dg, dbeta, dh0, dA_log,
+                         ddt_bias, B, T, H, Dk, Dv, C, dtype, prologue, workspace, workspace_bytes, nullptr, stream);
 }
 
+size_t dr_backward_varlen_workspace_bytes(int kind, int N, int T, int H, int Dk, int Dv, int C, int dtype,
+                                          int with_prologue) {
+    if (kind < 0 || kind > 2 || N < 1 || H <= 0 || T < 0) return 0;
+    if (dr_record_bytes(Dk, Dv, C, dtype) == 0) return 0;
+    const VarlenLayout V = varlen_layout(N, T, H, Dk, dtype);
+    const size_t core = (V.bytes - V.table) + bwd_layout_n((size_t)H * V.maxchunks, Dk).bytes;
+    return with_prologue ? probwd_layout(kind, 1, T, H, Dk, dtype, core).bytes : core;
+}
+
+dr_status dr_backward_varlen(int kind, const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, const int* cu_seqlens, int N, const float* h0, const void* dout,
+                             const float* dhT, void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dh0,
+                             float* dA_log, float* ddt_bias, int T, int H, int Dk, int Dv, int C, int dtype,
+                             const dr_prologue* prologue, void* workspace, size_t workspace_bytes, unsigned* flags,
+                             void* stream) {
+    if (N < 1 || !cu_seqlens || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return DR_ERR_INVALID_ARG;
+    return backward_impl(kind, q, k, v, g, beta, cu_seqlens, N, h0, dout, dhT, dq, dk, dv, dg, dbeta, dh0, dA_log,
+                         ddt_bias, 1, T, H, Dk, Dv, C, dtype, prologue, workspace, workspace_bytes, flags, stream);
+}
 
 size_t dr_record_bytes(int Dk, int Dv, int C, int dtype) {
     if (Dk != Dv || (Dk != 64 && Dk != 128) || C != dr::kChunk) return 0;
@@ -805,6 +870,6 @@ const char* dr_status_string(int status) {
     }
 }
 
-int dr_abi_version(void) { return 4; }
+int dr_abi_version(void) { return 5; }
 
 }  // extern "C"

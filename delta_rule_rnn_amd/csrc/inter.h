@@ -201,7 +201,12 @@ __global__ __launch_bounds__(inter_threads<PFD>()) void inter_kernel(const uint8
     const int G = gridDim.x, bid = blockIdx.x;
     const int logical = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
     const int chain = logical / NV, slice = logical % NV;
-    const int b = chain / H, h = chain % H;
+    // packed sequences take chains head-major (chain = h * N + sequence), so
+    // that each XCD's contiguous range of logical ids holds every sequence
+    // for a few heads and the XCDs get equal token counts whatever the
+    // lengths; the dense layout is (b, h) as stored
+    const int nseq = G / (NV * H);
+    const int b = VARLEN ? chain % nseq : chain / H, h = VARLEN ? chain / nseq : chain % H;
     const int dv0 = slice * DVS;
 
     // this launch runs nseg chunks of the chain from its record chain_rec on,

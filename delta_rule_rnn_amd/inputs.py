@@ -35,7 +35,7 @@ from __future__ import annotations
 
 import math
 from dataclasses import dataclass, replace
-from typing import Dict, Optional
+from typing import Dict, List, Optional
 
 import torch
 
@@ -153,3 +153,15 @@ def generate_raw(w: Workload, device: Optional[str] = None) -> Dict[str, Optiona
     if device is not None:
         out = {n: (t.to(device) if t is not None else None) for n, t in out.items()}
     return out
+
+
+def packed_lengths(T: int, seed: int = 7, lo: int = 64, hi: int = 4096) -> List[int]:
+    """Sequence lengths for a packed batch of T tokens: seeded draws uniform
+    in [lo, hi] until T is used up (the last sequence takes the remainder)."""
+    rng = torch.Generator().manual_seed(seed)
+    lengths, left = [], T
+    while left > 0:
+        n = min(left, int(torch.randint(lo, hi + 1, (1,), generator=rng).item()))
+        lengths.append(n)
+        left -= n
+    return lengths

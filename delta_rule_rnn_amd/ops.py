@@ -390,6 +390,80 @@ def backward(kind: str, q, k, v, g, beta=None, h0=None, do=None, dhT=None, chunk
     return dq, dk, dv, dg, dbeta, dh0, dA_log, ddt
 
 
+def backward_varlen_workspace_bytes(kind: str, N: int, T: int, H: int, Dk: int, Dv: int, dtype: torch.dtype,
+                                    chunk_size: int = CHUNK, with_prologue: bool = False) -> int:
+    code = DR_BF16 if dtype == torch.bfloat16 else DR_F32
+    return int(_lib.load().dr_backward_varlen_workspace_bytes(KINDS[kind], N, T, H, Dk, Dv, chunk_size, code,
+                                                              int(with_prologue)))
+
+
+def backward_varlen(kind: str, q, k, v, g, beta=None, cu_seqlens=None, h0=None, do=None, dhT=None,
+                    chunk_size=CHUNK, workspace=None, flags=None, stream=None,
+                    prologue: Optional[Prologue] = None):
+    """Backward of forward_varlen: sequences packed along the token axis,
+    q, k [T,H,Dk] (or [1,T,H,Dk]), v and do [T,H,Dv], g [T,H,Dk] (kda) or
+    [T,H], beta [T,H], cu_seqlens int32 [N+1] on the device, h0 and dhT
+    [N,H,Dk,Dv] fp32 or None.  Returns what backward() returns, the token
+    tensors with the leading 1 kept when q has it and dh0 [N,H,Dk,Dv]."""
+    lib = _lib.load()
+    if cu_seqlens is None:
+        raise DeltaRuleError("cu_seqlens is required")
+    squeeze = q.dim() == 4
+    if squeeze:
+        if q.shape[0] != 1:
+            raise DeltaRuleError("packed sequences take q as [T,H,D] or [1,T,H,D]")
+        q, k, v, g = q[0], k[0], v[0], g[0]
+        beta = None if beta is None else beta[0]
+        do = None if do is None else do[0]
+    T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    _need(q, "q"); _need(k, "k", dt, q.shape); _need(v, "v", dt, (T, H, Dv))
+    _need(g, "g", torch.float32, (T, H, Dk) if kind == "kda" else (T, H))
+    if kind != "decay_la":
+        if beta is None:
+            raise DeltaRuleError("beta is required")
+        _need(beta, "beta", torch.float32, (T, H))
+    else:
+        beta = None
+    if do is None:
+        raise DeltaRuleError("do (the adjoint of o) is required")
+    _need(do, "do", dt, (T, H, Dv))
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise DeltaRuleError("cu_seqlens must be int32 [N+1] with N >= 1")
+    N = cu_seqlens.numel() - 1
+    _need(h0, "h0", torch.float32, (N, H, Dk, Dv))
+    _need(dhT, "dhT", torch.float32, (N, H, Dk, Dv))
+    if flags is not None:
+        _need(flags, "flags", torch.int32, (1,))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg = torch.empty_like(g)
+    dbeta = torch.empty_like(beta) if beta is not None else None
+    dh0 = torch.empty(N, H, Dk, Dv, dtype=torch.float32, device=q.device)
+    code = DR_BF16 if dt == torch.bfloat16 else DR_F32
+    need = backward_varlen_workspace_bytes(kind, N, T, H, Dk, Dv, dt, chunk_size, prologue is not None)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8)
+    gate = prologue is not None and prologue.A_log is not None
+    dA_log = torch.empty(H, dtype=torch.float32, device=q.device) if gate else None
+    ddt = torch.empty(H, dtype=torch.float32, device=q.device) if gate and prologue.dt_bias is not None else None
+    keep, pro = _pro_arg(prologue, H)
+    st = lib.dr_backward_varlen(KINDS[kind], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N,
+                                _ptr(h0), _ptr(do), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta),
+                                _ptr(dh0), _ptr(dA_log), _ptr(ddt), T, H, Dk, Dv, chunk_size, code, pro,
+                                _ptr(workspace), workspace.numel(), _ptr(flags), _stream(stream))
+    del keep
+    _check(st, "dr_backward_varlen")
+    if squeeze:
+        dq, dk, dv, dg = dq[None], dk[None], dv[None], dg[None]
+        dbeta = None if dbeta is None else dbeta[None]
+    if prologue is None:
+        return dq, dk, dv, dg, dbeta, dh0
+    return dq, dk, dv, dg, dbeta, dh0, dA_log, ddt
+
+
 # ---- individual steps ------------------------------------------------------
 
 def chunk_cumsum(g: torch.Tensor, chunk_size: int = CHUNK, stream=None) -> torch.Tensor:

@@ -271,8 +271,10 @@ dr_status dr_decode(int kind, const void* q, const void* k, const void* v, const
  *   workspace: at least dr_backward_workspace_bytes(...): the recomputed
  *          fp32 chunk operands, the chunk entry states and exit adjoints
  *          (fp32 [Dk,Dv] per chunk) and Vnew / dVnew per chunk
- * All arithmetic is fp32.  Other conventions and errors as for kda_fwd.
- * T = 0 writes dh0 = dhT (or zero) and nothing else.
+ * All arithmetic is fp32.  dbeta and dg are sums of per-wave partials added
+ * in shared memory in no fixed order, so repeated calls may differ in their
+ * last bits; dq, dk, dv and dh0 are reproducible.  Other conventions and
+ * errors as for kda_fwd.  T = 0 writes dh0 = dhT (or zero) and nothing else.
  */
 size_t dr_backward_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, int C, int dtype);
 dr_status dr_backward(int kind, const void* q, const void* k, const void* v, const float* g,
@@ -314,6 +316,40 @@ dr_status dr_backward_prologue(int kind, const void* q, const void* k, const voi
                                int B, int T, int H, int Dk, int Dv, int C, int dtype,
                                const dr_prologue* prologue, void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/*
+ * Backward of the packed-sequence forward (dr_forward_varlen): N sequences
+ * concatenated along the token axis, each with its own state chain; chunks
+ * never straddle two sequences ("Gated DeltaNet", section "反向传播：状态伴随
+ * 与三角变换梯度", run per sequence as the packed forward runs).  The
+ * gradients of each sequence are those dr_backward(_prologue) gives for that
+ * sequence alone.
+ *   q, k, v, g, beta, dout, dq, dk, dv, dg, dbeta: as for dr_backward with
+ *          B = 1 and T the packed token count
+ *   cu_seqlens: DEVICE int [N+1] token offsets, 0 = cu[0] <= ... <= cu[N] = T
+ *          (4-byte aligned).  Offsets are clamped into [0, T] and made
+ *          non-decreasing on the device; malformed ones raise
+ *          DR_FLAG_BAD_SEQLENS in *flags (flags may be NULL).
+ *   h0, dhT, dh0: [N,H,Dk,Dv] float, one state per sequence (may be NULL)
+ *   dA_log, ddt_bias, prologue: as for dr_backward_prologue (prologue NULL:
+ *          the plain path; dA_log / ddt_bias then ignored)
+ *   workspace: at least dr_backward_varlen_workspace_bytes(kind, N, T, H,
+ *          Dk, Dv, C, dtype, with_prologue), with_prologue nonzero when a
+ *          prologue that does something is passed: the chunk table and
+ *          sequence descriptors, then dr_backward's per-chunk buffers for
+ *          ceil(T/C) + N chunk slots per head (plus the prologue's part).
+ * A sequence of length 0 gets dh0 = dhT (or zero).  Other conventions and
+ * errors as for dr_backward.
+ */
+size_t dr_backward_varlen_workspace_bytes(int kind, int N, int T, int H, int Dk, int Dv, int C, int dtype,
+                                          int with_prologue);
+dr_status dr_backward_varlen(int kind, const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, const int* cu_seqlens, int N, const float* h0,
+                             const void* dout, const float* dhT, void* dq, void* dk, void* dv, float* dg,
+                             float* dbeta, float* dh0, float* dA_log, float* ddt_bias,
+                             int T, int H, int Dk, int Dv, int C, int dtype,
+                             const dr_prologue* prologue, void* workspace, size_t workspace_bytes,
+                             unsigned* flags, void* stream);
 
 /* ---- the individual steps ---------------------------------------------- */
 
@@ -390,8 +426,9 @@ size_t dr_record_bytes(int Dk, int Dv, int C, int dtype);
 /* Human-readable text for a status code (static storage). */
 const char* dr_status_string(int status);
 
-/* ABI version of this library: 4 (1, plus the prologue entry points in 2, the
- * backward in 3, the backward through the prologue in 4). */
+/* ABI version of this library: 5 (1, plus the prologue entry points in 2, the
+ * backward in 3, the backward through the prologue in 4, the packed-sequence
+ * backward in 5). */
 int dr_abi_version(void);
 
 #ifdef __cplusplus

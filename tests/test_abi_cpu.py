@@ -38,7 +38,7 @@ def test_header_and_binding_agree():
 def test_every_declared_symbol_is_exported(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.dr_abi_version() == 4
+    assert lib.dr_abi_version() == 5
 
 
 def test_status_strings(lib):
@@ -168,6 +168,32 @@ def test_backward_rejects(lib):
     assert bwd(dg=None) == -1
     assert bwd(dbeta=None) == -1                 # gdn needs dbeta
     assert bwd(q=FAKE + 8) == -1                 # misaligned
+    assert bwd(D=96) == -2
+    assert bwd(ws=None) == -4
+    assert bwd(wsb=need - 1) == -4
+
+
+def test_backward_varlen_rejects(lib):
+    """dr_backward_varlen refuses bad arguments on the host, before any launch."""
+    need = lib.dr_backward_varlen_workspace_bytes(1, 3, 200, 2, 64, 64, 64, 1, 0)
+    with_pro = lib.dr_backward_varlen_workspace_bytes(1, 3, 200, 2, 64, 64, 64, 1, 1)
+    assert 0 < need < with_pro
+    # more sequences: more chunk slots (ceil(T/C) + N per head)
+    assert lib.dr_backward_varlen_workspace_bytes(1, 9, 200, 2, 64, 64, 64, 1, 0) > need
+    assert lib.dr_backward_varlen_workspace_bytes(1, 0, 200, 2, 64, 64, 64, 1, 0) == 0
+    assert lib.dr_backward_varlen_workspace_bytes(1, 3, 200, 2, 96, 96, 64, 1, 0) == 0
+
+    def bwd(kind=1, cu=FAKE, N=3, dout=FAKE, dq=FAKE, dbeta=FAKE, ws=FAKE, wsb=1 << 40, D=64, T=200):
+        return lib.dr_backward_varlen(kind, FAKE, FAKE, FAKE, FAKE, FAKE, cu, N, None, dout, None, dq, FAKE, FAKE,
+                                      FAKE, dbeta, None, None, None, T, 2, D, D, 64, 1, None, ws, wsb, None, None)
+
+    assert bwd(kind=3) == -1
+    assert bwd(cu=None) == -1
+    assert bwd(cu=FAKE + 2) == -1                # cu_seqlens must be 4-byte aligned
+    assert bwd(N=0) == -1
+    assert bwd(dout=None) == -1
+    assert bwd(dq=None) == -1
+    assert bwd(dbeta=None) == -1
     assert bwd(D=96) == -2
     assert bwd(ws=None) == -4
     assert bwd(wsb=need - 1) == -4
