@@ -20,7 +20,6 @@ cores.
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
 import json
 import os
@@ -59,10 +58,16 @@ def algorithmic(kind: str, w, io_bytes: int):
     return k1, k2, flops
 
 
+# The sources the forward's two kernels (intra_kernel, inter_kernel) are
+# compiled from, and the build script with the compiler flags.
+FORWARD_KERNEL_SOURCES = ("csrc/common.h", "csrc/intra.h", "csrc/inter.h", "build.py")
+
+
 def kernel_source_hash() -> str:
-    """sha256 over the kernel sources and the build script, in name order."""
+    """sha256 over the forward kernels' sources and the build script, in name
+    order (a change anywhere else, e.g. the backward, leaves it alone)."""
     pkg = os.path.join(ROOT, "delta_rule_rnn_amd")
-    files = sorted(glob.glob(os.path.join(pkg, "csrc", "*"))) + [os.path.join(pkg, "build.py")]
+    files = sorted(os.path.join(pkg, f) for f in FORWARD_KERNEL_SOURCES)
     h = hashlib.sha256()
     for f in files:
         h.update(os.path.basename(f).encode())

@@ -219,19 +219,21 @@ template <int ROWS, int COLS, int NTHR>
 struct Staged {
     static constexpr int PER = COLS / 4, IT = ROWS * PER / NTHR;
     static_assert(COLS % 4 == 0 && (ROWS * PER) % NTHR == 0, "staging shape");
-    float4 v[IT];
+    // native 4-float vectors (not the float4 struct, whose copies become
+    // memcpy and keep a loop-carried array out of registers)
+    f32x4 v[IT];
     __device__ __forceinline__ void load(const float* __restrict__ src, size_t gs, int tid) {
 #pragma unroll
         for (int j = 0; j < IT; ++j) {
             const int idx = tid + j * NTHR, r = idx / PER, c4 = (idx % PER) * 4;
-            v[j] = *reinterpret_cast<const float4*>(src + r * gs + c4);
+            v[j] = *reinterpret_cast<const f32x4*>(src + r * gs + c4);
         }
     }
     __device__ __forceinline__ void store(float* dst, int ls, int tid) const {
 #pragma unroll
         for (int j = 0; j < IT; ++j) {
             const int idx = tid + j * NTHR, r = idx / PER, c4 = (idx % PER) * 4;
-            *reinterpret_cast<float4*>(dst + r * ls + c4) = v[j];
+            *reinterpret_cast<f32x4*>(dst + r * ls + c4) = v[j];
         }
     }
 };
@@ -535,6 +537,24 @@ __device__ __forceinline__ void l2_touch(const float* __restrict__ src, size_t g
 // (C) the state update in place | the store wave writing Vnew / dVnew.
 constexpr int kStateThreads = 320;
 
+// One chunk's operands of the forward state pass as the 256 compute threads
+// hold them between their load and their LDS store.
+template <int DK>
+struct FwdOps {
+    Staged<C, DK, 256> w, k;
+    Staged<C, kSV, 256> u;
+    float ph;
+    template <bool DELTA>
+    __device__ __forceinline__ void load(const float* __restrict__ pc, int dv0, int tid) {
+        using P = Prep<DK>;
+        if constexpr (DELTA) w.load(pc + P::W, DK, tid);
+        k.load(pc + P::KB, DK, tid);
+        u.load(pc + P::U + dv0, DK, tid);
+        ph = tid < DK ? pc[P::PHI + tid] : 0.f;
+    }
+};
+
+
 // Forward state pass: writes the entry state S_c [DK][DV] and Vnew_c [C][DV]
 // of every chunk.
 template <int KIND, int DK>
@@ -567,31 +587,31 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_fwd_kernel(const floa
             sS[r * LSV + cc] = h0 ? h0[((size_t)chain * DK + r) * DV + dv0 + cc] : 0.f;
         }
     }
+    // the chunk operands travel one chunk ahead in registers: loaded during
+    // the products of the previous chunk, stored to LDS at the step's start
+    FwdOps<DK> op;
+    if (!storer && cl.nseg > 0) op.template load<DELTA>(prep + cl.ci0 * P::FLOATS, dv0, tid);
     lds_barrier();
     for (int c = 0; c < cl.nseg; ++c) {
         const size_t ci = cl.ci0 + c;
         const float* pc = prep + ci * P::FLOATS;
         // (A)
         if (!storer) {
-            // every load of the chunk in flight before the first LDS store
-            Staged<C, DK, 256> gw, gk;
-            Staged<C, kSV, 256> gu;
-            if constexpr (DELTA) gw.load(pc + P::W, DK, tid);
-            gk.load(pc + P::KB, DK, tid);
-            gu.load(pc + P::U + dv0, DV, tid);
-            const float ph = tid < DK ? pc[P::PHI + tid] : 0.f;
-            if constexpr (DELTA) gw.store(sW, LDN, tid);
-            gk.store(sKb, LDT, tid);
-            gu.store(sVn, LSV, tid);
-            if (tid < DK) sPhi[tid] = ph;
+            if constexpr (DELTA) op.w.store(sW, LDN, tid);
+            op.k.store(sKb, LDT, tid);
+            op.u.store(sVn, LSV, tid);
+            if (tid < DK) sPhi[tid] = op.ph;
         } else {
             unstage<DK, kSV, 64>(hs + ci * DK * DV + dv0, DV, sS, LSV, tid - 256);
         }
         lds_barrier();
         // (B) Vnew = U - W S: 4 tiles, one per compute wave
         if (!storer) {
-            if (c + 1 < cl.nseg) {
-                const float* pn = pc + P::FLOATS;
+            // next chunk into registers (the last chunk reloads itself, so
+            // that the loads stay unconditional), the one after into L2
+            op.template load<DELTA>(prep + (cl.ci0 + min(c + 1, cl.nseg - 1)) * P::FLOATS, dv0, tid);
+            if (c + 2 < cl.nseg) {
+                const float* pn = pc + 2 * P::FLOATS;
                 if constexpr (DELTA) l2_touch(pn + P::W, DK, C, DK, tid, 256, sink);
                 l2_touch(pn + P::KB, DK, C, DK, tid, 256, sink);
                 l2_touch(pn + P::U + dv0, DV, C, kSV, tid, 256, sink);
@@ -669,17 +689,16 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_rev_kernel(const floa
     for (int c = cl.nseg - 1; c >= 0; --c) {
         const size_t ci = cl.ci0 + c;
         const float* pc = prep + ci * P::FLOATS;
-        // (A)
+        // (A) every load of the chunk in flight; what (B) reads goes to LDS
+        // now, Q~ and W (read only in (C)) after (B)'s products, so that
+        // their fetch overlaps them
+        Staged<C, C, 256> ga;
+        Staged<C, DK, 256> gk, gq, gw;
         if (!storer) {
-            // every load of the chunk in flight before the first LDS store
-            Staged<C, C, 256> ga;
-            Staged<C, DK, 256> gk, gq, gw;
             constexpr int NDO = (C * kSV) / 256;
             float xo[NDO];
             ga.load(pc + P::AQK, C, tid);
             gk.load(pc + P::KB, DK, tid);
-            gq.load(pc + P::QT, DK, tid);
-            if constexpr (DELTA) gw.load(pc + P::W, DK, tid);
             const float ph = tid < DK ? pc[P::PHI + tid] : 0.f;
 #pragma unroll
             for (int it_ = 0; it_ < NDO; ++it_) {
@@ -687,10 +706,10 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_rev_kernel(const floa
                 const int tok = c * C + r;
                 xo[it_] = to_f(dout[((cl.tok0 + min(tok, cl.tlim - 1)) * H + h) * DV + dv0 + cc]);
             }
+            gq.load(pc + P::QT, DK, tid);
+            if constexpr (DELTA) gw.load(pc + P::W, DK, tid);
             ga.store(sAqk, LCT, tid);
             gk.store(sKb, LDN, tid);
-            gq.store(sQt, LDT, tid);
-            if constexpr (DELTA) gw.store(sW, LDT, tid);
             if (tid < DK) sPhi[tid] = ph;
 #pragma unroll
             for (int it_ = 0; it_ < NDO; ++it_) {
@@ -703,6 +722,17 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_rev_kernel(const floa
         lds_barrier();
         // (B) dVnew = Aqk^T dO + Kbar dS': 4 tiles, one per compute wave
         if (!storer) {
+            const int ti = wave;
+            f32x4 acc = mmk<C>(zero4(), sAqk + ti * 16, 1, LCT, sDO, LSV, 1, lane);
+            acc = mmk<DK>(acc, sKb + ti * 16 * LDN, LDN, 1, sD, LSV, 1, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sDV[(ti * 16 + arow(lane, i)) * LSV + (lane & 15)] = acc[i];
+            // (C)'s operands: the previous chunk's (C) finished reading these
+            // buffers before the end of its step
+            gq.store(sQt, LDT, tid);
+            if constexpr (DELTA) gw.store(sW, LDT, tid);
+            // the previous chunk's lines into L2 (after the stores above, so
+            // that waiting for Q~ and W does not wait for these)
             if (c > 0) {
                 const float* pn = pc - P::FLOATS;
                 l2_touch(pn + P::AQK, C, C, C, tid, 256, sink);
@@ -710,11 +740,6 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_rev_kernel(const floa
                 l2_touch(pn + P::QT, DK, C, DK, tid, 256, sink);
                 if constexpr (DELTA) l2_touch(pn + P::W, DK, C, DK, tid, 256, sink);
             }
-            const int ti = wave;
-            f32x4 acc = mmk<C>(zero4(), sAqk + ti * 16, 1, LCT, sDO, LSV, 1, lane);
-            acc = mmk<DK>(acc, sKb + ti * 16 * LDN, LDN, 1, sD, LSV, 1, lane);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sDV[(ti * 16 + arow(lane, i)) * LSV + (lane & 15)] = acc[i];
         }
         lds_barrier();
         // (C) dS = Q~^T dO + diag(phi) dS' - W^T dVnew, in place; the store
