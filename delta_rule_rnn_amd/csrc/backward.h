@@ -190,6 +190,22 @@ __device__ __forceinline__ f32x4 mmc(f32x4 acc, const float* A, int ar, const fl
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 __device__ __forceinline__ int arow(int lane, int i) { return 4 * (lane >> 4) + i; }
 
+// Sum over each row of 16 lanes (one accumulator column set), left in every
+// lane of the row, with four DPP moves inside the VALU (no LDS crossbar):
+// swap neighbours, swap pairs (quad sums), mirror within 8 lanes (quad 0 <->
+// quad 1), mirror within 16 lanes (half 0 <-> half 1).
+template <int CTRL>
+__device__ __forceinline__ float dpp_peer(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_peer<0xB1>(v);     // quad_perm [1,0,3,2]
+    v += dpp_peer<0x4E>(v);     // quad_perm [2,3,0,1]
+    v += dpp_peer<0x141>(v);    // row_half_mirror
+    v += dpp_peer<0x140>(v);    // row_mirror
+    return v;
+}
+
 // Cooperative copy of a [ROWS][COLS] fp32 block (row stride gs floats) into
 // LDS (row stride ls floats, a multiple of 4) by NTHR threads.  The shape is
 // known at compile time, so each thread issues up to 8 float4 loads before
@@ -879,25 +895,30 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     float* do1 = smem + SM::DO1;
     float* v1 = smem + SM::V1;
     float* p1 = smem + SM::P1;
+    // the value slices travel one slice ahead in registers: slice s+1 loads
+    // during slice s's products (the last slice reloads itself, so that the
+    // loads stay unconditional)
+    Staged<DK, kVS, 512> g1, g2;
+    Staged<C, kVS, 512> g3, g4;
+    constexpr int NE = (C * kVS) / 512;
+    float xd[NE], xv[NE];
+    auto load_slice = [&](int dv0) {
+        g1.load(hs + ci * DK * DV + dv0, DV, tid);
+        g2.load(dhs + ci * DK * DV + dv0, DV, tid);
+        g3.load(vn + ci * C * DV + dv0, DV, tid);
+        g4.load(dvn + ci * C * DV + dv0, DV, tid);
+#pragma unroll
+        for (int it_ = 0; it_ < NE; ++it_) {
+            const int idx = tid + it_ * 512, r = idx / kVS, cc = idx % kVS;
+            const size_t off = (row0 + (size_t)min(r, nvalid - 1) * H) * DV + dv0 + cc;
+            xd[it_] = to_f(dout[off]);
+            xv[it_] = to_f(v[off]);
+        }
+    };
+    load_slice(0);
     for (int s = 0; s < NVS; ++s) {
         const int dv0 = s * kVS;
         {
-            // every load of the slice in flight before the first LDS store
-            Staged<DK, kVS, 512> g1, g2;
-            Staged<C, kVS, 512> g3, g4;
-            constexpr int NE = (C * kVS) / 512;
-            float xd[NE], xv[NE];
-            g1.load(hs + ci * DK * DV + dv0, DV, tid);
-            g2.load(dhs + ci * DK * DV + dv0, DV, tid);
-            g3.load(vn + ci * C * DV + dv0, DV, tid);
-            g4.load(dvn + ci * C * DV + dv0, DV, tid);
-#pragma unroll
-            for (int it_ = 0; it_ < NE; ++it_) {
-                const int idx = tid + it_ * 512, r = idx / kVS, cc = idx % kVS;
-                const size_t off = (row0 + (size_t)min(r, nvalid - 1) * H) * DV + dv0 + cc;
-                xd[it_] = to_f(dout[off]);
-                xv[it_] = to_f(v[off]);
-            }
             g1.store(s1, LVS, tid);
             g2.store(ds1, LVS, tid);
             g3.store(vn1, LVS, tid);
@@ -910,6 +931,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             }
         }
         lds_barrier();
+        load_slice(min(s + 1, NVS - 1) * kVS);
         {
             const int ti = wave >> 1, tj = wave & 1;    // one [C][32] tile per wave
             if constexpr (DELTA) {
@@ -923,8 +945,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
                     p1[r * LVS + cc] = bt * vv - mscale(r) * x[i];
                     if (r < nvalid) dv[(row0 + (size_t)r * H) * DV + dv0 + cc] = from_f<T>(bt * dn[i]);
                     float part = dn[i] * vv;
-#pragma unroll
-                    for (int off = 1; off < 16; off <<= 1) part += __shfl_xor(part, off, 64);
+                    part = row16_sum(part);
                     if ((lane & 15) == 0) atomicAdd(&sDb[r], part);
                 }
             } else {
@@ -993,9 +1014,12 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             lk[m][i] = in_at(k, r, d);
         }
     }
+    // sum of dKbar * Kbar over this lane's elements: every owned tile of a
+    // wave has the same 16 columns (t = wave + 8m, NCT divides 8), so a lane
+    // keeps one column d = ecol(0)
+    float fpart = 0.f;
 #pragma unroll
     for (int m = 0; m < OWN; ++m) {
-        const int d = ecol(m);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float gm = lg[m][i], e = __builtin_amdgcn_exp2f(gm);
@@ -1007,15 +1031,18 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             aq[m][i] = dQt[m][i] * e;
             ak[m][i] = dKb[m][i] * kbf;
             aE[m][i] = dQt[m][i] * qq * e - dKb[m][i] * kbar;
-            float part = dKb[m][i] * kbar;
-            if constexpr (PERCH) {
-                atomicAdd(&sF[d], part);
-            } else {
-#pragma unroll
-                for (int off = 1; off < 16; off <<= 1) part += __shfl_xor(part, off, 64);
-                if ((lane & 15) == 0) atomicAdd(&sF[0], part);
-            }
+            fpart += dKb[m][i] * kbar;
         }
+    }
+    static_assert(8 % NCT == 0, "owned tiles share their columns");
+    // the four row groups of a column (lanes l, l+16, l+32, l+48)
+    fpart += __shfl_xor(fpart, 16, 64);
+    fpart += __shfl_xor(fpart, 32, 64);
+    if constexpr (PERCH) {
+        if (lane < 16) atomicAdd(&sF[ecol(0)], fpart);
+    } else {
+        fpart = row16_sum(fpart);
+        if (lane == 0) atomicAdd(&sF[0], fpart);
     }
 
     if constexpr (DELTA) {
@@ -1043,8 +1070,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
                 ak[m][i] += bt * e * dm;
                 aE[m][i] += dm * bt * kp;
                 float part = dm * kp;
-#pragma unroll
-                for (int off = 1; off < 16; off <<= 1) part += __shfl_xor(part, off, 64);
+                part = row16_sum(part);
                 if ((lane & 15) == 0) atomicAdd(&sDb[r], part);
             }
         }
@@ -1087,8 +1113,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
                 const float da = cc < r ? -acc[i] : 0.f;
                 sDL[r * LDC + cc] = beta_at(r) * da;
                 float part = da * lrc[m][i];
-#pragma unroll
-                for (int off = 1; off < 16; off <<= 1) part += __shfl_xor(part, off, 64);
+                part = row16_sum(part);
                 if ((lane & 15) == 0) atomicAdd(&sDb[r], part);
             }
         }
@@ -1234,19 +1259,38 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     }
     lds_barrier();
     if constexpr (PERCH) {
-        if (tid < DK) {
-            const int d = tid;
-            float acc = sF[d] + sDphi[d] * sPhi[d];
-            for (int r = C - 1; r >= 0; --r) {
-                acc += sEm[r * LDK + d];
-                if (r < nvalid) dg[(row0 + (size_t)r * H) * DK + d] = acc;
-            }
+        // reverse cumsum down each column, 512 / DK threads per column, each
+        // over a block of rows: block sums, then each block's scan from the
+        // sum of the blocks below it
+        constexpr int NB = 512 / DK, RB = C / NB;
+        float* sBlk = smem + SM::KP;     // [NB][DK]: K+ is no longer read
+        static_assert(SM::KP + NB * DK <= SM::E, "block sums overlap E");
+        const int d = tid % DK, b = tid / DK;
+        float bs = 0.f;
+#pragma unroll
+        for (int j = 0; j < RB; ++j) bs += sEm[(b * RB + j) * LDK + d];
+        sBlk[b * DK + d] = bs;
+        lds_barrier();
+        float acc = sF[d] + sDphi[d] * sPhi[d];
+#pragma unroll
+        for (int b2 = NB - 1; b2 > b; --b2) acc += sBlk[b2 * DK + d];
+#pragma unroll
+        for (int j = RB - 1; j >= 0; --j) {
+            const int r = b * RB + j;
+            acc += sEm[r * LDK + d];
+            if (r < nvalid) dg[(row0 + (size_t)r * H) * DK + d] = acc;
         }
     } else {
-        if (tid < C) {
-            float s = sE[tid];
-            for (int d = 0; d < DK; ++d) s += sEm[tid * LDK + d];
-            sRow[tid] = s;
+        // row sums over the DK columns, 8 threads per row
+        {
+            const int r = tid >> 3, part0 = tid & 7;
+            float s = 0.f;
+#pragma unroll
+            for (int j = 0; j < DK / 8; ++j) s += sEm[r * LDK + part0 * (DK / 8) + j];
+            s += __shfl_xor(s, 1, 64);
+            s += __shfl_xor(s, 2, 64);
+            s += __shfl_xor(s, 4, 64);
+            if (part0 == 0) sRow[r] = s + sE[r];
         }
         if (tid == C) {
             float s = 0.f;
