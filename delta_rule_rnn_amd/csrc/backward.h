@@ -188,6 +188,15 @@ __device__ __forceinline__ f32x4 mmc(f32x4 acc, const float* A, int ar, const fl
     else return mmk<K>(acc, A, ar, 1, B, 1, bc, lane);
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Four adjacent elements stored as one access (8 bytes bf16, 16 bytes fp32).
+__device__ __forceinline__ void st4(bf16* p, f32x4 v) {
+    bf16x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = (bf16)v[j];
+    *reinterpret_cast<bf16x4*>(p) = o;
+}
+__device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
 __device__ __forceinline__ int arow(int lane, int i) { return 4 * (lane >> 4) + i; }
 
 // Sum over each row of 16 lanes (one accumulator column set), left in every
@@ -856,13 +865,24 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     };
 
     // ---- set-up: K+ (or k), T, beta, gamma, phi
-    #pragma unroll 8
-    for (int it_ = 0; it_ < (C * DK) / 512; ++it_) {
+    // four adjacent channels per thread and access
+#pragma unroll
+    for (int it_ = 0; it_ < (C * DK) / (4 * 512); ++it_) {
         const int idx = tid + it_ * 512;
-        const int r = idx / DK, d = idx % DK;
-        const float kl = to_f(k[(row0 + (size_t)min(r, nvalid - 1) * H) * DK + d]);
-        const float kk = r < nvalid ? kl : 0.f;
-        sKp[r * LDK + d] = PERCH ? kk * __builtin_amdgcn_exp2f(pc[P::GAM + (size_t)r * DK + d]) : kk;
+        const int r = idx / (DK / 4), d0 = (idx % (DK / 4)) * 4;
+        const bool ok = r < nvalid;
+        Raw4<T> xk;
+        xk.load(k + (row0 + (size_t)min(r, nvalid - 1) * H) * DK + d0);
+        f32x4 kp;
+        if constexpr (PERCH) {
+            const f32x4 gm = *reinterpret_cast<const f32x4*>(pc + P::GAM + (size_t)r * DK + d0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) kp[j] = (ok ? xk[j] : 0.f) * __builtin_amdgcn_exp2f(gm[j]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) kp[j] = ok ? xk[j] : 0.f;
+        }
+        *reinterpret_cast<f32x4*>(sKp + r * LDK + d0) = kp;
     }
     if constexpr (DELTA) stage<C, C, 512>(sT, LDC, pc + P::TI, C, tid);
     if (tid < C) {
@@ -1135,18 +1155,33 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     float* sKm = smem + SM::KM;     // kda: K-;  scalar: raw q
     float* sQt = smem + SM::QT;     // kda: Q~
     float* sDL = smem + SM::DL;
-    #pragma unroll 8
-    for (int it_ = 0; it_ < (C * DK) / 512; ++it_) {
+    // four adjacent channels per thread and access
+    constexpr int DK4 = DK / 4;
+    #pragma unroll 4
+    for (int it_ = 0; it_ < (C * DK4) / 512; ++it_) {
         const int idx = tid + it_ * 512;
-        const int r = idx / DK, d = idx % DK;
-        const float qq = in_at(q, r, d);
+        const int r = idx / DK4, d0 = (idx % DK4) * 4;
+        const bool ok = r < nvalid;
+        const size_t go = (row0 + (size_t)min(r, nvalid - 1) * H) * DK + d0;
+        Raw4<T> xq;
+        xq.load(q + go);
         if constexpr (PERCH) {
-            const float gm = pc[P::GAM + (size_t)r * DK + d];
-            const float kk = in_at(k, r, d);
-            sKm[r * LDK + d] = kk * __builtin_amdgcn_exp2f(-gm);
-            sQt[r * LDK + d] = qq * __builtin_amdgcn_exp2f(gm);
+            Raw4<T> xk;
+            xk.load(k + go);
+            const f32x4 gm = *reinterpret_cast<const f32x4*>(pc + P::GAM + (size_t)r * DK + d0);
+            f32x4 km, qt;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                km[j] = (ok ? xk[j] : 0.f) * __builtin_amdgcn_exp2f(-gm[j]);
+                qt[j] = (ok ? xq[j] : 0.f) * __builtin_amdgcn_exp2f(gm[j]);
+            }
+            *reinterpret_cast<f32x4*>(sKm + r * LDK + d0) = km;
+            *reinterpret_cast<f32x4*>(sQt + r * LDK + d0) = qt;
         } else {
-            sKm[r * LDK + d] = qq;
+            f32x4 qv;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) qv[j] = ok ? xq[j] : 0.f;
+            *reinterpret_cast<f32x4*>(sKm + r * LDK + d0) = qv;
         }
     }
     if constexpr (!PERCH) {
@@ -1243,6 +1278,11 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
 
     // ---- phase 3: write dq, dk; E to LDS, then the reverse cumsum per column
     float* sEm = smem + SM::E;
+    // dq, dk staged in LDS (the phase 2 buffers past E) so that they leave as
+    // four adjacent channels per access
+    float* sDq = smem + SM::Y;
+    float* sDk = sDq + SM::MAT;
+    static_assert(SM::Y >= SM::E + SM::MAT && SM::Y + 2 * SM::MAT <= SM::END2, "dq/dk staging");
 #pragma unroll
     for (int m = 0; m < OWN; ++m) {
         const int d = ecol(m);
@@ -1250,14 +1290,24 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         for (int i = 0; i < 4; ++i) {
             const int r = erow(m, i);
             sEm[r * LDK + d] = aE[m][i];
-            if (r < nvalid) {
-                const size_t off = (row0 + (size_t)r * H) * DK + d;
-                dq[off] = from_f<T>(aq[m][i]);
-                dk[off] = from_f<T>(ak[m][i]);
-            }
+            sDq[r * LDK + d] = aq[m][i];
+            sDk[r * LDK + d] = ak[m][i];
         }
     }
     lds_barrier();
+    {
+        constexpr int DK4 = DK / 4;
+#pragma unroll
+        for (int it_ = 0; it_ < (C * DK4) / 512; ++it_) {
+            const int idx = tid + it_ * 512;
+            const int r = idx / DK4, d0 = (idx % DK4) * 4;
+            if (r < nvalid) {
+                const size_t off = (row0 + (size_t)r * H) * DK + d0;
+                st4(dq + off, *reinterpret_cast<const f32x4*>(sDq + r * LDK + d0));
+                st4(dk + off, *reinterpret_cast<const f32x4*>(sDk + r * LDK + d0));
+            }
+        }
+    }
     if constexpr (PERCH) {
         // reverse cumsum down each column, 512 / DK threads per column, each
         // over a block of rows: block sums, then each block's scan from the
