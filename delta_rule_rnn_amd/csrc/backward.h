@@ -343,25 +343,43 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
 
     // ---- gamma and the separable operands
     if constexpr (PERCH) {
-        if (tid < DK) {
-            const int d = tid;
-            float run = 0.f;
-            for (int r = 0; r < C; ++r) {
-                run += sB[r * LDK + d] * kLog2e;
-                const float e = __builtin_amdgcn_exp2f(run), ei = __builtin_amdgcn_exp2f(-run);
-                const float kk = sA[r * LDK + d];
-                sA[r * LDK + d] = kk * e;
-                sB[r * LDK + d] = kk * ei;
-                sQ[r * LDK + d] *= e;
-                out[P::GAM + (size_t)r * DK + d] = run;
-            }
+        // cumsum down each column by 256 / DK threads, each over a block of
+        // rows: block sums, then each block's running sum from the sum of the
+        // blocks above it (sL is free until L is formed)
+        constexpr int NB = 256 / DK, RB = C / NB;
+        float* sBlk = sL;
+        const int d = tid % DK, b = tid / DK;
+        float bs = 0.f;
+#pragma unroll
+        for (int j = 0; j < RB; ++j) bs += sB[(b * RB + j) * LDK + d];
+        sBlk[b * DK + d] = bs;
+        lds_barrier();
+        float run = 0.f;
+#pragma unroll
+        for (int b2 = 0; b2 < NB; ++b2)
+            if (b2 < b) run += sBlk[b2 * DK + d];
+        run *= kLog2e;
+        for (int j = 0; j < RB; ++j) {
+            const int r = b * RB + j;
+            run += sB[r * LDK + d] * kLog2e;
+            const float e = __builtin_amdgcn_exp2f(run), ei = __builtin_amdgcn_exp2f(-run);
+            const float kk = sA[r * LDK + d];
+            sA[r * LDK + d] = kk * e;
+            sB[r * LDK + d] = kk * ei;
+            sQ[r * LDK + d] *= e;
+            out[P::GAM + (size_t)r * DK + d] = run;
+        }
+        if (b == NB - 1) {
             const float phi = __builtin_amdgcn_exp2f(run);
             sPhi[d] = phi;
             out[P::PHI + d] = phi;
-            for (int r = 0; r < C; ++r) {
-                out[P::KB + (size_t)r * DK + d] = sB[r * LDK + d] * phi;
-                out[P::QT + (size_t)r * DK + d] = sQ[r * LDK + d];
-            }
+        }
+        lds_barrier();
+        const float phi = sPhi[d];
+        for (int j = 0; j < RB; ++j) {
+            const int r = b * RB + j;
+            out[P::KB + (size_t)r * DK + d] = sB[r * LDK + d] * phi;
+            out[P::QT + (size_t)r * DK + d] = sQ[r * LDK + d];
         }
     } else {
         if (wave == 0) {
