@@ -160,6 +160,46 @@ __device__ __forceinline__ f32x4 mmk(f32x4 acc, const float* A, int ar, int ak, 
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[k0 * ak], b[k0 * bk], acc, 0, 0, 0);
     return acc;
 }
+// The same product with A contiguous along k (A(r, k) = A[r*ar + k]), read
+// four k at a time: lane group q = l/16 takes the contiguous k range
+// [q*K/4, (q+1)*K/4) instead of every fourth k (the sum is the same, in
+// another order), so its A values arrive as 16-byte LDS reads.  ar and A
+// must keep those reads 16-byte aligned.
+template <int K>
+__device__ __forceinline__ f32x4 mmk_a(f32x4 acc, const float* A, int ar, const float* B, int bk, int bc,
+                                       int lane) {
+    static_assert(K % 16 == 0, "k range per lane group");
+    constexpr int KQ = K / 4;
+    const int r = lane & 15, q = lane >> 4;
+    const float* a = A + r * ar + q * KQ;
+    const float* b = B + (q * KQ) * bk + r * bc;
+#pragma unroll
+    for (int s0 = 0; s0 < KQ; s0 += 4) {
+        const f32x4 av = *reinterpret_cast<const f32x4*>(a + s0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], b[(s0 + j) * bk], acc, 0, 0, 0);
+    }
+    return acc;
+}
+// Both operands contiguous along k (A(r, k) = A[r*ar + k], B(k, c) =
+// B[c*bc + k]), both read four k at a time as above.
+template <int K>
+__device__ __forceinline__ f32x4 mmk_ab(f32x4 acc, const float* A, int ar, const float* B, int bc, int lane) {
+    static_assert(K % 16 == 0, "k range per lane group");
+    constexpr int KQ = K / 4;
+    const int r = lane & 15, q = lane >> 4;
+    const float* a = A + r * ar + q * KQ;
+    const float* b = B + r * bc + q * KQ;
+#pragma unroll
+    for (int s0 = 0; s0 < KQ; s0 += 4) {
+        const f32x4 av = *reinterpret_cast<const f32x4*>(a + s0);
+        const f32x4 bv = *reinterpret_cast<const f32x4*>(b + s0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bv[j], acc, 0, 0, 0);
+    }
+    return acc;
+}
 // The same product with both operands contiguous along k (A(r, k) =
 // A[r*ar + k], B(k, c) = B[c*bc + k]) on bf16 MFMA (v_mfma_f32_16x16x32_bf16):
 // lane l reads 8 consecutive fp32 values of row / column l%16 at k0 + 8*(l/16)
@@ -661,7 +701,7 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_fwd_kernel(const floa
             }
             if constexpr (DELTA) {
                 const int ti = wave;
-                const f32x4 acc = mmk<DK>(zero4(), sW + ti * 16 * LDN, LDN, 1, sS, LSV, 1, lane);
+                const f32x4 acc = mmk_a<DK>(zero4(), sW + ti * 16 * LDN, LDN, sS, LSV, 1, lane);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sVn[(ti * 16 + arow(lane, i)) * LSV + (lane & 15)] -= acc[i];
             }
@@ -767,7 +807,7 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_rev_kernel(const floa
         if (!storer) {
             const int ti = wave;
             f32x4 acc = mmk<C>(zero4(), sAqk + ti * 16, 1, LCT, sDO, LSV, 1, lane);
-            acc = mmk<DK>(acc, sKb + ti * 16 * LDN, LDN, 1, sD, LSV, 1, lane);
+            acc = mmk_a<DK>(acc, sKb + ti * 16 * LDN, LDN, sD, LSV, 1, lane);
 #pragma unroll
             for (int i = 0; i < 4; ++i) sDV[(ti * 16 + arow(lane, i)) * LSV + (lane & 15)] = acc[i];
             // (C)'s operands: the previous chunk's (C) finished reading these
@@ -974,7 +1014,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             const int ti = wave >> 1, tj = wave & 1;    // one [C][32] tile per wave
             if constexpr (DELTA) {
                 // P = N - M S_s (N = diag(beta) V), and dN = T^T dVnew -> dv, dbeta
-                const f32x4 x = mmk<DK>(zero4(), sKp + ti * 16 * LDK, LDK, 1, s1 + tj * 16, LVS, 1, lane);
+                const f32x4 x = mmk_a<DK>(zero4(), sKp + ti * 16 * LDK, LDK, s1 + tj * 16, LVS, 1, lane);
                 const f32x4 dn = mmk<C>(zero4(), sT + ti * 16, 1, LDC, dvn1 + tj * 16, LVS, 1, lane);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -1136,7 +1176,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const int t = wave + 8 * m, ti = t >> 2, tj = t & 3;
-            const f32x4 acc = mmk<C>(zero4(), sDT + ti * 16 * LDC, LDC, 1, sT + tj * 16 * LDC, 1, LDC, lane);
+            const f32x4 acc = mmk_ab<C>(zero4(), sDT + ti * 16 * LDC, LDC, sT + tj * 16 * LDC, LDC, lane);
 #pragma unroll
             for (int i = 0; i < 4; ++i) sY[(ti * 16 + arow(lane, i)) * LDC + tj * 16 + (lane & 15)] = acc[i];
         }
@@ -1236,7 +1276,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             int ti, tj;
             trc(m, ti, tj);
             const int d = ecol(m);
-            const f32x4 dkp = mmk<C>(zero4(), sDL + ti * 16 * LDC, LDC, 1, sKm + tj * 16, LDK, 1, lane);
+            const f32x4 dkp = mmk_a<C>(zero4(), sDL + ti * 16 * LDC, LDC, sKm + tj * 16, LDK, 1, lane);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = erow(m, i);
@@ -1263,7 +1303,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             int ti, tj;
             trc(m, ti, tj);
             const int d = ecol(m);
-            const f32x4 dqt = mmk<C>(zero4(), sDAqk + ti * 16 * LDC, LDC, 1, sKm + tj * 16, LDK, 1, lane);
+            const f32x4 dqt = mmk_a<C>(zero4(), sDAqk + ti * 16 * LDC, LDC, sKm + tj * 16, LDK, 1, lane);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = erow(m, i);
@@ -1281,10 +1321,10 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             // raw k (sKp), raw q (sKm): dk += G_L k + G_L^T k + G_Q^T q;  dq += G_Q k
             f32x4 dkk = mmk<C>(zero4(), sDAqk + ti * 16, 1, LDC, sKm + tj * 16, LDK, 1, lane);
             if constexpr (DELTA) {
-                dkk = mmk<C>(dkk, sDL + ti * 16 * LDC, LDC, 1, sKp + tj * 16, LDK, 1, lane);
+                dkk = mmk_a<C>(dkk, sDL + ti * 16 * LDC, LDC, sKp + tj * 16, LDK, 1, lane);
                 dkk = mmk<C>(dkk, sDL + ti * 16, 1, LDC, sKp + tj * 16, LDK, 1, lane);
             }
-            const f32x4 dqq = mmk<C>(zero4(), sDAqk + ti * 16 * LDC, LDC, 1, sKp + tj * 16, LDK, 1, lane);
+            const f32x4 dqq = mmk_a<C>(zero4(), sDAqk + ti * 16 * LDC, LDC, sKp + tj * 16, LDK, 1, lane);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 ak[m][i] += dkk[i];
