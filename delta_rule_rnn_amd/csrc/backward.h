@@ -239,21 +239,6 @@ __device__ __forceinline__ void st4(bf16* p, f32x4 v) {
 __device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
 __device__ __forceinline__ int arow(int lane, int i) { return 4 * (lane >> 4) + i; }
 
-// Sum over each row of 16 lanes (one accumulator column set), left in every
-// lane of the row, with four DPP moves inside the VALU (no LDS crossbar):
-// swap neighbours, swap pairs (quad sums), mirror within 8 lanes (quad 0 <->
-// quad 1), mirror within 16 lanes (half 0 <-> half 1).
-template <int CTRL>
-__device__ __forceinline__ float dpp_peer(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float row16_sum(float v) {
-    v += dpp_peer<0xB1>(v);     // quad_perm [1,0,3,2]
-    v += dpp_peer<0x4E>(v);     // quad_perm [2,3,0,1]
-    v += dpp_peer<0x141>(v);    // row_half_mirror
-    v += dpp_peer<0x140>(v);    // row_mirror
-    return v;
-}
 
 // Cooperative copy of a [ROWS][COLS] fp32 block (row stride gs floats) into
 // LDS (row stride ls floats, a multiple of 4) by NTHR threads.  The shape is

@@ -49,6 +49,30 @@ template <typename T> struct Frag;
 template <> struct Frag<bf16> { bf16x8 v; };
 template <> struct Frag<float> { float v[8]; };
 
+// Sums over aligned lane groups without the LDS crossbar: within each row of
+// 16 lanes four DPP moves (swap neighbours, swap pairs -- quad sums --,
+// mirror within 8 lanes, mirror within 16), then shuffles across rows.  The
+// result is left in every lane of the group.  All lanes must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_peer(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_peer<0xB1>(v);     // quad_perm [1,0,3,2]
+    v += dpp_peer<0x4E>(v);     // quad_perm [2,3,0,1]
+    v += dpp_peer<0x141>(v);    // row_half_mirror
+    v += dpp_peer<0x140>(v);    // row_mirror
+    return v;
+}
+template <int N>
+__device__ __forceinline__ float lane_group_sum(float v) {
+    static_assert(N == 16 || N == 32 || N == 64, "lane group");
+    v = row16_sum(v);
+    if constexpr (N >= 32) v += __shfl_xor(v, 16, 64);
+    if constexpr (N >= 64) v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
 __device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f(float x) { return x; }
 template <typename T> __device__ __forceinline__ T from_f(float x);

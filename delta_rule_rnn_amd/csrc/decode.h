@@ -82,11 +82,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
                     sk2 += kl[j] * kl[j];
                     sq2 += ql[j] * ql[j];
                 }
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    sk2 += __shfl_xor(sk2, off, 64);
-                    sq2 += __shfl_xor(sq2, off, 64);
-                }
+                sk2 = lane_group_sum<64>(sk2);
+                sq2 = lane_group_sum<64>(sq2);
                 nk = 1.f / sqrtf(sk2 + kNormEps);
                 nq *= 1.f / sqrtf(sq2 + kNormEps);
             }

@@ -189,7 +189,7 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
     if (tid < C) sBeta[tid] = (DELTA && tid < nvalid) ? (PRO ? pro_beta(ph, in.bt) : in.bt) : 0.f;
     // prologue: per-row factors of k and q (L2 normalisation, query scale).
     // A row's DK channels sit in the NCG = 32 adjacent lanes of one half
-    // wave, so its sum of squares is a butterfly over lane offsets 1..16.
+    // wave, so its sum of squares is a sum over that lane group.
     float nk[PL], nq[PL];
 #pragma unroll
     for (int i = 0; i < PL; ++i) nk[i] = nq[i] = 1.f;
@@ -204,11 +204,8 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
                     sk += kk * kk;
                     sq += qq * qq;
                 }
-#pragma unroll
-                for (int off = 1; off < NCG; off <<= 1) {
-                    sk += __shfl_xor(sk, off, 64);
-                    sq += __shfl_xor(sq, off, 64);
-                }
+                sk = lane_group_sum<NCG>(sk);
+                sq = lane_group_sum<NCG>(sq);
                 nk[i] = 1.f / sqrtf(sk + kNormEps);
                 nq[i] = 1.f / sqrtf(sq + kNormEps);
             }

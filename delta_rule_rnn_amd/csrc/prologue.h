@@ -55,11 +55,8 @@ __global__ __launch_bounds__(256) void prologue_apply_kernel(const T* __restrict
         }
         float nq = ph.scale, nk = 1.f;
         if (ph.ops & PRO_QK_L2NORM) {
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                sq += __shfl_xor(sq, off, 64);
-                sk += __shfl_xor(sk, off, 64);
-            }
+            sq = lane_group_sum<64>(sq);
+            sk = lane_group_sum<64>(sk);
             nq *= 1.f / sqrtf(sq + kNormEps);
             nk = 1.f / sqrtf(sk + kNormEps);
         }
@@ -115,11 +112,8 @@ __global__ __launch_bounds__(256) void prologue_backward_kernel(const T* __restr
             sk += kl[j] * kl[j];
         }
         if (norm) {
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                sq += __shfl_xor(sq, off, 64);
-                sk += __shfl_xor(sk, off, 64);
-            }
+            sq = lane_group_sum<64>(sq);
+            sk = lane_group_sum<64>(sk);
             const float iq = 1.f / sqrtf(sq + kNormEps), ik = 1.f / sqrtf(sk + kNormEps);
             float dotq = 0.f, dotk = 0.f;
 #pragma unroll
@@ -127,11 +121,8 @@ __global__ __launch_bounds__(256) void prologue_backward_kernel(const T* __restr
                 dotq += ql[j] * iq * gq[j];
                 dotk += kl[j] * ik * gk[j];
             }
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                dotq += __shfl_xor(dotq, off, 64);
-                dotk += __shfl_xor(dotk, off, 64);
-            }
+            dotq = lane_group_sum<64>(dotq);
+            dotk = lane_group_sum<64>(dotk);
 #pragma unroll
             for (int j = 0; j < NPL; ++j) {
                 gq[j] = (gq[j] - ql[j] * iq * dotq) * iq;
