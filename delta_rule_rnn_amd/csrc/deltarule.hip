@@ -306,7 +306,10 @@ dr_status forward_varlen(int kind, const void* q, const void* k, const void* v, 
     bool use_pro;
     if ((s = resolve_prologue(kind, pro, &pr, &use_pro)) != DR_OK) return s;
     if (N < 1 || !cu_seqlens) return DR_ERR_INVALID_ARG;
-    if ((long long)N * H * (Dv / 16) > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
+    // grid sizes, checked before the chunk table is enqueued
+    if ((long long)N * H * (Dv / 16) > 0x7fffffffLL ||
+        ((long long)ceil_div(T, dr::kChunk) + N) * H > 0x7fffffffLL)
+        return DR_ERR_UNSUPPORTED;
     if (T > 0 && !o) return DR_ERR_INVALID_ARG;
     if (!aligned16(o) || !aligned16(h0) || !aligned16(hT) || !aligned16(ws)) return DR_ERR_INVALID_ARG;
     if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return DR_ERR_INVALID_ARG;
@@ -561,7 +564,10 @@ dr_status backward_impl(int kind, const void* q, const void* k, const void* v, c
         if (!aligned16(p)) return DR_ERR_INVALID_ARG;
     if ((reinterpret_cast<uintptr_t>(dA_log) & 3u) || (reinterpret_cast<uintptr_t>(ddt_bias) & 3u))
         return DR_ERR_INVALID_ARG;
-    if ((long long)chains * H * (Dv / 16) > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
+    // grid sizes of the four kernels, checked before anything is enqueued
+    const long long items = packed ? ((long long)ceil_div(T, dr::kChunk) + N) * H
+                                   : (long long)B * ceil_div(T, dr::kChunk) * H;
+    if ((long long)chains * H * (Dv / 16) > 0x7fffffffLL || items > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
     // workspace: [prologue part][chunk table (packed)][core]; every check
     // before the first launch
     VarlenLayout V{};
