@@ -195,5 +195,6 @@ def test_backward_varlen_rejects(lib):
     assert bwd(dq=None) == -1
     assert bwd(dbeta=None) == -1
     assert bwd(D=96) == -2
+    assert bwd(N=1 << 30) == -2                  # grids past 2^31 workgroups, refused before any launch
     assert bwd(ws=None) == -4
     assert bwd(wsb=need - 1) == -4
