@@ -16,7 +16,7 @@ Contents
 Page keys used in citations (title of the page, then the section):
   [SD]   "TileLang 实战：KDA 从零到一--标量衰减"
   [KDA]  "TileLang 实战：KDA 从零到一–Kimi Delta Attention"
-  [GDN]  "Gated DeltaNet" (qwen35-gated-deltanet)
+  [GDN]  "Gated DeltaNet"
   [DPLR] "RNN的复兴04:线性注意力并行计算DPLR"
   [EVO]  "07 · linear 路线（二）：衰减机制的演进"
 

@@ -15,7 +15,7 @@
  *   [SD]   "TileLang 实战：KDA 从零到一--标量衰减"
  *          section 1.1: S_t = alpha S_{t-1} + v_t k_t^T, o_t = S_t q_t
  *          (scalar decay, no delta term); section 1.0 lets alpha vary per token.
- *   [GDN]  "Gated DeltaNet" (qwen35-gated-deltanet), section "DeltaNet 与
+ *   [GDN]  "Gated DeltaNet", section "DeltaNet 与
  *          Gated Delta Rule": decay the entry state first, then the rank-one
  *          residual write along k.  The scalar-gate case of [KDA]'s update.
  *

@@ -7,8 +7,8 @@ broken copies of the oracle (see test_oracle_pins.py) to show that they
 catch plausible mistakes.  Every pin raises AssertionError on failure.
 
 Page keys: [SD] "TileLang 实战：KDA 从零到一--标量衰减"; [KDA] "TileLang
-实战：KDA 从零到一–Kimi Delta Attention"; [GDN] "Gated DeltaNet"
-(qwen35-gated-deltanet); [DPLR] "RNN的复兴04:线性注意力并行计算DPLR";
+实战：KDA 从零到一–Kimi Delta Attention"; [GDN] "Gated DeltaNet";
+[DPLR] "RNN的复兴04:线性注意力并行计算DPLR";
 [EVO] "07 · linear 路线（二）：衰减机制的演进".
 """
 from __future__ import annotations
