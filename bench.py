@@ -398,8 +398,8 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only (the forward is a per-(batch, head) "
-              "chain; multi-GPU sharding is a design note, not built). Run with --gpus 1.",
+        print("bench.py: the library runs on one GPU (each (batch, head) chain is sequential and no "
+              "multi-GPU sharding is implemented); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
