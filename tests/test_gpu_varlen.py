@@ -130,3 +130,45 @@ def test_varlen_full_size_sampled():
             ro, rs = oracle.recurrence("kda", sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]))
             assert_close(o[a:b, h:h + 1][None], ro, "bf16", f"sequence {i} head {h} output")
             assert_close(hT[i:i + 1, h:h + 1], np.swapaxes(rs, -1, -2), "bf16", f"sequence {i} head {h} state")
+
+
+def test_many_short_sequences():
+    """2500 sequences of lengths 0..20 (the chunk table is built in blocks of
+    1024 sequences, with a carry between blocks): sequences on both sides of
+    each block boundary, and a spread of others, against the oracle, for
+    the forward and the backward."""
+    import random
+    from oracle.backward import recurrence_backward
+    dra = _ops()
+    r = random.Random(41)
+    lengths = [r.randint(0, 20) for _ in range(2500)]
+    x, h0, cu = _packed("gdn", "f32", 64, lengths, seed=42, H=1)
+    N, T = len(lengths), cu[-1]
+    d = to_dev(x)
+    cu_t = torch.tensor(cu, dtype=torch.int32, device="cuda:0")
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    gen = torch.Generator().manual_seed(43)
+    do = torch.randn(1, T, 1, 64, generator=gen)
+    dhT = torch.randn(N, 1, 64, 64, generator=gen) * 0.1
+    o, hT = dra.forward_varlen("gdn", d["q"], d["k"], d["v"], d["g"], d["beta"], cu_t, h0=h0.to("cuda:0"),
+                               flags=flags)
+    res = dra.backward_varlen("gdn", d["q"], d["k"], d["v"], d["g"], d["beta"], cu_t, h0.to("cuda:0"),
+                              do.to("cuda:0"), dhT.to("cuda:0"))
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 0
+    o, hT = o.cpu().numpy(), hT.cpu().numpy()
+    got = [t.cpu().numpy() for t in res]
+    picks = sorted({0, 1, 1022, 1023, 1024, 1025, 2046, 2047, 2048, 2049, N - 1} | set(r.sample(range(N), 20)))
+    for i in picks:
+        a, b = cu[i], cu[i + 1]
+        sl = lambda t: t[:, a:b].contiguous()
+        hi = h0[i:i + 1].transpose(-1, -2).contiguous()
+        ro, rs = oracle.recurrence("gdn", sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]), hi)
+        assert_close(hT[i:i + 1], np.swapaxes(rs, -1, -2), "f32", f"sequence {i} (length {b - a}) state")
+        ref = recurrence_backward("gdn", sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]), hi,
+                                  sl(do), dhT[i:i + 1].transpose(-1, -2))
+        assert_close(got[5][i:i + 1], np.swapaxes(ref["dh0"], -1, -2), "f32", f"sequence {i} dh0")
+        if b > a:
+            assert_close(o[:, a:b], ro, "f32", f"sequence {i} output")
+            for name, val in zip(["dq", "dk", "dv", "dg", "dbeta"], got[:5]):
+                assert_close(val[:, a:b], ref[name], "f32", f"sequence {i} {name}")
