@@ -1,4 +1,5 @@
-// backward.h -- gradients of the chunkwise gated delta rule: four kernels.
+// backward.h -- gradients of the chunkwise gated delta rule: three kernels
+// here, after the forward state pass.
 //
 // Page keys: [KDA] "TileLang 实战：KDA 从零到一–Kimi Delta Attention";
 // [SD] "TileLang 实战：KDA 从零到一--标量衰减"; [GDN] "Gated DeltaNet"
@@ -32,14 +33,16 @@
 // a full __syncthreads would also wait for every outstanding global load and
 // store (prefetches and result stores included).
 //
-// All four kernels compute in fp32 on fp32 MFMA (v_mfma_f32_16x16x4_f32) with
-// operands staged in LDS in natural row-major layout; the I/O dtype only
-// changes the loads of q, k, v, dO and the stores of dq, dk, dv.
+// The entry states S_c and Vnew_c of every chunk come first, from the
+// forward's own two kernels (the chunk-parallel records, then the state pass
+// in its STATES mode, fp32 state in accumulators).  The kernels here compute
+// in fp32, on fp32 MFMA (v_mfma_f32_16x16x4_f32) with operands staged in LDS
+// in natural row-major layout, or bf16 MFMA for the phase-1 value-slice
+// products of bf16 I/O; the I/O dtype otherwise only changes the loads of
+// q, k, v, dO and the stores of dq, dk, dv.
 //   bwd_prep_kernel     chunk-parallel: writes the natural fp32 chunk arrays
-//                       (Q~, W, Kbar, U, Aqk, L, T, phi, gamma)
-//   bwd_state_fwd_kernel   per (chain, 32 value columns), chunks in order:
-//                       entry states S_c and Vnew
-//   bwd_state_rev_kernel   per (chain, 32 value columns), chunks in reverse:
+//                       (Q~, W, Kbar, Aqk, L, T, phi, gamma)
+//   bwd_state_rev_kernel   per (chain, 16 value columns), chunks in reverse:
 //                       exit adjoints dS'_c, dVnew, and dh0
 //   bwd_grad_kernel     chunk-parallel: dq, dk, dv, dbeta, dg
 #pragma once
@@ -62,8 +65,7 @@ struct Prep {
     static constexpr size_t QT = 0;                         // [C][DK]  Q~
     static constexpr size_t W = QT + (size_t)C * DK;        // [C][DK]  W
     static constexpr size_t KB = W + (size_t)C * DK;        // [C][DK]  Kbar
-    static constexpr size_t U = KB + (size_t)C * DK;        // [C][DV]  U (decay_la: V)
-    static constexpr size_t AQK = U + (size_t)C * DV;       // [C][C]   Aqk
+    static constexpr size_t AQK = KB + (size_t)C * DK;      // [C][C]   Aqk
     static constexpr size_t L = AQK + (size_t)C * C;        // [C][C]   L (strictly lower)
     static constexpr size_t TI = L + (size_t)C * C;         // [C][C]   T = (I + diag(beta) L)^-1
     static constexpr size_t PHI = TI + (size_t)C * C;       // [DK]     phi
@@ -312,7 +314,7 @@ struct PrepSmem {
 
 template <int KIND, typename T, int DK>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
-                                                       const T* __restrict__ v, const float* __restrict__ g,
+                                                       const float* __restrict__ g,
                                                        const float* __restrict__ beta, float* __restrict__ prep,
                                                        int Tlen, int H, int NT, Pack pk)
 {
@@ -324,7 +326,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
     __shared__ __attribute__((aligned(16))) float smem[SM::FLOATS];
     float* sA = smem + SM::SA;     // kda: K+ (then M);  scalar: k (then M)
     float* sB = smem + SM::SB;     // kda: g, then K-
-    float* sQ = smem + SM::SQ;     // q (kda: Q~), later N = diag(beta) V
+    float* sQ = smem + SM::SQ;     // q (kda: Q~)
     float* sL = smem + SM::SL;
     float* sT = smem + SM::ST;
     float* sBeta = smem + SM::SBETA;
@@ -516,36 +518,26 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
         }
     }
 
-    // ---- M = diag(beta) K+ (in place) and N = diag(beta) V (into sQ)
-    #pragma unroll 8
-    for (int it_ = 0; it_ < (C * DK) / 256; ++it_) {
-        const int idx = tid + it_ * 256;
-        const int r = idx / DK, d = idx % DK;
-        const float vl = to_f(v[(row0 + (size_t)min(r, nvalid - 1) * H) * DV + d]);
-        const float vv = r < nvalid ? vl : 0.f;
-        if constexpr (DELTA) {
-            const float rs = PERCH ? sBeta[r] : sBeta[r] * __builtin_amdgcn_exp2f(sGam[r]);
-            sA[r * LDK + d] *= rs;
-            sQ[r * LDK + d] = sBeta[r] * vv;
-        } else {
-            out[P::U + (size_t)r * DV + d] = vv;
-        }
-    }
+    // ---- M = diag(beta) K+ (in place), W = T M (the forward state pass
+    // takes U, and Vnew, from the forward's own kernels)
     if constexpr (DELTA) {
+        #pragma unroll 8
+        for (int it_ = 0; it_ < (C * DK) / 256; ++it_) {
+            const int idx = tid + it_ * 256;
+            const int r = idx / DK, d = idx % DK;
+            sA[r * LDK + d] *= PERCH ? sBeta[r] : sBeta[r] * __builtin_amdgcn_exp2f(sGam[r]);
+        }
         lds_barrier();
-        // W = T M, U = T N: (C/16) x (DK/16) tiles each
+        // (C/16) x (DK/16) tiles
         constexpr int NTL = 4 * (DK / 16);
-        for (int job = wave; job < 2 * NTL; job += 4) {
-            const bool isW = job < NTL;
-            const int t = isW ? job : job - NTL, ti = t / (DK / 16), tj = t % (DK / 16);
-            const float* Bop = isW ? sA : sQ;
+        for (int t = wave; t < NTL; t += 4) {
+            const int ti = t / (DK / 16), tj = t % (DK / 16);
             // T is lower triangular: the reduction stops at block ti
             f32x4 acc = zero4();
             for (int kb = 0; kb <= ti; ++kb)
-                acc = mmk<16>(acc, sT + ti * 16 * LDC + kb * 16, LDC, 1, Bop + kb * 16 * LDK + tj * 16, LDK, 1, lane);
-            float* dst = out + (isW ? P::W : P::U);
+                acc = mmk<16>(acc, sT + ti * 16 * LDC + kb * 16, LDC, 1, sA + kb * 16 * LDK + tj * 16, LDK, 1, lane);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[(size_t)(ti * 16 + arow(lane, i)) * DK + tj * 16 + (lane & 15)] = acc[i];
+            for (int i = 0; i < 4; ++i) out[P::W + (size_t)(ti * 16 + arow(lane, i)) * DK + tj * 16 + (lane & 15)] = acc[i];
         }
     }
 }
@@ -571,9 +563,6 @@ struct StateSmem {
     static constexpr int LDN = DK + 4;     // [C][DK] read with the lane index along rows
     static constexpr int LDT = DK + 16;    // [C][DK] read transposed
     static constexpr int LCT = C + 16;     // [C][C] read transposed
-    // forward pass
-    static constexpr size_t S = 0, W = S + (size_t)DK * LSV, KBT = W + (size_t)C * LDN, VN = KBT + (size_t)C * LDT,
-                            PHI = VN + (size_t)C * LSV, SINK = PHI + DK, FWD = SINK + 64;
     // reverse pass
     static constexpr size_t D = 0, KBN = D + (size_t)DK * LSV, QT = KBN + (size_t)C * LDN, WT = QT + (size_t)C * LDT,
                             AQK = WT + (size_t)C * LDT, DV = AQK + (size_t)C * LCT, DO = DV + (size_t)C * LSV,
@@ -605,114 +594,7 @@ __device__ __forceinline__ void l2_touch(const float* __restrict__ src, size_t g
 // (C) the state update in place | the store wave writing Vnew / dVnew.
 constexpr int kStateThreads = 320;
 
-// One chunk's operands of the forward state pass as the 256 compute threads
-// hold them between their load and their LDS store.
-template <int DK>
-struct FwdOps {
-    Staged<C, DK, 256> w, k;
-    Staged<C, kSV, 256> u;
-    float ph;
-    template <bool DELTA>
-    __device__ __forceinline__ void load(const float* __restrict__ pc, int dv0, int tid) {
-        using P = Prep<DK>;
-        if constexpr (DELTA) w.load(pc + P::W, DK, tid);
-        k.load(pc + P::KB, DK, tid);
-        u.load(pc + P::U + dv0, DK, tid);
-        ph = tid < DK ? pc[P::PHI + tid] : 0.f;
-    }
-};
 
-
-// Forward state pass: writes the entry state S_c [DK][DV] and Vnew_c [C][DV]
-// of every chunk.
-template <int KIND, int DK>
-__global__ __launch_bounds__(kStateThreads) void bwd_state_fwd_kernel(const float* __restrict__ prep,
-                                                                      const float* __restrict__ h0,
-                                                                      float* __restrict__ hs, float* __restrict__ vn,
-                                                                      int H, int NT, int Tlen, Pack pk)
-{
-    using P = Prep<DK>;
-    using SM = StateSmem<DK>;
-    constexpr int DV = DK, LDN = SM::LDN, LDT = SM::LDT, NVS = DV / kSV;
-    constexpr bool DELTA = KIND != KIND_LA;
-    __shared__ __attribute__((aligned(16))) float smem[SM::FWD];
-    float* sS = smem + SM::S;
-    float* sW = smem + SM::W;
-    float* sKb = smem + SM::KBT;
-    float* sVn = smem + SM::VN;
-    float* sPhi = smem + SM::PHI;
-    float* sink = smem + SM::SINK;
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const bool storer = tid >= 256;
-    const int logical = xcd_logical(blockIdx.x, gridDim.x);
-    const int chain = chain_of(pk, logical / NVS, H, (int)gridDim.x / NVS), dv0 = (logical % NVS) * kSV;
-    const ChainLoc cl = locate_chain(pk, chain, H, Tlen, NT);
-    if (!storer) {
-#pragma unroll
-        for (int it_ = 0; it_ < (DK * kSV) / 256; ++it_) {
-            const int idx = tid + it_ * 256, r = idx / kSV, cc = idx % kSV;
-            sS[r * LSV + cc] = h0 ? h0[((size_t)chain * DK + r) * DV + dv0 + cc] : 0.f;
-        }
-    }
-    // the chunk operands travel one chunk ahead in registers: loaded during
-    // the products of the previous chunk, stored to LDS at the step's start
-    FwdOps<DK> op;
-    if (!storer && cl.nseg > 0) op.template load<DELTA>(prep + cl.ci0 * P::FLOATS, dv0, tid);
-    lds_barrier();
-    for (int c = 0; c < cl.nseg; ++c) {
-        const size_t ci = cl.ci0 + c;
-        const float* pc = prep + ci * P::FLOATS;
-        // (A)
-        if (!storer) {
-            if constexpr (DELTA) op.w.store(sW, LDN, tid);
-            op.k.store(sKb, LDT, tid);
-            op.u.store(sVn, LSV, tid);
-            if (tid < DK) sPhi[tid] = op.ph;
-        } else {
-            unstage<DK, kSV, 64>(hs + ci * DK * DV + dv0, DV, sS, LSV, tid - 256);
-        }
-        lds_barrier();
-        // (B) Vnew = U - W S: 4 tiles, one per compute wave
-        if (!storer) {
-            // next chunk into registers (the last chunk reloads itself, so
-            // that the loads stay unconditional), the one after into L2
-            op.template load<DELTA>(prep + (cl.ci0 + min(c + 1, cl.nseg - 1)) * P::FLOATS, dv0, tid);
-            if (c + 2 < cl.nseg) {
-                const float* pn = pc + 2 * P::FLOATS;
-                if constexpr (DELTA) l2_touch(pn + P::W, DK, C, DK, tid, 256, sink);
-                l2_touch(pn + P::KB, DK, C, DK, tid, 256, sink);
-                l2_touch(pn + P::U + dv0, DV, C, kSV, tid, 256, sink);
-            }
-            if constexpr (DELTA) {
-                const int ti = wave;
-                const f32x4 acc = mmk_a<DK>(zero4(), sW + ti * 16 * LDN, LDN, sS, LSV, 1, lane);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sVn[(ti * 16 + arow(lane, i)) * LSV + (lane & 15)] -= acc[i];
-            }
-        }
-        lds_barrier();
-        // (C) S' = diag(phi) S + Kbar^T Vnew, in place (each element has one
-        // owner); the store wave writes Vnew
-        if (!storer) {
-            for (int ti = wave; ti < DK / 16; ti += 4) {
-                f32x4 acc;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = ti * 16 + arow(lane, i);
-                    acc[i] = sPhi[r] * sS[r * LSV + (lane & 15)];
-                }
-                acc = mmk<C>(acc, sKb + ti * 16, 1, LDT, sVn, LSV, 1, lane);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sS[(ti * 16 + arow(lane, i)) * LSV + (lane & 15)] = acc[i];
-            }
-        } else {
-            unstage<C, kSV, 64>(vn + ci * C * DV + dv0, DV, sVn, LSV, tid - 256);
-        }
-        lds_barrier();
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
 
 // Reverse state pass, chunks in reverse: writes dS'_c (the exit-state adjoint
 // of chunk c) and dVnew_c, and dh0.

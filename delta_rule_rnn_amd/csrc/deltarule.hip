@@ -228,6 +228,56 @@ Problem make_problem(int kind, const void* q, const void* k, const void* v, cons
     return p;
 }
 
+// ---- the backward's forward state pass: the state-pass kernel in STATES
+// mode (entry state and Vnew of every chunk, no output) over the records the
+// chunk-parallel kernel wrote; slice width and prefetch as for the forward
+template <int KIND, typename E, int D, int NTN, int PFD>
+dr_status launch_states_p(const Problem& p, const float* h0, float* hs, float* vn, hipStream_t st) {
+    constexpr int NV = D / (16 * NTN);
+    dim3 grid(p.B * p.H * NV);
+    if (p.seqinfo) {
+        hipLaunchKernelGGL((dr::inter_kernel<KIND, E, D, D, NTN, PFD, true, true>), grid,
+                           dim3(dr::inter_threads<PFD>()), 0, st, p.ws, h0, static_cast<E*>(nullptr),
+                           static_cast<float*>(nullptr), p.T, p.H, p.NT, 0, 0, p.seqinfo, p.maxchunks, hs, vn);
+    } else {
+        hipLaunchKernelGGL((dr::inter_kernel<KIND, E, D, D, NTN, PFD, false, true>), grid,
+                           dim3(dr::inter_threads<PFD>()), 0, st, p.ws, h0, static_cast<E*>(nullptr),
+                           static_cast<float*>(nullptr), p.T, p.H, p.NT, 0, p.NT, nullptr, 0, hs, vn);
+    }
+    return check_launch();
+}
+template <int KIND, typename E, int D>
+dr_status launch_states_t(const Problem& p, const float* h0, float* hs, float* vn, hipStream_t st) {
+    const int ntn = pick_ntn(p.B * p.H, D);
+    const bool pf = pick_pfd() != 0;
+    if constexpr (sizeof(E) == 2) {
+        if (ntn == 1) return pf ? launch_states_p<KIND, E, D, 1, 2>(p, h0, hs, vn, st)
+                                : launch_states_p<KIND, E, D, 1, 0>(p, h0, hs, vn, st);
+        if (ntn == 2) return pf ? launch_states_p<KIND, E, D, 2, 2>(p, h0, hs, vn, st)
+                                : launch_states_p<KIND, E, D, 2, 0>(p, h0, hs, vn, st);
+        return launch_states_p<KIND, E, D, 4, 0>(p, h0, hs, vn, st);
+    } else {
+        // fp32 operands at 64 columns do not fit in registers: at most 32 columns
+        if (ntn == 1) return launch_states_p<KIND, E, D, 1, 0>(p, h0, hs, vn, st);
+        return launch_states_p<KIND, E, D, 2, 0>(p, h0, hs, vn, st);
+    }
+}
+dr_status launch_states(const Problem& p, const float* h0, float* hs, float* vn, hipStream_t st) {
+    auto by_kind = [&](auto kind_tag) -> dr_status {
+        constexpr int KIND = decltype(kind_tag)::value;
+        if (p.dtype == DR_BF16)
+            return p.D == 64 ? launch_states_t<KIND, bf16, 64>(p, h0, hs, vn, st)
+                             : launch_states_t<KIND, bf16, 128>(p, h0, hs, vn, st);
+        return p.D == 64 ? launch_states_t<KIND, float, 64>(p, h0, hs, vn, st)
+                         : launch_states_t<KIND, float, 128>(p, h0, hs, vn, st);
+    };
+    switch (p.kind) {
+        case DR_KIND_KDA: return by_kind(std::integral_constant<int, dr::KIND_KDA>{});
+        case DR_KIND_GDN: return by_kind(std::integral_constant<int, dr::KIND_GDN>{});
+        default: return by_kind(std::integral_constant<int, dr::KIND_LA>{});
+    }
+}
+
 dr_status forward(int kind, const void* q, const void* k, const void* v, const float* g,
                   const float* beta, const float* h0, void* o, float* hT, int B, int T, int H, int Dk,
                   int Dv, int C, int dtype, void* ws, size_t ws_bytes, unsigned* flags, void* stream,
@@ -294,6 +344,14 @@ dr_status launch_intra_varlen_p(const Problem& p, hipStream_t st) {
 template <int KIND>
 dr_status launch_intra_varlen_k(const Problem& p, hipStream_t st) {
     return p.use_pro ? launch_intra_varlen_p<KIND, true>(p, st) : launch_intra_varlen_p<KIND, false>(p, st);
+}
+
+dr_status launch_intra_varlen(const Problem& p, hipStream_t st) {
+    switch (p.kind) {
+        case DR_KIND_KDA: return launch_intra_varlen_k<dr::KIND_KDA>(p, st);
+        case DR_KIND_GDN: return launch_intra_varlen_k<dr::KIND_GDN>(p, st);
+        default: return launch_intra_varlen_k<dr::KIND_LA>(p, st);
+    }
 }
 
 dr_status forward_varlen(int kind, const void* q, const void* k, const void* v, const float* g,
@@ -412,11 +470,13 @@ dr_status decode(int kind, const void* q, const void* k, const void* v, const fl
 // states S_c [DK][DV], the exit adjoints dS'_c [DK][DV], Vnew_c and dVnew_c
 // [C][DV] of every chunk, each block 256-byte aligned.
 struct BwdLayout {
-    size_t prep, hs, dhs, vn, dvn, bytes;
+    size_t prep, hs, dhs, vn, dvn, rec, bytes;
 };
 // n = number of per-chunk entries (dense: B * H * ceil(T/C); packed:
 // H * maxchunks)
-BwdLayout bwd_layout_n(size_t n, int D) {
+// (the forward's chunk records come last: the forward state pass runs the
+// forward's own two kernels over them)
+BwdLayout bwd_layout_n(size_t n, int D, int dtype) {
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     const size_t pf = D == 64 ? dr::bw::Prep<64>::FLOATS : dr::bw::Prep<128>::FLOATS;
     BwdLayout L;
@@ -425,11 +485,12 @@ BwdLayout bwd_layout_n(size_t n, int D) {
     L.dhs = L.hs + up(n * D * D * 4);
     L.vn = L.dhs + up(n * D * D * 4);
     L.dvn = L.vn + up(n * dr::kChunk * D * 4);
-    L.bytes = L.dvn + up(n * dr::kChunk * D * 4);
+    L.rec = L.dvn + up(n * dr::kChunk * D * 4);
+    L.bytes = L.rec + up(n * record_bytes(D, dtype));
     return L;
 }
-BwdLayout bwd_layout(int B, int T, int H, int D) {
-    return bwd_layout_n((size_t)B * H * (size_t)ceil_div(T, dr::kChunk), D);
+BwdLayout bwd_layout(int B, int T, int H, int D, int dtype) {
+    return bwd_layout_n((size_t)B * H * (size_t)ceil_div(T, dr::kChunk), D, dtype);
 }
 
 // B is the sequence count for packed sequences (pk.table set; T is then the
@@ -460,13 +521,10 @@ dr_status launch_backward_t(const BwdArgs& a, hipStream_t st) {
     const long long items = a.pk.table ? (long long)a.pk.maxchunks * a.H : (long long)a.B * a.NT * a.H;
     const long long slices = (long long)a.B * a.H * (D / kSV);
     if (items > 0x7fffffffLL || slices > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((bwd_prep_kernel<KIND, E, D>), dim3((unsigned)items), dim3(256), 0, st, q, k, v, a.g, a.beta,
+    hipLaunchKernelGGL((bwd_prep_kernel<KIND, E, D>), dim3((unsigned)items), dim3(256), 0, st, q, k, a.g, a.beta,
                        prep, a.T, a.H, a.NT, a.pk);
     dr_status s = check_launch();
     if (s != DR_OK) return s;
-    hipLaunchKernelGGL((bwd_state_fwd_kernel<KIND, D>), dim3((unsigned)slices), dim3(kStateThreads), 0, st, prep, a.h0, hs, vn,
-                       a.H, a.NT, a.T, a.pk);
-    if ((s = check_launch()) != DR_OK) return s;
     hipLaunchKernelGGL((bwd_state_rev_kernel<KIND, E, D>), dim3((unsigned)slices), dim3(kStateThreads), 0, st, prep, dout, a.dhT,
                        dhs, dvn, a.dh0, a.T, a.H, a.NT, a.pk);
     if ((s = check_launch()) != DR_OK) return s;
@@ -576,9 +634,9 @@ dr_status backward_impl(int kind, const void* q, const void* k, const void* v, c
     if (packed) {
         V = varlen_layout(N, T, H, Dk, dtype);
         table_bytes = V.bytes - V.table;
-        L = bwd_layout_n((size_t)H * V.maxchunks, Dk);
+        L = bwd_layout_n((size_t)H * V.maxchunks, Dk, dtype);
     } else {
-        L = bwd_layout(B, T, H, Dk);
+        L = bwd_layout(B, T, H, Dk, dtype);
     }
     const size_t core_bytes = table_bytes + L.bytes;
     const ProBwdLayout PL = probwd_layout(kind, B, T, H, Dk, dtype, core_bytes);
@@ -626,8 +684,26 @@ dr_status backward_impl(int kind, const void* q, const void* k, const void* v, c
         if (s != DR_OK) return s;
         rq = qh; rk = kh; rg = gh; rb = bh;
     }
+    uint8_t* core = rest + table_bytes;
+    {
+        // forward state pass: the forward's chunk-parallel kernel writes the
+        // chunk records, the state-pass kernel in STATES mode the entry
+        // state and Vnew of every chunk (per-chunk arrays share the records'
+        // index, dense and packed)
+        Problem p = make_problem(kind, rq, rk, v, rg, rb, nullptr, chains, T, H, Dk, dtype, core + L.rec, nullptr);
+        if (packed) {
+            p.table = pk.table;
+            p.seqinfo = pk.seqinfo;
+            p.total = pk.total;
+            p.maxchunks = pk.maxchunks;
+        }
+        s = packed ? launch_intra_varlen(p, st) : launch_intra(p, 0, p.NT, st);
+        if (s != DR_OK) return s;
+        s = launch_states(p, h0, reinterpret_cast<float*>(core + L.hs), reinterpret_cast<float*>(core + L.vn), st);
+        if (s != DR_OK) return s;
+    }
     BwdArgs a{rq, rk, v, dout, rg, rb, h0, dhT, dq, dk, dv, dg, delta ? dbeta : nullptr, dh0,
-              chains, T, H, ceil_div(T, dr::kChunk), rest + table_bytes, L, pk};
+              chains, T, H, ceil_div(T, dr::kChunk), core, L, pk};
     switch (kind) {
         case DR_KIND_KDA: s = launch_backward_k<dr::KIND_KDA>(a, Dk, dtype, st); break;
         case DR_KIND_GDN: s = launch_backward_k<dr::KIND_GDN>(a, Dk, dtype, st); break;
@@ -646,7 +722,7 @@ extern "C" {
 size_t dr_backward_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, int C, int dtype) {
     if (kind < 0 || kind > 2 || B <= 0 || H <= 0 || T < 0) return 0;
     if (dr_record_bytes(Dk, Dv, C, dtype) == 0) return 0;
-    return bwd_layout(B, T, H, Dk).bytes;
+    return bwd_layout(B, T, H, Dk, dtype).bytes;
 }
 
 dr_status dr_backward(int kind, const void* q, const void* k, const void* v, const float* g, const float* beta,
@@ -660,7 +736,7 @@ dr_status dr_backward(int kind, const void* q, const void* k, const void* v, con
 size_t dr_backward_prologue_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, int C, int dtype) {
     if (kind < 0 || kind > 2 || B <= 0 || H <= 0 || T < 0) return 0;
     if (dr_record_bytes(Dk, Dv, C, dtype) == 0) return 0;
-    return probwd_layout(kind, B, T, H, Dk, dtype, bwd_layout(B, T, H, Dk).bytes).bytes;
+    return probwd_layout(kind, B, T, H, Dk, dtype, bwd_layout(B, T, H, Dk, dtype).bytes).bytes;
 }
 
 dr_status dr_backward_prologue(int kind, const void* q, const void* k, const void* v, const float* g,
@@ -677,7 +753,7 @@ size_t dr_backward_varlen_workspace_bytes(int kind, int N, int T, int H, int Dk,
     if (kind < 0 || kind > 2 || N < 1 || H <= 0 || T < 0) return 0;
     if (dr_record_bytes(Dk, Dv, C, dtype) == 0) return 0;
     const VarlenLayout V = varlen_layout(N, T, H, Dk, dtype);
-    const size_t core = (V.bytes - V.table) + bwd_layout_n((size_t)H * V.maxchunks, Dk).bytes;
+    const size_t core = (V.bytes - V.table) + bwd_layout_n((size_t)H * V.maxchunks, Dk, dtype).bytes;
     return with_prologue ? probwd_layout(kind, 1, T, H, Dk, dtype, core).bytes : core;
 }
 

@@ -169,14 +169,22 @@ constexpr int inter_threads() { return PFD > 0 ? kInterThreads + 64 : kInterThre
 // VARLEN: chains are (sequence, head) of packed sequences; seqinfo[i] =
 // {first record slot, chunks, first token, tokens} of sequence i (written by
 // varlen_table_kernel) replaces the dense layout's (Tlen, NT, c0, nseg).
-template <int KIND, typename T, int DK, int DV, int NTN, int PFD, bool VARLEN>
+//
+// STATES (the backward's forward state pass): instead of o, write for every
+// chunk its entry state S_c (fp32 [DK][DV] at states + r*DK*DV) and Vnew_c
+// (fp32 [C][DV] at vnew + r*C*DV), r the chunk's record index; the output
+// waves only keep the barriers.  Rows of a ragged last chunk past the end
+// get Vnew = 0 (their record rows are zero).
+template <int KIND, typename T, int DK, int DV, int NTN, int PFD, bool VARLEN, bool STATES = false>
 __global__ __launch_bounds__(inter_threads<PFD>()) void inter_kernel(const uint8_t* __restrict__ ws,
                                                               const float* __restrict__ h0,
                                                               T* __restrict__ o, float* __restrict__ hT,
                                                               int Tlen, int H, int NT, int c0,
                                                               int nseg_arg,
                                                               const int4* __restrict__ seqinfo,
-                                                              int maxchunks)
+                                                              int maxchunks,
+                                                              float* __restrict__ states = nullptr,
+                                                              float* __restrict__ vnew = nullptr)
 {
     using R = Rec<T, DK, DV>;
     constexpr int C = kChunk;
@@ -213,20 +221,20 @@ __global__ __launch_bounds__(inter_threads<PFD>()) void inter_kernel(const uint8
     // covering tokens tok0 .. tok0+tlim-1; the state enters through h0 and
     // leaves through hT
     int nseg, tlim;
-    size_t tok0;
-    const uint8_t* chain_rec;
+    size_t tok0, rec0;     // rec0: record index of the launch's first chunk
     if constexpr (VARLEN) {
         const int4 si = seqinfo[b];   // b is the sequence here
         nseg = si.y;
         tok0 = (size_t)si.z;
         tlim = si.w;
-        chain_rec = ws + ((size_t)h * maxchunks + si.x) * R::BYTES;
+        rec0 = (size_t)h * maxchunks + si.x;
     } else {
         nseg = nseg_arg;
         tok0 = (size_t)b * Tlen + (size_t)c0 * C;
         tlim = Tlen - c0 * C;
-        chain_rec = ws + (((size_t)b * H + h) * (size_t)NT + c0) * R::BYTES;
+        rec0 = ((size_t)b * H + h) * (size_t)NT + c0;
     }
+    const uint8_t* chain_rec = ws + rec0 * R::BYTES;
 
     auto fS_read = [&](Frag<T> (&fS)[NKB][NTN]) {
 #pragma unroll
@@ -282,7 +290,20 @@ __global__ __launch_bounds__(inter_threads<PFD>()) void inter_kernel(const uint8
         auto load = [&](Ops& op, int c) {
             load_recur<KIND, T, DK, DV, NTN>(op, chain_rec + (size_t)c * R::BYTES, wave, lane, dv0);
         };
-        auto step = [&](int, const Ops& cur, auto) {
+        auto step = [&](int c, const Ops& cur, auto) {
+            if constexpr (STATES) {
+                // the chunk's entry state, as the final state is written
+                if (ownS) {
+                    float* sc = states + (rec0 + c) * (size_t)DK * DV + dv0 + r16;
+#pragma unroll
+                    for (int half = 0; half < 2; ++half)
+#pragma unroll
+                        for (int n = 0; n < NTN; ++n)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                sc[(size_t)(32 * wave + 8 * grp + 4 * half + i) * DV + 16 * n] = S[half][n][i];
+                }
+            }
             // phase A: Vnew at this lane's 4 positions
             f32x4 P[NTN];
 #pragma unroll
@@ -301,6 +322,13 @@ __global__ __launch_bounds__(inter_threads<PFD>()) void inter_kernel(const uint8
 #pragma unroll
                 for (int i = 0; i < 4; ++i) vn[i] = cur.u[n][i] - P[n][i];
                 st4(&sV[kbP][n][lane][4 * halfP], vn);
+                if constexpr (STATES) {
+                    // positions 32(w/2) + 8(l/16) + 4(w%2) + i, the layout of U
+                    float* vc = vnew + (rec0 + c) * (size_t)C * DV + dv0 + 16 * n + r16;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        vc[(size_t)(32 * kbP + 8 * grp + 4 * halfP + i) * DV] = vn[i];
+                }
             }
             lds_barrier();
             // phase B: state update, decay first, then accumulate
@@ -333,6 +361,14 @@ __global__ __launch_bounds__(inter_threads<PFD>()) void inter_kernel(const uint8
                         const int dk = 32 * wave + 8 * grp + 4 * half + i;
                         hT[(((size_t)b * H + h) * DK + dk) * DV + dv0 + 16 * n + r16] = S[half][n][i];
                     }
+        }
+    } else if constexpr (STATES) {
+        // no output: keep the recurrence waves' barriers (initial state, then
+        // two per chunk)
+        lds_barrier();
+        for (int c = 0; c < nseg; ++c) {
+            lds_barrier();
+            lds_barrier();
         }
     } else {
         // ---- output waves ---------------------------------------------------
