@@ -109,6 +109,80 @@ def cpu_baseline(w, x, max_tokens: int, threads: int):
                       f"{threads} threads, {dt:.2f} s wall"}
 
 
+
+def call_bytes(kind: str, w, io_b: int, tokens: int, chains: int, h0: bool, backward: bool = False) -> int:
+    """The least HBM traffic of one whole call: every input read once and
+    every output written once (the chunk records and the backward's other
+    workspace arrays are the implementation's own and are not counted).
+    Forward: q, k, v, g, beta in, o out, per chain h0 in (if given) and hT
+    out.  Backward: the same inputs plus do, then dq, dk, dv, dg, dbeta out,
+    per chain h0 (if given) and dhT in, dh0 out.  tokens counts tokens over
+    all sequences (each with the workload's H heads); chains counts
+    (sequence, head) pairs."""
+    dk, dv = w.Dk, w.Dv
+    gate = 4 * dk if kind == "kda" else 4
+    beta = 4 if kind != "decay_la" else 0
+    inputs = io_b * (2 * dk + dv) + gate + beta
+    state = 4 * dk * dv
+    if backward:
+        per_th = inputs + io_b * dv + inputs
+        per_chain = state * ((1 if h0 else 0) + 2)
+    else:
+        per_th = inputs + io_b * dv
+        per_chain = state * ((1 if h0 else 0) + 1)
+    return per_th * tokens * w.H + per_chain * chains
+
+
+def whole_call_roofline(kernel: str, alg_bytes: int, avg_ms: float):
+    """HBM roofline of a whole library call (several launches), from its
+    least traffic and its average duration between HIP events on the launch
+    stream."""
+    gbs = alg_bytes / (avg_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "avg_ms": round(avg_ms, 4),
+            "alg_bytes": int(alg_bytes)}
+
+
+def time_calls(call, steps: int, warmup: int):
+    """(wall ms per call, average ms per call between HIP events recorded on
+    torch's current stream, which is the stream the library launches on)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record(stream)
+        call()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / steps
+    return ms, sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+
+
+def cpu_threads(args) -> int:
+    return args.cpu_threads or min(16, len(os.sched_getaffinity(0)))
+
+
+def cpu_baseline_backward(kind, x, do, dhT, Ts: int):
+    """The oracle's reverse sweep (fp64 numpy, one thread) over the first Ts
+    tokens of every head of the first sequence; tokens/s of that sample."""
+    from threadpoolctl import threadpool_limits
+    from oracle.backward import recurrence_backward
+    sl = lambda t: None if t is None else t[:1, :Ts].contiguous()
+    h0 = None if x.get("h0") is None else x["h0"][:1].transpose(-1, -2).contiguous()
+    dT = None if dhT is None else dhT[:1].transpose(-1, -2).contiguous()
+    t0 = time.perf_counter()
+    with threadpool_limits(1):
+        recurrence_backward(kind, sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]), h0, sl(do), dT)
+    dt = time.perf_counter() - t0
+    H = x["q"].shape[2]
+    return {"value": Ts / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{kind} H={H} first {Ts} tokens of one sequence, fp64 reverse sweep over tokens "
+                      f"(numpy, 1 thread), {dt:.2f} s wall"}
+
 def decode_bench(args):
     """Recurrent decode step: --decode-batch sequences x the workload's heads
     and head size, --decode-tokens new tokens each per call, the state
@@ -122,7 +196,8 @@ def decode_bench(args):
     w = w0.with_(name=w0.name + "_decode", B=args.decode_batch, T=args.decode_tokens, h0_std=0.5)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    d = {n: (t.to(dev) if t is not None else None) for n, t in generate(w).items()}
+    x = generate(w)
+    d = {n: (t.to(dev) if t is not None else None) for n, t in x.items()}
     state = d["h0"].clone()
     o = torch.empty(w.B, w.T, w.H, w.Dv, dtype=d["q"].dtype, device=dev)
     stream = torch.cuda.current_stream()
@@ -156,9 +231,26 @@ def decode_bench(args):
         "roofline": {"bound": "hbm", "kernel": "decode", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "avg_ms": round(k_ms, 4), "alg_bytes": int(alg)},
-        "cpu_baseline": None,
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_decode(w, x, cpu_threads(args)),
     }
     print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_decode(w, x, threads: int):
+    """The oracle's token recurrence on the same decode call (every sequence,
+    head and new token from the same states), repeated for about 2 s."""
+    import oracle
+    h0 = x["h0"].transpose(-1, -2).contiguous()
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.recurrence(w.kind, x["q"], x["k"], x["v"], x["g"], x["beta"], h0, nthreads=threads)
+        n += 1
+        dt = time.perf_counter() - t0
+        if dt >= 2.0:
+            break
+    return {"value": n * w.B * w.T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole decode call ({w.B} sequences x {w.T} tokens, H={w.H}) {n} times, fp64 token "
+                      f"recurrence, {threads} threads, {dt:.2f} s wall"}
 
 
 def varlen_bench(args):
@@ -176,7 +268,8 @@ def varlen_bench(args):
     cu = torch.tensor([0] + list(torch.tensor(lengths).cumsum(0).tolist()), dtype=torch.int32)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    d = {n: (t.to(dev) if t is not None else None) for n, t in generate(w).items()}
+    x = generate(w)
+    d = {n: (t.to(dev) if t is not None else None) for n, t in x.items()}
     sq = lambda t: None if t is None else t[0]
     cu = cu.to(dev)
     N = len(lengths)
@@ -184,14 +277,30 @@ def varlen_bench(args):
                      device=dev)
     call = lambda: dra.forward_varlen(w.kind, sq(d["q"]), sq(d["k"]), sq(d["v"]), sq(d["g"]), sq(d["beta"]), cu,
                                       workspace=ws)
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        call()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+    ms, ev_ms = time_calls(call, args.steps, args.warmup)
+    io_b = 2 if d["q"].dtype == torch.bfloat16 else 4
+    roof = whole_call_roofline("dr_forward_varlen (chunk table, K1, K2)",
+                               call_bytes(w.kind, w, io_b, T, N * w.H, h0=False), ev_ms)
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = cpu_threads(args)
+        # whole sequences from the front of the batch, up to --cpu-tokens
+        n, Ts = 0, 0
+        while n < N and (n == 0 or Ts + lengths[n] <= args.cpu_tokens):
+            Ts += lengths[n]
+            n += 1
+        import oracle
+        t0 = time.perf_counter()
+        a = 0
+        for i in range(n):
+            sl = lambda t: None if t is None else t[:, a:a + lengths[i]].contiguous()
+            oracle.recurrence(w.kind, sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]), None,
+                              nthreads=threads)
+            a += lengths[i]
+        dt = time.perf_counter() - t0
+        cpu = {"value": Ts / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"the first {n} sequences ({Ts} tokens, H={w.H}), fp64 token recurrence, "
+                         f"{threads} threads, {dt:.2f} s wall"}
     line = {
         "metric": "packed-sequence fwd tokens/sec (1 GPU)", "value": round(T / (ms / 1000.0), 1),
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -199,7 +308,7 @@ def varlen_bench(args):
         "dtype": "bf16" if d["q"].dtype == torch.bfloat16 else "f32", "data": "synthetic",
         "config": {"workload": f"{w.kind}_fwd_varlen N={N} T={T} H={w.H} dk={w.Dk} dv={w.Dv} C={w.C}",
                    "sequences": N, "min_len": min(lengths), "max_len": max(lengths), "parallelism": "single GPU"},
-        "roofline": None, "cpu_baseline": None,
+        "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
@@ -208,7 +317,7 @@ def backward_bench(args):
     """Backward of the workload's forward (dq, dk, dv, dg, dbeta, dh0 from do
     and dhT), inputs and cotangents resident in HBM, one dr_backward call per
     step timed with HIP events on the launch stream.  The split between its
-    four kernels comes from a rocprofv3 kernel trace (profiles/)."""
+    kernels comes from a rocprofv3 kernel trace (profiles/)."""
     import torch
     import delta_rule_rnn_amd as dra
     from delta_rule_rnn_amd.inputs import WORKLOADS, generate
@@ -216,27 +325,23 @@ def backward_bench(args):
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    d = {n: (t.to(dev) if t is not None else None) for n, t in generate(w).items()}
+    x = generate(w)
+    d = {n: (t.to(dev) if t is not None else None) for n, t in x.items()}
     gen = torch.Generator().manual_seed(99)
-    do = torch.randn(w.B, w.T, w.H, w.Dv, generator=gen).to(d["q"].dtype).to(dev)
-    dhT = (torch.randn(w.B, w.H, w.Dk, w.Dv, generator=gen) * 0.1).to(dev)
+    do_c = torch.randn(w.B, w.T, w.H, w.Dv, generator=gen).to(d["q"].dtype)
+    dhT_c = torch.randn(w.B, w.H, w.Dk, w.Dv, generator=gen) * 0.1
+    do, dhT = do_c.to(dev), dhT_c.to(dev)
     ws = torch.empty(dra.backward_workspace_bytes(w.kind, w.B, w.T, w.H, w.Dk, w.Dv, d["q"].dtype),
                      dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
     call = lambda: dra.backward(w.kind, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], do, dhT, workspace=ws)
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for e in evs:
-        e[0].record(stream)
-        call()
-        e[1].record(stream)
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1000.0 / args.steps
-    ev_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    ms, ev_ms = time_calls(call, args.steps, args.warmup)
     tokens = w.B * w.T
+    io_b = 2 if d["q"].dtype == torch.bfloat16 else 4
+    roof = whole_call_roofline("dr_backward (all launches)",
+                               call_bytes(w.kind, w, io_b, tokens, w.B * w.H, h0=d["h0"] is not None,
+                                          backward=True), ev_ms)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_backward(w.kind, x, do_c, dhT_c,
+                                                                   min(w.T, args.cpu_bwd_tokens))
     line = {
         "metric": "bwd tokens/sec (1 GPU), all gradients", "value": round(tokens / (ms / 1000.0), 1),
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -245,8 +350,7 @@ def backward_bench(args):
         "data": "synthetic",
         "config": {"workload": f"{w.kind}_bwd B={w.B} H={w.H} T={w.T} dk={w.Dk} dv={w.Dv} C={w.C}",
                    "workspace_bytes": ws.numel(), "parallelism": "single GPU"},
-        "median_ms_per_call_events": round(ev_ms[len(ev_ms) // 2], 4),
-        "roofline": None, "cpu_baseline": None,
+        "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
@@ -267,25 +371,29 @@ def backward_varlen_bench(args):
     N = len(lengths)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    d = {n: (t.to(dev) if t is not None else None) for n, t in generate(w).items()}
+    x = generate(w)
+    d = {n: (t.to(dev) if t is not None else None) for n, t in x.items()}
     sq = lambda t: None if t is None else t[0]
     cu = torch.tensor([0] + list(torch.tensor(lengths).cumsum(0).tolist()), dtype=torch.int32).to(dev)
     gen = torch.Generator().manual_seed(99)
-    do = torch.randn(T, w.H, w.Dv, generator=gen).to(d["q"].dtype).to(dev)
-    dhT = (torch.randn(N, w.H, w.Dk, w.Dv, generator=gen) * 0.1).to(dev)
-    h0 = (torch.randn(N, w.H, w.Dk, w.Dv, generator=gen) * 0.1).to(dev)
+    do_c = torch.randn(T, w.H, w.Dv, generator=gen).to(d["q"].dtype)
+    dhT_c = torch.randn(N, w.H, w.Dk, w.Dv, generator=gen) * 0.1
+    h0_c = torch.randn(N, w.H, w.Dk, w.Dv, generator=gen) * 0.1
+    do, dhT, h0 = do_c.to(dev), dhT_c.to(dev), h0_c.to(dev)
     ws = torch.empty(dra.backward_varlen_workspace_bytes(w.kind, N, T, w.H, w.Dk, w.Dv, d["q"].dtype),
                      dtype=torch.uint8, device=dev)
     call = lambda: dra.backward_varlen(w.kind, sq(d["q"]), sq(d["k"]), sq(d["v"]), sq(d["g"]), sq(d["beta"]), cu,
                                        h0, do, dhT, workspace=ws)
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        call()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+    ms, ev_ms = time_calls(call, args.steps, args.warmup)
+    io_b = 2 if d["q"].dtype == torch.bfloat16 else 4
+    roof = whole_call_roofline("dr_backward_varlen (all launches)",
+                               call_bytes(w.kind, w, io_b, T, N * w.H, h0=True, backward=True), ev_ms)
+    cpu = None
+    if not args.no_cpu_baseline:
+        # a prefix of the first sequence is itself a sequence
+        first = dict(x, h0=h0_c[:1])
+        cpu = cpu_baseline_backward(w.kind, first, do_c.unsqueeze(0), dhT_c[:1],
+                                    min(lengths[0], args.cpu_bwd_tokens))
     line = {
         "metric": "packed-sequence bwd tokens/sec (1 GPU), all gradients", "value": round(T / (ms / 1000.0), 1),
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -295,7 +403,7 @@ def backward_varlen_bench(args):
         "config": {"workload": f"{w.kind}_bwd_varlen N={N} T={T} H={w.H} dk={w.Dk} dv={w.Dv} C={w.C}",
                    "sequences": N, "min_len": min(lengths), "max_len": max(lengths),
                    "workspace_bytes": ws.numel(), "parallelism": "single GPU"},
-        "roofline": None, "cpu_baseline": None,
+        "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
@@ -313,7 +421,8 @@ def prologue_bench(args):
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    d = {n: (t.to(dev) if t is not None else None) for n, t in generate_raw(w).items()}
+    raw = generate_raw(w)
+    d = {n: (t.to(dev) if t is not None else None) for n, t in raw.items()}
     has_beta = w.kind != "decay_la"
     scale = w.Dk ** -0.5
     pro = dra.Prologue(qk_l2norm=True, scale=scale, beta_sigmoid=has_beta,
@@ -344,9 +453,29 @@ def prologue_bench(args):
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1000.0 / args.steps
 
-    ms = timeit(fused)
+    ms, ev_ms = time_calls(fused, args.steps, args.warmup)
     ms_unfused = timeit(unfused)
     tokens = w.B * w.T
+    io_b = 2 if d["q"].dtype == torch.bfloat16 else 4
+    roof = whole_call_roofline("dr_forward_prologue (K1 with the prologue, K2)",
+                               call_bytes(w.kind, w, io_b, tokens, w.B * w.H, h0=d["h0"] is not None), ev_ms)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        from oracle.prologue import apply
+        threads = cpu_threads(args)
+        # the numpy prologue dominates: half the forward's sample
+        Ts = min(w.T, max(1, args.cpu_tokens // 2))
+        sl = lambda t: None if t is None else t[:, :Ts].contiguous()
+        t0 = time.perf_counter()
+        q, k, g, beta = apply(w.kind, sl(raw["q"]), sl(raw["k"]), sl(raw["g"]), sl(raw["beta"]), qk_l2norm=True,
+                              scale=scale, beta_sigmoid=has_beta, A_log=raw["A_log"], dt_bias=raw["dt_bias"])
+        h0 = None if raw["h0"] is None else raw["h0"].transpose(-1, -2).contiguous()
+        oracle.recurrence(w.kind, q, k, sl(raw["v"]), g, beta, h0, nthreads=threads)
+        dt = time.perf_counter() - t0
+        cpu = {"value": w.B * Ts / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"{w.kind} B={w.B} H={w.H} first {Ts} of {w.T} tokens: fp64 prologue (numpy), then the "
+                         f"fp64 token recurrence on {threads} threads, {dt:.2f} s wall"}
     line = {
         "metric": "fwd tokens/sec (1 GPU) with the fused input prologue", "value": round(tokens / (ms / 1000.0), 1),
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -358,7 +487,7 @@ def prologue_bench(args):
                    "parallelism": "single GPU"},
         "unfused_prepass": {"ms_per_step": round(ms_unfused, 4),
                             "tokens_per_s": round(tokens / (ms_unfused / 1000.0), 1)},
-        "roofline": None, "cpu_baseline": None,
+        "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
@@ -372,6 +501,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens of the workload the CPU oracle is timed on")
+    ap.add_argument("--cpu-bwd-tokens", type=int, default=2048,
+                    help="tokens of one sequence the CPU oracle's backward is timed on")
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--mode", choices=("prefill", "decode", "varlen", "prologue", "backward", "backward_varlen"), default="prefill",
                     help="prefill: the chunked forward (the benchmark line); decode: the "
