@@ -111,4 +111,24 @@ def test_autograd_packed_with_prologue(kind):
         if leaf not in leaves:
             assert r is None
             continue
-        _same(n, leaves[leaf].grad, r)
+        if n in ("dA_log", "ddt_bias"):
+            _same_head_sum(n, leaves[leaf].grad, r, ref[3], plain)
+        else:
+            _same(n, leaves[leaf].grad, r)
+
+
+def _same_head_sum(name, a, b, dg, x):
+    """dA_log and ddt_bias are per-head sums over every token of fp32 terms
+    whose order the atomics do not fix: with the gate g^ = -exp(A_log)
+    softplus(a + dt_bias), the token terms are dg_t (ddt_bias) and
+    dg_t softplus(a_t + dt_bias) / sigmoid(a_t + dt_bias) (dA_log), dg the
+    gradient of the raw gate input.  Two summation orders of n fp32 terms
+    differ by at most about n eps sum|term|; with n in the hundreds that is
+    1e-5 of sum|term| per head."""
+    z = (x["g"] + x["dt_bias"]).float()
+    terms = dg.float().abs()
+    if name == "dA_log":
+        terms = terms * torch.nn.functional.softplus(z) / torch.sigmoid(z)
+    bound = 1e-5 * terms.sum(0)
+    err = (a.float() - b.float()).abs()
+    assert torch.all(err <= bound), (name, err.tolist(), bound.tolist())
