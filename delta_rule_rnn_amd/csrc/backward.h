@@ -565,7 +565,8 @@ struct StateSmem {
     static constexpr int LCT = C + 16;     // [C][C] read transposed
     // reverse pass
     static constexpr size_t D = 0, KBN = D + (size_t)DK * LSV, QT = KBN + (size_t)C * LDN, WT = QT + (size_t)C * LDT,
-                            AQK = WT + (size_t)C * LDT, DV = AQK + (size_t)C * LCT, DO = DV + (size_t)C * LSV,
+                            AQK = WT + (size_t)C * LDT, DV = AQK + (size_t)C * LCT, DV2 = DV + (size_t)C * LSV,
+                            DO = DV2 + (size_t)C * LSV,
                             RPHI = DO + (size_t)C * LSV, RSINK = RPHI + DK, REV = RSINK + 64;
 };
 
@@ -585,16 +586,30 @@ __device__ __forceinline__ void l2_touch(const float* __restrict__ src, size_t g
     }
 }
 
-// Both state passes run 4 compute waves and a fifth store wave.  The store
-// wave copies the tiles the compute waves publish in LDS (states, adjoints,
-// Vnew / dVnew) to HBM, so the compute waves never wait on a store (vector
-// memory counters count stores and loads in issue order).  Per chunk, three
+// The reverse pass runs 8 compute waves (two per SIMD, so that one's LDS and
+// memory waits overlap the other's products) and a ninth store wave.  The
+// store wave copies the tiles the compute waves publish in LDS (adjoints,
+// dVnew) to HBM, so the compute waves never wait on a store (vector memory
+// counters count stores and loads in issue order).  Per chunk, three
 // barriers separate: (A) staging of the chunk's operands | the store wave
-// writing the state that enters the chunk; (B) the Vnew / dVnew products;
-// (C) the state update in place | the store wave writing Vnew / dVnew.
-constexpr int kStateThreads = 320;
+// writing the adjoint that leaves the chunk; (B) the dVnew products; (C) the
+// adjoint update in place | the store wave writing dVnew.
+constexpr int kRevCompute = 512;
+constexpr int kStateThreads = kRevCompute + 64;
 
-
+// acc += A (B1 + B2) with the layout of mmk: the B operand is the sum of two
+// LDS tiles (the two halves of a split reduction), added as it is read.
+template <int K>
+__device__ __forceinline__ f32x4 mmk2(f32x4 acc, const float* A, int ar, int ak, const float* B1, const float* B2,
+                                      int bk, int bc, int lane) {
+    const int r = lane & 15, q = lane >> 4;
+    const float* a = A + r * ar + q * ak;
+    const int bo = q * bk + r * bc;
+#pragma unroll 8
+    for (int k0 = 0; k0 < K; k0 += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[k0 * ak], B1[bo + k0 * bk] + B2[bo + k0 * bk], acc, 0, 0, 0);
+    return acc;
+}
 
 // Reverse state pass, chunks in reverse: writes dS'_c (the exit-state adjoint
 // of chunk c) and dVnew_c, and dh0.
@@ -609,29 +624,33 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_rev_kernel(const floa
 {
     using P = Prep<DK>;
     using SM = StateSmem<DK>;
-    constexpr int DV = DK, LDN = SM::LDN, LDT = SM::LDT, LCT = SM::LCT, NVS = DV / kSV;
+    constexpr int DV = DK, LDN = SM::LDN, LDT = SM::LDT, LCT = SM::LCT, NVS = DV / kSV, NC = kRevCompute;
     constexpr bool DELTA = KIND != KIND_LA;
+    // dVnew tile ti is split over waves ti and ti + 4: wave ti takes Aqk^T dO
+    // and the first KS key channels of Kbar dS', wave ti + 4 the rest
+    constexpr int KS = (DK - C) / 2;
     __shared__ __attribute__((aligned(16))) float smem[SM::REV];
     float* sD = smem + SM::D;         // dS'
     float* sKb = smem + SM::KBN;
     float* sQt = smem + SM::QT;
     float* sW = smem + SM::WT;
     float* sAqk = smem + SM::AQK;
-    float* sDV = smem + SM::DV;       // dVnew
+    float* sDV = smem + SM::DV;       // dVnew = sDV + sDV2
+    float* sDV2 = smem + SM::DV2;
     float* sDO = smem + SM::DO;
     float* sPhi = smem + SM::RPHI;
     float* sink = smem + SM::RSINK;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const bool storer = tid >= 256;
+    const bool storer = tid >= NC;
     const int logical = xcd_logical(blockIdx.x, gridDim.x);
     const int chain = chain_of(pk, logical / NVS, H, (int)gridDim.x / NVS), dv0 = (logical % NVS) * kSV;
     const int h = chain % H;
     const ChainLoc cl = locate_chain(pk, chain, H, Tlen, NT);
     if (!storer) {
 #pragma unroll
-        for (int it_ = 0; it_ < (DK * kSV) / 256; ++it_) {
-            const int idx = tid + it_ * 256, r = idx / kSV, cc = idx % kSV;
+        for (int it_ = 0; it_ < (DK * kSV) / NC; ++it_) {
+            const int idx = tid + it_ * NC, r = idx / kSV, cc = idx % kSV;
             sD[r * LSV + cc] = dhT ? dhT[((size_t)chain * DK + r) * DV + dv0 + cc] : 0.f;
         }
     }
@@ -642,17 +661,17 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_rev_kernel(const floa
         // (A) every load of the chunk in flight; what (B) reads goes to LDS
         // now, Q~ and W (read only in (C)) after (B)'s products, so that
         // their fetch overlaps them
-        Staged<C, C, 256> ga;
-        Staged<C, DK, 256> gk, gq, gw;
+        Staged<C, C, NC> ga;
+        Staged<C, DK, NC> gk, gq, gw;
         if (!storer) {
-            constexpr int NDO = (C * kSV) / 256;
+            constexpr int NDO = (C * kSV) / NC;
             float xo[NDO];
             ga.load(pc + P::AQK, C, tid);
             gk.load(pc + P::KB, DK, tid);
             const float ph = tid < DK ? pc[P::PHI + tid] : 0.f;
 #pragma unroll
             for (int it_ = 0; it_ < NDO; ++it_) {
-                const int idx = tid + it_ * 256, r = idx / kSV, cc = idx % kSV;
+                const int idx = tid + it_ * NC, r = idx / kSV, cc = idx % kSV;
                 const int tok = c * C + r;
                 xo[it_] = to_f(dout[((cl.tok0 + min(tok, cl.tlim - 1)) * H + h) * DV + dv0 + cc]);
             }
@@ -663,20 +682,26 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_rev_kernel(const floa
             if (tid < DK) sPhi[tid] = ph;
 #pragma unroll
             for (int it_ = 0; it_ < NDO; ++it_) {
-                const int idx = tid + it_ * 256, r = idx / kSV, cc = idx % kSV;
+                const int idx = tid + it_ * NC, r = idx / kSV, cc = idx % kSV;
                 sDO[r * LSV + cc] = c * C + r < cl.tlim ? xo[it_] : 0.f;
             }
         } else {
-            unstage<DK, kSV, 64>(dhs + ci * DK * DV + dv0, DV, sD, LSV, tid - 256);
+            unstage<DK, kSV, 64>(dhs + ci * DK * DV + dv0, DV, sD, LSV, tid - NC);
         }
         lds_barrier();
-        // (B) dVnew = Aqk^T dO + Kbar dS': 4 tiles, one per compute wave
+        // (B) dVnew = Aqk^T dO + Kbar dS': 4 tiles, two waves each
         if (!storer) {
-            const int ti = wave;
-            f32x4 acc = mmk<C>(zero4(), sAqk + ti * 16, 1, LCT, sDO, LSV, 1, lane);
-            acc = mmk_a<DK>(acc, sKb + ti * 16 * LDN, LDN, sD, LSV, 1, lane);
+            const int ti = wave & 3;
+            f32x4 acc = zero4();
+            if (wave < 4) {
+                acc = mmk<C>(acc, sAqk + ti * 16, 1, LCT, sDO, LSV, 1, lane);
+                if constexpr (KS > 0) acc = mmk_a<KS>(acc, sKb + ti * 16 * LDN, LDN, sD, LSV, 1, lane);
+            } else {
+                acc = mmk_a<DK - KS>(acc, sKb + ti * 16 * LDN + KS, LDN, sD + KS * LSV, LSV, 1, lane);
+            }
+            float* dst = wave < 4 ? sDV : sDV2;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sDV[(ti * 16 + arow(lane, i)) * LSV + (lane & 15)] = acc[i];
+            for (int i = 0; i < 4; ++i) dst[(ti * 16 + arow(lane, i)) * LSV + (lane & 15)] = acc[i];
             // (C)'s operands: the previous chunk's (C) finished reading these
             // buffers before the end of its step
             gq.store(sQt, LDT, tid);
@@ -685,17 +710,19 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_rev_kernel(const floa
             // that waiting for Q~ and W does not wait for these)
             if (c > 0) {
                 const float* pn = pc - P::FLOATS;
-                l2_touch(pn + P::AQK, C, C, C, tid, 256, sink);
-                l2_touch(pn + P::KB, DK, C, DK, tid, 256, sink);
-                l2_touch(pn + P::QT, DK, C, DK, tid, 256, sink);
-                if constexpr (DELTA) l2_touch(pn + P::W, DK, C, DK, tid, 256, sink);
+                l2_touch(pn + P::AQK, C, C, C, tid, NC, sink);
+                l2_touch(pn + P::KB, DK, C, DK, tid, NC, sink);
+                l2_touch(pn + P::QT, DK, C, DK, tid, NC, sink);
+                if constexpr (DELTA) l2_touch(pn + P::W, DK, C, DK, tid, NC, sink);
             }
         }
         lds_barrier();
-        // (C) dS = Q~^T dO + diag(phi) dS' - W^T dVnew, in place; the store
-        // wave writes dVnew
+        // (C) dS = Q~^T dO + diag(phi) dS' - W^T dVnew, in place, one tile
+        // per wave; the store wave writes dVnew
         if (!storer) {
-            for (int ti = wave; ti < DK / 16; ti += 4) {
+            static_assert(DK / 16 <= 8, "one adjoint tile per compute wave");
+            const int ti = wave;
+            if (ti < DK / 16) {
                 f32x4 acc;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -704,7 +731,7 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_rev_kernel(const floa
                 }
                 acc = mmk<C>(acc, sQt + ti * 16, 1, LDT, sDO, LSV, 1, lane);
                 if constexpr (DELTA) {
-                    const f32x4 wv = mmk<C>(zero4(), sW + ti * 16, 1, LDT, sDV, LSV, 1, lane);
+                    const f32x4 wv = mmk2<C>(zero4(), sW + ti * 16, 1, LDT, sDV, sDV2, LSV, 1, lane);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) acc[i] -= wv[i];
                 }
@@ -712,11 +739,20 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_rev_kernel(const floa
                 for (int i = 0; i < 4; ++i) sD[(ti * 16 + arow(lane, i)) * LSV + (lane & 15)] = acc[i];
             }
         } else {
-            unstage<C, kSV, 64>(dvn + ci * C * DV + dv0, DV, sDV, LSV, tid - 256);
+            // dVnew = sDV + sDV2, [C][16], 16 floats per store-wave thread
+            const int t = tid - NC;
+            float* dst = dvn + ci * C * DV + dv0;
+#pragma unroll
+            for (int i = 0; i < (C * kSV) / (4 * 64); ++i) {
+                const int idx = t + i * 64, r = idx / (kSV / 4), c4 = (idx % (kSV / 4)) * 4;
+                const f32x4 x = *reinterpret_cast<const f32x4*>(sDV + r * LSV + c4);
+                const f32x4 y = *reinterpret_cast<const f32x4*>(sDV2 + r * LSV + c4);
+                *reinterpret_cast<f32x4*>(dst + (size_t)r * DV + c4) = x + y;
+            }
         }
         lds_barrier();
     }
-    if (dh0 && !storer) unstage<DK, kSV, 256>(dh0 + (size_t)chain * DK * DV + dv0, DV, sD, LSV, tid);
+    if (dh0 && tid < 256) unstage<DK, kSV, 256>(dh0 + (size_t)chain * DK * DV + dv0, DV, sD, LSV, tid);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 

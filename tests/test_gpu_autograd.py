@@ -1,20 +1,27 @@
-"""GPU: the differentiable entry point chunk_delta_rule gives, through
-torch.autograd, exactly the gradients of the library's backward called
-directly with the same cotangents (which the backward parity tests compare
-with the fp64 oracle), for the dense and packed layouts, with and without
-the prologue.  dq, dk, dv and the state gradients are bit-identical; dbeta,
-dg and the per-head parameter gradients add per-wave partials with atomics
-in no fixed order, so they are compared to fp32 reassociation (1e-5 of
-their largest magnitude).
+"""GPU: the differentiable entry point chunk_delta_rule, through
+torch.autograd, for the dense and packed layouts, with and without the
+prologue.
+
+dq, dk, dv and the state gradients are deterministic: they must equal, bit
+for bit, those of the library's backward called directly with the same
+cotangents.  dbeta, dg and the per-head parameter gradients add per-wave
+partials with atomics in no fixed order, so two calls may differ by fp32
+reassociation, which cancellation inside those sums can make large next to
+the result.  They are compared with the fp64 oracle instead (the reverse
+sweep, and for the prologue its chain rule), at the tolerances of the
+backward parity tests: a wrong tensor or cotangent in the autograd plumbing
+fails either check.
 """
 from __future__ import annotations
 
+import numpy as np
 import pytest
 import torch
 
+from oracle.backward import recurrence_backward
 from delta_rule_rnn_amd.inputs import Workload, generate, generate_raw
 
-from .test_gpu_parity import to_dev
+from .test_gpu_parity import assert_close, to_dev
 
 pytestmark = pytest.mark.gpu
 EXACT = ("dq", "dk", "dv", "dh0")
@@ -25,12 +32,8 @@ def _ops():
     return dra
 
 
-def _same(name, a, b):
-    if name in EXACT:
-        assert torch.equal(a, b), name
-    else:
-        err = (a.float() - b.float()).abs().max().item()
-        assert err <= 1e-5 * max(b.float().abs().max().item(), 1e-30), (name, err)
+def _cpu(t):
+    return None if t is None else t.detach().float().cpu()
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
@@ -38,7 +41,8 @@ def _same(name, a, b):
 def test_autograd_dense_matches_backward(kind, dt):
     dra = _ops()
     w = Workload(f"{kind}_ag", kind, dt, B=2, H=2, T=150, Dk=64, Dv=64, h0_std=0.2, seed=91)
-    d = to_dev(generate(w))
+    x = generate(w)
+    d = to_dev(x)
     names = ["q", "k", "v", "g", "beta", "h0"]
     leaves = {n: (d[n].clone().requires_grad_(True) if d[n] is not None else None) for n in names}
     o, hT = dra.chunk_delta_rule(kind, leaves["q"], leaves["k"], leaves["v"], leaves["g"], leaves["beta"],
@@ -47,14 +51,20 @@ def test_autograd_dense_matches_backward(kind, dt):
     w1 = torch.randn(o.shape, generator=gen).to("cuda:0")
     w2 = (torch.randn(hT.shape, generator=gen) * 0.1).to("cuda:0")
     ((o.float() * w1).sum() + (hT * w2).sum()).backward()
-    ref = dra.backward(kind, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], w1.to(o.dtype).contiguous(), w2)
+    do = w1.to(o.dtype).contiguous()
+    ref = dra.backward(kind, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], do, w2)
     torch.cuda.synchronize()
-    for n, r in zip(["dq", "dk", "dv", "dg", "dbeta", "dh0"], ref):
-        leaf = leaves[{"dq": "q", "dk": "k", "dv": "v", "dg": "g", "dbeta": "beta", "dh0": "h0"}[n]]
-        if leaf is None:
-            assert r is None
-            continue
-        _same(n, leaf.grad, r)
+    grads = dict(zip(["dq", "dk", "dv", "dg", "dbeta", "dh0"], ref))
+    leaf_of = {"dq": "q", "dk": "k", "dv": "v", "dh0": "h0"}
+    for n in EXACT:
+        assert torch.equal(leaves[leaf_of[n]].grad, grads[n]), n
+    orc = recurrence_backward(kind, x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"].transpose(-1, -2),
+                              _cpu(do), _cpu(w2).transpose(-1, -2))
+    assert_close(leaves["g"].grad.float().cpu().numpy(), orc["dg"], dt, f"{kind} {dt} autograd dg")
+    if kind == "decay_la":
+        assert grads["dbeta"] is None and leaves["beta"] is None
+    else:
+        assert_close(leaves["beta"].grad.float().cpu().numpy(), orc["dbeta"], dt, f"{kind} {dt} autograd dbeta")
 
 
 def test_autograd_output_only():
@@ -78,14 +88,18 @@ def test_autograd_packed_with_prologue(kind):
     """Packed sequences (one empty) on raw projections through the prologue:
     gradients of every raw input, the per-sequence initial states and, for
     the scalar gate, A_log and dt_bias."""
+    from oracle import prologue as opro
     dra = _ops()
     lengths = [90, 0, 64, 33]
-    T = sum(lengths)
-    w = Workload(f"{kind}_ag_pk", kind, "bf16", B=1, H=2, T=T, Dk=64, Dv=64, seed=95)
-    x = to_dev(generate_raw(w))
-    cu = torch.tensor([0, 90, 90, 154, 187], dtype=torch.int32, device="cuda:0")
-    N = len(lengths)
-    h0 = (torch.randn(N, 2, 64, 64, generator=torch.Generator().manual_seed(96)) * 0.2).to("cuda:0")
+    T, H, D, N = sum(lengths), 2, 64, len(lengths)
+    cu = [0]
+    for n in lengths:
+        cu.append(cu[-1] + n)
+    w = Workload(f"{kind}_ag_pk", kind, "bf16", B=1, H=H, T=T, Dk=D, Dv=D, seed=95)
+    raw = generate_raw(w)
+    x = to_dev(raw)
+    cu_t = torch.tensor(cu, dtype=torch.int32, device="cuda:0")
+    h0 = (torch.randn(N, H, D, D, generator=torch.Generator().manual_seed(96)) * 0.2).to("cuda:0")
     gate = x["A_log"] is not None
     sq = lambda t: t[0].contiguous()
     leaves = {"q": sq(x["q"]), "k": sq(x["k"]), "v": sq(x["v"]), "g": sq(x["g"]), "beta": sq(x["beta"]), "h0": h0}
@@ -95,40 +109,54 @@ def test_autograd_packed_with_prologue(kind):
     mk = lambda src: dra.Prologue(qk_l2norm=True, scale=0.125, beta_sigmoid=True,
                                   A_log=src.get("A_log"), dt_bias=src.get("dt_bias"))
     o, hT = dra.chunk_delta_rule(kind, leaves["q"], leaves["k"], leaves["v"], leaves["g"], leaves["beta"],
-                                 initial_state=leaves["h0"], output_final_state=True, cu_seqlens=cu,
+                                 initial_state=leaves["h0"], output_final_state=True, cu_seqlens=cu_t,
                                  prologue=mk(leaves))
     gen = torch.Generator().manual_seed(97)
     w1 = torch.randn(o.shape, generator=gen).to("cuda:0")
     w2 = (torch.randn(hT.shape, generator=gen) * 0.1).to("cuda:0")
     ((o.float() * w1).sum() + (hT * w2).sum()).backward()
     plain = {n: t.detach() for n, t in leaves.items()}
-    ref = dra.backward_varlen(kind, plain["q"], plain["k"], plain["v"], plain["g"], plain["beta"], cu, plain["h0"],
-                              w1.to(o.dtype).contiguous(), w2, prologue=mk(plain))
+    do = w1.to(o.dtype).contiguous()
+    ref = dra.backward_varlen(kind, plain["q"], plain["k"], plain["v"], plain["g"], plain["beta"], cu_t, plain["h0"],
+                              do, w2, prologue=mk(plain))
     torch.cuda.synchronize()
-    pairs = [("dq", "q"), ("dk", "k"), ("dv", "v"), ("dg", "g"), ("dbeta", "beta"), ("dh0", "h0"),
-             ("dA_log", "A_log"), ("ddt_bias", "dt_bias")]
-    for (n, leaf), r in zip(pairs, ref):
-        if leaf not in leaves:
-            assert r is None
+    grads = dict(zip(["dq", "dk", "dv", "dg", "dbeta", "dh0", "dA_log", "ddt_bias"], ref))
+    for n, leaf in (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dh0", "h0")):
+        assert torch.equal(leaves[leaf].grad, grads[n]), n
+    if not gate:
+        assert grads["dA_log"] is None and grads["ddt_bias"] is None
+
+    # the oracle: prologue, reverse sweep per sequence, chain rule back
+    ok = dict(qk_l2norm=True, scale=0.125, beta_sigmoid=True,
+              A_log=raw["A_log"] if gate else None, dt_bias=raw["dt_bias"] if gate else None)
+    q2, k2, g2, b2 = opro.apply(kind, raw["q"], raw["k"], raw["g"], raw["beta"], **ok)
+    do_c, w2_c, h0_c = _cpu(do)[None], _cpu(w2), _cpu(h0)
+    core_dg = np.zeros_like(g2)
+    dg_got = leaves["g"].grad.float().cpu().numpy()[None]
+    db_got = leaves["beta"].grad.float().cpu().numpy()[None]
+    for i in range(N):
+        a, b = cu[i], cu[i + 1]
+        if a == b:
             continue
-        if n in ("dA_log", "ddt_bias"):
-            _same_head_sum(n, leaves[leaf].grad, r, ref[3], plain)
-        else:
-            _same(n, leaves[leaf].grad, r)
-
-
-def _same_head_sum(name, a, b, dg, x):
-    """dA_log and ddt_bias are per-head sums over every token of fp32 terms
-    whose order the atomics do not fix: with the gate g^ = -exp(A_log)
-    softplus(a + dt_bias), the token terms are dg_t (ddt_bias) and
-    dg_t softplus(a_t + dt_bias) / sigmoid(a_t + dt_bias) (dA_log), dg the
-    gradient of the raw gate input.  Two summation orders of n fp32 terms
-    differ by at most about n eps sum|term|; with n in the hundreds that is
-    1e-5 of sum|term| per head."""
-    z = (x["g"] + x["dt_bias"]).float()
-    terms = dg.float().abs()
-    if name == "dA_log":
-        terms = terms * torch.nn.functional.softplus(z) / torch.sigmoid(z)
-    bound = 1e-5 * terms.sum(0)
-    err = (a.float() - b.float()).abs()
-    assert torch.all(err <= bound), (name, err.tolist(), bound.tolist())
+        sl = lambda t: np.ascontiguousarray(t[:, a:b])
+        core = recurrence_backward(kind, sl(q2), sl(k2), raw["v"][:, a:b], sl(g2), sl(b2),
+                                   h0_c[i:i + 1].transpose(-1, -2), do_c[:, a:b], w2_c[i:i + 1].transpose(-1, -2))
+        core_dg[:, a:b] = core["dg"]
+        sr = lambda t: t[:, a:b]
+        r = opro.apply_backward(kind, sr(raw["q"]), sr(raw["k"]), sr(raw["g"]), sr(raw["beta"]), core["dq"],
+                                core["dk"], core["dg"], core["dbeta"], **ok)
+        assert_close(dg_got[:, a:b], r["dg"], "bf16", f"{kind} autograd seq {i} dg")
+        assert_close(db_got[:, a:b], r["dbeta"], "bf16", f"{kind} autograd seq {i} dbeta")
+    if gate:
+        # per-head sums over every token, held to the bf16 tolerance times
+        # sum_t |coef_t| * max_t |dg^_t| (the size of the terms they add)
+        full = opro.apply_backward(kind, raw["q"], raw["k"], raw["g"], raw["beta"], np.zeros_like(q2),
+                                   np.zeros_like(k2), core_dg, None, **ok)
+        gh = opro.scalar_gate(raw["g"], raw["A_log"], raw["dt_bias"])
+        coef_dt = -np.exp(opro._f64(raw["A_log"])) * opro.sigmoid(opro._f64(raw["g"]) + opro._f64(raw["dt_bias"]))
+        dgmax = np.max(np.abs(core_dg), axis=(0, 1))
+        for name, leaf, coef in (("dA_log", "A_log", gh), ("ddt_bias", "dt_bias", coef_dt)):
+            val = leaves[leaf].grad.float().cpu().numpy()
+            scale = np.sum(np.abs(coef), axis=(0, 1)) * dgmax
+            err = np.abs(val - full[name])
+            assert np.all(err <= 2e-2 * scale), f"{kind} autograd {name}: |err| {err} > 2e-2 * {scale}"
