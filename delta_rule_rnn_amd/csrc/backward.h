@@ -586,16 +586,15 @@ __device__ __forceinline__ void l2_touch(const float* __restrict__ src, size_t g
     }
 }
 
-// The reverse pass runs 8 compute waves (two per SIMD, so that one's LDS and
-// memory waits overlap the other's products) and a ninth store wave.  The
-// store wave copies the tiles the compute waves publish in LDS (adjoints,
-// dVnew) to HBM, so the compute waves never wait on a store (vector memory
-// counters count stores and loads in issue order).  Per chunk, three
-// barriers separate: (A) staging of the chunk's operands | the store wave
-// writing the adjoint that leaves the chunk; (B) the dVnew products; (C) the
-// adjoint update in place | the store wave writing dVnew.
+// The reverse pass runs 8 waves, two per SIMD, so that one wave's LDS and
+// memory waits overlap the other's products.  Each chunk's operands are
+// loaded one step ahead into registers: Aqk, Kbar and dO right after the
+// previous step's copies went to LDS in (A), Q~ and W after theirs in (B).
+// Per chunk, three barriers separate: (A) Aqk, Kbar, dO to LDS; (B) the
+// dVnew products, Q~ and W to LDS, the exit adjoint dS'_c stored; (C) the
+// adjoint update in place, dVnew stored.
 constexpr int kRevCompute = 512;
-constexpr int kStateThreads = kRevCompute + 64;
+constexpr int kStateThreads = kRevCompute;
 
 // acc += A (B1 + B2) with the layout of mmk: the B operand is the sum of two
 // LDS tiles (the two halves of a split reduction), added as it is read.
@@ -642,55 +641,59 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_rev_kernel(const floa
     float* sink = smem + SM::RSINK;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const bool storer = tid >= NC;
     const int logical = xcd_logical(blockIdx.x, gridDim.x);
     const int chain = chain_of(pk, logical / NVS, H, (int)gridDim.x / NVS), dv0 = (logical % NVS) * kSV;
     const int h = chain % H;
     const ChainLoc cl = locate_chain(pk, chain, H, Tlen, NT);
-    if (!storer) {
+    constexpr int NDO = (C * kSV) / NC;
+    Staged<C, C, NC> ga;
+    Staged<C, DK, NC> gk, gq, gw;
+    float xo[NDO];
+    float ph = 0.f;
+    // every load unconditional: rows of dO past the end read the last row
+    auto load_a = [&](int c) {
+        const float* pc = prep + (cl.ci0 + c) * P::FLOATS;
+        ga.load(pc + P::AQK, C, tid);
+        gk.load(pc + P::KB, DK, tid);
+        ph = tid < DK ? pc[P::PHI + tid] : 0.f;
 #pragma unroll
-        for (int it_ = 0; it_ < (DK * kSV) / NC; ++it_) {
+        for (int it_ = 0; it_ < NDO; ++it_) {
             const int idx = tid + it_ * NC, r = idx / kSV, cc = idx % kSV;
-            sD[r * LSV + cc] = dhT ? dhT[((size_t)chain * DK + r) * DV + dv0 + cc] : 0.f;
+            xo[it_] = to_f(dout[((cl.tok0 + min(c * C + r, cl.tlim - 1)) * H + h) * DV + dv0 + cc]);
         }
+    };
+    auto load_b = [&](int c) {
+        const float* pc = prep + (cl.ci0 + c) * P::FLOATS;
+        gq.load(pc + P::QT, DK, tid);
+        if constexpr (DELTA) gw.load(pc + P::W, DK, tid);
+    };
+    if (cl.nseg > 0) {
+        load_a(cl.nseg - 1);
+        load_b(cl.nseg - 1);
+    }
+#pragma unroll
+    for (int it_ = 0; it_ < (DK * kSV) / NC; ++it_) {
+        const int idx = tid + it_ * NC, r = idx / kSV, cc = idx % kSV;
+        sD[r * LSV + cc] = dhT ? dhT[((size_t)chain * DK + r) * DV + dv0 + cc] : 0.f;
     }
     lds_barrier();
     for (int c = cl.nseg - 1; c >= 0; --c) {
         const size_t ci = cl.ci0 + c;
-        const float* pc = prep + ci * P::FLOATS;
-        // (A) every load of the chunk in flight; what (B) reads goes to LDS
-        // now, Q~ and W (read only in (C)) after (B)'s products, so that
-        // their fetch overlaps them
-        Staged<C, C, NC> ga;
-        Staged<C, DK, NC> gk, gq, gw;
-        if (!storer) {
-            constexpr int NDO = (C * kSV) / NC;
-            float xo[NDO];
-            ga.load(pc + P::AQK, C, tid);
-            gk.load(pc + P::KB, DK, tid);
-            const float ph = tid < DK ? pc[P::PHI + tid] : 0.f;
+        const int cn = c > 0 ? c - 1 : 0;    // the next chunk (the last reloads itself)
+        // (A) Aqk, Kbar, dO, phi to LDS; the next chunk's copies in flight
+        ga.store(sAqk, LCT, tid);
+        gk.store(sKb, LDN, tid);
+        if (tid < DK) sPhi[tid] = ph;
 #pragma unroll
-            for (int it_ = 0; it_ < NDO; ++it_) {
-                const int idx = tid + it_ * NC, r = idx / kSV, cc = idx % kSV;
-                const int tok = c * C + r;
-                xo[it_] = to_f(dout[((cl.tok0 + min(tok, cl.tlim - 1)) * H + h) * DV + dv0 + cc]);
-            }
-            gq.load(pc + P::QT, DK, tid);
-            if constexpr (DELTA) gw.load(pc + P::W, DK, tid);
-            ga.store(sAqk, LCT, tid);
-            gk.store(sKb, LDN, tid);
-            if (tid < DK) sPhi[tid] = ph;
-#pragma unroll
-            for (int it_ = 0; it_ < NDO; ++it_) {
-                const int idx = tid + it_ * NC, r = idx / kSV, cc = idx % kSV;
-                sDO[r * LSV + cc] = c * C + r < cl.tlim ? xo[it_] : 0.f;
-            }
-        } else {
-            unstage<DK, kSV, 64>(dhs + ci * DK * DV + dv0, DV, sD, LSV, tid - NC);
+        for (int it_ = 0; it_ < NDO; ++it_) {
+            const int idx = tid + it_ * NC, r = idx / kSV, cc = idx % kSV;
+            sDO[r * LSV + cc] = c * C + r < cl.tlim ? xo[it_] : 0.f;
         }
+        load_a(cn);
         lds_barrier();
-        // (B) dVnew = Aqk^T dO + Kbar dS': 4 tiles, two waves each
-        if (!storer) {
+        // (B) dVnew = Aqk^T dO + Kbar dS': 4 tiles, two waves each; Q~ and W
+        // (read only in (C)) to LDS, the next chunk's in flight; dS'_c out
+        {
             const int ti = wave & 3;
             f32x4 acc = zero4();
             if (wave < 4) {
@@ -702,14 +705,14 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_rev_kernel(const floa
             float* dst = wave < 4 ? sDV : sDV2;
 #pragma unroll
             for (int i = 0; i < 4; ++i) dst[(ti * 16 + arow(lane, i)) * LSV + (lane & 15)] = acc[i];
-            // (C)'s operands: the previous chunk's (C) finished reading these
-            // buffers before the end of its step
             gq.store(sQt, LDT, tid);
             if constexpr (DELTA) gw.store(sW, LDT, tid);
-            // the previous chunk's lines into L2 (after the stores above, so
-            // that waiting for Q~ and W does not wait for these)
-            if (c > 0) {
-                const float* pn = pc - P::FLOATS;
+            load_b(cn);
+            constexpr int NS = (DK * kSV) / 4 < NC ? (DK * kSV) / 4 : NC;
+            if (tid < NS) unstage<DK, kSV, NS>(dhs + ci * DK * DV + dv0, DV, sD, LSV, tid);
+            // the lines of the chunk after the one in flight into L2
+            if (c > 1) {
+                const float* pn = prep + (ci - 2) * P::FLOATS;
                 l2_touch(pn + P::AQK, C, C, C, tid, NC, sink);
                 l2_touch(pn + P::KB, DK, C, DK, tid, NC, sink);
                 l2_touch(pn + P::QT, DK, C, DK, tid, NC, sink);
@@ -718,9 +721,9 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_rev_kernel(const floa
         }
         lds_barrier();
         // (C) dS = Q~^T dO + diag(phi) dS' - W^T dVnew, in place, one tile
-        // per wave; the store wave writes dVnew
-        if (!storer) {
-            static_assert(DK / 16 <= 8, "one adjoint tile per compute wave");
+        // per wave; dVnew = sDV + sDV2 out
+        {
+            static_assert(DK / 16 <= 8, "one adjoint tile per wave");
             const int ti = wave;
             if (ti < DK / 16) {
                 f32x4 acc;
@@ -738,16 +741,11 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_rev_kernel(const floa
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sD[(ti * 16 + arow(lane, i)) * LSV + (lane & 15)] = acc[i];
             }
-        } else {
-            // dVnew = sDV + sDV2, [C][16], 16 floats per store-wave thread
-            const int t = tid - NC;
-            float* dst = dvn + ci * C * DV + dv0;
-#pragma unroll
-            for (int i = 0; i < (C * kSV) / (4 * 64); ++i) {
-                const int idx = t + i * 64, r = idx / (kSV / 4), c4 = (idx % (kSV / 4)) * 4;
+            if (tid < (C * kSV) / 4) {
+                const int r = tid / (kSV / 4), c4 = (tid % (kSV / 4)) * 4;
                 const f32x4 x = *reinterpret_cast<const f32x4*>(sDV + r * LSV + c4);
                 const f32x4 y = *reinterpret_cast<const f32x4*>(sDV2 + r * LSV + c4);
-                *reinterpret_cast<f32x4*>(dst + (size_t)r * DV + c4) = x + y;
+                *reinterpret_cast<f32x4*>(dvn + ci * C * DV + dv0 + (size_t)r * DV + c4) = x + y;
             }
         }
         lds_barrier();
