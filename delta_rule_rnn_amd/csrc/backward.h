@@ -301,7 +301,11 @@ __device__ __forceinline__ void unstage(float* __restrict__ dst, size_t gs, cons
 }
 
 // ===========================================================================
-// Prep: one 256-thread workgroup per (chunk, head, batch), heads fastest.
+constexpr int kPrepThreads = 512;
+
+// Prep: one 512-thread workgroup per (chunk, head, batch), heads fastest
+// (one workgroup per CU by LDS: eight waves keep loads and products in
+// flight together).
 // ===========================================================================
 template <int KIND, typename T, int DK>
 struct PrepSmem {
@@ -313,14 +317,14 @@ struct PrepSmem {
 };
 
 template <int KIND, typename T, int DK>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
+__global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                        const float* __restrict__ g,
                                                        const float* __restrict__ beta, float* __restrict__ prep,
                                                        int Tlen, int H, int NT, Pack pk)
 {
     using P = Prep<DK>;
     using SM = PrepSmem<KIND, T, DK>;
-    constexpr int DV = DK, LDK = SM::LDK;
+    constexpr int DV = DK, LDK = SM::LDK, NTH = kPrepThreads, NW = NTH / 64;
     constexpr bool DELTA = KIND != KIND_LA;
     constexpr bool PERCH = KIND == KIND_KDA;
     __shared__ __attribute__((aligned(16))) float smem[SM::FLOATS];
@@ -342,8 +346,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
 
     // ---- inputs, rows past the end of a ragged chunk zero
     #pragma unroll 8
-    for (int it_ = 0; it_ < (C * DK) / 256; ++it_) {
-        const int idx = tid + it_ * 256;
+    for (int it_ = 0; it_ < (C * DK) / NTH; ++it_) {
+        const int idx = tid + it_ * NTH;
         const int r = idx / DK, d = idx % DK;
         // rows past the end load the last valid row (every load unconditional)
         const bool ok = r < nvalid;
@@ -370,10 +374,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
 
     // ---- gamma and the separable operands
     if constexpr (PERCH) {
-        // cumsum down each column by 256 / DK threads, each over a block of
+        // cumsum down each column by NTH / DK threads, each over a block of
         // rows: block sums, then each block's running sum from the sum of the
         // blocks above it (sL is free until L is formed)
-        constexpr int NB = 256 / DK, RB = C / NB;
+        constexpr int NB = NTH / DK, RB = C / NB;
         float* sBlk = sL;
         const int d = tid % DK, b = tid / DK;
         float bs = 0.f;
@@ -423,8 +427,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
         lds_barrier();
         const float gl = sGam[C - 1];
         #pragma unroll 8
-        for (int it_ = 0; it_ < (C * DK) / 256; ++it_) {
-            const int idx = tid + it_ * 256;
+        for (int it_ = 0; it_ < (C * DK) / NTH; ++it_) {
+            const int idx = tid + it_ * NTH;
             const int r = idx / DK, d = idx % DK;
             out[P::QT + (size_t)r * DK + d] = sQ[r * LDK + d] * __builtin_amdgcn_exp2f(sGam[r]);
             out[P::KB + (size_t)r * DK + d] = sA[r * LDK + d] * __builtin_amdgcn_exp2f(gl - sGam[r]);
@@ -437,7 +441,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
     lds_barrier();
 
     // ---- L and Aqk: 16 tiles each, 32 jobs over 4 waves
-    for (int job = wave; job < 32; job += 4) {
+    for (int job = wave; job < 32; job += NW) {
         const bool isL = job < 16;
         const int t = job & 15, ti = t >> 2, tj = t & 3;
         f32x4 acc = zero4();
@@ -483,8 +487,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
 #pragma unroll
             for (int i = 0; i < 16; ++i) sT[(o + i) * LDC + o + j] = t[i];
         } else {
-            // zero blocks above the diagonal: 6 blocks of 256 over 192 threads
-            for (int idx = tid - 64; idx < 6 * 256; idx += 192) {
+            // zero blocks above the diagonal: 6 blocks of 256 over NTH - 64 threads
+            for (int idx = tid - 64; idx < 6 * 256; idx += NTH - 64) {
                 const int blk = idx >> 8, e = idx & 255;
                 const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
                 const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
@@ -512,8 +516,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
             lds_barrier();
         }
         #pragma unroll 8
-        for (int it_ = 0; it_ < (C * C) / 256; ++it_) {
-            const int idx = tid + it_ * 256;
+        for (int it_ = 0; it_ < (C * C) / NTH; ++it_) {
+            const int idx = tid + it_ * NTH;
             out[P::TI + idx] = sT[(idx / C) * LDC + idx % C];
         }
     }
@@ -522,15 +526,15 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
     // takes U, and Vnew, from the forward's own kernels)
     if constexpr (DELTA) {
         #pragma unroll 8
-        for (int it_ = 0; it_ < (C * DK) / 256; ++it_) {
-            const int idx = tid + it_ * 256;
+        for (int it_ = 0; it_ < (C * DK) / NTH; ++it_) {
+            const int idx = tid + it_ * NTH;
             const int r = idx / DK, d = idx % DK;
             sA[r * LDK + d] *= PERCH ? sBeta[r] : sBeta[r] * __builtin_amdgcn_exp2f(sGam[r]);
         }
         lds_barrier();
         // (C/16) x (DK/16) tiles
         constexpr int NTL = 4 * (DK / 16);
-        for (int t = wave; t < NTL; t += 4) {
+        for (int t = wave; t < NTL; t += NW) {
             const int ti = t / (DK / 16), tj = t % (DK / 16);
             // T is lower triangular: the reduction stops at block ti
             f32x4 acc = zero4();

@@ -521,7 +521,7 @@ dr_status launch_backward_t(const BwdArgs& a, hipStream_t st) {
     const long long items = a.pk.table ? (long long)a.pk.maxchunks * a.H : (long long)a.B * a.NT * a.H;
     const long long slices = (long long)a.B * a.H * (D / kSV);
     if (items > 0x7fffffffLL || slices > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((bwd_prep_kernel<KIND, E, D>), dim3((unsigned)items), dim3(256), 0, st, q, k, a.g, a.beta,
+    hipLaunchKernelGGL((bwd_prep_kernel<KIND, E, D>), dim3((unsigned)items), dim3(kPrepThreads), 0, st, q, k, a.g, a.beta,
                        prep, a.T, a.H, a.NT, a.pk);
     dr_status s = check_launch();
     if (s != DR_OK) return s;
