@@ -622,7 +622,7 @@ dr_status backward_impl(int kind, const void* q, const void* k, const void* v, c
         if (!aligned16(p)) return DR_ERR_INVALID_ARG;
     if ((reinterpret_cast<uintptr_t>(dA_log) & 3u) || (reinterpret_cast<uintptr_t>(ddt_bias) & 3u))
         return DR_ERR_INVALID_ARG;
-    // grid sizes of the four kernels, checked before anything is enqueued
+    // grid sizes of the backward's kernels, checked before anything is enqueued
     const long long items = packed ? ((long long)ceil_div(T, dr::kChunk) + N) * H
                                    : (long long)B * ceil_div(T, dr::kChunk) * H;
     if ((long long)chains * H * (Dv / 16) > 0x7fffffffLL || items > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
