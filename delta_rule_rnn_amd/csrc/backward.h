@@ -939,9 +939,21 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
                 }
             }
         }
-        if (tid < DK) {
-#pragma unroll 8
-            for (int e = 0; e < kVS; ++e) dphi += s1[tid * LVS + e] * ds1[tid * LVS + e];
+        // dphi_d += sum over the slice of S .* dS' in row d: four lanes per
+        // row, eight columns each, quad sum by DPP (every lane of the quad
+        // keeps the row's total)
+        if (tid < DK * 4) {
+            const int d = tid >> 2, c0 = (tid & 3) * (kVS / 4);
+            float part = 0.f;
+#pragma unroll
+            for (int e = 0; e < kVS / 4; e += 4) {
+                const f32x4 a = *reinterpret_cast<const f32x4*>(s1 + d * LVS + c0 + e);
+                const f32x4 b = *reinterpret_cast<const f32x4*>(ds1 + d * LVS + c0 + e);
+                part += a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+            }
+            part += dpp_peer<0xB1>(part);
+            part += dpp_peer<0x4E>(part);
+            dphi += part;
         }
         lds_barrier();
         // one product at a time (compiler barriers between them keep the
@@ -976,7 +988,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         }
         lds_barrier();
     }
-    if (tid < DK) sDphi[tid] = dphi;
+    if (tid < DK * 4 && (tid & 3) == 0) sDphi[tid >> 2] = dphi;
 
     // ---- per-element accumulators: dq, dk, E (gamma adjoint, natural units)
     f32x4 aq[OWN], ak[OWN], aE[OWN];
