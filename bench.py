@@ -106,7 +106,18 @@ def cpu_baseline(w, x, max_tokens: int, threads: int):
     tokens = w.B * Ts
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{w.kind} B={w.B} H={w.H} first {Ts} of {w.T} tokens, fp64 token recurrence, "
-                      f"{threads} threads, {dt:.2f} s wall"}
+                      f"{threads} threads, {dt:.2f} s wall", "cpu": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 
@@ -592,6 +603,19 @@ def main():
     k1 = [e[0].elapsed_time(e[1]) for e in evs]
     k2 = [e[1].elapsed_time(e[2]) for e in evs]
     per_step = sorted(e[0].elapsed_time(e[2]) for e in evs)
+
+    # the same steps with the 256 MB last-level cache (MALL) flushed before
+    # each one by a 512 MB write; only the step itself is inside the events
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(args.steps):
+        flush.fill_(1)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        step(ev)
+        torch.cuda.synchronize()
+        cold.append(ev[0].elapsed_time(ev[2]))
+    cold.sort()
+    del flush
     ms = wall * 1000.0 / args.steps
     tokens = B * T
     value = tokens / (ms / 1000.0)
@@ -628,6 +652,9 @@ def main():
                    "global_batch": B, "seq_len": T, "heads": H, "parallelism": "single GPU",
                    "gate": f"a ~ U[{w.gate_lo}, {w.gate_hi}]"},
         "median_ms_per_step_events": round(per_step[len(per_step) // 2], 4),
+        "min_ms_per_step_events": round(per_step[0], 4),
+        "mall_flushed": {"median_ms": round(cold[len(cold) // 2], 4), "min_ms": round(cold[0], 4),
+                         "note": "512 MB written before each step, outside its events"},
         "mfma_frac_bf16": round(mfma_frac, 4),
         "roofline": roof,
         "cpu_baseline": cpu,
