@@ -73,6 +73,8 @@ WORKLOADS: Dict[str, Workload] = {
     "kda_bf16_long_stress": Workload("kda_bf16_long_stress", "kda", "bf16", 1, 32, 32768,
                                      128, 128, gate_lo=0.8),
     "gdn_bf16_long": Workload("gdn_bf16_long", "gdn", "bf16", 1, 32, 32768, 128, 128),
+    # one GPU's share of kda_bf16_long when its heads are split over 8 GPUs
+    "kda_bf16_long_h4": Workload("kda_bf16_long_h4", "kda", "bf16", 1, 4, 32768, 128, 128),
 }
 
 
