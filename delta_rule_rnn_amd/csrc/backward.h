@@ -547,12 +547,12 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const T* __restr
 }
 
 // ===========================================================================
-// State passes: one 256-thread workgroup per (chain, SV = 16 value columns)
+// Reverse state pass: one workgroup per (chain, SV = 16 value columns)
 // (value columns evolve independently, [KDA] section 3.4).  Consecutive
 // logical ids -- the slices of one chain -- are placed on one XCD (hardware
-// dispatches workgroup i to XCD i % 8) so they share its L2, and while a
-// chunk is computed the next chunk's operand lines are pulled into L2 (one
-// 4-byte LDS-DMA per 128-byte line into a scratch word).
+// dispatches workgroup i to XCD i % 8) so they share its L2, and the lines
+// of the chunk after the one in flight are pulled into L2 (one 4-byte
+// LDS-DMA per 128-byte line into a scratch word).
 // ===========================================================================
 constexpr int kSV = 16;              // value columns per state-pass workgroup
 // LDS row strides.  The tile product reads an operand either with the lane
