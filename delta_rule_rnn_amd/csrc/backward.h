@@ -230,6 +230,49 @@ __device__ __forceinline__ f32x4 mmc(f32x4 acc, const float* A, int ar, const fl
     else return mmk<K>(acc, A, ar, 1, B, 1, bc, lane);
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+// bf16 MFMA (v_mfma_f32_16x16x32_bf16) over fp32 LDS operands of any
+// layout: at step k0 lane l packs A(l%16, k0 + 8(l/16) + j) and
+// B(k0 + 8(l/16) + j, l%16), j = 0..7, to bf16; fp32 accumulation.
+// A(r, k) = A[r*ar + k*ak] (ACONT: ak = 1, read as two 16-byte loads, which
+// needs ar and A 16-byte aligned); B(k, c) = B[k*bk + c*bc].
+template <int K, bool ACONT>
+__device__ __forceinline__ f32x4 mmb_g(f32x4 acc, const float* A, int ar, int ak, const float* B, int bk, int bc,
+                                       int lane) {
+    const int r = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 32) {
+        const int kk = k0 + 8 * q;
+        float av[8], bv[8];
+        if constexpr (ACONT) {
+            const f32x4 a0 = *reinterpret_cast<const f32x4*>(A + r * ar + kk);
+            const f32x4 a1 = *reinterpret_cast<const f32x4*>(A + r * ar + kk + 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { av[j] = a0[j]; av[4 + j] = a1[j]; }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) av[j] = A[r * ar + (kk + j) * ak];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bv[j] = B[(kk + j) * bk + r * bc];
+        bf16x8 fa, fb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { fa[j] = (bf16)av[j]; fb[j] = (bf16)bv[j]; }
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc, 0, 0, 0);
+    }
+    return acc;
+}
+// The pairwise products of the gradient kernel on the MFMA of the I/O
+// dtype: bf16 operands for bf16 I/O (as the value-slice products), fp32
+// otherwise.  ACONT as in mmb_g; the fp32 form takes mmk_a when A is
+// contiguous along k.
+template <typename T, int K, bool ACONT>
+__device__ __forceinline__ f32x4 mmp(f32x4 acc, const float* A, int ar, int ak, const float* B, int bk, int bc,
+                                     int lane) {
+    if constexpr (sizeof(T) == 2) return mmb_g<K, ACONT>(acc, A, ar, ak, B, bk, bc, lane);
+    else if constexpr (ACONT) return mmk_a<K>(acc, A, ar, B, bk, bc, lane);
+    else return mmk<K>(acc, A, ar, ak, B, bk, bc, lane);
+}
+
 
 // Four adjacent elements stored as one access (8 bytes bf16, 16 bytes fp32).
 __device__ __forceinline__ void st4(bf16* p, f32x4 v) {
@@ -1193,7 +1236,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             int ti, tj;
             trc(m, ti, tj);
             const int d = ecol(m);
-            const f32x4 dkp = mmk_a<C>(zero4(), sDL + ti * 16 * LDC, LDC, sKm + tj * 16, LDK, 1, lane);
+            const f32x4 dkp = mmp<T, C, true>(zero4(), sDL + ti * 16 * LDC, LDC, 1, sKm + tj * 16, LDK, 1, lane);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = erow(m, i);
@@ -1206,8 +1249,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             int ti, tj;
             trc(m, ti, tj);
             const int d = ecol(m);
-            f32x4 dkm = mmk<C>(zero4(), sDL + ti * 16, 1, LDC, sKp + tj * 16, LDK, 1, lane);
-            dkm = mmk<C>(dkm, sDAqk + ti * 16, 1, LDC, sQt + tj * 16, LDK, 1, lane);
+            f32x4 dkm = mmp<T, C, false>(zero4(), sDL + ti * 16, 1, LDC, sKp + tj * 16, LDK, 1, lane);
+            dkm = mmp<T, C, false>(dkm, sDAqk + ti * 16, 1, LDC, sQt + tj * 16, LDK, 1, lane);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = erow(m, i);
@@ -1220,7 +1263,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             int ti, tj;
             trc(m, ti, tj);
             const int d = ecol(m);
-            const f32x4 dqt = mmk_a<C>(zero4(), sDAqk + ti * 16 * LDC, LDC, sKm + tj * 16, LDK, 1, lane);
+            const f32x4 dqt = mmp<T, C, true>(zero4(), sDAqk + ti * 16 * LDC, LDC, 1, sKm + tj * 16, LDK, 1, lane);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = erow(m, i);
@@ -1236,12 +1279,12 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         if constexpr (PERCH) {
         } else {
             // raw k (sKp), raw q (sKm): dk += G_L k + G_L^T k + G_Q^T q;  dq += G_Q k
-            f32x4 dkk = mmk<C>(zero4(), sDAqk + ti * 16, 1, LDC, sKm + tj * 16, LDK, 1, lane);
+            f32x4 dkk = mmp<T, C, false>(zero4(), sDAqk + ti * 16, 1, LDC, sKm + tj * 16, LDK, 1, lane);
             if constexpr (DELTA) {
-                dkk = mmk_a<C>(dkk, sDL + ti * 16 * LDC, LDC, sKp + tj * 16, LDK, 1, lane);
-                dkk = mmk<C>(dkk, sDL + ti * 16, 1, LDC, sKp + tj * 16, LDK, 1, lane);
+                dkk = mmp<T, C, true>(dkk, sDL + ti * 16 * LDC, LDC, 1, sKp + tj * 16, LDK, 1, lane);
+                dkk = mmp<T, C, false>(dkk, sDL + ti * 16, 1, LDC, sKp + tj * 16, LDK, 1, lane);
             }
-            const f32x4 dqq = mmk_a<C>(zero4(), sDAqk + ti * 16 * LDC, LDC, sKp + tj * 16, LDK, 1, lane);
+            const f32x4 dqq = mmp<T, C, true>(zero4(), sDAqk + ti * 16 * LDC, LDC, 1, sKp + tj * 16, LDK, 1, lane);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 ak[m][i] += dkk[i];
