@@ -1095,7 +1095,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         for (int m = 0; m < OWN; ++m) {
             int ti, tj;
             trc(m, ti, tj);
-            const f32x4 acc = mmk<C>(zero4(), sT + ti * 16, 1, LDC, sNW + tj * 16, LDK, 1, lane);
+            const f32x4 acc = mmp<T, C, false>(zero4(), sT + ti * 16, 1, LDC, sNW + tj * 16, LDK, 1, lane);
             const int d = ecol(m);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -1136,7 +1136,9 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const int t = wave + 8 * m, ti = t >> 2, tj = t & 3;
-            const f32x4 acc = mmk_ab<C>(zero4(), sDT + ti * 16 * LDC, LDC, sT + tj * 16 * LDC, LDC, lane);
+            f32x4 acc;
+            if constexpr (sizeof(T) == 2) acc = mmb<C>(zero4(), sDT + ti * 16 * LDC, LDC, sT + tj * 16 * LDC, LDC, lane);
+            else acc = mmk_ab<C>(zero4(), sDT + ti * 16 * LDC, LDC, sT + tj * 16 * LDC, LDC, lane);
 #pragma unroll
             for (int i = 0; i < 4; ++i) sY[(ti * 16 + arow(lane, i)) * LDC + tj * 16 + (lane & 15)] = acc[i];
         }
@@ -1144,7 +1146,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const int t = wave + 8 * m, ti = t >> 2, tj = t & 3;
-            const f32x4 acc = mmk<C>(zero4(), sT + ti * 16, 1, LDC, sY + tj * 16, LDC, 1, lane);
+            const f32x4 acc = mmp<T, C, false>(zero4(), sT + ti * 16, 1, LDC, sY + tj * 16, LDC, 1, lane);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = ti * 16 + arow(lane, i), cc = tj * 16 + (lane & 15);
