@@ -640,8 +640,7 @@ __device__ __forceinline__ void l2_touch(const float* __restrict__ src, size_t g
 // Per chunk, three barriers separate: (A) Aqk, Kbar, dO to LDS; (B) the
 // dVnew products, Q~ and W to LDS, the exit adjoint dS'_c stored; (C) the
 // adjoint update in place, dVnew stored.
-constexpr int kRevCompute = 512;
-constexpr int kStateThreads = kRevCompute;
+constexpr int kStateThreads = 512;
 
 // acc += A (B1 + B2) with the layout of mmk: the B operand is the sum of two
 // LDS tiles (the two halves of a split reduction), added as it is read.
@@ -670,7 +669,7 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_rev_kernel(const floa
 {
     using P = Prep<DK>;
     using SM = StateSmem<DK>;
-    constexpr int DV = DK, LDN = SM::LDN, LDT = SM::LDT, LCT = SM::LCT, NVS = DV / kSV, NC = kRevCompute;
+    constexpr int DV = DK, LDN = SM::LDN, LDT = SM::LDT, LCT = SM::LCT, NVS = DV / kSV, NC = kStateThreads;
     constexpr bool DELTA = KIND != KIND_LA;
     // dVnew tile ti is split over waves ti and ti + 4: wave ti takes Aqk^T dO
     // and the first KS key channels of Kbar dS', wave ti + 4 the rest
