@@ -35,11 +35,13 @@
 //
 // The entry states S_c and Vnew_c of every chunk come first, from the
 // forward's own two kernels (the chunk-parallel records, then the state pass
-// in its STATES mode, fp32 state in accumulators).  The kernels here compute
-// in fp32, on fp32 MFMA (v_mfma_f32_16x16x4_f32) with operands staged in LDS
-// in natural row-major layout, or bf16 MFMA for the phase-1 value-slice
-// products of bf16 I/O; the I/O dtype otherwise only changes the loads of
-// q, k, v, dO and the stores of dq, dk, dv.
+// in its STATES mode, fp32 state in accumulators).  The kernels here keep
+// their operands as fp32 in LDS, in natural row-major layout, and compute on
+// fp32 MFMA (v_mfma_f32_16x16x4_f32), except for bf16 I/O: the prep's L and
+// Aqk, and the gradient kernel's value-slice, pairwise and T products, run
+// on bf16 MFMA (operands rounded as they are read, fp32 accumulation).  The
+// I/O dtype otherwise only changes the loads of q, k, v, dO and the stores
+// of dq, dk, dv.
 //   bwd_prep_kernel     chunk-parallel: writes the natural fp32 chunk arrays
 //                       (Q~, W, Kbar, Aqk, L, T, phi, gamma)
 //   bwd_state_rev_kernel   per (chain, 16 value columns), chunks in reverse:
