@@ -80,12 +80,7 @@ struct Prep {
 // (varlen_table_kernel): table[slot] = {sequence, first token, valid rows, -},
 // seqinfo[n] = {first slot, chunks, first token, tokens}; per-chunk arrays
 // are indexed h * maxchunks + slot.
-struct Pack {
-    const int4* table;
-    const int4* seqinfo;
-    const int* total;
-    int maxchunks;
-};
+// (struct Pack is declared in common.h, where the host code sees it too.)
 
 // The chunk a chunk-parallel workgroup handles: its first token row (token
 // index times H plus h), its valid rows and its per-chunk array index; false

@@ -327,4 +327,16 @@ __device__ __forceinline__ void prefetch_pair(int n, Load&& load, Step&& step)
     }
 }
 
+// Packed-sequence chunk table as the backward kernels take it (written by
+// varlen_table_kernel): table[slot] = {sequence, first token, valid rows, -},
+// seqinfo[n] = {first slot, chunks, first token, tokens}, *total slots.
+namespace bw {
+struct Pack {
+    const int4* table;
+    const int4* seqinfo;
+    const int* total;
+    int maxchunks;
+};
+}  // namespace bw
+
 }  // namespace dr

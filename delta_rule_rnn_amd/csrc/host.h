@@ -1,0 +1,248 @@
+// host.h -- host-side pieces shared by the library's translation units:
+// argument checks, problem descriptors, workspace layouts and the launchers
+// each kernel translation unit defines.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "../../include/deltarule.h"
+#include "common.h"
+
+namespace drh {
+
+using dr::bf16;
+
+inline bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline dr_status check_launch() {
+    return hipGetLastError() == hipSuccess ? DR_OK : DR_ERR_HIP;
+}
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+inline size_t record_bytes(int D, int dtype) {
+    if (dtype == DR_BF16) return D == 64 ? dr::Rec<bf16, 64, 64>::BYTES : dr::Rec<bf16, 128, 128>::BYTES;
+    return D == 64 ? dr::Rec<float, 64, 64>::BYTES : dr::Rec<float, 128, 128>::BYTES;
+}
+
+// Shared validation for the full forward and the fused step entry points.
+inline dr_status validate(int kind, const void* q, const void* k, const void* v, const float* g,
+                   const float* beta, int B, int T, int H, int Dk, int Dv, int C, int dtype) {
+    if (kind < 0 || kind > 2) return DR_ERR_INVALID_ARG;
+    if (B <= 0 || H <= 0 || T < 0) return DR_ERR_INVALID_ARG;
+    if (dtype != DR_F32 && dtype != DR_BF16) return DR_ERR_INVALID_ARG;
+    if (Dk <= 0 || Dv <= 0 || C <= 0) return DR_ERR_INVALID_ARG;
+    if (Dk != Dv || (Dk != 64 && Dk != 128) || C != dr::kChunk) return DR_ERR_UNSUPPORTED;
+    if ((long long)B * T * H * Dk > (1LL << 40)) return DR_ERR_INVALID_ARG;
+    if (T > 0 && (!q || !k || !v || !g)) return DR_ERR_INVALID_ARG;
+    if (T > 0 && kind != DR_KIND_DECAY_LA && !beta) return DR_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(beta))
+        return DR_ERR_INVALID_ARG;
+    return DR_OK;
+}
+
+// One forward problem: the arguments every launch needs.
+struct Problem {
+    int kind, dtype, D, B, T, H, NT;
+    const void *q, *k, *v;
+    const float *g, *beta;
+    void* o;
+    uint8_t* ws;
+    unsigned* flags;
+    // packed sequences only: B sequences, chunk table and descriptors in the
+    // workspace (see varlen_layout)
+    const int4* table = nullptr;
+    const int4* seqinfo = nullptr;
+    const int* total = nullptr;
+    int maxchunks = 0;
+    // input prologue (use_pro selects the kernels that apply it)
+    dr::Prologue pro{0u, 1.f, nullptr, nullptr};
+    bool use_pro = false;
+};
+
+// Checks a caller's prologue and converts it; *use is false when it is
+// absent or does nothing (no ops, scale 1).
+inline dr_status resolve_prologue(int kind, const dr_prologue* in, dr::Prologue* out, bool* use) {
+    *use = false;
+    *out = dr::Prologue{0u, 1.f, nullptr, nullptr};
+    if (in == nullptr) return DR_OK;
+    const unsigned known = DR_PRO_QK_L2NORM | DR_PRO_BETA_SIGMOID | DR_PRO_BETA_X2 | DR_PRO_GATE;
+    if (in->ops & ~known) return DR_ERR_INVALID_ARG;
+    if (!(in->scale == in->scale) || in->scale > 3.0e38f || in->scale < -3.0e38f) return DR_ERR_INVALID_ARG;
+    if ((in->ops & DR_PRO_BETA_X2) && !(in->ops & DR_PRO_BETA_SIGMOID)) return DR_ERR_INVALID_ARG;
+    if ((in->ops & (DR_PRO_BETA_SIGMOID | DR_PRO_BETA_X2)) && kind == DR_KIND_DECAY_LA) return DR_ERR_INVALID_ARG;
+    if (in->ops & DR_PRO_GATE) {
+        if (kind == DR_KIND_KDA) return DR_ERR_UNSUPPORTED;
+        if (!in->A_log) return DR_ERR_INVALID_ARG;
+        if ((reinterpret_cast<uintptr_t>(in->A_log) & 3u) || (reinterpret_cast<uintptr_t>(in->dt_bias) & 3u))
+            return DR_ERR_INVALID_ARG;
+    }
+    static_assert(DR_PRO_QK_L2NORM == dr::PRO_QK_L2NORM && DR_PRO_BETA_SIGMOID == dr::PRO_BETA_SIGMOID &&
+                      DR_PRO_BETA_X2 == dr::PRO_BETA_X2 && DR_PRO_GATE == dr::PRO_GATE,
+                  "prologue bits");
+    *out = dr::Prologue{in->ops, in->scale, (in->ops & DR_PRO_GATE) ? in->A_log : nullptr,
+                        (in->ops & DR_PRO_GATE) ? in->dt_bias : nullptr};
+    *use = in->ops != 0 || in->scale != 1.f;
+    return DR_OK;
+}
+
+inline int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// Value columns per state-pass workgroup (16 * ntn): the widest slice that
+// still gives every CU a workgroup.  Narrow slices multiply the reads of the
+// operands all slices of a chain share (W, Q~, Kbar, Aqk); too few workgroups
+// leave CUs idle.  DR_INTER_NTN (1, 2 or 4) overrides the choice for tuning.
+inline int pick_ntn(int chains, int D) {
+    if (const char* e = getenv("DR_INTER_NTN")) {
+        const int v = atoi(e);
+        if ((v == 1 || v == 2 || v == 4) && 16 * v <= D) return v;
+    }
+    const int cols = D / 16, cus = device_cus();
+    int ntn = 4;
+    while (ntn > 1 && (ntn > cols || (long long)chains * (cols / ntn) < cus)) ntn /= 2;
+    return ntn;
+}
+
+inline int pick_pfd() {
+    if (const char* e = getenv("DR_INTER_PFD")) {
+        const int v = atoi(e);
+        if (v == 0 || v == 2) return v;
+    }
+    return 2;
+}
+
+inline Problem make_problem(int kind, const void* q, const void* k, const void* v, const float* g,
+                     const float* beta, void* o, int B, int T, int H, int D, int dtype, void* ws,
+                     unsigned* flags) {
+    Problem p;
+    p.kind = kind; p.dtype = dtype; p.D = D; p.B = B; p.T = T; p.H = H;
+    p.NT = ceil_div(T, dr::kChunk);
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = kind == DR_KIND_DECAY_LA ? nullptr : beta;
+    p.o = o; p.ws = static_cast<uint8_t*>(ws); p.flags = flags;
+    return p;
+}
+
+
+// Workspace of the varlen forward: records [H][maxchunks], then the chunk
+// table [maxchunks] int4, the sequence descriptors [N] int4 and the slot
+// count, each block 256-byte aligned.  maxchunks = ceil(T/C) + N bounds
+// sum_i ceil(len_i / C).
+struct VarlenLayout {
+    size_t rec, table, seqinfo, total, bytes;
+    int maxchunks;
+};
+inline VarlenLayout varlen_layout(int N, int T, int H, int D, int dtype) {
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    VarlenLayout L;
+    L.maxchunks = ceil_div(T, dr::kChunk) + N;
+    L.rec = 0;
+    L.table = up((size_t)H * L.maxchunks * record_bytes(D, dtype));
+    L.seqinfo = L.table + up((size_t)L.maxchunks * sizeof(int4));
+    L.total = L.seqinfo + up((size_t)N * sizeof(int4));
+    L.bytes = L.total + 256;
+    return L;
+}
+
+// ---- recurrent decode step --------------------------------------------------
+struct DecodeArgs {
+    const void *q, *k, *v;
+    const float *g, *beta;
+    float* state;
+    void* o;
+    int B, T, H;
+    dr::Prologue pro;
+};
+
+// State sizes above half the MI355X last-level cache (256 MB) use streaming
+// state stores (see decode.h).
+constexpr size_t kDecodeStreamBytes = (size_t)128 << 20;
+
+// bytes of the backward prep kernel's per-chunk arrays (floats), defined with
+// the backward kernels
+size_t bwd_prep_floats(int D);
+
+// states S_c [DK][DV], the exit adjoints dS'_c [DK][DV], Vnew_c and dVnew_c
+// [C][DV] of every chunk, each block 256-byte aligned.
+struct BwdLayout {
+    size_t prep, hs, dhs, vn, dvn, rec, bytes;
+};
+// n = number of per-chunk entries (dense: B * H * ceil(T/C); packed:
+// H * maxchunks)
+// (the forward's chunk records come last: the forward state pass runs the
+// forward's own two kernels over them)
+inline BwdLayout bwd_layout_n(size_t n, int D, int dtype) {
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t pf = D == 64 ? bwd_prep_floats(64) : bwd_prep_floats(128);
+    BwdLayout L;
+    L.prep = 0;
+    L.hs = up(n * pf * 4);
+    L.dhs = L.hs + up(n * D * D * 4);
+    L.vn = L.dhs + up(n * D * D * 4);
+    L.dvn = L.vn + up(n * dr::kChunk * D * 4);
+    L.rec = L.dvn + up(n * dr::kChunk * D * 4);
+    L.bytes = L.rec + up(n * record_bytes(D, dtype));
+    return L;
+}
+inline BwdLayout bwd_layout(int B, int T, int H, int D, int dtype) {
+    return bwd_layout_n((size_t)B * H * (size_t)ceil_div(T, dr::kChunk), D, dtype);
+}
+
+// B is the sequence count for packed sequences (pk.table set; T is then the
+// packed token count and the tensors have a batch of one).
+struct BwdArgs {
+    const void *q, *k, *v, *dout;
+    const float *g, *beta, *h0, *dhT;
+    void *dq, *dk, *dv;
+    float *dg, *dbeta, *dh0;
+    int B, T, H, NT;
+    uint8_t* ws;
+    BwdLayout L;
+    dr::bw::Pack pk;
+};
+
+struct ProBwdLayout {
+    size_t qh, kh, gh, bh, core, bytes;
+};
+// core: the bytes of what follows the prologue's part (the backward's own
+// workspace, with the chunk table first for packed sequences)
+inline ProBwdLayout probwd_layout(int kind, int B, int T, int H, int D, int dtype, size_t core) {
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t n = (size_t)B * T * H, esz = dtype == DR_BF16 ? 2 : 4;
+    ProBwdLayout L;
+    L.qh = 0;
+    L.kh = up(n * D * esz);
+    L.gh = L.kh + up(n * D * esz);
+    L.bh = L.gh + up(n * (kind == DR_KIND_KDA ? D : 1) * 4);
+    L.core = L.bh + up(n * 4);
+    L.bytes = L.core + core;
+    return L;
+}
+
+// ---- launchers (one kernel family per translation unit) -------------------
+dr_status launch_intra(const Problem& p, int c0, int n, hipStream_t st);           // k_intra.hip
+dr_status launch_intra_varlen(const Problem& p, hipStream_t st);                   // k_intra.hip
+dr_status launch_inter(const Problem& p, const float* h0, float* hT, int c0, int n, hipStream_t st);  // k_inter.hip
+dr_status launch_states(const Problem& p, const float* h0, float* hs, float* vn, hipStream_t st);     // k_inter.hip
+dr_status launch_backward(int kind, const BwdArgs& a, int D, int dtype, hipStream_t st);              // k_bwd.hip
+dr_status launch_decode(int kind, const DecodeArgs& a, bool use_pro, int D, int dtype, hipStream_t st);  // k_misc.hip
+dr_status launch_prologue(bool backward, int kind, int D, int dtype, const void* q, const void* k, const float* g,
+                          const float* beta, void* qh, void* kh, float* gh, float* bh, void* dq, void* dk, float* dg,
+                          float* dbeta, float* dA_log, float* ddt, int B, int T, int H, const dr::Prologue& pro,
+                          hipStream_t st);                                                               // k_misc.hip
+dr_status launch_varlen_table(const int* cu_seqlens, int N, int T, int maxchunks, int4* table, int4* seqinfo,
+                              int* total, unsigned* flags, hipStream_t st);                              // k_misc.hip
+dr_status launch_copy_or_zero(float* dst, const float* src, size_t n, hipStream_t st);                  // k_misc.hip
+
+}  // namespace drh
