@@ -7,7 +7,7 @@ namespace drh {
 dr_status forward(int kind, const void* q, const void* k, const void* v, const float* g,
                   const float* beta, const float* h0, void* o, float* hT, int B, int T, int H, int Dk,
                   int Dv, int C, int dtype, void* ws, size_t ws_bytes, unsigned* flags, void* stream,
-                  const dr_prologue* pro = nullptr) {
+                  const dr_prologue* pro) {
     dr_status s = validate(kind, q, k, v, g, beta, B, T, H, Dk, Dv, C, dtype);
     if (s != DR_OK) return s;
     dr::Prologue pr;
@@ -383,11 +383,14 @@ const char* dr_status_string(int status) {
         case DR_ERR_UNSUPPORTED: return "unsupported size (Dk == Dv in {64, 128}, C == 64)";
         case DR_ERR_HIP: return "HIP launch failed";
         case DR_ERR_WORKSPACE: return "workspace missing or too small";
+        case DR_ERR_SCRATCH_LIMIT:
+            return "problem needs more workspace than the library's static scratch array holds "
+                   "(dr_noalloc_scratch_bytes()); call dr_forward with a caller workspace";
         default: return "unknown status";
     }
 }
 
-int dr_abi_version(void) { return 5; }
+int dr_abi_version(void) { return 6; }
 
 }  // extern "C"
 

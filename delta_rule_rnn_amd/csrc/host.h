@@ -230,6 +230,11 @@ inline ProBwdLayout probwd_layout(int kind, int B, int T, int H, int D, int dtyp
     return L;
 }
 
+// The whole forward (dense layout), as dr_forward runs it (deltarule.hip).
+dr_status forward(int kind, const void* q, const void* k, const void* v, const float* g, const float* beta,
+                  const float* h0, void* o, float* hT, int B, int T, int H, int Dk, int Dv, int C, int dtype,
+                  void* ws, size_t ws_bytes, unsigned* flags, void* stream, const dr_prologue* pro = nullptr);
+
 // ---- launchers (one kernel family per translation unit) -------------------
 dr_status launch_intra(const Problem& p, int c0, int n, hipStream_t st);           // k_intra.hip
 dr_status launch_intra_varlen(const Problem& p, hipStream_t st);                   // k_intra.hip

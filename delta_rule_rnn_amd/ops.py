@@ -155,6 +155,36 @@ def _forward(kind: str, q, k, v, g, beta, h0, output_final_state, chunk_size, wo
     return o, hT
 
 
+def forward_noalloc(kind: str, q, k, v, g, beta=None, h0=None, output_final_state=True, chunk_size=CHUNK,
+                    flags=None, stream=None, prologue: Optional[Prologue] = None):
+    """The forward of ``kind`` through dr_forward_noalloc: the library's own
+    static device array serves as the workspace (no workspace is allocated
+    for the call; o and hT are still allocated here, as for every entry
+    point).  Same arguments and results as :func:`forward`."""
+    lib = _lib.load()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    _need(q, "q"); _need(k, "k", dt, q.shape); _need(v, "v", dt, (B, T, H, Dv))
+    _need(g, "g", torch.float32, (B, T, H, Dk) if kind == "kda" else (B, T, H))
+    if kind != "decay_la":
+        if beta is None:
+            raise DeltaRuleError("beta is required")
+        _need(beta, "beta", torch.float32, (B, T, H))
+    _need(h0, "h0", torch.float32, (B, H, Dk, Dv))
+    if flags is not None:
+        _need(flags, "flags", torch.int32, (1,))
+    o = torch.empty(B, T, H, Dv, dtype=dt, device=q.device)
+    hT = torch.empty(B, H, Dk, Dv, dtype=torch.float32, device=q.device) if output_final_state else None
+    keep, pro = _pro_arg(prologue, H)
+    st = lib.dr_forward_noalloc(KINDS[kind], _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                _ptr(beta) if kind != "decay_la" else None, _ptr(h0), _ptr(o), _ptr(hT), B, T, H,
+                                Dk, Dv, chunk_size, _dtype_code(q), pro, _ptr(flags), _stream(stream))
+    del keep
+    _check(st, "dr_forward_noalloc")
+    return o, hT
+
+
 def kda_fwd(q, k, v, g, beta, h0=None, output_final_state=True, chunk_size=CHUNK, workspace=None,
             flags=None, stream=None, prologue: Optional[Prologue] = None):
     """KDA forward.  q, k [B,T,H,Dk], v [B,T,H,Dv] (bf16 or fp32); g [B,T,H,Dk]

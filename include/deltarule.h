@@ -56,7 +56,9 @@ typedef enum {
     DR_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, bad size or dtype   */
     DR_ERR_UNSUPPORTED = -2,   /* valid but not built: Dk/Dv/C combination     */
     DR_ERR_HIP = -3,           /* a HIP launch failed                          */
-    DR_ERR_WORKSPACE = -4      /* workspace pointer null or too small          */
+    DR_ERR_WORKSPACE = -4,     /* workspace pointer null or too small          */
+    DR_ERR_SCRATCH_LIMIT = -5  /* dr_forward_noalloc: problem exceeds the
+                                  library's static scratch array            */
 } dr_status;
 
 typedef enum { DR_F32 = 0, DR_BF16 = 1 } dr_dtype;
@@ -236,6 +238,30 @@ dr_status dr_forward(int kind, const void* q, const void* k, const void* v, cons
                      int B, int T, int H, int Dk, int Dv, int C, int dtype,
                      const dr_prologue* prologue, void* workspace, size_t workspace_bytes,
                      unsigned* flags, void* stream);
+/*
+ * dr_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Arguments, layouts, results and errors are those
+ * of dr_forward; the same kernels run.  The workspace is a fixed device array
+ * inside the library of DR_NOALLOC_SCRATCH_BYTES bytes (also returned by
+ * dr_noalloc_scratch_bytes()).  Every GPU the library's code is loaded on
+ * holds its own copy until the process ends.  The call itself allocates
+ * nothing: its only set-up is a lookup of the array's device address, once
+ * per device, on the first call on that device.
+ *   Limit: problems whose dr_workspace_bytes(...) exceeds the array return
+ *     DR_ERR_SCRATCH_LIMIT with nothing enqueued.
+ *   Sharing: all calls on one GPU use that GPU's single array.  Calls that
+ *     can overlap on one GPU (different streams, or several host threads
+ *     without ordering) race on it and give wrong results; serialise them.
+ *     Nothing in the array needs to be cleared between calls: each call
+ *     writes every workspace byte it reads.
+ */
+#define DR_NOALLOC_SCRATCH_BYTES (64u << 20)
+size_t dr_noalloc_scratch_bytes(void);
+dr_status dr_forward_noalloc(int kind, const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, const float* h0, void* o, float* hT,
+                             int B, int T, int H, int Dk, int Dv, int C, int dtype,
+                             const dr_prologue* prologue, unsigned* flags, void* stream);
 /* The packed-sequence forwards selected by `kind`, with a prologue. */
 dr_status dr_forward_varlen(int kind, const void* q, const void* k, const void* v, const float* g,
                             const float* beta, const int* cu_seqlens, int N,

@@ -38,11 +38,11 @@ def test_header_and_binding_agree():
 def test_every_declared_symbol_is_exported(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.dr_abi_version() == 5
+    assert lib.dr_abi_version() == 6
 
 
 def test_status_strings(lib):
-    for s in (0, -1, -2, -3, -4):
+    for s in (0, -1, -2, -3, -4, -5):
         assert lib.dr_status_string(s)
     assert lib.dr_status_string(7) == b"unknown status"
 
@@ -75,6 +75,22 @@ def test_kda_fwd_rejects(lib, case, expect):
                      a["T"], a["H"], a["Dk"], a["Dv"], a["C"], a["dtype"], a["ws"], a["ws_bytes"],
                      a["flags"], a["stream"])
     assert st == expect
+
+
+def test_noalloc_limit_is_checked_on_the_host(lib):
+    """dr_forward_noalloc: bad sizes and problems larger than the static
+    scratch array are rejected before any device call."""
+    cap = lib.dr_noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    args = lambda B, T, H: (0, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, B, T, H, 128, 128, 64, 1,
+                            None, None, None)
+    assert lib.dr_forward_noalloc(*args(0, 64, 1)) == -1
+    assert lib.dr_forward_noalloc(5, *args(1, 64, 1)[1:]) == -1
+    rec = lib.dr_record_bytes(128, 128, 64, 1)
+    chunks = cap // rec + 1                      # one chunk-head more than fits
+    st = lib.dr_forward_noalloc(*args(1, 64 * chunks, 1))
+    assert st == -5 and b"static scratch" in lib.dr_status_string(st)
+    assert lib.dr_workspace_bytes(0, 1, 64 * (chunks - 1), 1, 128, 128, 64, 1) <= cap
 
 
 def test_other_entry_points_reject(lib):
