@@ -180,3 +180,75 @@ def chunk_forward(kind: str, q, k, v, g, beta=None, h0=None, C: int = 64,
             hT[b, hh] = S
     return ChunkResult(o=o, hT=hT, gamma=gamma, prep=prep, A=A_all, Tinv=T_all,
                        W=W_all, U=U_all, Vnew=Vn_all, Aqk=Aqk_all, h=h_all)
+
+
+@dataclass
+class SegmentResult:
+    o: np.ndarray          # [B,T,H,Dv]
+    hT: np.ndarray         # [B,H,Dk,Dv]
+    o_local: np.ndarray    # [B,T,H,Dv]  output of each segment from a zero entry state
+    q_eff: np.ndarray      # [B,T,H,Dk]  o = o_local + q_eff S_in(segment)
+    M: np.ndarray          # [B,H,NS,Dk,Dk] transition of each segment
+    N: np.ndarray          # [B,H,NS,Dk,Dv] exit state of each segment from a zero entry state
+    S_in: np.ndarray       # [B,H,NS+1,Dk,Dv] entry state of each segment (last = hT)
+
+
+def segment_forward(kind: str, q, k, v, g, beta=None, h0=None, C: int = 64, L: int = 2) -> SegmentResult:
+    """The chunk form evaluated segment-parallel: the chunks of a sequence are
+    grouped into segments of L chunks, and every segment is run from the
+    augmented entry state X = [I | 0] ([Dk, Dk+Dv]).  Its first Dk columns
+    carry the segment's transition P (the product of the per-token maps
+    S -> (I - beta k k^T) Diag(a) S, kernel orientation), the other Dv the
+    state reached from a zero entry state.  Per chunk, with U_bar = [0 | U]:
+        Y = U_bar - W X,   Z = Q~ X + Aqk Y,   X <- Diag(phi) X + Kbar^T Y
+    (decay_la: Y = [0 | V]).  Z's first Dk columns are the chunk's
+    effective queries q_eff, the rest its output from the zero entry state.
+    A segment ends with X = [M | N]; the entry states follow by
+    S_in[0] = h0, S_in[r+1] = M_r S_in[r] + N_r, and o = o_local +
+    q_eff S_in[segment].
+
+    This is the entry-state hand-off of sequence-split (context-parallel)
+    evaluation on [GDN] "前向计算的矩阵分解" (the chunked forward's pre-process
+    that computes each split's initial state), with the segment transition
+    written as the product of the per-token transition matrices, whose WY
+    form is [DPLR] section 2 (D - W^T Y)."""
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(g)
+    beta, h0 = _f64(beta), _f64(h0)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    delta = kind in ("kda", "gdn")
+    gamma = chunk_log2_cumsum(g, C)
+    prep = separable_prep(q, k, gamma, C)
+    Kp, Km, Qp, phi, Kbar = prep["Kp"], prep["Km"], prep["Qp"], prep["phi"], prep["Kbar"]
+    bounds = chunk_bounds(T, C)
+    NT = len(bounds)
+    NS = max(1, -(-NT // L))
+    o_loc = np.zeros((B, T, H, Dv))
+    q_eff = np.zeros((B, T, H, Dk))
+    M = np.zeros((B, H, NS, Dk, Dk))
+    N = np.zeros((B, H, NS, Dk, Dv))
+    S_in = np.zeros((B, H, NS + 1, Dk, Dv))
+    o = np.zeros((B, T, H, Dv))
+    for b in range(B):
+        for hh in range(H):
+            for r in range(NS):
+                X = np.concatenate([np.eye(Dk), np.zeros((Dk, Dv))], axis=1)
+                for c in range(r * L, min(NT, (r + 1) * L)):
+                    s, e = bounds[c]
+                    kp, km, qp = Kp[b, s:e, hh], Km[b, s:e, hh], Qp[b, s:e, hh]
+                    if delta:
+                        _, _, W, U = ut_solve(kp, km, v[b, s:e, hh], beta[b, s:e, hh])
+                        Y = np.concatenate([np.zeros((e - s, Dk)), U], axis=1) - W @ X
+                    else:
+                        Y = np.concatenate([np.zeros((e - s, Dk)), v[b, s:e, hh]], axis=1)
+                    Z = qp @ X + np.tril(qp @ km.T) @ Y
+                    q_eff[b, s:e, hh] = Z[:, :Dk]
+                    o_loc[b, s:e, hh] = Z[:, Dk:]
+                    X = phi[b, c, hh][:, None] * X + Kbar[b, s:e, hh].T @ Y
+                M[b, hh, r], N[b, hh, r] = X[:, :Dk], X[:, Dk:]
+            S_in[b, hh, 0] = h0[b, hh] if h0 is not None else 0.0
+            for r in range(NS):
+                S_in[b, hh, r + 1] = M[b, hh, r] @ S_in[b, hh, r] + N[b, hh, r]
+            for c, (s, e) in enumerate(bounds):
+                o[b, s:e, hh] = o_loc[b, s:e, hh] + q_eff[b, s:e, hh] @ S_in[b, hh, c // L]
+    return SegmentResult(o=o, hT=S_in[:, :, NS].copy(), o_local=o_loc, q_eff=q_eff, M=M, N=N, S_in=S_in)

@@ -287,6 +287,55 @@ def pin_chunk_form_equals_recurrence(rec, chunked):
             assert rel(np.swapaxes(res.hT, -1, -2), s) < 1e-12, f"chunk form state {kind} T={T} C={C}"
 
 
+def _token_maps(kind, k, g, bt):
+    """Per-token transition maps of one (b, h) chain in kernel orientation
+    (state [Dk, Dv]): S -> (I - beta k k^T) Diag(a) S, decay_la: Diag(a) S,
+    built directly from the recurrence's definition ([KDA] opening equation,
+    transposed)."""
+    T, Dk = k.shape
+    out = []
+    for t in range(T):
+        a = np.exp(g[t]) * np.ones(Dk)
+        F = np.diag(a)
+        if kind != "decay_la":
+            F = (np.eye(Dk) - bt[t] * np.outer(k[t], k[t])) @ F
+        out.append(F)
+    return out
+
+
+def pin_segment_form(rec, chunked):
+    """The segment-parallel evaluation (chunks grouped into segments, each run
+    from [I | 0], entry states composed afterwards) must equal the recurrence
+    to rounding, for segments of 1, several and more than all chunks and a
+    ragged tail; and its pieces must be what they claim, checked against
+    products of the per-token maps written out directly: each segment's
+    transition M_r is the product of its tokens' maps in time order, N_r the
+    recurrence from a zero state over its tokens, and the effective query of
+    token t is q_t^T times the product of the maps from the segment's first
+    token through t."""
+    for kind in ("kda", "gdn", "decay_la"):
+        for (T, C, L) in ((40, 4, 3), (23, 8, 1), (12, 4, 9), (33, 4, 2)):
+            q, k, v, g, bt, h0 = rand_case(kind, B=2, T=T, H=2, Dk=4, Dv=3, seed=131 + T + L, h0_std=0.5)
+            bt_ = None if kind == "decay_la" else bt
+            o, s = rec(kind, q, k, v, g, bt_, h0)
+            res = chunked.segment_forward(kind, q, k, v, g, bt_, np.swapaxes(h0, -1, -2), C, L)
+            assert rel(res.o, o) < 1e-12, f"segment form output {kind} T={T} C={C} L={L}"
+            assert rel(np.swapaxes(res.hT, -1, -2), s) < 1e-12, f"segment form state {kind} T={T} L={L}"
+            b, hh = 1, 0
+            maps = _token_maps(kind, k[b, :, hh], g[b, :, hh], None if bt_ is None else bt_[b, :, hh])
+            for r in range(res.M.shape[2]):
+                t0, t1 = r * L * C, min(T, (r + 1) * L * C)
+                P = np.eye(k.shape[-1])
+                for t in range(t0, t1):
+                    P = maps[t] @ P
+                    qe = q[b, t, hh] @ P
+                    assert rel(res.q_eff[b, t, hh], qe) < 1e-12, f"effective query {kind} t={t}"
+                assert rel(res.M[b, hh, r], P) < 1e-12, f"segment transition {kind} r={r}"
+                _, sN = rec(kind, q[b:b + 1, t0:t1], k[b:b + 1, t0:t1], v[b:b + 1, t0:t1], g[b:b + 1, t0:t1],
+                            None if bt_ is None else bt_[b:b + 1, t0:t1], None)
+                assert rel(res.N[b, hh, r], sN[0, hh].T) < 1e-12, f"segment exit state {kind} r={r}"
+
+
 ALL_RECURRENCE_PINS = [
     pin_retention_parallel, pin_ssd_dual, pin_wy_brute_force, pin_iplr_wy,
     pin_beta_zero_pure_decay, pin_vanilla_linear_attention,

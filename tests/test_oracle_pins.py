@@ -25,6 +25,10 @@ def test_chunk_form_equals_recurrence():
     pins.pin_chunk_form_equals_recurrence(oracle.recurrence, chunked)
 
 
+def test_segment_form_equals_recurrence_and_token_maps():
+    pins.pin_segment_form(oracle.recurrence, chunked)
+
+
 def test_printed_decay_tables():
     """[SD] section 2.2: alpha=0.5, C=4 gives gamma = (0.5, 0.25, 0.125,
     0.0625) and Gamma(4,1) = 0.125; the alpha=0.9 D and Gamma matrices.
