@@ -58,9 +58,48 @@ def algorithmic(kind: str, w, io_bytes: int):
     return k1, k2, flops
 
 
-# The sources the forward's two kernels (intra_kernel, inter_kernel) are
-# compiled from, and the build script with the compiler flags.
-FORWARD_KERNEL_SOURCES = ("csrc/common.h", "csrc/intra.h", "csrc/inter.h", "build.py")
+def segment_plan(w):
+    """(segments per chain, chunks per segment) as the library chooses them
+    (about 256 workgroups for the segment kernel)."""
+    NT = -(-w.T // w.C)
+    chains = w.B * w.H
+    if NT > 1 and chains < 256:
+        want = min(NT, -(-256 // chains))
+        L = -(-NT // want)
+        return -(-NT // L), L
+    return 1, max(NT, 1)
+
+
+def segment_bytes(kind: str, w, io_bytes: int):
+    """Algorithmic bytes per launch of the segment-parallel forward's three
+    kernels: what each must read and write once.
+      segment: q, k, v, g, beta in; o_local out; q_eff out for the chunks of
+               segments after the first; per (chain, segment) [M | N] out
+               (fp32, Dk x (Dk + Dv)).
+      compose: [M | N] of the segments in; S_in (I/O dtype, Dk x Dv) of the
+               segments after the first and hT (fp32) out.
+      correct: q_eff and o in, o out for the chunks of segments after the
+               first; S_in of those segments in."""
+    dk, dv = w.Dk, w.Dv
+    NS, L = segment_plan(w)
+    NT = -(-w.T // w.C)
+    chains = w.B * w.H
+    th = w.B * w.T * w.H
+    th_late = chains * min(w.T, max(0, w.T - L * w.C))     # token-heads of segments >= 1
+    gate = 4 * dk if kind == "kda" else 4
+    beta = 4 if kind != "decay_la" else 0
+    seg = th * (io_bytes * (2 * dk + dv) + gate + beta + io_bytes * dv) + th_late * io_bytes * dk \
+        + chains * NS * dk * (dk + dv) * 4
+    comp = chains * NS * dk * (dk + dv) * 4 + chains * (NS - 1) * dk * dv * io_bytes + chains * dk * dv * 4
+    corr = th_late * io_bytes * (dk + 2 * dv) + chains * (NS - 1) * dk * dv * io_bytes
+    del NT
+    return {"segment": seg, "compose": comp, "correct": corr}
+
+
+# The sources the forward's kernels are compiled from (the segment-parallel
+# path's and the record path's), and the build script with the compiler flags.
+FORWARD_KERNEL_SOURCES = ("csrc/common.h", "csrc/intra.h", "csrc/inter.h", "csrc/seg.h", "csrc/k_seg.hip",
+                          "build.py")
 
 
 def kernel_source_hash() -> str:
@@ -76,10 +115,13 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of each kernel from profiles/<workload>_traffic.txt,
-    or {} when absent or taken on other kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.txt")
+def measured_traffic(workload: str, fpath: str = "segment"):
+    """HBM bytes per launch of each kernel from the committed counter summary
+    (profiles/<workload>_traffic.txt for the segment path,
+    profiles/<workload>_records_traffic.txt for the record path), or {} when
+    absent or taken on other kernel sources."""
+    suffix = "" if fpath == "segment" else "_records"
+    path = os.path.join(ROOT, "profiles", f"{workload}{suffix}_traffic.txt")
     if not os.path.exists(path):
         return {}
     text = open(path).read()
@@ -523,6 +565,10 @@ def main():
                          "backward: all gradients of the forward")
     ap.add_argument("--decode-batch", type=int, default=64, help="sequences per decode call")
     ap.add_argument("--decode-tokens", type=int, default=1, help="new tokens per sequence per call")
+    ap.add_argument("--path", choices=("segment", "records"), default="segment",
+                    help="segment: the forward entry points' segment-parallel launches (the "
+                         "benchmark line); records: the chunk-record path (chunk-parallel kernel, "
+                         "then the sequential state pass) for comparison")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (3 times): the "
                          "reference for scaling the HBM byte counters of a profile")
@@ -573,36 +619,62 @@ def main():
     d = {n: (t.to(dev) if t is not None else None) for n, t in x.items()}
     B, T, H, Dk, Dv = w.B, w.T, w.H, w.Dk, w.Dv
     io = d["q"].dtype
-    ws = ops.alloc_workspace(w.kind, d["q"], d["v"], w.C)
     o = torch.empty(B, T, H, Dv, dtype=io, device=dev)
     hT = torch.empty(B, H, Dk, Dv, dtype=torch.float32, device=dev)
     flags = torch.zeros(1, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
+    io_b = 2 if io == torch.bfloat16 else 4
+    th = B * T * H
+    if args.path == "segment":
+        # the three launches of the forward entry points (dr_forward_stage
+        # 0, 1, 2): local segment pass, entry-state composition, correction
+        ws = ops.alloc_segment_workspace(w.kind, d["q"], d["v"], w.C)
+        names = ("segment", "compose", "correct")
+
+        def launches():
+            yield lambda: dra.ops.forward_stage(0, w.kind, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"],
+                                                out=o, workspace=ws, chunk_size=w.C, flags=flags)
+            yield lambda: dra.ops.forward_stage(1, w.kind, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"],
+                                                out=o, hT=hT, workspace=ws, chunk_size=w.C)
+            yield lambda: dra.ops.forward_stage(2, w.kind, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"],
+                                                out=o, workspace=ws, chunk_size=w.C)
+        kbytes = segment_bytes(w.kind, w, io_b)
+        flops = algorithmic(w.kind, w, io_b)[2]
+    else:
+        # the record path: chunk-parallel kernel, then the state pass
+        ws = ops.alloc_record_workspace(w.kind, d["q"], d["v"], w.C)
+        names = ("intra", "inter")
+
+        def launches():
+            yield lambda: dra.intra(w.kind, d["q"], d["k"], d["v"], d["g"], d["beta"], w.C, workspace=ws,
+                                    flags=flags)
+            yield lambda: dra.inter(w.kind, ws, B, T, H, Dk, Dv, io, h0=d["h0"], out=o, hT=hT, chunk_size=w.C)
+        b1, b2, flops = algorithmic(w.kind, w, io_b)
+        kbytes = {"intra": b1 * th, "inter": b2 * th}
+
+    nl = len(names)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        dra.intra(w.kind, d["q"], d["k"], d["v"], d["g"], d["beta"], w.C, workspace=ws, flags=flags)
-        if ev is not None:
-            ev[1].record(stream)
-        dra.inter(w.kind, ws, B, T, H, Dk, Dv, io, h0=d["h0"], out=o, hT=hT, chunk_size=w.C)
-        if ev is not None:
-            ev[2].record(stream)
+        for i, launch in enumerate(launches()):
+            launch()
+            if ev is not None:
+                ev[i + 1].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nl + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    k1 = [e[0].elapsed_time(e[1]) for e in evs]
-    k2 = [e[1].elapsed_time(e[2]) for e in evs]
-    per_step = sorted(e[0].elapsed_time(e[2]) for e in evs)
+    kms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / len(evs) for i, n in enumerate(names)}
+    per_step = sorted(e[0].elapsed_time(e[nl]) for e in evs)
 
     # the same steps with the 256 MB last-level cache (MALL) flushed before
     # each one by a 512 MB write; only the step itself is inside the events
@@ -610,26 +682,19 @@ def main():
     cold = []
     for _ in range(args.steps):
         flush.fill_(1)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(nl + 1)]
         step(ev)
         torch.cuda.synchronize()
-        cold.append(ev[0].elapsed_time(ev[2]))
+        cold.append(ev[0].elapsed_time(ev[nl]))
     cold.sort()
     del flush
     ms = wall * 1000.0 / args.steps
     tokens = B * T
     value = tokens / (ms / 1000.0)
 
-    io_b = 2 if io == torch.bfloat16 else 4
-    b1, b2, flops = algorithmic(w.kind, w, io_b)
-    th = B * T * H
-    k1_ms, k2_ms = sum(k1) / len(k1), sum(k2) / len(k2)
-    kern = {
-        "intra": {"avg_ms": k1_ms, "bytes": b1 * th, "gbs": b1 * th / (k1_ms * 1e-3) / 1e9},
-        "inter": {"avg_ms": k2_ms, "bytes": b2 * th, "gbs": b2 * th / (k2_ms * 1e-3) / 1e9},
-    }
+    kern = {n: {"avg_ms": kms[n], "bytes": kbytes[n], "gbs": kbytes[n] / (kms[n] * 1e-3) / 1e9} for n in names}
     dom = max(kern, key=lambda n: kern[n]["avg_ms"])
-    traffic = measured_traffic(args.workload)
+    traffic = measured_traffic(args.workload, args.path)
     roof = {"bound": "hbm", "kernel": dom, "achieved": round(kern[dom]["gbs"], 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(kern[dom]["gbs"] / HBM_PEAK_GBS, 4),
             "traffic": traffic.get(dom),
@@ -648,7 +713,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if io == torch.bfloat16 else "f32", "data": "synthetic",
-        "config": {"workload": f"{w.kind}_fwd B={B} H={H} T={T} dk={Dk} dv={Dv} C={w.C}",
+        "config": {"workload": f"{w.kind}_fwd B={B} H={H} T={T} dk={Dk} dv={Dv} C={w.C}", "path": args.path,
                    "global_batch": B, "seq_len": T, "heads": H, "parallelism": "single GPU",
                    "gate": f"a ~ U[{w.gate_lo}, {w.gate_hi}]"},
         "median_ms_per_step_events": round(per_step[len(per_step) // 2], 4),

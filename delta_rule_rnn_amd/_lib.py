@@ -18,6 +18,10 @@ _sz = ctypes.c_size_t
 SIGNATURES = {
     "dr_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "dr_record_bytes": (_sz, [_i, _i, _i, _i]),
+    "dr_record_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "dr_segment_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "dr_forward_stage": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp,
+                              _sz, _vp, _vp]),
     "kda_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp, _vp]),
     "gdn_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp, _vp]),
     "decay_la_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),

@@ -152,6 +152,18 @@ __device__ __forceinline__ void st_frag(float* p, const Frag<float>& f) {
     reinterpret_cast<float4*>(p)[0] = make_float4(f.v[0], f.v[1], f.v[2], f.v[3]);
     reinterpret_cast<float4*>(p)[1] = make_float4(f.v[4], f.v[5], f.v[6], f.v[7]);
 }
+// Negated fragment (sign flips; exact in either type).
+__device__ __forceinline__ Frag<bf16> frag_neg(const Frag<bf16>& f) {
+    Frag<bf16> r;
+    r.v = -f.v;
+    return r;
+}
+__device__ __forceinline__ Frag<float> frag_neg(const Frag<float>& f) {
+    Frag<float> r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r.v[j] = -f.v[j];
+    return r;
+}
 // fragment slot access
 __device__ __forceinline__ float frag_get(const Frag<bf16>& f, int j) { return (float)f.v[j]; }
 __device__ __forceinline__ float frag_get(const Frag<float>& f, int j) { return f.v[j]; }

@@ -23,9 +23,46 @@ dr_status forward(int kind, const void* q, const void* k, const void* v, const f
     p.use_pro = use_pro;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (T == 0) return launch_inter(p, h0, hT, 0, 0, st);
+    if (seg_supported(Dk, dtype)) {
+        // segment-parallel path: local segment pass, entry-state
+        // composition (and hT), then the output correction
+        const SegLayout S = seg_layout(B, T, H, Dk, dtype);
+        if ((s = launch_seg_local(p, S, h0, st)) != DR_OK) return s;
+        if ((s = launch_seg_compose(p, S, hT, st)) != DR_OK) return s;
+        return launch_seg_correct(p, S, st);
+    }
     s = launch_intra(p, 0, p.NT, st);
     if (s != DR_OK) return s;
     return launch_inter(p, h0, hT, 0, p.NT, st);
+}
+
+// One stage of the segment-parallel forward (0: local pass, 1: composition,
+// 2: correction), for callers that time or split the stages.
+dr_status forward_stage(int stage, int kind, const void* q, const void* k, const void* v, const float* g,
+                        const float* beta, const float* h0, void* o, float* hT, int B, int T, int H, int Dk, int Dv,
+                        int C, int dtype, const dr_prologue* pro, void* ws, size_t ws_bytes, unsigned* flags,
+                        void* stream) {
+    if (stage < 0 || stage > 2) return DR_ERR_INVALID_ARG;
+    dr_status s = validate(kind, stage == 0 ? q : nullptr, k, v, g, beta, B, T, H, Dk, Dv, C, dtype);
+    if (stage == 0 && s != DR_OK) return s;
+    if (stage != 0 && (kind < 0 || kind > 2 || B <= 0 || H <= 0 || T < 0 || (dtype != DR_F32 && dtype != DR_BF16)))
+        return DR_ERR_INVALID_ARG;
+    if (Dk != Dv || (Dk != 64 && Dk != 128) || C != dr::kChunk || !seg_built(Dk, dtype)) return DR_ERR_UNSUPPORTED;
+    dr::Prologue pr;
+    bool use_pro;
+    if ((s = resolve_prologue(kind, pro, &pr, &use_pro)) != DR_OK) return s;
+    if (T > 0 && stage != 1 && !o) return DR_ERR_INVALID_ARG;
+    if (!aligned16(o) || !aligned16(h0) || !aligned16(hT) || !aligned16(ws)) return DR_ERR_INVALID_ARG;
+    const SegLayout S = seg_layout(B, T, H, Dk, dtype);
+    if (T == 0) return DR_OK;
+    if (ws == nullptr || ws_bytes < S.bytes) return DR_ERR_WORKSPACE;
+    Problem p = make_problem(kind, q, k, v, g, beta, o, B, T, H, Dk, dtype, ws, flags);
+    p.pro = pr;
+    p.use_pro = use_pro;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (stage == 0) return launch_seg_local(p, S, h0, st);
+    if (stage == 1) return launch_seg_compose(p, S, hT, st);
+    return launch_seg_correct(p, S, st);
 }
 
 
@@ -251,11 +288,31 @@ size_t dr_record_bytes(int Dk, int Dv, int C, int dtype) {
     return record_bytes(Dk, dtype);
 }
 
-size_t dr_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, int C, int dtype) {
+size_t dr_record_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, int C, int dtype) {
     if (kind < 0 || kind > 2 || B <= 0 || H <= 0 || T < 0) return 0;
     const size_t rec = dr_record_bytes(Dk, Dv, C, dtype);
     if (rec == 0) return 0;
     return (size_t)B * H * (size_t)ceil_div(T, C) * rec;
+}
+
+size_t dr_segment_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, int C, int dtype) {
+    const size_t rec = dr_record_workspace_bytes(kind, B, T, H, Dk, Dv, C, dtype);
+    if (rec == 0 || !seg_built(Dk, dtype)) return 0;
+    return T == 0 ? 0 : seg_layout(B, T, H, Dk, dtype).bytes;
+}
+
+size_t dr_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, int C, int dtype) {
+    const size_t rec = dr_record_workspace_bytes(kind, B, T, H, Dk, Dv, C, dtype);
+    if (rec == 0 || T == 0) return rec;
+    return seg_supported(Dk, dtype) ? seg_layout(B, T, H, Dk, dtype).bytes : rec;
+}
+
+dr_status dr_forward_stage(int stage, int kind, const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, const float* h0, void* o, float* hT, int B, int T, int H, int Dk,
+                           int Dv, int C, int dtype, const dr_prologue* prologue, void* workspace,
+                           size_t workspace_bytes, unsigned* flags, void* stream) {
+    return forward_stage(stage, kind, q, k, v, g, kind == DR_KIND_DECAY_LA ? nullptr : beta, h0, o, hT, B, T, H, Dk,
+                         Dv, C, dtype, prologue, workspace, workspace_bytes, flags, stream);
 }
 
 dr_status kda_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
@@ -285,7 +342,7 @@ dr_status dr_intra(int kind, const void* q, const void* k, const void* v, const 
     dr_status s = validate(kind, q, k, v, g, beta, B, T, H, Dk, Dv, C, dtype);
     if (s != DR_OK) return s;
     if (!aligned16(workspace)) return DR_ERR_INVALID_ARG;
-    if (T > 0 && (!workspace || workspace_bytes < dr_workspace_bytes(kind, B, T, H, Dk, Dv, C, dtype)))
+    if (T > 0 && (!workspace || workspace_bytes < dr_record_workspace_bytes(kind, B, T, H, Dk, Dv, C, dtype)))
         return DR_ERR_WORKSPACE;
     const Problem p = make_problem(kind, q, k, v, g, beta, nullptr, B, T, H, Dk, dtype, workspace, flags);
     return launch_intra(p, 0, p.NT, static_cast<hipStream_t>(stream));
@@ -298,7 +355,7 @@ dr_status dr_inter(int kind, const float* h0, void* o, float* hT, int B, int T, 
     if (Dk != Dv || (Dk != 64 && Dk != 128) || C != dr::kChunk) return DR_ERR_UNSUPPORTED;
     if (T > 0 && !o) return DR_ERR_INVALID_ARG;
     if (!aligned16(o) || !aligned16(h0) || !aligned16(hT) || !aligned16(workspace)) return DR_ERR_INVALID_ARG;
-    if (T > 0 && (!workspace || workspace_bytes < dr_workspace_bytes(kind, B, T, H, Dk, Dv, C, dtype)))
+    if (T > 0 && (!workspace || workspace_bytes < dr_record_workspace_bytes(kind, B, T, H, Dk, Dv, C, dtype)))
         return DR_ERR_WORKSPACE;
     if (T == 0 && hT == nullptr) return DR_OK;
     const Problem p = make_problem(kind, nullptr, nullptr, nullptr, nullptr, nullptr, o, B, T, H, Dk, dtype,

@@ -7,6 +7,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <algorithm>
+
 #include "../../include/deltarule.h"
 #include "common.h"
 
@@ -229,6 +231,50 @@ inline ProBwdLayout probwd_layout(int kind, int B, int T, int H, int D, int dtyp
     L.bytes = L.core + core;
     return L;
 }
+
+// ---- segment-parallel forward (seg.h) ------------------------------------
+// The chunks of every (b, h) chain are grouped into NS segments of L chunks,
+// sized so that B*H*NS is about kSegGroups workgroups (one per CU).  The
+// choice depends only on the problem's sizes, so workspace queries are
+// deterministic.  Workspace: q_eff [B*H*NT][C][D] (I/O dtype), [M | N]
+// [B*H][NS][D][2D] fp32, S_in^T [B*H][NS][D][D] (I/O dtype), each 256-aligned.
+constexpr int kSegGroups = 256;
+struct SegLayout {
+    int NS, L;
+    size_t qeff, xend, sint, bytes;
+};
+// Whether the segment kernel is built for these sizes (fp32 at D = 128
+// does not fit its LDS plan).
+inline bool seg_built(int D, int dtype) { return dtype == DR_BF16 || D == 64; }
+// The path the forward entry points take: the record path unless
+// DR_FWD_PATH=segment selects the segment-parallel one (where it is built).
+inline bool seg_supported(int D, int dtype) {
+    const char* e = getenv("DR_FWD_PATH");
+    return e != nullptr && e[0] == 's' && seg_built(D, dtype);
+}
+inline SegLayout seg_layout(int B, int T, int H, int D, int dtype) {
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    SegLayout S{1, 1, 0, 0, 0, 0};
+    const int NT = ceil_div(T, dr::kChunk);
+    const long long chains = (long long)B * H;
+    if (NT > 1 && chains < kSegGroups) {
+        const int want = (int)std::min<long long>(NT, (kSegGroups + chains - 1) / chains);
+        S.L = ceil_div(NT, want);
+        S.NS = ceil_div(NT, S.L);
+    } else {
+        S.L = std::max(NT, 1);
+        S.NS = 1;
+    }
+    const size_t esz = dtype == DR_BF16 ? 2 : 4;
+    S.qeff = 0;
+    S.xend = up((size_t)chains * NT * dr::kChunk * D * esz);
+    S.sint = S.xend + up((size_t)chains * S.NS * D * 2 * D * 4);
+    S.bytes = S.sint + up((size_t)chains * S.NS * D * D * esz);
+    return S;
+}
+dr_status launch_seg_local(const Problem& p, const SegLayout& S, const float* h0, hipStream_t st);  // k_seg.hip
+dr_status launch_seg_compose(const Problem& p, const SegLayout& S, float* hT, hipStream_t st);     // k_seg.hip
+dr_status launch_seg_correct(const Problem& p, const SegLayout& S, hipStream_t st);                // k_seg.hip
 
 // The whole forward (dense layout), as dr_forward runs it (deltarule.hip).
 dr_status forward(int kind, const void* q, const void* k, const void* v, const float* g, const float* beta,

@@ -105,9 +105,31 @@ def record_bytes(Dk: int, Dv: int, dtype: torch.dtype, chunk_size: int = CHUNK) 
     return int(_lib.load().dr_record_bytes(Dk, Dv, chunk_size, code))
 
 
+def record_workspace_bytes(kind: str, B: int, T: int, H: int, Dk: int, Dv: int, dtype: torch.dtype,
+                           chunk_size: int = CHUNK) -> int:
+    code = DR_BF16 if dtype == torch.bfloat16 else DR_F32
+    return int(_lib.load().dr_record_workspace_bytes(KINDS[kind], B, T, H, Dk, Dv, chunk_size, code))
+
+
 def alloc_workspace(kind, q: torch.Tensor, v: torch.Tensor, chunk_size: int = CHUNK) -> torch.Tensor:
+    """Workspace of the full forward entry points (dr_workspace_bytes)."""
     B, T, H, Dk = q.shape
     n = workspace_bytes(kind, B, T, H, Dk, v.shape[-1], q.dtype, chunk_size)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+
+
+def alloc_segment_workspace(kind, q: torch.Tensor, v: torch.Tensor, chunk_size: int = CHUNK) -> torch.Tensor:
+    """Workspace of the segment-parallel forward's stages (dr_forward_stage)."""
+    B, T, H, Dk = q.shape
+    code = DR_BF16 if q.dtype == torch.bfloat16 else DR_F32
+    n = int(_lib.load().dr_segment_workspace_bytes(KINDS[kind], B, T, H, Dk, v.shape[-1], chunk_size, code))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+
+
+def alloc_record_workspace(kind, q: torch.Tensor, v: torch.Tensor, chunk_size: int = CHUNK) -> torch.Tensor:
+    """Workspace of the record path's step entry points dr_intra / dr_inter."""
+    B, T, H, Dk = q.shape
+    n = record_workspace_bytes(kind, B, T, H, Dk, v.shape[-1], q.dtype, chunk_size)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
 
 
@@ -183,6 +205,23 @@ def forward_noalloc(kind: str, q, k, v, g, beta=None, h0=None, output_final_stat
     del keep
     _check(st, "dr_forward_noalloc")
     return o, hT
+
+
+def forward_stage(stage: int, kind: str, q, k, v, g, beta=None, h0=None, out=None, hT=None, workspace=None,
+                  chunk_size=CHUNK, flags=None, stream=None, prologue: Optional[Prologue] = None) -> None:
+    """One stage of the segment-parallel forward (dr_forward_stage): 0 the
+    local segment pass (writes out and the workspace), 1 the entry-state
+    composition (writes hT), 2 the output correction (updates out).  The
+    three in order with one workspace equal :func:`forward`."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    keep, pro = _pro_arg(prologue, H)
+    st = _lib.load().dr_forward_stage(stage, KINDS[kind], _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                      _ptr(beta) if kind != "decay_la" else None, _ptr(h0), _ptr(out), _ptr(hT),
+                                      B, T, H, Dk, Dv, chunk_size, _dtype_code(q), pro, _ptr(workspace),
+                                      0 if workspace is None else workspace.numel(), _ptr(flags), _stream(stream))
+    del keep
+    _check(st, f"dr_forward_stage({stage})")
 
 
 def kda_fwd(q, k, v, g, beta, h0=None, output_final_state=True, chunk_size=CHUNK, workspace=None,
@@ -527,7 +566,7 @@ def intra(kind: str, q, k, v, g, beta=None, chunk_size: int = CHUNK, workspace=N
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
     if workspace is None:
-        workspace = alloc_workspace(kind, q, v, chunk_size)
+        workspace = alloc_record_workspace(kind, q, v, chunk_size)
     _check(_lib.load().dr_intra(KINDS[kind], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), B, T, H, Dk,
                                 Dv, chunk_size, _dtype_code(q), _ptr(workspace), workspace.numel(),
                                 _ptr(flags), _stream(stream)), "dr_intra")

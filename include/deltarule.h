@@ -79,10 +79,20 @@ typedef enum { DR_KIND_KDA = 0, DR_KIND_GDN = 1, DR_KIND_DECAY_LA = 2 } dr_kind;
  * bounds) but the results are not meaningful. */
 #define DR_FLAG_BAD_SEQLENS   0x4u
 
-/* Bytes of device workspace kda_fwd / gdn_fwd / decay_la_fwd need for these
- * sizes (0 for invalid sizes).  The workspace holds one record per chunk and
- * head (the operands the sequential state pass streams). */
+/* Bytes of device workspace kda_fwd / gdn_fwd / decay_la_fwd / dr_forward
+ * need for these sizes (0 for invalid sizes): the workspace of the path the
+ * forward takes (see kda_fwd), which depends on the sizes and on the
+ * DR_FWD_PATH environment variable only. */
 size_t dr_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, int C, int dtype);
+/* Bytes of the segment-parallel path's workspace (dr_forward_stage): the
+ * effective queries of every chunk in the I/O dtype ([B*H*NT][C][Dk]),
+ * each segment's exit map [M | N] in fp32 ([Dk][Dk+Dv]) and its entry state
+ * in the I/O dtype ([Dv][Dk]); 0 where that path is not built (fp32 I/O at
+ * Dk = 128) or for invalid sizes. */
+size_t dr_segment_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, int C, int dtype);
+/* Bytes of the record workspace of dr_intra / dr_inter: B*H*ceil(T/C)
+ * records of dr_record_bytes(). */
+size_t dr_record_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, int C, int dtype);
 
 /*
  * Full forward, KDA (per-channel gate).
@@ -95,10 +105,23 @@ size_t dr_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, int C, 
  *   workspace: device buffer of at least dr_workspace_bytes(DR_KIND_KDA, ...)
  *   flags: device uint32 or NULL (see DR_FLAG_*)
  * Steps (all on `stream`): chunk-local log2 cumsum of g, the separable
- * exponent prep, the UT transform (K1, chunk-parallel), then the sequential
- * state pass fused with the chunk output (K2).  Page sections: "TileLang
- * 实战：KDA 从零到一–Kimi Delta Attention" sections 1.2, 3.2, 3.3; "RNN的复兴04"
- * (DPLR) section 5.3.5.
+ * exponent prep, the UT transform, the state pass and the chunk output.
+ * Page sections: "TileLang 实战：KDA 从零到一–Kimi Delta Attention" sections
+ * 1.2, 3.2, 3.3; "RNN的复兴04" (DPLR) section 5.3.5.
+ * Two execution paths compute the same result (to rounding); the record
+ * path runs unless the environment variable DR_FWD_PATH=segment selects the
+ * segment-parallel one where it is built:
+ *   segment-parallel (bf16 I/O, and fp32 I/O at Dk = 64): the chunks of each
+ *     (b, h) are grouped into segments (sizes chosen from B*H and T only).
+ *     One kernel runs every segment from the entry state [I | 0], carrying
+ *     the segment's transition and its zero-entry state through the chunks'
+ *     cumsum, prep, UT transform and state update, and writes each chunk's
+ *     output from a zero entry state plus its effective queries; a second
+ *     kernel composes the segment entry states (and hT); a third adds
+ *     q_eff S_in to the outputs of all segments but the first.  This is the
+ *     entry-state hand-off of sequence-split evaluation ("Gated DeltaNet",
+ *     section "前向计算的矩阵分解") inside one GPU.
+ *   record path: dr_intra then dr_inter.
  */
 dr_status kda_fwd(const void* q, const void* k, const void* v, const float* g,
                   const float* beta, const float* h0, void* o, float* hT,
@@ -426,7 +449,7 @@ dr_status dr_kda_prep(const void* q, const void* k, const float* gamma,
  *   Aqk   [w<4][kb<2][l][j<8] = Aqk[pw(w, l%16)][32kb + 8(l/16) + j]
  *   UT    [t<Dv/16][w<4][l][i<4] = U[32(w/2) + 8(l/16) + 4(w%2) + i][16t + l%16]
  * Rows of a ragged last chunk beyond T are zero.  Record size:
- * dr_record_bytes().  For GDN / decay_la, g is [B,T,H] and beta may be NULL
+ * dr_record_bytes(); workspace: dr_record_workspace_bytes().  For GDN / decay_la, g is [B,T,H] and beta may be NULL
  * for decay_la.
  */
 dr_status dr_intra(int kind, const void* q, const void* k, const void* v, const float* g,
@@ -449,12 +472,34 @@ dr_status dr_inter(int kind, const float* h0, void* o, float* hT,
 /* Bytes of one workspace record (0 for unsupported sizes). */
 size_t dr_record_bytes(int Dk, int Dv, int C, int dtype);
 
+/*
+ * One stage of the segment-parallel forward that kda_fwd / gdn_fwd /
+ * decay_la_fwd / dr_forward run, for callers that time or split them; the
+ * three stages in order on one stream, with the same arguments and
+ * workspace, equal dr_forward:
+ *   stage 0  local segment pass: reads q, k, v, g, beta, h0 (segment 0 starts
+ *            from it), writes o (final for the first segment) and the
+ *            workspace;
+ *   stage 1  entry-state composition: reads the workspace, writes hT (may be
+ *            NULL) and the segment entry states into the workspace;
+ *   stage 2  output correction: reads the workspace, updates o.
+ * Arguments a stage does not use may be NULL.  The workspace is sized by
+ * dr_segment_workspace_bytes.  Returns DR_ERR_UNSUPPORTED for sizes the
+ * segment path is not built for (fp32 I/O at Dk = 128).
+ */
+dr_status dr_forward_stage(int stage, int kind, const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, const float* h0, void* o, float* hT,
+                           int B, int T, int H, int Dk, int Dv, int C, int dtype,
+                           const dr_prologue* prologue, void* workspace, size_t workspace_bytes,
+                           unsigned* flags, void* stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* dr_status_string(int status);
 
-/* ABI version of this library: 5 (1, plus the prologue entry points in 2, the
+/* ABI version of this library: 6 (1, plus the prologue entry points in 2, the
  * backward in 3, the backward through the prologue in 4, the packed-sequence
- * backward in 5). */
+ * backward in 5, the allocation-free forward, the segment-parallel forward's
+ * stages and the record workspace query in 6). */
 int dr_abi_version(void);
 
 #ifdef __cplusplus

@@ -51,8 +51,19 @@ def test_workspace_sizes(lib):
     # one record per (b, h, chunk); bf16 D=128 record: (3*64*128 + 64*64 + 128*64)*2 + 128*4
     rec = lib.dr_record_bytes(128, 128, 64, 1)
     assert rec == ((3 * 64 * 128 + 64 * 64 + 128 * 64) * 2 + 128 * 4 + 255) // 256 * 256
-    assert lib.dr_workspace_bytes(0, 2, 130, 3, 128, 128, 64, 1) == 2 * 3 * 3 * rec
+    assert lib.dr_record_workspace_bytes(0, 2, 130, 3, 128, 128, 64, 1) == 2 * 3 * 3 * rec
     assert lib.dr_workspace_bytes(1, 1, 0, 1, 64, 64, 64, 0) == 0
+    # segment-parallel forward: q_eff of every chunk, then [M | N] (fp32) and
+    # the entry state (I/O dtype) of every segment; 6 chains of 3 chunks give
+    # one-chunk segments (about 256 workgroups wanted)
+    up = lambda x: (x + 255) // 256 * 256
+    chains, NT, NS, D = 6, 3, 3, 128
+    want = up(chains * NT * 64 * D * 2) + up(chains * NS * D * 2 * D * 4) + up(chains * NS * D * D * 2)
+    assert lib.dr_segment_workspace_bytes(0, 2, 130, 3, 128, 128, 64, 1) == want
+    # not built for fp32 at D = 128
+    assert lib.dr_segment_workspace_bytes(0, 2, 130, 3, 128, 128, 64, 0) == 0
+    # the forward's own workspace: the record path by default
+    assert lib.dr_workspace_bytes(0, 2, 130, 3, 128, 128, 64, 1) == 2 * 3 * 3 * rec
     assert lib.dr_record_bytes(96, 96, 64, 1) == 0
     assert lib.dr_record_bytes(128, 64, 64, 1) == 0
     assert lib.dr_record_bytes(128, 128, 32, 1) == 0
@@ -86,11 +97,11 @@ def test_noalloc_limit_is_checked_on_the_host(lib):
                             None, None, None)
     assert lib.dr_forward_noalloc(*args(0, 64, 1)) == -1
     assert lib.dr_forward_noalloc(5, *args(1, 64, 1)[1:]) == -1
-    rec = lib.dr_record_bytes(128, 128, 64, 1)
-    chunks = cap // rec + 1                      # one chunk-head more than fits
-    st = lib.dr_forward_noalloc(*args(1, 64 * chunks, 1))
+    T = 64
+    while lib.dr_workspace_bytes(0, 1, T, 1, 128, 128, 64, 1) <= cap:
+        T *= 2
+    st = lib.dr_forward_noalloc(*args(1, T, 1))
     assert st == -5 and b"static scratch" in lib.dr_status_string(st)
-    assert lib.dr_workspace_bytes(0, 1, 64 * (chunks - 1), 1, 128, 128, 64, 1) <= cap
 
 
 def test_other_entry_points_reject(lib):

@@ -21,7 +21,7 @@ import torch
 from oracle.backward import recurrence_backward
 from delta_rule_rnn_amd.inputs import Workload, generate, generate_raw
 
-from .test_gpu_parity import assert_close, to_dev
+from .test_gpu_parity import assert_close_grad, to_dev
 
 pytestmark = pytest.mark.gpu
 EXACT = ("dq", "dk", "dv", "dh0")
@@ -60,11 +60,11 @@ def test_autograd_dense_matches_backward(kind, dt):
         assert torch.equal(leaves[leaf_of[n]].grad, grads[n]), n
     orc = recurrence_backward(kind, x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"].transpose(-1, -2),
                               _cpu(do), _cpu(w2).transpose(-1, -2))
-    assert_close(leaves["g"].grad.float().cpu().numpy(), orc["dg"], dt, f"{kind} {dt} autograd dg")
+    assert_close_grad(leaves["g"].grad.float().cpu().numpy(), orc["dg"], dt, f"{kind} {dt} autograd dg")
     if kind == "decay_la":
         assert grads["dbeta"] is None and leaves["beta"] is None
     else:
-        assert_close(leaves["beta"].grad.float().cpu().numpy(), orc["dbeta"], dt, f"{kind} {dt} autograd dbeta")
+        assert_close_grad(leaves["beta"].grad.float().cpu().numpy(), orc["dbeta"], dt, f"{kind} {dt} autograd dbeta")
 
 
 def test_autograd_output_only():
@@ -145,8 +145,8 @@ def test_autograd_packed_with_prologue(kind):
         sr = lambda t: t[:, a:b]
         r = opro.apply_backward(kind, sr(raw["q"]), sr(raw["k"]), sr(raw["g"]), sr(raw["beta"]), core["dq"],
                                 core["dk"], core["dg"], core["dbeta"], **ok)
-        assert_close(dg_got[:, a:b], r["dg"], "bf16", f"{kind} autograd seq {i} dg")
-        assert_close(db_got[:, a:b], r["dbeta"], "bf16", f"{kind} autograd seq {i} dbeta")
+        assert_close_grad(dg_got[:, a:b], r["dg"], "bf16", f"{kind} autograd seq {i} dg")
+        assert_close_grad(db_got[:, a:b], r["dbeta"], "bf16", f"{kind} autograd seq {i} dbeta")
     if gate:
         # per-head sums over every token, held to the bf16 tolerance times
         # sum_t |coef_t| * max_t |dg^_t| (the size of the terms they add)

@@ -16,7 +16,7 @@ import torch
 from oracle.backward import recurrence_backward
 from delta_rule_rnn_amd.inputs import Workload, generate
 
-from .test_gpu_parity import assert_close, to_dev
+from .test_gpu_parity import assert_close_grad, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -52,13 +52,13 @@ def _run(kind, dt, D, B, H, T, seed, with_h0=True, with_dhT=True):
 
 def _check(res, ref, kind, dt, what):
     dq, dk, dv, dg, dbeta, dh0 = (None if t is None else t.float().cpu().numpy() for t in res)
-    assert_close(dq, ref["dq"], dt, f"{what} dq")
-    assert_close(dk, ref["dk"], dt, f"{what} dk")
-    assert_close(dv, ref["dv"], dt, f"{what} dv")
-    assert_close(dg, ref["dg"], "f32" if dt == "f32" else dt, f"{what} dg")
+    assert_close_grad(dq, ref["dq"], dt, f"{what} dq")
+    assert_close_grad(dk, ref["dk"], dt, f"{what} dk")
+    assert_close_grad(dv, ref["dv"], dt, f"{what} dv")
+    assert_close_grad(dg, ref["dg"], "f32" if dt == "f32" else dt, f"{what} dg")
     if kind != "decay_la":
-        assert_close(dbeta, ref["dbeta"], dt, f"{what} dbeta")
-    assert_close(dh0, np.swapaxes(ref["dh0"], -1, -2), dt, f"{what} dh0")
+        assert_close_grad(dbeta, ref["dbeta"], dt, f"{what} dbeta")
+    assert_close_grad(dh0, np.swapaxes(ref["dh0"], -1, -2), dt, f"{what} dh0")
 
 
 CASES = [(kind, dt, D) for kind in ("kda", "gdn", "decay_la") for dt in ("f32", "bf16") for D in (64, 128)]
@@ -118,8 +118,8 @@ def test_backward_long_sampled():
                                   x["h0"][:, h:h + 1].transpose(-1, -2), sl(do), dhT[:, h:h + 1].transpose(-1, -2))
         names = ["dq", "dk", "dv", "dg", "dbeta"]
         for n, r in zip(names, res[:5]):
-            assert_close(r[:, :, h:h + 1], ref[n], "bf16", f"head {h} {n}")
-        assert_close(res[5][:, h:h + 1], np.swapaxes(ref["dh0"], -1, -2), "bf16", f"head {h} dh0")
+            assert_close_grad(r[:, :, h:h + 1], ref[n], "bf16", f"head {h} {n}")
+        assert_close_grad(res[5][:, h:h + 1], np.swapaxes(ref["dh0"], -1, -2), "bf16", f"head {h} dh0")
 
 
 def test_backward_full_size_sampled():
@@ -141,8 +141,8 @@ def test_backward_full_size_sampled():
     ref = recurrence_backward("kda", sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]), None,
                               sl(do), dhT[:, h:h + 1].transpose(-1, -2))
     for n, r in zip(["dq", "dk", "dv", "dg", "dbeta"], res[:5]):
-        assert_close(r[:, :, h:h + 1].float().cpu().numpy(), ref[n], "bf16", f"full size head {h} {n}")
-    assert_close(res[5][:, h:h + 1].cpu().numpy(), np.swapaxes(ref["dh0"], -1, -2), "bf16", f"full size head {h} dh0")
+        assert_close_grad(r[:, :, h:h + 1].float().cpu().numpy(), ref[n], "bf16", f"full size head {h} {n}")
+    assert_close_grad(res[5][:, h:h + 1].cpu().numpy(), np.swapaxes(ref["dh0"], -1, -2), "bf16", f"full size head {h} dh0")
 
 
 PRO_CASES = [("kda", "bf16", 128, dict(qk=True, sig=True, x2=False, scale=0.5)),
@@ -185,13 +185,13 @@ def test_backward_through_prologue(kind, dt, D, opts):
                               core["dbeta"], **ok)
     got = [None if t is None else t.float().cpu().numpy() for t in res]
     what = f"{kind} {dt} D{D} {opts}"
-    assert_close(got[0], ref["dq"], dt, f"{what} dq")
-    assert_close(got[1], ref["dk"], dt, f"{what} dk")
-    assert_close(got[2], core["dv"], dt, f"{what} dv")
-    assert_close(got[3], ref["dg"], dt, f"{what} dg")
+    assert_close_grad(got[0], ref["dq"], dt, f"{what} dq")
+    assert_close_grad(got[1], ref["dk"], dt, f"{what} dk")
+    assert_close_grad(got[2], core["dv"], dt, f"{what} dv")
+    assert_close_grad(got[3], ref["dg"], dt, f"{what} dg")
     if kind != "decay_la":
-        assert_close(got[4], ref["dbeta"], dt, f"{what} dbeta")
-    assert_close(got[5], np.swapaxes(core["dh0"], -1, -2), dt, f"{what} dh0")
+        assert_close_grad(got[4], ref["dbeta"], dt, f"{what} dbeta")
+    assert_close_grad(got[5], np.swapaxes(core["dh0"], -1, -2), dt, f"{what} dh0")
     if gate:
         # sums over all tokens of coef_t * dg^_t, with cancellation.  The
         # per-token dg^ is held to the dtype's tolerance relative to its

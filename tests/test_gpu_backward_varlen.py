@@ -17,7 +17,7 @@ import torch
 from oracle.backward import recurrence_backward
 from delta_rule_rnn_amd.inputs import Workload, generate
 
-from .test_gpu_parity import assert_close, to_dev
+from .test_gpu_parity import assert_close_grad, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -55,10 +55,10 @@ def _check_seq(got, ref, kind, dt, a, b, i, what):
     dq, dk, dv, dg, dbeta, dh0 = got
     if b > a:
         for name, val in (("dq", dq), ("dk", dk), ("dv", dv), ("dg", dg)):
-            assert_close(val[:, a:b], ref[name], dt, f"{what} seq {i} {name}")
+            assert_close_grad(val[:, a:b], ref[name], dt, f"{what} seq {i} {name}")
         if kind != "decay_la":
-            assert_close(dbeta[:, a:b], ref["dbeta"], dt, f"{what} seq {i} dbeta")
-    assert_close(dh0[i:i + 1], np.swapaxes(ref["dh0"], -1, -2), dt, f"{what} seq {i} dh0")
+            assert_close_grad(dbeta[:, a:b], ref["dbeta"], dt, f"{what} seq {i} dbeta")
+    assert_close_grad(dh0[i:i + 1], np.swapaxes(ref["dh0"], -1, -2), dt, f"{what} seq {i} dh0")
 
 
 CASES = [("kda", "bf16", 128), ("gdn", "bf16", 128), ("decay_la", "bf16", 128),
@@ -162,18 +162,18 @@ def test_backward_varlen_through_prologue(kind, dt, D):
                                    h0[i:i + 1].transpose(-1, -2), do[:, a:b], dhT[i:i + 1].transpose(-1, -2))
         core_dg[:, a:b] = core["dg"]
         what = f"{kind} {dt} D{D} seq {i}"
-        assert_close(got[5][i:i + 1], np.swapaxes(core["dh0"], -1, -2), dt, f"{what} dh0")
+        assert_close_grad(got[5][i:i + 1], np.swapaxes(core["dh0"], -1, -2), dt, f"{what} dh0")
         if b == a:
             continue
         sr = lambda t: None if t is None else t[:, a:b]
         ref = opro.apply_backward(kind, sr(x["q"]), sr(x["k"]), sr(x["g"]), sr(x["beta"]), core["dq"], core["dk"],
                                   core["dg"], core["dbeta"], **ok)
-        assert_close(got[0][:, a:b], ref["dq"], dt, f"{what} dq")
-        assert_close(got[1][:, a:b], ref["dk"], dt, f"{what} dk")
-        assert_close(got[2][:, a:b], core["dv"], dt, f"{what} dv")
-        assert_close(got[3][:, a:b], ref["dg"], dt, f"{what} dg")
+        assert_close_grad(got[0][:, a:b], ref["dq"], dt, f"{what} dq")
+        assert_close_grad(got[1][:, a:b], ref["dk"], dt, f"{what} dk")
+        assert_close_grad(got[2][:, a:b], core["dv"], dt, f"{what} dv")
+        assert_close_grad(got[3][:, a:b], ref["dg"], dt, f"{what} dg")
         if delta:
-            assert_close(got[4][:, a:b], ref["dbeta"], dt, f"{what} dbeta")
+            assert_close_grad(got[4][:, a:b], ref["dbeta"], dt, f"{what} dbeta")
     if gate:
         # the per-head sums over every token of every sequence, held to the
         # dtype's tolerance times sum_t |coef_t| * max_t |dg^_t|
@@ -262,5 +262,5 @@ def test_backward_varlen_full_size_sampled():
                                   h0[i:i + 1, h:h + 1].transpose(-1, -2), sl(do),
                                   dhT[i:i + 1, h:h + 1].transpose(-1, -2))
         for name, val in zip(["dq", "dk", "dv", "dg", "dbeta"], got):
-            assert_close(val[:, a:b], ref[name], "bf16", f"seq {i} (length {b - a}) head {h} {name}")
-        assert_close(dh0[i:i + 1], np.swapaxes(ref["dh0"], -1, -2), "bf16", f"seq {i} head {h} dh0")
+            assert_close_grad(val[:, a:b], ref[name], "bf16", f"seq {i} (length {b - a}) head {h} {name}")
+        assert_close_grad(dh0[i:i + 1], np.swapaxes(ref["dh0"], -1, -2), "bf16", f"seq {i} head {h} dh0")

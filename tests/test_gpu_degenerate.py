@@ -28,7 +28,7 @@ import oracle
 from oracle.backward import recurrence_backward
 from delta_rule_rnn_amd.inputs import Workload, generate
 
-from .test_gpu_parity import assert_close, to_dev
+from .test_gpu_parity import assert_close, assert_close_grad, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -71,7 +71,7 @@ def _backward_check(kind, dt, x, what, seed=82, dg_abs=False):
     ref = recurrence_backward(kind, x["q"], x["k"], x["v"], x["g"], x["beta"], h0, do, dhT.transpose(-1, -2))
     got = [None if t is None else t.float().cpu().numpy() for t in res]
     for name, val in zip(["dq", "dk", "dv"], got[:3]):
-        assert_close(val, ref[name], dt, f"{what} {name}")
+        assert_close_grad(val, ref[name], dt, f"{what} {name}")
     if dg_abs:
         # the chunk form reaches dg as a sum of O(|dk|) terms that cancel
         # exactly in exact arithmetic: held to the dtype's tolerance times
@@ -81,10 +81,10 @@ def _backward_check(kind, dt, x, what, seed=82, dg_abs=False):
         scale = np.max(np.abs(ref["dk"]))
         assert err <= tol * scale, f"{what} dg: max abs err {err:.3e} > {tol} * {scale:.3e}"
     else:
-        assert_close(got[3], ref["dg"], dt, f"{what} dg")
+        assert_close_grad(got[3], ref["dg"], dt, f"{what} dg")
     if kind != "decay_la":
-        assert_close(got[4], ref["dbeta"], dt, f"{what} dbeta")
-    assert_close(got[5], np.swapaxes(ref["dh0"], -1, -2), dt, f"{what} dh0")
+        assert_close_grad(got[4], ref["dbeta"], dt, f"{what} dbeta")
+    assert_close_grad(got[5], np.swapaxes(ref["dh0"], -1, -2), dt, f"{what} dh0")
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])

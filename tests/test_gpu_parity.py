@@ -6,13 +6,20 @@ Tolerances (per output, o and the final state hT separately):
              output RMS: the pages' kernel acceptance metric, "TileLang 实战：
              KDA 从零到一--标量衰减" section 7 item 4)
              max|gpu - ref| / max|ref| <= 2e-2   (max relative error)
-  max|gpu - ref| / rms(ref) is printed too, next to its floor: the same
-  quantity for the fp64 reference merely rounded to bf16, which already
-  exceeds 2e-2 on the delta-rule workloads (heavy-tailed outputs), so no
-  bf16-output implementation can meet that stricter reading.
-Small cases compare every element; the full-size workloads run in the same
-launch configuration as the benchmark and compare sampled (b, h) chains,
-which the oracle computes one by one.
+             max|gpu - ref| / rms(ref) <= 2e-2 + 3 floor, where floor is the
+             same quantity for the fp64 reference merely rounded to bf16
+             (what storing the exact result in bf16 costs: 1.0e-2 to 3.4e-2
+             of the rms on these heavy-tailed outputs).  The three floor
+             units are the roundings that scale with the largest output
+             element in the bf16-operand chunk form: the output's own store
+             and the bf16 state and pseudo-value operands of the two products
+             that form it; a CPU emulation of the chunk form with its bf16
+             operand roundings lands at about 2.8 floor units.
+Both forward paths are checked: the segment-parallel one the entry points
+take, and the record path (dr_intra + dr_inter) selected with
+DR_FWD_PATH.  Small cases compare every element; the full-size workloads
+run in the same launch configuration as the benchmark and compare every
+element of every chain against one oracle pass over the whole batch.
 """
 from __future__ import annotations
 
@@ -51,15 +58,38 @@ def bf16_floor(ref: np.ndarray) -> float:
     return float(np.max(np.abs(r - ref)) / max(np.sqrt(np.mean(ref ** 2)), 1e-30))
 
 
-def assert_close(gpu, ref, dtype: str, what: str, tol_l2=2e-2, tol_max=2e-2):
+def assert_close(gpu, ref, dtype: str, what: str, tol_l2=2e-2, tol_max=2e-2, tol_rms=2e-2):
+    """The forward's tolerance (module docstring); tol_rms=None leaves out the
+    max/rms bound (gradients, see assert_close_grad)."""
     e_max, e_l2, e_rms = errs(gpu, ref)
     assert np.all(np.isfinite(gpu)), f"{what}: non-finite values"
     if dtype == "f32":
         assert e_max <= 1e-4, f"{what}: max rel err {e_max:.3e} > 1e-4"
     else:
+        fl = bf16_floor(ref)
         assert e_l2 <= tol_l2, f"{what}: rel-L2 {e_l2:.3e} > {tol_l2}"
         assert e_max <= tol_max, f"{what}: max rel err {e_max:.3e} > {tol_max}"
+        if tol_rms is not None:
+            assert e_rms <= tol_rms + 3 * fl, f"{what}: max/rms {e_rms:.3e} > {tol_rms} + 3 floor ({fl:.3e})"
     return e_max, e_l2, e_rms
+
+
+def assert_close_grad(gpu, ref, dtype: str, what: str, **kw):
+    """Gradients: rel-L2 and max|d|/max|ref| within the dtype's bound, as for
+    the forward, without the max/rms bound the forward's o and hT carry (the
+    pages state no tolerance for gradients)."""
+    return assert_close(gpu, ref, dtype, what, tol_rms=None, **kw)
+
+
+@pytest.fixture(params=["segment", "records"])
+def fwd_path(request, monkeypatch):
+    """Runs a test once per forward path (the record path through
+    DR_FWD_PATH, which the library reads at every call)."""
+    if request.param == "segment":
+        monkeypatch.setenv("DR_FWD_PATH", "segment")
+    else:
+        monkeypatch.delenv("DR_FWD_PATH", raising=False)
+    return request.param
 
 
 def run_gpu(w: Workload, x: dict, **kw):
@@ -104,15 +134,15 @@ for kind in ("kda", "gdn", "decay_la"):
 
 
 @pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
-def test_small_parity(w):
+def test_small_parity(w, fwd_path):
     x = generate(w)
     o, hT = run_gpu(w, x)
     check_full(w, x, o, hT)
 
 
-@pytest.mark.parametrize("T", [1, 17, 63, 64, 65, 128, 130])
+@pytest.mark.parametrize("T", [1, 17, 63, 64, 65, 128, 130, 1000])
 @pytest.mark.parametrize("kind", ["kda", "gdn", "decay_la"])
-def test_lengths(kind, T):
+def test_lengths(kind, T, fwd_path):
     w = Workload(f"{kind}_T{T}", kind, "bf16", B=1, H=2, T=T, Dk=128, Dv=128, h0_std=0.1, seed=T)
     x = generate(w)
     o, hT = run_gpu(w, x)
@@ -132,9 +162,11 @@ def test_empty_sequence_copies_state():
     assert torch.count_nonzero(hT0).item() == 0
 
 
-def test_resume_is_exact():
+def test_resume(fwd_path):
     """Splitting at a chunk boundary and handing the state over through
-    h0/hT gives bit-identical results (same chunks, same arithmetic)."""
+    h0/hT: bit-identical on the record path (same chunks, same arithmetic);
+    on the segment path the segments, and so the rounding, depend on the
+    length of each call, and the two agree within the bf16 tolerance."""
     dra = _ops()
     w = Workload("kda_resume", "kda", "bf16", B=1, H=4, T=320, Dk=128, Dv=128, h0_std=0.1, seed=5)
     x = to_dev(generate(w))
@@ -146,8 +178,15 @@ def test_resume_is_exact():
     o2, h2 = dra.kda_fwd(cut(x["q"], s, 320), cut(x["k"], s, 320), cut(x["v"], s, 320),
                          cut(x["g"], s, 320), cut(x["beta"], s, 320), h1)
     torch.cuda.synchronize()
-    assert torch.equal(torch.cat([o1, o2], 1), o)
-    assert torch.equal(h2, hT)
+    if fwd_path == "records":
+        assert torch.equal(torch.cat([o1, o2], 1), o)
+        assert torch.equal(h2, hT)
+    else:
+        xc = {n: (t.cpu() if t is not None else None) for n, t in x.items()}
+        ro, rs = oracle.recurrence("kda", xc["q"], xc["k"], xc["v"], xc["g"], xc["beta"],
+                                   xc["h0"].transpose(-1, -2))
+        assert_close(torch.cat([o1, o2], 1).float().cpu().numpy(), ro, "bf16", "resumed output")
+        assert_close(h2.cpu().numpy(), np.swapaxes(rs, -1, -2), "bf16", "resumed state")
 
 
 
@@ -161,6 +200,7 @@ def test_state_pass_layouts_agree(kind, dt, monkeypatch):
     dra = _ops()
     w = Workload(f"{kind}_layouts", kind, dt, B=2, H=3, T=64 * 5 + 9, Dk=128, Dv=128, h0_std=0.1, seed=9)
     x = to_dev(generate(w))
+    monkeypatch.delenv("DR_FWD_PATH", raising=False)
     monkeypatch.setenv("DR_INTER_NTN", "1")
     monkeypatch.setenv("DR_INTER_PFD", "0")
     o1, h1 = dra.forward(kind, x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"])
@@ -173,7 +213,7 @@ def test_state_pass_layouts_agree(kind, dt, monkeypatch):
             torch.cuda.synchronize()
             assert torch.equal(o2, o1) and torch.equal(h2, h1), f"columns {16 * int(ntn)}, prefetch {pfd}"
 
-def test_deterministic():
+def test_deterministic(fwd_path):
     w = Workload("gdn_det", "gdn", "bf16", B=2, H=4, T=500, Dk=128, Dv=128, h0_std=0.1, seed=6)
     x = generate(w)
     o1, h1 = run_gpu(w, x)
@@ -256,7 +296,8 @@ def test_step_a3_records(kind, dt, D):
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
-def test_inter_from_records_matches_forward(dt):
+def test_inter_from_records_matches_forward(dt, monkeypatch):
+    monkeypatch.delenv("DR_FWD_PATH", raising=False)
     dra = _ops()
     w = Workload("split", "kda", dt, B=2, H=2, T=300, Dk=128, Dv=128, h0_std=0.1, seed=8)
     d = to_dev(generate(w))
@@ -266,6 +307,60 @@ def test_inter_from_records_matches_forward(dt):
     o2, _ = dra.inter("kda", ws, 2, 300, 2, 128, 128, d["q"].dtype, h0=d["h0"], hT=hT2)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(hT, hT2)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_segment_stages_equal_forward(dt, D, monkeypatch):
+    """dr_forward_stage 0, 1, 2 in order equal the forward entry point bit for
+    bit (the same three launches)."""
+    if dt == "f32" and D == 128:
+        pytest.skip("the segment path is not built for fp32 at D = 128")
+    monkeypatch.setenv("DR_FWD_PATH", "segment")
+    dra = _ops()
+    from delta_rule_rnn_amd import ops
+    w = Workload("stages", "kda", dt, B=2, H=3, T=700, Dk=D, Dv=D, h0_std=0.1, seed=12)
+    d = to_dev(generate(w))
+    o, hT = dra.kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"])
+    ws = ops.alloc_segment_workspace("kda", d["q"], d["v"])
+    o2, h2 = torch.empty_like(o), torch.empty_like(hT)
+    for st in range(3):
+        ops.forward_stage(st, "kda", d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], out=o2, hT=h2,
+                          workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(hT, h2)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_kda_channel_equal_gates_match_gdn(dt, D, fwd_path):
+    """KDA with every channel's gate equal to the GDN scalar gate must give the
+    GDN result ("TileLang 实战：KDA 从零到一–Kimi Delta Attention" section 3.4:
+    the degenerate case it checks first).  On the GPU the two take different
+    code: the separable exponent k 2^(+-gamma) for KDA, the masked ratio
+    2^(gamma_i - gamma_j) for GDN; they must agree to the dtype's tolerance."""
+    dra = _ops()
+    w = Workload("ceq", "gdn", dt, B=2, H=3, T=64 * 4 + 21, Dk=D, Dv=D, h0_std=0.1, seed=21 + D)
+    x = generate(w)
+    d = to_dev(x)
+    g_kda = d["g"][..., None].expand(*d["g"].shape, D).contiguous()
+    o_g, h_g = dra.gdn_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"])
+    o_k, h_k = dra.kda_fwd(d["q"], d["k"], d["v"], g_kda, d["beta"], d["h0"])
+    torch.cuda.synchronize()
+    # both against the GDN recurrence, and to each other
+    ro, rs = oracle.recurrence("gdn", x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"].transpose(-1, -2))
+    rs = np.swapaxes(rs, -1, -2)
+    for name, o_, h_ in (("kda", o_k, h_k), ("gdn", o_g, h_g)):
+        assert_close(o_.float().cpu().numpy(), ro, dt, f"channel-equal {name} output")
+        assert_close(h_.cpu().numpy(), rs, dt, f"channel-equal {name} state")
+    e = errs(o_k.float().cpu().numpy(), o_g.float().cpu().double().numpy())
+    es = errs(h_k.cpu().numpy(), h_g.cpu().double().numpy())
+    if dt == "f32":
+        assert e[0] <= 1e-4 and es[0] <= 1e-4, (e, es)
+    else:
+        assert e[1] <= 2e-2 and es[1] <= 2e-2, (e, es)
+    print(f"channel-equal KDA vs GDN ({fwd_path}, {dt}, D={D}): o max-rel {e[0]:.2e} rel-L2 {e[1]:.2e};"
+          f" hT max-rel {es[0]:.2e}", flush=True)
 
 
 def test_gate_range_flags():
@@ -292,21 +387,37 @@ def test_workload_gdn_f32_small_full():
     check_full(w, x, o, hT)
 
 
-@pytest.mark.parametrize("name", ["la_bf16", "gdn_bf16", "kda_bf16", "kda_bf16_long",
-                                  "kda_bf16_long_stress", "gdn_bf16_long"])
-def test_workload_full_size_sampled(name):
+FULL = [("la_bf16", "segment"), ("gdn_bf16", "segment"), ("kda_bf16", "segment"),
+        ("kda_bf16_long", "segment"), ("kda_bf16_long_stress", "segment"), ("gdn_bf16_long", "segment"),
+        ("kda_bf16_long", "records")]
+
+
+@pytest.mark.parametrize("name,path", FULL, ids=lambda v: str(v))
+def test_workload_full_size(name, path, monkeypatch):
+    """Every element of every chain of the full-size workload, in the
+    benchmark's launch configuration, against one oracle pass over the whole
+    batch (all host cores).  Prints the error next to each tolerance."""
+    if path == "segment":
+        monkeypatch.setenv("DR_FWD_PATH", "segment")
+    else:
+        monkeypatch.delenv("DR_FWD_PATH", raising=False)
     w = WORKLOADS[name]
     x = generate(w)
-    print(f"{name}: inputs generated", flush=True)
+    print(f"{name} ({path}): inputs generated", flush=True)
     o, hT = run_gpu(w, x)
     assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(hT).all())
-    chains = [(0, 0), (w.B - 1, w.H - 1)]
-    refs = oracle_chains(w, x, chains)
-    for (b, h), (ro, rs) in zip(chains, refs):
-        eo = assert_close(o[b, :, h].float().cpu().numpy(), ro, w.dtype, f"{name} o b={b} h={h}")
-        es = assert_close(hT[b, h].cpu().numpy(), rs, w.dtype, f"{name} hT b={b} h={h}")
-        print(f"{name} chain ({b},{h}): o max-rel {eo[0]:.2e} rel-L2 {eo[1]:.2e} max/rms {eo[2]:.2e}"
-              f" (bf16 floor {bf16_floor(ro):.2e}); hT max-rel {es[0]:.2e} rel-L2 {es[1]:.2e}", flush=True)
+    h0 = None if x["h0"] is None else x["h0"].transpose(-1, -2)
+    ro, rs = oracle.recurrence(w.kind, x["q"], x["k"], x["v"], x["g"], x["beta"], h0)
+    print(f"{name} ({path}): oracle done", flush=True)
+    got = o.float().cpu().numpy()
+    del o
+    eo = assert_close(got, ro, w.dtype, f"{name} output")
+    fl = bf16_floor(ro)
+    del got, ro
+    es = assert_close(hT.cpu().numpy(), np.swapaxes(rs, -1, -2), w.dtype, f"{name} state")
+    print(f"margins {name} ({path}): o rel-L2 {eo[1]:.2e}/2e-2, max-rel {eo[0]:.2e}/2e-2, "
+          f"max/rms {eo[2]:.2e}/{2e-2 + 3 * fl:.2e} (floor {fl:.2e}); hT rel-L2 {es[1]:.2e}, max-rel {es[0]:.2e}",
+          flush=True)
 
 
 def test_stress_gate_km_range():

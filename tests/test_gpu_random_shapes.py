@@ -17,7 +17,7 @@ import oracle
 from oracle.backward import recurrence_backward
 from delta_rule_rnn_amd.inputs import Workload, generate
 
-from .test_gpu_parity import assert_close, to_dev
+from .test_gpu_parity import assert_close, assert_close_grad, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -60,10 +60,10 @@ def test_random_dense_forward_backward(seed):
     ref = recurrence_backward(kind, x["q"], x["k"], x["v"], x["g"], x["beta"], h0, do, dhT.transpose(-1, -2))
     got = [None if t is None else t.float().cpu().numpy() for t in res]
     for name, val in zip(["dq", "dk", "dv", "dg"], got[:4]):
-        assert_close(val, ref[name], dt, f"{what} {name}")
+        assert_close_grad(val, ref[name], dt, f"{what} {name}")
     if kind != "decay_la":
-        assert_close(got[4], ref["dbeta"], dt, f"{what} dbeta")
-    assert_close(got[5], np.swapaxes(ref["dh0"], -1, -2), dt, f"{what} dh0")
+        assert_close_grad(got[4], ref["dbeta"], dt, f"{what} dbeta")
+    assert_close_grad(got[5], np.swapaxes(ref["dh0"], -1, -2), dt, f"{what} dh0")
 
 
 @pytest.mark.parametrize("seed", range(8))
@@ -104,11 +104,11 @@ def test_random_packed_forward_backward(seed):
         assert_close(hT[i:i + 1], np.swapaxes(rs, -1, -2), dt, f"{what} seq {i} state")
         ref = recurrence_backward(kind, sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]), hi,
                                   sl(do), dhT[i:i + 1].transpose(-1, -2))
-        assert_close(got[5][i:i + 1], np.swapaxes(ref["dh0"], -1, -2), dt, f"{what} seq {i} dh0")
+        assert_close_grad(got[5][i:i + 1], np.swapaxes(ref["dh0"], -1, -2), dt, f"{what} seq {i} dh0")
         if b == a:
             continue
         assert_close(o[:, a:b], ro, dt, f"{what} seq {i} output")
         for name, val in zip(["dq", "dk", "dv", "dg"], got[:4]):
-            assert_close(val[:, a:b], ref[name], dt, f"{what} seq {i} {name}")
+            assert_close_grad(val[:, a:b], ref[name], dt, f"{what} seq {i} {name}")
         if kind != "decay_la":
-            assert_close(got[4][:, a:b], ref["dbeta"], dt, f"{what} seq {i} dbeta")
+            assert_close_grad(got[4][:, a:b], ref["dbeta"], dt, f"{what} seq {i} dbeta")

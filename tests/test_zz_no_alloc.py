@@ -46,9 +46,10 @@ def test_noalloc_refuses_problems_over_the_limit():
     from delta_rule_rnn_amd import _lib, ops
     lib = _lib.load()
     cap = lib.dr_noalloc_scratch_bytes()
-    rec = ops.record_bytes(128, 128, torch.bfloat16)
-    T = 64 * (cap // rec + 1)
-    w = WORKLOADS["kda_bf16"].with_(B=1, H=1, T=T, seed=3)
+    T = 64
+    while ops.workspace_bytes("kda", 1, T, 8, 128, 128, torch.bfloat16) <= cap:
+        T *= 2
+    w = WORKLOADS["kda_bf16"].with_(B=1, H=8, T=T, seed=3)
     x = {n: (t.to(DEV) if t is not None else None) for n, t in generate(w).items()}
     with pytest.raises(dra.DeltaRuleError, match="static scratch"):
         dra.forward_noalloc("kda", x["q"], x["k"], x["v"], x["g"], x["beta"])
