@@ -264,6 +264,42 @@ __device__ __forceinline__ void st4_stream(float* p, const float* in) {
     st_stream(reinterpret_cast<float4*>(p), make_float4(in[0], in[1], in[2], in[3]));
 }
 
+// Buffer stores: a resource over [base, base + bytes) whose out-of-range
+// lanes the hardware drops, so a store needs no branch on the row index (a
+// branch around a store leaves the compiler unable to count outstanding
+// memory operations, and it then waits for all of them at the next use of a
+// prefetched load).  The third resource word is the raw 32-bit data format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// four consecutive elements (8 bytes bf16, 16 bytes fp32) at byte offset off
+__device__ __forceinline__ void buf_st4(__amdgpu_buffer_rsrc_t r, unsigned off, const bf16* /*type tag*/,
+                                        const float* in) {
+    bf16x4 x;
+    x[0] = (bf16)in[0]; x[1] = (bf16)in[1]; x[2] = (bf16)in[2]; x[3] = (bf16)in[3];
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), r, (int)off, 0, 0);
+}
+__device__ __forceinline__ Raw4<bf16> buf_ld4(__amdgpu_buffer_rsrc_t r, unsigned off, const bf16* /*type tag*/) {
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    Raw4<bf16> x;
+    x.v = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+    return x;
+}
+__device__ __forceinline__ Raw4<float> buf_ld4(__amdgpu_buffer_rsrc_t r, unsigned off, const float* /*type tag*/) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    Raw4<float> x;
+    x.v = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+    return x;
+}
+__device__ __forceinline__ void buf_st4(__amdgpu_buffer_rsrc_t r, unsigned off, const float* /*type tag*/,
+                                        const float* in) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    typedef float f32x4_ __attribute__((ext_vector_type(4)));
+    const f32x4_ x = {in[0], in[1], in[2], in[3]};
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, (int)off, 0, 0);
+}
+
 // Workgroup barrier that orders LDS traffic only: waits for this wave's LDS
 // operations, then meets the other waves.  Unlike __syncthreads() it does not
 // wait for outstanding global loads and stores, so prefetches and record

@@ -10,7 +10,9 @@ namespace {
 template <int KIND, typename E, int D, bool PRO>
 dr_status launch_seg_local_t(const Problem& p, const SegLayout& S, const float* h0, hipStream_t st) {
     const long long groups = (long long)p.B * p.H * S.NS;
-    if (groups > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
+    // the kernel addresses one chunk of o (C rows of H*D elements) with 32-bit offsets
+    if (groups > 0x7fffffffLL || (long long)dr::kChunk * p.H * D * (long long)sizeof(E) > 0x7fffffffLL)
+        return DR_ERR_UNSUPPORTED;
     hipLaunchKernelGGL((dr::seg_kernel<KIND, E, D, D, PRO>), dim3((unsigned)groups), dim3(dr::kSegThreads), 0, st,
                        static_cast<const E*>(p.q), static_cast<const E*>(p.k), static_cast<const E*>(p.v), p.g,
                        p.beta, h0, static_cast<E*>(p.o), reinterpret_cast<E*>(p.ws + S.qeff),
@@ -44,7 +46,8 @@ dr_status launch_compose_t(const Problem& p, const SegLayout& S, float* hT, hipS
 
 template <typename E, int D>
 dr_status launch_correct_t(const Problem& p, const SegLayout& S, hipStream_t st) {
-    const long long items = (long long)p.B * p.H * (p.NT - S.L);
+    const long long groups = (S.L + dr::kCorrChunks - 1) / dr::kCorrChunks;
+    const long long items = (long long)p.B * p.H * (S.NS - 1) * groups;
     if (items <= 0) return DR_OK;
     if (items > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
     hipLaunchKernelGGL((dr::correct_kernel<E, D, D>), dim3((unsigned)items), dim3(dr::kThreads), 0, st,

@@ -49,7 +49,7 @@ constexpr int kSegTargetGroups = 256;       // segments are sized to give about 
 //   KM  K- [C][LDK] (P1 -> P2), then U^T [DV][LDC] (P4 -> P5)
 //   QP  Q~ [C][LDK]                         P1 -> P5
 //   A   A fp32 [C][LDF] (P2 -> P3), then W [C][LDK] (P4 -> P5)
-//   TT  per-group gate totals (P1), then T fp32 [C][LDF] (P3 -> P4)
+//   TT  per-group gate totals and their prefixes (P1), then T fp32 [C][LDF]
 //   VT  V^T [DV][LDC]                       P1 -> P4 (decay_la: -> P5)
 //   KBT Kbar^T [DK][LDC]                    P1 -> P5
 //   AQK Aqk [C][LDC]                        P2 -> P5
@@ -74,7 +74,7 @@ struct SegCfg {
     static constexpr size_t R_QP = R_KM + up16(mx(SZ_CK, SZ_TC));
     static constexpr size_t R_A = R_QP + up16(SZ_CK);
     static constexpr size_t R_TT = R_A + up16(mx(SZ_F, SZ_CK));
-    static constexpr size_t R_VT = R_TT + up16(mx(SZ_F, (size_t)NQ * DK * sizeof(float)));
+    static constexpr size_t R_VT = R_TT + up16(mx(SZ_F, (size_t)(NQ + 1) * DK * sizeof(float)));
     static constexpr size_t R_KBT = R_VT + up16(SZ_TC);
     static constexpr size_t R_AQK = R_KBT + up16(SZ_TC);
     static constexpr size_t R_BETA = R_AQK + up16((size_t)C * LDC * sizeof(T));
@@ -107,28 +107,30 @@ template <int KIND, typename T, int DK, int DV>
 __device__ __forceinline__ void seg_load(SegIn<KIND, T, DK, DV>& in, const T* __restrict__ q,
                                          const T* __restrict__ k, const T* __restrict__ v,
                                          const float* __restrict__ g, const float* __restrict__ beta,
-                                         size_t row0, int nvalid, int H)
+                                         size_t row0, int nvalid, int H, int tid)
 {
     using Cfg = SegCfg<KIND, T, DK, DV>;
     using In = SegIn<KIND, T, DK, DV>;
     using VT = typename In::VT;
     using VG = typename In::VG;
     constexpr int NCG = Cfg::NCG, PL = Cfg::PL, CPT = Cfg::CPT;
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int lane = tid & 63;
     const int last = nvalid - 1;
     const int ch0 = CPT * (tid % NCG), p0 = (tid / NCG) * PL;
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
         const size_t off = (row0 + (size_t)min(p0 + i, last) * H) * DK + ch0;
-        if constexpr (KIND == KIND_KDA) in.gv[i] = ld_stream(reinterpret_cast<const VG*>(g + off));
-        in.kv[i] = ld_stream(reinterpret_cast<const VT*>(k + off));
-        in.qv[i] = ld_stream(reinterpret_cast<const VT*>(q + off));
+        if constexpr (KIND == KIND_KDA) in.gv[i] = *reinterpret_cast<const VG*>(g + off);
+        in.kv[i] = *reinterpret_cast<const VT*>(k + off);
+        in.qv[i] = *reinterpret_cast<const VT*>(q + off);
     }
-    if constexpr (KIND != KIND_KDA) in.gs = (tid < 64) ? ld_stream(g + row0 + (size_t)min(lane, last) * H) : 0.f;
-    if constexpr (KIND != KIND_LA) in.bt = (tid < kChunk) ? ld_stream(beta + row0 + (size_t)min(tid, last) * H) : 0.f;
+    // every thread loads (waves past the first re-read rows already fetched)
+    // so that the loads are unconditional
+    if constexpr (KIND != KIND_KDA) in.gs = g[row0 + (size_t)min(lane, last) * H];
+    if constexpr (KIND != KIND_LA) in.bt = beta[row0 + (size_t)min(lane, last) * H];
 #pragma unroll
     for (int i = 0; i < PL; ++i)
-        in.vv[i] = ld_stream(reinterpret_cast<const VT*>(v + (row0 + (size_t)min(p0 + i, last) * H) * DV + ch0));
+        in.vv[i] = *reinterpret_cast<const VT*>(v + (row0 + (size_t)min(p0 + i, last) * H) * DV + ch0);
 }
 
 // Pack two accumulator tiles (rows 8q..8q+3 and 8q+4..8q+7 of a 32-row block)
@@ -145,12 +147,16 @@ __device__ __forceinline__ Frag<T> pack_frag(const f32x4& lo, const f32x4& hi) {
 }
 
 // ---------------------------------------------------------------------------
-// Steps a1-a3 of one chunk into LDS (P0-P4).  On return (after a barrier)
-// LDS holds Q~ (QP), W (A; delta kinds), U^T (KM; decay_la: V^T in VT), Kbar^T
-// (KBT), Aqk (AQK) and phi (PHI) of the chunk.
-template <int KIND, typename T, int DK, int DV, bool PRO>
+// Steps a1-a3 of one chunk into LDS (P0-P3).  On return (after a barrier)
+// LDS holds K+ (KP), Q~ (QP), V^T (VT), Kbar^T (KBT), Aqk (AQK), phi (PHI)
+// and, for the delta kinds, T = (I + A)^-1 (TT, fp32) and beta.  The state
+// step forms the chunk's pseudo values as Y = T diag(beta) (U_bar - K+ X),
+// the product U - W X of the UT transform taken in the other order, so W and
+// U are never materialised.
+template <int KIND, typename T, int DK, int DV, bool PRO, typename NF>
 __device__ __forceinline__ void seg_chunk_ops(const SegIn<KIND, T, DK, DV>& in, uint8_t* smem,
-                                              unsigned* __restrict__ flags, int nvalid, const ProHead& ph)
+                                              float& mxneg_seg, int nvalid, const ProHead& ph,
+                                              int tid, NF&& next_loads)
 {
     using Cfg = SegCfg<KIND, T, DK, DV>;
     constexpr int C = kChunk;
@@ -165,10 +171,8 @@ __device__ __forceinline__ void seg_chunk_ops(const SegIn<KIND, T, DK, DV>& in, 
 
     T* sKp = reinterpret_cast<T*>(smem + Cfg::R_KP);
     T* sKm = reinterpret_cast<T*>(smem + Cfg::R_KM);
-    T* sUt = reinterpret_cast<T*>(smem + Cfg::R_KM);
     T* sQp = reinterpret_cast<T*>(smem + Cfg::R_QP);
     float* sA = reinterpret_cast<float*>(smem + Cfg::R_A);
-    T* sW = reinterpret_cast<T*>(smem + Cfg::R_A);
     float* sTot = reinterpret_cast<float*>(smem + Cfg::R_TT);
     float* sT = reinterpret_cast<float*>(smem + Cfg::R_TT);
     T* sVt = reinterpret_cast<T*>(smem + Cfg::R_VT);
@@ -178,7 +182,8 @@ __device__ __forceinline__ void seg_chunk_ops(const SegIn<KIND, T, DK, DV>& in, 
     float* sGam = reinterpret_cast<float*>(smem + Cfg::R_GAM);
     float* sPhi = reinterpret_cast<float*>(smem + Cfg::R_PHI);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar register)
     const int r16 = lane & 15, grp = lane >> 4;
 
     // ---- P0: inputs, rows past the end of a ragged chunk zeroed ------------
@@ -241,18 +246,34 @@ __device__ __forceinline__ void seg_chunk_ops(const SegIn<KIND, T, DK, DV>& in, 
             *reinterpret_cast<VG*>(sTot + qg * DK + ch0) = tot;
         }
         lds_barrier();
-        float pre[CPT], all[CPT];
+        // exclusive prefix of the NQ = 16 group totals per channel, in place:
+        // four adjacent lanes per channel take four groups each, then scan
+        // across the four lanes; the channel's total goes to sAll
+        static_assert(NQ == 16, "group scan");
+        float* sAll = sTot + NQ * DK;
+        if (tid < 4 * DK) {
+            const int ch = tid >> 2, qq = tid & 3;
+            float t[4], e[4], sum = 0.f;
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) pre[j] = all[j] = 0.f;
+            for (int i = 0; i < 4; ++i) t[i] = sTot[(4 * qq + i) * DK + ch];
 #pragma unroll
-        for (int jq = 0; jq < NQ; ++jq) {
-            const VG a = *reinterpret_cast<const VG*>(sTot + jq * DK + ch0);
-#pragma unroll
-            for (int j = 0; j < CPT; ++j) {
-                if (jq < qg) pre[j] += a[j];
-                all[j] += a[j];
+            for (int i = 0; i < 4; ++i) {
+                e[i] = sum;
+                sum += t[i];
             }
+            float x = sum;
+            float y = __shfl_up(x, 1, 4);
+            if (qq >= 1) x += y;
+            y = __shfl_up(x, 2, 4);
+            if (qq >= 2) x += y;
+            const float excl = x - sum;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sTot[(4 * qq + i) * DK + ch] = excl + e[i];
+            if (qq == 3) sAll[ch] = x;
         }
+        lds_barrier();
+        const VG pre = *reinterpret_cast<const VG*>(sTot + qg * DK + ch0);
+        const VG all = *reinterpret_cast<const VG*>(sAll + ch0);
 #pragma unroll
         for (int j = 0; j < CPT; ++j) glast[j] = all[j] * kLog2e;
 #pragma unroll
@@ -321,76 +342,88 @@ __device__ __forceinline__ void seg_chunk_ops(const SegIn<KIND, T, DK, DV>& in, 
             }
         }
         // Kbar^T and V^T: PL consecutive positions of one channel per store
+        // (V moves as stored, without a round trip through fp32)
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
             st4(sKbT + (ch0 + j) * LDC + p0, kb[j]);
-            float vt[PL];
+            typename VecOf<T, 4>::type vt;
 #pragma unroll
-            for (int i = 0; i < PL; ++i) vt[i] = (float)vv[i][j];
-            st4(sVt + (ch0 + j) * LDC + p0, vt);
+            for (int i = 0; i < PL; ++i) vt[i] = vv[i][j];
+            *reinterpret_cast<typename VecOf<T, 4>::type*>(sVt + (ch0 + j) * LDC + p0) = vt;
         }
         if (qg == 0) {
 #pragma unroll
             for (int j = 0; j < CPT; ++j) sPhi[ch0 + j] = phi[j];
         }
-        if constexpr (PERCH) {
-            if (flags) {
-                const unsigned long long b16 = __ballot(mxneg >= 16.f);
-                const unsigned long long b126 = __ballot(mxneg >= 126.f);
-                if (lane == 0 && (b16 | b126)) atomicOr(flags, (b16 ? 1u : 0u) | (b126 ? 2u : 0u));
-            }
-        }
+        if constexpr (PERCH) mxneg_seg = fmaxf(mxneg_seg, mxneg);
     }
+    next_loads();
     lds_barrier();
 
     // ---- P2: A (fp32, natural) and Aqk (natural, inclusive diagonal) -------
+    // The three lower 32x32 blocks (0,0), (1,0), (1,1) of each, one block per
+    // wave (waves 0-2: A, waves 3-5: Aqk), four 16x16 tiles sharing their
+    // operand loads; the diagonal blocks' upper tiles are written masked
+    // (zero), so the state step can read Aqk in 32-wide key blocks.
     {
         const T* kminus = PERCH ? sKm : sKp;
-        constexpr int NA = DELTA ? 10 : 0;
-        // items: NA lower tiles of A, 10 lower tiles of Aqk, and the two
-        // upper tiles (0,1), (2,3) of Aqk that the state step's 32-wide key
-        // blocks read (zero)
-        for (int idx = wave; idx < NA + 12; idx += kSegThreads / 64) {
-            if (idx >= NA + 10) {
-                const int ti = idx == NA + 10 ? 0 : 2;
-                T* dst = sAqk + (16 * ti) * LDC + 16 * (ti + 1);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dst[(4 * grp + i) * LDC + r16] = from_f<T>(0.f);
-                continue;
-            }
-            const bool isA = idx < NA;
-            int ti, tj;
-            lower_tile(isA ? idx : idx - NA, ti, tj);
+        const int item = DELTA ? wave : wave + 3;   // decay_la: Aqk only (waves 0-2)
+        if (item < 6) {
+            const bool isA = item < 3;
+            const int bi = item % 3;
+            const int bI = bi == 0 ? 0 : 1, bJ = bi == 2 ? 1 : 0;   // (0,0) (1,0) (1,1)
             const T* arows = isA ? sKp : sQp;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            f32x4 acc[2][2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int v = 0; v < 2; ++v) acc[u][v] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                const Frag<T> fa = ld_frag(arows + (16 * ti + r16) * LDK + 32 * kb + 8 * grp);
-                const Frag<T> fb = ld_frag(kminus + (16 * tj + r16) * LDK + 32 * kb + 8 * grp);
-                mma(acc, fa, fb);
-            }
-            const int col = 16 * tj + r16;
+                Frag<T> fa[2], fb[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * ti + 4 * grp + i;
-                float ratio = 1.f;
-                if constexpr (!PERCH) ratio = (col <= row) ? __builtin_amdgcn_exp2f(sGam[row] - sGam[col]) : 0.f;
-                if (isA) sA[row * LDF + col] = (col < row) ? sBeta[row] * ratio * acc[i] : 0.f;
-                else sAqk[row * LDC + col] = from_f<T>((col <= row) ? ratio * acc[i] : 0.f);
+                for (int u = 0; u < 2; ++u) {
+                    fa[u] = ld_frag(arows + (32 * bI + 16 * u + r16) * LDK + 32 * kb + 8 * grp);
+                    fb[u] = ld_frag(kminus + (32 * bJ + 16 * u + r16) * LDK + 32 * kb + 8 * grp);
+                }
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int v = 0; v < 2; ++v) mma(acc[u][v], fa[u], fb[v]);
             }
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int v = 0; v < 2; ++v) {
+                    const int col = 32 * bJ + 16 * v + r16;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = 32 * bI + 16 * u + 4 * grp + i;
+                        float ratio = 1.f;
+                        if constexpr (!PERCH) ratio = (col <= row) ? __builtin_amdgcn_exp2f(sGam[row] - sGam[col]) : 0.f;
+                        if (isA) sA[row * LDF + col] = (col < row) ? sBeta[row] * ratio * acc[u][v][i] : 0.f;
+                        else sAqk[row * LDC + col] = from_f<T>((col <= row) ? ratio * acc[u][v][i] : 0.f);
+                    }
+                }
         }
     }
     lds_barrier();
     if constexpr (!PERCH) {
-        // scalar gates: Q~ = q 2^gamma in place (every reader of raw q is done)
+        // scalar gates: Q~ = q 2^gamma and K+ = k 2^gamma in place (every
+        // reader of the raw rows is done)
 #pragma unroll
         for (int i = 0; i < PL; ++i) {
             const int p = p0 + i;
             const float sc = __builtin_amdgcn_exp2f(sGam[p]);
             VT x = *reinterpret_cast<const VT*>(sQp + p * LDK + ch0);
+            VT y = *reinterpret_cast<const VT*>(sKp + p * LDK + ch0);
 #pragma unroll
-            for (int j = 0; j < CPT; ++j) x[j] = from_f<T>((float)x[j] * sc);
+            for (int j = 0; j < CPT; ++j) {
+                x[j] = from_f<T>((float)x[j] * sc);
+                y[j] = from_f<T>((float)y[j] * sc);
+            }
             *reinterpret_cast<VT*>(sQp + p * LDK + ch0) = x;
+            *reinterpret_cast<VT*>(sKp + p * LDK + ch0) = y;
         }
     }
     if constexpr (!DELTA) {
@@ -399,23 +432,41 @@ __device__ __forceinline__ void seg_chunk_ops(const SegIn<KIND, T, DK, DV>& in, 
     }
 
     // ---- P3: T = (I + A)^-1 ([GDN] "对角子块前代" and "合并相邻子块") ---------
-    if (wave == 0) {
-        const int blk = lane >> 4, col = lane & 15;
-        float x[16];
+    // Diagonal 16x16 blocks, one wave each: with N the block of A (strictly
+    // lower, so N^16 = 0), (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8).
+    // The factors are powers of N and commute; the six dependent 16x16
+    // products run on fp32 MFMA with the powers kept in an LDS block of T
+    // that the later products never read (blocks (0,2), (0,3), (1,2), (1,3)).
+    if (wave < 4) {
+        const int blk = wave;
+        float* Tb = sT + 16 * blk * LDF + 16 * blk;                             // the diagonal block
+        float* Pw = sT + 16 * (blk >> 1) * LDF + 16 * (2 + (blk & 1));         // scratch block
+        const float* Nb = sA + 16 * blk * LDF + 16 * blk;
+        // T0 = I - N, in the accumulator layout (lane: column r16, rows 4 grp + i)
+        f32x4 t;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float* arow = sA + (16 * blk + r) * LDF + 16 * blk;
-            float acc = (r == col) ? 1.f : 0.f;
+        for (int i = 0; i < 4; ++i) {
+            const int row = 4 * grp + i;
+            t[i] = (row == r16 ? 1.f : 0.f) - Nb[row * LDF + r16];
+        }
+        const float* P = Nb;
 #pragma unroll
-            for (int j = 0; j < r; ++j) acc -= arow[j] * x[j];
-            x[r] = acc;
+        for (int k = 0; k < 3; ++k) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Tb[(4 * grp + i) * LDF + r16] = t[i];
+            const f32x4 p2 = mm16_lds(P, LDF, P, LDF, lane, f32x4{0.f, 0.f, 0.f, 0.f});   // P <- P^2
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Pw[(4 * grp + i) * LDF + r16] = p2[i];
+            P = Pw;
+            t = mm16_lds(Tb, LDF, Pw, LDF, lane, t);                                   // T <- T (I + P)
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sT[(16 * blk + r) * LDF + 16 * blk + col] = x[r];
-        if ((blk & 1) == 0) {
+        for (int i = 0; i < 4; ++i) Tb[(4 * grp + i) * LDF + r16] = t[i];
+    } else if (wave < 6) {
+        // T01 and T23 are read by the 32-wide products below: zero
+        float* z = sT + 16 * 2 * (wave - 4) * LDF + 16 * (2 * (wave - 4) + 1);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sT[(16 * blk + r) * LDF + 16 * (blk + 1) + col] = 0.f;
-        }
+        for (int i = 0; i < 4; ++i) z[(4 * grp + i) * LDF + r16] = 0.f;
     }
     lds_barrier();
 #pragma unroll
@@ -431,71 +482,6 @@ __device__ __forceinline__ void seg_chunk_ops(const SegIn<KIND, T, DK, DV>& in, 
         }
         lds_barrier();
     }
-
-    // ---- P4: [W | U] = T diag(beta) [K+ | V] ---------------------------------
-    // (scalar gates: W = T diag(beta 2^gamma) K).  n-tiles of 16 columns:
-    // waves 0-3 take W's, waves 4-7 U's.
-    {
-        constexpr int NTWt = DK / 16, NTUt = DV / 16;
-        constexpr int PER = (NTWt + NTUt) / 8;
-        static_assert(PER >= 1 && NTWt == 4 * PER, "n-tile split");
-        const bool isW = wave < 4;
-        const int nt0 = (wave & 3) * PER;
-        Frag<T> fb[PER][2];
-#pragma unroll
-        for (int n = 0; n < PER; ++n) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                if (isW) {
-                    const int col = 16 * (nt0 + n) + r16;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int p = 32 * kb + 8 * grp + j;
-                        float s = to_f(sKp[p * LDK + col]);
-                        if constexpr (!PERCH) s *= __builtin_amdgcn_exp2f(sGam[p]);
-                        frag_set(fb[n][kb], j, s);
-                    }
-                } else {
-                    fb[n][kb] = ld_frag(sVt + (16 * (nt0 + n) + r16) * LDC + 32 * kb + 8 * grp);
-                }
-            }
-        }
-        f32x4 acc[4][PER];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int n = 0; n < PER; ++n) acc[mt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                if (kb == 1 && mt < 2) continue;   // T is lower triangular
-                Frag<T> fa;
-                const float* src = sT + (16 * mt + r16) * LDF + 32 * kb + 8 * grp;
-                const float* bsrc = sBeta + 32 * kb + 8 * grp;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) frag_set(fa, j, src[j] * bsrc[j]);
-#pragma unroll
-                for (int n = 0; n < PER; ++n) mma(acc[mt][n], fa, fb[n][kb]);
-            }
-        }
-        // W natural into the A region (A is dead after the merges); U^T into
-        // the K- region (dead after P2): 4 consecutive positions per store
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int n = 0; n < PER; ++n) {
-                const int col = 16 * (nt0 + n) + r16;
-                if (isW) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) sW[(16 * mt + 4 * grp + i) * LDK + col] = from_f<T>(acc[mt][n][i]);
-                } else {
-                    const float u4[4] = {acc[mt][n][0], acc[mt][n][1], acc[mt][n][2], acc[mt][n][3]};
-                    st4(sUt + col * LDC + 16 * mt + 4 * grp, u4);
-                }
-            }
-    }
-    lds_barrier();
 }
 
 // ---------------------------------------------------------------------------
@@ -514,11 +500,12 @@ __global__ __launch_bounds__(kSegThreads, 1) void seg_kernel(
     constexpr int C = kChunk;
     constexpr int NKB = DK / 32;
     constexpr int NCW = Cfg::NCW, NTW = Cfg::NTW;
-    constexpr int LDK = Cfg::LDK, LDC = Cfg::LDC;
+    constexpr int LDK = Cfg::LDK, LDC = Cfg::LDC, LDF = Cfg::LDF;
     constexpr bool DELTA = KIND != KIND_LA;
     __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::BYTES];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar register)
     const int r16 = lane & 15, grp = lane >> 4;
     const int r = blockIdx.x % NS;
     const int chain = blockIdx.x / NS;
@@ -556,32 +543,58 @@ __global__ __launch_bounds__(kSegThreads, 1) void seg_kernel(
     }
 
     const T* sQp = reinterpret_cast<const T*>(smem + Cfg::R_QP);
-    const T* sW = reinterpret_cast<const T*>(smem + Cfg::R_A);
-    const T* sU = reinterpret_cast<const T*>(smem + (DELTA ? Cfg::R_KM : Cfg::R_VT));
+    const T* sKp = reinterpret_cast<const T*>(smem + Cfg::R_KP);
+    const T* sV = reinterpret_cast<const T*>(smem + Cfg::R_VT);
+    const float* sT = reinterpret_cast<const float*>(smem + Cfg::R_TT);
+    const float* sBeta = reinterpret_cast<const float*>(smem + Cfg::R_BETA);
     const T* sKbT = reinterpret_cast<const T*>(smem + Cfg::R_KBT);
     const T* sAqk = reinterpret_cast<const T*>(smem + Cfg::R_AQK);
     const float* sPhi = reinterpret_cast<const float*>(smem + Cfg::R_PHI);
 
+    float mxneg_seg = 0.f;   // largest chunk-local -gamma seen (gate-range flags)
     SegIn<KIND, T, DK, DV> in;
     auto row0_of = [&](int c) { return ((size_t)b * Tlen + (size_t)c * C) * H + h; };
     auto nvalid_of = [&](int c) { return min(C, Tlen - c * C); };
-    if (cbeg < cend) seg_load<KIND, T, DK, DV>(in, q, k, v, g, beta, row0_of(cbeg), nvalid_of(cbeg), H);
+    // (cbeg < cend for every workgroup of the grid; the load stays
+    // unconditional so that the compiler can count outstanding loads)
+    seg_load<KIND, T, DK, DV>(in, q, k, v, g, beta, row0_of(cbeg), nvalid_of(cbeg), H, tid);
+    {
+        // As many stores as every chunk step issues after its loads, into an
+        // empty range (the hardware drops them): the first chunk then sees
+        // the same count of memory operations behind its inputs as every
+        // later one, and the compiler waits for the inputs alone instead of
+        // for everything outstanding.
+        // (their data is the last loaded value, which keeps them behind the loads)
+        const auto none = buffer_rsrc(o, 0u);
+        const float z = (float)in.vv[Cfg::PL - 1][0];
+        const float z4[4] = {z, z, z, z};
+#pragma unroll
+        for (int i = 0; i < 4 * NTW; ++i) buf_st4(none, 16u * i, (const T*)nullptr, z4);
+    }
 
     for (int c = cbeg; c < cend; ++c) {
         const int nvalid = nvalid_of(c);
-        seg_chunk_ops<KIND, T, DK, DV, PRO>(in, smem, flags, nvalid, ph);
-        // next chunk's inputs (clamped to the last chunk: unconditional loads)
-        {
-            const int cn = min(c + 1, cend - 1);
-            seg_load<KIND, T, DK, DV>(in, q, k, v, g, beta, row0_of(cn), nvalid_of(cn), H);
-        }
+        // The thread index is re-read through an empty asm each chunk, so the
+        // compiler recomputes the lane-dependent addresses inside the loop
+        // instead of keeping dozens of them live across it (registers are
+        // the scarce resource here: X alone takes 64 per lane).
+        int tidv = threadIdx.x;
+        asm volatile("" : "+v"(tidv));
+        const int lane = tidv & 63, r16 = lane & 15, grp = lane >> 4;
+        // next chunk's inputs (clamped to the last chunk: unconditional loads),
+        // issued as soon as this chunk's are in LDS
+        const int cn = min(c + 1, cend - 1);
+        seg_chunk_ops<KIND, T, DK, DV, PRO>(in, smem, mxneg_seg, nvalid, ph, tidv, [&]() {
+            seg_load<KIND, T, DK, DV>(in, q, k, v, g, beta, row0_of(cn), nvalid_of(cn), H, tidv);
+        });
 
         // ---- P5: state step on this wave's NCW columns of X ----------------
-        // Phases are kept apart with scheduling barriers so that only one
-        // phase's operand fragments are in flight at a time; the bf16 copy of
-        // X is re-formed where it is used (cheap packs) instead of being kept.
+        // The bf16 copy of X is re-formed where it is used (cheap packs)
+        // instead of being kept in registers.
         auto xfrag = [&](int kb, int n) { return pack_frag<T>(X[kb][0][n], X[kb][1][n]); };
-        // Y = U_bar - W X  (rows: positions 32 kbp + 8 grp + 4 hh + i)
+        // Y = T diag(beta) (U_bar - K+ X)  ([KDA] 3.2: U - W X with W = T diag(beta)
+        // K+, U = T diag(beta) V), rows: positions 32 kbp + 8 grp + 4 hh + i.
+        // decay_la: Y = U_bar.
         f32x4 Y[2][2][NTW];
 #pragma unroll
         for (int kbp = 0; kbp < 2; ++kbp)
@@ -592,12 +605,13 @@ __global__ __launch_bounds__(kSegThreads, 1) void seg_kernel(
                     f32x4 u = {0.f, 0.f, 0.f, 0.f};
                     if (isS) {
                         float u4[4];
-                        ld4(sU + (col0 + 16 * n + r16) * LDC + 32 * kbp + 8 * grp + 4 * hh, u4);
+                        ld4(sV + (col0 + 16 * n + r16) * LDC + 32 * kbp + 8 * grp + 4 * hh, u4);
                         u = f32x4{u4[0], u4[1], u4[2], u4[3]};
                     }
                     Y[kbp][hh][n] = u;
                 }
         if constexpr (DELTA) {
+            // R = U_bar - K+ X (in Y's registers)
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 Frag<T> xf[NTW];
@@ -607,27 +621,49 @@ __global__ __launch_bounds__(kSegThreads, 1) void seg_kernel(
                 for (int kbp = 0; kbp < 2; ++kbp)
 #pragma unroll
                     for (int hh = 0; hh < 2; ++hh) {
-                        // negated W: the product accumulates U_bar - W X directly
-                        Frag<T> fw = ld_frag(sW + (32 * kbp + prow(hh, r16)) * LDK + 32 * kb + 8 * grp);
-                        fw = frag_neg(fw);
+                        Frag<T> fk = ld_frag(sKp + (32 * kbp + prow(hh, r16)) * LDK + 32 * kb + 8 * grp);
+                        fk = frag_neg(fk);
 #pragma unroll
-                        for (int n = 0; n < NTW; ++n) mma(Y[kbp][hh][n], fw, xf[n]);
+                        for (int n = 0; n < NTW; ++n) mma(Y[kbp][hh][n], fk, xf[n]);
                     }
-                __builtin_amdgcn_sched_barrier(0);
             }
+            Frag<T> Rf[2][NTW];
+#pragma unroll
+            for (int kbp = 0; kbp < 2; ++kbp)
+#pragma unroll
+                for (int n = 0; n < NTW; ++n) Rf[kbp][n] = pack_frag<T>(Y[kbp][0][n], Y[kbp][1][n]);
+            // Y = (T diag(beta)) R; T is lower triangular
+#pragma unroll
+            for (int kbo = 0; kbo < 2; ++kbo)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+                    for (int n = 0; n < NTW; ++n) Y[kbo][hh][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kbi = 0; kbi <= kbo; ++kbi) {
+                        const float* trow = sT + (32 * kbo + prow(hh, r16)) * LDF + 32 * kbi + 8 * grp;
+                        const float* brow = sBeta + 32 * kbi + 8 * grp;
+                        Frag<T> ft;
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) frag_set(ft, j, trow[j] * brow[j]);
+#pragma unroll
+                        for (int n = 0; n < NTW; ++n) mma(Y[kbo][hh][n], ft, Rf[kbi][n]);
+                    }
+                }
         }
         Frag<T> Yf[2][NTW];
 #pragma unroll
         for (int kbp = 0; kbp < 2; ++kbp)
 #pragma unroll
             for (int n = 0; n < NTW; ++n) Yf[kbp][n] = pack_frag<T>(Y[kbp][0][n], Y[kbp][1][n]);
-        __builtin_amdgcn_sched_barrier(0);
         // Z^T = X^T Q~^T + Y^T Aqk^T, 32 positions at a time: lane (r16, grp)
         // holds columns col0 + 16 n + 4 grp + i of position 16 pt + r16;
         // stored as o_local (S waves) or q_eff (P waves, segments >= 1)
-        // chunk bases are uniform; lanes add 32-bit offsets
-        T* const ochunk = o + (((size_t)b * Tlen + (size_t)c * C) * H + h) * DV;
-        T* const qchunk = qeff + ((size_t)chain * NT + c) * C * DK;
+        // chunk bases are uniform; lanes add 32-bit offsets.  o: rows past a
+        // ragged chunk's end fall outside the resource and are dropped.
+        const auto orsrc = buffer_rsrc(o + (((size_t)b * Tlen + (size_t)c * C) * H + h) * DV,
+                                       (unsigned)(nvalid * H * DV * sizeof(T)));
+        const auto qrsrc = buffer_rsrc(qeff + ((size_t)chain * NT + c) * C * DK, (unsigned)(C * DK * sizeof(T)));
         const unsigned ocol = (unsigned)(col0 + 4 * grp);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -647,7 +683,6 @@ __global__ __launch_bounds__(kSegThreads, 1) void seg_kernel(
 #pragma unroll
                     for (int n = 0; n < NTW; ++n) mma(Zt[n][u], xf[n], fq);
                 }
-                __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
@@ -660,24 +695,17 @@ __global__ __launch_bounds__(kSegThreads, 1) void seg_kernel(
             }
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                const int pos = 16 * (2 * half + u) + r16;
-                if (isS) {
-                    if (pos < nvalid) {
+                // every wave issues the same stores on every path (segment 0's
+                // effective queries are written too, and never read)
+                const unsigned pos = (unsigned)(16 * (2 * half + u) + r16);
+                const auto rs = isS ? orsrc : qrsrc;
+                const unsigned rowst = isS ? (unsigned)(H * DV) : (unsigned)DK;
 #pragma unroll
-                        for (int n = 0; n < NTW; ++n) {
-                            const float z4[4] = {Zt[n][u][0], Zt[n][u][1], Zt[n][u][2], Zt[n][u][3]};
-                            st4(ochunk + ((unsigned)pos * (unsigned)(H * DV) + ocol + 16 * n), z4);
-                        }
-                    }
-                } else if (r > 0) {
-#pragma unroll
-                    for (int n = 0; n < NTW; ++n) {
-                        const float z4[4] = {Zt[n][u][0], Zt[n][u][1], Zt[n][u][2], Zt[n][u][3]};
-                        st4(qchunk + ((unsigned)pos * DK + ocol + 16 * n), z4);
-                    }
+                for (int n = 0; n < NTW; ++n) {
+                    const float z4[4] = {Zt[n][u][0], Zt[n][u][1], Zt[n][u][2], Zt[n][u][3]};
+                    buf_st4(rs, (pos * rowst + ocol + 16 * n) * (unsigned)sizeof(T), (const T*)nullptr, z4);
                 }
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
         // X <- Diag(phi) X + Kbar^T Y
 #pragma unroll
@@ -697,11 +725,17 @@ __global__ __launch_bounds__(kSegThreads, 1) void seg_kernel(
                     for (int n = 0; n < NTW; ++n) mma(X[kb][hh][n], fk, Yf[kbp][n]);
                 }
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
         lds_barrier();   // LDS operands are rewritten by the next chunk
     }
 
+    if constexpr (KIND == KIND_KDA) {
+        if (flags) {
+            const unsigned long long b16 = __ballot(mxneg_seg >= 16.f);
+            const unsigned long long b126 = __ballot(mxneg_seg >= 126.f);
+            if ((tid & 63) == 0 && (b16 | b126)) atomicOr(flags, (b16 ? 1u : 0u) | (b126 ? 2u : 0u));
+        }
+    }
     // ---- segment end: [M | N] -------------------------------------------------
     float* xe = xend + ((size_t)chain * NS + r) * DK * (DK + DV) + (isS ? DK : 0) + col0 + r16;
 #pragma unroll
@@ -775,9 +809,14 @@ __global__ __launch_bounds__(kComposeThreads) void compose_kernel(const float* _
 
 // ---------------------------------------------------------------------------
 // correct_kernel: o[c] += q_eff[c] S_in[r] for the chunks c of segments
-// r >= 1.  One 256-thread workgroup per (chunk, chain) item; wave w owns the
-// value columns DV/4 * w ..; lanes hold 4 consecutive columns of one
-// position (O^T = S_in^T q_eff^T on MFMA).
+// r >= 1.  One 256-thread workgroup per (chain, segment r >= 1, group of
+// kCorrChunks chunks of it): S_in^T (I/O dtype, [DV][DK]) is staged in LDS
+// once, then each chunk's q_eff and o stream through registers, the next
+// chunk's loaded while the current one is multiplied.  Wave w owns the 16
+// positions 16 w ..; lanes hold 4 consecutive value columns of one position
+// (O^T = S_in^T q_eff^T on MFMA), so o is read and written 8 (bf16) or 16
+// (fp32) bytes per lane and tile.
+constexpr int kCorrChunks = 8;
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(kThreads) void correct_kernel(const T* __restrict__ qeff, const T* __restrict__ sinT,
                                                            T* __restrict__ o, int Tlen, int H, int NT, int L,
@@ -785,49 +824,65 @@ __global__ __launch_bounds__(kThreads) void correct_kernel(const T* __restrict__
 {
     constexpr int C = kChunk;
     constexpr int NKB = DK / 32;
-    constexpr int NTWc = DV / 64;          // 16-column tiles per wave
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int NCT = DV / 16;           // 16-column tiles
+    constexpr int LDS_ = DK + 8;           // padded row of S_in^T in LDS
+    __shared__ __attribute__((aligned(16))) T sS[DV * LDS_];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, grp = lane >> 4;
-    const int per = NT - L;                // corrected chunks per chain
+    const int groups = (L + kCorrChunks - 1) / kCorrChunks;
+    const int per = (NS - 1) * groups;
     const int chain = blockIdx.x / per;
-    const int c = L + blockIdx.x % per;
-    const int r = c / L;
+    const int rem = blockIdx.x % per;
+    const int r = 1 + rem / groups;
+    const int c0 = r * L + (rem % groups) * kCorrChunks;
+    const int c1 = min(min(c0 + kCorrChunks, (r + 1) * L), NT);
+    if (c0 >= c1) return;
     const int b = chain / H, h = chain % H;
-    const int nvalid = min(C, Tlen - c * C);
+    // S_in^T into LDS: 8 elements per thread and step
     const T* S = sinT + ((size_t)chain * NS + r) * DV * DK;
-    const T* Q = qeff + ((size_t)chain * NT + c) * C * DK;
-    f32x4 acc[NTWc][4];
-#pragma unroll
-    for (int n = 0; n < NTWc; ++n)
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt) acc[n][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-        Frag<T> fs[NTWc];
-#pragma unroll
-        for (int n = 0; n < NTWc; ++n)
-            fs[n] = ld_frag(S + (size_t)((DV / 4) * wave + 16 * n + r16) * DK + 32 * kb + 8 * grp);
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-            const Frag<T> fq = ld_frag(Q + (size_t)(16 * pt + r16) * DK + 32 * kb + 8 * grp);
-#pragma unroll
-            for (int n = 0; n < NTWc; ++n) mma(acc[n][pt], fs[n], fq);
-        }
+    for (int e = tid * 8; e < DV * DK; e += kThreads * 8) {
+        const int row = e / DK, col = e % DK;
+        st_frag(sS + row * LDS_ + col, ld_frag(S + e));
     }
-    T* orow = o + (((size_t)b * Tlen + (size_t)c * C) * H + h) * DV + (DV / 4) * wave + 4 * grp;
+    lds_barrier();
+    const int pos = 16 * wave + r16;
+    const unsigned ostr = (unsigned)(H * DV);
+    auto load_q = [&](Frag<T> (&fq)[NKB], int c) {
+        const T* Q = qeff + ((size_t)chain * NT + c) * C * DK + (size_t)pos * DK + 8 * grp;
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
-        const int pos = 16 * pt + r16;
-        if (pos < nvalid) {
+        for (int kb = 0; kb < NKB; ++kb) fq[kb] = ld_frag(Q + 32 * kb);
+    };
+    auto orsrc_of = [&](int c) {
+        return buffer_rsrc(o + (((size_t)b * Tlen + (size_t)c * C) * H + h) * DV,
+                           (unsigned)(min(C, Tlen - c * C) * H * DV * sizeof(T)));
+    };
+    Frag<T> fq[NKB];
+    load_q(fq, c0);
+    for (int c = c0; c < c1; ++c) {
+        Frag<T> cur[NKB];
 #pragma unroll
-            for (int n = 0; n < NTWc; ++n) {
-                T* p = orow + (size_t)pos * H * DV + 16 * n;
-                float cur[4];
-                ld4(p, cur);
-                const float z4[4] = {cur[0] + acc[n][pt][0], cur[1] + acc[n][pt][1], cur[2] + acc[n][pt][2],
-                                     cur[3] + acc[n][pt][3]};
-                st4(p, z4);
-            }
+        for (int kb = 0; kb < NKB; ++kb) cur[kb] = fq[kb];
+        load_q(fq, min(c + 1, c1 - 1));
+        const auto rs = orsrc_of(c);
+        const unsigned obase = ((unsigned)pos * ostr + 4u * grp) * (unsigned)sizeof(T);
+        // current o, read before the products (dropped rows read as zero)
+        Raw4<T> oc[NCT];
+#pragma unroll
+        for (int n = 0; n < NCT; ++n) oc[n] = buf_ld4(rs, obase + 16u * n * (unsigned)sizeof(T), (const T*)nullptr);
+        f32x4 acc[NCT];
+#pragma unroll
+        for (int n = 0; n < NCT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int n = 0; n < NCT; ++n)
+                mma(acc[n], ld_frag(sS + (16 * n + r16) * LDS_ + 32 * kb + 8 * grp), cur[kb]);
+#pragma unroll
+        for (int n = 0; n < NCT; ++n) {
+            const float z4[4] = {oc[n][0] + acc[n][0], oc[n][1] + acc[n][1], oc[n][2] + acc[n][2],
+                                 oc[n][3] + acc[n][3]};
+            buf_st4(rs, obase + 16u * n * (unsigned)sizeof(T), (const T*)nullptr, z4);
         }
     }
 }
