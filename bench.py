@@ -569,6 +569,9 @@ def main():
                     help="segment: the forward entry points' segment-parallel launches (the "
                          "benchmark line); records: the chunk-record path (chunk-parallel kernel, "
                          "then the sequential state pass) for comparison")
+    ap.add_argument("--chunk", type=int, choices=(64, 128), default=0,
+                    help="chunk size C (default: the workload's, 64).  C = 128 runs the record path "
+                         "with 64-token sub-chunks (the segment-parallel path is built for C = 64)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (3 times): the "
                          "reference for scaling the HBM byte counters of a profile")
@@ -613,6 +616,10 @@ def main():
     from delta_rule_rnn_amd.inputs import WORKLOADS, generate
 
     w = WORKLOADS[args.workload]
+    if args.chunk:
+        w = w.with_(C=args.chunk)
+    if w.C != 64:
+        args.path = "records"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     x = generate(w)

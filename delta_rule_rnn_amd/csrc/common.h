@@ -325,16 +325,18 @@ __device__ __forceinline__ int pw(int w, int r) { return 32 * (w >> 1) + prow(w 
 //
 // Every block is stored in MFMA fragment order for the state pass, so one
 // wave-wide load of 8 elements per lane reads a contiguous 64*8-element run
-// (lane l, element j; NKB = DK/32; pw() and prow() above):
-//   W, QT  [w 4][kb NKB][l 64][j 8]    = X[pw(w, l%16)][32kb + 8(l/16) + j]
-//   KBT    [w NKB][h 2][kb 2][l][j 8]  = Kbar[32kb + 8(l/16) + j][32w + prow(h, l%16)]
-//   AQK    [w 4][kb 2][l][j 8]         = Aqk[pw(w, l%16)][32kb + 8(l/16) + j]
-//   UT     [t DV/16][w 4][l][i 4]      = U[32(w/2) + 8(l/16) + 4(w%2) + i][16t + l%16]
+// (lane l, element j; NKB = DK/32; NW = C/16 position groups of 16; pw() and
+// prow() above, with pw(w, r) = 32(w/2) + prow(w%2, r) for any w < NW):
+//   W, QT  [w NW][kb NKB][l 64][j 8]     = X[pw(w, l%16)][32kb + 8(l/16) + j]
+//   KBT    [w NKB][h 2][kb C/32][l][j 8] = Kbar[32kb + 8(l/16) + j][32w + prow(h, l%16)]
+//   AQK    [w NW][kb C/32][l][j 8]       = Aqk[pw(w, l%16)][32kb + 8(l/16) + j]
+//   UT     [t DV/16][w NW][l][i 4]       = U[32(w/2) + 8(l/16) + 4(w%2) + i][16t + l%16]
 //   PHI    [DK] float
+// C is 64, or 128 for the sub-chunked records of 128-token chunks.
 // ---------------------------------------------------------------------------
-template <typename T, int DK, int DV>
+template <typename T, int DK, int DV, int CH = kChunk>
 struct Rec {
-    static constexpr int C = kChunk;
+    static constexpr int C = CH;
     static constexpr size_t W = 0;                       // C*DK
     static constexpr size_t QT = W + (size_t)C * DK;     // C*DK
     static constexpr size_t KBT = QT + (size_t)C * DK;   // DK*C

@@ -8,7 +8,7 @@ dr_status forward(int kind, const void* q, const void* k, const void* v, const f
                   const float* beta, const float* h0, void* o, float* hT, int B, int T, int H, int Dk,
                   int Dv, int C, int dtype, void* ws, size_t ws_bytes, unsigned* flags, void* stream,
                   const dr_prologue* pro) {
-    dr_status s = validate(kind, q, k, v, g, beta, B, T, H, Dk, Dv, C, dtype);
+    dr_status s = validate(kind, q, k, v, g, beta, B, T, H, Dk, Dv, C, dtype, true);
     if (s != DR_OK) return s;
     dr::Prologue pr;
     bool use_pro;
@@ -18,12 +18,12 @@ dr_status forward(int kind, const void* q, const void* k, const void* v, const f
     const size_t need = dr_workspace_bytes(kind, B, T, H, Dk, Dv, C, dtype);
     if (T > 0 && (ws == nullptr || ws_bytes < need)) return DR_ERR_WORKSPACE;
     if (T == 0 && hT == nullptr) return DR_OK;
-    Problem p = make_problem(kind, q, k, v, g, beta, o, B, T, H, Dk, dtype, ws, flags);
+    Problem p = make_problem(kind, q, k, v, g, beta, o, B, T, H, Dk, dtype, ws, flags, C);
     p.pro = pr;
     p.use_pro = use_pro;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (T == 0) return launch_inter(p, h0, hT, 0, 0, st);
-    if (seg_supported(Dk, dtype)) {
+    if (C == dr::kChunk && seg_supported(Dk, dtype)) {
         // segment-parallel path: local segment pass, entry-state
         // composition (and hT), then the output correction
         const SegLayout S = seg_layout(B, T, H, Dk, dtype);
@@ -235,7 +235,7 @@ extern "C" {
 
 size_t dr_backward_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, int C, int dtype) {
     if (kind < 0 || kind > 2 || B <= 0 || H <= 0 || T < 0) return 0;
-    if (dr_record_bytes(Dk, Dv, C, dtype) == 0) return 0;
+    if (C != dr::kChunk || dr_record_bytes(Dk, Dv, C, dtype) == 0) return 0;
     return bwd_layout(B, T, H, Dk, dtype).bytes;
 }
 
@@ -249,7 +249,7 @@ dr_status dr_backward(int kind, const void* q, const void* k, const void* v, con
 
 size_t dr_backward_prologue_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, int C, int dtype) {
     if (kind < 0 || kind > 2 || B <= 0 || H <= 0 || T < 0) return 0;
-    if (dr_record_bytes(Dk, Dv, C, dtype) == 0) return 0;
+    if (C != dr::kChunk || dr_record_bytes(Dk, Dv, C, dtype) == 0) return 0;
     return probwd_layout(kind, B, T, H, Dk, dtype, bwd_layout(B, T, H, Dk, dtype).bytes).bytes;
 }
 
@@ -265,7 +265,7 @@ dr_status dr_backward_prologue(int kind, const void* q, const void* k, const voi
 size_t dr_backward_varlen_workspace_bytes(int kind, int N, int T, int H, int Dk, int Dv, int C, int dtype,
                                           int with_prologue) {
     if (kind < 0 || kind > 2 || N < 1 || H <= 0 || T < 0) return 0;
-    if (dr_record_bytes(Dk, Dv, C, dtype) == 0) return 0;
+    if (C != dr::kChunk || dr_record_bytes(Dk, Dv, C, dtype) == 0) return 0;
     const VarlenLayout V = varlen_layout(N, T, H, Dk, dtype);
     const size_t core = (V.bytes - V.table) + bwd_layout_n((size_t)H * V.maxchunks, Dk, dtype).bytes;
     return with_prologue ? probwd_layout(kind, 1, T, H, Dk, dtype, core).bytes : core;
@@ -283,9 +283,10 @@ dr_status dr_backward_varlen(int kind, const void* q, const void* k, const void*
 }
 
 size_t dr_record_bytes(int Dk, int Dv, int C, int dtype) {
-    if (Dk != Dv || (Dk != 64 && Dk != 128) || C != dr::kChunk) return 0;
+    if (Dk != Dv || (Dk != 64 && Dk != 128)) return 0;
     if (dtype != DR_F32 && dtype != DR_BF16) return 0;
-    return record_bytes(Dk, dtype);
+    if (C != dr::kChunk && !(C == kChunk128 && chunk128_built(Dk, dtype))) return 0;
+    return record_bytes(Dk, dtype, C);
 }
 
 size_t dr_record_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, int C, int dtype) {
@@ -297,14 +298,14 @@ size_t dr_record_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, 
 
 size_t dr_segment_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, int C, int dtype) {
     const size_t rec = dr_record_workspace_bytes(kind, B, T, H, Dk, Dv, C, dtype);
-    if (rec == 0 || !seg_built(Dk, dtype)) return 0;
+    if (rec == 0 || C != dr::kChunk || !seg_built(Dk, dtype)) return 0;
     return T == 0 ? 0 : seg_layout(B, T, H, Dk, dtype).bytes;
 }
 
 size_t dr_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, int C, int dtype) {
     const size_t rec = dr_record_workspace_bytes(kind, B, T, H, Dk, Dv, C, dtype);
     if (rec == 0 || T == 0) return rec;
-    return seg_supported(Dk, dtype) ? seg_layout(B, T, H, Dk, dtype).bytes : rec;
+    return C == dr::kChunk && seg_supported(Dk, dtype) ? seg_layout(B, T, H, Dk, dtype).bytes : rec;
 }
 
 dr_status dr_forward_stage(int stage, int kind, const void* q, const void* k, const void* v, const float* g,
@@ -339,12 +340,12 @@ dr_status decay_la_fwd(const void* q, const void* k, const void* v, const float*
 dr_status dr_intra(int kind, const void* q, const void* k, const void* v, const float* g, const float* beta,
                    int B, int T, int H, int Dk, int Dv, int C, int dtype, void* workspace,
                    size_t workspace_bytes, unsigned* flags, void* stream) {
-    dr_status s = validate(kind, q, k, v, g, beta, B, T, H, Dk, Dv, C, dtype);
+    dr_status s = validate(kind, q, k, v, g, beta, B, T, H, Dk, Dv, C, dtype, true);
     if (s != DR_OK) return s;
     if (!aligned16(workspace)) return DR_ERR_INVALID_ARG;
     if (T > 0 && (!workspace || workspace_bytes < dr_record_workspace_bytes(kind, B, T, H, Dk, Dv, C, dtype)))
         return DR_ERR_WORKSPACE;
-    const Problem p = make_problem(kind, q, k, v, g, beta, nullptr, B, T, H, Dk, dtype, workspace, flags);
+    const Problem p = make_problem(kind, q, k, v, g, beta, nullptr, B, T, H, Dk, dtype, workspace, flags, C);
     return launch_intra(p, 0, p.NT, static_cast<hipStream_t>(stream));
 }
 
@@ -352,20 +353,20 @@ dr_status dr_inter(int kind, const float* h0, void* o, float* hT, int B, int T, 
                    int C, int dtype, const void* workspace, size_t workspace_bytes, void* stream) {
     if (kind < 0 || kind > 2 || B <= 0 || H <= 0 || T < 0) return DR_ERR_INVALID_ARG;
     if (dtype != DR_F32 && dtype != DR_BF16) return DR_ERR_INVALID_ARG;
-    if (Dk != Dv || (Dk != 64 && Dk != 128) || C != dr::kChunk) return DR_ERR_UNSUPPORTED;
+    if (Dk != Dv || (Dk != 64 && Dk != 128) || dr_record_bytes(Dk, Dv, C, dtype) == 0) return DR_ERR_UNSUPPORTED;
     if (T > 0 && !o) return DR_ERR_INVALID_ARG;
     if (!aligned16(o) || !aligned16(h0) || !aligned16(hT) || !aligned16(workspace)) return DR_ERR_INVALID_ARG;
     if (T > 0 && (!workspace || workspace_bytes < dr_record_workspace_bytes(kind, B, T, H, Dk, Dv, C, dtype)))
         return DR_ERR_WORKSPACE;
     if (T == 0 && hT == nullptr) return DR_OK;
     const Problem p = make_problem(kind, nullptr, nullptr, nullptr, nullptr, nullptr, o, B, T, H, Dk, dtype,
-                                   const_cast<void*>(workspace), nullptr);
+                                   const_cast<void*>(workspace), nullptr, C);
     return launch_inter(p, h0, hT, 0, p.NT, static_cast<hipStream_t>(stream));
 }
 
 size_t dr_workspace_bytes_varlen(int kind, int N, int T, int H, int Dk, int Dv, int C, int dtype) {
     if (kind < 0 || kind > 2 || N < 1 || H <= 0 || T < 0) return 0;
-    if (dr_record_bytes(Dk, Dv, C, dtype) == 0) return 0;
+    if (C != dr::kChunk || dr_record_bytes(Dk, Dv, C, dtype) == 0) return 0;
     return varlen_layout(N, T, H, Dk, dtype).bytes;
 }
 
@@ -437,7 +438,9 @@ const char* dr_status_string(int status) {
     switch (status) {
         case DR_OK: return "ok";
         case DR_ERR_INVALID_ARG: return "invalid argument";
-        case DR_ERR_UNSUPPORTED: return "unsupported size (Dk == Dv in {64, 128}, C == 64)";
+        case DR_ERR_UNSUPPORTED:
+            return "unsupported size (Dk == Dv in {64, 128}; C == 64, or C == 128 for the dense forward "
+                   "except fp32 at Dk = 128)";
         case DR_ERR_HIP: return "HIP launch failed";
         case DR_ERR_WORKSPACE: return "workspace missing or too small";
         case DR_ERR_SCRATCH_LIMIT:
@@ -447,7 +450,7 @@ const char* dr_status_string(int status) {
     }
 }
 
-int dr_abi_version(void) { return 6; }
+int dr_abi_version(void) { return 7; }
 
 }  // extern "C"
 

@@ -24,19 +24,33 @@ inline dr_status check_launch() {
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-inline size_t record_bytes(int D, int dtype) {
+// 128-token chunks (sub-chunked records) are built for the dense forward in
+// bf16 at both head sizes and in fp32 at D = 64 (an fp32 D = 128 sub-chunk
+// alone fills the LDS).
+constexpr int kChunk128 = 2 * dr::kChunk;
+inline bool chunk128_built(int D, int dtype) { return dtype == DR_BF16 || D == 64; }
+
+inline size_t record_bytes(int D, int dtype, int C = dr::kChunk) {
+    if (C == kChunk128) {
+        if (dtype == DR_BF16)
+            return D == 64 ? dr::Rec<bf16, 64, 64, kChunk128>::BYTES : dr::Rec<bf16, 128, 128, kChunk128>::BYTES;
+        return D == 64 ? dr::Rec<float, 64, 64, kChunk128>::BYTES : dr::Rec<float, 128, 128, kChunk128>::BYTES;
+    }
     if (dtype == DR_BF16) return D == 64 ? dr::Rec<bf16, 64, 64>::BYTES : dr::Rec<bf16, 128, 128>::BYTES;
     return D == 64 ? dr::Rec<float, 64, 64>::BYTES : dr::Rec<float, 128, 128>::BYTES;
 }
 
-// Shared validation for the full forward and the fused step entry points.
+// Shared validation for the full forward and the fused step entry points
+// (allow128: the caller runs the dense forward, which also takes C = 128).
 inline dr_status validate(int kind, const void* q, const void* k, const void* v, const float* g,
-                   const float* beta, int B, int T, int H, int Dk, int Dv, int C, int dtype) {
+                   const float* beta, int B, int T, int H, int Dk, int Dv, int C, int dtype,
+                   bool allow128 = false) {
     if (kind < 0 || kind > 2) return DR_ERR_INVALID_ARG;
     if (B <= 0 || H <= 0 || T < 0) return DR_ERR_INVALID_ARG;
     if (dtype != DR_F32 && dtype != DR_BF16) return DR_ERR_INVALID_ARG;
     if (Dk <= 0 || Dv <= 0 || C <= 0) return DR_ERR_INVALID_ARG;
-    if (Dk != Dv || (Dk != 64 && Dk != 128) || C != dr::kChunk) return DR_ERR_UNSUPPORTED;
+    if (Dk != Dv || (Dk != 64 && Dk != 128)) return DR_ERR_UNSUPPORTED;
+    if (C != dr::kChunk && !(allow128 && C == kChunk128 && chunk128_built(Dk, dtype))) return DR_ERR_UNSUPPORTED;
     if ((long long)B * T * H * Dk > (1LL << 40)) return DR_ERR_INVALID_ARG;
     if (T > 0 && (!q || !k || !v || !g)) return DR_ERR_INVALID_ARG;
     if (T > 0 && kind != DR_KIND_DECAY_LA && !beta) return DR_ERR_INVALID_ARG;
@@ -48,6 +62,7 @@ inline dr_status validate(int kind, const void* q, const void* k, const void* v,
 // One forward problem: the arguments every launch needs.
 struct Problem {
     int kind, dtype, D, B, T, H, NT;
+    int C = dr::kChunk;     // record chunk: 64, or 128 (sub-chunked)
     const void *q, *k, *v;
     const float *g, *beta;
     void* o;
@@ -127,10 +142,11 @@ inline int pick_pfd() {
 
 inline Problem make_problem(int kind, const void* q, const void* k, const void* v, const float* g,
                      const float* beta, void* o, int B, int T, int H, int D, int dtype, void* ws,
-                     unsigned* flags) {
+                     unsigned* flags, int C = dr::kChunk) {
     Problem p;
     p.kind = kind; p.dtype = dtype; p.D = D; p.B = B; p.T = T; p.H = H;
-    p.NT = ceil_div(T, dr::kChunk);
+    p.C = C;
+    p.NT = ceil_div(T, C);
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = kind == DR_KIND_DECAY_LA ? nullptr : beta;
     p.o = o; p.ws = static_cast<uint8_t*>(ws); p.flags = flags;
     return p;

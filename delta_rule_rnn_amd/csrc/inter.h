@@ -47,31 +47,42 @@ namespace dr {
 
 constexpr int kInterThreads = 512;   // 4 recurrence + 4 output waves
 
+// A workgroup of a C-token record chunk has NW = C/16 recurrence waves (16
+// positions each) and as many output waves.  Recurrence wave w owns the S
+// rows of its NH = 128/C 16-row groups g = NH*w + h (rows 32(g/2) +
+// prow(g%2, .)), each reduced over the C/32 position blocks of Kbar^T.
+template <int C2> struct InterShape {
+    static constexpr int NW = C2 / 16, NH = 128 / C2, KQ = C2 / 32;
+    static_assert(C2 == 64 || C2 == 128, "record chunk");
+};
+
 // Operands of one chunk for a recurrence wave.
-template <typename T, int DK, int NTN>
+template <typename T, int DK, int NTN, int C2 = kChunk>
 struct RecurOps {
     static constexpr int NKB = DK / 32;
-    Frag<T> w[NKB];        // W rows of this wave's positions
-    Frag<T> kb[2][2];      // Kbar^T rows (half, key block) of this wave's S rows
-    Raw4<T> u[NTN];        // U (or V) at this lane's 4 positions, per n-tile
-    float phi[2][4];       // phi at this lane's S rows (half, i)
+    using Sh = InterShape<C2>;
+    Frag<T> w[NKB];               // W rows of this wave's positions
+    Frag<T> kb[Sh::NH][Sh::KQ];   // Kbar^T rows (group, position block) of this wave's S rows
+    Raw4<T> u[NTN];               // U (or V) at this lane's 4 positions, per n-tile
+    float phi[Sh::NH][4];         // phi at this lane's S rows (group, i)
 };
 
 // Operands of one chunk for an output wave.
-template <typename T, int DK>
+template <typename T, int DK, int C2 = kChunk>
 struct OutOps {
     static constexpr int NKB = DK / 32;
-    Frag<T> qt[NKB];       // Q~ rows of this wave's positions
-    Frag<T> aqk[2];        // Aqk rows, key blocks 0..1
+    Frag<T> qt[NKB];                       // Q~ rows of this wave's positions
+    Frag<T> aqk[InterShape<C2>::KQ];       // Aqk rows, key blocks
 };
 
 // All record blocks are in fragment order: lane l's 8 (or 4) elements are
 // contiguous and a wave-wide load is one contiguous run.
-template <int KIND, typename T, int DK, int DV, int NTN>
-__device__ __forceinline__ void load_recur(RecurOps<T, DK, NTN>& op, const uint8_t* recb, int wave,
+template <int KIND, typename T, int DK, int DV, int NTN, int C2 = kChunk>
+__device__ __forceinline__ void load_recur(RecurOps<T, DK, NTN, C2>& op, const uint8_t* recb, int wave,
                                            int lane, int dv0)
 {
-    using R = Rec<T, DK, DV>;
+    using R = Rec<T, DK, DV, C2>;
+    using Sh = InterShape<C2>;
     constexpr int NKB = DK / 32;
     const T* base = reinterpret_cast<const T*>(recb);
     if constexpr (KIND != KIND_LA) {
@@ -79,35 +90,37 @@ __device__ __forceinline__ void load_recur(RecurOps<T, DK, NTN>& op, const uint8
         for (int kb = 0; kb < NKB; ++kb)
             op.w[kb] = ld_frag(base + R::W + ((size_t)(wave * NKB + kb) * 64 + lane) * 8);
     }
-    if (NKB >= 4 || wave < NKB) {
+    if (Sh::NH * wave < 2 * NKB) {
         const float* phi = reinterpret_cast<const float*>(recb + R::PHI_BYTE);
         const int grp = lane >> 4;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
+        for (int hh = 0; hh < Sh::NH; ++hh) {
+            const int g = Sh::NH * wave + hh;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                op.kb[half][kb] = ld_frag(base + R::KBT + ((size_t)((wave * 2 + half) * 2 + kb) * 64 + lane) * 8);
-            ld4(phi + 32 * wave + 8 * grp + 4 * half, op.phi[half]);
+            for (int kb = 0; kb < Sh::KQ; ++kb)
+                op.kb[hh][kb] = ld_frag(base + R::KBT + ((size_t)(g * Sh::KQ + kb) * 64 + lane) * 8);
+            ld4(phi + 32 * (g >> 1) + 8 * grp + 4 * (g & 1), op.phi[hh]);
         }
     }
 #pragma unroll
     for (int n = 0; n < NTN; ++n)
-        op.u[n].load(base + R::UT + ((size_t)((dv0 / 16 + n) * 4 + wave) * 64 + lane) * 4);
+        op.u[n].load(base + R::UT + ((size_t)((dv0 / 16 + n) * Sh::NW + wave) * 64 + lane) * 4);
 }
 
-template <typename T, int DK, int DV>
-__device__ __forceinline__ void load_out(OutOps<T, DK>& op, const uint8_t* recb, int wave, int lane)
+template <typename T, int DK, int DV, int C2 = kChunk>
+__device__ __forceinline__ void load_out(OutOps<T, DK, C2>& op, const uint8_t* recb, int wave, int lane)
 {
-    using R = Rec<T, DK, DV>;
+    using R = Rec<T, DK, DV, C2>;
+    constexpr int KQ = InterShape<C2>::KQ;
     constexpr int NKB = DK / 32;
     const T* base = reinterpret_cast<const T*>(recb);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
         op.qt[kb] = ld_frag(base + R::QT + ((size_t)(wave * NKB + kb) * 64 + lane) * 8);
-    // both key blocks: the record holds zeros above the diagonal, so the
-    // block past this wave's positions contributes nothing
+    // every key block: the record holds zeros above the diagonal, so the
+    // blocks past this wave's positions contribute nothing
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) op.aqk[kb] = ld_frag(base + R::AQK + ((size_t)(wave * 2 + kb) * 64 + lane) * 8);
+    for (int kb = 0; kb < KQ; ++kb) op.aqk[kb] = ld_frag(base + R::AQK + ((size_t)(wave * KQ + kb) * 64 + lane) * 8);
 }
 
 // Asynchronous copy global -> LDS of BYTES bytes per lane from the lane's own
@@ -163,8 +176,8 @@ __device__ __forceinline__ void l2_prefetch_wave(const uint8_t* chain_rec, int n
 // 128-byte line into a scratch LDS word, so the lines are in L2 by the time
 // the compute waves load them.  The NV workgroups of a chain share the
 // chain's L2 (same XCD) and split the lines between them.
-template <int PFD>
-constexpr int inter_threads() { return PFD > 0 ? kInterThreads + 64 : kInterThreads; }
+template <int PFD, int C2 = kChunk>
+constexpr int inter_threads() { return 2 * 64 * InterShape<C2>::NW + (PFD > 0 ? 64 : 0); }
 
 // VARLEN: chains are (sequence, head) of packed sequences; seqinfo[i] =
 // {first record slot, chunks, first token, tokens} of sequence i (written by
@@ -175,8 +188,12 @@ constexpr int inter_threads() { return PFD > 0 ? kInterThreads + 64 : kInterThre
 // (fp32 [C][DV] at vnew + r*C*DV), r the chunk's record index; the output
 // waves only keep the barriers.  Rows of a ragged last chunk past the end
 // get Vnew = 0 (their record rows are zero).
-template <int KIND, typename T, int DK, int DV, int NTN, int PFD, bool VARLEN, bool STATES = false>
-__global__ __launch_bounds__(inter_threads<PFD>()) void inter_kernel(const uint8_t* __restrict__ ws,
+//
+// C2 = 128 (sub-chunked 128-token records): 8 recurrence and 8 output waves,
+// one 16-row group of S per recurrence wave; dense layout, no prefetch wave.
+template <int KIND, typename T, int DK, int DV, int NTN, int PFD, bool VARLEN, bool STATES = false,
+          int C2 = kChunk>
+__global__ __launch_bounds__((inter_threads<PFD, C2>())) void inter_kernel(const uint8_t* __restrict__ ws,
                                                               const float* __restrict__ h0,
                                                               T* __restrict__ o, float* __restrict__ hT,
                                                               int Tlen, int H, int NT, int c0,
@@ -186,25 +203,28 @@ __global__ __launch_bounds__(inter_threads<PFD>()) void inter_kernel(const uint8
                                                               float* __restrict__ states = nullptr,
                                                               float* __restrict__ vnew = nullptr)
 {
-    using R = Rec<T, DK, DV>;
-    constexpr int C = kChunk;
+    using R = Rec<T, DK, DV, C2>;
+    using Sh = InterShape<C2>;
+    constexpr int C = C2;
+    constexpr int NW = Sh::NW, NH = Sh::NH, KQ = Sh::KQ;
     constexpr int DVS = 16 * NTN;
     constexpr int NV = DV / DVS;
     constexpr int NKB = DK / 32;
     constexpr bool DELTA = KIND != KIND_LA;
     static_assert(DV % DVS == 0, "value split");
+    static_assert(C2 == kChunk || (PFD == 0 && !VARLEN && !STATES), "128-token records: dense forward only");
 
     // B-fragment exchange buffers: [block][n-tile][lane][8 slots]
     __shared__ __attribute__((aligned(16))) T sS[NKB][NTN][64][8];
-    __shared__ __attribute__((aligned(16))) T sV[2][NTN][64][8];
+    __shared__ __attribute__((aligned(16))) T sV[KQ][NTN][64][8];
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const bool recur = tid < 256;               // waves 0..3
-    const int wave = (tid >> 6) & 3;            // position group of either role
+    const bool recur = tid < 64 * NW;            // waves 0..NW-1
+    const int wave = (tid >> 6) & (NW - 1);      // position group of either role
     __shared__ __attribute__((aligned(16))) uint8_t sink[PFD > 0 ? 256 : 16];
     const int r16 = lane & 15, grp = lane >> 4;
     const int kbP = wave >> 1, halfP = wave & 1;
-    const bool ownS = recur && (NKB >= 4 || wave < NKB);   // Dk = 128: every recurrence wave
+    const bool ownS = recur && NH * wave < 2 * NKB;   // Dk = 128: every recurrence wave
 
     const int G = gridDim.x, bid = blockIdx.x;
     const int logical = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
@@ -242,31 +262,36 @@ __global__ __launch_bounds__(inter_threads<PFD>()) void inter_kernel(const uint8
 #pragma unroll
             for (int n = 0; n < NTN; ++n) fS[kb][n] = ld_frag(&sS[kb][n][lane][0]);
     };
-    auto fV_read = [&](Frag<T> (&fV)[2][NTN]) {
+    auto fV_read = [&](Frag<T> (&fV)[KQ][NTN]) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KQ; ++kb)
 #pragma unroll
             for (int n = 0; n < NTN; ++n) fV[kb][n] = ld_frag(&sV[kb][n][lane][0]);
     };
 
     if constexpr (PFD > 0) {
-        if (tid >= kInterThreads) {
+        if (tid >= 2 * 64 * NW) {
             l2_prefetch_wave<T, DK, DV, NV, PFD>(chain_rec, nseg, slice, lane, sink);
             return;
         }
     }
     if (recur) {
         // ---- recurrence waves ---------------------------------------------
-        f32x4 S[2][NTN];
+        // S rows of group g = NH*wave + half: 32(g/2) + 8(l/16) + 4(g%2) + i
+        auto srow = [&](int half, int i) {
+            const int g = NH * wave + half;
+            return 32 * (g >> 1) + 8 * grp + 4 * (g & 1) + i;
+        };
+        f32x4 S[NH][NTN];
 #pragma unroll
-        for (int half = 0; half < 2; ++half)
+        for (int half = 0; half < NH; ++half)
 #pragma unroll
             for (int n = 0; n < NTN; ++n) {
                 f32x4 s = {0.f, 0.f, 0.f, 0.f};
                 if (ownS && h0 != nullptr) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int dk = 32 * wave + 8 * grp + 4 * half + i;
+                        const int dk = srow(half, i);
                         s[i] = h0[(((size_t)b * H + h) * DK + dk) * DV + dv0 + 16 * n + r16];
                     }
                 }
@@ -277,18 +302,19 @@ __global__ __launch_bounds__(inter_threads<PFD>()) void inter_kernel(const uint8
 #pragma unroll
                 for (int n = 0; n < NTN; ++n)
 #pragma unroll
-                    for (int half = 0; half < 2; ++half) {
+                    for (int half = 0; half < NH; ++half) {
+                        const int g = NH * wave + half;
                         float tmp[4] = {S[half][n][0], S[half][n][1], S[half][n][2], S[half][n][3]};
-                        st4(&sS[wave][n][lane][4 * half], tmp);
+                        st4(&sS[g >> 1][n][lane][4 * (g & 1)], tmp);
                     }
             }
         };
         publish_state();
         lds_barrier();
 
-        using Ops = RecurOps<T, DK, NTN>;
+        using Ops = RecurOps<T, DK, NTN, C2>;
         auto load = [&](Ops& op, int c) {
-            load_recur<KIND, T, DK, DV, NTN>(op, chain_rec + (size_t)c * R::BYTES, wave, lane, dv0);
+            load_recur<KIND, T, DK, DV, NTN, C2>(op, chain_rec + (size_t)c * R::BYTES, wave, lane, dv0);
         };
         auto step = [&](int c, const Ops& cur, auto) {
             if constexpr (STATES) {
@@ -296,12 +322,12 @@ __global__ __launch_bounds__(inter_threads<PFD>()) void inter_kernel(const uint8
                 if (ownS) {
                     float* sc = states + (rec0 + c) * (size_t)DK * DV + dv0 + r16;
 #pragma unroll
-                    for (int half = 0; half < 2; ++half)
+                    for (int half = 0; half < NH; ++half)
 #pragma unroll
                         for (int n = 0; n < NTN; ++n)
 #pragma unroll
                             for (int i = 0; i < 4; ++i)
-                                sc[(size_t)(32 * wave + 8 * grp + 4 * half + i) * DV + 16 * n] = S[half][n][i];
+                                sc[(size_t)srow(half, i) * DV + 16 * n] = S[half][n][i];
                 }
             }
             // phase A: Vnew at this lane's 4 positions
@@ -332,17 +358,17 @@ __global__ __launch_bounds__(inter_threads<PFD>()) void inter_kernel(const uint8
             }
             lds_barrier();
             // phase B: state update, decay first, then accumulate
-            Frag<T> fV[2][NTN];
+            Frag<T> fV[KQ][NTN];
             fV_read(fV);
             if (ownS) {
 #pragma unroll
-                for (int half = 0; half < 2; ++half)
+                for (int half = 0; half < NH; ++half)
 #pragma unroll
                     for (int n = 0; n < NTN; ++n) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i) S[half][n][i] *= cur.phi[half][i];
 #pragma unroll
-                        for (int kb = 0; kb < 2; ++kb) mma(S[half][n], cur.kb[half][kb], fV[kb][n]);
+                        for (int kb = 0; kb < KQ; ++kb) mma(S[half][n], cur.kb[half][kb], fV[kb][n]);
                     }
             }
             publish_state();
@@ -353,12 +379,12 @@ __global__ __launch_bounds__(inter_threads<PFD>()) void inter_kernel(const uint8
         // ---- final state ---------------------------------------------------
         if (ownS && hT != nullptr) {
 #pragma unroll
-            for (int half = 0; half < 2; ++half)
+            for (int half = 0; half < NH; ++half)
 #pragma unroll
                 for (int n = 0; n < NTN; ++n)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int dk = 32 * wave + 8 * grp + 4 * half + i;
+                        const int dk = srow(half, i);
                         hT[(((size_t)b * H + h) * DK + dk) * DV + dv0 + 16 * n + r16] = S[half][n][i];
                     }
         }
@@ -378,9 +404,9 @@ __global__ __launch_bounds__(inter_threads<PFD>()) void inter_kernel(const uint8
         const size_t ostride = (size_t)H * DV;
         T* const orow = o + ((tok0 + pos) * H + h) * DV + dv0 + 4 * grp;
 
-        using Ops = OutOps<T, DK>;
+        using Ops = OutOps<T, DK, C2>;
         auto load = [&](Ops& op, int c) {
-            load_out<T, DK, DV>(op, chain_rec + (size_t)c * R::BYTES, wave, lane);
+            load_out<T, DK, DV, C2>(op, chain_rec + (size_t)c * R::BYTES, wave, lane);
         };
         auto step = [&](int c, const Ops& cur, auto guard_tag) {
             constexpr bool GUARD = decltype(guard_tag)::value;
@@ -398,10 +424,10 @@ __global__ __launch_bounds__(inter_threads<PFD>()) void inter_kernel(const uint8
             }
             lds_barrier();
             // phase B: intra-chunk term (Aqk is zero past the diagonal), store
-            Frag<T> fV[2][NTN];
+            Frag<T> fV[KQ][NTN];
             fV_read(fV);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < KQ; ++kb)
 #pragma unroll
                 for (int n = 0; n < NTN; ++n) mma(Ot[n], fV[kb][n], cur.aqk[kb]);
             if (!GUARD || c * C + pos < tlim) {

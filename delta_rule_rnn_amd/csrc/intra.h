@@ -111,7 +111,7 @@ __device__ __forceinline__ void intra_load(IntraIn<KIND, T, DK, DV>& in, const T
     using VG = typename In::VG;
     constexpr int C = kChunk;
     constexpr int NCG = In::Cfg::NCG, PL = In::Cfg::PL, CPT = In::Cfg::CPT;
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x & (kThreads - 1), lane = tid & 63;
     const int last = nvalid - 1;
     const int ch0 = CPT * (tid % NCG), p0 = (tid / NCG) * PL;
     // gates first, then k and q (step a1 needs them first), v last
@@ -137,14 +137,24 @@ __device__ __forceinline__ void intra_load(IntraIn<KIND, T, DK, DV>& in, const T
 // registers (nvalid of its C rows are tokens); writes the chunk's record at
 // recb.  With PRO, the input prologue (common.h) is applied to the loaded
 // q, k, beta and scalar gates first.
-template <int KIND, typename T, int DK, int DV, bool PRO>
-__device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, uint8_t* smem,
+//
+// C2 = 128 (sub-chunked 128-token chunks, [KDA] 2.3): a 512-thread workgroup
+// runs this body once per 64-row sub-chunk, threads 256*s .. 256*s+255 on
+// sub-chunk s with the LDS regions at smem + s*Cfg::BYTES.  Each sub-chunk
+// re-bases gamma at its own start, so K- never exceeds 2^(max -gamma) over
+// 64 positions; the halves then exchange their gate totals and assemble the
+// 128-row record (intra_merge below).
+template <int KIND, typename T, int DK, int DV, bool PRO, int C2 = kChunk>
+__device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, uint8_t* smem_all,
                                             unsigned* __restrict__ flags,
                                             uint8_t* __restrict__ recb, int nvalid, const ProHead& ph)
 {
     using Cfg = IntraCfg<KIND, T, DK, DV>;
-    using R = Rec<T, DK, DV>;
+    using R = Rec<T, DK, DV, C2>;
     constexpr int C = kChunk;
+    constexpr bool SUB = C2 == 2 * kChunk;
+    static_assert(C2 == kChunk || SUB, "record chunk");
+    constexpr int KQ = C2 / 32, NW = C2 / 16;   // key blocks, position groups of the record
     constexpr bool DELTA = KIND != KIND_LA;
     constexpr bool PERCH = KIND == KIND_KDA;
     constexpr int LDK = Cfg::LDK, LDF = Cfg::LDF, LDV = Cfg::LDV;
@@ -152,6 +162,13 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
     using In = IntraIn<KIND, T, DK, DV>;
     using VT = typename In::VT;
     using VG = typename In::VG;
+
+    // sub-chunk of this thread (0 unless SUB) and its LDS regions; sX: the
+    // halves' gate totals (log2), [2][DK] floats after both regions
+    const int half = SUB ? (int)(threadIdx.x >> 8) : 0;
+    uint8_t* smem = smem_all + (SUB ? half * Cfg::BYTES : 0);
+    float* sX = reinterpret_cast<float*>(smem_all + 2 * Cfg::BYTES);
+    (void)sX;
 
     T* sKp = reinterpret_cast<T*>(smem + Cfg::R_KP);
     T* sKm = reinterpret_cast<T*>(smem + Cfg::R_KM);
@@ -164,7 +181,7 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
     float* sGam = reinterpret_cast<float*>(smem + Cfg::R_GAM);
     float* sTot = reinterpret_cast<float*>(smem + Cfg::R_TOT);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x & (kThreads - 1), lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, grp = lane >> 4;
     T* rW = reinterpret_cast<T*>(recb) + R::W;
     T* rQ = reinterpret_cast<T*>(recb) + R::QT;
@@ -276,11 +293,33 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
 #pragma unroll
         for (int j = 0; j < CPT; ++j) glast[j] = sGam[C - 1];
     }
-
-    {
-        float phi[CPT];
+    // SUB: the other sub-chunk's gate totals
+    float gother[CPT];
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) phi[j] = __builtin_amdgcn_exp2f(glast[j]);
+    for (int j = 0; j < CPT; ++j) gother[j] = 0.f;
+    if constexpr (SUB) {
+        if (PERCH ? qg == 0 : tid == 0) {
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) sX[half * DK + ch0 + j] = glast[j];
+        }
+        lds_barrier();
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) gother[j] = sX[(1 - half) * DK + (PERCH ? ch0 + j : 0)];
+    }
+
+    // Kbar of the merge (SUB, first sub-chunk): relative to the sub-chunk's
+    // end, natural layout (this thread's CPT channels x PL positions)
+    T kbl[SUB ? CPT : 1][SUB ? PL : 1];
+    {
+        // phi and Kbar of the record are relative to the record chunk's end
+        // (for the first sub-chunk of a 128-token chunk, the totals of both)
+        float phi[CPT], phl[CPT];
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            phl[j] = __builtin_amdgcn_exp2f(glast[j]);
+            phi[j] = (SUB && half == 0) ? __builtin_amdgcn_exp2f(glast[j] + gother[j]) : phl[j];
+        }
+        (void)phl;
         float kb[CPT][PL];
         float mxneg = 0.f;
 #pragma unroll
@@ -299,6 +338,7 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
                     qp[j] = from_f<T>(qq * e);
                     // Kbar = k 2^(gamma_last - gamma) = (k 2^-gamma) 2^gamma_last
                     kb[j][i] = kk * (ei * phi[j]);
+                    if constexpr (SUB) kbl[j][i] = from_f<T>(kk * (ei * phl[j]));
                 }
                 *reinterpret_cast<VT*>(sKp + p * LDK + ch0) = kp;
                 *reinterpret_cast<VT*>(sKm + p * LDK + ch0) = km;
@@ -315,8 +355,12 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
                 *reinterpret_cast<VT*>(sKp + p * LDK + ch0) = kn;
                 *reinterpret_cast<VT*>(sQp + p * LDK + ch0) = qn;
                 const float r = __builtin_amdgcn_exp2f(glast[0] - gam[i][0]) * nk[i];   // <= 1 (times nk)
+                const float rc = (SUB && half == 0) ? r * __builtin_amdgcn_exp2f(gother[0]) : r;
 #pragma unroll
-                for (int j = 0; j < CPT; ++j) kb[j][i] = (float)kv[i][j] * r;
+                for (int j = 0; j < CPT; ++j) {
+                    kb[j][i] = (float)kv[i][j] * rc;
+                    if constexpr (SUB) kbl[j][i] = from_f<T>((float)kv[i][j] * r);
+                }
             }
         }
         // Kbar in fragment order: channel ch is row prow(h, r) of key block
@@ -331,10 +375,11 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
                 Frag<T> f;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) frag_set(f, j, kb[cc][i0 + j]);
-                st_frag_stream(rKb + ((size_t)(((wk * 2 + hh) * 2 + (p >> 5)) * 64) + rr + 16 * ((p & 31) >> 3)) * 8, f);
+                st_frag_stream(rKb + ((size_t)(((wk * 2 + hh) * KQ + (p >> 5) + 2 * half) * 64) + rr +
+                                      16 * ((p & 31) >> 3)) * 8, f);
             }
         }
-        if (qg == 0) {
+        if (qg == 0 && half == 0) {
             VG ph;
 #pragma unroll
             for (int j = 0; j < CPT; ++j) ph[j] = phi[j];
@@ -360,7 +405,8 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
                 for (int i = 0; i < PL; i += 4) {
                     const int p = p0 + i;
                     const int wv = 2 * (p >> 5) + ((p >> 2) & 1);
-                    st4_stream(rU + ((size_t)(((ch >> 4) * 4 + wv) * 64) + (ch & 15) + 16 * ((p & 31) >> 3)) * 4, &vt[i]);
+                    st4_stream(rU + ((size_t)(((ch >> 4) * NW + wv + 4 * half) * 64) + (ch & 15) +
+                                     16 * ((p & 31) >> 3)) * 4, &vt[i]);
                 }
             }
         }
@@ -375,7 +421,9 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
         // items: NA tiles of A, then the 6 nonzero 32x32 blocks (w, kb) of Aqk,
         // kb <= w/2, each computed transposed (keys x queries) with rows and
         // columns permuted so that the accumulators are fragment-ordered
-        for (int idx = wave; idx < NA + 6; idx += 4) {
+        // (SUB: then 4 of the 8 blocks of Aqk10, below)
+        constexpr int NX = SUB ? 4 : 0;
+        for (int idx = wave; idx < NA + 6 + NX; idx += 4) {
             if (idx < NA) {
                 int ti, tj;
                 lower_tile(idx, ti, tj);
@@ -394,7 +442,7 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
                     if constexpr (!PERCH) ratio = (col < row) ? __builtin_amdgcn_exp2f(sGam[row] - sGam[col]) : 0.f;
                     sA[row * LDF + col] = (col < row) ? sBeta[row] * ratio * acc[i] : 0.f;
                 }
-            } else {
+            } else if (idx < NA + 6) {
                 const int bI = idx - NA;   // (w, kb): (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
                 const int w = bI < 2 ? bI : 2 + ((bI - 2) >> 1);
                 const int kbk = bI < 2 ? 0 : ((bI - 2) & 1);
@@ -422,15 +470,61 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
                         }
                         frag_set(out, 4 * hh + i, val);
                     }
-                st_frag_stream(rAqk + ((size_t)(w * 2 + kbk) * 64 + lane) * 8, out);
+                st_frag_stream(rAqk + ((size_t)((w + 4 * half) * KQ + kbk + 2 * half) * 64 + lane) * 8, out);
+            } else {
+                // SUB: block (w1, kbk) of Aqk10 = Q~1 K-0^T, queries of the
+                // second sub-chunk against keys of the first.  With gamma
+                // based at the chunk start, Q~1 = (its sub-chunk's Q~) * phi0
+                // <= 1 and K-0 stays within the first sub-chunk's range.
+                const int bx = 4 * half + (idx - NA - 6);
+                const int w1 = bx >> 1, kbk = bx & 1;
+                const T* q1 = reinterpret_cast<const T*>(smem_all + Cfg::BYTES + Cfg::R_QP);
+                const T* k0 = reinterpret_cast<const T*>(smem_all + (PERCH ? Cfg::R_KM : Cfg::R_KP));
+                const float* gam0 = reinterpret_cast<const float*>(smem_all + Cfg::R_GAM);
+                const float* gam1 = reinterpret_cast<const float*>(smem_all + Cfg::BYTES + Cfg::R_GAM);
+                const int query = pw(w1, r16);
+                f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+                for (int kd = 0; kd < NKB; ++kd) {
+                    Frag<T> fq = ld_frag(q1 + query * LDK + 32 * kd + 8 * grp);
+                    if constexpr (PERCH) {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            frag_set(fq, j, frag_get(fq, j) * __builtin_amdgcn_exp2f(sX[32 * kd + 8 * grp + j]));
+                    }
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const Frag<T> fk = ld_frag(k0 + (32 * kbk + prow(hh, r16)) * LDK + 32 * kd + 8 * grp);
+                        mma(acc[hh], fk, fq);   // [key][query]
+                    }
+                }
+                Frag<T> out;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int key = 32 * kbk + 8 * grp + 4 * hh + i;
+                        float val = acc[hh][i];
+                        if constexpr (!PERCH) val *= __builtin_amdgcn_exp2f(gam1[query] + sX[0] - gam0[key]);
+                        frag_set(out, 4 * hh + i, val);
+                    }
+                st_frag_stream(rAqk + ((size_t)((4 + w1) * KQ + kbk) * 64 + lane) * 8, out);
             }
         }
         // the two blocks above the diagonal (w = 0, 1; kb = 1) are zero
-        if (tid < 128) {
+        // (SUB: and, for the first sub-chunk's rows, both blocks of the second
+        // sub-chunk's keys)
+        {
             Frag<T> z;
 #pragma unroll
             for (int j = 0; j < 8; ++j) frag_set(z, j, 0.f);
-            st_frag_stream(rAqk + ((size_t)((tid >> 6) * 2 + 1) * 64 + (tid & 63)) * 8, z);
+            if (tid < 128)
+                st_frag_stream(rAqk + ((size_t)(((tid >> 6) + 4 * half) * KQ + 1 + 2 * half) * 64 + (tid & 63)) * 8, z);
+            if (SUB && half == 0) {
+#pragma unroll
+                for (int kz = 2; kz < 4; ++kz)
+                    st_frag_stream(rAqk + ((size_t)((tid >> 6) * KQ + kz) * 64 + (tid & 63)) * 8, z);
+            }
         }
         // Q~ in fragment order, from the LDS copy (scalar gates scale it here)
         for (int e = tid; e < 4 * NKB * 64; e += kThreads) {
@@ -438,11 +532,16 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
             const int row = pw(w, l & 15);
             Frag<T> f = ld_frag(sQp + row * LDK + 32 * kq + 8 * (l >> 4));
             if constexpr (!PERCH) {
-                const float sc = __builtin_amdgcn_exp2f(sGam[row]);
+                // (the second sub-chunk: gamma re-based to the chunk start)
+                const float sc = __builtin_amdgcn_exp2f(sGam[row] + (half ? sX[0] : 0.f));
 #pragma unroll
                 for (int j = 0; j < 8; ++j) frag_set(f, j, frag_get(f, j) * sc);
+            } else if (SUB && half == 1) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    frag_set(f, j, frag_get(f, j) * __builtin_amdgcn_exp2f(sX[32 * kq + 8 * (l >> 4) + j]));
             }
-            st_frag_stream(rQ + (size_t)e * 8, f);
+            st_frag_stream(rQ + ((size_t)e + (size_t)half * 4 * NKB * 64) * 8, f);
         }
     }
     if constexpr (!DELTA) return;
@@ -499,7 +598,7 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
 
     // ---- P4: [W | U] = T diag(beta) [K+ | V] --------------------------------
     {
-        constexpr int NTW = DK / 16, NTN = (DK + DV) / 16, PER = NTN / 4;
+        constexpr int NTW = DK / 16, NTN = (DK + DV) / 16, PER = NTN / 4, NKB = DK / 32;
         static_assert(NTN % 4 == 0 && (NTW % PER) == 0, "n-tile split");
         const int nt0 = wave * PER;
         const bool isW = nt0 < NTW;
@@ -543,56 +642,178 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
                 for (int n = 0; n < PER; ++n) mma(acc[mt][n], fa, fb[n][kb]);
             }
         }
-        if (isW) {
-            if constexpr (sizeof(T) == 2) {
-                // bf16: stage W in LDS (the A region is free now) so the global
-                // stores below are 16-byte row segments
+        // bf16: W is staged in LDS (the A region is free now) so the global
+        // stores are 16-byte row segments
+        auto stage_w = [&]() {
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
+            for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                    for (int n = 0; n < PER; ++n)
+                for (int n = 0; n < PER; ++n)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            sW[(16 * mt + 4 * grp + i) * LDK + 16 * (nt0 + n) + r16] = from_f<T>(acc[mt][n][i]);
-            } else {
-                // fp32: 4-byte elements, stored straight from the accumulators
-                // into their fragment-order slots.  (Staging these through LDS
-                // hit a miscompile in this toolchain: two of the four row stores
-                // were merged into one ds_write2_b32 whose first offset was
-                // encoded wrong at Dk = 128.)
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                    for (int n = 0; n < PER; ++n)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int row = 16 * mt + 4 * grp + i, col = 16 * (nt0 + n) + r16;
-                            const int qq = row & 31;
-                            const int wr = 2 * (row >> 5) + ((qq >> 2) & 1), rr = 4 * (qq >> 3) + (qq & 3);
-                            const size_t e = ((size_t)(wr * (DK / 32) + (col >> 5)) * 64 + rr + 16 * ((col & 31) >> 3)) * 8 + (col & 7);
-                            rW[e] = from_f<T>(acc[mt][n][i]);
-                        }
+                    for (int i = 0; i < 4; ++i)
+                        sW[(16 * mt + 4 * grp + i) * LDK + 16 * (nt0 + n) + r16] = from_f<T>(acc[mt][n][i]);
+        };
+        auto copy_w = [&]() {
+            // W in fragment order from the staged natural tile
+            for (int e = tid; e < 4 * NKB * 64; e += kThreads) {
+                const int l = e & 63, kq = (e >> 6) % NKB, w = (e >> 6) / NKB;
+                st_frag_stream(rW + ((size_t)e + (size_t)half * 4 * NKB * 64) * 8,
+                               ld_frag(sW + pw(w, l & 15) * LDK + 32 * kq + 8 * (l >> 4)));
             }
-        } else {
-            // U: m-tile mt holds the rows of state-pass wave mt, so each lane's 4
-            // values are one fragment-order slot group
+        };
+        // fp32: 4-byte elements, stored straight from the accumulators into
+        // their fragment-order slots.  (Staging these through LDS hit a
+        // miscompile in this toolchain: two of the four row stores were merged
+        // into one ds_write2_b32 whose first offset was encoded wrong at
+        // Dk = 128.)
+        auto direct_w = [&]() {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int n = 0; n < PER; ++n)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = 16 * mt + 4 * grp + i, col = 16 * (nt0 + n) + r16;
+                        const int qq = row & 31;
+                        const int wr = 2 * (row >> 5) + ((qq >> 2) & 1) + 4 * half, rr = 4 * (qq >> 3) + (qq & 3);
+                        const size_t e = ((size_t)(wr * NKB + (col >> 5)) * 64 + rr + 16 * ((col & 31) >> 3)) * 8 + (col & 7);
+                        rW[e] = from_f<T>(acc[mt][n][i]);
+                    }
+        };
+        // U: m-tile mt holds the rows of state-pass wave mt, so each lane's 4
+        // values are one fragment-order slot group
+        auto store_u = [&]() {
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int n = 0; n < PER; ++n) {
                     const int t = nt0 + n - NTW;
                     float vals[4] = {acc[mt][n][0], acc[mt][n][1], acc[mt][n][2], acc[mt][n][3]};
-                    st4_stream(rU + ((size_t)(t * 4 + mt) * 64 + lane) * 4, vals);
+                    st4_stream(rU + ((size_t)(t * NW + mt + 4 * half) * 64 + lane) * 4, vals);
                 }
-        }
-    }
-    if constexpr (sizeof(T) == 2) {
-        lds_barrier();
-        // W in fragment order from the staged natural tile
-        constexpr int NKB = DK / 32;
-        for (int e = tid; e < 4 * NKB * 64; e += kThreads) {
-            const int l = e & 63, kq = (e >> 6) % NKB, w = (e >> 6) / NKB;
-            st_frag_stream(rW + (size_t)e * 8, ld_frag(sW + pw(w, l & 15) * LDK + 32 * kq + 8 * (l >> 4)));
+        };
+        if constexpr (!SUB) {
+            if (isW) {
+                if constexpr (sizeof(T) == 2) stage_w();
+                else direct_w();
+            } else {
+                store_u();
+            }
+            if constexpr (sizeof(T) == 2) {
+                lds_barrier();
+                copy_w();
+            }
+        } else {
+            // ---- SUB: the second sub-chunk's rows of the 128-row W and U.
+            // Block elimination of (I + A) over the two sub-chunks gives
+            // T10 = -T11 A10 T00 with A10 = diag(beta1) K+1 Kbar0^T (both
+            // factors sub-chunk local), so with G = W1 Kbar0^T = T11 A10:
+            //   W1 <- W1 Diag(phi0) - G W0,   U1 <- U1 - G U0
+            // (W1, U1 of the second sub-chunk alone; W0, U0 of the first,
+            // whose gamma base is already the chunk start).
+            T* sW1 = reinterpret_cast<T*>(smem_all + Cfg::BYTES + Cfg::R_A);                // W1, natural rows
+            T* sKb0 = reinterpret_cast<T*>(smem_all + Cfg::R_KP);                          // Kbar0, natural rows
+            T* sWU0 = reinterpret_cast<T*>(smem_all + Cfg::R_KM);                          // [W0|U0] B fragments
+            float* sG = reinterpret_cast<float*>(smem_all + Cfg::BYTES + Cfg::R_KP);      // G [64][LDF]
+            static_assert((size_t)NTN * 2 * 64 * 8 * sizeof(T) <= Cfg::R_A - Cfg::R_KM, "[W0|U0] staging");
+            static_assert((size_t)C * LDF * sizeof(float) <= Cfg::R_QP, "G staging");
+            static_assert((size_t)C * LDK * sizeof(T) <= Cfg::R_SMALL - Cfg::R_A, "W staging");
+            if (isW && (sizeof(T) == 2 || half == 1)) stage_w();
+            lds_barrier();   // every P4 operand read done; W staged
+            if (half == 0) {
+#pragma unroll
+                for (int i = 0; i < PL; ++i) {
+                    VT x;
+#pragma unroll
+                    for (int cc = 0; cc < CPT; ++cc) x[cc] = kbl[cc][i];
+                    *reinterpret_cast<VT*>(sKb0 + (p0 + i) * LDK + ch0) = x;
+                }
+                // natural B fragments over the positions: slots 0-3 from
+                // m-tile 2kb, 4-7 from 2kb+1 (W: rows 32kb + 4(l/16) + i and
+                // 32kb + 16 + ..., U: rows 32kb + 8(l/16) + j)
+#pragma unroll
+                for (int n = 0; n < PER; ++n)
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+                        Frag<T> f;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            frag_set(f, i, acc[2 * kb][n][i]);
+                            frag_set(f, 4 + i, acc[2 * kb + 1][n][i]);
+                        }
+                        st_frag(sWU0 + ((size_t)((nt0 + n) * 2 + kb) * 64 + lane) * 8, f);
+                    }
+                // (copy_w is strided over all of the sub-chunk's threads)
+                if constexpr (sizeof(T) == 2) copy_w();
+                if (isW) {
+                    if constexpr (sizeof(T) == 4) direct_w();
+                } else {
+                    store_u();
+                }
+            }
+            lds_barrier();   // Kbar0 and [W0|U0] visible
+            {
+                // G = W1 Kbar0^T: 16 tiles over the 8 waves
+                const int w8 = (int)(threadIdx.x >> 6);
+#pragma unroll
+                for (int tt = w8; tt < 16; tt += 8) {
+                    const int ti = tt >> 2, tj = tt & 3;
+                    f32x4 g4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb)
+                        mma(g4, ld_frag(sW1 + (16 * ti + r16) * LDK + 32 * kb + 8 * grp),
+                            ld_frag(sKb0 + (16 * tj + r16) * LDK + 32 * kb + 8 * grp));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sG[(16 * ti + 4 * grp + i) * LDF + 16 * tj + r16] = g4[i];
+                }
+            }
+            lds_barrier();   // G visible; W1 staging free
+            if (half == 1) {
+                if (isW) {
+#pragma unroll
+                    for (int n = 0; n < PER; ++n) {
+                        const int col = 16 * (nt0 + n) + r16;
+                        const float p0s = __builtin_amdgcn_exp2f(sX[PERCH ? col : 0]);
+#pragma unroll
+                        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) acc[mt][n][i] *= p0s;
+                    }
+                }
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    const int grow = isW ? 16 * mt + r16 : pw(mt, r16);
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+                        // -G row grow, in the slot order of the fragments above
+                        const float* gr = sG + grow * LDF + 32 * kb;
+                        float gv8[8];
+                        if (isW) {
+                            ld4(gr + 4 * grp, gv8);
+                            ld4(gr + 16 + 4 * grp, gv8 + 4);
+                        } else {
+                            ld4(gr + 8 * grp, gv8);
+                            ld4(gr + 8 * grp + 4, gv8 + 4);
+                        }
+                        Frag<T> fa;
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) frag_set(fa, j, -gv8[j]);
+#pragma unroll
+                        for (int n = 0; n < PER; ++n)
+                            mma(acc[mt][n], fa, ld_frag(sWU0 + ((size_t)((nt0 + n) * 2 + kb) * 64 + lane) * 8));
+                    }
+                }
+                if (isW) {
+                    if constexpr (sizeof(T) == 2) stage_w();
+                    else direct_w();
+                } else {
+                    store_u();
+                }
+            }
+            if constexpr (sizeof(T) == 2) {
+                lds_barrier();
+                if (half == 1) copy_w();
+            }
         }
     }
 }
@@ -621,6 +842,38 @@ __global__ __launch_bounds__(kThreads, 2) void intra_kernel(
     if constexpr (PRO) ph = pro_head(pro, h);
     intra_chunk<KIND, T, DK, DV, PRO>(in, smem, flags,
                                       ws + (((size_t)b * H + h) * NT + c) * Rec<T, DK, DV>::BYTES, nvalid, ph);
+}
+
+// 128-token chunks of 64-row sub-chunks ([KDA] 2.3): one 512-thread
+// workgroup per (chunk, head, batch), heads fastest; threads 256s .. 256s+255
+// load and process sub-chunk s (intra_chunk with C2 = 128).
+template <int KIND, typename T, int DK, int DV, bool PRO>
+__global__ __launch_bounds__(2 * kThreads, 1) void intra128_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, uint8_t* __restrict__ ws,
+    unsigned* __restrict__ flags, int Tlen, int H, int NT, int c0, int n, int B, Prologue pro)
+{
+    using Cfg = IntraCfg<KIND, T, DK, DV>;
+    constexpr int C2 = 2 * kChunk;
+    constexpr size_t BYTES = 2 * Cfg::BYTES + 2 * DK * sizeof(float);
+    static_assert(BYTES <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[BYTES];
+    const unsigned it = blockIdx.x;
+    const int h = (int)(it % (unsigned)H);
+    const unsigned t = it / (unsigned)H;
+    const int c = c0 + (int)(t % (unsigned)n), b = (int)(t / (unsigned)n);
+    const int nv = min(C2, Tlen - c * C2);
+    const int half = (int)(threadIdx.x >> 8);
+    const int nvh = min(max(nv - kChunk * half, 0), kChunk);
+    const size_t row_chunk = ((size_t)b * Tlen + (size_t)c * C2) * H + h;
+    // an empty second sub-chunk loads the chunk's first row (and zeroes it)
+    const size_t row0 = nvh > 0 ? row_chunk + (size_t)half * kChunk * H : row_chunk;
+    IntraIn<KIND, T, DK, DV> in;
+    intra_load<KIND, T, DK, DV>(in, q, k, v, g, beta, row0, max(nvh, 1), H);
+    ProHead ph{};
+    if constexpr (PRO) ph = pro_head(pro, h);
+    intra_chunk<KIND, T, DK, DV, PRO, C2>(in, smem, flags,
+                                          ws + (((size_t)b * H + h) * NT + c) * Rec<T, DK, DV, C2>::BYTES, nvh, ph);
 }
 
 // Packed sequences: one workgroup per (chunk slot, head), heads fastest.  The

@@ -41,8 +41,33 @@ dr_status launch_inter_t(const Problem& p, const float* h0, float* hT, int c0, i
     return DR_ERR_UNSUPPORTED;
 }
 
+// 128-token records: 8 recurrence + 8 output waves, no prefetch wave; at
+// most 32 value columns per workgroup (the 1024-thread workgroup leaves 128
+// registers per lane)
+template <int KIND, typename E, int D, int NTN>
+dr_status launch_inter128_n(const Problem& p, const float* h0, float* hT, int c0, int n, hipStream_t st) {
+    constexpr int NV = D / (16 * NTN);
+    dim3 grid(p.B * p.H * NV);
+    hipLaunchKernelGGL((dr::inter_kernel<KIND, E, D, D, NTN, 0, false, false, kChunk128>), grid,
+                       dim3(dr::inter_threads<0, kChunk128>()), 0, st, p.ws, h0, static_cast<E*>(p.o), hT, p.T,
+                       p.H, p.NT, c0, n, nullptr, 0, nullptr, nullptr);
+    return check_launch();
+}
+template <int KIND, typename E, int D>
+dr_status launch_inter128_t(const Problem& p, const float* h0, float* hT, int c0, int n, hipStream_t st) {
+    if (sizeof(E) == 4 || pick_ntn(p.B * p.H, D) == 1) return launch_inter128_n<KIND, E, D, 1>(p, h0, hT, c0, n, st);
+    return launch_inter128_n<KIND, E, D, 2>(p, h0, hT, c0, n, st);
+}
+
 template <int KIND>
 dr_status launch_inter_k(const Problem& p, const float* h0, float* hT, int c0, int n, hipStream_t st) {
+    if (p.C == kChunk128) {
+        if (p.dtype == DR_BF16)
+            return p.D == 64 ? launch_inter128_t<KIND, bf16, 64>(p, h0, hT, c0, n, st)
+                             : launch_inter128_t<KIND, bf16, 128>(p, h0, hT, c0, n, st);
+        if (p.D == 64) return launch_inter128_t<KIND, float, 64>(p, h0, hT, c0, n, st);
+        return DR_ERR_UNSUPPORTED;
+    }
     if (p.dtype == DR_BF16) {
         if (p.D == 64) return launch_inter_t<KIND, bf16, 64>(p, h0, hT, c0, n, st);
         return launch_inter_t<KIND, bf16, 128>(p, h0, hT, c0, n, st);

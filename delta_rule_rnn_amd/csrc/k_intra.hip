@@ -16,8 +16,26 @@ dr_status launch_intra_t(const Problem& p, int c0, int n, hipStream_t st) {
     return check_launch();
 }
 
+// 128-token chunks: one 512-thread workgroup per chunk (two sub-chunks)
+template <int KIND, typename E, int D, bool PRO>
+dr_status launch_intra128_t(const Problem& p, int c0, int n, hipStream_t st) {
+    const long long items = (long long)p.B * n * p.H;
+    if (items > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL((dr::intra128_kernel<KIND, E, D, D, PRO>), dim3((unsigned)items), dim3(2 * dr::kThreads), 0,
+                       st, static_cast<const E*>(p.q), static_cast<const E*>(p.k), static_cast<const E*>(p.v),
+                       p.g, p.beta, p.ws, p.flags, p.T, p.H, p.NT, c0, n, p.B, p.pro);
+    return check_launch();
+}
+
 template <int KIND, bool PRO>
 dr_status launch_intra_p(const Problem& p, int c0, int n, hipStream_t st) {
+    if (p.C == kChunk128) {
+        if (p.dtype == DR_BF16)
+            return p.D == 64 ? launch_intra128_t<KIND, bf16, 64, PRO>(p, c0, n, st)
+                             : launch_intra128_t<KIND, bf16, 128, PRO>(p, c0, n, st);
+        if (p.D == 64) return launch_intra128_t<KIND, float, 64, PRO>(p, c0, n, st);
+        return DR_ERR_UNSUPPORTED;
+    }
     if (p.dtype == DR_BF16) {
         if (p.D == 64) return launch_intra_t<KIND, bf16, 64, PRO>(p, c0, n, st);
         return launch_intra_t<KIND, bf16, 128, PRO>(p, c0, n, st);

@@ -595,17 +595,18 @@ def _pw(w, r):
 
 def _frag_maps(C: int, Dk: int, Dv: int):
     """For each record block, the natural (row, col) of every stored element,
-    in storage order (the fragment order of include/deltarule.h, dr_intra)."""
+    in storage order (the fragment order of include/deltarule.h, dr_intra;
+    nw = C/16 position groups, kq = C/32 position blocks)."""
     import numpy as np
-    nkb = Dk // 32
-    w, kb, l, j = np.meshgrid(np.arange(4), np.arange(nkb), np.arange(64), np.arange(8), indexing="ij")
+    nkb, nw, kq = Dk // 32, C // 16, C // 32
+    w, kb, l, j = np.meshgrid(np.arange(nw), np.arange(nkb), np.arange(64), np.arange(8), indexing="ij")
     wq = (_pw(w, l % 16), 32 * kb + 8 * (l // 16) + j)                      # W, Qt: [pos][dk]
-    w2, h, kb2, l2, j2 = np.meshgrid(np.arange(nkb), np.arange(2), np.arange(2), np.arange(64),
+    w2, h, kb2, l2, j2 = np.meshgrid(np.arange(nkb), np.arange(2), np.arange(kq), np.arange(64),
                                      np.arange(8), indexing="ij")
     kbt = (32 * w2 + _prow(h, l2 % 16), 32 * kb2 + 8 * (l2 // 16) + j2)     # KbT: [dk][pos]
-    w3, kb3, l3, j3 = np.meshgrid(np.arange(4), np.arange(2), np.arange(64), np.arange(8), indexing="ij")
+    w3, kb3, l3, j3 = np.meshgrid(np.arange(nw), np.arange(kq), np.arange(64), np.arange(8), indexing="ij")
     aqk = (_pw(w3, l3 % 16), 32 * kb3 + 8 * (l3 // 16) + j3)                # Aqk: [pos][pos]
-    t4, w4, l4, i4 = np.meshgrid(np.arange(Dv // 16), np.arange(4), np.arange(64), np.arange(4),
+    t4, w4, l4, i4 = np.meshgrid(np.arange(Dv // 16), np.arange(nw), np.arange(64), np.arange(4),
                                  indexing="ij")
     ut = (16 * t4 + l4 % 16, 32 * (w4 >> 1) + 8 * (l4 // 16) + 4 * (w4 & 1) + i4)  # UT: [dv][pos]
     return {"W": wq, "Qt": wq, "KbT": kbt, "Aqk": aqk, "UT": ut}

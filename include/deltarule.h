@@ -33,7 +33,15 @@
  *     page, section 2: a >= 0.9 keeps 2^(-gamma) small); the range is
  *     reported through `flags`, see DR_FLAG_*.
  *   Shapes: B, H >= 1, T >= 0 (T = 0 copies h0 to hT, or zeros it),
- *     Dk == Dv in {64, 128}, C == 64.  T need not be a multiple of C: the
+ *     Dk == Dv in {64, 128}, C == 64.  The dense forward (kda_fwd, gdn_fwd,
+ *     decay_la_fwd, dr_forward, dr_forward_noalloc, dr_intra / dr_inter)
+ *     also takes C == 128 (bf16 I/O, and fp32 I/O at Dk = 64): 128-token
+ *     chunks built from two 64-token sub-chunks whose gate cumsum restarts
+ *     at the sub-chunk ("TileLang 实战：KDA 从零到一–Kimi Delta Attention",
+ *     section 2.3, the sub-chunk safeguard), so 2^(-gamma) never spans more
+ *     than 64 positions; the rows of the 128 x 128 UT system are then
+ *     joined by block elimination.  Other entry points return
+ *     DR_ERR_UNSUPPORTED for C == 128.  T need not be a multiple of C: the
  *     last chunk is masked.
  *   Streams: `stream` is a hipStream_t (0 = the null stream).  All work is
  *     enqueued on it; nothing synchronises with the host.
@@ -67,6 +75,8 @@ typedef enum { DR_KIND_KDA = 0, DR_KIND_GDN = 1, DR_KIND_DECAY_LA = 2 } dr_kind;
 /* Gate-range flags, OR-ed into *flags (a device uint32) when flags != NULL.
  * The caller clears the word before the call and reads it after syncing.
  * Only the per-channel (KDA) path materialises 2^(-gamma):
+ * (At C == 128 "chunk" means each 64-token sub-chunk, the span over which
+ * the kernels form 2^(-gamma).)
  *   DR_FLAG_KM_FP16_RANGE: some chunk has -gamma_log2 >= 16 somewhere, so
  *     |k| * 2^(-gamma) could exceed the fp16 maximum 65504 (values are kept in
  *     bf16/fp32 here, so results stay valid);
@@ -121,7 +131,7 @@ size_t dr_record_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, 
  *     q_eff S_in to the outputs of all segments but the first.  This is the
  *     entry-state hand-off of sequence-split evaluation ("Gated DeltaNet",
  *     section "前向计算的矩阵分解") inside one GPU.
- *   record path: dr_intra then dr_inter.
+ *   record path: dr_intra then dr_inter (always at C == 128).
  */
 dr_status kda_fwd(const void* q, const void* k, const void* v, const float* g,
                   const float* beta, const float* h0, void* o, float* hT,
@@ -444,11 +454,14 @@ dr_status dr_kda_prep(const void* q, const void* k, const float* gamma,
  * Each block is stored in the MFMA fragment order the state pass reads
  * (lane l, element j, 32-row blocks split by prow(h, r) = 8(r/4) + 4h + r%4,
  * pw(w, r) = 32(w/2) + prow(w%2, r)):
- *   W, Qt [w<4][kb<Dk/32][l<64][j<8] = X[pw(w, l%16)][32kb + 8(l/16) + j]
- *   KbT   [w<Dk/32][h<2][kb<2][l][j<8] = Kbar[32kb + 8(l/16) + j][32w + prow(h, l%16)]
- *   Aqk   [w<4][kb<2][l][j<8] = Aqk[pw(w, l%16)][32kb + 8(l/16) + j]
- *   UT    [t<Dv/16][w<4][l][i<4] = U[32(w/2) + 8(l/16) + 4(w%2) + i][16t + l%16]
- * Rows of a ragged last chunk beyond T are zero.  Record size:
+ *   W, Qt [w<C/16][kb<Dk/32][l<64][j<8] = X[pw(w, l%16)][32kb + 8(l/16) + j]
+ *   KbT   [w<Dk/32][h<2][kb<C/32][l][j<8] = Kbar[32kb + 8(l/16) + j][32w + prow(h, l%16)]
+ *   Aqk   [w<C/16][kb<C/32][l][j<8] = Aqk[pw(w, l%16)][32kb + 8(l/16) + j]
+ *   UT    [t<Dv/16][w<C/16][l][i<4] = U[32(w/2) + 8(l/16) + 4(w%2) + i][16t + l%16]
+ * Rows of a ragged last chunk beyond T are zero.  At C == 128 the record is
+ * that of the whole 128-token chunk (gamma based at its start, Kbar and phi
+ * at its end, Aqk 128 x 128) although the kernel builds it from the two
+ * sub-chunks.  Record size:
  * dr_record_bytes(); workspace: dr_record_workspace_bytes().  For GDN / decay_la, g is [B,T,H] and beta may be NULL
  * for decay_la.
  */
@@ -469,7 +482,8 @@ dr_status dr_inter(int kind, const float* h0, void* o, float* hT,
                    int B, int T, int H, int Dk, int Dv, int C, int dtype,
                    const void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of one workspace record (0 for unsupported sizes). */
+/* Bytes of one workspace record (0 for unsupported sizes; C is 64, or 128
+ * where built). */
 size_t dr_record_bytes(int Dk, int Dv, int C, int dtype);
 
 /*
@@ -496,10 +510,11 @@ dr_status dr_forward_stage(int stage, int kind, const void* q, const void* k, co
 /* Human-readable text for a status code (static storage). */
 const char* dr_status_string(int status);
 
-/* ABI version of this library: 6 (1, plus the prologue entry points in 2, the
+/* ABI version of this library: 7 (1, plus the prologue entry points in 2, the
  * backward in 3, the backward through the prologue in 4, the packed-sequence
  * backward in 5, the allocation-free forward, the segment-parallel forward's
- * stages and the record workspace query in 6). */
+ * stages and the record workspace query in 6, 128-token sub-chunked chunks
+ * for the dense forward in 7). */
 int dr_abi_version(void);
 
 #ifdef __cplusplus

@@ -38,7 +38,7 @@ def test_header_and_binding_agree():
 def test_every_declared_symbol_is_exported(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.dr_abi_version() == 6
+    assert lib.dr_abi_version() == 7
 
 
 def test_status_strings(lib):
@@ -69,12 +69,31 @@ def test_workspace_sizes(lib):
     assert lib.dr_record_bytes(128, 128, 32, 1) == 0
 
 
+def test_workspace_sizes_chunk128(lib):
+    """128-token chunks: one 128-row record per (b, h, chunk) with the same
+    blocks (W, Q~, Kbar^T, the 128 x 128 Aqk, U^T, phi); the dense forward
+    only, not built for fp32 at D = 128."""
+    rec = lib.dr_record_bytes(128, 128, 128, 1)
+    assert rec == ((3 * 128 * 128 + 128 * 128 + 128 * 128) * 2 + 128 * 4 + 255) // 256 * 256
+    assert lib.dr_record_bytes(64, 64, 128, 0) == ((3 * 128 * 64 + 128 * 128 + 64 * 128) * 4 + 64 * 4 + 255) // 256 * 256
+    assert lib.dr_record_bytes(128, 128, 128, 0) == 0
+    # T = 300 is 3 chunks of 128; the forward takes the record path
+    assert lib.dr_record_workspace_bytes(0, 2, 300, 3, 128, 128, 128, 1) == 2 * 3 * 3 * rec
+    assert lib.dr_workspace_bytes(0, 2, 300, 3, 128, 128, 128, 1) == 2 * 3 * 3 * rec
+    assert lib.dr_segment_workspace_bytes(0, 2, 300, 3, 128, 128, 128, 1) == 0
+    # packed sequences and the backward take C = 64 only
+    assert lib.dr_workspace_bytes_varlen(0, 2, 300, 1, 64, 64, 128, 1) == 0
+    assert lib.dr_backward_workspace_bytes(1, 1, 128, 2, 64, 64, 128, 1) == 0
+    assert lib.dr_backward_varlen_workspace_bytes(1, 2, 128, 2, 64, 64, 128, 1, 0) == 0
+
+
 FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation first
 
 
 @pytest.mark.parametrize("case,expect", [
     (dict(B=0), -1), (dict(H=0), -1), (dict(T=-1), -1), (dict(dtype=5), -1),
-    (dict(Dk=96, Dv=96), -2), (dict(Dk=128, Dv=64), -2), (dict(C=32), -2),
+    (dict(Dk=96, Dv=96), -2), (dict(Dk=128, Dv=64), -2), (dict(C=32), -2), (dict(C=96), -2),
+    (dict(C=128, Dk=128, Dv=128, dtype=0), -2), (dict(C=128, q=None), -1), (dict(C=128, ws_bytes=100), -4),
     (dict(q=None), -1), (dict(beta=None), -1), (dict(q=FAKE + 4), -1), (dict(o=FAKE + 8), -1),
     (dict(ws=None), -4), (dict(ws_bytes=100), -4),
 ])
