@@ -815,8 +815,14 @@ struct GradSmem {
                             KM = TI, QT = TI + 5 * SQ, END2 = QT + MAT;
     static constexpr size_t E = TI;                  // phase 3: E over the K- slot
     static constexpr size_t BIG = END1 > END2 ? END1 : END2;
-    static constexpr size_t DB = BIG, SE = DB + C, GAM = SE + C, PHI = GAM + C, FCOL = PHI + DK, DPHI = FCOL + DK,
-                            ROW = DPHI + DK, BT = ROW + C, FLOATS = BT + C;
+    // reductions in a fixed order: dbeta partials [NDB][C], one slot per
+    // source (the phase-1 value tiles' two column halves, the DK/16 column
+    // tiles of phase 2a, the four column tiles of phase 2b), each written by
+    // one wave; the column sums of dKbar * Kbar [8][16] per wave
+    static constexpr int NDB = 2 + DK / 16 + 4;
+    static constexpr size_t DB = BIG, SE = DB + (size_t)NDB * C, GAM = SE + C, PHI = GAM + C, FCOL = PHI + DK,
+                            FP = FCOL + DK, DPHI = FP + 128, ROW = DPHI + DK, BT = ROW + C, FLOATS = BT + C;
+    static_assert(FLOATS * 4 <= 160 * 1024, "LDS");
     static_assert(KM + MAT <= DL, "K- slot overlaps dL");
     static_assert(NW + MAT <= DL, "nW slot overlaps dL");
 };
@@ -842,6 +848,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     float* sGam = smem + SM::GAM;
     float* sPhi = smem + SM::PHI;
     float* sF = smem + SM::FCOL;
+    float* sFp = smem + SM::FP;
     float* sDphi = smem + SM::DPHI;
     float* sRow = smem + SM::ROW;
     float* sBt = smem + SM::BT;      // beta, zero past the end and for decay_la
@@ -890,7 +897,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     if (tid < C) {
         const float bb = DELTA ? beta[row0 + (size_t)min(tid, nvalid - 1) * H] : 0.f;
         sBt[tid] = tid < nvalid ? bb : 0.f;
-        sDb[tid] = 0.f;
+#pragma unroll
+        for (int j = 0; j < SM::NDB; ++j) sDb[j * C + tid] = 0.f;
         sE[tid] = 0.f;
         sRow[tid] = 0.f;
         if constexpr (!PERCH) sGam[tid] = pc[P::GAM + tid];
@@ -968,7 +976,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
                     if (r < nvalid) dv[(row0 + (size_t)r * H) * DV + dv0 + cc] = from_f<T>(bt * dn[i]);
                     float part = dn[i] * vv;
                     part = row16_sum(part);
-                    if ((lane & 15) == 0) atomicAdd(&sDb[r], part);
+                    // slot tj: this wave alone adds to it, slice after slice
+                    if ((lane & 15) == 0) sDb[tj * C + r] += part;
                 }
             } else {
 #pragma unroll
@@ -1072,11 +1081,12 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     // the four row groups of a column (lanes l, l+16, l+32, l+48)
     fpart += __shfl_xor(fpart, 16, 64);
     fpart += __shfl_xor(fpart, 32, 64);
+    // one slot per contributing wave (waves w and w + NCT share columns)
     if constexpr (PERCH) {
-        if (lane < 16) atomicAdd(&sF[ecol(0)], fpart);
+        if (lane < 16) sFp[(wave / NCT) * DK + ecol(0)] = fpart;
     } else {
         fpart = row16_sum(fpart);
-        if (lane == 0) atomicAdd(&sF[0], fpart);
+        if (lane == 0) sFp[wave] = fpart;
     }
 
     if constexpr (DELTA) {
@@ -1105,7 +1115,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
                 aE[m][i] += dm * bt * kp;
                 float part = dm * kp;
                 part = row16_sum(part);
-                if ((lane & 15) == 0) atomicAdd(&sDb[r], part);
+                if ((lane & 15) == 0) sDb[(2 + tj) * C + r] = part;
             }
         }
         lds_barrier();
@@ -1150,7 +1160,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
                 sDL[r * LDC + cc] = beta_at(r) * da;
                 float part = da * lrc[m][i];
                 part = row16_sum(part);
-                if ((lane & 15) == 0) atomicAdd(&sDb[r], part);
+                if ((lane & 15) == 0) sDb[(2 + NCT + tj) * C + r] = part;
             }
         }
     }
@@ -1200,6 +1210,9 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             *reinterpret_cast<f32x4*>(sKm + r * LDK + d0) = qv;
         }
     }
+    // scalar gates: the pair terms c_ij = dX_ij X_ij go to a [C][C] matrix in
+    // the Y slot (free in this phase), summed by rows and columns below
+    float* sCx = smem + SM::Y;
     if constexpr (!PERCH) {
         // G = dX .* Gamma in place, and the log-gate terms of the pair products:
         // E_i += sum_j dX_ij X_ij,  E_j -= sum_i dX_ij X_ij  (X = L, Aqk)
@@ -1219,13 +1232,20 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
                     sDL[r * LDC + cc] = dl * gmm;
                 }
             }
-            if (contrib != 0.f) {
-                atomicAdd(&sE[r], contrib);
-                atomicAdd(&sE[cc], -contrib);
-            }
+            sCx[r * LDC + cc] = contrib;
         }
     }
     lds_barrier();
+    if constexpr (!PERCH) {
+        // E_r = sum_{c <= r} c_rc - sum_{r' >= r} c_r'r, in a fixed order
+        // (read in phase 3, after its barrier)
+        if (tid < C) {
+            float e = 0.f;
+            for (int c2 = 0; c2 <= tid; ++c2) e += sCx[tid * LDC + c2];
+            for (int r2 = tid; r2 < C; ++r2) e -= sCx[r2 * LDC + tid];
+            sE[tid] = e;
+        }
+    }
     if constexpr (PERCH) {
         // dK+ += dL K-;  dK- = dL^T K+ + dAqk^T Q~;  dQ~ += dAqk K- (one
         // product at a time over the owned tiles, which keeps few results live)
@@ -1337,7 +1357,10 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         for (int j = 0; j < RB; ++j) bs += sEm[(b * RB + j) * LDK + d];
         sBlk[b * DK + d] = bs;
         lds_barrier();
-        float acc = sF[d] + sDphi[d] * sPhi[d];
+        float fsum = 0.f;
+#pragma unroll
+        for (int sl = 0; sl < 8 / NCT; ++sl) fsum += sFp[sl * DK + d];
+        float acc = fsum + sDphi[d] * sPhi[d];
 #pragma unroll
         for (int b2 = NB - 1; b2 > b; --b2) acc += sBlk[b2 * DK + d];
 #pragma unroll
@@ -1365,7 +1388,10 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         }
         lds_barrier();
         if (tid == 0) {
-            float acc = sF[0] + sF[1];
+            float f0 = 0.f;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) f0 += sFp[w];
+            float acc = f0 + sF[1];
             for (int r = C - 1; r >= 0; --r) {
                 acc += sRow[r];
                 if (r < nvalid) dg[row0 + (size_t)r * H] = acc;
@@ -1373,7 +1399,12 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         }
     }
     if constexpr (DELTA) {
-        if (tid < nvalid) dbeta[row0 + (size_t)tid * H] = sDb[tid];
+        if (tid < nvalid) {
+            float db = 0.f;
+#pragma unroll
+            for (int j = 0; j < SM::NDB; ++j) db += sDb[j * C + tid];
+            dbeta[row0 + (size_t)tid * H] = db;
+        }
     }
 }
 

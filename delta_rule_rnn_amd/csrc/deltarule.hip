@@ -222,9 +222,13 @@ dr_status backward_impl(int kind, const void* q, const void* k, const void* v, c
               chains, T, H, ceil_div(T, dr::kChunk), core, L, pk};
     s = launch_backward(kind, a, Dk, dtype, st);
     if (s != DR_OK || !use_pro) return s;
-    // gradients with respect to the raw inputs, in place
+    // gradients with respect to the raw inputs, in place; the gate
+    // parameters' per-workgroup partial sums go to the prologue's q slot
+    // (its last reader, the gradient kernel, has run) and are summed in a
+    // fixed order
     return launch_prologue(true, kind, Dk, dtype, q, k, g, delta ? beta : nullptr, nullptr, nullptr, nullptr,
-                           nullptr, dq, dk, dg, delta ? dbeta : nullptr, dA_log, ddt_bias, B, T, H, pr, st);
+                           nullptr, dq, dk, dg, delta ? dbeta : nullptr, dA_log, ddt_bias, B, T, H, pr, st,
+                           reinterpret_cast<float*>(w + PL.qh));
 }
 
 }  // namespace drh

@@ -307,7 +307,7 @@ dr_status launch_decode(int kind, const DecodeArgs& a, bool use_pro, int D, int 
 dr_status launch_prologue(bool backward, int kind, int D, int dtype, const void* q, const void* k, const float* g,
                           const float* beta, void* qh, void* kh, float* gh, float* bh, void* dq, void* dk, float* dg,
                           float* dbeta, float* dA_log, float* ddt, int B, int T, int H, const dr::Prologue& pro,
-                          hipStream_t st);                                                               // k_misc.hip
+                          hipStream_t st, float* gpart = nullptr);                                      // k_misc.hip
 dr_status launch_varlen_table(const int* cu_seqlens, int N, int T, int maxchunks, int4* table, int4* seqinfo,
                               int* total, unsigned* flags, hipStream_t st);                              // k_misc.hip
 dr_status launch_copy_or_zero(float* dst, const float* src, size_t n, hipStream_t st);                  // k_misc.hip

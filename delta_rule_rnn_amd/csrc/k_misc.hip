@@ -48,10 +48,14 @@ dr_status launch_decode(int kind, const DecodeArgs& a, bool use_pro, int D, int 
 template <typename E, int D, bool PERCH>
 dr_status launch_prologue_t(bool backward, const void* q, const void* k, const float* g, const float* beta, void* qh,
                             void* kh, float* gh, float* bh, void* dq, void* dk, float* dg, float* dbeta,
-                            float* dA_log, float* ddt, int B, int T, int H, const dr::Prologue& pro, hipStream_t st) {
+                            float* dA_log, float* ddt, int B, int T, int H, const dr::Prologue& pro, hipStream_t st,
+                            float* gpart) {
     const long long rows = (long long)B * T;
-    const long long blocks = (long long)H * ((rows + dr::kProRows - 1) / dr::kProRows);
+    const long long nblk = (rows + dr::kProRows - 1) / dr::kProRows;
+    const long long blocks = (long long)H * nblk;
     if (blocks > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
+    const bool gate = backward && !PERCH && (pro.ops & dr::PRO_GATE);
+    if (gate && !gpart) return DR_ERR_INVALID_ARG;
     if (!backward)
         hipLaunchKernelGGL((dr::prologue_apply_kernel<E, D, PERCH>), dim3((unsigned)blocks), dim3(256), 0, st,
                            static_cast<const E*>(q), static_cast<const E*>(k), g, beta, static_cast<E*>(qh),
@@ -59,16 +63,22 @@ dr_status launch_prologue_t(bool backward, const void* q, const void* k, const f
     else
         hipLaunchKernelGGL((dr::prologue_backward_kernel<E, D, PERCH>), dim3((unsigned)blocks), dim3(256), 0, st,
                            static_cast<const E*>(q), static_cast<const E*>(k), g, beta, static_cast<E*>(dq),
-                           static_cast<E*>(dk), dg, dbeta, dA_log, ddt, rows, H, pro);
+                           static_cast<E*>(dk), dg, dbeta, gpart, (int)nblk, rows, H, pro);
+    if (gate) {
+        if (check_launch() != DR_OK) return DR_ERR_HIP;
+        hipLaunchKernelGGL(dr::prologue_gate_sum_kernel, dim3((unsigned)H), dim3(256), 0, st, gpart, (int)nblk, H,
+                           dA_log, ddt);
+    }
     return check_launch();
 }
 
 dr_status launch_prologue(bool backward, int kind, int D, int dtype, const void* q, const void* k, const float* g,
                           const float* beta, void* qh, void* kh, float* gh, float* bh, void* dq, void* dk, float* dg,
                           float* dbeta, float* dA_log, float* ddt, int B, int T, int H, const dr::Prologue& pro,
-                          hipStream_t st) {
+                          hipStream_t st, float* gpart) {
 #define DR_PRO(E, DD, PC) \
-    return launch_prologue_t<E, DD, PC>(backward, q, k, g, beta, qh, kh, gh, bh, dq, dk, dg, dbeta, dA_log, ddt, B, T, H, pro, st)
+    return launch_prologue_t<E, DD, PC>(backward, q, k, g, beta, qh, kh, gh, bh, dq, dk, dg, dbeta, dA_log, ddt, B, T, H, \
+                                        pro, st, gpart)
     const bool perch = kind == DR_KIND_KDA;
     if (dtype == DR_BF16) {
         if (D == 64) { if (perch) DR_PRO(bf16, 64, true); else DR_PRO(bf16, 64, false); }

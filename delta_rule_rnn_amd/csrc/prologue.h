@@ -76,16 +76,16 @@ __global__ __launch_bounds__(256) void prologue_apply_kernel(const T* __restrict
 // In place: dq, dk (DK per row, I/O dtype), dg (per-channel or one per row),
 // dbeta (one per row) hold the gradients with respect to the recurrence's
 // inputs and are overwritten with those with respect to the raw inputs.
-// dA_log / ddt_bias ([H], zeroed by the caller) accumulate one atomic add per
-// workgroup.
+// With gate generation, each workgroup (head h, row block j) writes its sums
+// of the dA_log and ddt_bias terms to gpart[h * nblk + j] and
+// gpart[(H + h) * nblk + j]; prologue_gate_sum_kernel adds them up.
 template <typename T, int DK, bool PERCH>
 __global__ __launch_bounds__(256) void prologue_backward_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                                 const float* __restrict__ g,
                                                                 const float* __restrict__ beta, T* __restrict__ dq,
                                                                 T* __restrict__ dk, float* __restrict__ dg,
                                                                 float* __restrict__ dbeta,
-                                                                float* __restrict__ dA_log,
-                                                                float* __restrict__ ddt_bias,
+                                                                float* __restrict__ gpart, int nblk,
                                                                 long long rows_per_head, int H, Prologue pro)
 {
     constexpr int NPL = DK / 64;
@@ -158,10 +158,36 @@ __global__ __launch_bounds__(256) void prologue_backward_kernel(const T* __restr
             }
             __syncthreads();
             if (threadIdx.x == 0) {
-                atomicAdd(dA_log + h, red[0][0] + red[0][1] + red[0][2] + red[0][3]);
-                if (ddt_bias) atomicAdd(ddt_bias + h, red[1][0] + red[1][1] + red[1][2] + red[1][3]);
+                const int j = (int)(blockIdx.x / H);
+                gpart[(size_t)h * nblk + j] = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+                gpart[((size_t)H + h) * nblk + j] = red[1][0] + red[1][1] + red[1][2] + red[1][3];
             }
         }
+    }
+}
+
+// dA_log[h] and ddt_bias[h] (when given) from the per-workgroup partials of
+// prologue_backward_kernel, one workgroup per head, in a fixed order: each
+// thread adds blocks tid, tid + 256, ... in turn, then the wave sums and
+// the four wave totals in order.
+__global__ __launch_bounds__(256) void prologue_gate_sum_kernel(const float* __restrict__ gpart, int nblk, int H,
+                                                                float* __restrict__ dA_log,
+                                                                float* __restrict__ ddt_bias)
+{
+    __shared__ float red[2][4];
+    const int h = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+        const float* src = gpart + ((size_t)a * H + h) * nblk;
+        float s = 0.f;
+        for (int j = threadIdx.x; j < nblk; j += 256) s += src[j];
+        s = lane_group_sum<64>(s);
+        if (lane == 0) red[a][wave] = s;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        dA_log[h] = ((red[0][0] + red[0][1]) + red[0][2]) + red[0][3];
+        if (ddt_bias) ddt_bias[h] = ((red[1][0] + red[1][1]) + red[1][2]) + red[1][3];
     }
 }
 

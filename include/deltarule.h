@@ -330,10 +330,17 @@ dr_status dr_decode(int kind, const void* q, const void* k, const void* v, const
  *   workspace: at least dr_backward_workspace_bytes(...): the recomputed
  *          fp32 chunk operands, the chunk entry states and exit adjoints
  *          (fp32 [Dk,Dv] per chunk) and Vnew / dVnew per chunk
- * All arithmetic is fp32.  dbeta and dg are sums of per-wave partials added
- * in shared memory in no fixed order, so repeated calls may differ in their
- * last bits; dq, dk, dv and dh0 are reproducible.  Other conventions and
- * errors as for kda_fwd.  T = 0 writes dh0 = dhT (or zero) and nothing else.
+ * Precision: operands are held in fp32 and accumulated in fp32.  With fp32
+ * I/O every product runs on fp32 MFMA.  With bf16 I/O the chunk-form L and
+ * Aqk, and the gradient kernel's value-slice, pairwise and T products, take
+ * their operands rounded to bf16 as they are read (bf16 MFMA, fp32
+ * accumulation); the entry states come from the forward's state pass on the
+ * bf16 records.
+ * Reproducibility: every reduction (the dbeta and dg partials of the waves
+ * of a chunk, the per-head sums of dr_backward_prologue) adds its terms in a
+ * fixed order, so repeated calls with the same arguments give bit-identical
+ * results.  Other conventions and errors as for kda_fwd.  T = 0 writes dh0 =
+ * dhT (or zero) and nothing else.  C must be 64.
  */
 size_t dr_backward_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, int C, int dtype);
 dr_status dr_backward(int kind, const void* q, const void* k, const void* v, const float* g,
@@ -359,8 +366,8 @@ dr_status dr_backward(int kind, const void* q, const void* k, const void* v, con
  *   dA_log:   DEVICE float [H], written (required with DR_PRO_GATE, else
  *             ignored); ddt_bias: DEVICE float [H], written (required when
  *             the prologue has a dt_bias, else ignored).  Both are sums of
- *             per-workgroup partials added atomically: their summation order
- *             is not fixed.
+ *             per-workgroup partials (kept in the workspace) added in a
+ *             fixed order by one more kernel.
  *   prologue: as for dr_forward; NULL gives dr_backward.
  *   workspace: at least dr_backward_prologue_workspace_bytes(...): the
  *             recurrence's inputs (q^, k^, g^, beta^) plus dr_backward's.

@@ -2,15 +2,15 @@
 torch.autograd, for the dense and packed layouts, with and without the
 prologue.
 
-dq, dk, dv and the state gradients are deterministic: they must equal, bit
-for bit, those of the library's backward called directly with the same
-cotangents.  dbeta, dg and the per-head parameter gradients add per-wave
-partials with atomics in no fixed order, so two calls may differ by fp32
-reassociation, which cancellation inside those sums can make large next to
-the result.  They are compared with the fp64 oracle instead (the reverse
-sweep, and for the prologue its chain rule), at the tolerances of the
-backward parity tests: a wrong tensor or cotangent in the autograd plumbing
-fails either check.
+Every gradient the library returns is reproducible (its reductions add in
+a fixed order), so each must equal, bit for bit, that of the library's
+backward called directly with the same cotangents: a wrong tensor or
+cotangent in the autograd plumbing fails that check.  dg and dbeta are also
+compared with the fp64 oracle (the reverse sweep, and for the prologue its
+chain rule) at the tolerances of the backward parity tests.  The per-head
+sums dA_log and ddt_bias are checked against the fp64 sums of the
+per-token terms the library itself returns, to fp32 summation error, and
+against the oracle.
 """
 from __future__ import annotations
 
@@ -24,7 +24,7 @@ from delta_rule_rnn_amd.inputs import Workload, generate, generate_raw
 from .test_gpu_parity import assert_close_grad, to_dev
 
 pytestmark = pytest.mark.gpu
-EXACT = ("dq", "dk", "dv", "dh0")
+EXACT = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
 
 
 def _ops():
@@ -55,8 +55,11 @@ def test_autograd_dense_matches_backward(kind, dt):
     ref = dra.backward(kind, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], do, w2)
     torch.cuda.synchronize()
     grads = dict(zip(["dq", "dk", "dv", "dg", "dbeta", "dh0"], ref))
-    leaf_of = {"dq": "q", "dk": "k", "dv": "v", "dh0": "h0"}
+    leaf_of = {"dq": "q", "dk": "k", "dv": "v", "dg": "g", "dbeta": "beta", "dh0": "h0"}
     for n in EXACT:
+        if grads[n] is None:
+            assert leaves[leaf_of[n]] is None
+            continue
         assert torch.equal(leaves[leaf_of[n]].grad, grads[n]), n
     orc = recurrence_backward(kind, x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"].transpose(-1, -2),
                               _cpu(do), _cpu(w2).transpose(-1, -2))
@@ -121,7 +124,10 @@ def test_autograd_packed_with_prologue(kind):
                               do, w2, prologue=mk(plain))
     torch.cuda.synchronize()
     grads = dict(zip(["dq", "dk", "dv", "dg", "dbeta", "dh0", "dA_log", "ddt_bias"], ref))
-    for n, leaf in (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dh0", "h0")):
+    pairs = [("dq", "q"), ("dk", "k"), ("dv", "v"), ("dg", "g"), ("dbeta", "beta"), ("dh0", "h0")]
+    if gate:
+        pairs += [("dA_log", "A_log"), ("ddt_bias", "dt_bias")]
+    for n, leaf in pairs:
         assert torch.equal(leaves[leaf].grad, grads[n]), n
     if not gate:
         assert grads["dA_log"] is None and grads["ddt_bias"] is None
@@ -148,7 +154,22 @@ def test_autograd_packed_with_prologue(kind):
         assert_close_grad(dg_got[:, a:b], r["dg"], "bf16", f"{kind} autograd seq {i} dg")
         assert_close_grad(db_got[:, a:b], r["dbeta"], "bf16", f"{kind} autograd seq {i} dbeta")
     if gate:
-        # per-head sums over every token, held to the bf16 tolerance times
+        # the reduction itself: ddt_bias[h] adds the per-token raw-gate
+        # gradients the library returns in dg (da_t), and dA_log[h] the terms
+        # g^_t dg^_t = softplus(a_t + dt_h) / sigmoid(a_t + dt_h) * da_t.
+        # Against their fp64 sums the only error is fp32 summation over T
+        # terms: 64 eps_f32 sum_t |term_t| bounds it with room to spare.
+        a = raw["g"][0].double().numpy() + raw["dt_bias"].double().numpy()[None, :]    # [T, H]
+        da = dg_got[0].astype(np.float64)                                               # [T, H]
+        sp = np.logaddexp(0.0, a)
+        sig = 1.0 / (1.0 + np.exp(-a))
+        eps = float(np.finfo(np.float32).eps)
+        for name, leaf, terms in (("ddt_bias", "dt_bias", da), ("dA_log", "A_log", sp / sig * da)):
+            val = leaves[leaf].grad.double().cpu().numpy()
+            exact = terms.sum(axis=0)
+            bound = 64 * eps * np.abs(terms).sum(axis=0)
+            assert np.all(np.abs(val - exact) <= bound), f"{kind} {name}: {val} vs fp64 sum {exact}, bound {bound}"
+        # and the whole chain against the oracle: the bf16 tolerance times
         # sum_t |coef_t| * max_t |dg^_t| (the size of the terms they add)
         full = opro.apply_backward(kind, raw["q"], raw["k"], raw["g"], raw["beta"], np.zeros_like(q2),
                                    np.zeros_like(k2), core_dg, None, **ok)
@@ -160,3 +181,40 @@ def test_autograd_packed_with_prologue(kind):
             scale = np.sum(np.abs(coef), axis=(0, 1)) * dgmax
             err = np.abs(val - full[name])
             assert np.all(err <= 2e-2 * scale), f"{kind} autograd {name}: |err| {err} > 2e-2 * {scale}"
+
+
+@pytest.mark.parametrize("kind,dt,pro", [("kda", "bf16", False), ("gdn", "f32", False), ("gdn", "bf16", True)])
+def test_backward_is_reproducible(kind, dt, pro):
+    """Two calls of the backward (dense; and packed through the prologue
+    with gate generation) with the same arguments return bit-identical
+    gradients, dbeta, dg, dA_log and ddt_bias included."""
+    dra = _ops()
+    w = Workload(f"{kind}_rep", kind, dt, B=2, H=3, T=300, Dk=64, Dv=64, h0_std=0.2, seed=98)
+    if pro:
+        x = generate_raw(w)
+        d = to_dev(x)
+        P = dra.Prologue(qk_l2norm=True, scale=0.5, beta_sigmoid=True, A_log=d["A_log"], dt_bias=d["dt_bias"])
+    else:
+        d = to_dev(generate(w))
+        P = None
+    gen = torch.Generator().manual_seed(99)
+    do = torch.randn(d["v"].shape, generator=gen).to(d["v"].dtype).to("cuda:0")
+    dhT = (torch.randn(d["h0"].shape, generator=gen) * 0.1).to("cuda:0")
+    run = lambda: dra.backward(kind, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], do, dhT, prologue=P)
+    r1, r2 = run(), run()
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(r1, r2)):
+        assert (a is None) == (b is None)
+        if a is not None:
+            assert torch.equal(a, b), f"result {i} differs between calls"
+    if pro:
+        cu = torch.tensor([0, 170, 170, 300], dtype=torch.int32, device="cuda:0")
+        sq = lambda t: t[:1].reshape(t.shape[1:]).contiguous()
+        h0p = torch.zeros(3, 3, 64, 64, device="cuda:0")
+        runp = lambda: dra.backward_varlen(kind, sq(d["q"]), sq(d["k"]), sq(d["v"]), sq(d["g"]), sq(d["beta"]), cu,
+                                           h0p, sq(do), None, prologue=P)
+        p1, p2 = runp(), runp()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(p1, p2)):
+            if a is not None:
+                assert torch.equal(a, b), f"packed result {i} differs between calls"
