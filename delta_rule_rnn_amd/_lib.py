@@ -74,10 +74,14 @@ class LibraryMissing(RuntimeError):
     pass
 
 
-def load(path: str = LIB_PATH) -> ctypes.CDLL:
+def load(path: str = "") -> ctypes.CDLL:
+    """Load the library once: `path`, else the file the environment variable
+    DR_LIBRARY names (another build of the same sources, e.g. one with host
+    sanitizers), else the in-tree build."""
     global _LIB
     if _LIB is not None:
         return _LIB
+    path = path or os.environ.get("DR_LIBRARY") or LIB_PATH
     if not os.path.exists(path):
         raise LibraryMissing(
             f"{path} is not built; run __graft_entry__.build() (hipcc, gfx950) first")

@@ -23,6 +23,7 @@ dr_status forward(int kind, const void* q, const void* k, const void* v, const f
     p.use_pro = use_pro;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (T == 0) return launch_inter(p, h0, hT, 0, 0, st);
+    if ((s = poison_workspace(ws, need, st)) != DR_OK) return s;
     if (C == dr::kChunk && seg_supported(Dk, dtype)) {
         // segment-parallel path: local segment pass, entry-state
         // composition (and hT), then the output correction
@@ -60,7 +61,11 @@ dr_status forward_stage(int stage, int kind, const void* q, const void* k, const
     p.pro = pr;
     p.use_pro = use_pro;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (stage == 0) return launch_seg_local(p, S, h0, st);
+    if (stage == 0) {
+        // (the later stages read what stage 0 wrote: only stage 0 poisons)
+        if ((s = poison_workspace(ws, S.bytes, st)) != DR_OK) return s;
+        return launch_seg_local(p, S, h0, st);
+    }
     if (stage == 1) return launch_seg_compose(p, S, hT, st);
     return launch_seg_correct(p, S, st);
 }
@@ -94,6 +99,7 @@ dr_status forward_varlen(int kind, const void* q, const void* k, const void* v, 
     p.pro = pr;
     p.use_pro = use_pro;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((s = poison_workspace(ws, L.bytes, st)) != DR_OK) return s;
     s = launch_varlen_table(cu_seqlens, N, T, L.maxchunks, reinterpret_cast<int4*>(w + L.table),
                             reinterpret_cast<int4*>(w + L.seqinfo), reinterpret_cast<int*>(w + L.total), flags, st);
     if (s != DR_OK) return s;
@@ -176,6 +182,7 @@ dr_status backward_impl(int kind, const void* q, const void* k, const void* v, c
         return launch_copy_or_zero(dh0, dhT, n, st);
     }
     uint8_t* w = static_cast<uint8_t*>(workspace);
+    if ((s = poison_workspace(w, use_pro ? PL.bytes : core_bytes, st)) != DR_OK) return s;
     uint8_t* rest = use_pro ? w + PL.core : w;     // [chunk table][core]
     dr::bw::Pack pk{nullptr, nullptr, nullptr, 0};
     if (packed) {
@@ -238,7 +245,7 @@ using namespace drh;
 extern "C" {
 
 size_t dr_backward_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, int C, int dtype) {
-    if (kind < 0 || kind > 2 || B <= 0 || H <= 0 || T < 0) return 0;
+    if (kind < 0 || kind > 2 || B <= 0 || H <= 0 || T < 0 || !within_limit(B, T, H, Dk)) return 0;
     if (C != dr::kChunk || dr_record_bytes(Dk, Dv, C, dtype) == 0) return 0;
     return bwd_layout(B, T, H, Dk, dtype).bytes;
 }
@@ -252,7 +259,7 @@ dr_status dr_backward(int kind, const void* q, const void* k, const void* v, con
 }
 
 size_t dr_backward_prologue_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, int C, int dtype) {
-    if (kind < 0 || kind > 2 || B <= 0 || H <= 0 || T < 0) return 0;
+    if (kind < 0 || kind > 2 || B <= 0 || H <= 0 || T < 0 || !within_limit(B, T, H, Dk)) return 0;
     if (C != dr::kChunk || dr_record_bytes(Dk, Dv, C, dtype) == 0) return 0;
     return probwd_layout(kind, B, T, H, Dk, dtype, bwd_layout(B, T, H, Dk, dtype).bytes).bytes;
 }
@@ -268,7 +275,8 @@ dr_status dr_backward_prologue(int kind, const void* q, const void* k, const voi
 
 size_t dr_backward_varlen_workspace_bytes(int kind, int N, int T, int H, int Dk, int Dv, int C, int dtype,
                                           int with_prologue) {
-    if (kind < 0 || kind > 2 || N < 1 || H <= 0 || T < 0) return 0;
+    if (kind < 0 || kind > 2 || N < 1 || H <= 0 || T < 0 || !within_limit(1, T, H, Dk)) return 0;
+    if (((long long)ceil_div(T, dr::kChunk) + N) * H > 0x7fffffffLL) return 0;
     if (C != dr::kChunk || dr_record_bytes(Dk, Dv, C, dtype) == 0) return 0;
     const VarlenLayout V = varlen_layout(N, T, H, Dk, dtype);
     const size_t core = (V.bytes - V.table) + bwd_layout_n((size_t)H * V.maxchunks, Dk, dtype).bytes;
@@ -294,7 +302,7 @@ size_t dr_record_bytes(int Dk, int Dv, int C, int dtype) {
 }
 
 size_t dr_record_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, int C, int dtype) {
-    if (kind < 0 || kind > 2 || B <= 0 || H <= 0 || T < 0) return 0;
+    if (kind < 0 || kind > 2 || B <= 0 || H <= 0 || T < 0 || !within_limit(B, T, H, Dk)) return 0;
     const size_t rec = dr_record_bytes(Dk, Dv, C, dtype);
     if (rec == 0) return 0;
     return (size_t)B * H * (size_t)ceil_div(T, C) * rec;
@@ -350,6 +358,9 @@ dr_status dr_intra(int kind, const void* q, const void* k, const void* v, const 
     if (T > 0 && (!workspace || workspace_bytes < dr_record_workspace_bytes(kind, B, T, H, Dk, Dv, C, dtype)))
         return DR_ERR_WORKSPACE;
     const Problem p = make_problem(kind, q, k, v, g, beta, nullptr, B, T, H, Dk, dtype, workspace, flags, C);
+    if ((s = poison_workspace(workspace, dr_record_workspace_bytes(kind, B, T, H, Dk, Dv, C, dtype),
+                              static_cast<hipStream_t>(stream))) != DR_OK)
+        return s;
     return launch_intra(p, 0, p.NT, static_cast<hipStream_t>(stream));
 }
 
@@ -369,7 +380,8 @@ dr_status dr_inter(int kind, const float* h0, void* o, float* hT, int B, int T, 
 }
 
 size_t dr_workspace_bytes_varlen(int kind, int N, int T, int H, int Dk, int Dv, int C, int dtype) {
-    if (kind < 0 || kind > 2 || N < 1 || H <= 0 || T < 0) return 0;
+    if (kind < 0 || kind > 2 || N < 1 || H <= 0 || T < 0 || !within_limit(1, T, H, Dk)) return 0;
+    if (((long long)ceil_div(T, dr::kChunk) + N) * H > 0x7fffffffLL) return 0;
     if (C != dr::kChunk || dr_record_bytes(Dk, Dv, C, dtype) == 0) return 0;
     return varlen_layout(N, T, H, Dk, dtype).bytes;
 }

@@ -22,7 +22,15 @@ inline dr_status check_launch() {
     return hipGetLastError() == hipSuccess ? DR_OK : DR_ERR_HIP;
 }
 
-inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+// (in 64-bit arithmetic: a may be as large as INT_MAX)
+inline int ceil_div(int a, int b) { return (int)(((long long)a + b - 1) / b); }
+
+// The largest problem any entry point or size query accepts: B*T*H*D
+// elements of one tensor at most 2^40 (evaluated in floating point, so that
+// no product of the four ints can overflow).
+inline bool within_limit(int B, int T, int H, int D) {
+    return (double)B * (double)T * (double)H * (double)D <= 1099511627776.0;
+}
 
 // 128-token chunks (sub-chunked records) are built for the dense forward in
 // bf16 at both head sizes and in fp32 at D = 64 (an fp32 D = 128 sub-chunk
@@ -51,7 +59,7 @@ inline dr_status validate(int kind, const void* q, const void* k, const void* v,
     if (Dk <= 0 || Dv <= 0 || C <= 0) return DR_ERR_INVALID_ARG;
     if (Dk != Dv || (Dk != 64 && Dk != 128)) return DR_ERR_UNSUPPORTED;
     if (C != dr::kChunk && !(allow128 && C == kChunk128 && chunk128_built(Dk, dtype))) return DR_ERR_UNSUPPORTED;
-    if ((long long)B * T * H * Dk > (1LL << 40)) return DR_ERR_INVALID_ARG;
+    if (!within_limit(B, T, H, Dk)) return DR_ERR_INVALID_ARG;
     if (T > 0 && (!q || !k || !v || !g)) return DR_ERR_INVALID_ARG;
     if (T > 0 && kind != DR_KIND_DECAY_LA && !beta) return DR_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(beta))
@@ -311,5 +319,9 @@ dr_status launch_prologue(bool backward, int kind, int D, int dtype, const void*
 dr_status launch_varlen_table(const int* cu_seqlens, int N, int T, int maxchunks, int4* table, int4* seqinfo,
                               int* total, unsigned* flags, hipStream_t st);                              // k_misc.hip
 dr_status launch_copy_or_zero(float* dst, const float* src, size_t n, hipStream_t st);                  // k_misc.hip
+// Debug aid: with the environment variable DR_POISON_WORKSPACE=1, fills the
+// first `bytes` of a workspace with NaN before an entry point's launches, so
+// that a read of workspace the call never wrote shows as NaN in the results.
+dr_status poison_workspace(void* ws, size_t bytes, hipStream_t st);                                     // k_misc.hip
 
 }  // namespace drh

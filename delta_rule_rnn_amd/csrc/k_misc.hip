@@ -96,6 +96,15 @@ dr_status launch_varlen_table(const int* cu_seqlens, int N, int T, int maxchunks
     return check_launch();
 }
 
+dr_status poison_workspace(void* ws, size_t bytes, hipStream_t st) {
+    const char* e = getenv("DR_POISON_WORKSPACE");
+    if (!e || e[0] != '1' || !ws || bytes < 4) return DR_OK;
+    const size_t n = bytes / 4;
+    const size_t blocks = std::min<size_t>((n + 255) / 256, 65536);
+    hipLaunchKernelGGL(dr::poison_kernel, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<uint32_t*>(ws), n);
+    return check_launch();
+}
+
 dr_status launch_copy_or_zero(float* dst, const float* src, size_t n, hipStream_t st) {
     if (n == 0) return DR_OK;
     hipLaunchKernelGGL(dr::copy_or_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dst, src, n);

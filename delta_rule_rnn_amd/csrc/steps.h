@@ -168,6 +168,13 @@ __global__ __launch_bounds__(1024) void varlen_table_kernel(const int* __restric
 
 // dst[i] = src ? src[i] : 0 for i < n (a fill that graph capture records as
 // a kernel node).
+// Debug fill: every 32-bit word of [p, p + 4 * n) set to all ones (a NaN
+// as fp32, and two NaNs as bf16), grid-stride.
+__global__ __launch_bounds__(256) void poison_kernel(uint32_t* __restrict__ p, size_t n)
+{
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0xFFFFFFFFu;
+}
+
 __global__ __launch_bounds__(256) void copy_or_zero_kernel(float* __restrict__ dst, const float* __restrict__ src,
                                                            size_t n)
 {

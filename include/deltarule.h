@@ -45,6 +45,12 @@
  *     last chunk is masked.
  *   Streams: `stream` is a hipStream_t (0 = the null stream).  All work is
  *     enqueued on it; nothing synchronises with the host.
+ *   Debugging: with the environment variable DR_POISON_WORKSPACE=1 every
+ *     entry point that takes a workspace first fills it with NaN (all-ones
+ *     32-bit words, on `stream`), so that a kernel reading workspace the
+ *     call has not written shows as NaN in the results.  (Stages 1 and 2 of
+ *     dr_forward_stage and dr_inter read what an earlier call wrote and do
+ *     not poison.)
  *   Errors: argument problems are detected on the host and return a negative
  *     status with nothing enqueued.  A failed launch returns DR_ERR_HIP.
  *     No exception crosses the ABI.  All entry points are reentrant; calls

@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "deltarule.h")
 @pytest.fixture(scope="module")
 def lib():
     from delta_rule_rnn_amd import _lib
-    if not os.path.exists(_lib.LIB_PATH):
+    if not os.environ.get("DR_LIBRARY") and not os.path.exists(_lib.LIB_PATH):
         from delta_rule_rnn_amd.build import build_library
         build_library()
     return _lib.load()
@@ -244,3 +244,31 @@ def test_backward_varlen_rejects(lib):
     assert bwd(N=1 << 30) == -2                  # grids past 2^31 workgroups, refused before any launch
     assert bwd(ws=None) == -4
     assert bwd(wsb=need - 1) == -4
+
+
+def test_size_queries_at_extreme_sizes(lib):
+    """Every size query at INT_MAX and other extreme sizes: 0 where q would
+    hold more than 2^40 elements, else the exact size (no overflow; with the
+    host sanitizer build these also run under UndefinedBehaviorSanitizer)."""
+    big = 2147483647
+    for B, T, H in ((1, big, 1), (big, big, big), (big, 1, 1), (1, 1, big), (2, 1 << 30, 8), (big, big, 1)):
+        ok = B * T * H * 128 <= (1 << 40)
+        for C in (64, 128):
+            rec = lib.dr_record_bytes(128, 128, C, 1)
+            want = B * H * (-(-T // C)) * rec if ok else 0
+            assert lib.dr_record_workspace_bytes(1, B, T, H, 128, 128, C, 1) == want
+            assert lib.dr_workspace_bytes(0, B, T, H, 128, 128, C, 1) == want
+            assert (lib.dr_segment_workspace_bytes(0, B, T, H, 128, 128, C, 1) > 0) == (ok and C == 64)
+        okb = B * T * H * 64 <= (1 << 40)
+        assert (lib.dr_backward_workspace_bytes(1, B, T, H, 64, 64, 64, 1) > 0) == okb
+        assert (lib.dr_backward_prologue_workspace_bytes(1, B, T, H, 64, 64, 64, 1) > 0) == okb
+        okv = T * H * 64 <= (1 << 40) and ((-(-T // 64)) + B) * H <= big
+        assert (lib.dr_workspace_bytes_varlen(0, B, T, H, 64, 64, 64, 1) > 0) == okv
+        assert (lib.dr_backward_varlen_workspace_bytes(0, B, T, H, 64, 64, 64, 1, 1) > 0) == okv
+    # the largest accepted problem (2^40 elements of q) and one token more
+    T = (1 << 40) // (128 * 128)
+    assert lib.dr_workspace_bytes(0, 1, T, 128, 128, 128, 64, 1) > 0
+    assert lib.dr_workspace_bytes(0, 1, T + 1, 128, 128, 128, 64, 1) == 0
+    # entry points reject the same sizes on the host
+    assert lib.kda_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, big, big, big, 64, 64, 64, 1, FAKE,
+                       1 << 30, None, None) == -1
