@@ -270,11 +270,11 @@ struct SegLayout {
 // Whether the segment kernel is built for these sizes (fp32 at D = 128
 // does not fit its LDS plan).
 inline bool seg_built(int D, int dtype) { return dtype == DR_BF16 || D == 64; }
-// The path the forward entry points take: the record path unless
-// DR_FWD_PATH=segment selects the segment-parallel one (where it is built).
+// The path the forward entry points take: the segment-parallel one where it
+// is built, unless DR_FWD_PATH=records selects the record path.
 inline bool seg_supported(int D, int dtype) {
     const char* e = getenv("DR_FWD_PATH");
-    return e != nullptr && e[0] == 's' && seg_built(D, dtype);
+    return !(e != nullptr && e[0] == 'r') && seg_built(D, dtype);
 }
 inline SegLayout seg_layout(int B, int T, int H, int D, int dtype) {
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };

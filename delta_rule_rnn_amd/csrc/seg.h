@@ -753,57 +753,75 @@ __global__ __launch_bounds__(kSegThreads, 1) void seg_kernel(
 // compose_kernel: per (chain, 16 value columns): S = N_0 (segment 0 began at
 // the true initial state); for r = 1 .. NS-1: S_in[r] = S, written transposed
 // in the I/O type for correct_kernel, then S <- M_r S + N_r.  Finally hT = S.
-// fp32 throughout (FMA on the vector ALUs); 256 threads, thread t owns row
-// t / 2 and 8 of the 16 columns.
+// fp32 MFMA (16x16x4) with fp32 operands; 256 threads, wave w owns the row
+// tiles w*TPW .. of S (accumulators).  M_r does not depend on S, so the rows
+// of the next segment's [M | N] are loaded into registers while the current
+// product runs.
 constexpr int kComposeThreads = 256;
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(kComposeThreads) void compose_kernel(const float* __restrict__ xend,
                                                                   T* __restrict__ sinT, float* __restrict__ hT,
                                                                   int NS)
 {
-    static_assert(DK <= 128, "rows per thread");
+    constexpr int LDX = DK + DV, NKB = DK / 32, NRT = DK / 16, TPW = NRT / 4;
+    constexpr int LDT = DK + 4;      // padded row of S^T in LDS
     constexpr int NSL = DV / 16;
-    constexpr int LDX = DK + DV;
-    __shared__ __attribute__((aligned(16))) float sS[DK][16];
-    const int tid = threadIdx.x;
+    static_assert(NRT % 4 == 0, "row tiles per wave");
+    __shared__ __attribute__((aligned(16))) float sST[16 * LDT];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, grp = lane >> 4;
     const int chain = blockIdx.x / NSL, c0 = (blockIdx.x % NSL) * 16;
-    const int row = tid >> 1, half = tid & 1;
-    const bool act = row < DK;
     const float* xe0 = xend + (size_t)chain * NS * DK * LDX;
-    float s[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) s[j] = act ? xe0[(size_t)row * LDX + DK + c0 + 8 * half + j] : 0.f;
-    for (int rr = 1; rr < NS; ++rr) {
-        if (act) {
-            T* dst = sinT + ((size_t)chain * NS + rr) * DV * DK;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) dst[(size_t)(c0 + 8 * half + j) * DK + row] = from_f<T>(s[j]);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) sS[row][8 * half + j] = s[j];
-        }
-        __syncthreads();
+    struct Ops {
+        Frag<float> m[TPW][NKB];   // rows of M_r (A fragments)
+        float n[TPW][4];           // N_r at this lane's accumulator slots
+    };
+    auto trow = [&](int t) { return 16 * (wave * TPW + t); };
+    auto load = [&](Ops& op, int rr) {
         const float* xe = xe0 + (size_t)rr * DK * LDX;
-        float acc[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = act ? xe[(size_t)row * LDX + DK + c0 + 8 * half + j] : 0.f;
-        if (act) {
-            const float* mrow = xe + (size_t)row * LDX;
-            for (int kk = 0; kk < DK; kk += 4) {
-                const float4 m4 = *reinterpret_cast<const float4*>(mrow + kk);
-                const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
+        for (int t = 0; t < TPW; ++t) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
+            for (int kb = 0; kb < NKB; ++kb)
+                op.m[t][kb] = ld_frag(xe + (size_t)(trow(t) + r16) * LDX + 32 * kb + 8 * grp);
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) acc[j] = fmaf(mv[e], sS[kk + e][8 * half + j], acc[j]);
-            }
+            for (int i = 0; i < 4; ++i) op.n[t][i] = xe[(size_t)(trow(t) + 4 * grp + i) * LDX + DK + c0 + r16];
         }
-        __syncthreads();
+    };
+    f32x4 S[TPW];
+    {
+        Ops first;
+        load(first, 0);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) s[j] = acc[j];
+        for (int t = 0; t < TPW; ++t) S[t] = f32x4{first.n[t][0], first.n[t][1], first.n[t][2], first.n[t][3]};
     }
-    if (act && hT != nullptr) {
+    Ops cur, nxt;
+    if (NS > 1) load(cur, 1);
+    for (int rr = 1; rr < NS; ++rr) {
+        load(nxt, min(rr + 1, NS - 1));
+        T* dst = sinT + ((size_t)chain * NS + rr) * DV * DK + (size_t)(c0 + r16) * DK;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) hT[((size_t)chain * DK + row) * DV + c0 + 8 * half + j] = s[j];
+        for (int t = 0; t < TPW; ++t) {
+            const float v4[4] = {S[t][0], S[t][1], S[t][2], S[t][3]};
+            st4(dst + trow(t) + 4 * grp, v4);
+            *reinterpret_cast<f32x4*>(sST + r16 * LDT + trow(t) + 4 * grp) = S[t];
+        }
+        lds_barrier();
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            f32x4 acc = {cur.n[t][0], cur.n[t][1], cur.n[t][2], cur.n[t][3]};
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) mma(acc, cur.m[t][kb], ld_frag(sST + r16 * LDT + 32 * kb + 8 * grp));
+            S[t] = acc;
+        }
+        lds_barrier();
+        cur = nxt;
+    }
+    if (hT != nullptr) {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hT[((size_t)chain * DK + trow(t) + 4 * grp + i) * DV + c0 + r16] = S[t][i];
     }
 }
 
@@ -811,11 +829,12 @@ __global__ __launch_bounds__(kComposeThreads) void compose_kernel(const float* _
 // correct_kernel: o[c] += q_eff[c] S_in[r] for the chunks c of segments
 // r >= 1.  One 256-thread workgroup per (chain, segment r >= 1, group of
 // kCorrChunks chunks of it): S_in^T (I/O dtype, [DV][DK]) is staged in LDS
-// once, then each chunk's q_eff and o stream through registers, the next
-// chunk's loaded while the current one is multiplied.  Wave w owns the 16
-// positions 16 w ..; lanes hold 4 consecutive value columns of one position
-// (O^T = S_in^T q_eff^T on MFMA), so o is read and written 8 (bf16) or 16
-// (fp32) bytes per lane and tile.
+// once; wave w owns the 16 positions 16 w .. of every chunk.  Per chunk the
+// wave forms its [16][DV] correction on MFMA (O^T = S_in^T q_eff^T), parks
+// it in its own fp32 LDS slab, and then reads, adds and writes o by whole
+// rows, 16 bytes per lane (16 lanes cover a bf16 row of 128 values).  The
+// next chunk's q_eff and o rows are loaded while the current one is
+// processed.
 constexpr int kCorrChunks = 8;
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(kThreads) void correct_kernel(const T* __restrict__ qeff, const T* __restrict__ sinT,
@@ -826,7 +845,15 @@ __global__ __launch_bounds__(kThreads) void correct_kernel(const T* __restrict__
     constexpr int NKB = DK / 32;
     constexpr int NCT = DV / 16;           // 16-column tiles
     constexpr int LDS_ = DK + 8;           // padded row of S_in^T in LDS
+    constexpr int LDO = DV + 4;            // padded row of a correction slab (floats)
+    constexpr int EPL = 16 / sizeof(T);    // o elements per lane and access (16 bytes)
+    constexpr int LPR = DV / EPL;          // lanes per o row
+    constexpr int RPI = 64 / LPR;          // rows per wave-wide access
+    constexpr int NIT = 16 / RPI;          // accesses for the wave's 16 rows
+    static_assert(64 % LPR == 0 && 16 % RPI == 0, "row split");
+    using V16 = typename VecOf<T, EPL>::type;
     __shared__ __attribute__((aligned(16))) T sS[DV * LDS_];
+    __shared__ __attribute__((aligned(16))) float sO[4][16 * LDO];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, grp = lane >> 4;
@@ -846,6 +873,7 @@ __global__ __launch_bounds__(kThreads) void correct_kernel(const T* __restrict__
         st_frag(sS + row * LDS_ + col, ld_frag(S + e));
     }
     lds_barrier();
+    float* slab = sO[wave];
     const int pos = 16 * wave + r16;
     const unsigned ostr = (unsigned)(H * DV);
     auto load_q = [&](Frag<T> (&fq)[NKB], int c) {
@@ -857,19 +885,32 @@ __global__ __launch_bounds__(kThreads) void correct_kernel(const T* __restrict__
         return buffer_rsrc(o + (((size_t)b * Tlen + (size_t)c * C) * H + h) * DV,
                            (unsigned)(min(C, Tlen - c * C) * H * DV * sizeof(T)));
     };
+    // this lane's o accesses: row 16 w + it*RPI + lane/LPR, elements
+    // EPL*(lane%LPR) .. (rows past the end are dropped: read as zero, not
+    // written)
+    const int orow0 = 16 * wave + lane / LPR, ocol = EPL * (lane % LPR);
+    auto ooff = [&](int it) { return ((unsigned)(orow0 + it * RPI) * ostr + (unsigned)ocol) * (unsigned)sizeof(T); };
+    using U4 = unsigned __attribute__((ext_vector_type(4)));
+    auto load_o = [&](U4 (&ov)[NIT], int c) {
+        const auto rs = orsrc_of(c);
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) ov[it] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)ooff(it), 0, 0);
+    };
     Frag<T> fq[NKB];
+    U4 on[NIT];
     load_q(fq, c0);
+    load_o(on, c0);
     for (int c = c0; c < c1; ++c) {
         Frag<T> cur[NKB];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) cur[kb] = fq[kb];
-        load_q(fq, min(c + 1, c1 - 1));
-        const auto rs = orsrc_of(c);
-        const unsigned obase = ((unsigned)pos * ostr + 4u * grp) * (unsigned)sizeof(T);
-        // current o, read before the products (dropped rows read as zero)
-        Raw4<T> oc[NCT];
+        U4 oc[NIT];
 #pragma unroll
-        for (int n = 0; n < NCT; ++n) oc[n] = buf_ld4(rs, obase + 16u * n * (unsigned)sizeof(T), (const T*)nullptr);
+        for (int it = 0; it < NIT; ++it) oc[it] = on[it];
+        // (the last chunk reloads itself: the loads stay unconditional, and
+        // the reload of o precedes this chunk's store)
+        load_q(fq, min(c + 1, c1 - 1));
+        load_o(on, min(c + 1, c1 - 1));
         f32x4 acc[NCT];
 #pragma unroll
         for (int n = 0; n < NCT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -878,12 +919,24 @@ __global__ __launch_bounds__(kThreads) void correct_kernel(const T* __restrict__
 #pragma unroll
             for (int n = 0; n < NCT; ++n)
                 mma(acc[n], ld_frag(sS + (16 * n + r16) * LDS_ + 32 * kb + 8 * grp), cur[kb]);
+        // the wave's [16][DV] correction, row r16, columns 16n + 4(l/16) ..
 #pragma unroll
-        for (int n = 0; n < NCT; ++n) {
-            const float z4[4] = {oc[n][0] + acc[n][0], oc[n][1] + acc[n][1], oc[n][2] + acc[n][2],
-                                 oc[n][3] + acc[n][3]};
-            buf_st4(rs, obase + 16u * n * (unsigned)sizeof(T), (const T*)nullptr, z4);
+        for (int n = 0; n < NCT; ++n) *reinterpret_cast<f32x4*>(slab + r16 * LDO + 16 * n + 4 * grp) = acc[n];
+        // LDS accesses of one wave complete in order: the reads below see
+        // the writes above (of other lanes of this wave)
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const auto rs = orsrc_of(c);
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const float* src = slab + (lane / LPR + it * RPI) * LDO + ocol;
+            const V16 x = __builtin_bit_cast(V16, oc[it]);
+            V16 y;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) y[e] = from_f<T>(to_f(x[e]) + src[e]);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(U4, y), rs, (int)ooff(it), 0, 0);
         }
+        // the slab is rewritten for the next chunk only after these reads
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
 }
 

@@ -124,9 +124,10 @@ size_t dr_record_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, 
  * exponent prep, the UT transform, the state pass and the chunk output.
  * Page sections: "TileLang 实战：KDA 从零到一–Kimi Delta Attention" sections
  * 1.2, 3.2, 3.3; "RNN的复兴04" (DPLR) section 5.3.5.
- * Two execution paths compute the same result (to rounding); the record
- * path runs unless the environment variable DR_FWD_PATH=segment selects the
- * segment-parallel one where it is built:
+ * Two execution paths compute the same result (to rounding).  The
+ * segment-parallel one runs where it is built (C == 64 with bf16 I/O, or
+ * fp32 I/O at Dk = 64) unless the environment variable DR_FWD_PATH=records
+ * selects the record path; the record path runs everywhere else:
  *   segment-parallel (bf16 I/O, and fp32 I/O at Dk = 64): the chunks of each
  *     (b, h) are grouped into segments (sizes chosen from B*H and T only).
  *     One kernel runs every segment from the entry state [I | 0], carrying

@@ -47,7 +47,7 @@ def test_status_strings(lib):
     assert lib.dr_status_string(7) == b"unknown status"
 
 
-def test_workspace_sizes(lib):
+def test_workspace_sizes(lib, monkeypatch):
     # one record per (b, h, chunk); bf16 D=128 record: (3*64*128 + 64*64 + 128*64)*2 + 128*4
     rec = lib.dr_record_bytes(128, 128, 64, 1)
     assert rec == ((3 * 64 * 128 + 64 * 64 + 128 * 64) * 2 + 128 * 4 + 255) // 256 * 256
@@ -62,7 +62,12 @@ def test_workspace_sizes(lib):
     assert lib.dr_segment_workspace_bytes(0, 2, 130, 3, 128, 128, 64, 1) == want
     # not built for fp32 at D = 128
     assert lib.dr_segment_workspace_bytes(0, 2, 130, 3, 128, 128, 64, 0) == 0
-    # the forward's own workspace: the record path by default
+    # the forward's own workspace: the segment-parallel path's by default,
+    # the record path's with DR_FWD_PATH=records and where the segment path
+    # is not built
+    assert lib.dr_workspace_bytes(0, 2, 130, 3, 128, 128, 64, 1) == want
+    assert lib.dr_workspace_bytes(0, 2, 130, 3, 128, 128, 64, 0) == 2 * 3 * 3 * lib.dr_record_bytes(128, 128, 64, 0)
+    monkeypatch.setenv("DR_FWD_PATH", "records")
     assert lib.dr_workspace_bytes(0, 2, 130, 3, 128, 128, 64, 1) == 2 * 3 * 3 * rec
     assert lib.dr_record_bytes(96, 96, 64, 1) == 0
     assert lib.dr_record_bytes(128, 64, 64, 1) == 0
@@ -246,11 +251,12 @@ def test_backward_varlen_rejects(lib):
     assert bwd(wsb=need - 1) == -4
 
 
-def test_size_queries_at_extreme_sizes(lib):
+def test_size_queries_at_extreme_sizes(lib, monkeypatch):
     """Every size query at INT_MAX and other extreme sizes: 0 where q would
     hold more than 2^40 elements, else the exact size (no overflow; with the
     host sanitizer build these also run under UndefinedBehaviorSanitizer)."""
     big = 2147483647
+    monkeypatch.setenv("DR_FWD_PATH", "records")     # dr_workspace_bytes = the record workspace
     for B, T, H in ((1, big, 1), (big, big, big), (big, 1, 1), (1, 1, big), (2, 1 << 30, 8), (big, big, 1)):
         ok = B * T * H * 128 <= (1 << 40)
         for C in (64, 128):

@@ -88,7 +88,7 @@ def fwd_path(request, monkeypatch):
     if request.param == "segment":
         monkeypatch.setenv("DR_FWD_PATH", "segment")
     else:
-        monkeypatch.delenv("DR_FWD_PATH", raising=False)
+        monkeypatch.setenv("DR_FWD_PATH", "records")
     return request.param
 
 
@@ -200,7 +200,7 @@ def test_state_pass_layouts_agree(kind, dt, monkeypatch):
     dra = _ops()
     w = Workload(f"{kind}_layouts", kind, dt, B=2, H=3, T=64 * 5 + 9, Dk=128, Dv=128, h0_std=0.1, seed=9)
     x = to_dev(generate(w))
-    monkeypatch.delenv("DR_FWD_PATH", raising=False)
+    monkeypatch.setenv("DR_FWD_PATH", "records")
     monkeypatch.setenv("DR_INTER_NTN", "1")
     monkeypatch.setenv("DR_INTER_PFD", "0")
     o1, h1 = dra.forward(kind, x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"])
@@ -297,7 +297,7 @@ def test_step_a3_records(kind, dt, D):
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_inter_from_records_matches_forward(dt, monkeypatch):
-    monkeypatch.delenv("DR_FWD_PATH", raising=False)
+    monkeypatch.setenv("DR_FWD_PATH", "records")
     dra = _ops()
     w = Workload("split", "kda", dt, B=2, H=2, T=300, Dk=128, Dv=128, h0_std=0.1, seed=8)
     d = to_dev(generate(w))
@@ -400,7 +400,7 @@ def test_workload_full_size(name, path, monkeypatch):
     if path == "segment":
         monkeypatch.setenv("DR_FWD_PATH", "segment")
     else:
-        monkeypatch.delenv("DR_FWD_PATH", raising=False)
+        monkeypatch.setenv("DR_FWD_PATH", "records")
     w = WORKLOADS[name]
     x = generate(w)
     print(f"{name} ({path}): inputs generated", flush=True)

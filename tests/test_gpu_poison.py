@@ -49,7 +49,7 @@ def test_forward_poisoned_workspace(kind, dt, D, C, path, monkeypatch):
     if path == "segment":
         monkeypatch.setenv("DR_FWD_PATH", "segment")
     else:
-        monkeypatch.delenv("DR_FWD_PATH", raising=False)
+        monkeypatch.setenv("DR_FWD_PATH", "records")
     w = Workload(f"poison_{kind}", kind, dt, B=2, H=3, T=300, Dk=D, Dv=D, h0_std=0.1, seed=61)
     d = to_dev(generate(w))
     kw = {} if kind == "decay_la" else {"flags": torch.zeros(1, dtype=torch.int32, device="cuda:0")}

@@ -69,7 +69,7 @@ def test_varlen_matches_oracle_per_sequence(kind, dt, D):
 def test_equal_lengths_match_dense_batch(kind, L, monkeypatch):
     """Packing B sequences of one length reproduces the dense [B, L] forward
     of the record path (the path packed sequences take) bit for bit."""
-    monkeypatch.delenv("DR_FWD_PATH", raising=False)
+    monkeypatch.setenv("DR_FWD_PATH", "records")
     dra = _ops()
     B, H = 3, 4
     w = Workload(f"{kind}_dense", kind, "bf16", B=B, H=H, T=L, Dk=128, Dv=128, h0_std=0.1, seed=33)
