@@ -147,6 +147,7 @@ def cpu_baseline(w, x, max_tokens: int, threads: int):
     del torch
     tokens = w.B * Ts
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
             "sample": f"{w.kind} B={w.B} H={w.H} first {Ts} of {w.T} tokens, fp64 token recurrence, "
                       f"{threads} threads, {dt:.2f} s wall", "cpu": cpu_model()}
 
@@ -216,7 +217,14 @@ def time_calls(call, steps: int, warmup: int):
 
 
 def cpu_threads(args) -> int:
-    return args.cpu_threads or min(16, len(os.sched_getaffinity(0)))
+    """Threads of the CPU oracle: every core this process may use (its
+    affinity mask, bounded by OMP_NUM_THREADS where the host sets the job's
+    CPU share that way)."""
+    n = len(os.sched_getaffinity(0))
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    if share.isdigit() and int(share) > 0:
+        n = min(n, int(share))
+    return args.cpu_threads or n
 
 
 def cpu_baseline_backward(kind, x, do, dhT, Ts: int):
@@ -552,6 +560,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="kda_bf16_long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gdn", action="store_true",
+                    help="leave out the GDN workload that the KDA benchmark line carries in `extra`")
     ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens of the workload the CPU oracle is timed on")
     ap.add_argument("--cpu-bwd-tokens", type=int, default=2048,
@@ -563,7 +573,9 @@ def main():
                          "packed sequences of mixed lengths with the workload's token count; "
                          "prologue: the forward with the fused input prologue on raw inputs; "
                          "backward: all gradients of the forward")
-    ap.add_argument("--decode-batch", type=int, default=64, help="sequences per decode call")
+    ap.add_argument("--decode-batch", type=int, default=256,
+                    help="sequences per decode call (256 x H=32 fp32 states = 537 MB, beyond the 256 MB "
+                         "last-level cache)")
     ap.add_argument("--decode-tokens", type=int, default=1, help="new tokens per sequence per call")
     ap.add_argument("--path", choices=("segment", "records"), default="segment",
                     help="segment: the forward entry points' segment-parallel launches (the "
@@ -610,16 +622,57 @@ def main():
         backward_varlen_bench(args)
         return
 
-    import torch
-    import delta_rule_rnn_amd as dra
-    from delta_rule_rnn_amd import ops
-    from delta_rule_rnn_amd.inputs import WORKLOADS, generate
+    from delta_rule_rnn_amd.inputs import WORKLOADS
 
     w = WORKLOADS[args.workload]
     if args.chunk:
         w = w.with_(C=args.chunk)
     if w.C != 64:
         args.path = "records"
+    r = time_forward(w, args.path, args.steps, args.warmup, args.workload)
+    # the metric names KDA and GDN: the scalar-gate workload of the same
+    # shape, timed the same way, rides along (not part of `value`)
+    extra = {}
+    if args.workload == "kda_bf16_long" and not args.no_gdn:
+        wg = WORKLOADS["gdn_bf16_long"].with_(C=w.C)
+        rg = time_forward(wg, args.path, args.steps, args.warmup, "gdn_bf16_long")
+        extra["gdn_bf16_long"] = {"workload": rg["workload"], "value": rg["value"], "unit": "tokens/s",
+                                  "ms_per_step": rg["ms"], "roofline": rg["roof"]}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, r["x"], args.cpu_tokens, cpu_threads(args))
+
+    line = {
+        "metric": METRIC, "value": r["value"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["ms"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": r["dtype"], "data": "synthetic",
+        "config": {"workload": r["workload"], "path": args.path,
+                   "global_batch": w.B, "seq_len": w.T, "heads": w.H, "parallelism": "single GPU",
+                   "gate": f"a ~ U[{w.gate_lo}, {w.gate_hi}]"},
+        "median_ms_per_step_events": r["median_ev"],
+        "min_ms_per_step_events": r["min_ev"],
+        "mall_flushed": {"median_ms": r["cold_median"], "min_ms": r["cold_min"],
+                         "note": "512 MB written before each step, outside its events"},
+        "mfma_frac_bf16": r["mfma_frac"],
+        "roofline": r["roof"],
+        "cpu_baseline": cpu,
+        "gate_flags": r["flags"],
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def time_forward(w, path: str, steps: int, warmup: int, workload_name: str) -> dict:
+    """One workload's forward on `path`: warmup, then `steps` timed steps
+    (wall clock around all of them, HIP events per launch on the launch
+    stream), then the same steps with the last-level cache flushed; the
+    roofline of the dominant kernel."""
+    import torch
+    import delta_rule_rnn_amd as dra
+    from delta_rule_rnn_amd import ops
+    from delta_rule_rnn_amd.inputs import generate
+
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     x = generate(w)
@@ -632,7 +685,7 @@ def main():
     stream = torch.cuda.current_stream()
     io_b = 2 if io == torch.bfloat16 else 4
     th = B * T * H
-    if args.path == "segment":
+    if path == "segment":
         # the three launches of the forward entry points (dr_forward_stage
         # 0, 1, 2): local segment pass, entry-state composition, correction
         ws = ops.alloc_segment_workspace(w.kind, d["q"], d["v"], w.C)
@@ -669,14 +722,14 @@ def main():
             if ev is not None:
                 ev[i + 1].record(stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nl + 1)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nl + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -687,7 +740,7 @@ def main():
     # each one by a 512 MB write; only the step itself is inside the events
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     cold = []
-    for _ in range(args.steps):
+    for _ in range(steps):
         flush.fill_(1)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(nl + 1)]
         step(ev)
@@ -695,13 +748,12 @@ def main():
         cold.append(ev[0].elapsed_time(ev[nl]))
     cold.sort()
     del flush
-    ms = wall * 1000.0 / args.steps
-    tokens = B * T
-    value = tokens / (ms / 1000.0)
+    ms = wall * 1000.0 / steps
+    value = B * T / (ms / 1000.0)
 
     kern = {n: {"avg_ms": kms[n], "bytes": kbytes[n], "gbs": kbytes[n] / (kms[n] * 1e-3) / 1e9} for n in names}
     dom = max(kern, key=lambda n: kern[n]["avg_ms"])
-    traffic = measured_traffic(args.workload, args.path)
+    traffic = measured_traffic(workload_name + ("_c128" if w.C != 64 else ""), path)
     roof = {"bound": "hbm", "kernel": dom, "achieved": round(kern[dom]["gbs"], 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(kern[dom]["gbs"] / HBM_PEAK_GBS, 4),
             "traffic": traffic.get(dom),
@@ -709,30 +761,12 @@ def main():
                                "achieved_GBs": round(v["gbs"], 1), "traffic": traffic.get(n)}
                            for n, v in kern.items()}}
     mfma_frac = flops * th / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        threads = args.cpu_threads or min(16, len(os.sched_getaffinity(0)))
-        cpu = cpu_baseline(w, x, args.cpu_tokens, threads)
-
-    line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if io == torch.bfloat16 else "f32", "data": "synthetic",
-        "config": {"workload": f"{w.kind}_fwd B={B} H={H} T={T} dk={Dk} dv={Dv} C={w.C}", "path": args.path,
-                   "global_batch": B, "seq_len": T, "heads": H, "parallelism": "single GPU",
-                   "gate": f"a ~ U[{w.gate_lo}, {w.gate_hi}]"},
-        "median_ms_per_step_events": round(per_step[len(per_step) // 2], 4),
-        "min_ms_per_step_events": round(per_step[0], 4),
-        "mall_flushed": {"median_ms": round(cold[len(cold) // 2], 4), "min_ms": round(cold[0], 4),
-                         "note": "512 MB written before each step, outside its events"},
-        "mfma_frac_bf16": round(mfma_frac, 4),
-        "roofline": roof,
-        "cpu_baseline": cpu,
-        "gate_flags": int(flags.item()),
-    }
-    print(json.dumps(line), flush=True)
+    return {"x": x, "value": round(value, 1), "ms": round(ms, 4), "roof": roof,
+            "dtype": "bf16" if io == torch.bfloat16 else "f32",
+            "workload": f"{w.kind}_fwd B={B} H={H} T={T} dk={Dk} dv={Dv} C={w.C}",
+            "median_ev": round(per_step[len(per_step) // 2], 4), "min_ev": round(per_step[0], 4),
+            "cold_median": round(cold[len(cold) // 2], 4), "cold_min": round(cold[0], 4),
+            "mfma_frac": round(mfma_frac, 4), "flags": int(flags.item())}
 
 
 if __name__ == "__main__":
