@@ -112,3 +112,34 @@ def test_random_packed_forward_backward(seed):
             assert_close_grad(val[:, a:b], ref[name], dt, f"{what} seq {i} {name}")
         if kind != "decay_la":
             assert_close_grad(got[4][:, a:b], ref["dbeta"], dt, f"{what} seq {i} dbeta")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_forward_path_and_chunk(seed, monkeypatch):
+    """The forward over random shapes on a random path (segment-parallel or
+    record) and chunk size (64, or 128 where built), long enough for many
+    segments (up to 40 chunks per chain, so segments of one or a few
+    chunks), against the oracle."""
+    dra = _ops()
+    r = random.Random(5000 + seed)
+    kind = r.choice(["kda", "gdn", "decay_la"])
+    dt = r.choice(["f32", "bf16"])
+    D = r.choice([64, 128])
+    C = r.choice([64, 128]) if (dt == "bf16" or D == 64) else 64
+    path = r.choice(["segment", "records"])
+    B, H = r.randint(1, 3), r.randint(1, 4)
+    T = r.choice([r.randint(1, 130), r.randint(131, 2500)])
+    use_h0 = r.random() < 0.7
+    monkeypatch.setenv("DR_FWD_PATH", path)
+    w = Workload(f"randp{seed}", kind, dt, B=B, H=H, T=T, Dk=D, Dv=D, h0_std=0.2 if use_h0 else 0.0,
+                 seed=6000 + seed)
+    x = generate(w)
+    d = to_dev(x)
+    what = f"seed {seed}: {kind} {dt} D{D} C{C} {path} B{B} H{H} T{T} h0={use_h0}"
+    print(what, flush=True)
+    o, hT = dra.forward(kind, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], chunk_size=C)
+    torch.cuda.synchronize()
+    h0 = None if x["h0"] is None else x["h0"].transpose(-1, -2)
+    ro, rs = oracle.recurrence(kind, x["q"], x["k"], x["v"], x["g"], x["beta"], h0)
+    assert_close(o.float().cpu().numpy(), ro, dt, f"{what} output")
+    assert_close(hT.cpu().numpy(), np.swapaxes(rs, -1, -2), dt, f"{what} state")
