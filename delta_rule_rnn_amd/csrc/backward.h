@@ -75,6 +75,19 @@ struct Prep {
     static constexpr size_t FLOATS = GAM + (size_t)C * DK;
 };
 
+// bf16 operands of one chunk for the segment-parallel reverse pass
+// (revseg.h), written by bwd_prep_kernel for bf16 I/O in the layouts that
+// pass stages into LDS: every product there reduces along contiguous
+// elements.
+template <int DK>
+struct RevRec {
+    static constexpr size_t KB = 0;                         // [C][DK]  Kbar
+    static constexpr size_t AT = KB + (size_t)C * DK;       // [C][C]   Aqk^T: AT[i][j] = Aqk[j][i]
+    static constexpr size_t QT = AT + (size_t)C * C;        // [DK][C]  Q~^T
+    static constexpr size_t WT = QT + (size_t)DK * C;       // [DK][C]  W^T
+    static constexpr size_t ELEMS = WT + (size_t)DK * C;    // bf16 elements
+};
+
 // Packed sequences (table == null: the dense [B, T] layout).  The chunk table
 // and sequence descriptors are those of the packed forward
 // (varlen_table_kernel): table[slot] = {sequence, first token, valid rows, -},
@@ -360,9 +373,10 @@ template <int KIND, typename T, int DK>
 __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                        const float* __restrict__ g,
                                                        const float* __restrict__ beta, float* __restrict__ prep,
-                                                       int Tlen, int H, int NT, Pack pk)
+                                                       bf16* __restrict__ rrec, int Tlen, int H, int NT, Pack pk)
 {
     using P = Prep<DK>;
+    using RR = RevRec<DK>;
     using SM = PrepSmem<KIND, T, DK>;
     constexpr int DV = DK, LDK = SM::LDK, NTH = kPrepThreads, NW = NTH / 64;
     constexpr bool DELTA = KIND != KIND_LA;
@@ -383,6 +397,8 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const T* __restr
     const int nvalid = loc.nvalid;
     const size_t row0 = loc.row0;   // token row of position 0
     float* out = prep + loc.ci * P::FLOATS;
+    // the bf16 record of the segment-parallel reverse pass (null: not used)
+    bf16* rr = rrec ? rrec + loc.ci * RR::ELEMS : nullptr;
 
     // ---- inputs, rows past the end of a ragged chunk zero
     #pragma unroll 8
@@ -449,8 +465,10 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const T* __restr
         const float phi = sPhi[d];
         for (int j = 0; j < RB; ++j) {
             const int r = b * RB + j;
-            out[P::KB + (size_t)r * DK + d] = sB[r * LDK + d] * phi;
+            const float kb = sB[r * LDK + d] * phi;
+            out[P::KB + (size_t)r * DK + d] = kb;
             out[P::QT + (size_t)r * DK + d] = sQ[r * LDK + d];
+            if (rr) rr[RR::KB + (size_t)r * DK + d] = (bf16)kb;
         }
     } else {
         if (wave == 0) {
@@ -471,7 +489,9 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const T* __restr
             const int idx = tid + it_ * NTH;
             const int r = idx / DK, d = idx % DK;
             out[P::QT + (size_t)r * DK + d] = sQ[r * LDK + d] * __builtin_amdgcn_exp2f(sGam[r]);
-            out[P::KB + (size_t)r * DK + d] = sA[r * LDK + d] * __builtin_amdgcn_exp2f(gl - sGam[r]);
+            const float kb = sA[r * LDK + d] * __builtin_amdgcn_exp2f(gl - sGam[r]);
+            out[P::KB + (size_t)r * DK + d] = kb;
+            if (rr) rr[RR::KB + (size_t)r * DK + d] = (bf16)kb;
         }
         if (tid < DK) {
             sPhi[tid] = __builtin_amdgcn_exp2f(gl);
@@ -479,6 +499,22 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const T* __restr
         }
     }
     lds_barrier();
+    if (rr) {
+        // Q~^T for the reverse pass: 8 positions of one channel per 16-byte
+        // store (scalar gates: Q~ = q 2^gamma formed here)
+        static_assert((DK * (C / 8)) % NTH == 0, "Q~^T trip count");
+        for (int u = tid; u < DK * (C / 8); u += NTH) {
+            const int d = u / (C / 8), r0 = (u % (C / 8)) * 8;
+            bf16x8 x;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float qv = sQ[(r0 + j) * LDK + d];
+                if constexpr (!PERCH) qv *= __builtin_amdgcn_exp2f(sGam[r0 + j]);
+                x[j] = (bf16)qv;
+            }
+            *reinterpret_cast<bf16x8*>(rr + RR::QT + (size_t)d * C + r0) = x;
+        }
+    }
 
     // ---- L and Aqk: 16 tiles each, 32 jobs over 4 waves
     for (int job = wave; job < 32; job += NW) {
@@ -492,6 +528,7 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const T* __restr
             // for bf16 I/O, as the forward's products
             acc = mmc<T, DK>(acc, Aop + ti * 16 * LDK, LDK, Bop + tj * 16 * LDK, LDK, lane);
         }
+        bf16x4 at;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = ti * 16 + arow(lane, i), cc = tj * 16 + (lane & 15);
@@ -502,9 +539,14 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const T* __restr
                 sL[r * LDC + cc] = x;
                 out[P::L + (size_t)r * C + cc] = x;
             } else {
-                out[P::AQK + (size_t)r * C + cc] = cc <= r ? x : 0.f;
+                x = cc <= r ? x : 0.f;
+                out[P::AQK + (size_t)r * C + cc] = x;
             }
+            at[i] = (bf16)x;
         }
+        // Aqk^T for the reverse pass: the lane's four rows are adjacent there
+        if (!isL && rr)
+            *reinterpret_cast<bf16x4*>(rr + RR::AT + (size_t)(tj * 16 + (lane & 15)) * C + ti * 16 + 4 * (lane >> 4)) = at;
     }
     lds_barrier();
 
@@ -582,6 +624,13 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const T* __restr
                 acc = mmk<16>(acc, sT + ti * 16 * LDC + kb * 16, LDC, 1, sA + kb * 16 * LDK + tj * 16, LDK, 1, lane);
 #pragma unroll
             for (int i = 0; i < 4; ++i) out[P::W + (size_t)(ti * 16 + arow(lane, i)) * DK + tj * 16 + (lane & 15)] = acc[i];
+            if (rr) {
+                // W^T for the reverse pass
+                bf16x4 wt;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) wt[i] = (bf16)acc[i];
+                *reinterpret_cast<bf16x4*>(rr + RR::WT + (size_t)(tj * 16 + (lane & 15)) * C + ti * 16 + 4 * (lane >> 4)) = wt;
+            }
         }
     }
 }

@@ -199,16 +199,53 @@ constexpr size_t kDecodeStreamBytes = (size_t)128 << 20;
 // the backward kernels
 size_t bwd_prep_floats(int D);
 
+// Segments of the chains: the chunks of each of `chains` chains grouped
+// into NS segments of L consecutive chunks, so that chains * NS is about
+// kSegGroups workgroups (one per CU); NS = 1 where the chains alone fill the
+// GPU.  Used by the segment-parallel forward and the segment-parallel
+// reverse pass of the backward; it depends only on the sizes.
+constexpr int kSegGroups = 256;
+struct SegPlan {
+    int NS, L;
+};
+inline SegPlan seg_plan(long long chains, int NT) {
+    SegPlan S{1, 1};
+    if (NT > 1 && chains < kSegGroups) {
+        const int want = (int)std::min<long long>(NT, (kSegGroups + chains - 1) / chains);
+        S.L = ceil_div(NT, want);
+        S.NS = ceil_div(NT, S.L);
+    } else {
+        S.L = std::max(NT, 1);
+        S.NS = 1;
+    }
+    return S;
+}
+
+size_t bwd_rrec_elems(int D);   // k_bwd.hip
+// Whether the segment-parallel reverse pass of the backward (revseg.h) is
+// built for these sizes: bf16 I/O, the dense layout.
+inline bool rev_seg_built(int D, int dtype) { return dtype == DR_BF16 && (D == 64 || D == 128); }
+// The reverse pass the dense backward takes: the segment-parallel one where
+// it is built, unless DR_BWD_REV=slices selects the value-slice kernel.
+inline bool rev_seg_selected() {
+    const char* e = getenv("DR_BWD_REV");
+    return !(e != nullptr && e[0] == 's');
+}
+
 // states S_c [DK][DV], the exit adjoints dS'_c [DK][DV], Vnew_c and dVnew_c
-// [C][DV] of every chunk, each block 256-byte aligned.
+// [C][DV] of every chunk, each block 256-byte aligned.  Where the
+// segment-parallel reverse pass is built (dense layout): its bf16 chunk
+// operands (RevRec), the segment maps [Pi_r | N_r] [chains][NS][D][2D] and
+// the segment exit adjoints E_r [chains][NS][D][D] (fp32); NS = 0 otherwise.
 struct BwdLayout {
-    size_t prep, hs, dhs, vn, dvn, rec, bytes;
+    size_t prep, hs, dhs, vn, dvn, rec, rrec, xmap, ein, bytes;
+    int NS, L;
 };
 // n = number of per-chunk entries (dense: B * H * ceil(T/C); packed:
-// H * maxchunks)
-// (the forward's chunk records come last: the forward state pass runs the
-// forward's own two kernels over them)
-inline BwdLayout bwd_layout_n(size_t n, int D, int dtype) {
+// H * maxchunks); chains > 0 (dense) adds the reverse pass's segment arrays
+// (the forward's chunk records come before them: the forward state pass runs
+// the forward's own two kernels over them)
+inline BwdLayout bwd_layout_n(size_t n, int D, int dtype, long long chains = 0, int NT = 0) {
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     const size_t pf = D == 64 ? bwd_prep_floats(64) : bwd_prep_floats(128);
     BwdLayout L;
@@ -218,11 +255,21 @@ inline BwdLayout bwd_layout_n(size_t n, int D, int dtype) {
     L.vn = L.dhs + up(n * D * D * 4);
     L.dvn = L.vn + up(n * dr::kChunk * D * 4);
     L.rec = L.dvn + up(n * dr::kChunk * D * 4);
-    L.bytes = L.rec + up(n * record_bytes(D, dtype));
+    L.rrec = L.xmap = L.ein = L.bytes = L.rec + up(n * record_bytes(D, dtype));
+    L.NS = L.L = 0;
+    if (chains > 0 && rev_seg_built(D, dtype)) {
+        const SegPlan S = seg_plan(chains, NT);
+        L.NS = S.NS;
+        L.L = S.L;
+        L.xmap = L.rrec + up(n * bwd_rrec_elems(D) * 2);
+        L.ein = L.xmap + up((size_t)chains * S.NS * D * 2 * D * 4);
+        L.bytes = L.ein + up((size_t)chains * S.NS * D * D * 4);
+    }
     return L;
 }
 inline BwdLayout bwd_layout(int B, int T, int H, int D, int dtype) {
-    return bwd_layout_n((size_t)B * H * (size_t)ceil_div(T, dr::kChunk), D, dtype);
+    const int NT = ceil_div(T, dr::kChunk);
+    return bwd_layout_n((size_t)B * H * (size_t)NT, D, dtype, (long long)B * H, NT);
 }
 
 // B is the sequence count for packed sequences (pk.table set; T is then the
@@ -257,12 +304,9 @@ inline ProBwdLayout probwd_layout(int kind, int B, int T, int H, int D, int dtyp
 }
 
 // ---- segment-parallel forward (seg.h) ------------------------------------
-// The chunks of every (b, h) chain are grouped into NS segments of L chunks,
-// sized so that B*H*NS is about kSegGroups workgroups (one per CU).  The
-// choice depends only on the problem's sizes, so workspace queries are
-// deterministic.  Workspace: q_eff [B*H*NT][C][D] (I/O dtype), [M | N]
+// The chunks of every (b, h) chain are grouped into NS segments of L chunks
+// (seg_plan).  Workspace: q_eff [B*H*NT][C][D] (I/O dtype), [M | N]
 // [B*H][NS][D][2D] fp32, S_in^T [B*H][NS][D][D] (I/O dtype), each 256-aligned.
-constexpr int kSegGroups = 256;
 struct SegLayout {
     int NS, L;
     size_t qeff, xend, sint, bytes;
@@ -281,14 +325,9 @@ inline SegLayout seg_layout(int B, int T, int H, int D, int dtype) {
     SegLayout S{1, 1, 0, 0, 0, 0};
     const int NT = ceil_div(T, dr::kChunk);
     const long long chains = (long long)B * H;
-    if (NT > 1 && chains < kSegGroups) {
-        const int want = (int)std::min<long long>(NT, (kSegGroups + chains - 1) / chains);
-        S.L = ceil_div(NT, want);
-        S.NS = ceil_div(NT, S.L);
-    } else {
-        S.L = std::max(NT, 1);
-        S.NS = 1;
-    }
+    const SegPlan P = seg_plan(chains, NT);
+    S.NS = P.NS;
+    S.L = P.L;
     const size_t esz = dtype == DR_BF16 ? 2 : 4;
     S.qeff = 0;
     S.xend = up((size_t)chains * NT * dr::kChunk * D * esz);

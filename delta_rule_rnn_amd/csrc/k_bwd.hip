@@ -1,10 +1,43 @@
-// k_bwd.hip -- launchers of the backward kernels (backward.h).
+// k_bwd.hip -- launchers of the backward kernels (backward.h, revseg.h).
 #include "host.h"
 #include "backward.h"
+#include "revseg.h"
 
 namespace drh {
 
 size_t bwd_prep_floats(int D) { return D == 64 ? dr::bw::Prep<64>::FLOATS : dr::bw::Prep<128>::FLOATS; }
+size_t bwd_rrec_elems(int D) { return D == 64 ? dr::bw::RevRec<64>::ELEMS : dr::bw::RevRec<128>::ELEMS; }
+
+namespace {
+
+// The segment-parallel reverse pass (bf16 I/O, dense layout): segment maps
+// (segments 1 .. NS-1), their composition, then every segment from its exit
+// adjoint.
+template <int KIND, int D>
+dr_status launch_rev_seg(const BwdArgs& a, const bf16* rrec, const float* prep, float* dhs, float* dvn,
+                         hipStream_t st) {
+    using namespace dr::bw;
+    const long long chains = (long long)a.B * a.H;
+    const int NS = a.L.NS, L = a.L.L;
+    const bf16* dout = static_cast<const bf16*>(a.dout);
+    float* xmap = reinterpret_cast<float*>(a.ws + a.L.xmap);
+    float* ein = reinterpret_cast<float*>(a.ws + a.L.ein);
+    if (chains * NS > 0x7fffffffLL || chains * (D / 16) > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
+    dr_status s;
+    if (NS > 1) {
+        hipLaunchKernelGGL((rev_seg_kernel<KIND, D, true>), dim3((unsigned)(chains * (NS - 1))), dim3(kRevThreads), 0,
+                           st, rrec, prep, dout, ein, xmap, dhs, dvn, a.dh0, a.T, a.H, a.NT, L, NS);
+        if ((s = check_launch()) != DR_OK) return s;
+    }
+    hipLaunchKernelGGL((rev_compose_kernel<D>), dim3((unsigned)(chains * (D / 16))), dim3(kRevComposeThreads), 0, st,
+                       xmap, a.dhT, ein, NS);
+    if ((s = check_launch()) != DR_OK) return s;
+    hipLaunchKernelGGL((rev_seg_kernel<KIND, D, false>), dim3((unsigned)(chains * NS)), dim3(kRevThreads), 0, st,
+                       rrec, prep, dout, ein, xmap, dhs, dvn, a.dh0, a.T, a.H, a.NT, L, NS);
+    return check_launch();
+}
+
+}  // namespace
 
 template <int KIND, typename E, int D>
 dr_status launch_backward_t(const BwdArgs& a, hipStream_t st) {
@@ -21,13 +54,23 @@ dr_status launch_backward_t(const BwdArgs& a, hipStream_t st) {
     const long long items = a.pk.table ? (long long)a.pk.maxchunks * a.H : (long long)a.B * a.NT * a.H;
     const long long slices = (long long)a.B * a.H * (D / kSV);
     if (items > 0x7fffffffLL || slices > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
+    // the segment-parallel reverse pass where its workspace is laid out
+    // (bf16 I/O, dense layout) unless the value-slice kernel is selected
+    const bool seg = std::is_same<E, bf16>::value && a.L.NS > 0 && !a.pk.table && rev_seg_selected();
+    bf16* rrec = seg ? reinterpret_cast<bf16*>(a.ws + a.L.rrec) : nullptr;
     hipLaunchKernelGGL((bwd_prep_kernel<KIND, E, D>), dim3((unsigned)items), dim3(kPrepThreads), 0, st, q, k, a.g, a.beta,
-                       prep, a.T, a.H, a.NT, a.pk);
+                       prep, rrec, a.T, a.H, a.NT, a.pk);
     dr_status s = check_launch();
     if (s != DR_OK) return s;
-    hipLaunchKernelGGL((bwd_state_rev_kernel<KIND, E, D>), dim3((unsigned)slices), dim3(kStateThreads), 0, st, prep, dout, a.dhT,
-                       dhs, dvn, a.dh0, a.T, a.H, a.NT, a.pk);
-    if ((s = check_launch()) != DR_OK) return s;
+    if constexpr (std::is_same<E, bf16>::value) {
+        if (seg) s = launch_rev_seg<KIND, D>(a, rrec, prep, dhs, dvn, st);
+    }
+    if (!seg) {
+        hipLaunchKernelGGL((bwd_state_rev_kernel<KIND, E, D>), dim3((unsigned)slices), dim3(kStateThreads), 0, st, prep,
+                           dout, a.dhT, dhs, dvn, a.dh0, a.T, a.H, a.NT, a.pk);
+        s = check_launch();
+    }
+    if (s != DR_OK) return s;
     hipLaunchKernelGGL((bwd_grad_kernel<KIND, E, D>), dim3((unsigned)items), dim3(512), 0, st, q, k, v, a.beta, dout,
                        prep, hs, dhs, vn, dvn, static_cast<E*>(a.dq), static_cast<E*>(a.dk), static_cast<E*>(a.dv),
                        a.dg, a.dbeta, a.T, a.H, a.NT, a.pk);

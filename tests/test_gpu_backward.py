@@ -88,6 +88,28 @@ def test_backward_zero_initial_state(kind):
     _check(res, ref, kind, "bf16", f"{kind} zero h0")
 
 
+@pytest.mark.parametrize("path", ["segment", "slices"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("kind", ["kda", "gdn", "decay_la"])
+@pytest.mark.parametrize("B,H,T", [(1, 2, 2600), (2, 2, 8300)])
+def test_backward_reverse_pass_paths(kind, D, path, B, H, T, monkeypatch):
+    """bf16 I/O: the segment-parallel reverse pass (the default) and the
+    value-slice kernel (DR_BWD_REV=slices), each against the oracle.  2 chains
+    of 41 chunks give 41 one-chunk segments; 4 chains of 130 chunks (the last
+    ragged) give 44 segments of 3 chunks, the last with one."""
+    monkeypatch.setenv("DR_BWD_REV", path)
+    res, ref = _run(kind, "bf16", D, B=B, H=H, T=T, seed=76)
+    _check(res, ref, kind, "bf16", f"{kind} D{D} {path} T={T}")
+
+
+def test_backward_many_chains_one_segment(monkeypatch):
+    """256 chains fill the GPU by themselves: the segment-parallel pass runs
+    each chain as one segment (no maps, no composition)."""
+    monkeypatch.delenv("DR_BWD_REV", raising=False)
+    res, ref = _run("gdn", "bf16", 64, B=2, H=128, T=150, seed=77)
+    _check(res, ref, "gdn", "bf16", "gdn 256 chains")
+
+
 def test_backward_no_tokens():
     dra = _ops()
     w = Workload("gdn_bwd0", "gdn", "f32", B=2, H=2, T=0, Dk=64, Dv=64, h0_std=1.0, seed=73)
