@@ -35,7 +35,9 @@
 //
 // The entry states S_c and Vnew_c of every chunk come first, from the
 // forward's own two kernels (the chunk-parallel records, then the state pass
-// in its STATES mode, fp32 state in accumulators).  The kernels here keep
+// in its STATES mode, fp32 state in accumulators).  The per-chunk state
+// arrays (S_c, Vnew_c, and the exit adjoints dS'_c, dVnew_c) are stored in
+// the I/O dtype, rounded from fp32 accumulators.  The kernels here keep
 // their operands as fp32 in LDS, in natural row-major layout, and compute on
 // fp32 MFMA (v_mfma_f32_16x16x4_f32), except for bf16 I/O: the prep's L and
 // Aqk, and the gradient kernel's value-slice, pairwise and T products, run
@@ -43,9 +45,12 @@
 // I/O dtype otherwise only changes the loads of q, k, v, dO and the stores
 // of dq, dk, dv.
 //   bwd_prep_kernel     chunk-parallel: writes the natural fp32 chunk arrays
-//                       (Q~, W, Kbar, Aqk, L, T, phi, gamma)
+//                       (Q~, W, Kbar, Aqk, L, T, phi, gamma), and for bf16
+//                       I/O the segment-parallel reverse pass's operands
 //   bwd_state_rev_kernel   per (chain, 16 value columns), chunks in reverse:
-//                       exit adjoints dS'_c, dVnew, and dh0
+//                       exit adjoints dS'_c, dVnew, and dh0 (fp32 I/O and
+//                       packed sequences; bf16 I/O in the dense layout takes
+//                       the segment-parallel pass of revseg.h)
 //   bwd_grad_kernel     chunk-parallel: dq, dk, dv, dbeta, dg
 #pragma once
 
@@ -319,37 +324,43 @@ __device__ __forceinline__ void stage(float* dst, int ls, const float* __restric
     }
 }
 // The two halves of a staging copy, for issuing the loads of several blocks
-// before any of their LDS stores.
-template <int ROWS, int COLS, int NTHR>
+// before any of their LDS stores.  The source holds fp32 or bf16 (S); the
+// LDS copy is fp32.
+template <int ROWS, int COLS, int NTHR, typename S = float>
 struct Staged {
     static constexpr int PER = COLS / 4, IT = ROWS * PER / NTHR;
     static_assert(COLS % 4 == 0 && (ROWS * PER) % NTHR == 0, "staging shape");
-    // native 4-float vectors (not the float4 struct, whose copies become
+    // native 4-element vectors (not the float4 struct, whose copies become
     // memcpy and keep a loop-carried array out of registers)
-    f32x4 v[IT];
-    __device__ __forceinline__ void load(const float* __restrict__ src, size_t gs, int tid) {
+    using V4 = typename VecOf<S, 4>::type;
+    V4 v[IT];
+    __device__ __forceinline__ void load(const S* __restrict__ src, size_t gs, int tid) {
 #pragma unroll
         for (int j = 0; j < IT; ++j) {
             const int idx = tid + j * NTHR, r = idx / PER, c4 = (idx % PER) * 4;
-            v[j] = *reinterpret_cast<const f32x4*>(src + r * gs + c4);
+            v[j] = *reinterpret_cast<const V4*>(src + r * gs + c4);
         }
     }
     __device__ __forceinline__ void store(float* dst, int ls, int tid) const {
 #pragma unroll
         for (int j = 0; j < IT; ++j) {
             const int idx = tid + j * NTHR, r = idx / PER, c4 = (idx % PER) * 4;
-            *reinterpret_cast<f32x4*>(dst + r * ls + c4) = v[j];
+            f32x4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = (float)v[j][e];
+            *reinterpret_cast<f32x4*>(dst + r * ls + c4) = x;
         }
     }
 };
-template <int ROWS, int COLS, int NTHR>
-__device__ __forceinline__ void unstage(float* __restrict__ dst, size_t gs, const float* src, int ls, int tid) {
+// fp32 LDS block to global memory (fp32 or bf16, four elements per access)
+template <int ROWS, int COLS, int NTHR, typename D>
+__device__ __forceinline__ void unstage(D* __restrict__ dst, size_t gs, const float* src, int ls, int tid) {
     constexpr int PER = COLS / 4, N = ROWS * PER, IT = N / NTHR;
     static_assert(COLS % 4 == 0 && N % NTHR == 0, "staging shape");
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
         const int idx = tid + i * NTHR, r = idx / PER, c4 = (idx % PER) * 4;
-        *reinterpret_cast<float4*>(dst + r * gs + c4) = *reinterpret_cast<const float4*>(src + r * ls + c4);
+        st4(dst + r * gs + c4, *reinterpret_cast<const f32x4*>(src + r * ls + c4));
     }
 }
 
@@ -708,8 +719,8 @@ template <int KIND, typename T, int DK>
 __global__ __launch_bounds__(kStateThreads) void bwd_state_rev_kernel(const float* __restrict__ prep,
                                                                       const T* __restrict__ dout,
                                                                       const float* __restrict__ dhT,
-                                                                      float* __restrict__ dhs,
-                                                                      float* __restrict__ dvn,
+                                                                      T* __restrict__ dhs,
+                                                                      T* __restrict__ dvn,
                                                                       float* __restrict__ dh0, int Tlen, int H,
                                                                       int NT, Pack pk)
 {
@@ -837,7 +848,7 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_rev_kernel(const floa
                 const int r = tid / (kSV / 4), c4 = (tid % (kSV / 4)) * 4;
                 const f32x4 x = *reinterpret_cast<const f32x4*>(sDV + r * LSV + c4);
                 const f32x4 y = *reinterpret_cast<const f32x4*>(sDV2 + r * LSV + c4);
-                *reinterpret_cast<f32x4*>(dvn + ci * C * DV + dv0 + (size_t)r * DV + c4) = x + y;
+                st4(dvn + ci * C * DV + dv0 + (size_t)r * DV + c4, x + y);
             }
         }
         lds_barrier();
@@ -879,8 +890,8 @@ struct GradSmem {
 template <int KIND, typename T, int DK>
 __global__ __launch_bounds__(512) void bwd_grad_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ beta,
-    const T* __restrict__ dout, const float* __restrict__ prep, const float* __restrict__ hs,
-    const float* __restrict__ dhs, const float* __restrict__ vn, const float* __restrict__ dvn,
+    const T* __restrict__ dout, const float* __restrict__ prep, const T* __restrict__ hs,
+    const T* __restrict__ dhs, const T* __restrict__ vn, const T* __restrict__ dvn,
     T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv, float* __restrict__ dg, float* __restrict__ dbeta,
     int Tlen, int H, int NT, Pack pk)
 {
@@ -977,8 +988,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     // the value slices travel one slice ahead in registers: slice s+1 loads
     // during slice s's products (the last slice reloads itself, so that the
     // loads stay unconditional)
-    Staged<DK, kVS, 512> g1, g2;
-    Staged<C, kVS, 512> g3, g4;
+    Staged<DK, kVS, 512, T> g1, g2;
+    Staged<C, kVS, 512, T> g3, g4;
     constexpr int NE = (C * kVS) / 512;
     float xd[NE], xv[NE];
     auto load_slice = [&](int dv0) {

@@ -222,7 +222,7 @@ dr_status backward_impl(int kind, const void* q, const void* k, const void* v, c
         }
         s = packed ? launch_intra_varlen(p, st) : launch_intra(p, 0, p.NT, st);
         if (s != DR_OK) return s;
-        s = launch_states(p, h0, reinterpret_cast<float*>(core + L.hs), reinterpret_cast<float*>(core + L.vn), st);
+        s = launch_states(p, h0, core + L.hs, core + L.vn, st);
         if (s != DR_OK) return s;
     }
     BwdArgs a{rq, rk, v, dout, rg, rb, h0, dhT, dq, dk, dv, dg, delta ? dbeta : nullptr, dh0,

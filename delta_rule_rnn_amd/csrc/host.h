@@ -233,7 +233,8 @@ inline bool rev_seg_selected() {
 }
 
 // states S_c [DK][DV], the exit adjoints dS'_c [DK][DV], Vnew_c and dVnew_c
-// [C][DV] of every chunk, each block 256-byte aligned.  Where the
+// [C][DV] of every chunk, in the I/O dtype, each block 256-byte aligned.
+// Where the
 // segment-parallel reverse pass is built (dense layout): its bf16 chunk
 // operands (RevRec), the segment maps [Pi_r | N_r] [chains][NS][D][2D] and
 // the segment exit adjoints E_r [chains][NS][D][D] (fp32); NS = 0 otherwise.
@@ -251,10 +252,11 @@ inline BwdLayout bwd_layout_n(size_t n, int D, int dtype, long long chains = 0, 
     BwdLayout L;
     L.prep = 0;
     L.hs = up(n * pf * 4);
-    L.dhs = L.hs + up(n * D * D * 4);
-    L.vn = L.dhs + up(n * D * D * 4);
-    L.dvn = L.vn + up(n * dr::kChunk * D * 4);
-    L.rec = L.dvn + up(n * dr::kChunk * D * 4);
+    const size_t esz = dtype == DR_BF16 ? 2 : 4;
+    L.dhs = L.hs + up(n * D * D * esz);
+    L.vn = L.dhs + up(n * D * D * esz);
+    L.dvn = L.vn + up(n * dr::kChunk * D * esz);
+    L.rec = L.dvn + up(n * dr::kChunk * D * esz);
     L.rrec = L.xmap = L.ein = L.bytes = L.rec + up(n * record_bytes(D, dtype));
     L.NS = L.L = 0;
     if (chains > 0 && rev_seg_built(D, dtype)) {
@@ -348,7 +350,8 @@ dr_status forward(int kind, const void* q, const void* k, const void* v, const f
 dr_status launch_intra(const Problem& p, int c0, int n, hipStream_t st);           // k_intra.hip
 dr_status launch_intra_varlen(const Problem& p, hipStream_t st);                   // k_intra.hip
 dr_status launch_inter(const Problem& p, const float* h0, float* hT, int c0, int n, hipStream_t st);  // k_inter.hip
-dr_status launch_states(const Problem& p, const float* h0, float* hs, float* vn, hipStream_t st);     // k_inter.hip
+// S_c and Vnew_c of every chunk, in the I/O type
+dr_status launch_states(const Problem& p, const float* h0, void* hs, void* vn, hipStream_t st);       // k_inter.hip
 dr_status launch_backward(int kind, const BwdArgs& a, int D, int dtype, hipStream_t st);              // k_bwd.hip
 dr_status launch_decode(int kind, const DecodeArgs& a, bool use_pro, int D, int dtype, hipStream_t st);  // k_misc.hip
 dr_status launch_prologue(bool backward, int kind, int D, int dtype, const void* q, const void* k, const float* g,

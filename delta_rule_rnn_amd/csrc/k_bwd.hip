@@ -14,7 +14,7 @@ namespace {
 // (segments 1 .. NS-1), their composition, then every segment from its exit
 // adjoint.
 template <int KIND, int D>
-dr_status launch_rev_seg(const BwdArgs& a, const bf16* rrec, const float* prep, float* dhs, float* dvn,
+dr_status launch_rev_seg(const BwdArgs& a, const bf16* rrec, const float* prep, bf16* dhs, bf16* dvn,
                          hipStream_t st) {
     using namespace dr::bw;
     const long long chains = (long long)a.B * a.H;
@@ -43,10 +43,10 @@ template <int KIND, typename E, int D>
 dr_status launch_backward_t(const BwdArgs& a, hipStream_t st) {
     using namespace dr::bw;
     float* prep = reinterpret_cast<float*>(a.ws + a.L.prep);
-    float* hs = reinterpret_cast<float*>(a.ws + a.L.hs);
-    float* dhs = reinterpret_cast<float*>(a.ws + a.L.dhs);
-    float* vn = reinterpret_cast<float*>(a.ws + a.L.vn);
-    float* dvn = reinterpret_cast<float*>(a.ws + a.L.dvn);
+    E* hs = reinterpret_cast<E*>(a.ws + a.L.hs);
+    E* dhs = reinterpret_cast<E*>(a.ws + a.L.dhs);
+    E* vn = reinterpret_cast<E*>(a.ws + a.L.vn);
+    E* dvn = reinterpret_cast<E*>(a.ws + a.L.dvn);
     const E* q = static_cast<const E*>(a.q);
     const E* k = static_cast<const E*>(a.k);
     const E* v = static_cast<const E*>(a.v);

@@ -87,7 +87,7 @@ dr_status launch_inter(const Problem& p, const float* h0, float* hT, int c0, int
 // mode (entry state and Vnew of every chunk, no output) over the records the
 // chunk-parallel kernel wrote; slice width and prefetch as for the forward
 template <int KIND, typename E, int D, int NTN, int PFD>
-dr_status launch_states_p(const Problem& p, const float* h0, float* hs, float* vn, hipStream_t st) {
+dr_status launch_states_p(const Problem& p, const float* h0, E* hs, E* vn, hipStream_t st) {
     constexpr int NV = D / (16 * NTN);
     dim3 grid(p.B * p.H * NV);
     if (p.seqinfo) {
@@ -102,7 +102,9 @@ dr_status launch_states_p(const Problem& p, const float* h0, float* hs, float* v
     return check_launch();
 }
 template <int KIND, typename E, int D>
-dr_status launch_states_t(const Problem& p, const float* h0, float* hs, float* vn, hipStream_t st) {
+dr_status launch_states_t(const Problem& p, const float* h0, void* hs_, void* vn_, hipStream_t st) {
+    E* hs = static_cast<E*>(hs_);
+    E* vn = static_cast<E*>(vn_);
     const int ntn = pick_ntn(p.B * p.H, D);
     const bool pf = pick_pfd() != 0;
     if constexpr (sizeof(E) == 2) {
@@ -117,7 +119,7 @@ dr_status launch_states_t(const Problem& p, const float* h0, float* hs, float* v
         return launch_states_p<KIND, E, D, 2, 0>(p, h0, hs, vn, st);
     }
 }
-dr_status launch_states(const Problem& p, const float* h0, float* hs, float* vn, hipStream_t st) {
+dr_status launch_states(const Problem& p, const float* h0, void* hs, void* vn, hipStream_t st) {
     auto by_kind = [&](auto kind_tag) -> dr_status {
         constexpr int KIND = decltype(kind_tag)::value;
         if (p.dtype == DR_BF16)

@@ -24,8 +24,9 @@
 //                         0), E_{r-1} = Pi_r E_r + N_r; every E_r is written.
 //   rev_seg_kernel<OUT>   one workgroup per (chain, segment): the segment's
 //                         chunks backwards from D = E_r, storing dS'_c = D
-//                         and dVnew_c = Y of every chunk, and dh0 (the D left
-//                         at the start of segment 0).
+//                         and dVnew_c = Y of every chunk (bf16, the I/O
+//                         dtype), and dh0 (fp32: the D left at the start of
+//                         segment 0).
 // Products run on bf16 MFMA with fp32 accumulation: the chunk operands come
 // as bf16 (bwd_prep_kernel's RevRec), X and Y are rounded to bf16 as they
 // are read (as the forward's state products round S), X stays fp32 in the
@@ -147,12 +148,12 @@ __device__ __forceinline__ void rev_stage(const RevIn<KIND, DK>& in, uint8_t* sm
 //   rrec  [chains * NT] RevRec (bf16);  prep: phi of every chunk (fp32)
 //   ein   [chains][NS][DK][DV] fp32: E_r (OUT)
 //   xmap  [chains][NS][DK][2 DK] fp32: [Pi_r | N_r] (MAPS)
-//   dhs   [chains * NT][DK][DV], dvn [chains * NT][C][DV] fp32 (OUT)
+//   dhs   [chains * NT][DK][DV], dvn [chains * NT][C][DV] bf16 (OUT)
 //   dh0   [chains][DK][DV] fp32 or null (OUT)
 template <int KIND, int DK, bool MAPS>
 __global__ __launch_bounds__(kRevThreads, 1) void rev_seg_kernel(
     const bf16* __restrict__ rrec, const float* __restrict__ prep, const bf16* __restrict__ dout,
-    const float* __restrict__ ein, float* __restrict__ xmap, float* __restrict__ dhs, float* __restrict__ dvn,
+    const float* __restrict__ ein, float* __restrict__ xmap, bf16* __restrict__ dhs, bf16* __restrict__ dvn,
     float* __restrict__ dh0, int Tlen, int H, int NT, int L, int NS)
 {
     using Cfg = RevCfg<DK, MAPS>;
@@ -213,7 +214,7 @@ __global__ __launch_bounds__(kRevThreads, 1) void rev_seg_kernel(
         if (active) {
             if constexpr (!MAPS) {
                 // dS'_c: the adjoint of this chunk's exit state
-                float* dst = dhs + ci * DK * DV + col0 + r16;
+                bf16* dst = dhs + ci * DK * DV + col0 + r16;
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -222,7 +223,7 @@ __global__ __launch_bounds__(kRevThreads, 1) void rev_seg_kernel(
                         for (int n = 0; n < NTW; ++n)
 #pragma unroll
                             for (int i = 0; i < 4; ++i)
-                                dst[(size_t)(32 * kb + 8 * grp + 4 * hh + i) * DV + 16 * n] = X[kb][hh][n][i];
+                                dst[(size_t)(32 * kb + 8 * grp + 4 * hh + i) * DV + 16 * n] = (bf16)X[kb][hh][n][i];
             }
             // dO^T fragments of this wave's columns (D columns only)
             Frag<bf16> dof[2][NTW];
@@ -269,7 +270,7 @@ __global__ __launch_bounds__(kRevThreads, 1) void rev_seg_kernel(
             if constexpr (!MAPS) {
                 // dVnew_c (rows past a ragged end are zero: Kbar's and
                 // Aqk^T's are)
-                float* dst = dvn + ci * C * DV + col0 + r16;
+                bf16* dst = dvn + ci * C * DV + col0 + r16;
 #pragma unroll
                 for (int kbp = 0; kbp < 2; ++kbp)
 #pragma unroll
@@ -278,7 +279,7 @@ __global__ __launch_bounds__(kRevThreads, 1) void rev_seg_kernel(
                         for (int n = 0; n < NTW; ++n)
 #pragma unroll
                             for (int i = 0; i < 4; ++i)
-                                dst[(size_t)(32 * kbp + 8 * grp + 4 * hh + i) * DV + 16 * n] = Y[kbp][hh][n][i];
+                                dst[(size_t)(32 * kbp + 8 * grp + 4 * hh + i) * DV + 16 * n] = (bf16)Y[kbp][hh][n][i];
             }
             // X <- Diag(phi) X - W^T Y (+ Q~^T dO)
             Frag<bf16> Yf[2][NTW];

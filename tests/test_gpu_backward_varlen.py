@@ -88,10 +88,14 @@ def test_backward_varlen_matches_oracle_per_sequence(kind, dt, D):
 
 @pytest.mark.parametrize("kind", ["kda", "gdn", "decay_la"])
 @pytest.mark.parametrize("L", [192, 150])
-def test_backward_equal_lengths_match_dense_batch(kind, L):
+def test_backward_equal_lengths_match_dense_batch(kind, L, monkeypatch):
     """Packing B sequences of one length reproduces the dense [B, L]
     backward bit for bit, every gradient (same chunks, same arithmetic,
-    reductions in a fixed order)."""
+    reductions in a fixed order).  Packed sequences take the value-slice
+    reverse pass, so the dense call is pinned to it (DR_BWD_REV=slices); the
+    dense default, the segment-parallel pass, is checked against the oracle
+    in test_gpu_backward.py."""
+    monkeypatch.setenv("DR_BWD_REV", "slices")
     dra = _ops()
     B, H = 3, 4
     w = Workload(f"{kind}_dense_bwd", kind, "bf16", B=B, H=H, T=L, Dk=128, Dv=128, h0_std=0.1, seed=43)
