@@ -45,8 +45,10 @@
 // I/O dtype otherwise only changes the loads of q, k, v, dO and the stores
 // of dq, dk, dv.
 //   bwd_prep_kernel     chunk-parallel: writes the natural fp32 chunk arrays
-//                       (Q~, W, Kbar, Aqk, L, T, phi, gamma), and for bf16
-//                       I/O the segment-parallel reverse pass's operands
+//                       (Aqk, L, T, phi, gamma, and for the value-slice
+//                       reverse pass Q~, W, Kbar), or for the segment-
+//                       parallel reverse pass its bf16 operands instead of
+//                       the fp32 Q~, W, Kbar
 //   bwd_state_rev_kernel   per (chain, 16 value columns), chunks in reverse:
 //                       exit adjoints dS'_c, dVnew, and dh0 (fp32 I/O and
 //                       packed sequences; bf16 I/O in the dense layout takes
@@ -408,7 +410,10 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const T* __restr
     const int nvalid = loc.nvalid;
     const size_t row0 = loc.row0;   // token row of position 0
     float* out = prep + loc.ci * P::FLOATS;
-    // the bf16 record of the segment-parallel reverse pass (null: not used)
+    // the bf16 record of the segment-parallel reverse pass (null: not used);
+    // with it, the fp32 Q~, W and Kbar (read only by the value-slice reverse
+    // pass; the gradient kernel forms its own from q, k and gamma) are not
+    // written
     bf16* rr = rrec ? rrec + loc.ci * RR::ELEMS : nullptr;
 
     // ---- inputs, rows past the end of a ragged chunk zero
@@ -477,9 +482,12 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const T* __restr
         for (int j = 0; j < RB; ++j) {
             const int r = b * RB + j;
             const float kb = sB[r * LDK + d] * phi;
-            out[P::KB + (size_t)r * DK + d] = kb;
-            out[P::QT + (size_t)r * DK + d] = sQ[r * LDK + d];
-            if (rr) rr[RR::KB + (size_t)r * DK + d] = (bf16)kb;
+            if (rr) {
+                rr[RR::KB + (size_t)r * DK + d] = (bf16)kb;
+            } else {
+                out[P::KB + (size_t)r * DK + d] = kb;
+                out[P::QT + (size_t)r * DK + d] = sQ[r * LDK + d];
+            }
         }
     } else {
         if (wave == 0) {
@@ -499,10 +507,13 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const T* __restr
         for (int it_ = 0; it_ < (C * DK) / NTH; ++it_) {
             const int idx = tid + it_ * NTH;
             const int r = idx / DK, d = idx % DK;
-            out[P::QT + (size_t)r * DK + d] = sQ[r * LDK + d] * __builtin_amdgcn_exp2f(sGam[r]);
             const float kb = sA[r * LDK + d] * __builtin_amdgcn_exp2f(gl - sGam[r]);
-            out[P::KB + (size_t)r * DK + d] = kb;
-            if (rr) rr[RR::KB + (size_t)r * DK + d] = (bf16)kb;
+            if (rr) {
+                rr[RR::KB + (size_t)r * DK + d] = (bf16)kb;
+            } else {
+                out[P::QT + (size_t)r * DK + d] = sQ[r * LDK + d] * __builtin_amdgcn_exp2f(sGam[r]);
+                out[P::KB + (size_t)r * DK + d] = kb;
+            }
         }
         if (tid < DK) {
             sPhi[tid] = __builtin_amdgcn_exp2f(gl);
@@ -633,14 +644,16 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const T* __restr
             f32x4 acc = zero4();
             for (int kb = 0; kb <= ti; ++kb)
                 acc = mmk<16>(acc, sT + ti * 16 * LDC + kb * 16, LDC, 1, sA + kb * 16 * LDK + tj * 16, LDK, 1, lane);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) out[P::W + (size_t)(ti * 16 + arow(lane, i)) * DK + tj * 16 + (lane & 15)] = acc[i];
             if (rr) {
                 // W^T for the reverse pass
                 bf16x4 wt;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) wt[i] = (bf16)acc[i];
                 *reinterpret_cast<bf16x4*>(rr + RR::WT + (size_t)(tj * 16 + (lane & 15)) * C + ti * 16 + 4 * (lane >> 4)) = wt;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    out[P::W + (size_t)(ti * 16 + arow(lane, i)) * DK + tj * 16 + (lane & 15)] = acc[i];
             }
         }
     }
