@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include <algorithm>
 
@@ -225,25 +226,26 @@ size_t bwd_rrec_elems(int D);   // k_bwd.hip
 // Whether the segment-parallel reverse pass of the backward (revseg.h) is
 // built for these sizes: bf16 I/O, the dense layout.
 inline bool rev_seg_built(int D, int dtype) { return dtype == DR_BF16 && (D == 64 || D == 128); }
-// The reverse pass the dense backward takes: the segment-parallel one where
-// it is built, unless DR_BWD_REV=slices selects the value-slice kernel.
+// The reverse pass the backward takes: the segment-parallel one where it is
+// built, unless DR_BWD_REV=slices selects the value-slice kernel.
 inline bool rev_seg_selected() {
     const char* e = getenv("DR_BWD_REV");
-    return !(e != nullptr && e[0] == 's');
+    return !(e != nullptr && strcmp(e, "slices") == 0);
 }
 
 // states S_c [DK][DV], the exit adjoints dS'_c [DK][DV], Vnew_c and dVnew_c
 // [C][DV] of every chunk, in the I/O dtype, each block 256-byte aligned.
-// Where the
-// segment-parallel reverse pass is built (dense layout): its bf16 chunk
-// operands (RevRec), the segment maps [Pi_r | N_r] [chains][NS][D][2D] and
-// the segment exit adjoints E_r [chains][NS][D][D] (fp32); NS = 0 otherwise.
+// Where the segment-parallel reverse pass is built: its bf16 chunk operands
+// (RevRec), and for more than one segment per chain (dense layout) the
+// segment maps [Pi_r | N_r] [chains][NS][D][2D] and the segment exit
+// adjoints E_r [chains][NS][D][D] (fp32); packed sequences take one segment
+// per chain.  NS = 0 where the pass is not built.
 struct BwdLayout {
     size_t prep, hs, dhs, vn, dvn, rec, rrec, xmap, ein, bytes;
     int NS, L;
 };
 // n = number of per-chunk entries (dense: B * H * ceil(T/C); packed:
-// H * maxchunks); chains > 0 (dense) adds the reverse pass's segment arrays
+// H * maxchunks); chains and NT (dense) size the reverse pass's segments
 // (the forward's chunk records come before them: the forward state pass runs
 // the forward's own two kernels over them)
 inline BwdLayout bwd_layout_n(size_t n, int D, int dtype, long long chains = 0, int NT = 0) {
@@ -259,13 +261,19 @@ inline BwdLayout bwd_layout_n(size_t n, int D, int dtype, long long chains = 0, 
     L.rec = L.dvn + up(n * dr::kChunk * D * esz);
     L.rrec = L.xmap = L.ein = L.bytes = L.rec + up(n * record_bytes(D, dtype));
     L.NS = L.L = 0;
-    if (chains > 0 && rev_seg_built(D, dtype)) {
-        const SegPlan S = seg_plan(chains, NT);
-        L.NS = S.NS;
-        L.L = S.L;
-        L.xmap = L.rrec + up(n * bwd_rrec_elems(D) * 2);
-        L.ein = L.xmap + up((size_t)chains * S.NS * D * 2 * D * 4);
-        L.bytes = L.ein + up((size_t)chains * S.NS * D * D * 4);
+    if (rev_seg_built(D, dtype)) {
+        L.xmap = L.ein = L.bytes = L.rrec + up(n * bwd_rrec_elems(D) * 2);
+        L.NS = 1;
+        L.L = std::max(NT, 1);
+        if (chains > 0) {
+            const SegPlan S = seg_plan(chains, NT);
+            L.NS = S.NS;
+            L.L = S.L;
+            if (S.NS > 1) {
+                L.ein = L.xmap + up((size_t)chains * S.NS * D * 2 * D * 4);
+                L.bytes = L.ein + up((size_t)chains * S.NS * D * D * 4);
+            }
+        }
     }
     return L;
 }

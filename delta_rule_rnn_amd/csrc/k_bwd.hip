@@ -10,30 +10,33 @@ size_t bwd_rrec_elems(int D) { return D == 64 ? dr::bw::RevRec<64>::ELEMS : dr::
 
 namespace {
 
-// The segment-parallel reverse pass (bf16 I/O, dense layout): segment maps
-// (segments 1 .. NS-1), their composition, then every segment from its exit
-// adjoint.
+// The segment-parallel reverse pass (bf16 I/O): segment maps (segments
+// 1 .. NS-1), their composition, then every segment from its exit adjoint;
+// with one segment per chain (packed sequences, or chains that fill the GPU)
+// only the last, from dhT.
 template <int KIND, int D>
 dr_status launch_rev_seg(const BwdArgs& a, const bf16* rrec, const float* prep, bf16* dhs, bf16* dvn,
                          hipStream_t st) {
     using namespace dr::bw;
-    const long long chains = (long long)a.B * a.H;
-    const int NS = a.L.NS, L = a.L.L;
+    const long long chains = (long long)a.B * a.H;    // B: sequences for packed sequences
+    const int NS = a.pk.table ? 1 : a.L.NS, L = a.L.L;
     const bf16* dout = static_cast<const bf16*>(a.dout);
     float* xmap = reinterpret_cast<float*>(a.ws + a.L.xmap);
     float* ein = reinterpret_cast<float*>(a.ws + a.L.ein);
     if (chains * NS > 0x7fffffffLL || chains * (D / 16) > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
     dr_status s;
+    const float* e = a.dhT;       // one segment: it starts from dhT
     if (NS > 1) {
         hipLaunchKernelGGL((rev_seg_kernel<KIND, D, true>), dim3((unsigned)(chains * (NS - 1))), dim3(kRevThreads), 0,
-                           st, rrec, prep, dout, ein, xmap, dhs, dvn, a.dh0, a.T, a.H, a.NT, L, NS);
+                           st, rrec, prep, dout, ein, xmap, dhs, dvn, a.dh0, a.T, a.H, a.NT, L, NS, a.pk);
         if ((s = check_launch()) != DR_OK) return s;
+        hipLaunchKernelGGL((rev_compose_kernel<D>), dim3((unsigned)(chains * (D / 16))), dim3(kRevComposeThreads), 0,
+                           st, xmap, a.dhT, ein, NS);
+        if ((s = check_launch()) != DR_OK) return s;
+        e = ein;
     }
-    hipLaunchKernelGGL((rev_compose_kernel<D>), dim3((unsigned)(chains * (D / 16))), dim3(kRevComposeThreads), 0, st,
-                       xmap, a.dhT, ein, NS);
-    if ((s = check_launch()) != DR_OK) return s;
     hipLaunchKernelGGL((rev_seg_kernel<KIND, D, false>), dim3((unsigned)(chains * NS)), dim3(kRevThreads), 0, st,
-                       rrec, prep, dout, ein, xmap, dhs, dvn, a.dh0, a.T, a.H, a.NT, L, NS);
+                       rrec, prep, dout, e, xmap, dhs, dvn, a.dh0, a.T, a.H, a.NT, L, NS, a.pk);
     return check_launch();
 }
 
@@ -55,8 +58,8 @@ dr_status launch_backward_t(const BwdArgs& a, hipStream_t st) {
     const long long slices = (long long)a.B * a.H * (D / kSV);
     if (items > 0x7fffffffLL || slices > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
     // the segment-parallel reverse pass where its workspace is laid out
-    // (bf16 I/O, dense layout) unless the value-slice kernel is selected
-    const bool seg = std::is_same<E, bf16>::value && a.L.NS > 0 && !a.pk.table && rev_seg_selected();
+    // (bf16 I/O) unless the value-slice kernel is selected
+    const bool seg = std::is_same<E, bf16>::value && a.L.NS > 0 && rev_seg_selected();
     bf16* rrec = seg ? reinterpret_cast<bf16*>(a.ws + a.L.rrec) : nullptr;
     hipLaunchKernelGGL((bwd_prep_kernel<KIND, E, D>), dim3((unsigned)items), dim3(kPrepThreads), 0, st, q, k, a.g, a.beta,
                        prep, rrec, a.T, a.H, a.NT, a.pk);

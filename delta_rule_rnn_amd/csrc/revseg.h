@@ -145,8 +145,11 @@ __device__ __forceinline__ void rev_stage(const RevIn<KIND, DK>& in, uint8_t* sm
 
 // rev_seg_kernel: one workgroup per (chain, segment r); MAPS: r = 1 .. NS-1
 // (the grid holds chains * (NS - 1) workgroups), else r = 0 .. NS-1.
-//   rrec  [chains * NT] RevRec (bf16);  prep: phi of every chunk (fp32)
-//   ein   [chains][NS][DK][DV] fp32: E_r (OUT)
+// Packed sequences (pk.table set): OUT only, NS = 1, the chains of
+// locate_chain (a sequence without tokens writes dh0 = dhT).
+//   rrec  RevRec (bf16) per chunk index;  prep: phi of every chunk (fp32)
+//   ein   [chains][NS][DK][DV] fp32: E_r (OUT; with NS = 1 it is dhT, or
+//         null for a zero exit adjoint)
 //   xmap  [chains][NS][DK][2 DK] fp32: [Pi_r | N_r] (MAPS)
 //   dhs   [chains * NT][DK][DV], dvn [chains * NT][C][DV] bf16 (OUT)
 //   dh0   [chains][DK][DV] fp32 or null (OUT)
@@ -154,7 +157,7 @@ template <int KIND, int DK, bool MAPS>
 __global__ __launch_bounds__(kRevThreads, 1) void rev_seg_kernel(
     const bf16* __restrict__ rrec, const float* __restrict__ prep, const bf16* __restrict__ dout,
     const float* __restrict__ ein, float* __restrict__ xmap, bf16* __restrict__ dhs, bf16* __restrict__ dvn,
-    float* __restrict__ dh0, int Tlen, int H, int NT, int L, int NS)
+    float* __restrict__ dh0, int Tlen, int H, int NT, int L, int NS, Pack pk)
 {
     using Cfg = RevCfg<DK, MAPS>;
     using RR = RevRec<DK>;
@@ -176,15 +179,31 @@ __global__ __launch_bounds__(kRevThreads, 1) void rev_seg_kernel(
     const int nsg = MAPS ? NS - 1 : NS;
     const int chain = blockIdx.x / nsg;
     const int r = blockIdx.x % nsg + (MAPS ? 1 : 0);
-    const int b = chain / H, h = chain % H;
-    const int cbeg = r * L, cend = min(NT, cbeg + L);     // cbeg < cend: NS = ceil(NT / L)
+    const int h = chain % H;
+    // the chain's chunks: per-chunk index ci0 + c, token rows (tok0 + c C + p) H + h
+    size_t ci0, tok0;
+    int tlim, cbeg, cend;
+    if (pk.table) {
+        const ChainLoc cl = locate_chain(pk, chain, H, Tlen, NT);
+        ci0 = cl.ci0;
+        tok0 = cl.tok0;
+        tlim = cl.tlim;
+        cbeg = 0;
+        cend = cl.nseg;
+    } else {
+        ci0 = (size_t)chain * NT;
+        tok0 = (size_t)(chain / H) * Tlen;
+        tlim = Tlen;
+        cbeg = r * L;
+        cend = min(NT, cbeg + L);     // cbeg < cend: NS = ceil(NT / L)
+    }
     // this wave's columns of X: MAPS: waves < NACT/2 hold P, the others D
     const bool active = wave < NACT;
     const bool isD = MAPS ? wave >= NACT / 2 : true;
     const int col0 = (MAPS ? wave % (NACT / 2) : wave) * NCW;
 
     f32x4 X[NKB][2][NTW];
-    const float* e0 = ein + ((size_t)chain * NS + r) * DK * DV;
+    const float* e0 = ein ? ein + ((size_t)chain * NS + r) * DK * DV : nullptr;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -195,19 +214,19 @@ __global__ __launch_bounds__(kRevThreads, 1) void rev_seg_kernel(
                 for (int i = 0; i < 4; ++i) {
                     const int row = 32 * kb + 8 * grp + 4 * hh + i, col = col0 + 16 * n + r16;
                     if constexpr (MAPS) X[kb][hh][n][i] = (!isD && row == col) ? 1.f : 0.f;
-                    else X[kb][hh][n][i] = active ? e0[(size_t)row * DV + col] : 0.f;
+                    else X[kb][hh][n][i] = (active && ein) ? e0[(size_t)row * DV + col] : 0.f;
                 }
 
-    auto drow0_of = [&](int c) { return ((size_t)b * Tlen + (size_t)c * C) * H + h; };
-    auto nvalid_of = [&](int c) { return min(C, Tlen - c * C); };
+    auto drow0_of = [&](int c) { return (tok0 + (size_t)c * C) * H + h; };
+    auto nvalid_of = [&](int c) { return min(C, tlim - c * C); };
     auto load = [&](RevIn<KIND, DK>& in, int c) {
-        const size_t ci = (size_t)chain * NT + c;
+        const size_t ci = ci0 + c;
         rev_load<KIND, DK>(in, rrec + ci * RR::ELEMS, prep + ci * P::FLOATS, dout, drow0_of(c), nvalid_of(c), H, tid);
     };
     RevIn<KIND, DK> in;
-    load(in, cend - 1);
+    if (cend > cbeg) load(in, cend - 1);    // (a packed sequence may have no tokens)
     for (int c = cend - 1; c >= cbeg; --c) {
-        const size_t ci = (size_t)chain * NT + c;
+        const size_t ci = ci0 + c;
         rev_stage<KIND, DK, MAPS>(in, smem, nvalid_of(c), tid);
         load(in, max(c - 1, cbeg));           // the next chunk (the last reloads itself)
         lds_barrier();

@@ -61,14 +61,17 @@ def _check_seq(got, ref, kind, dt, a, b, i, what):
     assert_close_grad(dh0[i:i + 1], np.swapaxes(ref["dh0"], -1, -2), dt, f"{what} seq {i} dh0")
 
 
-CASES = [("kda", "bf16", 128), ("gdn", "bf16", 128), ("decay_la", "bf16", 128),
-         ("kda", "f32", 64), ("gdn", "f32", 64), ("decay_la", "f32", 64)]
+# bf16 I/O runs both reverse passes: the segment-parallel one (the default,
+# one segment per sequence and head) and the value-slice one
+CASES = [(kind, "bf16", 128, path) for kind in ("kda", "gdn", "decay_la") for path in ("segment", "slices")] + \
+        [("kda", "f32", 64, "slices"), ("gdn", "f32", 64, "slices"), ("decay_la", "f32", 64, "slices")]
 
 
-@pytest.mark.parametrize("kind,dt,D", CASES, ids=lambda c: str(c))
-def test_backward_varlen_matches_oracle_per_sequence(kind, dt, D):
+@pytest.mark.parametrize("kind,dt,D,path", CASES, ids=lambda c: str(c))
+def test_backward_varlen_matches_oracle_per_sequence(kind, dt, D, path, monkeypatch):
     """Ragged lengths: several chunks with a ragged tail, an empty sequence,
     one token, one short of a chunk, one chunk, one chunk plus one."""
+    monkeypatch.setenv("DR_BWD_REV", path)
     dra = _ops()
     lengths = [200, 0, 1, 63, 64, 65, 130, 7]
     x, h0, dhT, do, cu = _packed(kind, dt, D, lengths, seed=41)
