@@ -239,37 +239,6 @@ __device__ __forceinline__ f32x4 mmb(f32x4 acc, const float* A, int ar, const fl
     }
     return acc;
 }
-// The same product with each fp32 operand split into bf16 high and low parts
-// (x = hi + lo, lo = bf16(x - hi)): acc += A_hi B_hi + A_hi B_lo + A_lo B_hi,
-// three bf16 MFMAs per step, about 16 significant bits per operand.  For
-// operands that are not bf16 values themselves (the gate-scaled q and k of
-// per-channel gates), where a plain bf16 product loses the small results of
-// nearly orthogonal rows to the operands' rounding.
-__device__ __forceinline__ void split8(const f32x4& x0, const f32x4& x1, bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        hi[j] = (bf16)x0[j];
-        hi[4 + j] = (bf16)x1[j];
-        lo[j] = (bf16)(x0[j] - (float)hi[j]);
-        lo[4 + j] = (bf16)(x1[j] - (float)hi[4 + j]);
-    }
-}
-template <int K>
-__device__ __forceinline__ f32x4 mmb_split(f32x4 acc, const float* A, int ar, const float* B, int bc, int lane) {
-    const int r = lane & 15, q = lane >> 4;
-    const float* a = A + r * ar + 8 * q;
-    const float* b = B + r * bc + 8 * q;
-#pragma unroll
-    for (int k0 = 0; k0 < K; k0 += 32) {
-        bf16x8 ah, al, bh, bl;
-        split8(*reinterpret_cast<const f32x4*>(a + k0), *reinterpret_cast<const f32x4*>(a + k0 + 4), ah, al);
-        split8(*reinterpret_cast<const f32x4*>(b + k0), *reinterpret_cast<const f32x4*>(b + k0 + 4), bh, bl);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
-    }
-    return acc;
-}
 // Product with k contiguous in both operands, on the MFMA of the I/O dtype:
 // bf16 operands for bf16 I/O (as the forward's products), fp32 otherwise.
 template <typename T, int K>
@@ -578,10 +547,13 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const T* __restr
             const float* Aop = isL ? sA : sQ;
             const float* Bop = PERCH ? sB : sA;
             // both operands run along the key channels (contiguous): bf16 MFMA
-            // for bf16 I/O, as the forward's products; per-channel gates scale
-            // q and k off the bf16 grid, so their products take split operands
-            if constexpr (PERCH && sizeof(T) == 2)
-                acc = mmb_split<DK>(acc, Aop + ti * 16 * LDK, LDK, Bop + tj * 16 * LDK, LDK, lane);
+            // for bf16 I/O, as the forward's products, except Aqk under
+            // per-channel gates: q 2^gamma and k 2^-gamma are off the bf16
+            // grid, and rounding them loses the small Aqk of nearly orthogonal
+            // rows, which reaches dVnew = Aqk^T dO + ... and through it dv
+            // and dbeta; that product stays fp32
+            if (PERCH && !isL)
+                acc = mmk_ab<DK>(acc, Aop + ti * 16 * LDK, LDK, Bop + tj * 16 * LDK, LDK, lane);
             else
                 acc = mmc<T, DK>(acc, Aop + ti * 16 * LDK, LDK, Bop + tj * 16 * LDK, LDK, lane);
         }
