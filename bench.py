@@ -518,7 +518,7 @@ def prologue_bench(args):
     ms_unfused = timeit(unfused)
     tokens = w.B * w.T
     io_b = 2 if d["q"].dtype == torch.bfloat16 else 4
-    roof = whole_call_roofline("dr_forward_prologue (K1 with the prologue, K2)",
+    roof = whole_call_roofline("dr_forward (prologue fused into the forward's chunk kernel; all launches)",
                                call_bytes(w.kind, w, io_b, tokens, w.B * w.H, h0=d["h0"] is not None), ev_ms)
     cpu = None
     if not args.no_cpu_baseline:

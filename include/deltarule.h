@@ -335,14 +335,23 @@ dr_status dr_decode(int kind, const void* q, const void* k, const void* v, const
  *   dbeta: [B,T,H] float, written (delta kinds; ignored for decay_la)
  *   dh0:   [B,H,Dk,Dv] float, written, or NULL
  *   workspace: at least dr_backward_workspace_bytes(...): the recomputed
- *          fp32 chunk operands, the chunk entry states and exit adjoints
- *          (fp32 [Dk,Dv] per chunk) and Vnew / dVnew per chunk
+ *          chunk operands (fp32; for bf16 I/O also their bf16 copies for the
+ *          reverse pass), the chunk entry states S_c, exit adjoints dS'_c
+ *          ([Dk,Dv] per chunk) and Vnew_c (in the I/O dtype), dVnew_c (fp32),
+ *          and for bf16 I/O the reverse pass's segment maps and exit adjoints
+ * Reverse pass (the state adjoint): with bf16 I/O the segment-parallel one:
+ * the chunks of each (b, h) are grouped into segments, each segment's
+ * affine adjoint map is formed from an identity start, the maps are
+ * composed, and every segment is rerun from its true exit adjoint; the
+ * environment variable DR_BWD_REV=slices selects the value-slice kernel
+ * instead (the only one for fp32 I/O).
  * Precision: operands are held in fp32 and accumulated in fp32.  With fp32
- * I/O every product runs on fp32 MFMA.  With bf16 I/O the chunk-form L and
- * Aqk, and the gradient kernel's value-slice, pairwise and T products, take
- * their operands rounded to bf16 as they are read (bf16 MFMA, fp32
- * accumulation); the entry states come from the forward's state pass on the
- * bf16 records.
+ * I/O every product runs on fp32 MFMA.  With bf16 I/O the chunk-form L (and
+ * Aqk except under per-channel gates), the segment-parallel reverse pass,
+ * and the gradient kernel's value-slice, pairwise and T products take their
+ * operands rounded to bf16 as they are read (bf16 MFMA, fp32 accumulation),
+ * and S_c, dS'_c and Vnew_c are stored in bf16; the entry states come from
+ * the forward's state pass on the bf16 records.
  * Reproducibility: every reduction (the dbeta and dg partials of the waves
  * of a chunk, the per-head sums of dr_backward_prologue) adds its terms in a
  * fixed order, so repeated calls with the same arguments give bit-identical
@@ -411,8 +420,9 @@ dr_status dr_backward_prologue(int kind, const void* q, const void* k, const voi
  *          prologue that does something is passed: the chunk table and
  *          sequence descriptors, then dr_backward's per-chunk buffers for
  *          ceil(T/C) + N chunk slots per head (plus the prologue's part).
- * A sequence of length 0 gets dh0 = dhT (or zero).  Other conventions and
- * errors as for dr_backward.
+ * The segment-parallel reverse pass (bf16 I/O) takes one segment per
+ * sequence and head.  A sequence of length 0 gets dh0 = dhT (or zero).
+ * Other conventions and errors as for dr_backward.
  */
 size_t dr_backward_varlen_workspace_bytes(int kind, int N, int T, int H, int Dk, int Dv, int C, int dtype,
                                           int with_prologue);
