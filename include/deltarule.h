@@ -355,8 +355,11 @@ dr_status dr_decode(int kind, const void* q, const void* k, const void* v, const
  * Reproducibility: every reduction (the dbeta and dg partials of the waves
  * of a chunk, the per-head sums of dr_backward_prologue) adds its terms in a
  * fixed order, so repeated calls with the same arguments give bit-identical
- * results.  Other conventions and errors as for kda_fwd.  T = 0 writes dh0 =
- * dhT (or zero) and nothing else.  C must be 64.
+ * results.  Gate range: the backward raises no DR_FLAG_KM_* flags; they are
+ * those of the forward call on the same inputs, which is the caller's check
+ * (dr_backward_varlen's flags carries DR_FLAG_BAD_SEQLENS only).  Other
+ * conventions and errors as for kda_fwd.  T = 0 writes dh0 = dhT (or zero)
+ * and nothing else.  C must be 64.
  */
 size_t dr_backward_workspace_bytes(int kind, int B, int T, int H, int Dk, int Dv, int C, int dtype);
 dr_status dr_backward(int kind, const void* q, const void* k, const void* v, const float* g,
