@@ -278,6 +278,41 @@ __device__ __forceinline__ f32x4 mmb_g(f32x4 acc, const float* A, int ar, int ak
     }
     return acc;
 }
+// acc += A B on bf16 MFMA where B holds bf16 values exactly (slices of the
+// per-chunk state arrays, stored in bf16 for bf16 I/O), so that it converts
+// without loss, and A is fp32: split into bf16 high and low parts (x = hi +
+// lo, lo = bf16(x - hi)), two MFMAs per step, about 16 significant bits;
+// SPLIT false when A holds bf16 values too (one MFMA, exact).  Layouts as in
+// mmb_g.
+template <int K, bool ACONT, bool SPLIT>
+__device__ __forceinline__ f32x4 mms(f32x4 acc, const float* A, int ar, int ak, const float* B, int bk, int bc,
+                                     int lane) {
+    const int r = lane & 15, q = lane >> 4;
+#pragma unroll 1
+    for (int k0 = 0; k0 < K; k0 += 32) {
+        const int kk = k0 + 8 * q;
+        float av[8];
+        if constexpr (ACONT) {
+            const f32x4 a0 = *reinterpret_cast<const f32x4*>(A + r * ar + kk);
+            const f32x4 a1 = *reinterpret_cast<const f32x4*>(A + r * ar + kk + 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { av[j] = a0[j]; av[4 + j] = a1[j]; }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) av[j] = A[r * ar + (kk + j) * ak];
+        }
+        bf16x8 ah, al, fb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            ah[j] = (bf16)av[j];
+            al[j] = (bf16)(av[j] - (float)ah[j]);
+            fb[j] = (bf16)B[(kk + j) * bk + r * bc];
+        }
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, fb, acc, 0, 0, 0);
+        if constexpr (SPLIT) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, fb, acc, 0, 0, 0);
+    }
+    return acc;
+}
 // The pairwise products of the gradient kernel on the MFMA of the I/O
 // dtype: bf16 operands for bf16 I/O (as the value-slice products), fp32
 // otherwise.  ACONT as in mmb_g; the fp32 form takes mmk_a when A is
@@ -1046,8 +1081,18 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             const int ti = wave >> 1, tj = wave & 1;    // one [C][32] tile per wave
             if constexpr (DELTA) {
                 // P = N - M S_s (N = diag(beta) V), and dN = T^T dVnew -> dv, dbeta
-                const f32x4 x = mmk_a<DK>(zero4(), sKp + ti * 16 * LDK, LDK, s1 + tj * 16, LVS, 1, lane);
-                const f32x4 dn = mmk<C>(zero4(), sT + ti * 16, 1, LDC, dvn1 + tj * 16, LVS, 1, lane);
+                // fp32 I/O: fp32 MFMA.  bf16 I/O: the S and dVnew slices hold
+                // bf16 values, so bf16 MFMA with K+ (KDA; scalar gates: the
+                // bf16 k itself) and T split into high and low parts keeps
+                // about 16 bits of them (these products reach dv and dbeta)
+                f32x4 x, dn;
+                if constexpr (sizeof(T) == 2) {
+                    x = mms<DK, true, PERCH>(zero4(), sKp + ti * 16 * LDK, LDK, 1, s1 + tj * 16, LVS, 1, lane);
+                    dn = mms<C, false, true>(zero4(), sT + ti * 16, 1, LDC, dvn1 + tj * 16, LVS, 1, lane);
+                } else {
+                    x = mmk_a<DK>(zero4(), sKp + ti * 16 * LDK, LDK, s1 + tj * 16, LVS, 1, lane);
+                    dn = mmk<C>(zero4(), sT + ti * 16, 1, LDC, dvn1 + tj * 16, LVS, 1, lane);
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = ti * 16 + arow(lane, i), cc = tj * 16 + (lane & 15);
