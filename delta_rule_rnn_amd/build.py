@@ -10,7 +10,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ("deltarule.hip", "k_intra.hip", "k_inter.hip", "k_seg.hip", "k_bwd.hip", "k_misc.hip",
+SOURCES = ("deltarule.hip", "k_intra.hip", "k_inter.hip", "k_seg.hip", "k_bwd.hip", "k_gradb.hip", "k_misc.hip",
            "k_noalloc.hip")
 LIB = os.path.join(HERE, "libdeltarule.so")
 OBJDIR = os.path.join(os.path.dirname(HERE), "_build")

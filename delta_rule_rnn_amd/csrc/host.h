@@ -233,6 +233,14 @@ inline bool rev_seg_selected() {
     return !(e != nullptr && strcmp(e, "slices") == 0);
 }
 
+// The gradient kernel the backward takes for bf16 I/O: the one with bf16
+// LDS operands (gradb.h, two workgroups per CU), unless DR_BWD_GRAD=f32lds
+// selects the one with fp32 LDS operands (backward.h; fp32 I/O always).
+inline bool gradb_selected() {
+    const char* e = getenv("DR_BWD_GRAD");
+    return !(e != nullptr && strcmp(e, "f32lds") == 0);
+}
+
 // states S_c [DK][DV], the exit adjoints dS'_c [DK][DV], Vnew_c and dVnew_c
 // [C][DV] of every chunk, in the I/O dtype, each block 256-byte aligned.
 // Where the segment-parallel reverse pass is built: its bf16 chunk operands
@@ -294,6 +302,10 @@ struct BwdArgs {
     BwdLayout L;
     dr::bw::Pack pk;
 };
+
+template <int KIND, int D>
+dr_status launch_gradb(const BwdArgs& a, const float* prep, const bf16* hs, const bf16* dhs, const bf16* vn,
+                       const bf16* dvn, hipStream_t st);
 
 struct ProBwdLayout {
     size_t qh, kh, gh, bh, core, bytes;

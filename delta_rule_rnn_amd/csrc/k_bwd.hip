@@ -74,6 +74,9 @@ dr_status launch_backward_t(const BwdArgs& a, hipStream_t st) {
         s = check_launch();
     }
     if (s != DR_OK) return s;
+    if constexpr (std::is_same<E, bf16>::value) {
+        if (gradb_selected()) return launch_gradb<KIND, D>(a, prep, hs, dhs, vn, dvn, st);
+    }
     hipLaunchKernelGGL((bwd_grad_kernel<KIND, E, D>), dim3((unsigned)items), dim3(512), 0, st, q, k, v, a.beta, dout,
                        prep, hs, dhs, vn, dvn, static_cast<E*>(a.dq), static_cast<E*>(a.dk), static_cast<E*>(a.dv),
                        a.dg, a.dbeta, a.T, a.H, a.NT, a.pk);

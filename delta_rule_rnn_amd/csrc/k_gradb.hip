@@ -1,0 +1,31 @@
+// k_gradb.hip -- launcher of the bf16 gradient kernel (gradb.h).
+#include "host.h"
+#include "gradb.h"
+
+namespace drh {
+
+template <int KIND, int D>
+dr_status launch_gradb(const BwdArgs& a, const float* prep, const bf16* hs, const bf16* dhs, const bf16* vn,
+                       const bf16* dvn, hipStream_t st) {
+    using namespace dr::bw;
+    const long long items = a.pk.table ? (long long)a.pk.maxchunks * a.H : (long long)a.B * a.NT * a.H;
+    if (items > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL((bwd_gradb_kernel<KIND, D>), dim3((unsigned)items), dim3(kGradbThreads), 0, st,
+                       static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
+                       a.beta, static_cast<const bf16*>(a.dout), prep, hs, dhs, vn, dvn, static_cast<bf16*>(a.dq),
+                       static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.dg, a.dbeta, a.T, a.H, a.NT, a.pk);
+    return check_launch();
+}
+
+#define DR_GRADB(KIND, D)                                                                                         \
+    template dr_status launch_gradb<KIND, D>(const BwdArgs&, const float*, const bf16*, const bf16*, const bf16*, \
+                                            const bf16*, hipStream_t);
+DR_GRADB(dr::KIND_KDA, 64)
+DR_GRADB(dr::KIND_KDA, 128)
+DR_GRADB(dr::KIND_GDN, 64)
+DR_GRADB(dr::KIND_GDN, 128)
+DR_GRADB(dr::KIND_LA, 64)
+DR_GRADB(dr::KIND_LA, 128)
+#undef DR_GRADB
+
+}  // namespace drh
