@@ -403,6 +403,7 @@ __device__ __forceinline__ void unstage(D* __restrict__ dst, size_t gs, const fl
 
 // ===========================================================================
 constexpr int kPrepThreads = 512;
+constexpr unsigned PREP_W_GAM = 1, PREP_W_AQK = 2;
 
 // Prep: one 512-thread workgroup per (chunk, head, batch), heads fastest
 // (one workgroup per CU by LDS: eight waves keep loads and products in
@@ -421,7 +422,8 @@ template <int KIND, typename T, int DK>
 __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                        const float* __restrict__ g,
                                                        const float* __restrict__ beta, float* __restrict__ prep,
-                                                       bf16* __restrict__ rrec, int Tlen, int H, int NT, Pack pk)
+                                                       bf16* __restrict__ rrec, int Tlen, int H, int NT, Pack pk,
+                                                       unsigned wmask)
 {
     using P = Prep<DK>;
     using RR = RevRec<DK>;
@@ -450,6 +452,11 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const T* __restr
     // pass; the gradient kernel forms its own from q, k and gamma) are not
     // written
     bf16* rr = rrec ? rrec + loc.ci * RR::ELEMS : nullptr;
+    // the per-channel gamma and Aqk arrays only where a later kernel reads
+    // them (PREP_W_GAM: the gradient kernel with fp32 LDS operands;
+    // PREP_W_AQK: the value-slice reverse pass, and scalar gates' gradient
+    // kernels); the per-row gamma of scalar gates is always written
+    const bool wgam = (wmask & PREP_W_GAM) != 0, waqk = (wmask & PREP_W_AQK) != 0;
 
     // ---- inputs, rows past the end of a ragged chunk zero
     #pragma unroll 8
@@ -505,7 +512,7 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const T* __restr
             sA[r * LDK + d] = kk * e;
             sB[r * LDK + d] = kk * ei;
             sQ[r * LDK + d] *= e;
-            out[P::GAM + (size_t)r * DK + d] = run;
+            if (wgam) out[P::GAM + (size_t)r * DK + d] = run;
         }
         if (b == NB - 1) {
             const float phi = __builtin_amdgcn_exp2f(run);
@@ -604,7 +611,7 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const T* __restr
                 out[P::L + (size_t)r * C + cc] = x;
             } else {
                 x = cc <= r ? x : 0.f;
-                out[P::AQK + (size_t)r * C + cc] = x;
+                if (waqk) out[P::AQK + (size_t)r * C + cc] = x;
             }
             at[i] = (bf16)x;
         }

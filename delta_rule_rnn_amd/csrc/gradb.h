@@ -107,7 +107,7 @@ struct GradbSmem {
     // wave (5..8); scalar gates: the pair terms' row and column sums per wave,
     // the per-element E row sums per wave, the gamma_last sums per wave
     static constexpr int NDB = 9;
-    static constexpr int BT = BIG, GAM = BT + C * 4, PHI = GAM + C * 4, GL = PHI + DK * 4, DPHI = GL + DK * 4,
+    static constexpr int BT = BIG, GAM = BT + C * 4, PHI = GAM + C * 4, DPHI = PHI + DK * 4,
                          DB = DPHI + DK * 4, ER = DB + NDB * C * 4, EC = ER + (SCALAR ? 4 * C * 4 : 0),
                          RS = EC + (SCALAR ? 4 * C * 4 : 0), FP = RS + (SCALAR ? 4 * C * 4 : 0),
                          BYTES = FP + 16 * 4;
@@ -119,7 +119,8 @@ struct GradbSmem {
 template <int KIND, int DK>
 __global__ __launch_bounds__(kGradbThreads, 2) void bwd_gradb_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const float* __restrict__ beta, const bf16* __restrict__ dout, const float* __restrict__ prep,
+    const float* __restrict__ g, const float* __restrict__ beta, const bf16* __restrict__ dout,
+    const float* __restrict__ prep,
     const bf16* __restrict__ hs, const bf16* __restrict__ dhs, const bf16* __restrict__ vn,
     const bf16* __restrict__ dvn, bf16* __restrict__ dq, bf16* __restrict__ dk, bf16* __restrict__ dv,
     float* __restrict__ dg, float* __restrict__ dbeta, int Tlen, int H, int NT, Pack pk)
@@ -136,7 +137,6 @@ __global__ __launch_bounds__(kGradbThreads, 2) void bwd_gradb_kernel(
     float* sBt = F32(SM::BT);      // beta, zero past the end and for decay_la
     float* sGam = F32(SM::GAM);    // scalar gates: gamma per row
     float* sPhi = F32(SM::PHI);
-    float* sGl = F32(SM::GL);      // kda: gamma_last per column
     float* sDphi = F32(SM::DPHI);
     float* sDb = F32(SM::DB);
 
@@ -179,10 +179,7 @@ __global__ __launch_bounds__(kGradbThreads, 2) void bwd_gradb_kernel(
         sBt[tid] = tid < nvalid ? bb : 0.f;
         if constexpr (!PERCH) sGam[tid] = pc[P::GAM + tid];
     }
-    if (tid < DK) {
-        sPhi[tid] = pc[P::PHI + tid];
-        if constexpr (PERCH) sGl[tid] = pc[P::GAM + (size_t)(C - 1) * DK + tid];
-    }
+    if (tid < DK) sPhi[tid] = pc[P::PHI + tid];
     for (int i = tid; i < SM::NZ; i += kGradbThreads) sDb[i] = 0.f;
 
     // ---- phase 1: value slices of 32 columns, one slice ahead in registers
@@ -576,7 +573,7 @@ __global__ __launch_bounds__(kGradbThreads, 2) void bwd_gradb_kernel(
             // that no 64-bit address per row is kept in registers
             const char* qc = reinterpret_cast<const char*>(q + row0 * DK);
             const char* kc = reinterpret_cast<const char*>(k + row0 * DK);
-            const char* gc = reinterpret_cast<const char*>(pc + P::GAM);
+            const char* gc = reinterpret_cast<const char*>(g + row0 * DK);
             const unsigned rowb = (unsigned)(H * DK * 2);
             // the column and row bases laundered per tile: offsets are
             // recomputed rather than kept from the previous tile
@@ -591,18 +588,57 @@ __global__ __launch_bounds__(kGradbThreads, 2) void bwd_gradb_kernel(
                         // rows past the end load the last valid row (every
                         // load unconditional) and are zeroed
                         const int row = 32 * s + rb + 4 * h + r;
-                        const unsigned ob = (unsigned)min(row, nvalid - 1) * rowb + (unsigned)dl * 2u;
+                        const unsigned rc = (unsigned)min(row, nvalid - 1);
+                        const unsigned ob = rc * rowb + (unsigned)dl * 2u;
                         const bf16 qv = *reinterpret_cast<const bf16*>(qc + ob);
                         const bf16 kv = *reinterpret_cast<const bf16*>(kc + ob);
                         lq8[s][4 * h + r] = row < nvalid ? qv : (bf16)0.f;
                         lk8[s][4 * h + r] = row < nvalid ? kv : (bf16)0.f;
-                        if constexpr (PERCH)
-                            lg[s][h][r] = *reinterpret_cast<const float*>(gc + ((unsigned)row * DK + (unsigned)dl) * 4u);
-                        else
+                        if constexpr (PERCH) {
+                            const unsigned og = (rc * (unsigned)(H * DK) + (unsigned)dl) * 4u;
+                            const float gv = *reinterpret_cast<const float*>(gc + og);
+                            lg[s][h][r] = row < nvalid ? gv : 0.f;
+                        } else {
                             lg[s][h][r] = sGam[32 * s + 8 * g4 + 4 * h + r];
+                        }
                     }
         }
-        const float gl = PERCH ? sGl[d] : sGam[C - 1];
+        float gl;
+        if constexpr (PERCH) {
+            // gamma = log2(e) * cumsum of g down the column (rows past the
+            // end add zero): the lane's eight rows of each block, then the
+            // lane groups before it in the block, then block 0's total for
+            // block 1
+            float tot[2], ex[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                float run = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    run += lg[s][j >> 2][j & 3];
+                    lg[s][j >> 2][j & 3] = run;
+                }
+                float e0 = 0.f, t0 = 0.f;
+#pragma unroll
+                for (int gg = 0; gg < 4; ++gg) {
+                    const float x = __shfl(run, l16 + 16 * gg, 64);
+                    if (gg < g4) e0 += x;
+                    t0 += x;
+                }
+                ex[s] = e0;
+                tot[s] = t0;
+            }
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        lg[s][h][r] = kLog2e * (lg[s][h][r] + ex[s] + (s == 1 ? tot[0] : 0.f));
+            gl = kLog2e * (tot[0] + tot[1]);
+        } else {
+            gl = sGam[C - 1];
+        }
         float fpart = 0.f;
 #pragma unroll
         for (int s = 0; s < 2; ++s)

@@ -61,8 +61,14 @@ dr_status launch_backward_t(const BwdArgs& a, hipStream_t st) {
     // (bf16 I/O) unless the value-slice kernel is selected
     const bool seg = std::is_same<E, bf16>::value && a.L.NS > 0 && rev_seg_selected();
     bf16* rrec = seg ? reinterpret_cast<bf16*>(a.ws + a.L.rrec) : nullptr;
+    // the gradient kernel with bf16 LDS operands forms per-channel gamma from
+    // g itself; only scalar gates' gradient kernels and the value-slice
+    // reverse pass read Aqk
+    const bool gb = std::is_same<E, bf16>::value && gradb_selected();
+    const bool perch = KIND == dr::KIND_KDA;
+    const unsigned wmask = ((perch && gb) ? 0u : PREP_W_GAM) | ((perch && gb && seg) ? 0u : PREP_W_AQK);
     hipLaunchKernelGGL((bwd_prep_kernel<KIND, E, D>), dim3((unsigned)items), dim3(kPrepThreads), 0, st, q, k, a.g, a.beta,
-                       prep, rrec, a.T, a.H, a.NT, a.pk);
+                       prep, rrec, a.T, a.H, a.NT, a.pk, wmask);
     dr_status s = check_launch();
     if (s != DR_OK) return s;
     if constexpr (std::is_same<E, bf16>::value) {
@@ -75,7 +81,7 @@ dr_status launch_backward_t(const BwdArgs& a, hipStream_t st) {
     }
     if (s != DR_OK) return s;
     if constexpr (std::is_same<E, bf16>::value) {
-        if (gradb_selected()) return launch_gradb<KIND, D>(a, prep, hs, dhs, vn, dvn, st);
+        if (gb) return launch_gradb<KIND, D>(a, prep, hs, dhs, vn, dvn, st);
     }
     hipLaunchKernelGGL((bwd_grad_kernel<KIND, E, D>), dim3((unsigned)items), dim3(512), 0, st, q, k, v, a.beta, dout,
                        prep, hs, dhs, vn, dvn, static_cast<E*>(a.dq), static_cast<E*>(a.dk), static_cast<E*>(a.dv),

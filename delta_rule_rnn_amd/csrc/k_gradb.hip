@@ -12,7 +12,7 @@ dr_status launch_gradb(const BwdArgs& a, const float* prep, const bf16* hs, cons
     if (items > 0x7fffffffLL) return DR_ERR_UNSUPPORTED;
     hipLaunchKernelGGL((bwd_gradb_kernel<KIND, D>), dim3((unsigned)items), dim3(kGradbThreads), 0, st,
                        static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
-                       a.beta, static_cast<const bf16*>(a.dout), prep, hs, dhs, vn, dvn, static_cast<bf16*>(a.dq),
+                       a.g, a.beta, static_cast<const bf16*>(a.dout), prep, hs, dhs, vn, dvn, static_cast<bf16*>(a.dq),
                        static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.dg, a.dbeta, a.T, a.H, a.NT, a.pk);
     return check_launch();
 }
