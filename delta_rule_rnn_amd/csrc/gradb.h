@@ -554,13 +554,7 @@ __global__ __launch_bounds__(kGradbThreads, 2) void bwd_gradb_kernel(
     bf16x8 lastq[2], lastk[2];
     bf16* sStash = B16(SM::TR) + (size_t)(w * (CTW > 1 ? CTW - 1 : 1) * 64 + lane) * 32;
     static_assert(4 * (CTW > 1 ? CTW - 1 : 1) * 64 * 64 <= 3 * SM::CC, "stash fits T, dT, Y^T");
-    float rowE[2][2][4];
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) rowE[s][h][r] = 0.f;
+    float* sRS = F32(SM::RS);      // scalar gates: E row sums, one slot per wave
     float fpw = 0.f;
 #pragma unroll
     for (int c = 0; c < CTW; ++c) {
@@ -758,7 +752,11 @@ __global__ __launch_bounds__(kGradbThreads, 2) void bwd_gradb_kernel(
                     for (int r = 0; r < 4; ++r) {
                         ak[h][r] += dkk[r];
                         aq[h][r] += dqq[r];
-                        rowE[s][h][r] += aE[h][r];
+                        // E's row sum over the wave's columns: this tile's 16,
+                        // added to the slot after the previous tiles' in order
+                        const int row = 32 * s + 8 * g4 + 4 * h + r;
+                        const float x = row16_sum(aE[h][r]);
+                        if (l16 == 0) sRS[w * C + row] = (c == 0 ? 0.f : sRS[w * C + row]) + x;
                     }
                 }
             }
@@ -816,19 +814,8 @@ __global__ __launch_bounds__(kGradbThreads, 2) void bwd_gradb_kernel(
         asm volatile("" ::: "memory");
     }
     if constexpr (!PERCH) {
-        // E row sums over the wave's columns (lanes l16 of each row group),
-        // and the gamma_last sum, one slot per wave
-        float* sRS = F32(SM::RS);
+        // the gamma_last sum, one slot per wave
         float* sFP = F32(SM::FP);
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float x = row16_sum(rowE[s][h][r]);
-                    if (l16 == 0) sRS[w * C + 32 * s + 8 * g4 + 4 * h + r] = x;
-                }
         const float fp = lane_group_sum<64>(fpw);
         if (lane == 0) sFP[w] = fp;
     }

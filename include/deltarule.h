@@ -337,21 +337,27 @@ dr_status dr_decode(int kind, const void* q, const void* k, const void* v, const
  *   workspace: at least dr_backward_workspace_bytes(...): the recomputed
  *          chunk operands (fp32; for bf16 I/O also their bf16 copies for the
  *          reverse pass), the chunk entry states S_c, exit adjoints dS'_c
- *          ([Dk,Dv] per chunk) and Vnew_c (in the I/O dtype), dVnew_c (fp32),
- *          and for bf16 I/O the reverse pass's segment maps and exit adjoints
+ *          ([Dk,Dv] per chunk), Vnew_c and dVnew_c (all four in the I/O
+ *          dtype), and for bf16 I/O the reverse pass's segment maps and exit
+ *          adjoints
  * Reverse pass (the state adjoint): with bf16 I/O the segment-parallel one:
  * the chunks of each (b, h) are grouped into segments, each segment's
  * affine adjoint map is formed from an identity start, the maps are
  * composed, and every segment is rerun from its true exit adjoint; the
  * environment variable DR_BWD_REV=slices selects the value-slice kernel
  * instead (the only one for fp32 I/O).
- * Precision: operands are held in fp32 and accumulated in fp32.  With fp32
- * I/O every product runs on fp32 MFMA.  With bf16 I/O the chunk-form L (and
+ * Gradient kernel (dq, dk, dv, dg, dbeta per chunk): with bf16 I/O one whose
+ * operands are bf16 in LDS (two workgroups per compute unit), which forms
+ * the chunk's P = N - M S as (I + diag(beta) L) Vnew (the same matrix, since
+ * Vnew = (I + diag(beta) L)^-1 (N - M S)); DR_BWD_GRAD=f32lds selects the
+ * kernel with fp32 LDS operands instead (the only one for fp32 I/O).
+ * Precision: accumulation is fp32 throughout.  With fp32 I/O every product
+ * runs on fp32 MFMA with fp32 operands.  With bf16 I/O the chunk-form L (and
  * Aqk except under per-channel gates), the segment-parallel reverse pass,
- * and the gradient kernel's value-slice, pairwise and T products take their
- * operands rounded to bf16 as they are read (bf16 MFMA, fp32 accumulation),
- * and S_c, dS'_c and Vnew_c are stored in bf16; the entry states come from
- * the forward's state pass on the bf16 records.
+ * and the gradient kernel's products take bf16 operands (bf16 MFMA): its
+ * T^T dVnew product, which reaches dv, splits T into bf16 high and low
+ * parts; S_c, dS'_c, Vnew_c and dVnew_c are stored in bf16; the entry
+ * states come from the forward's state pass on the bf16 records.
  * Reproducibility: every reduction (the dbeta and dg partials of the waves
  * of a chunk, the per-head sums of dr_backward_prologue) adds its terms in a
  * fixed order, so repeated calls with the same arguments give bit-identical
