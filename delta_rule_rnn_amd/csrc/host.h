@@ -304,6 +304,8 @@ struct BwdArgs {
 };
 
 template <int KIND, int D>
+dr_status launch_prepb(const BwdArgs& a, float* prep, bf16* rrec, hipStream_t st);
+template <int KIND, int D>
 dr_status launch_gradb(const BwdArgs& a, const float* prep, const bf16* hs, const bf16* dhs, const bf16* vn,
                        const bf16* dvn, hipStream_t st);
 

@@ -67,9 +67,17 @@ dr_status launch_backward_t(const BwdArgs& a, hipStream_t st) {
     const bool gb = std::is_same<E, bf16>::value && gradb_selected();
     const bool perch = KIND == dr::KIND_KDA;
     const unsigned wmask = ((perch && gb) ? 0u : PREP_W_GAM) | ((perch && gb && seg) ? 0u : PREP_W_AQK);
-    hipLaunchKernelGGL((bwd_prep_kernel<KIND, E, D>), dim3((unsigned)items), dim3(kPrepThreads), 0, st, q, k, a.g, a.beta,
-                       prep, rrec, a.T, a.H, a.NT, a.pk, wmask);
-    dr_status s = check_launch();
+    dr_status s;
+    if constexpr (std::is_same<E, bf16>::value) {
+        // the bf16 prep (two workgroups per CU) writes what the segment-
+        // parallel reverse pass and the bf16 gradient kernel read
+        if (gb && seg) s = launch_prepb<KIND, D>(a, prep, rrec, st);
+    }
+    if (!(gb && seg)) {
+        hipLaunchKernelGGL((bwd_prep_kernel<KIND, E, D>), dim3((unsigned)items), dim3(kPrepThreads), 0, st, q, k, a.g,
+                           a.beta, prep, rrec, a.T, a.H, a.NT, a.pk, wmask);
+        s = check_launch();
+    }
     if (s != DR_OK) return s;
     if constexpr (std::is_same<E, bf16>::value) {
         if (seg) s = launch_rev_seg<KIND, D>(a, rrec, prep, dhs, dvn, st);
