@@ -208,25 +208,29 @@ dr_status backward_impl(int kind, const void* q, const void* k, const void* v, c
         rq = qh; rk = kh; rg = gh; rb = bh;
     }
     uint8_t* core = rest + table_bytes;
+    // forward state pass: the forward's chunk-parallel kernel writes the
+    // chunk records, the state-pass kernel in STATES mode the entry state and
+    // Vnew of every chunk (per-chunk arrays share the records' index, dense
+    // and packed).  On the bf16 prep path the prep writes the records the
+    // state pass reads, and both run inside launch_backward.
+    const bool fused = bwd_fused_prep(Dk, dtype);
+    Problem p = make_problem(kind, rq, rk, v, rg, rb, nullptr, chains, T, H, Dk, dtype, core + L.rec, nullptr);
     {
-        // forward state pass: the forward's chunk-parallel kernel writes the
-        // chunk records, the state-pass kernel in STATES mode the entry
-        // state and Vnew of every chunk (per-chunk arrays share the records'
-        // index, dense and packed)
-        Problem p = make_problem(kind, rq, rk, v, rg, rb, nullptr, chains, T, H, Dk, dtype, core + L.rec, nullptr);
         if (packed) {
             p.table = pk.table;
             p.seqinfo = pk.seqinfo;
             p.total = pk.total;
             p.maxchunks = pk.maxchunks;
         }
-        s = packed ? launch_intra_varlen(p, st) : launch_intra(p, 0, p.NT, st);
-        if (s != DR_OK) return s;
-        s = launch_states(p, h0, core + L.hs, core + L.vn, st);
-        if (s != DR_OK) return s;
+        if (!fused) {
+            s = packed ? launch_intra_varlen(p, st) : launch_intra(p, 0, p.NT, st);
+            if (s != DR_OK) return s;
+            s = launch_states(p, h0, core + L.hs, core + L.vn, st);
+            if (s != DR_OK) return s;
+        }
     }
     BwdArgs a{rq, rk, v, dout, rg, rb, h0, dhT, dq, dk, dv, dg, delta ? dbeta : nullptr, dh0,
-              chains, T, H, ceil_div(T, dr::kChunk), core, L, pk};
+              chains, T, H, ceil_div(T, dr::kChunk), core, L, pk, fused ? &p : nullptr};
     s = launch_backward(kind, a, Dk, dtype, st);
     if (s != DR_OK || !use_pro) return s;
     // gradients with respect to the raw inputs, in place; the gate

@@ -241,6 +241,14 @@ inline bool gradb_selected() {
     return !(e != nullptr && strcmp(e, "f32lds") == 0);
 }
 
+// The backward takes the bf16 prep (prepb.h) for bf16 I/O where the
+// segment-parallel reverse pass is built and selected and the bf16 gradient
+// kernel is selected; that prep also writes the forward state pass's
+// records, so the forward's chunk kernel does not run.
+inline bool bwd_fused_prep(int D, int dtype) {
+    return dtype == DR_BF16 && rev_seg_built(D, dtype) && rev_seg_selected() && gradb_selected();
+}
+
 // states S_c [DK][DV], the exit adjoints dS'_c [DK][DV], Vnew_c and dVnew_c
 // [C][DV] of every chunk, in the I/O dtype, each block 256-byte aligned.
 // Where the segment-parallel reverse pass is built: its bf16 chunk operands
@@ -301,10 +309,14 @@ struct BwdArgs {
     uint8_t* ws;
     BwdLayout L;
     dr::bw::Pack pk;
+    // bf16 prep path (bwd_fused_prep): the forward state pass's problem; the
+    // prep writes that pass's records, which then runs between the prep and
+    // the reverse pass.  Null: the caller has run the forward state pass.
+    const Problem* fwd;
 };
 
 template <int KIND, int D>
-dr_status launch_prepb(const BwdArgs& a, float* prep, bf16* rrec, hipStream_t st);
+dr_status launch_prepb(const BwdArgs& a, float* prep, bf16* rrec, uint8_t* recs, hipStream_t st);
 template <int KIND, int D>
 dr_status launch_gradb(const BwdArgs& a, const float* prep, const bf16* hs, const bf16* dhs, const bf16* vn,
                        const bf16* dvn, hipStream_t st);

@@ -71,13 +71,16 @@ dr_status launch_backward_t(const BwdArgs& a, hipStream_t st) {
     if constexpr (std::is_same<E, bf16>::value) {
         // the bf16 prep (two workgroups per CU) writes what the segment-
         // parallel reverse pass and the bf16 gradient kernel read
-        if (gb && seg) s = launch_prepb<KIND, D>(a, prep, rrec, st);
+        if (gb && seg) s = launch_prepb<KIND, D>(a, prep, rrec, a.fwd ? a.ws + a.L.rec : nullptr, st);
     }
     if (!(gb && seg)) {
+        if (a.fwd) return DR_ERR_UNSUPPORTED;     // only the bf16 prep writes the records
         hipLaunchKernelGGL((bwd_prep_kernel<KIND, E, D>), dim3((unsigned)items), dim3(kPrepThreads), 0, st, q, k, a.g,
                            a.beta, prep, rrec, a.T, a.H, a.NT, a.pk, wmask);
         s = check_launch();
     }
+    // the forward state pass on the prep's records (bf16 prep path)
+    if (s == DR_OK && a.fwd) s = launch_states(*a.fwd, a.h0, hs, vn, st);
     if (s != DR_OK) return s;
     if constexpr (std::is_same<E, bf16>::value) {
         if (seg) s = launch_rev_seg<KIND, D>(a, rrec, prep, dhs, dvn, st);

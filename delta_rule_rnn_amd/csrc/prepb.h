@@ -57,9 +57,9 @@ struct PrepbSmem {
 
 template <int KIND, int DK>
 __global__ __launch_bounds__(kPrepbThreads, 2) void bwd_prepb_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
-    const float* __restrict__ beta, float* __restrict__ prep, bf16* __restrict__ rrec, int Tlen, int H, int NT,
-    Pack pk)
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ g,
+    const float* __restrict__ beta, float* __restrict__ prep, bf16* __restrict__ rrec, uint8_t* __restrict__ recs,
+    int Tlen, int H, int NT, Pack pk)
 {
     using P = Prep<DK>;
     using RR = RevRec<DK>;
@@ -85,11 +85,18 @@ __global__ __launch_bounds__(kPrepbThreads, 2) void bwd_prepb_kernel(
     const size_t row0 = loc.row0;
     float* out = prep + loc.ci * P::FLOATS;
     bf16* rr = rrec + loc.ci * RR::ELEMS;
+    // the forward state pass's record of this chunk (its W, Kbar^T, U^T and
+    // phi fields, in the fragment order that pass reads), or null
+    using Rc = Rec<bf16, DK, DK>;
+    uint8_t* recb = recs ? recs + loc.ci * Rc::BYTES : nullptr;
+    bf16* rcW = recb ? reinterpret_cast<bf16*>(recb) + Rc::W : nullptr;
+    bf16* rcKb = recb ? reinterpret_cast<bf16*>(recb) + Rc::KBT : nullptr;
+    bf16* rcU = recb ? reinterpret_cast<bf16*>(recb) + Rc::UT : nullptr;
 
     // ---- inputs: channels ch0 .. ch0 + CPT - 1 at positions p0 .. p0 + 7;
     // rows past the end load the last valid row and are zeroed
     const int cg = tid % 32, qg = tid / 32, ch0 = CPT * cg, p0 = PL * qg;
-    VT kv[PL], qv[PL];
+    VT kv[PL], qv[PL], vv[PL];
     VG gv[PERCH ? PL : 1];
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
@@ -97,6 +104,12 @@ __global__ __launch_bounds__(kPrepbThreads, 2) void bwd_prepb_kernel(
         if constexpr (PERCH) gv[i] = *reinterpret_cast<const VG*>(g + off);
         kv[i] = *reinterpret_cast<const VT*>(k + off);
         qv[i] = *reinterpret_cast<const VT*>(q + off);
+    }
+    // v only for the record (U = T diag(beta) V; decay_la: V itself)
+    if (recb) {
+#pragma unroll
+        for (int i = 0; i < PL; ++i)
+            vv[i] = *reinterpret_cast<const VT*>(v + (row0 + (size_t)min(p0 + i, nvalid - 1) * H) * DK + ch0);
     }
     if (tid < C) {
         const float bb = DELTA ? beta[row0 + (size_t)min(tid, nvalid - 1) * H] : 0.f;
@@ -121,6 +134,7 @@ __global__ __launch_bounds__(kPrepbThreads, 2) void bwd_prepb_kernel(
         if (p0 + i >= nvalid) {
             kv[i] = VT{};
             qv[i] = VT{};
+            vv[i] = VT{};
             if constexpr (PERCH) gv[i] = VG{};
         }
     }
@@ -180,7 +194,7 @@ __global__ __launch_bounds__(kPrepbThreads, 2) void bwd_prepb_kernel(
         float phi[CPT];
 #pragma unroll
         for (int j = 0; j < CPT; ++j) phi[j] = __builtin_amdgcn_exp2f(glast[j]);
-        float qt[CPT][PL];
+        float qt[CPT][PL], kbt[CPT][PL];
 #pragma unroll
         for (int i = 0; i < PL; ++i) {
             const int p = p0 + i;
@@ -190,12 +204,10 @@ __global__ __launch_bounds__(kPrepbThreads, 2) void bwd_prepb_kernel(
                 const float kk = (float)kv[i][j], qq = (float)qv[i][j];
                 const float e = __builtin_amdgcn_exp2f(gam[i][j]), ei = __builtin_amdgcn_exp2f(-gam[i][j]);
                 qt[j][i] = qq * e;
-                if constexpr (PERCH) {
-                    // Kbar = (k 2^-gamma) 2^gamma_last, as the prep's
-                    kb[j] = (bf16)(kk * ei * phi[j]);
-                } else {
-                    kb[j] = (bf16)(kk * __builtin_amdgcn_exp2f(glast[j] - gam[i][j]));
-                }
+                // Kbar = (k 2^-gamma) 2^gamma_last, as the prep's (scalar
+                // gates: k 2^(gamma_last - gamma))
+                kbt[j][i] = PERCH ? kk * ei * phi[j] : kk * __builtin_amdgcn_exp2f(glast[j] - gam[i][j]);
+                kb[j] = (bf16)kbt[j][i];
             }
             *reinterpret_cast<VT*>(rr + RR::KB + (size_t)p * DK + ch0) = kb;
             if constexpr (PERCH) {
@@ -230,6 +242,39 @@ __global__ __launch_bounds__(kPrepbThreads, 2) void bwd_prepb_kernel(
 #pragma unroll
             for (int j = 0; j < CPT; ++j) ph[j] = phi[j];
             *reinterpret_cast<VG*>(out + P::PHI + ch0) = ph;
+            if (recb) *reinterpret_cast<VG*>(reinterpret_cast<float*>(recb + Rc::PHI_BYTE) + ch0) = ph;
+        }
+        if (recb) {
+            // the record's Kbar^T: channel ch is row prow(h, r) of key block
+            // ch/32 there, and this thread's eight positions are one
+            // fragment slot run (one 16-byte store per channel)
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) {
+                const int ch = ch0 + j, qq = ch & 31;
+                const int wk = ch >> 5, hh = (qq >> 2) & 1, rl = 4 * (qq >> 3) + (qq & 3);
+                bf16x8 x;
+#pragma unroll
+                for (int i = 0; i < PL; ++i) x[i] = (bf16)kbt[j][i];
+                *reinterpret_cast<bf16x8*>(rcKb + ((size_t)((wk * 2 + hh) * (C / 32) + (p0 >> 5)) * 64 + rl +
+                                                   16 * ((p0 & 31) >> 3)) * 8) = x;
+            }
+            if constexpr (!DELTA) {
+                // decay_la: the state pass reads V from the U slot: U[32(w/2) +
+                // 8(l/16) + 4(w%2) + i][16t + l%16], four positions per store
+#pragma unroll
+                for (int j = 0; j < CPT; ++j) {
+                    const int ch = ch0 + j;
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        bf16x4 x;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) x[i] = vv[4 * hf + i][j];
+                        const int wv = 2 * (p0 >> 5) + hf;
+                        *reinterpret_cast<bf16x4*>(rcU + ((size_t)((ch >> 4) * 4 + wv) * 64 + (ch & 15) +
+                                                          16 * ((p0 & 31) >> 3)) * 4) = x;
+                    }
+                }
+            }
         }
     }
     lds_barrier();
@@ -400,6 +445,71 @@ __global__ __launch_bounds__(kPrepbThreads, 2) void bwd_prepb_kernel(
     for (int it_ = 0; it_ < (C * C) / (4 * kPrepbThreads); ++it_) {
         const int idx = tid + it_ * kPrepbThreads, r = idx >> 4, c4 = (idx & 15) * 4;
         *reinterpret_cast<f32x4*>(out + P::TI + (size_t)r * C + c4) = *reinterpret_cast<const f32x4*>(sT + r * LDF + c4);
+    }
+
+    // ---- the record's W and U^T (T split into bf16 high and low parts):
+    // W^T = M^T T^T over tiles whose rows (channels) follow prow() and whose
+    // columns (positions) follow pw(), so that a lane's two accumulators of a
+    // key block are its fragment-order slot run of W; U = T (diag(beta) V)
+    // with rows in pw() order, as the record's U^T slots
+    if (recb) {
+        // (beta V)^T to R0 (beta L, read by the solve, is dead)
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            bf16x8 x;
+#pragma unroll
+            for (int i = 0; i < PL; ++i) x[i] = (bf16)(sBeta[p0 + i] * (float)vv[i][j]);
+            *reinterpret_cast<bf16x8*>(r0 + (ch0 + j) * LDQ + p0) = x;
+        }
+        lds_barrier();
+        // the T row of position pos, k-step ks, split into high and low parts
+        auto trow = [&](int pos, int ks, bf16x8& hi, bf16x8& lo) {
+            const int ko = 32 * ks + 8 * g4;
+            const f32x4 a0 = *reinterpret_cast<const f32x4*>(sT + pos * LDF + ko);
+            const f32x4 a1 = *reinterpret_cast<const f32x4*>(sT + pos * LDF + ko + 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                hi[j] = (bf16)a0[j];
+                hi[4 + j] = (bf16)a1[j];
+                lo[j] = (bf16)(a0[j] - (float)hi[j]);
+                lo[4 + j] = (bf16)(a1[j] - (float)hi[4 + j]);
+            }
+        };
+        constexpr int NKB = DK / 32;
+#pragma unroll 1
+        for (int pi = w; pi < 4 * NKB; pi += 4) {
+            const int wr = pi / NKB, kb = pi % NKB, pos = pw(wr, l16);
+            f32x4 acc[2] = {zero4(), zero4()};
+            for (int ks = 0; ks <= (wr >> 1); ++ks) {       // T[pos][j] = 0 for j > pos
+                bf16x8 bh, bl;
+                trow(pos, ks, bh, bl);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const bf16x8 a = ld8(r3 + (32 * kb + prow(h, l16)) * LDQ + 32 * ks + 8 * g4);
+                    acc[h] = mf(a, bh, acc[h]);
+                    acc[h] = mf(a, bl, acc[h]);
+                }
+            }
+            bf16x8 f;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) f[4 * h + r] = (bf16)acc[h][r];
+            *reinterpret_cast<bf16x8*>(rcW + ((size_t)(wr * NKB + kb) * 64 + lane) * 8) = f;
+        }
+#pragma unroll 1
+        for (int ui = w; ui < 4 * (DK / 16); ui += 4) {
+            const int wr = ui & 3, t = ui >> 2, pos = pw(wr, l16);
+            f32x4 acc = zero4();
+            for (int ks = 0; ks <= (wr >> 1); ++ks) {
+                bf16x8 ah, al;
+                trow(pos, ks, ah, al);
+                const bf16x8 b = ld8(r0 + (16 * t + l16) * LDQ + 32 * ks + 8 * g4);
+                acc = mf(ah, b, acc);
+                acc = mf(al, b, acc);
+            }
+            *reinterpret_cast<bf16x4*>(rcU + ((size_t)(t * 4 + wr) * 64 + lane) * 4) = pack4(acc);
+        }
     }
 
     // ---- W = T M over (C/16) x (DK/16) tiles, eight per wave (T split into
