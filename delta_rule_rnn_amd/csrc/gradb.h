@@ -103,10 +103,10 @@ struct GradbSmem {
     static constexpr int BIG0 = END1 > END2 ? END1 : END2;
     static constexpr int BIG = BIG0 > END3 ? BIG0 : END3;
     // fp32 vectors.  dbeta partial slots [NDB][C], each row written by one
-    // wave: the value-slice products (slot 0), dM per wave and column tile
-    // (1 .. 4 CTW), dA per wave (the last four); scalar gates: the pair terms' row and column sums per wave,
+    // wave: the value-slice products (slot 0), dM per wave (1..4), dA per
+    // wave (5..8); scalar gates: the pair terms' row and column sums per wave,
     // the per-element E row sums per wave, the gamma_last sums per wave
-    static constexpr int NDB = 1 + 4 * (DK / 64) + 4;
+    static constexpr int NDB = 9;
     static constexpr int BT = BIG, GAM = BT + C * 4, PHI = GAM + C * 4, DPHI = PHI + DK * 4,
                          DB = DPHI + DK * 4, ER = DB + NDB * C * 4, EC = ER + (SCALAR ? 4 * C * 4 : 0),
                          RS = EC + (SCALAR ? 4 * C * 4 : 0), FP = RS + (SCALAR ? 4 * C * 4 : 0),
@@ -454,49 +454,6 @@ __global__ __launch_bounds__(kGradbThreads, 2) void bwd_gradb_kernel(
         if (lane % LPD == 0) sDphi[w * DPW + lane / LPD] = dphi;
     }
 
-    // per-element inputs of the wave's elements (rows 32 s + 8 g4 + j, j =
-    // 4 h + r, column ccol(c)): q and k as bf16 (exact), g (kda) or the
-    // row's gamma, loaded at the start of their column tile (loading them
-    // ahead, across phase 2b, kept more loads in flight than the registers
-    // hold and made the kernel slower)
-    bf16x8 Lq[CTW][2], Lk[CTW][2];
-    f32x4 Lg[CTW][2][2];
-    auto load_elems = [&](int c) {
-        const int d = ccol(c);
-        // byte offsets from the chunk's first row (wave-uniform bases), so
-        // that no 64-bit address per row is kept in registers
-        const char* qc = reinterpret_cast<const char*>(q + row0 * DK);
-        const char* kc = reinterpret_cast<const char*>(k + row0 * DK);
-        const char* gc = reinterpret_cast<const char*>(g + row0 * DK);
-        const unsigned rowb = (unsigned)(H * DK * 2);
-        // the column and row bases laundered per tile: offsets are
-        // recomputed rather than kept from the previous tile
-        int dl = d, rb = 8 * g4;
-        asm volatile("" : "+v"(dl), "+v"(rb));
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    // rows past the end load the last valid row (every
-                    // load unconditional) and are zeroed
-                    const int row = 32 * s + rb + 4 * h + r;
-                    const unsigned rc = (unsigned)min(row, nvalid - 1);
-                    const unsigned ob = rc * rowb + (unsigned)dl * 2u;
-                    const bf16 qv = *reinterpret_cast<const bf16*>(qc + ob);
-                    const bf16 kv = *reinterpret_cast<const bf16*>(kc + ob);
-                    Lq[c][s][4 * h + r] = row < nvalid ? qv : (bf16)0.f;
-                    Lk[c][s][4 * h + r] = row < nvalid ? kv : (bf16)0.f;
-                    if constexpr (PERCH) {
-                        const unsigned og = (rc * (unsigned)(H * DK) + (unsigned)dl) * 4u;
-                        const float gv = *reinterpret_cast<const float*>(gc + og);
-                        Lg[c][s][h][r] = row < nvalid ? gv : 0.f;
-                    } else {
-                        Lg[c][s][h][r] = sGam[32 * s + 8 * g4 + 4 * h + r];
-                    }
-                }
-    };
     lds_barrier();
 
     // ---- phase 2b (it needs only dT, T, beta and L, so it runs before the
@@ -557,7 +514,7 @@ __global__ __launch_bounds__(kGradbThreads, 2) void bwd_gradb_kernel(
                     const float da = j < i ? -acc[rr] : 0.f;
                     float dl = sBt[i] * da;
                     const float part = row16_sum(da * lrc[t][rr]);
-                    if (l16 == 0) sDb[(1 + 4 * CTW + w) * C + i] = part;
+                    if (l16 == 0) sDb[(5 + w) * C + i] = part;
                     if constexpr (!PERCH) {
                         cval[rr] = dl * lrc[t][rr];
                         dl *= j < i ? __builtin_amdgcn_exp2f(sGam[i] - sGam[j]) : 0.f;
@@ -602,9 +559,44 @@ __global__ __launch_bounds__(kGradbThreads, 2) void bwd_gradb_kernel(
 #pragma unroll
     for (int c = 0; c < CTW; ++c) {
         const int d = ccol(c);
-        load_elems(c);
-        bf16x8 lq8[2] = {Lq[c][0], Lq[c][1]}, lk8[2] = {Lk[c][0], Lk[c][1]};
-        f32x4 ee[2][2], lg[2][2] = {{Lg[c][0][0], Lg[c][0][1]}, {Lg[c][1][0], Lg[c][1][1]}};
+        // q and k of rows 32 s + 8 g4 + j (j = 4 h + r), kept as bf16 (exact)
+        bf16x8 lq8[2], lk8[2];
+        f32x4 ee[2][2], lg[2][2];
+        {
+            // byte offsets from the chunk's first row (wave-uniform bases), so
+            // that no 64-bit address per row is kept in registers
+            const char* qc = reinterpret_cast<const char*>(q + row0 * DK);
+            const char* kc = reinterpret_cast<const char*>(k + row0 * DK);
+            const char* gc = reinterpret_cast<const char*>(g + row0 * DK);
+            const unsigned rowb = (unsigned)(H * DK * 2);
+            // the column and row bases laundered per tile: offsets are
+            // recomputed rather than kept from the previous tile
+            int dl = d, rb = 8 * g4;
+            asm volatile("" : "+v"(dl), "+v"(rb));
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        // rows past the end load the last valid row (every
+                        // load unconditional) and are zeroed
+                        const int row = 32 * s + rb + 4 * h + r;
+                        const unsigned rc = (unsigned)min(row, nvalid - 1);
+                        const unsigned ob = rc * rowb + (unsigned)dl * 2u;
+                        const bf16 qv = *reinterpret_cast<const bf16*>(qc + ob);
+                        const bf16 kv = *reinterpret_cast<const bf16*>(kc + ob);
+                        lq8[s][4 * h + r] = row < nvalid ? qv : (bf16)0.f;
+                        lk8[s][4 * h + r] = row < nvalid ? kv : (bf16)0.f;
+                        if constexpr (PERCH) {
+                            const unsigned og = (rc * (unsigned)(H * DK) + (unsigned)dl) * 4u;
+                            const float gv = *reinterpret_cast<const float*>(gc + og);
+                            lg[s][h][r] = row < nvalid ? gv : 0.f;
+                        } else {
+                            lg[s][h][r] = sGam[32 * s + 8 * g4 + 4 * h + r];
+                        }
+                    }
+        }
         float gl;
         if constexpr (PERCH) {
             // gamma = log2(e) * cumsum of g down the column (rows past the
@@ -709,10 +701,10 @@ __global__ __launch_bounds__(kGradbThreads, 2) void bwd_gradb_kernel(
                         // M = diag(beta) K+: dk += beta e dM, E += dM M, dbeta += dM K+
                         ak[h][r] += bt * e * dm;
                         aE[h][r] += dm * bt * kp;
-                        // this tile's 16 columns of row `row`, one slot per
-                        // wave and column tile
+                        // the wave's columns of row `row`: this tile's 16, added
+                        // to the slot after the previous tiles' in order
                         const float part = row16_sum(dm * kp);
-                        if (l16 == 0) sDb[(1 + w * CTW + c) * C + row] = part;
+                        if (l16 == 0) sDb[(1 + w) * C + row] = (c == 0 ? 0.f : sDb[(1 + w) * C + row]) + part;
                     }
                 }
             }
