@@ -874,7 +874,7 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_rev_kernel(const floa
             if constexpr (DELTA) gw.store(sW, LDT, tid);
             load_b(cn);
             constexpr int NS = (DK * kSV) / 4 < NC ? (DK * kSV) / 4 : NC;
-            if (tid < NS) unstage<DK, kSV, NS>(dhs + ci * DK * DV + dv0, DV, sD, LSV, tid);
+            if (tid < NS) unstage<DK, kSV, NS>(dhs + ci * DK * DV + slc(0, dv0, DK), 32, sD, LSV, tid);
             // the lines of the chunk after the one in flight into L2
             if (c > 1) {
                 const float* pn = prep + (ci - 2) * P::FLOATS;
@@ -910,7 +910,7 @@ __global__ __launch_bounds__(kStateThreads) void bwd_state_rev_kernel(const floa
                 const int r = tid / (kSV / 4), c4 = (tid % (kSV / 4)) * 4;
                 const f32x4 x = *reinterpret_cast<const f32x4*>(sDV + r * LSV + c4);
                 const f32x4 y = *reinterpret_cast<const f32x4*>(sDV2 + r * LSV + c4);
-                st4(dvn + ci * C * DV + dv0 + (size_t)r * DV + c4, x + y);
+                st4(dvn + ci * C * DV + slc(r, dv0 + c4, C), x + y);
             }
         }
         lds_barrier();
@@ -1055,10 +1055,11 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     constexpr int NE = (C * kVS) / 512;
     float xd[NE], xv[NE];
     auto load_slice = [&](int dv0) {
-        g1.load(hs + ci * DK * DV + dv0, DV, tid);
-        g2.load(dhs + ci * DK * DV + dv0, DV, tid);
-        g3.load(vn + ci * C * DV + dv0, DV, tid);
-        g4.load(dvn + ci * C * DV + dv0, DV, tid);
+        // one slice of the slice-major state arrays (slc()): contiguous
+        g1.load(hs + ci * DK * DV + slc(0, dv0, DK), 32, tid);
+        g2.load(dhs + ci * DK * DV + slc(0, dv0, DK), 32, tid);
+        g3.load(vn + ci * C * DV + slc(0, dv0, C), 32, tid);
+        g4.load(dvn + ci * C * DV + slc(0, dv0, C), 32, tid);
 #pragma unroll
         for (int it_ = 0; it_ < NE; ++it_) {
             const int idx = tid + it_ * 512, r = idx / kVS, cc = idx % kVS;

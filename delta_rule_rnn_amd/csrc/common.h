@@ -319,6 +319,15 @@ __device__ __forceinline__ int prow(int half, int r) { return 8 * (r >> 2) + 4 *
 // owns the 16 positions of 32-block w/2 selected by prow(w%2, .).
 __device__ __forceinline__ int pw(int w, int r) { return 32 * (w >> 1) + prow(w & 1, r); }
 
+// The backward's per-chunk state arrays ([rows][D] matrices: the entry
+// states S_c, Vnew_c and their adjoints) are stored slice-major: 32-column
+// slices, each a contiguous [rows][32] block, so that a kernel reading one
+// value slice takes whole cache lines.  Element (row, col) of a [rows][D]
+// array:
+__host__ __device__ constexpr size_t slc(int row, int col, int rows) {
+    return (size_t)(col >> 5) * rows * 32 + (size_t)row * 32 + (col & 31);
+}
+
 // ---------------------------------------------------------------------------
 // Chunk record: the operands the sequential pass streams, one record per
 // (b, h, chunk).  Offsets in elements of the I/O type T except phi (float).

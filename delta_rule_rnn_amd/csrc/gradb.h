@@ -198,11 +198,11 @@ __global__ __launch_bounds__(kGradbThreads, 2) void bwd_gradb_kernel(
 #pragma unroll
         for (int j = 0; j < NUS; ++j) {
             const int u = tid + j * kGradbThreads, d = u >> 2, c8 = (u & 3) * 8;
-            rS[j] = ld8(hs + ci * DK * DV + (size_t)d * DV + dv0 + c8);
-            rDS[j] = ld8(dhs + ci * DK * DV + (size_t)d * DV + dv0 + c8);
+            rS[j] = ld8(hs + ci * DK * DV + slc(d, dv0 + c8, DK));
+            rDS[j] = ld8(dhs + ci * DK * DV + slc(d, dv0 + c8, DK));
         }
-        rVn = ld8(vn + ci * C * DV + (size_t)pp * DV + dv0 + pc8);
-        rDVn = ld8(dvn + ci * C * DV + (size_t)pp * DV + dv0 + pc8);
+        rVn = ld8(vn + ci * C * DV + slc(pp, dv0 + pc8, C));
+        rDVn = ld8(dvn + ci * C * DV + slc(pp, dv0 + pc8, C));
         rDO = ld8(dout + (row0 + (size_t)min(pp, nvalid - 1) * H) * DV + dv0 + pc8);
         if constexpr (DELTA) {
             const int r = 16 * w + l16;

@@ -186,7 +186,8 @@ constexpr int inter_threads() { return 2 * 64 * InterShape<C2>::NW + (PFD > 0 ? 
 // STATES (the backward's forward state pass): instead of o, write for every
 // chunk its entry state S_c ([DK][DV] at states + r*DK*DV) and Vnew_c
 // ([C][DV] at vnew + r*C*DV), both in the I/O type (rounded from the fp32
-// accumulators), r the chunk's record index; the output
+// accumulators) and slice-major (slc(), common.h), r the chunk's record
+// index; the output
 // waves only keep the barriers.  Rows of a ragged last chunk past the end
 // get Vnew = 0 (their record rows are zero).
 //
@@ -321,14 +322,14 @@ __global__ __launch_bounds__((inter_threads<PFD, C2>())) void inter_kernel(const
             if constexpr (STATES) {
                 // the chunk's entry state, as the final state is written
                 if (ownS) {
-                    T* sc = states + (rec0 + c) * (size_t)DK * DV + dv0 + r16;
+                    T* sc = states + (rec0 + c) * (size_t)DK * DV;
 #pragma unroll
                     for (int half = 0; half < NH; ++half)
 #pragma unroll
                         for (int n = 0; n < NTN; ++n)
 #pragma unroll
                             for (int i = 0; i < 4; ++i)
-                                sc[(size_t)srow(half, i) * DV + 16 * n] = from_f<T>(S[half][n][i]);
+                                sc[slc(srow(half, i), dv0 + 16 * n + r16, DK)] = from_f<T>(S[half][n][i]);
                 }
             }
             // phase A: Vnew at this lane's 4 positions
@@ -351,10 +352,10 @@ __global__ __launch_bounds__((inter_threads<PFD, C2>())) void inter_kernel(const
                 st4(&sV[kbP][n][lane][4 * halfP], vn);
                 if constexpr (STATES) {
                     // positions 32(w/2) + 8(l/16) + 4(w%2) + i, the layout of U
-                    T* vc = vnew + (rec0 + c) * (size_t)C * DV + dv0 + 16 * n + r16;
+                    T* vc = vnew + (rec0 + c) * (size_t)C * DV;
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        vc[(size_t)(32 * kbP + 8 * grp + 4 * halfP + i) * DV] = from_f<T>(vn[i]);
+                        vc[slc(32 * kbP + 8 * grp + 4 * halfP + i, dv0 + 16 * n + r16, C)] = from_f<T>(vn[i]);
                 }
             }
             lds_barrier();

@@ -233,7 +233,8 @@ __global__ __launch_bounds__(kRevThreads, 1) void rev_seg_kernel(
         if (active) {
             if constexpr (!MAPS) {
                 // dS'_c: the adjoint of this chunk's exit state
-                bf16* dst = dhs + ci * DK * DV + col0 + r16;
+                // (slice-major, slc())
+                bf16* dst = dhs + ci * DK * DV;
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -242,7 +243,7 @@ __global__ __launch_bounds__(kRevThreads, 1) void rev_seg_kernel(
                         for (int n = 0; n < NTW; ++n)
 #pragma unroll
                             for (int i = 0; i < 4; ++i)
-                                dst[(size_t)(32 * kb + 8 * grp + 4 * hh + i) * DV + 16 * n] = (bf16)X[kb][hh][n][i];
+                                dst[slc(32 * kb + 8 * grp + 4 * hh + i, col0 + 16 * n + r16, DK)] = (bf16)X[kb][hh][n][i];
             }
             // dO^T fragments of this wave's columns (D columns only)
             Frag<bf16> dof[2][NTW];
@@ -289,7 +290,7 @@ __global__ __launch_bounds__(kRevThreads, 1) void rev_seg_kernel(
             if constexpr (!MAPS) {
                 // dVnew_c (rows past a ragged end are zero: Kbar's and
                 // Aqk^T's are)
-                bf16* dst = dvn + ci * C * DV + col0 + r16;
+                bf16* dst = dvn + ci * C * DV;
 #pragma unroll
                 for (int kbp = 0; kbp < 2; ++kbp)
 #pragma unroll
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(kRevThreads, 1) void rev_seg_kernel(
                         for (int n = 0; n < NTW; ++n)
 #pragma unroll
                             for (int i = 0; i < 4; ++i)
-                                dst[(size_t)(32 * kbp + 8 * grp + 4 * hh + i) * DV + 16 * n] = (bf16)Y[kbp][hh][n][i];
+                                dst[slc(32 * kbp + 8 * grp + 4 * hh + i, col0 + 16 * n + r16, C)] = (bf16)Y[kbp][hh][n][i];
             }
             // X <- Diag(phi) X - W^T Y (+ Q~^T dO)
             Frag<bf16> Yf[2][NTW];
