@@ -25,8 +25,8 @@
 //   already; T is split into high and low bf16 parts for the product that
 //   reaches dv), each stored so that the product reads it along contiguous
 //   elements, with rows padded by 16 bytes.
-// - Wave w owns key columns [w Dk/4, (w+1) Dk/4) of every [C][Dk] result (all
-//   64 rows).  Its tile rows are permuted by prow(): tile (s, h) row r holds
+// - Wave w owns the key columns of column tiles w and w + 4 (d = 128; tile w
+//   at d = 64) of every [C][Dk] result (all 64 rows).  Its tile rows are permuted by prow(): tile (s, h) row r holds
 //   chunk row 32 s + prow(h, r), so a lane's accumulators of the two tiles of
 //   block s hold rows 32 s + 8 (l/16) + 0..7 of its column, which is a
 //   natural B fragment.  The later products over chunk positions (T^T dW,
@@ -146,8 +146,11 @@ __global__ __launch_bounds__(kGradbThreads, 2) void bwd_gradb_kernel(
     const int nvalid = loc.nvalid;
     const size_t row0 = loc.row0, ci = loc.ci;
     const float* pc = prep + ci * P::FLOATS;
-    // the wave's column tiles and the chunk row of permuted tile (s, h) row l16
-    auto ccol = [&](int c) { return 16 * (w * CTW + c) + l16; };
+    // the wave's column tiles, w and w + 4 (d = 128): for each tile index c
+    // the four waves hold 64 adjacent columns, so that their per-element
+    // loads and dg stores of one tile take whole cache lines together; and
+    // the chunk row of permuted tile (s, h) row l16
+    auto ccol = [&](int c) { return 16 * (w + 4 * c) + l16; };
     auto prw = [&](int s, int h) { return 32 * s + prow(h, l16); };
 
     // ---- set-up: T^T (high, low), L, beta, gamma, phi; zeroed slots
