@@ -102,6 +102,22 @@ def test_backward_reverse_pass_paths(kind, D, path, B, H, T, monkeypatch):
     _check(res, ref, kind, "bf16", f"{kind} D{D} {path} T={T}")
 
 
+@pytest.mark.parametrize("grad", ["bf16lds", "f32lds"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("kind", ["kda", "gdn", "decay_la"])
+def test_backward_gradient_kernel_paths(kind, D, grad, monkeypatch):
+    """bf16 I/O: the gradient kernel with bf16 LDS operands (the default,
+    with the bf16 prep that also writes the state pass's records) and the one
+    with fp32 LDS operands (DR_BWD_GRAD=f32lds, with the forward's chunk
+    kernel and the fp32-operand prep), each against the oracle: 2 batches
+    of 3 chunks (the last ragged) and a 260-token chain of 5 chunks."""
+    monkeypatch.setenv("DR_BWD_GRAD", grad)
+    monkeypatch.delenv("DR_BWD_REV", raising=False)
+    for (B, H, T, seed) in ((2, 2, 150, 81), (1, 3, 260, 82)):
+        res, ref = _run(kind, "bf16", D, B=B, H=H, T=T, seed=seed)
+        _check(res, ref, kind, "bf16", f"{kind} D{D} {grad} T={T}")
+
+
 def test_backward_many_chains_one_segment(monkeypatch):
     """256 chains fill the GPU by themselves: the segment-parallel pass runs
     each chain as one segment (no maps, no composition)."""
