@@ -351,13 +351,18 @@ dr_status dr_decode(int kind, const void* q, const void* k, const void* v, const
  * the chunk's P = N - M S as (I + diag(beta) L) Vnew (the same matrix, since
  * Vnew = (I + diag(beta) L)^-1 (N - M S)); DR_BWD_GRAD=f32lds selects the
  * kernel with fp32 LDS operands instead (the only one for fp32 I/O).
- * Precision: accumulation is fp32 throughout.  With fp32 I/O every product
+ * Chunk operands: on the path that takes both bf16 kernels above (the
+ * default for bf16 I/O) one kernel recomputes them and also writes the chunk
+ * records the forward state pass reads, so the forward's record kernel does
+ * not run; on the other paths it runs first and a separate kernel
+ * recomputes the operands in fp32.
+ * Precision: accumulation is fp32 throughout. With fp32 I/O every product
  * runs on fp32 MFMA with fp32 operands.  With bf16 I/O the chunk-form L (and
- * Aqk except under per-channel gates), the segment-parallel reverse pass,
- * and the gradient kernel's products take bf16 operands (bf16 MFMA): its
- * T^T dVnew product, which reaches dv, splits T into bf16 high and low
- * parts; S_c, dS'_c, Vnew_c and dVnew_c are stored in bf16; the entry
- * states come from the forward's state pass on the bf16 records.
+ * Aqk except under per-channel gates), the segment-parallel reverse pass, and
+ * the gradient kernel's products take bf16 operands (bf16 MFMA): where an
+ * fp32 operand reaches dv or dbeta directly (T, and L in P) it is split into
+ * bf16 high and low parts; S_c, dS'_c, Vnew_c and dVnew_c are stored in bf16;
+ * the entry states come from the forward's state pass on the bf16 records.
  * Reproducibility: every reduction (the dbeta and dg partials of the waves
  * of a chunk, the per-head sums of dr_backward_prologue) adds its terms in a
  * fixed order, so repeated calls with the same arguments give bit-identical
