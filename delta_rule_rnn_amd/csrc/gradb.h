@@ -75,6 +75,8 @@ __device__ __forceinline__ void tile_up(int id, int& it, int& jt) {
     jt = id < 3 ? id + 1 : id < 5 ? id - 1 : 3;
 }
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
 // LDS regions (byte offsets) of one workgroup.
 template <int KIND, int DK>
 struct GradbSmem {
@@ -559,6 +561,17 @@ __global__ __launch_bounds__(kGradbThreads, 2) void bwd_gradb_kernel(
     static_assert(4 * (CTW > 1 ? CTW - 1 : 1) * 64 * 64 <= 3 * SM::CC, "stash fits T, dT, Y^T");
     float* sRS = F32(SM::RS);      // scalar gates: E row sums, one slot per wave
     float fpw = 0.f;
+    // lane bases of the fp32 vectors, kept opaque to the compiler: they lie
+    // above 64 KB of LDS, past the 16-bit offset field of the LDS
+    // instructions, so a constant address per row would take a register of
+    // its own; from a base, each row is the instruction's offset
+    const float* sBtg = sBt + 8 * g4;                 // rows 8 g4 + j
+    float* sDbg = sDb + (1 + w) * C + 8 * g4;         // the wave's dM slot
+    float* sRSg = sRS + w * C + 8 * g4;
+    const float* sPhc = sPhi + 16 * w + l16;          // column 16 w + l16
+    asm volatile("" : "+v"(sBtg), "+v"(sDbg), "+v"(sRSg), "+v"(sPhc));
+    const float* sGamg = sBtg + (SM::GAM - SM::BT) / 4;
+    const float* sDphc = sPhc + (SM::DPHI - SM::PHI) / 4;
 #pragma unroll
     for (int c = 0; c < CTW; ++c) {
         const int d = ccol(c);
@@ -596,9 +609,19 @@ __global__ __launch_bounds__(kGradbThreads, 2) void bwd_gradb_kernel(
                             const float gv = *reinterpret_cast<const float*>(gc + og);
                             lg[s][h][r] = row < nvalid ? gv : 0.f;
                         } else {
-                            lg[s][h][r] = sGam[32 * s + 8 * g4 + 4 * h + r];
+                            lg[s][h][r] = sGamg[32 * s + 4 * h + r];
                         }
                     }
+        }
+        // q and k stay packed, two rows per register (16 registers, not 32
+        // of one element each): opaque words, unpacked where they are used
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            u32x4 pq = __builtin_bit_cast(u32x4, lq8[s]), pk = __builtin_bit_cast(u32x4, lk8[s]);
+            asm volatile("" : "+v"(pq[0]), "+v"(pq[1]), "+v"(pq[2]), "+v"(pq[3]));
+            asm volatile("" : "+v"(pk[0]), "+v"(pk[1]), "+v"(pk[2]), "+v"(pk[3]));
+            lq8[s] = __builtin_bit_cast(bf16x8, pq);
+            lk8[s] = __builtin_bit_cast(bf16x8, pk);
         }
         float gl;
         if constexpr (PERCH) {
@@ -667,7 +690,7 @@ __global__ __launch_bounds__(kGradbThreads, 2) void bwd_gradb_kernel(
             float fp = fpart;
             fp += __shfl_xor(fp, 16, 64);
             fp += __shfl_xor(fp, 32, 64);
-            F = fp + sDphi[d] * sPhi[d];
+            F = fp + sDphc[64 * c] * sPhc[64 * c];            // column d
         } else {
             fpw += fpart;
         }
@@ -697,17 +720,17 @@ __global__ __launch_bounds__(kGradbThreads, 2) void bwd_gradb_kernel(
                         acc = mf(ld8(sTT + pr * LC + 32 * sp + 8 * g4), nWf[sp][c], acc);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int row = 32 * s + 8 * g4 + 4 * h + r;
-                        const float bt = sBt[row];
+                        const int o = 32 * s + 4 * h + r;          // row 8 g4 + o
+                        const float bt = sBtg[o];
                         const float dm = -acc[r], e = ee[s][h][r];
                         const float kp = (float)lk8[s][4 * h + r] * e;     // K+ = k e
                         // M = diag(beta) K+: dk += beta e dM, E += dM M, dbeta += dM K+
                         ak[h][r] += bt * e * dm;
                         aE[h][r] += dm * bt * kp;
-                        // the wave's columns of row `row`: this tile's 16, added
+                        // the wave's columns of the row: this tile's 16, added
                         // to the slot after the previous tiles' in order
                         const float part = row16_sum(dm * kp);
-                        if (l16 == 0) sDb[(1 + w) * C + row] = (c == 0 ? 0.f : sDb[(1 + w) * C + row]) + part;
+                        if (l16 == 0) sDbg[o] = (c == 0 ? 0.f : sDbg[o]) + part;
                     }
                 }
             }
@@ -757,9 +780,9 @@ __global__ __launch_bounds__(kGradbThreads, 2) void bwd_gradb_kernel(
                         aq[h][r] += dqq[r];
                         // E's row sum over the wave's columns: this tile's 16,
                         // added to the slot after the previous tiles' in order
-                        const int row = 32 * s + 8 * g4 + 4 * h + r;
                         const float x = row16_sum(aE[h][r]);
-                        if (l16 == 0) sRS[w * C + row] = (c == 0 ? 0.f : sRS[w * C + row]) + x;
+                        const int o = 32 * s + 4 * h + r;          // row 8 g4 + o
+                        if (l16 == 0) sRSg[o] = (c == 0 ? 0.f : sRSg[o]) + x;
                     }
                 }
             }
