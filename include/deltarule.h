@@ -359,10 +359,11 @@ dr_status dr_decode(int kind, const void* q, const void* k, const void* v, const
  * Precision: accumulation is fp32 throughout. With fp32 I/O every product
  * runs on fp32 MFMA with fp32 operands.  With bf16 I/O the chunk-form L (and
  * Aqk except under per-channel gates), the segment-parallel reverse pass, and
- * the gradient kernel's products take bf16 operands (bf16 MFMA): where an
- * fp32 operand reaches dv or dbeta directly (T, and L in P) it is split into
- * bf16 high and low parts; S_c, dS'_c, Vnew_c and dVnew_c are stored in bf16;
- * the entry states come from the forward's state pass on the bf16 records.
+ * the gradient kernel's products take bf16 operands (bf16 MFMA): in the
+ * product T^T dVnew, which gives dv and dbeta's value term, T is split into
+ * bf16 high and low parts; S_c, dS'_c, Vnew_c and dVnew_c are stored in
+ * bf16; the entry states come from the forward's state pass on the bf16
+ * records.
  * Reproducibility: every reduction (the dbeta and dg partials of the waves
  * of a chunk, the per-head sums of dr_backward_prologue) adds its terms in a
  * fixed order, so repeated calls with the same arguments give bit-identical
