@@ -76,6 +76,7 @@ __device__ __forceinline__ void tile_up(int id, int& it, int& jt) {
 }
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) float lds_f32;   // a float in LDS
 
 // LDS regions (byte offsets) of one workgroup.
 template <int KIND, int DK>
@@ -564,14 +565,16 @@ __global__ __launch_bounds__(kGradbThreads, 2) void bwd_gradb_kernel(
     // lane bases of the fp32 vectors, kept opaque to the compiler: they lie
     // above 64 KB of LDS, past the 16-bit offset field of the LDS
     // instructions, so a constant address per row would take a register of
-    // its own; from a base, each row is the instruction's offset
-    const float* sBtg = sBt + 8 * g4;                 // rows 8 g4 + j
-    float* sDbg = sDb + (1 + w) * C + 8 * g4;         // the wave's dM slot
-    float* sRSg = sRS + w * C + 8 * g4;
-    const float* sPhc = sPhi + 16 * w + l16;          // column 16 w + l16
+    // its own; from a base, each row is the instruction's offset.  Typed as
+    // LDS pointers, so that the accesses stay LDS instructions (a generic
+    // pointer through the asm would become flat accesses)
+    lds_f32* sBtg = (lds_f32*)(sBt + 8 * g4);                 // rows 8 g4 + j
+    lds_f32* sDbg = (lds_f32*)(sDb + (1 + w) * C + 8 * g4);   // the wave's dM slot
+    lds_f32* sRSg = (lds_f32*)(sRS + w * C + 8 * g4);
+    lds_f32* sPhc = (lds_f32*)(sPhi + 16 * w + l16);          // column 16 w + l16
     asm volatile("" : "+v"(sBtg), "+v"(sDbg), "+v"(sRSg), "+v"(sPhc));
-    const float* sGamg = sBtg + (SM::GAM - SM::BT) / 4;
-    const float* sDphc = sPhc + (SM::DPHI - SM::PHI) / 4;
+    lds_f32* sGamg = sBtg + (SM::GAM - SM::BT) / 4;
+    lds_f32* sDphc = sPhc + (SM::DPHI - SM::PHI) / 4;
 #pragma unroll
     for (int c = 0; c < CTW; ++c) {
         const int d = ccol(c);
