@@ -44,13 +44,15 @@ namespace dr {
 constexpr int kSegThreads = 512;            // 8 waves, one workgroup per CU
 constexpr int kSegTargetGroups = 256;       // segments are sized to give about this many workgroups
 
-// LDS plan of seg_kernel (bytes).  Regions are reused across phases:
-//   KP  K+ [C][LDK]                         P1 -> P4
-//   KM  K- [C][LDK] (P1 -> P2), then U^T [DV][LDC] (P4 -> P5)
+// LDS plan of seg_kernel (bytes).  Regions are reused across phases (P5 is
+// the state step):
+//   KP  K+ [C][LDK]                         P1 -> P5
+//   KM  K- [C][LDK] (P1 -> P2), then T diag(beta) [C][LDC] in the I/O type
+//       (P3 -> P5)
 //   QP  Q~ [C][LDK]                         P1 -> P5
-//   A   A fp32 [C][LDF] (P2 -> P3), then W [C][LDK] (P4 -> P5)
-//   TT  per-group gate totals and their prefixes (P1), then T fp32 [C][LDF]
-//   VT  V^T [DV][LDC]                       P1 -> P4 (decay_la: -> P5)
+//   A   A fp32 [C][LDF]                     P2 -> P3
+//   TT  per-group gate totals and their prefixes (P1), then T fp32 [C][LDF] (P3)
+//   VT  V^T [DV][LDC]                       P1 -> P5
 //   KBT Kbar^T [DK][LDC]                    P1 -> P5
 //   AQK Aqk [C][LDC]                        P2 -> P5
 //   beta [C], gamma [C] (scalar gates), phi [DK] floats
@@ -117,20 +119,31 @@ __device__ __forceinline__ void seg_load(SegIn<KIND, T, DK, DV>& in, const T* __
     const int lane = tid & 63;
     const int last = nvalid - 1;
     const int ch0 = CPT * (tid % NCG), p0 = (tid / NCG) * PL;
+    // byte offsets from the chunk's first row (wave-uniform bases in scalar
+    // registers): no 64-bit address per load
+    const char* qc = reinterpret_cast<const char*>(q + row0 * DK);
+    const char* kc = reinterpret_cast<const char*>(k + row0 * DK);
+    const char* vc = reinterpret_cast<const char*>(v + row0 * DV);
+    const char* gc = reinterpret_cast<const char*>(g + row0 * (KIND == KIND_KDA ? DK : 1));
+    const char* bc = reinterpret_cast<const char*>(beta + row0);
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
-        const size_t off = (row0 + (size_t)min(p0 + i, last) * H) * DK + ch0;
-        if constexpr (KIND == KIND_KDA) in.gv[i] = *reinterpret_cast<const VG*>(g + off);
-        in.kv[i] = *reinterpret_cast<const VT*>(k + off);
-        in.qv[i] = *reinterpret_cast<const VT*>(q + off);
+        const unsigned rr = (unsigned)min(p0 + i, last) * (unsigned)H;
+        const unsigned ek = rr * (unsigned)DK + (unsigned)ch0;
+        if constexpr (KIND == KIND_KDA) in.gv[i] = *reinterpret_cast<const VG*>(gc + ek * 4u);
+        in.kv[i] = *reinterpret_cast<const VT*>(kc + ek * (unsigned)sizeof(T));
+        in.qv[i] = *reinterpret_cast<const VT*>(qc + ek * (unsigned)sizeof(T));
     }
     // every thread loads (waves past the first re-read rows already fetched)
     // so that the loads are unconditional
-    if constexpr (KIND != KIND_KDA) in.gs = g[row0 + (size_t)min(lane, last) * H];
-    if constexpr (KIND != KIND_LA) in.bt = beta[row0 + (size_t)min(lane, last) * H];
+    const unsigned rl = (unsigned)min(lane, last) * (unsigned)H * 4u;
+    if constexpr (KIND != KIND_KDA) in.gs = *reinterpret_cast<const float*>(gc + rl);
+    if constexpr (KIND != KIND_LA) in.bt = *reinterpret_cast<const float*>(bc + rl);
 #pragma unroll
-    for (int i = 0; i < PL; ++i)
-        in.vv[i] = *reinterpret_cast<const VT*>(v + (row0 + (size_t)min(p0 + i, last) * H) * DV + ch0);
+    for (int i = 0; i < PL; ++i) {
+        const unsigned ev = (unsigned)min(p0 + i, last) * (unsigned)(H * DV) + (unsigned)ch0;
+        in.vv[i] = *reinterpret_cast<const VT*>(vc + ev * (unsigned)sizeof(T));
+    }
 }
 
 // Pack two accumulator tiles (rows 8q..8q+3 and 8q+4..8q+7 of a 32-row block)
@@ -149,7 +162,8 @@ __device__ __forceinline__ Frag<T> pack_frag(const f32x4& lo, const f32x4& hi) {
 // ---------------------------------------------------------------------------
 // Steps a1-a3 of one chunk into LDS (P0-P3).  On return (after a barrier)
 // LDS holds K+ (KP), Q~ (QP), V^T (VT), Kbar^T (KBT), Aqk (AQK), phi (PHI)
-// and, for the delta kinds, T = (I + A)^-1 (TT, fp32) and beta.  The state
+// and, for the delta kinds, T = (I + A)^-1 (TT, fp32), T diag(beta) in the
+// I/O type (KM) and beta.  The state
 // step forms the chunk's pseudo values as Y = T diag(beta) (U_bar - K+ X),
 // the product U - W X of the UT transform taken in the other order, so W and
 // U are never materialised.
@@ -437,6 +451,11 @@ __device__ __forceinline__ void seg_chunk_ops(const SegIn<KIND, T, DK, DV>& in, 
     // The factors are powers of N and commute; the six dependent 16x16
     // products run on fp32 MFMA with the powers kept in an LDS block of T
     // that the later products never read (blocks (0,2), (0,3), (1,2), (1,3)).
+    // T diag(beta) in the I/O type, row-major [C][LDC], over K- (dead after
+    // P2): the state step's operand, written by the wave that finishes each
+    // block
+    T* sTb = reinterpret_cast<T*>(smem + Cfg::R_KM);
+    static_assert((size_t)C * LDC * sizeof(T) <= Cfg::R_QP - Cfg::R_KM, "T diag(beta) fits K-");
     if (wave < 4) {
         const int blk = wave;
         float* Tb = sT + 16 * blk * LDF + 16 * blk;                             // the diagonal block
@@ -460,13 +479,21 @@ __device__ __forceinline__ void seg_chunk_ops(const SegIn<KIND, T, DK, DV>& in, 
             P = Pw;
             t = mm16_lds(Tb, LDF, Pw, LDF, lane, t);                                   // T <- T (I + P)
         }
+        const float bc = sBeta[16 * blk + r16];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Tb[(4 * grp + i) * LDF + r16] = t[i];
+        for (int i = 0; i < 4; ++i) {
+            Tb[(4 * grp + i) * LDF + r16] = t[i];
+            sTb[(16 * blk + 4 * grp + i) * LDC + 16 * blk + r16] = from_f<T>(t[i] * bc);
+        }
     } else if (wave < 6) {
         // T01 and T23 are read by the 32-wide products below: zero
         float* z = sT + 16 * 2 * (wave - 4) * LDF + 16 * (2 * (wave - 4) + 1);
+        T* zb = sTb + 16 * 2 * (wave - 4) * LDC + 16 * (2 * (wave - 4) + 1);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) z[(4 * grp + i) * LDF + r16] = 0.f;
+        for (int i = 0; i < 4; ++i) {
+            z[(4 * grp + i) * LDF + r16] = 0.f;
+            zb[(4 * grp + i) * LDC + r16] = from_f<T>(0.f);
+        }
     }
     lds_barrier();
 #pragma unroll
@@ -477,8 +504,12 @@ __device__ __forceinline__ void seg_chunk_ops(const SegIn<KIND, T, DK, DV>& in, 
             for (int m = j; m < i; ++m)
                 y = mm16_lds(sA + 16 * i * LDF + 16 * m, LDF, sT + 16 * m * LDF + 16 * j, LDF, lane, y);
             const f32x4 z = mm16_acc(sT + 16 * i * LDF + 16 * i, LDF, y, lane);
+            const float bc = sBeta[16 * j + r16];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sT[(16 * i + 4 * grp + e) * LDF + 16 * j + r16] = -z[e];
+            for (int e = 0; e < 4; ++e) {
+                sT[(16 * i + 4 * grp + e) * LDF + 16 * j + r16] = -z[e];
+                sTb[(16 * i + 4 * grp + e) * LDC + 16 * j + r16] = from_f<T>(-z[e] * bc);
+            }
         }
         lds_barrier();
     }
@@ -545,8 +576,7 @@ __global__ __launch_bounds__(kSegThreads, 1) void seg_kernel(
     const T* sQp = reinterpret_cast<const T*>(smem + Cfg::R_QP);
     const T* sKp = reinterpret_cast<const T*>(smem + Cfg::R_KP);
     const T* sV = reinterpret_cast<const T*>(smem + Cfg::R_VT);
-    const float* sT = reinterpret_cast<const float*>(smem + Cfg::R_TT);
-    const float* sBeta = reinterpret_cast<const float*>(smem + Cfg::R_BETA);
+    const T* sTb = reinterpret_cast<const T*>(smem + Cfg::R_KM);   // T diag(beta)
     const T* sKbT = reinterpret_cast<const T*>(smem + Cfg::R_KBT);
     const T* sAqk = reinterpret_cast<const T*>(smem + Cfg::R_AQK);
     const float* sPhi = reinterpret_cast<const float*>(smem + Cfg::R_PHI);
@@ -641,11 +671,7 @@ __global__ __launch_bounds__(kSegThreads, 1) void seg_kernel(
                     for (int n = 0; n < NTW; ++n) Y[kbo][hh][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kbi = 0; kbi <= kbo; ++kbi) {
-                        const float* trow = sT + (32 * kbo + prow(hh, r16)) * LDF + 32 * kbi + 8 * grp;
-                        const float* brow = sBeta + 32 * kbi + 8 * grp;
-                        Frag<T> ft;
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) frag_set(ft, j, trow[j] * brow[j]);
+                        const Frag<T> ft = ld_frag(sTb + (32 * kbo + prow(hh, r16)) * LDC + 32 * kbi + 8 * grp);
 #pragma unroll
                         for (int n = 0; n < NTW; ++n) mma(Y[kbo][hh][n], ft, Rf[kbi][n]);
                     }
