@@ -496,23 +496,44 @@ __device__ __forceinline__ void seg_chunk_ops(const SegIn<KIND, T, DK, DV>& in, 
         }
     }
     lds_barrier();
+    // the 32-row diagonal halves, then the lower-left 32 x 32 block:
+    // T10 = -T11 A10 T00 and T32 = -T33 A32 T22 (waves 0, 1); then
+    // T[2:4][0:2] = -T[2:4][2:4] A[2:4][0:2] T[0:2][0:2], one 16 x 16 block
+    // (i, j) per wave, the inner product Y = A[2:4][0:2] T[0:2][j] kept in
+    // the wave's accumulators
+    auto put = [&](int i, int j, const f32x4& z) {
+        const float bc = sBeta[16 * j + r16];
 #pragma unroll
-    for (int dist = 1; dist <= 3; ++dist) {
-        if (wave < 4 - dist) {
-            const int i = wave + dist, j = wave;
-            f32x4 y = {0.f, 0.f, 0.f, 0.f};
-            for (int m = j; m < i; ++m)
-                y = mm16_lds(sA + 16 * i * LDF + 16 * m, LDF, sT + 16 * m * LDF + 16 * j, LDF, lane, y);
-            const f32x4 z = mm16_acc(sT + 16 * i * LDF + 16 * i, LDF, y, lane);
-            const float bc = sBeta[16 * j + r16];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sT[(16 * i + 4 * grp + e) * LDF + 16 * j + r16] = -z[e];
-                sTb[(16 * i + 4 * grp + e) * LDC + 16 * j + r16] = from_f<T>(-z[e] * bc);
-            }
+        for (int e = 0; e < 4; ++e) {
+            sT[(16 * i + 4 * grp + e) * LDF + 16 * j + r16] = -z[e];
+            sTb[(16 * i + 4 * grp + e) * LDC + 16 * j + r16] = from_f<T>(-z[e] * bc);
         }
-        lds_barrier();
+    };
+    if (wave < 2) {
+        const int i = 2 * wave + 1, j = 2 * wave;
+        const f32x4 y = mm16_lds(sA + 16 * i * LDF + 16 * j, LDF, sT + 16 * j * LDF + 16 * j, LDF, lane,
+                                 f32x4{0.f, 0.f, 0.f, 0.f});
+        put(i, j, mm16_acc(sT + 16 * i * LDF + 16 * i, LDF, y, lane));
     }
+    lds_barrier();
+    if (wave < 4) {
+        const int i = 2 + (wave >> 1), j = wave & 1;
+        auto yrow = [&](int r) {        // (A[2:4][0:2] T[0:2][j]) block row r
+            f32x4 y = {0.f, 0.f, 0.f, 0.f};
+            for (int m = j; m < 2; ++m)
+                y = mm16_lds(sA + 16 * r * LDF + 16 * m, LDF, sT + 16 * m * LDF + 16 * j, LDF, lane, y);
+            return y;
+        };
+        const f32x4 y2 = yrow(2);
+        f32x4 z = mm16_acc(sT + 16 * i * LDF + 32, LDF, y2, lane);          // T(i, 2) Y(2)
+        if (i == 3) {
+            const f32x4 z3 = mm16_acc(sT + 48 * LDF + 48, LDF, yrow(3), lane);   // T(3, 3) Y(3)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) z[e] += z3[e];
+        }
+        put(i, j, z);
+    }
+    lds_barrier();
 }
 
 // ---------------------------------------------------------------------------
