@@ -162,8 +162,9 @@ def test_backward_long_sampled():
 
 def test_backward_full_size_sampled():
     """The benchmark workload (KDA bf16, B=1, H=32, T=32768, d=128) through
-    the same call bench.py --mode backward times; every gradient of one
-    sampled head against the oracle run on that head alone."""
+    the same call bench.py --mode backward times; every gradient of three
+    sampled heads (the first, one inside, the last: different workgroups of
+    every launch) against the oracle run on each head alone."""
     dra = _ops()
     from delta_rule_rnn_amd.inputs import WORKLOADS
     w = WORKLOADS["kda_bf16_long"]
@@ -174,13 +175,14 @@ def test_backward_full_size_sampled():
     d = to_dev(x)
     res = dra.backward("kda", d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], do.to("cuda:0"), dhT.to("cuda:0"))
     torch.cuda.synchronize()
-    h = 13
-    sl = lambda t: t[:, :, h:h + 1].contiguous()
-    ref = recurrence_backward("kda", sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]), None,
-                              sl(do), dhT[:, h:h + 1].transpose(-1, -2))
-    for n, r in zip(["dq", "dk", "dv", "dg", "dbeta"], res[:5]):
-        assert_close_grad(r[:, :, h:h + 1].float().cpu().numpy(), ref[n], "bf16", f"full size head {h} {n}")
-    assert_close_grad(res[5][:, h:h + 1].cpu().numpy(), np.swapaxes(ref["dh0"], -1, -2), "bf16", f"full size head {h} dh0")
+    res = [t.float().cpu().numpy() for t in res]
+    for h in (0, 13, w.H - 1):
+        sl = lambda t: t[:, :, h:h + 1].contiguous()
+        ref = recurrence_backward("kda", sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]), None,
+                                  sl(do), dhT[:, h:h + 1].transpose(-1, -2))
+        for n, r in zip(["dq", "dk", "dv", "dg", "dbeta"], res[:5]):
+            assert_close_grad(r[:, :, h:h + 1], ref[n], "bf16", f"full size head {h} {n}")
+        assert_close_grad(res[5][:, h:h + 1], np.swapaxes(ref["dh0"], -1, -2), "bf16", f"full size head {h} dh0")
 
 
 PRO_CASES = [("kda", "bf16", 128, dict(qk=True, sig=True, x2=False, scale=0.5)),
