@@ -64,14 +64,26 @@ __device__ __forceinline__ float row16_sum(float v) {
     v += dpp_peer<0x140>(v);    // row_mirror
     return v;
 }
+// Across rows: v_permlane16_swap / v_permlane32_swap of a value with
+// itself leave the two rows (halves) of each pair in the two results, so
+// their sum is the pair's total in every lane, without the LDS crossbar.
 template <int N>
 __device__ __forceinline__ float lane_group_sum(float v) {
     static_assert(N == 16 || N == 32 || N == 64, "lane group");
     v = row16_sum(v);
-    if constexpr (N >= 32) v += __shfl_xor(v, 16, 64);
-    if constexpr (N >= 64) v += __shfl_xor(v, 32, 64);
+    if constexpr (N >= 32) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    if constexpr (N >= 64) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
     return v;
 }
+// 1 / sqrt(x) for the L2 norms (x >= the norm epsilon > 0): the hardware
+// reciprocal square root, within an ulp or two of the rounded quotient
+__device__ __forceinline__ float inv_sqrt(float x) { return __builtin_amdgcn_rsqf(x); }
 
 __device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f(float x) { return x; }
@@ -119,7 +131,9 @@ __device__ __forceinline__ float pro_gate(const ProHead& p, float a) {
 }
 __device__ __forceinline__ float pro_beta(const ProHead& p, float b) {
     if (!(p.ops & PRO_BETA_SIGMOID)) return b;
-    const float s = 1.f / (1.f + expf(-b));
+    // 1 / (1 + e^-b) from the hardware exp2 and reciprocal (e^-b = inf for
+    // very negative b gives 0, as it should)
+    const float s = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-b * kLog2e));
     return (p.ops & PRO_BETA_X2) ? 2.f * s : s;
 }
 

@@ -84,8 +84,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
                 }
                 sk2 = lane_group_sum<64>(sk2);
                 sq2 = lane_group_sum<64>(sq2);
-                nk = 1.f / sqrtf(sk2 + kNormEps);
-                nq *= 1.f / sqrtf(sq2 + kNormEps);
+                nk = inv_sqrt(sk2 + kNormEps);
+                nq *= inv_sqrt(sq2 + kNormEps);
             }
 #pragma unroll
             for (int j = 0; j < NPL; ++j) {

@@ -223,8 +223,8 @@ __device__ __forceinline__ void intra_chunk(const IntraIn<KIND, T, DK, DV>& in, 
                 }
                 sk = lane_group_sum<NCG>(sk);
                 sq = lane_group_sum<NCG>(sq);
-                nk[i] = 1.f / sqrtf(sk + kNormEps);
-                nq[i] = 1.f / sqrtf(sq + kNormEps);
+                nk[i] = inv_sqrt(sk + kNormEps);
+                nq[i] = inv_sqrt(sq + kNormEps);
             }
         }
 #pragma unroll

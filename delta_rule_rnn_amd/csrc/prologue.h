@@ -57,8 +57,8 @@ __global__ __launch_bounds__(256) void prologue_apply_kernel(const T* __restrict
         if (ph.ops & PRO_QK_L2NORM) {
             sq = lane_group_sum<64>(sq);
             sk = lane_group_sum<64>(sk);
-            nq *= 1.f / sqrtf(sq + kNormEps);
-            nk = 1.f / sqrtf(sk + kNormEps);
+            nq *= inv_sqrt(sq + kNormEps);
+            nk = inv_sqrt(sk + kNormEps);
         }
 #pragma unroll
         for (int j = 0; j < NPL; ++j) {
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void prologue_backward_kernel(const T* __restr
         if (norm) {
             sq = lane_group_sum<64>(sq);
             sk = lane_group_sum<64>(sk);
-            const float iq = 1.f / sqrtf(sq + kNormEps), ik = 1.f / sqrtf(sk + kNormEps);
+            const float iq = inv_sqrt(sq + kNormEps), ik = inv_sqrt(sk + kNormEps);
             float dotq = 0.f, dotk = 0.f;
 #pragma unroll
             for (int j = 0; j < NPL; ++j) {
