@@ -356,14 +356,31 @@ __device__ __forceinline__ void seg_chunk_ops(const SegIn<KIND, T, DK, DV>& in, 
             }
         }
         // Kbar^T and V^T: PL consecutive positions of one channel per store
-        // (V moves as stored, without a round trip through fp32)
+        // (V moves as stored, without a round trip through fp32).  The lanes
+        // of one store hold channels CPT apart, rows whose addresses fall
+        // on few LDS banks; at CPT = 4 each lane takes its channels in an
+        // order rotated by (cg / 4) mod 4, so that one store's 64 lanes
+        // spread over all banks
+        const int rot = CPT == 4 ? (cg >> 2) & 3 : 0;
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
-            st4(sKbT + (ch0 + j) * LDC + p0, kb[j]);
+            const int jj = (j + rot) & (CPT - 1);
+            float kr[PL];
             typename VecOf<T, 4>::type vt;
 #pragma unroll
-            for (int i = 0; i < PL; ++i) vt[i] = vv[i][j];
-            *reinterpret_cast<typename VecOf<T, 4>::type*>(sVt + (ch0 + j) * LDC + p0) = vt;
+            for (int i = 0; i < PL; ++i) {
+                float x = kb[0][i];
+                T y = vv[i][0];
+#pragma unroll
+                for (int c = 1; c < CPT; ++c) {
+                    x = jj == c ? kb[c][i] : x;
+                    y = jj == c ? vv[i][c] : y;
+                }
+                kr[i] = x;
+                vt[i] = y;
+            }
+            st4(sKbT + (ch0 + jj) * LDC + p0, kr);
+            *reinterpret_cast<typename VecOf<T, 4>::type*>(sVt + (ch0 + jj) * LDC + p0) = vt;
         }
         if (qg == 0) {
 #pragma unroll
