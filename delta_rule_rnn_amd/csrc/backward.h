@@ -736,10 +736,6 @@ struct StateSmem {
                             RPHI = DO + (size_t)C * LSV, RSINK = RPHI + DK, REV = RSINK + 64;
 };
 
-__device__ __forceinline__ int xcd_logical(int bid, int G) {
-    return (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
-}
-
 // Pull the 128-byte lines of [rows][cols] fp32 blocks (row stride gs) into
 // L2: one 4-byte LDS-DMA per line, spread over the workgroup's threads.
 __device__ __forceinline__ void l2_touch(const float* __restrict__ src, size_t gs, int rows, int cols, int tid,

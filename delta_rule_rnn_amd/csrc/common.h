@@ -67,6 +67,14 @@ __device__ __forceinline__ float row16_sum(float v) {
 // Across rows: v_permlane16_swap / v_permlane32_swap of a value with
 // itself leave the two rows (halves) of each pair in the two results, so
 // their sum is the pair's total in every lane, without the LDS crossbar.
+// Logical id of workgroup bid of a grid of G: the hardware dispatches
+// workgroup i to XCD i mod 8, so when G is a multiple of 8 each XCD gets the
+// contiguous logical range [x G/8, (x+1) G/8) and consecutive logical ids
+// share one XCD's L2; otherwise the identity.
+__device__ __forceinline__ int xcd_logical(int bid, int G) {
+    return (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+}
+
 template <int N>
 __device__ __forceinline__ float lane_group_sum(float v) {
     static_assert(N == 16 || N == 32 || N == 64, "lane group");

@@ -229,7 +229,7 @@ __global__ __launch_bounds__((inter_threads<PFD, C2>())) void inter_kernel(const
     const bool ownS = recur && NH * wave < 2 * NKB;   // Dk = 128: every recurrence wave
 
     const int G = gridDim.x, bid = blockIdx.x;
-    const int logical = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+    const int logical = xcd_logical(bid, G);
     const int chain = logical / NV, slice = logical % NV;
     // packed sequences take chains head-major (chain = h * N + sequence), so
     // that each XCD's contiguous range of logical ids holds every sequence

@@ -834,7 +834,10 @@ __global__ __launch_bounds__(kComposeThreads) void compose_kernel(const float* _
     __shared__ __attribute__((aligned(16))) float sST[16 * LDT];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, grp = lane >> 4;
-    const int chain = blockIdx.x / NSL, c0 = (blockIdx.x % NSL) * 16;
+    // the NSL slices of a chain read the same [M | N]: consecutive logical
+    // ids, so they share one XCD's L2
+    const int lb = xcd_logical(blockIdx.x, gridDim.x);
+    const int chain = lb / NSL, c0 = (lb % NSL) * 16;
     const float* xe0 = xend + (size_t)chain * NS * DK * LDX;
     struct Ops {
         Frag<float> m[TPW][NKB];   // rows of M_r (A fragments)
@@ -923,8 +926,11 @@ __global__ __launch_bounds__(kThreads) void correct_kernel(const T* __restrict__
     const int r16 = lane & 15, grp = lane >> 4;
     const int groups = (L + kCorrChunks - 1) / kCorrChunks;
     const int per = (NS - 1) * groups;
-    const int chain = blockIdx.x / per;
-    const int rem = blockIdx.x % per;
+    // a segment's workgroups read the same S_in: consecutive logical ids,
+    // so they share one XCD's L2
+    const int lb = xcd_logical(blockIdx.x, gridDim.x);
+    const int chain = lb / per;
+    const int rem = lb % per;
     const int r = 1 + rem / groups;
     const int c0 = r * L + (rem % groups) * kCorrChunks;
     const int c1 = min(min(c0 + kCorrChunks, (r + 1) * L), NT);
