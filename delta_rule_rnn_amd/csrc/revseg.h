@@ -374,7 +374,10 @@ __global__ __launch_bounds__(kRevComposeThreads) void rev_compose_kernel(const f
     __shared__ __attribute__((aligned(16))) float sET[16 * LDT];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, grp = lane >> 4;
-    const int chain = blockIdx.x / NSL, c0 = (blockIdx.x % NSL) * 16;
+    // the NSL slices of a chain read the same maps: consecutive logical
+    // ids, so they share one XCD's L2
+    const int lb = xcd_logical(blockIdx.x, gridDim.x);
+    const int chain = lb / NSL, c0 = (lb % NSL) * 16;
     auto trow = [&](int t) { return 16 * (wave * TPW + t); };
     f32x4 E[TPW];
 #pragma unroll
